@@ -1,0 +1,142 @@
+/*
+ * liblinattn -- kernelized linear attention on AMD Instinct MI355X (gfx950).
+ *
+ * Plain C ABI.  Every tensor argument is a DEVICE pointer owned by the caller;
+ * the library allocates nothing, keeps no per-call state and never blocks the
+ * host.  Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ * the default stream).  Argument errors are reported synchronously, before any
+ * work is enqueued, and leave every output untouched; la_last_error_message()
+ * then holds a one-line explanation (thread-local).
+ *
+ * Notation follows the pages: B batch, T tokens in this call, H heads, Dk
+ * query/key head size, Dv value head size, phi the feature map, eps the
+ * normalization epsilon.  All layouts are row-major with the innermost index
+ * last:
+ *   q, k       : (B, T, H, Dk)        v, out : (B, T, H, Dv)
+ *   mask       : (B, T) uint8, nonzero = valid token; NULL = all valid
+ *   state kv   : (B, H, Dk, Dv) float32  ("key_value_state")
+ *   state k    : (B, H, Dk)     float32  ("key_state"), only with the normalizer
+ * q, k, v and out share one floating dtype (la_dtype); state is always float32
+ * ("[Feature] LinearAttention layer for Keras", sections "Mathematical
+ * definition", "Streaming State", "Numerical Stability").
+ *
+ * Supported head sizes: Dk == Dv, one of 32, 64, 128.  Other sizes return
+ * LA_ERR_UNSUPPORTED (there is no slower fallback path).
+ */
+#ifndef LIBLINATTN_H
+#define LIBLINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_NULL_ARG = 1,     /* a required pointer is NULL */
+  LA_ERR_DTYPE = 2,        /* dtype code is not a supported floating type */
+  LA_ERR_SHAPE = 3,        /* negative / zero sizes, Hq not a multiple of Hkv, ... */
+  LA_ERR_STATE = 4,        /* state pointers inconsistent with mode / normalizer */
+  LA_ERR_BAD_ARG = 5,      /* bad enum, eps < 0, partial overlap of buffers, ... */
+  LA_ERR_UNSUPPORTED = 6,  /* valid request this library does not implement */
+  LA_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than la_*_workspace_size */
+  LA_ERR_DEVICE = 8        /* the HIP runtime reported an error at launch */
+} la_status;
+
+typedef enum { LA_DT_F32 = 0, LA_DT_BF16 = 1 } la_dtype;
+
+/* phi: elu(x)+1 (x+1 for x>0, exp(x) otherwise), or relu(x)+eps with the same
+ * eps as the denominator ("[Feature] LinearAttention layer for Keras", section
+ * "Feature maps"). */
+typedef enum { LA_FM_ELU_PLUS_ONE = 0, LA_FM_RELU_EPS = 1 } la_feature_map;
+
+/* Zero-fill a streaming state: kv (B,H,Dk,Dv) and, if k != NULL, k (B,H,Dk).
+ * The initial state of a causal stream is all zeros ("[Feature] LinearAttention
+ * layer for Keras", section "Streaming State", get_initial_state). */
+la_status la_initial_state(float* kv, float* k, int64_t B, int64_t H, int64_t Dk, int64_t Dv,
+                           void* stream);
+
+/* Bytes of device workspace la_forward needs for this shape (0 = none).  The
+ * value depends only on the arguments, never on the device. */
+la_status la_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                            int32_t dtype, int32_t causal, size_t* bytes);
+
+/* Full-sequence (or chunk-of-a-stream) attention.
+ *
+ * causal != 0 ("Mathematical definition / Causal", "Masking / Causal"): per
+ * (b,h), token by token, S += phi(k_t) v_t^T and Z += phi(k_t) for valid t, then
+ * out_t = phi(q_t)^T S / (phi(q_t)^T Z + eps) (or phi(q_t)^T S when
+ * use_normalizer == 0); the current token is in its own context; invalid tokens
+ * leave S, Z unchanged and get out_t = 0.  state_in_* (NULL = zeros) is the
+ * state before the first token, state_out_* (NULL = not returned) receives the
+ * state after the last one, so consecutive calls chain exactly like one call
+ * over the concatenated tokens ("Streaming State").  state_out may be the same
+ * buffers as state_in (in-place streaming); any other overlap is LA_ERR_BAD_ARG.
+ * With use_normalizer == 0 the k parts must be NULL (only kv is carried); with
+ * use_normalizer != 0, state_in_k / state_out_k are required whenever the
+ * matching kv pointer is given.
+ *
+ * causal == 0 ("Mathematical definition / Non-causal", "Masking / Non-causal"):
+ * S, Z are sums over all valid tokens, out_i = phi(q_i)^T S / (phi(q_i)^T Z + eps)
+ * at valid i and 0 at invalid i.  Non-causal attention exposes no state: all
+ * four state pointers must be NULL (else LA_ERR_STATE).
+ *
+ * T == 0 is allowed: nothing is read, state_out receives state_in (or zeros).
+ * workspace must hold la_workspace_size() bytes (may be NULL when that is 0);
+ * its contents on entry do not matter. */
+la_status la_forward(const void* q, const void* k, const void* v, const uint8_t* mask,
+                     const float* state_in_kv, const float* state_in_k,
+                     float* state_out_kv, float* state_out_k,
+                     int32_t causal, int32_t feature_map, int32_t use_normalizer, float eps,
+                     void* out, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                     int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* One causal decode step (T == 1): q, k, v are (B, H, Dk/Dv), mask is (B) or
+ * NULL, out is (B, H, Dv).  Same semantics as la_forward with T == 1
+ * ("Streaming State": token-by-token execution; "Execution Modes": a single
+ * token runs the recurrence).  state_in_kv is required (a stream always has a
+ * state; start one with la_initial_state); state_out may alias state_in
+ * exactly. */
+la_status la_step(const void* q, const void* k, const void* v, const uint8_t* mask,
+                  const float* state_in_kv, const float* state_in_k,
+                  float* state_out_kv, float* state_out_k,
+                  int32_t feature_map, int32_t use_normalizer, float eps,
+                  void* out, int64_t B, int64_t H, int64_t Dk, int64_t Dv, int32_t dtype,
+                  void* stream);
+
+/* Bytes of device workspace la_gated_forward needs (0 = none); shape-only. */
+la_status la_gated_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,
+                                  int64_t Dv, int32_t dtype, size_t* bytes);
+
+/* Gated linear recurrence with grouped-query heads (the LinearAttention
+ * operator page, ai.onnx since version 27: "gated" rule with a per-head scalar
+ * decay, or the "linear" rule when decay == NULL):
+ *   S_t = exp(g_t) S_{t-1} + k_t v_t^T        (per kv head)
+ *   o_t = scale * q_t^T S_t                   (per query head, S after the update)
+ * Query head h reads kv head h / (Hq/Hkv).  No feature map, no normalizer, no
+ * mask.  Packed layouts (byte-identical to the 4-D ones):
+ *   q (B,T,Hq*Dk), k (B,T,Hkv*Dk), v (B,T,Hkv*Dv), out (B,T,Hq*Dv) in `dtype`;
+ *   decay (B,T,Hkv) in `dtype`, log-space (NULL = all zero);
+ *   past_state (B,Hkv,Dk,Dv) float32 (NULL = zeros); present_state (same shape,
+ *   float32) is always written and may alias past_state exactly.
+ * scale == 0 means 1/sqrt(Dk).  Hq must be a positive multiple of Hkv
+ * (else LA_ERR_SHAPE). */
+la_status la_gated_forward(const void* q, const void* k, const void* v, const void* decay,
+                           const float* past_state, float* present_state, void* out,
+                           int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
+                           int32_t dtype, float scale, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Static string naming a status code. */
+const char* la_status_string(la_status s);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* la_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBLINATTN_H */

@@ -1,0 +1,567 @@
+// liblinattn C-ABI front end: argument validation, work planning and kernel
+// dispatch.  Every check runs on the host before anything is enqueued, so an
+// argument error never leaves a half-written output.  No device memory is
+// allocated here; the caller brings every buffer, including the workspace.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "liblinattn.h"
+#include "la_launch.hpp"
+
+#define LA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+la_status fail(la_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+la_status ok() {
+  g_msg[0] = '\0';
+  return LA_OK;
+}
+
+la_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(LA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Workgroups that keep all 256 compute units of an MI355X busy with two
+// resident chunk workgroups each.  A shape constant, not a device query, so
+// that workspace sizes depend on the shape alone.
+constexpr int64_t kTargetGroups = 512;
+constexpr int64_t kChunk = 64;
+constexpr int64_t kApplyGroups = 2048;
+
+bool head_size_ok(int64_t d) { return d == 32 || d == 64 || d == 128; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range range(const void* p, int64_t bytes) {
+  Range r;
+  r.lo = (uintptr_t)p;
+  r.hi = (uintptr_t)p + (uintptr_t)(bytes > 0 ? bytes : 0);
+  return r;
+}
+bool overlap(Range a, Range b) {
+  if (!a.lo || !b.lo || a.hi == a.lo || b.hi == b.lo) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Split of a causal sequence into segments of chunks (shape-only).
+struct CausalPlan {
+  int64_t nchunks, nseg, seg_chunks;
+};
+CausalPlan plan_causal(int64_t U, int64_t T) {
+  CausalPlan p;
+  p.nchunks = ceil_div(T, kChunk);
+  p.nseg = 1;
+  p.seg_chunks = p.nchunks;
+  if (U < kTargetGroups && p.nchunks > 1) {
+    int64_t want = ceil_div(kTargetGroups, U);
+    if (want > p.nchunks) want = p.nchunks;
+    p.seg_chunks = ceil_div(p.nchunks, want);
+    p.nseg = ceil_div(p.nchunks, p.seg_chunks);
+  }
+  return p;
+}
+
+struct NonCausalPlan {
+  int64_t nchunks, nsplit, split_chunks, apply_chunks, napply;
+};
+NonCausalPlan plan_noncausal(int64_t U, int64_t T) {
+  NonCausalPlan p;
+  p.nchunks = ceil_div(T, kChunk);
+  int64_t want = ceil_div(kTargetGroups, U);
+  if (want > p.nchunks) want = p.nchunks;
+  if (want < 1) want = 1;
+  p.split_chunks = ceil_div(p.nchunks, want);
+  p.nsplit = ceil_div(p.nchunks, p.split_chunks);
+  p.apply_chunks = ceil_div(U * p.nchunks, kApplyGroups);
+  if (p.apply_chunks > p.nchunks) p.apply_chunks = p.nchunks;
+  if (p.apply_chunks < 1) p.apply_chunks = 1;
+  p.napply = ceil_div(p.nchunks, p.apply_chunks);
+  return p;
+}
+
+int64_t state_elems(int64_t D, int norm) { return D * D + (norm ? D : 0); }
+
+size_t forward_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t D, int causal, int norm) {
+  const int64_t U = B * H;
+  if (U == 0 || T == 0) return 0;
+  if (causal) {
+    CausalPlan p = plan_causal(U, T);
+    if (p.nseg <= 1) return 0;
+    return (size_t)(U * p.nseg * state_elems(D, norm) * 4);
+  }
+  NonCausalPlan p = plan_noncausal(U, T);
+  return (size_t)(U * p.nsplit * state_elems(D, norm) * 4);
+}
+
+la_status check_common(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int32_t dtype) {
+  if (dtype != LA_DT_F32 && dtype != LA_DT_BF16)
+    return fail(LA_ERR_DTYPE, "dtype %d is not a supported floating type (0=f32, 1=bf16)", dtype);
+  if (B < 0 || T < 0 || H < 1 || Dk < 1 || Dv < 1)
+    return fail(LA_ERR_SHAPE, "bad sizes B=%lld T=%lld H=%lld Dk=%lld Dv=%lld", (long long)B,
+                (long long)T, (long long)H, (long long)Dk, (long long)Dv);
+  if (Dk != Dv || !head_size_ok(Dk))
+    return fail(LA_ERR_UNSUPPORTED, "head sizes Dk=%lld Dv=%lld: only Dk == Dv in {32,64,128}",
+                (long long)Dk, (long long)Dv);
+  if (B * H > (int64_t)1 << 30 || T > ((int64_t)1 << 31) - kChunk || H * Dk > (int64_t)1 << 30)
+    return fail(LA_ERR_SHAPE, "sizes exceed the 32-bit index ranges of the kernels");
+  return LA_OK;
+}
+
+}  // namespace
+
+LA_EXPORT const char* la_status_string(la_status s) {
+  switch (s) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_NULL_ARG: return "LA_ERR_NULL_ARG";
+    case LA_ERR_DTYPE: return "LA_ERR_DTYPE";
+    case LA_ERR_SHAPE: return "LA_ERR_SHAPE";
+    case LA_ERR_STATE: return "LA_ERR_STATE";
+    case LA_ERR_BAD_ARG: return "LA_ERR_BAD_ARG";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
+    case LA_ERR_DEVICE: return "LA_ERR_DEVICE";
+  }
+  return "LA_ERR_UNKNOWN";
+}
+
+LA_EXPORT const char* la_last_error_message(void) { return g_msg; }
+
+LA_EXPORT la_status la_initial_state(float* kv, float* k, int64_t B, int64_t H, int64_t Dk,
+                                     int64_t Dv, void* stream) {
+  if (B < 0 || H < 1 || Dk < 1 || Dv < 1) return fail(LA_ERR_SHAPE, "bad state sizes");
+  if (!kv) return fail(LA_ERR_NULL_ARG, "kv state pointer is NULL");
+  if (k && overlap(range(kv, B * H * Dk * Dv * 4), range(k, B * H * Dk * 4)))
+    return fail(LA_ERR_BAD_ARG, "kv and k state buffers overlap");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = la::launch_fill_zero(kv, B * H * Dk * Dv, st);
+  if (e == hipSuccess && k) e = la::launch_fill_zero(k, B * H * Dk, st);
+  return device_status(e, "la_initial_state");
+}
+
+LA_EXPORT la_status la_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                      int32_t dtype, int32_t causal, size_t* bytes) {
+  if (!bytes) return fail(LA_ERR_NULL_ARG, "bytes is NULL");
+  la_status s = check_common(B, T, H, Dk, Dv, dtype);
+  if (s != LA_OK) return s;
+  // the normaliser adds Dk floats per slot; size for it so the answer does not
+  // depend on use_normalizer
+  *bytes = forward_ws_bytes(B, T, H, Dk, causal != 0, 1);
+  return ok();
+}
+
+LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, const uint8_t* mask,
+                               const float* state_in_kv, const float* state_in_k,
+                               float* state_out_kv, float* state_out_k, int32_t causal,
+                               int32_t feature_map, int32_t use_normalizer, float eps, void* out,
+                               int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                               int32_t dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  la_status s = check_common(B, T, H, Dk, Dv, dtype);
+  if (s != LA_OK) return s;
+  if (feature_map != LA_FM_ELU_PLUS_ONE && feature_map != LA_FM_RELU_EPS)
+    return fail(LA_ERR_BAD_ARG, "feature_map %d is not 0 (elu+1) or 1 (relu+eps)", feature_map);
+  if (!(eps >= 0.f) || isinf(eps)) return fail(LA_ERR_BAD_ARG, "eps must be finite and >= 0");
+  const int norm = use_normalizer != 0;
+  const int64_t D = Dk;
+  const int64_t U = B * H;
+  const int64_t esz = dtype == LA_DT_BF16 ? 2 : 4;
+  const bool work = U > 0 && T > 0;
+  if (work && (!q || !k || !v || !out)) return fail(LA_ERR_NULL_ARG, "q, k, v and out are required");
+  if (!causal) {
+    if (state_in_kv || state_in_k || state_out_kv || state_out_k)
+      return fail(LA_ERR_STATE, "non-causal attention does not take or return a state");
+  } else if (!norm) {
+    if (state_in_k || state_out_k)
+      return fail(LA_ERR_STATE, "use_normalizer=0 carries only the kv state; k parts must be NULL");
+  } else {
+    if ((state_in_kv != nullptr) != (state_in_k != nullptr))
+      return fail(LA_ERR_STATE, "normalized state_in needs both kv and k (or neither)");
+    if ((state_out_kv != nullptr) != (state_out_k != nullptr))
+      return fail(LA_ERR_STATE, "normalized state_out needs both kv and k (or neither)");
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(state_in_kv) || !aligned16(state_out_kv))
+    return fail(LA_ERR_BAD_ARG, "q, k, v, out and kv states must be 16-byte aligned");
+  if (!aligned16(state_in_k) || !aligned16(state_out_k) || !aligned16(workspace))
+    return fail(LA_ERR_BAD_ARG, "k states and workspace must be 16-byte aligned");
+
+  const int64_t nqk = B * T * H * D * esz;
+  const Range rq = range(q, nqk), rk = range(k, nqk), rv = range(v, nqk), ro = range(out, nqk);
+  const Range rm = range(mask, B * T);
+  const Range rsi = range(state_in_kv, U * D * D * 4), rzi = range(state_in_k, U * D * 4);
+  const Range rso = range(state_out_kv, U * D * D * 4), rzo = range(state_out_k, U * D * 4);
+  const size_t need = forward_ws_bytes(B, T, H, D, causal != 0, norm);
+  const Range rw = range(workspace, (int64_t)need);
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(ro, rm) || overlap(ro, rsi) ||
+      overlap(ro, rzi) || overlap(ro, rso) || overlap(ro, rzo))
+    return fail(LA_ERR_BAD_ARG, "out overlaps another argument");
+  if (overlap(rso, rzo) || overlap(rsi, rzi))
+    return fail(LA_ERR_BAD_ARG, "kv and k state buffers overlap");
+  const Range outs[2] = {rso, rzo};
+  const Range ins[5] = {rq, rk, rv, rm, rw};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlap(o, i)) return fail(LA_ERR_BAD_ARG, "state_out overlaps an input or the workspace");
+  if ((overlap(rso, rsi) && state_out_kv != state_in_kv) ||
+      (overlap(rzo, rzi) && state_out_k != state_in_k) || overlap(rso, rzi) || overlap(rzo, rsi))
+    return fail(LA_ERR_BAD_ARG, "state_out may equal state_in exactly but not partially overlap it");
+  if (overlap(rw, rq) || overlap(rw, rk) || overlap(rw, rv) || overlap(rw, rm) || overlap(rw, rsi) ||
+      overlap(rw, rzi))
+    return fail(LA_ERR_BAD_ARG, "workspace overlaps an input");
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+
+  hipStream_t st = (hipStream_t)stream;
+  const int bf16 = dtype == LA_DT_BF16;
+  const int Di = (int)D;
+  hipError_t e = hipSuccess;
+
+  if (!work) {
+    // nothing to read: a causal state passes through unchanged (zeros if none)
+    if (causal && state_out_kv) {
+      const int64_t n = U * D * D;
+      e = (state_in_kv) ? (state_out_kv != state_in_kv ? la::launch_copy(state_out_kv, state_in_kv, n, st)
+                                                       : hipSuccess)
+                        : la::launch_fill_zero(state_out_kv, n, st);
+      if (e == hipSuccess && norm)
+        e = state_in_k ? (state_out_k != state_in_k ? la::launch_copy(state_out_k, state_in_k, U * D, st)
+                                                    : hipSuccess)
+                       : la::launch_fill_zero(state_out_k, U * D, st);
+    }
+    return device_status(e, "la_forward");
+  }
+
+  la::ChunkArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.mask = mask;
+  a.out = out;
+  a.T = (int32_t)T;
+  a.H = (int32_t)H;
+  a.eps = eps;
+  const int64_t SE = D * D, ZE = D;
+
+  if (causal) {
+    CausalPlan p = plan_causal(U, T);
+    if (p.nseg == 1) {
+      a.s_in = state_in_kv;
+      a.z_in = state_in_k;
+      a.s_in_u = SE;
+      a.z_in_u = ZE;
+      a.s_out = state_out_kv;
+      a.z_out = state_out_k;
+      a.s_out_u = SE;
+      a.z_out_u = ZE;
+      a.seg_count = 1;
+      a.seg_first = 0;
+      a.seg_chunks = (int32_t)p.nchunks;
+      a.nseg_total = 1;
+      e = la::launch_chunk(la::kModeCausal, bf16, Di, feature_map, norm, a, (int)U, st);
+      return device_status(e, "la_forward (causal)");
+    }
+    // split sequence: partial states of segments 0..nseg-2 -> slots 1..nseg-1,
+    // exclusive prefix (slot 0 = state_in), then every segment from its prefix.
+    float* ws_s = (float*)workspace;
+    float* ws_z = norm ? ws_s + U * p.nseg * SE : nullptr;
+    la::ChunkArgs ps = a;
+    ps.s_out = ws_s;
+    ps.z_out = ws_z;
+    ps.s_out_u = p.nseg * SE;
+    ps.s_out_s = SE;
+    ps.z_out_u = p.nseg * ZE;
+    ps.z_out_s = ZE;
+    ps.out_slot_off = 1;
+    ps.seg_count = (int32_t)(p.nseg - 1);
+    ps.seg_first = 0;
+    ps.seg_chunks = (int32_t)p.seg_chunks;
+    ps.nseg_total = (int32_t)p.nseg;
+    e = la::launch_chunk(la::kModeState, bf16, Di, feature_map, norm, ps, (int)(U * (p.nseg - 1)), st);
+    if (e == hipSuccess)
+      e = la::launch_seg_prefix(ws_s, ws_z, state_in_kv, state_in_k, (int)U, (int)p.nseg, Di, norm, st);
+    if (e == hipSuccess) {
+      la::ChunkArgs pc = a;
+      pc.s_in = ws_s;
+      pc.z_in = ws_z;
+      pc.s_in_u = p.nseg * SE;
+      pc.s_in_s = SE;
+      pc.z_in_u = p.nseg * ZE;
+      pc.z_in_s = ZE;
+      pc.s_out = state_out_kv;
+      pc.z_out = state_out_k;
+      pc.s_out_u = SE;
+      pc.z_out_u = ZE;
+      pc.seg_count = (int32_t)p.nseg;
+      pc.seg_first = 0;
+      pc.seg_chunks = (int32_t)p.seg_chunks;
+      pc.nseg_total = (int32_t)p.nseg;
+      e = la::launch_chunk(la::kModeCausal, bf16, Di, feature_map, norm, pc, (int)(U * p.nseg), st);
+    }
+    return device_status(e, "la_forward (causal, split)");
+  }
+
+  // non-causal: split reduction -> fixed-order sum -> readout
+  NonCausalPlan p = plan_noncausal(U, T);
+  float* ws_s = (float*)workspace;
+  float* ws_z = norm ? ws_s + U * p.nsplit * SE : nullptr;
+  la::ChunkArgs pr = a;
+  pr.s_out = ws_s;
+  pr.z_out = ws_z;
+  pr.s_out_u = p.nsplit * SE;
+  pr.s_out_s = SE;
+  pr.z_out_u = p.nsplit * ZE;
+  pr.z_out_s = ZE;
+  pr.out_slot_off = 0;
+  pr.seg_count = (int32_t)p.nsplit;
+  pr.seg_first = 0;
+  pr.seg_chunks = (int32_t)p.split_chunks;
+  pr.nseg_total = (int32_t)p.nsplit;
+  e = la::launch_chunk(la::kModeState, bf16, Di, feature_map, norm, pr, (int)(U * p.nsplit), st);
+  if (e == hipSuccess) e = la::launch_seg_sum(ws_s, ws_z, (int)U, (int)p.nsplit, Di, norm, st);
+  if (e == hipSuccess) {
+    la::ChunkArgs pa = a;
+    pa.s_in = ws_s;
+    pa.z_in = ws_z;
+    pa.s_in_u = p.nsplit * SE;
+    pa.s_in_s = 0;
+    pa.z_in_u = p.nsplit * ZE;
+    pa.z_in_s = 0;
+    pa.seg_count = (int32_t)p.napply;
+    pa.seg_first = 0;
+    pa.seg_chunks = (int32_t)p.apply_chunks;
+    pa.nseg_total = (int32_t)p.napply;
+    e = la::launch_chunk(la::kModeApply, bf16, Di, feature_map, norm, pa, (int)(U * p.napply), st);
+  }
+  return device_status(e, "la_forward (non-causal)");
+}
+
+LA_EXPORT la_status la_step(const void* q, const void* k, const void* v, const uint8_t* mask,
+                            const float* state_in_kv, const float* state_in_k,
+                            float* state_out_kv, float* state_out_k, int32_t feature_map,
+                            int32_t use_normalizer, float eps, void* out, int64_t B, int64_t H,
+                            int64_t Dk, int64_t Dv, int32_t dtype, void* stream) {
+  la_status s = check_common(B, 1, H, Dk, Dv, dtype);
+  if (s != LA_OK) return s;
+  if (feature_map != LA_FM_ELU_PLUS_ONE && feature_map != LA_FM_RELU_EPS)
+    return fail(LA_ERR_BAD_ARG, "feature_map %d is not 0 (elu+1) or 1 (relu+eps)", feature_map);
+  if (!(eps >= 0.f) || isinf(eps)) return fail(LA_ERR_BAD_ARG, "eps must be finite and >= 0");
+  const int norm = use_normalizer != 0;
+  const int64_t D = Dk, U = B * H;
+  const int64_t esz = dtype == LA_DT_BF16 ? 2 : 4;
+  if (U == 0) return ok();
+  if (!q || !k || !v || !out) return fail(LA_ERR_NULL_ARG, "q, k, v and out are required");
+  if (!state_in_kv || !state_out_kv)
+    return fail(LA_ERR_STATE, "a decode step needs state_in and state_out (kv)");
+  if (norm && (!state_in_k || !state_out_k))
+    return fail(LA_ERR_STATE, "use_normalizer=1 needs the k state in and out");
+  if (!norm && (state_in_k || state_out_k))
+    return fail(LA_ERR_STATE, "use_normalizer=0 carries only the kv state; k parts must be NULL");
+  if (!aligned16(state_in_kv) || !aligned16(state_out_kv))
+    return fail(LA_ERR_BAD_ARG, "kv states must be 16-byte aligned");
+  const Range rq = range(q, U * D * esz), rk = range(k, U * D * esz), rv = range(v, U * D * esz);
+  const Range ro = range(out, U * D * esz), rm = range(mask, B);
+  const Range rsi = range(state_in_kv, U * D * D * 4), rzi = range(state_in_k, U * D * 4);
+  const Range rso = range(state_out_kv, U * D * D * 4), rzo = range(state_out_k, U * D * 4);
+  const Range ins[4] = {rq, rk, rv, rm};
+  const Range outs[3] = {ro, rso, rzo};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlap(o, i)) return fail(LA_ERR_BAD_ARG, "an output overlaps q, k, v or mask");
+  if (overlap(ro, rsi) || overlap(ro, rzi) || overlap(ro, rso) || overlap(ro, rzo))
+    return fail(LA_ERR_BAD_ARG, "out overlaps a state buffer");
+  if ((overlap(rso, rsi) && state_out_kv != state_in_kv) ||
+      (overlap(rzo, rzi) && state_out_k != state_in_k) || overlap(rso, rzo) || overlap(rsi, rzi) ||
+      overlap(rso, rzi) || overlap(rzo, rsi))
+    return fail(LA_ERR_BAD_ARG, "state_out may equal state_in exactly but not partially overlap it");
+  la::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.mask = mask;
+  a.s_in = state_in_kv;
+  a.z_in = state_in_k;
+  a.s_out = state_out_kv;
+  a.z_out = state_out_k;
+  a.out = out;
+  a.H = (int32_t)H;
+  a.eps = eps;
+  hipError_t e = la::launch_decode(dtype == LA_DT_BF16, (int)D, feature_map, norm, a, (int)U,
+                                   (hipStream_t)stream);
+  return device_status(e, "la_step");
+}
+
+// ---------------------------------------------------------------------------
+// gated GQA recurrence
+
+namespace {
+struct GatedPlan {
+  int64_t nchunks, nseg, seg_chunks;
+};
+GatedPlan plan_gated(int64_t U, int64_t T) {
+  GatedPlan p;
+  p.nchunks = ceil_div(T, kChunk);
+  p.nseg = 1;
+  p.seg_chunks = p.nchunks;
+  if (U < kTargetGroups && p.nchunks > 1) {
+    int64_t want = ceil_div(kTargetGroups, U);
+    if (want > p.nchunks) want = p.nchunks;
+    p.seg_chunks = ceil_div(p.nchunks, want);
+    p.nseg = ceil_div(p.nchunks, p.seg_chunks);
+  }
+  return p;
+}
+size_t gated_ws_bytes(int64_t B, int64_t T, int64_t Hkv, int64_t D) {
+  const int64_t U = B * Hkv;
+  if (U == 0 || T == 0) return 0;
+  GatedPlan p = plan_gated(U, T);
+  if (p.nseg <= 1) return 0;
+  // slots of D*D floats plus one decay factor per slot (padded to 16 bytes)
+  return (size_t)(U * p.nseg * D * D * 4 + ceil_div(U * p.nseg, 4) * 16);
+}
+la_status check_gated(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
+                      int32_t dtype) {
+  if (dtype != LA_DT_F32 && dtype != LA_DT_BF16)
+    return fail(LA_ERR_DTYPE, "dtype %d is not a supported floating type (0=f32, 1=bf16)", dtype);
+  if (B < 0 || T < 0 || Hq < 1 || Hkv < 1 || Dk < 1 || Dv < 1)
+    return fail(LA_ERR_SHAPE, "bad sizes");
+  if (Hq % Hkv != 0)
+    return fail(LA_ERR_SHAPE, "q_num_heads (%lld) must be a positive multiple of kv_num_heads (%lld)",
+                (long long)Hq, (long long)Hkv);
+  const int64_t G = Hq / Hkv;
+  if (Dk != Dv || !head_size_ok(Dk))
+    return fail(LA_ERR_UNSUPPORTED, "head sizes Dk=%lld Dv=%lld: only Dk == Dv in {32,64,128}",
+                (long long)Dk, (long long)Dv);
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(LA_ERR_UNSUPPORTED, "q heads per kv head = %lld: supported 1, 2, 4, 8", (long long)G);
+  if (B * Hkv > (int64_t)1 << 30 || T > ((int64_t)1 << 31) - kChunk || Hq * Dk > (int64_t)1 << 30)
+    return fail(LA_ERR_SHAPE, "sizes exceed the 32-bit index ranges of the kernels");
+  return LA_OK;
+}
+}  // namespace
+
+LA_EXPORT la_status la_gated_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
+                                            int64_t Dk, int64_t Dv, int32_t dtype, size_t* bytes) {
+  if (!bytes) return fail(LA_ERR_NULL_ARG, "bytes is NULL");
+  la_status s = check_gated(B, T, Hq, Hkv, Dk, Dv, dtype);
+  if (s != LA_OK) return s;
+  *bytes = gated_ws_bytes(B, T, Hkv, Dk);
+  return ok();
+}
+
+LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v,
+                                     const void* decay, const float* past_state,
+                                     float* present_state, void* out, int64_t B, int64_t T,
+                                     int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
+                                     int32_t dtype, float scale, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  la_status s = check_gated(B, T, Hq, Hkv, Dk, Dv, dtype);
+  if (s != LA_OK) return s;
+  if (isnan(scale) || isinf(scale)) return fail(LA_ERR_BAD_ARG, "scale must be finite");
+  const int64_t D = Dk, U = B * Hkv, G = Hq / Hkv;
+  const int64_t esz = dtype == LA_DT_BF16 ? 2 : 4;
+  if (U > 0 && !present_state) return fail(LA_ERR_NULL_ARG, "present_state is required");
+  const bool work = U > 0 && T > 0;
+  if (work && (!q || !k || !v || !out)) return fail(LA_ERR_NULL_ARG, "q, k, v and out are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(past_state) ||
+      !aligned16(present_state) || !aligned16(workspace))
+    return fail(LA_ERR_BAD_ARG, "tensors and workspace must be 16-byte aligned");
+  const Range rq = range(q, B * T * Hq * D * esz), rk = range(k, B * T * Hkv * D * esz);
+  const Range rv = range(v, B * T * Hkv * D * esz), ro = range(out, B * T * Hq * D * esz);
+  const Range rg = range(decay, B * T * Hkv * esz);
+  const Range rpi = range(past_state, U * D * D * 4), rpo = range(present_state, U * D * D * 4);
+  const size_t need = gated_ws_bytes(B, T, Hkv, D);
+  const Range rw = range(workspace, (int64_t)need);
+  const Range ins[5] = {rq, rk, rv, rg, rw};
+  for (const Range& i : ins)
+    if (overlap(ro, i) || overlap(rpo, i)) return fail(LA_ERR_BAD_ARG, "an output overlaps an input");
+  if (overlap(ro, rpi) || overlap(ro, rpo) || overlap(rw, rpi) || overlap(rw, rq) || overlap(rw, rk) ||
+      overlap(rw, rv) || overlap(rw, rg))
+    return fail(LA_ERR_BAD_ARG, "buffers overlap");
+  if (overlap(rpo, rpi) && present_state != past_state)
+    return fail(LA_ERR_BAD_ARG, "present_state may equal past_state exactly but not partially overlap it");
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (scale == 0.f) scale = 1.f / sqrtf((float)D);
+  hipStream_t st = (hipStream_t)stream;
+  const int bf16 = dtype == LA_DT_BF16;
+  hipError_t e = hipSuccess;
+  if (!work) {
+    if (U > 0)
+      e = past_state ? (present_state != past_state
+                            ? la::launch_copy(present_state, past_state, U * D * D, st)
+                            : hipSuccess)
+                     : la::launch_fill_zero(present_state, U * D * D, st);
+    return device_status(e, "la_gated_forward");
+  }
+  la::GatedArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.decay = decay;
+  a.out = out;
+  a.T = (int32_t)T;
+  a.Hq = (int32_t)Hq;
+  a.Hkv = (int32_t)Hkv;
+  a.scale = scale;
+  const int64_t SE = D * D;
+  GatedPlan p = plan_gated(U, T);
+  if (p.nseg == 1) {
+    a.s_in = past_state;
+    a.s_in_u = SE;
+    a.s_out = present_state;
+    a.s_out_u = SE;
+    a.seg_count = 1;
+    a.seg_chunks = (int32_t)p.nchunks;
+    a.nseg_total = 1;
+    e = la::launch_gated(la::kModeCausal, bf16, (int)D, (int)G, a, (int)U, st);
+    return device_status(e, "la_gated_forward");
+  }
+  float* ws_s = (float*)workspace;
+  float* ws_a = ws_s + U * p.nseg * SE;
+  la::GatedArgs ps = a;
+  ps.s_out = ws_s;
+  ps.s_out_u = p.nseg * SE;
+  ps.s_out_s = SE;
+  ps.a_out = ws_a;
+  ps.out_slot_off = 1;
+  ps.seg_count = (int32_t)(p.nseg - 1);
+  ps.seg_chunks = (int32_t)p.seg_chunks;
+  ps.nseg_total = (int32_t)p.nseg;
+  e = la::launch_gated(la::kModeState, bf16, (int)D, (int)G, ps, (int)(U * (p.nseg - 1)), st);
+  if (e == hipSuccess)
+    e = la::launch_gated_prefix(ws_s, ws_a, past_state, (int)U, (int)p.nseg, (int)D, st);
+  if (e == hipSuccess) {
+    la::GatedArgs pc = a;
+    pc.s_in = ws_s;
+    pc.s_in_u = p.nseg * SE;
+    pc.s_in_s = SE;
+    pc.s_out = present_state;
+    pc.s_out_u = SE;
+    pc.seg_count = (int32_t)p.nseg;
+    pc.seg_chunks = (int32_t)p.seg_chunks;
+    pc.nseg_total = (int32_t)p.nseg;
+    e = la::launch_gated(la::kModeCausal, bf16, (int)D, (int)G, pc, (int)(U * p.nseg), st);
+  }
+  return device_status(e, "la_gated_forward (split)");
+}

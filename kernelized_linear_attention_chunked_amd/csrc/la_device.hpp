@@ -1,0 +1,127 @@
+// Device helpers shared by the liblinattn kernels (gfx950 / CDNA4 only).
+//
+// Conventions used by every kernel:
+//  * a workgroup is 256 threads = 4 wavefronts of 64 lanes;
+//  * lane l of a wave is split as lr = l % 16 (row/column inside a 16x16 MFMA
+//    tile) and lg = l / 16 (one of the four lane groups that share the
+//    contraction index);
+//  * MFMA tiles are 16x16 with fp32 accumulators.  For an accumulator the lane
+//    holds column lr and rows 4*lg + q (q = 0..3).  An A operand lane supplies
+//    row lr, a B operand lane supplies column lr, and both supply the same set
+//    of contraction indices for their lane group; which indices a lane group
+//    carries is free as long as A and B agree, which is how the kernels avoid
+//    transposes (see each contraction's comment);
+//  * bf16 data are handled as raw 16-bit patterns; conversions round to
+//    nearest even.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;  // 4 wavefronts
+constexpr int kChunk = 64;     // tokens per chunk of the chunk-parallel kernels
+
+enum FeatureMap { kEluPlusOne = 0, kReluEps = 1 };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// phi of the Keras proposal, section "Feature maps": elu(x)+1 with slope 1, or
+// relu(x)+eps.  Evaluated in fp32 (the accumulator type).
+template <int FM>
+__device__ __forceinline__ float phi(float x, float eps) {
+  if constexpr (FM == kEluPlusOne) {
+    return x > 0.f ? x + 1.f : __expf(x);
+  } else {
+    return fmaxf(x, 0.f) + eps;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Operand traits.  A "vector" is 16 bytes of one row in memory: 8 bf16 or 4
+// fp32 values.  One vector-step contracts KB = 4 * VEC indices: lane group lg
+// carries indices [KB*m + VEC*lg, KB*m + VEC*lg + VEC).  For bf16 that is one
+// v_mfma_f32_16x16x32_bf16; for fp32 four v_mfma_f32_16x16x4_f32 (element e of
+// the vector in the e-th instruction).
+template <typename DT>
+struct Op;
+
+template <>
+struct Op<uint16_t> {
+  static constexpr int VEC = 8;
+  static constexpr int KB = 32;
+  static constexpr int ESZ = 2;
+  __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
+  __device__ __forceinline__ static void unpack(const u32x4_t& v, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static u32x4_t pack(const float (&f)[8]) {
+    u32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    return r;
+  }
+};
+
+template <>
+struct Op<float> {
+  static constexpr int VEC = 4;
+  static constexpr int KB = 16;
+  static constexpr int ESZ = 4;
+  __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(b[e]), acc,
+                                                 0, 0, 0);
+  }
+  __device__ __forceinline__ static void unpack(const u32x4_t& v, float (&f)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  }
+  __device__ __forceinline__ static u32x4_t pack(const float (&f)[4]) {
+    u32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(f[i]);
+    return r;
+  }
+};
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return *(const u32x4_t*)p; }
+__device__ __forceinline__ void st16(void* p, const u32x4_t& v) { *(u32x4_t*)p = v; }
+
+// Store four consecutive fp32 results as the output dtype.
+__device__ __forceinline__ void store4(uint16_t* p, float a, float b, float c, float d) {
+  u32x2_t v;
+  v[0] = pack_bf16x2(a, b);
+  v[1] = pack_bf16x2(c, d);
+  *(u32x2_t*)p = v;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  f32x4_t v = {a, b, c, d};
+  *(f32x4_t*)p = v;
+}
+
+}  // namespace la

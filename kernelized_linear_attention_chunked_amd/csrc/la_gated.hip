@@ -1,0 +1,452 @@
+// Gated linear recurrence with grouped-query heads, chunk-parallel (the
+// "LinearAttention" operator page, ai.onnx since version 27, "gated" rule with a
+// per-head scalar decay, and "linear" when there is no decay):
+//   S_t = exp(g_t) S_{t-1} + k_t v_t^T ,   o_t = scale * q_t^T S_t
+// Query head h of a group reads kv head h / G.  The page allows any
+// chunk-parallel evaluation that reproduces the sequential recurrence.
+//
+// Inside a chunk of 64 tokens, with b_i = sum_{s<=i} g_s (inclusive, per chunk):
+//   o_i = scale * [ exp(b_i) q_i^T S_prev + sum_{j<=i} exp(b_i - b_j) (q_i.k_j) v_j ]
+//   S   = exp(b_63) S_prev + sum_j exp(b_63 - b_j) k_j v_j^T
+// Every factor is exp of a sum of g over a later stretch of tokens, so for
+// g <= 0 it never exceeds 1 (exp(-b_j) alone is never formed).
+//
+// One workgroup serves one (batch, kv head) unit and a segment of chunks, with
+// all G query heads of the group: 4*P wavefronts, wave w = (head part hp =
+// w/4, row part wr = w%4); the wave owns query rows [16wr, 16wr+16) of heads
+// hp, hp+P, ...  The state tiles are spread over all waves.  The k/v/decay of
+// a chunk are loaded once and shared by the G heads.
+#include "la_device.hpp"
+#include "la_launch.hpp"
+
+namespace la {
+
+template <int G>
+struct GatedShape {
+  static constexpr int P = G >= 2 ? 2 : 1;  // head parts per workgroup
+  static constexpr int NW = 4 * P;          // wavefronts
+  static constexpr int NTH = 64 * NW;       // threads
+  static constexpr int HPW = G / P;         // query heads per wave
+};
+
+template <typename DT>
+__device__ __forceinline__ float ld_scalar(const DT* p);
+template <>
+__device__ __forceinline__ float ld_scalar<uint16_t>(const uint16_t* p) {
+  return bf16_bits_to_f32(*p);
+}
+template <>
+__device__ __forceinline__ float ld_scalar<float>(const float* p) {
+  return *p;
+}
+
+template <typename DT, int D, int G, int MODE>
+__global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) {
+  using O = Op<DT>;
+  using SH = GatedShape<G>;
+  constexpr int P = SH::P, NW = SH::NW, NTH = SH::NTH, HPW = SH::HPW;
+  constexpr int VEC = O::VEC, KB = O::KB, ESZ = O::ESZ;
+  constexpr int NDT = D / 16;
+  constexpr int CB = D / VEC;
+  constexpr int LOADERS = NTH < kChunk * CB ? NTH : kChunk * CB;
+  constexpr int NTOK = kChunk * CB / LOADERS;
+  constexpr int NQ = D / KB;
+  constexpr int NKS = kChunk / KB;
+  constexpr int PADE = 16 / ESZ;
+  constexpr int KN_LD = D + PADE;
+  constexpr int VT_LD = kChunk + PADE;
+  constexpr int SB_LD = D + PADE;
+  constexpr bool OUT = MODE == kModeCausal;
+  constexpr int KN_BYTES = kChunk * KN_LD * ESZ;
+  constexpr int VT_BYTES = D * VT_LD * ESZ;
+  constexpr int SB_BYTES = OUT ? D * SB_LD * ESZ : 0;
+  constexpr int NS = NDT * NDT;
+  constexpr int TPW = (NS + NW - 1) / NW;
+  static_assert(NTOK >= 1 && NQ >= 1, "unsupported head size");
+
+  __shared__ __align__(16) unsigned char smem[KN_BYTES + VT_BYTES + SB_BYTES + 16];
+  DT* Kn = (DT*)smem;
+  DT* Vt = (DT*)(smem + KN_BYTES);
+  DT* Sb = (DT*)(smem + KN_BYTES + VT_BYTES);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hp = w >> 2, wr = w & 3;
+  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int u = blockIdx.x / a.seg_count;
+  const int s = a.seg_first + blockIdx.x % a.seg_count;
+  const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
+  const int b = u / Hkv, j = u % Hkv;
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const int c0 = s * a.seg_chunks;
+  const int c1 = min(c0 + a.seg_chunks, nchunks);
+  const int QS = Hq * D, KS = Hkv * D;  // token strides of q/out and k/v
+  const DT* qb = (const DT*)a.q + (int64_t)b * T * QS + (int64_t)(j * G) * D;
+  DT* ob = (DT*)a.out + (int64_t)b * T * QS + (int64_t)(j * G) * D;
+  const DT* kb = (const DT*)a.k + (int64_t)b * T * KS + (int64_t)j * D;
+  const DT* vb = (const DT*)a.v + (int64_t)b * T * KS + (int64_t)j * D;
+  const DT* gb = a.decay ? (const DT*)a.decay + (int64_t)b * T * Hkv + j : nullptr;
+  const float scale = a.scale;
+
+  f32x4_t sacc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) sacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (OUT) {
+    const float* sin = a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr;
+    if (sin) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int tau = w * TPW + i;
+        if (tau < NS) {
+          const int rt = tau / NDT, ct = tau % NDT;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sacc[i][q] = sin[(16 * rt + 4 * lg + q) * D + 16 * ct + lr];
+        }
+      }
+    }
+  }
+  auto write_sb = [&]() {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tau = w * TPW + i;
+      if (tau < NS) {
+        const int rt = tau / NDT, ct = tau % NDT;
+        DT* p = Sb + (16 * ct + lr) * SB_LD + 16 * rt + 4 * lg;
+        if constexpr (ESZ == 2) {
+          u32x2_t v2;
+          v2[0] = pack_bf16x2(sacc[i][0], sacc[i][1]);
+          v2[1] = pack_bf16x2(sacc[i][2], sacc[i][3]);
+          *(u32x2_t*)p = v2;
+        } else {
+          *(f32x4_t*)p = sacc[i];
+        }
+      }
+    }
+  };
+  if constexpr (OUT) write_sb();
+
+  // ---- prefetch registers
+  const int cb = tid % CB, tg = tid / CB;
+  const bool loader = tid < LOADERS;
+  u32x4_t pk[NTOK], pv[NTOK], pq[OUT ? HPW * NQ : 1];
+  float pg = 0.f;
+  auto prefetch = [&](int c) {
+    const int tb = c * kChunk;
+    if (loader) {
+#pragma unroll
+      for (int n = 0; n < NTOK; ++n) {
+        const int tok = tb + tg * NTOK + n;
+        if (tok < T) {
+          const int64_t off = (int64_t)tok * KS + cb * VEC;
+          pk[n] = ld16(kb + off);
+          pv[n] = ld16(vb + off);
+        } else {
+          pk[n] = u32x4_t{0u, 0u, 0u, 0u};
+          pv[n] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+    {
+      const int tok = tb + l;
+      pg = (gb && tok < T) ? ld_scalar<DT>(gb + (int64_t)tok * Hkv) : 0.f;
+    }
+    if constexpr (OUT) {
+      const int tok = tb + 16 * wr + lr;
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const int hq = hp + P * hh;
+#pragma unroll
+        for (int m = 0; m < NQ; ++m)
+          pq[hh * NQ + m] = tok < T ? ld16(qb + (int64_t)tok * QS + hq * D + KB * m + VEC * lg)
+                                    : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  u32x4_t qop[OUT ? HPW * NQ : 1];
+  float bcs = 0.f;  // lane l: inclusive cumulative decay of token l of the chunk
+  float seg_log = 0.f;
+  auto stage = [&]() {
+    if (loader) {
+#pragma unroll
+      for (int n = 0; n < NTOK; ++n) st16(Kn + (tg * NTOK + n) * KN_LD + cb * VEC, pk[n]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        DT* p = Vt + (cb * VEC + e) * VT_LD + tg * NTOK;
+        if constexpr (ESZ == 2) {
+          uint32_t hw[NTOK];
+#pragma unroll
+          for (int n = 0; n < NTOK; ++n) hw[n] = (pv[n][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          if constexpr (NTOK == 1) {
+            *(uint16_t*)p = (uint16_t)hw[0];
+          } else if constexpr (NTOK == 2) {
+            *(uint32_t*)p = hw[0] | (hw[1] << 16);
+          } else {
+#pragma unroll
+            for (int n = 0; n < NTOK; n += 4) {
+              u32x2_t v2;
+              v2[0] = hw[n] | (hw[n + 1] << 16);
+              v2[1] = hw[n + 2] | (hw[n + 3] << 16);
+              *(u32x2_t*)(p + n) = v2;
+            }
+          }
+        } else {
+          float fv[NTOK];
+#pragma unroll
+          for (int n = 0; n < NTOK; ++n) fv[n] = __uint_as_float(pv[n][e]);
+          if constexpr (NTOK == 1) {
+            *(float*)p = fv[0];
+          } else if constexpr (NTOK == 2) {
+            *(float2*)p = make_float2(fv[0], fv[1]);
+          } else {
+#pragma unroll
+            for (int n = 0; n < NTOK; n += 4)
+              *(f32x4_t*)(p + n) = f32x4_t{fv[n], fv[n + 1], fv[n + 2], fv[n + 3]};
+          }
+        }
+      }
+    }
+    // inclusive scan of the chunk's decays across the wave (each wave keeps its own copy)
+    float x = pg;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(x, off);
+      if (l >= off) x += y;
+    }
+    bcs = x;
+    if constexpr (OUT) {
+#pragma unroll
+      for (int i = 0; i < HPW * NQ; ++i) qop[i] = pq[i];
+    }
+  };
+
+  auto compute = [&](int c) {
+    const float btot = __shfl(bcs, 63);
+    if constexpr (OUT) {
+      const float bi = __shfl(bcs, 16 * wr + lr);
+      const float ebi = __expf(bi);
+      // decay factor of A^T element (key 16jt + 4lg + q, query 16wr + lr)
+      float fac[4][4];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float bj = __shfl(bcs, 16 * jt + 4 * lg + q);
+          fac[jt][q] = (jt < wr || (jt == wr && 4 * lg + q <= lr)) ? __expf(bi - bj) : 0.f;
+        }
+      const int tok = c * kChunk + 16 * wr + lr;
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        f32x4_t at[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          at[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (jt <= wr) {
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) {
+              const u32x4_t av = ld16(Kn + (16 * jt + lr) * KN_LD + KB * m + VEC * lg);
+              O::mma(at[jt], av, qop[hh * NQ + m]);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) at[jt][q] *= fac[jt][q];
+          }
+        }
+        f32x4_t nacc[NDT];
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct) nacc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (ESZ == 2) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            if (2 * p <= wr) {
+              const int j0 = 32 * p + 4 * lg, j1 = j0 + 16;
+              u32x4_t bv;
+              bv[0] = pack_bf16x2(at[2 * p][0], at[2 * p][1]);
+              bv[1] = pack_bf16x2(at[2 * p][2], at[2 * p][3]);
+              bv[2] = pack_bf16x2(at[2 * p + 1][0], at[2 * p + 1][1]);
+              bv[3] = pack_bf16x2(at[2 * p + 1][2], at[2 * p + 1][3]);
+#pragma unroll
+              for (int ct = 0; ct < NDT; ++ct) {
+                const DT* vr = Vt + (16 * ct + lr) * VT_LD;
+                const u32x2_t lo = *(const u32x2_t*)(vr + j0);
+                const u32x2_t hi = *(const u32x2_t*)(vr + j1);
+                O::mma(nacc[ct], u32x4_t{lo[0], lo[1], hi[0], hi[1]}, bv);
+              }
+            }
+          }
+        } else {
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt) {
+            if (jt <= wr) {
+#pragma unroll
+              for (int ct = 0; ct < NDT; ++ct) {
+                const f32x4_t av = *(const f32x4_t*)(Vt + (16 * ct + lr) * VT_LD + 16 * jt + 4 * lg);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  nacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], at[jt][q], nacc[ct], 0, 0, 0);
+              }
+            }
+          }
+        }
+        // inter-chunk term with the query scaled by exp(b_i)
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+          float f[VEC];
+          O::unpack(qop[hh * NQ + m], f);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) f[e] *= ebi;
+          const u32x4_t qd = O::pack(f);
+#pragma unroll
+          for (int ct = 0; ct < NDT; ++ct) {
+            const u32x4_t av = ld16(Sb + (16 * ct + lr) * SB_LD + KB * m + VEC * lg);
+            O::mma(nacc[ct], av, qd);
+          }
+        }
+        if (tok < T) {
+          DT* orow = ob + (int64_t)tok * QS + (hp + P * hh) * D + 4 * lg;
+#pragma unroll
+          for (int ct = 0; ct < NDT; ++ct)
+            store4(orow + 16 * ct, scale * nacc[ct][0], scale * nacc[ct][1], scale * nacc[ct][2],
+                   scale * nacc[ct][3]);
+        }
+      }
+    }
+    // state: S = exp(btot) S + sum_t exp(btot - b_t) k_t v_t^T
+    {
+      const float eb = __expf(btot);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) sacc[i] *= eb;
+      float kw[NKS][VEC];
+#pragma unroll
+      for (int m = 0; m < NKS; ++m)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) kw[m][e] = __expf(btot - __shfl(bcs, KB * m + VEC * lg + e));
+      u32x4_t kop[NKS];
+      int cur_rt = -1;
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int tau = w * TPW + i;
+        if (tau < NS) {
+          const int rt = tau / NDT, ct = tau % NDT;
+          if (rt != cur_rt) {
+            cur_rt = rt;
+#pragma unroll
+            for (int m = 0; m < NKS; ++m) {
+              const DT* kc = Kn + (KB * m + VEC * lg) * KN_LD + 16 * rt + lr;
+              float f[VEC];
+#pragma unroll
+              for (int e = 0; e < VEC; ++e) {
+                if constexpr (ESZ == 2)
+                  f[e] = bf16_bits_to_f32(((const uint16_t*)kc)[e * KN_LD]) * kw[m][e];
+                else
+                  f[e] = ((const float*)kc)[e * KN_LD] * kw[m][e];
+              }
+              kop[m] = O::pack(f);
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < NKS; ++m) {
+            const u32x4_t bv = ld16(Vt + (16 * ct + lr) * VT_LD + KB * m + VEC * lg);
+            O::mma(sacc[i], kop[m], bv);
+          }
+        }
+      }
+      seg_log += btot;
+    }
+  };
+
+  if (c0 < c1) prefetch(c0);
+  for (int c = c0; c < c1; ++c) {
+    stage();
+    __syncthreads();
+    if (c + 1 < c1) prefetch(c + 1);
+    compute(c);
+    __syncthreads();
+    if constexpr (OUT) write_sb();
+  }
+
+  float* sout = nullptr;
+  if constexpr (OUT) {
+    if (s == a.nseg_total - 1) sout = a.s_out + u * a.s_out_u;
+  } else {
+    sout = a.s_out + u * a.s_out_u + (s + a.out_slot_off) * a.s_out_s;
+    if (tid == 0) a.a_out[(int64_t)u * a.nseg_total + s + a.out_slot_off] = __expf(seg_log);
+  }
+  if (sout) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tau = w * TPW + i;
+      if (tau < NS) {
+        const int rt = tau / NDT, ct = tau % NDT;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sout[(16 * rt + 4 * lg + q) * D + 16 * ct + lr] = sacc[i][q];
+      }
+    }
+  }
+}
+
+// In-place affine prefix over segments: slot s (s >= 1) holds the increment of
+// segment s-1 and a[s] its total decay factor on entry; on exit slot s holds
+// the state before segment s:  S(0) = past (or 0),  S(s) = a[s] S(s-1) + dS(s-1).
+__global__ __launch_bounds__(kThreads) void gated_prefix_kernel(float* ws_s, const float* ws_a,
+                                                                const float* s_in, int U, int nseg,
+                                                                int D) {
+  const int64_t per = (int64_t)D * D;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (int64_t)U * per) return;
+  const int u = (int)(idx / per);
+  const int64_t e = idx % per;
+  float* base = ws_s + (int64_t)u * nseg * per + e;
+  float acc = s_in ? s_in[(int64_t)u * per + e] : 0.f;
+  base[0] = acc;
+  for (int s = 1; s < nseg; ++s) {
+    acc = fmaf(ws_a[(int64_t)u * nseg + s], acc, base[s * per]);
+    base[s * per] = acc;
+  }
+}
+
+template <typename DT, int D, int G>
+static hipError_t launch_g(int mode, const GatedArgs& a, int grid, hipStream_t st) {
+  constexpr int NTH = GatedShape<G>::NTH;
+  if (mode == kModeCausal)
+    hipLaunchKernelGGL((gated_kernel<DT, D, G, kModeCausal>), dim3(grid), dim3(NTH), 0, st, a);
+  else
+    hipLaunchKernelGGL((gated_kernel<DT, D, G, kModeState>), dim3(grid), dim3(NTH), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename DT, int D>
+static hipError_t launch_gd(int mode, int G, const GatedArgs& a, int grid, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_g<DT, D, 1>(mode, a, grid, st);
+    case 2: return launch_g<DT, D, 2>(mode, a, grid, st);
+    case 4: return launch_g<DT, D, 4>(mode, a, grid, st);
+    default: return launch_g<DT, D, 8>(mode, a, grid, st);
+  }
+}
+
+template <typename DT>
+static hipError_t launch_gdt(int mode, int D, int G, const GatedArgs& a, int grid, hipStream_t st) {
+  switch (D) {
+    case 32: return launch_gd<DT, 32>(mode, G, a, grid, st);
+    case 64: return launch_gd<DT, 64>(mode, G, a, grid, st);
+    default: return launch_gd<DT, 128>(mode, G, a, grid, st);
+  }
+}
+
+hipError_t launch_gated(int mode, int bf16, int D, int G, const GatedArgs& a, int grid,
+                        hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  return bf16 ? launch_gdt<uint16_t>(mode, D, G, a, grid, st)
+              : launch_gdt<float>(mode, D, G, a, grid, st);
+}
+
+hipError_t launch_gated_prefix(float* ws_s, const float* ws_a, const float* s_in, int U, int nseg,
+                               int D, hipStream_t st) {
+  const int64_t n = (int64_t)U * D * D;
+  const int grid = (int)((n + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(gated_prefix_kernel, dim3(grid), dim3(kThreads), 0, st, ws_s, ws_a, s_in, U,
+                     nseg, D);
+  return hipGetLastError();
+}
+
+}  // namespace la

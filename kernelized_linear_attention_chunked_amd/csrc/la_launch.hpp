@@ -1,0 +1,86 @@
+// Internal interface between the C-ABI front end (la_api.cpp) and the kernel
+// translation units.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+// Arguments of the chunk-parallel kernel (la_chunk.hip).  A workgroup handles
+// unit u = (b,h) and segment s = seg_first + blockIdx % seg_count, i.e. chunks
+// [s*seg_chunks, min((s+1)*seg_chunks, nchunks)) of 64 tokens.
+struct ChunkArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint8_t* mask;  // (B,T) or null
+  void* out;
+  // initial state of the segment (null = zeros): s_in + u*s_in_u + s*s_in_s
+  const float* s_in;
+  const float* z_in;
+  int64_t s_in_u, s_in_s, z_in_u, z_in_s;
+  // state written at the end (causal: by the last segment only; state mode:
+  // slot s + out_slot_off of unit u)
+  float* s_out;
+  float* z_out;
+  int64_t s_out_u, s_out_s, z_out_u, z_out_s;
+  int32_t out_slot_off;
+  int32_t T, H;
+  int32_t seg_count, seg_first, seg_chunks, nseg_total;
+  float eps;
+};
+
+enum { kModeCausal = 0, kModeState = 1, kModeApply = 2 };
+
+hipError_t launch_chunk(int mode, int bf16, int D, int fm, int norm, const ChunkArgs& a, int grid,
+                        hipStream_t st);
+hipError_t launch_seg_prefix(float* ws_s, float* ws_z, const float* s_in, const float* z_in, int U,
+                             int nseg, int D, int norm, hipStream_t st);
+hipError_t launch_seg_sum(float* ws_s, float* ws_z, int U, int nseg, int D, int norm,
+                          hipStream_t st);
+
+// T == 1 decode step (la_decode.hip).  q,k,v,out: (B,H,D); state (B,H,D,D)+(B,H,D).
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint8_t* mask;  // (B) or null
+  const float* s_in;
+  const float* z_in;
+  float* s_out;
+  float* z_out;
+  void* out;
+  int32_t H;
+  float eps;
+};
+hipError_t launch_decode(int bf16, int D, int fm, int norm, const DecodeArgs& a, int units,
+                         hipStream_t st);
+
+// Zero fill (la_decode.hip).
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+hipError_t launch_copy(float* dst, const float* src, int64_t n, hipStream_t st);
+
+// Gated GQA recurrence (la_gated.hip).
+struct GatedArgs {
+  const void* q;      // (B,T,Hq*D)
+  const void* k;      // (B,T,Hkv*D)
+  const void* v;      // (B,T,Hkv*D)
+  const void* decay;  // (B,T,Hkv) or null
+  void* out;          // (B,T,Hq*D)
+  const float* s_in;  // initial state of the segment, s_in + u*s_in_u + s*s_in_s (null = zeros)
+  int64_t s_in_u, s_in_s;
+  float* s_out;       // final/partial state, see launch_gated
+  int64_t s_out_u, s_out_s;
+  float* a_out;       // state mode: per (unit, slot) total decay factor
+  int32_t out_slot_off;
+  int32_t T, Hq, Hkv;
+  int32_t seg_count, seg_first, seg_chunks, nseg_total;
+  float scale;
+};
+hipError_t launch_gated(int mode, int bf16, int D, int G, const GatedArgs& a, int grid,
+                        hipStream_t st);
+hipError_t launch_gated_prefix(float* ws_s, const float* ws_a, const float* s_in, int U, int nseg,
+                               int D, hipStream_t st);
+
+}  // namespace la

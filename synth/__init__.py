@@ -1,0 +1,111 @@
+"""Seeded synthetic inputs for the five benchmark workloads and the tests.
+
+This module only draws random tensors (and masks) of the workloads' shapes,
+dtypes and distributions.  It holds none of the attention arithmetic, so the
+oracle and the HIP library can both be fed from it without sharing any code.
+
+Recipes (all values drawn in float32 from a torch generator seeded per tensor,
+then rounded to nearest even to the storage dtype):
+
+* ``causal_fp32_small``   B=1 H=2 T=256 D=32, fp32: q,k ~ N(0, 0.5^2), v ~ N(0,1).
+* ``causal_bf16_d64``     B=8 H=16 T=2048 D=64, bf16: same distributions.
+* ``noncausal_relu_d128`` B=4 H=16 T=16384 D=128, bf16: q,k,v ~ N(0,1); right-padding
+  mask, valid length of row b uniform on the integers {T/2, ..., T}.
+* ``streaming_d128``      B=256 H=32 D=128, bf16: 4096 prefill tokens and 512
+  decode tokens, q,k ~ N(0, 0.5^2), v ~ N(0,1).
+* ``gated_gqa_d128``      B=2 T=32768 Hq=32 Hkv=8 D=128, bf16: q,v ~ N(0,1); k drawn
+  N(0,1) then L2-normalised per (b,t,kv head) in fp32 before rounding; decay
+  g = logsigmoid(x), x ~ N(2,1), computed in fp32 then rounded.
+"""
+from __future__ import annotations
+
+import zlib
+
+import torch
+
+WORKLOADS = {
+    "causal_fp32_small": dict(B=1, H=2, T=256, D=32, dtype=torch.float32, seed=1),
+    "causal_bf16_d64": dict(B=8, H=16, T=2048, D=64, dtype=torch.bfloat16, seed=2),
+    "noncausal_relu_d128": dict(B=4, H=16, T=16384, D=128, dtype=torch.bfloat16, seed=3),
+    "streaming_d128": dict(B=256, H=32, T=4096, T_decode=512, D=128, dtype=torch.bfloat16, seed=4),
+    "gated_gqa_d128": dict(B=2, T=32768, Hq=32, Hkv=8, D=128, dtype=torch.bfloat16, seed=5),
+}
+
+
+def _gen(seed: int, name: str, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 1000003 + zlib.crc32(name.encode())) % (2**63 - 1))
+    return g
+
+
+def normal(shape, std, dtype, device, seed, name, chunk_elems=1 << 28):
+    """N(0, std^2) drawn in fp32 then rounded to ``dtype``; generated in slices
+    along dim 0 so the fp32 temporary stays bounded for very large tensors."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    g = _gen(seed, name, device)
+    flat = out.view(shape[0], -1)
+    per_row = flat.shape[1]
+    rows = max(1, chunk_elems // max(per_row, 1))
+    for r0 in range(0, shape[0], rows):
+        r1 = min(shape[0], r0 + rows)
+        tmp = torch.randn((r1 - r0, per_row), generator=g, device=device, dtype=torch.float32)
+        flat[r0:r1] = (tmp * std).to(dtype)
+    return out
+
+
+def qkv(B, T, H, D, dtype, device, seed, q_std=0.5, k_std=0.5, v_std=1.0, tag=""):
+    q = normal((B, T, H, D), q_std, dtype, device, seed, "q" + tag)
+    k = normal((B, T, H, D), k_std, dtype, device, seed, "k" + tag)
+    v = normal((B, T, H, D), v_std, dtype, device, seed, "v" + tag)
+    return q, k, v
+
+
+def right_padding_mask(B, T, device, seed, lo=None, hi=None):
+    """(B,T) bool: valid iff t < L_b with L_b uniform on {lo..hi} (default T/2..T)."""
+    lo = T // 2 if lo is None else lo
+    hi = T if hi is None else hi
+    g = _gen(seed, "mask", "cpu")
+    L = torch.randint(lo, hi + 1, (B,), generator=g)
+    m = torch.arange(T)[None, :] < L[:, None]
+    return m.to(device), L
+
+
+def random_mask(B, T, p_valid, device, seed, tag=""):
+    g = _gen(seed, "rmask" + tag, "cpu")
+    return (torch.rand((B, T), generator=g) < p_valid).to(device)
+
+
+def l2_normalized(shape, dtype, device, seed, name):
+    """N(0,1) rows normalised to unit L2 norm over the last dim (fp32), then rounded."""
+    x = normal(shape, 1.0, torch.float32, device, seed, name)
+    x = x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+    return x.to(dtype)
+
+
+def logsigmoid_decay(shape, dtype, device, seed, mean=2.0, std=1.0):
+    x = normal(shape, std, torch.float32, device, seed, "g") + mean
+    return torch.nn.functional.logsigmoid(x).to(dtype)
+
+
+def workload(name: str, device="cpu"):
+    """All inputs of a named workload as a dict of tensors on ``device``."""
+    w = WORKLOADS[name]
+    s, dt = w["seed"], w["dtype"]
+    if name == "gated_gqa_d128":
+        B, T, Hq, Hkv, D = w["B"], w["T"], w["Hq"], w["Hkv"], w["D"]
+        q = normal((B, T, Hq * D), 1.0, dt, device, s, "q")
+        k = l2_normalized((B, T, Hkv, D), dt, device, s, "k").reshape(B, T, Hkv * D)
+        v = normal((B, T, Hkv * D), 1.0, dt, device, s, "v")
+        g = logsigmoid_decay((B, T, Hkv), dt, device, s)
+        return dict(q=q, k=k, v=v, decay=g, Hq=Hq, Hkv=Hkv, D=D)
+    B, T, H, D = w["B"], w["T"], w["H"], w["D"]
+    if name == "noncausal_relu_d128":
+        q, k, v = qkv(B, T, H, D, dt, device, s, 1.0, 1.0, 1.0)
+        mask, L = right_padding_mask(B, T, device, s)
+        return dict(q=q, k=k, v=v, mask=mask, lengths=L)
+    q, k, v = qkv(B, T, H, D, dt, device, s)
+    out = dict(q=q, k=k, v=v)
+    if name == "streaming_d128":
+        Td = w["T_decode"]
+        out["q_dec"], out["k_dec"], out["v_dec"] = qkv(B, Td, H, D, dt, device, s, tag="_decode")
+    return out

@@ -1,0 +1,155 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch.
+
+Pointers passed here are fake (never dereferenced): every call below must fail
+validation, which happens before the library touches the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kernelized_linear_attention_chunked_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "liblinattn.h")
+
+OK, NULL_ARG, DTYPE, SHAPE, STATE, BAD_ARG, UNSUPPORTED, WORKSPACE, DEVICE = range(9)
+P = ctypes.c_void_p
+
+
+def fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return la.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:la_status|const char\*)\s+(la_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 8
+    assert sorted(la.EXPORTED_SYMBOLS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["LA_OK", "LA_ERR_NULL_ARG", "LA_ERR_DTYPE", "LA_ERR_SHAPE",
+                                 "LA_ERR_STATE", "LA_ERR_BAD_ARG", "LA_ERR_UNSUPPORTED",
+                                 "LA_ERR_WORKSPACE", "LA_ERR_DEVICE"]):
+        assert lib.la_status_string(code).decode() == name
+
+
+def fwd(lib, q=0x10000, k=0x20000000, v=0x40000000, mask=None, sik=None, sikk=None, sok=None,
+        sokk=None, causal=1, fm=0, norm=1, eps=1e-6, out=0x60000000, B=2, T=100, H=4, Dk=64,
+        Dv=64, dtype=1, ws=None, wsb=0):
+    f = lambda a: None if a is None else fake(a)
+    return lib.la_forward(f(q), f(k), f(v), f(mask), f(sik), f(sikk), f(sok), f(sokk), causal, fm,
+                          norm, eps, f(out), B, T, H, Dk, Dv, dtype, f(ws), wsb, None)
+
+
+def test_forward_argument_errors(lib):
+    big = 1 << 40  # far-apart fake buffers
+    assert fwd(lib, dtype=7) == DTYPE                      # non-floating dtype code
+    assert fwd(lib, B=-1) == SHAPE
+    assert fwd(lib, H=0) == SHAPE
+    assert fwd(lib, Dk=48, Dv=48) == UNSUPPORTED
+    assert fwd(lib, Dk=64, Dv=128) == UNSUPPORTED
+    assert fwd(lib, fm=5) == BAD_ARG
+    assert fwd(lib, eps=-1.0) == BAD_ARG
+    assert fwd(lib, eps=float("nan")) == BAD_ARG
+    assert fwd(lib, q=None) == NULL_ARG
+    assert fwd(lib, out=None) == NULL_ARG
+    # non-causal attention exposes no state
+    assert fwd(lib, causal=0, sik=big, sikk=2 * big) == STATE
+    assert fwd(lib, causal=0, sok=big, sokk=2 * big) == STATE
+    # normalized state needs both parts; unnormalized only kv
+    assert fwd(lib, sik=big) == STATE
+    assert fwd(lib, sok=big) == STATE
+    assert fwd(lib, norm=0, sik=big, sikk=2 * big) == STATE
+    # alignment
+    assert fwd(lib, q=0x10008) == BAD_ARG
+    # out overlapping q
+    assert fwd(lib, out=0x10000 + 64) == BAD_ARG
+    # partial overlap of state_out with state_in (exact aliasing is allowed)
+    assert fwd(lib, sik=big, sikk=2 * big, sok=big + 256, sokk=3 * big) == BAD_ARG
+    # the workspace is required for a split sequence (few units) ...
+    assert fwd(lib, B=1, H=2, T=4096) == WORKSPACE
+    n = ctypes.c_size_t(0)
+    assert lib.la_workspace_size(1, 4096, 2, 64, 64, 1, 1, ctypes.byref(n)) == OK
+    assert fwd(lib, B=1, H=2, T=4096, ws=big, wsb=n.value - 16) == WORKSPACE
+    # ... and for every non-causal call
+    assert fwd(lib, causal=0) == WORKSPACE
+    assert la.load_library().la_last_error_message().decode() != ""
+
+
+def test_workspace_sizes(lib):
+    n = ctypes.c_size_t(0)
+    # enough (batch, head) units: one pass, no workspace
+    assert lib.la_workspace_size(256, 1024, 32, 128, 128, 1, 1, ctypes.byref(n)) == OK
+    assert n.value == 0
+    # 128 units of 32 chunks: split into 4 segments of 8 chunks
+    assert lib.la_workspace_size(8, 2048, 16, 64, 64, 1, 1, ctypes.byref(n)) == OK
+    assert n.value == 128 * 4 * (64 * 64 + 64) * 4
+    # non-causal: 64 units of 256 chunks split 8 ways
+    assert lib.la_workspace_size(4, 16384, 16, 128, 128, 1, 0, ctypes.byref(n)) == OK
+    assert n.value == 64 * 8 * (128 * 128 + 128) * 4
+    # T == 0 needs nothing
+    assert lib.la_workspace_size(4, 0, 16, 128, 128, 1, 0, ctypes.byref(n)) == OK
+    assert n.value == 0
+    assert lib.la_workspace_size(4, 16, 16, 128, 128, 9, 0, ctypes.byref(n)) == DTYPE
+    assert lib.la_workspace_size(4, 16, 16, 128, 128, 1, 0, None) == NULL_ARG
+
+
+def test_step_argument_errors(lib):
+    f = fake
+    base = dict(q=f(0x10000), k=f(0x20000), v=f(0x30000), m=None, si=f(1 << 32), sik=f(1 << 33),
+                so=f(1 << 32), sok=f(1 << 33), fm=0, norm=1, eps=1e-6, out=f(0x40000), B=2, H=3,
+                Dk=128, Dv=128, dt=1)
+
+    def step(**kw):
+        a = dict(base, **kw)
+        return lib.la_step(a["q"], a["k"], a["v"], a["m"], a["si"], a["sik"], a["so"], a["sok"],
+                           a["fm"], a["norm"], a["eps"], a["out"], a["B"], a["H"], a["Dk"], a["Dv"],
+                           a["dt"], None)
+
+    assert step(si=None) == STATE
+    assert step(sik=None) == STATE
+    assert step(norm=0) == STATE              # k parts given without the normalizer
+    assert step(dt=3) == DTYPE
+    assert step(Dk=96, Dv=96) == UNSUPPORTED
+    assert step(out=f(0x10000)) == BAD_ARG    # out aliases q
+    assert step(so=f((1 << 32) + 512)) == BAD_ARG
+
+
+def test_gated_argument_errors(lib):
+    f = fake
+    n = ctypes.c_size_t(0)
+    assert lib.la_gated_workspace_size(2, 64, 6, 4, 128, 128, 1, ctypes.byref(n)) == SHAPE
+    assert lib.la_gated_workspace_size(2, 64, 48, 8, 128, 128, 1, ctypes.byref(n)) == UNSUPPORTED
+    assert lib.la_gated_workspace_size(2, 32768, 32, 8, 128, 128, 1, ctypes.byref(n)) == OK
+    assert n.value > 0
+
+    def g(**kw):
+        a = dict(q=f(1 << 30), k=f(2 << 30), v=f(3 << 30), d=None, past=None, pres=f(4 << 30),
+                 out=f(5 << 30), B=1, T=64, Hq=4, Hkv=2, Dk=64, Dv=64, dt=1, scale=0.0, ws=None,
+                 wsb=0)
+        a.update(kw)
+        return lib.la_gated_forward(a["q"], a["k"], a["v"], a["d"], a["past"], a["pres"], a["out"],
+                                    a["B"], a["T"], a["Hq"], a["Hkv"], a["Dk"], a["Dv"], a["dt"],
+                                    ctypes.c_float(a["scale"]), a["ws"], a["wsb"], None)
+
+    assert g(Hq=3) == SHAPE
+    assert g(Hkv=0) == SHAPE
+    assert g(pres=None) == NULL_ARG
+    assert g(dt=5) == DTYPE
+    assert g(scale=float("inf")) == BAD_ARG
+    assert g(T=4096) == WORKSPACE             # 2 units: the sequence is split
+    assert g(out=f(1 << 30)) == BAD_ARG       # out aliases q

@@ -1,0 +1,292 @@
+"""GPU parity of the HIP library against the fp64 oracle, at small sizes that
+still span several 64-token chunks, a ragged tail, split sequences and the
+single-pass path.  Every call goes through the C ABI (via the ctypes binding).
+
+Tolerance: floored relative error (tests/_util.py) <= 1e-4 for fp32 inputs,
+<= 2e-2 for bf16 inputs with fp32 state."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import kernelized_linear_attention_chunked_amd as la
+from _util import TOL, assert_close, f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+DTYPES = [torch.float32, torch.bfloat16]
+FMS = ["elu_plus_one", "relu"]
+
+
+def _inputs(B, T, H, D, dtype, seed, qk_std=0.5):
+    return synth.qkv(B, T, H, D, dtype, DEV, seed, qk_std, qk_std, 1.0)
+
+
+def _state(B, H, D, seed):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    S = torch.randn((B, H, D, D), generator=g) * 0.5
+    Z = torch.rand((B, H, D), generator=g) * 4 + 0.5
+    return S.to(DEV), Z.to(DEV)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("fm", FMS)
+@pytest.mark.parametrize("norm", [True, False], ids=["norm", "nonorm"])
+def test_causal_small(dtype, D, fm, norm):
+    B, T, H = 2, 200, 3                 # 4 chunks, ragged tail of 8 tokens, split sequence
+    seed = D + 7 * norm + 13 * (fm == "relu") + 31 * (dtype == torch.bfloat16)
+    q, k, v = _inputs(B, T, H, D, dtype, seed)
+    mask = synth.random_mask(B, T, 0.85, DEV, seed)
+    S0, Z0 = _state(B, H, D, seed)
+    state = (S0, Z0 if norm else None)
+    y, (S, Z) = la.la_forward(q, k, v, mask=mask, state=state, causal=True, feature_map=fm,
+                              use_normalizer=norm, eps=1e-6, return_state=True)
+    torch.cuda.synchronize()
+    yo, So, Zo = oracle.causal(f64(q), f64(k), f64(v), f64(mask) > 0, f64(S0),
+                               f64(Z0) if norm else None, fm, norm, 1e-6)
+    tol = TOL[dtype]
+    assert_close(y, yo, tol, "out")
+    assert_close(S, So, tol, "S")
+    if norm:
+        assert_close(Z, Zo, tol, "Z")
+    # masked queries are exactly zero
+    m = mask.cpu().numpy()
+    assert np.all(f64(y)[~m] == 0.0)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_causal_single_pass_path(dtype, D):
+    # 512 (batch, head) units: one pass, state carried across all chunks in a workgroup
+    B, T, H = 4, 130, 128
+    q, k, v = _inputs(B, T, H, D, dtype, 99 + D)
+    y, (S, Z) = la.la_forward(q, k, v, causal=True, return_state=True)
+    torch.cuda.synchronize()
+    idx = [(0, 0), (1, 77), (3, 127), (2, 5)]
+    for b, h in idx:
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        yo, So, Zo = oracle.causal(f64(q[sl]), f64(k[sl]), f64(v[sl]))
+        assert_close(y[sl], yo, TOL[dtype], "out %d,%d" % (b, h))
+        assert_close(S[b:b + 1, h:h + 1], So, TOL[dtype], "S")
+        assert_close(Z[b:b + 1, h:h + 1], Zo, TOL[dtype], "Z")
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 1000])
+def test_causal_lengths(T):
+    B, H, D = 1, 2, 64
+    q, k, v = _inputs(B, T, H, D, torch.bfloat16, T)
+    y, (S, Z) = la.la_forward(q, k, v, causal=True, return_state=True)
+    torch.cuda.synchronize()
+    yo, So, Zo = oracle.causal(f64(q), f64(k), f64(v))
+    assert_close(y, yo, 2e-2, "out")
+    assert_close(S, So, 2e-2, "S")
+    assert_close(Z, Zo, 2e-2, "Z")
+
+
+def test_causal_zero_length_passes_state_through():
+    B, H, D = 2, 3, 32
+    q = torch.empty((B, 0, H, D), device=DEV)
+    S0, Z0 = _state(B, H, D, 5)
+    y, (S, Z) = la.la_forward(q, q, q, state=(S0, Z0), causal=True, return_state=True)
+    torch.cuda.synchronize()
+    assert y.shape == (B, 0, H, D)
+    assert torch.equal(S, S0) and torch.equal(Z, Z0)
+    _, (S, Z) = la.la_forward(q, q, q, causal=True, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S) == 0 and torch.count_nonzero(Z) == 0
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("fm", FMS)
+def test_masked_garbage_does_not_leak(dtype, fm):
+    B, T, H, D = 2, 150, 2, 64
+    q, k, v = _inputs(B, T, H, D, dtype, 21)
+    mask = synth.random_mask(B, T, 0.7, DEV, 21)
+    y1, (S1, Z1) = la.la_forward(q, k, v, mask=mask, feature_map=fm, return_state=True)
+    qn, kn, vn = q.clone(), k.clone(), v.clone()
+    bad = ~mask
+    for t in (qn, kn, vn):
+        t[bad] = float("nan")
+    y2, (S2, Z2) = la.la_forward(qn, kn, vn, mask=mask, feature_map=fm, return_state=True)
+    y3 = la.la_forward(qn, kn, vn, mask=mask, feature_map=fm, causal=False)
+    y4 = la.la_forward(q, k, v, mask=mask, feature_map=fm, causal=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(S1, S2) and torch.equal(Z1, Z2)
+    assert torch.equal(y3, y4)
+    assert torch.all(y2[bad] == 0) and torch.all(y3[bad] == 0)
+
+
+def test_all_false_and_all_true_masks():
+    B, T, H, D = 2, 100, 2, 32
+    q, k, v = _inputs(B, T, H, D, torch.float32, 3)
+    S0, Z0 = _state(B, H, D, 3)
+    y, (S, Z) = la.la_forward(q, k, v, mask=torch.zeros((B, T), dtype=torch.bool, device=DEV),
+                              state=(S0, Z0), return_state=True)
+    ya = la.la_forward(q, k, v, mask=torch.ones((B, T), dtype=torch.bool, device=DEV))
+    yb = la.la_forward(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y) == 0
+    assert torch.equal(S, S0) and torch.equal(Z, Z0)
+    assert torch.equal(ya, yb)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("fm", FMS)
+@pytest.mark.parametrize("norm", [True, False], ids=["norm", "nonorm"])
+def test_noncausal_small(dtype, D, fm, norm):
+    B, T, H = 2, 300, 2
+    seed = 1000 + D + 7 * norm + 13 * (fm == "relu")
+    q, k, v = _inputs(B, T, H, D, dtype, seed, qk_std=1.0)
+    mask, _ = synth.right_padding_mask(B, T, DEV, seed, lo=100, hi=T)
+    y = la.la_forward(q, k, v, mask=mask, causal=False, feature_map=fm, use_normalizer=norm)
+    torch.cuda.synchronize()
+    yo, _, _ = oracle.noncausal(f64(q), f64(k), f64(v), mask.cpu().numpy(), fm, norm, 1e-6)
+    assert_close(y, yo, TOL[dtype], "out")
+    assert torch.all(y[~mask] == 0)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("fm", FMS)
+@pytest.mark.parametrize("norm", [True, False], ids=["norm", "nonorm"])
+@pytest.mark.parametrize("in_place", [True, False], ids=["inplace", "copy"])
+def test_decode_step(dtype, D, fm, norm, in_place):
+    B, H = 3, 5
+    seed = 2000 + D
+    q, k, v = _inputs(B, 1, H, D, dtype, seed)
+    S0, Z0 = _state(B, H, D, seed)
+    mask = torch.tensor([True, False, True], device=DEV)
+    s_kv, s_k = S0.clone(), (Z0.clone() if norm else None)
+    y, (S, Z) = la.la_step(q, k, v, (s_kv, s_k), mask=mask, feature_map=fm, use_normalizer=norm,
+                           in_place=in_place)
+    torch.cuda.synchronize()
+    yo, So, Zo = oracle.causal(f64(q), f64(k), f64(v), mask.cpu().numpy()[:, None], f64(S0),
+                               f64(Z0) if norm else None, fm, norm, 1e-6)
+    assert_close(y, yo[:, 0] if y.dim() == 3 else yo, TOL[dtype], "out")
+    assert_close(S, So, TOL[dtype], "S")
+    if norm:
+        assert_close(Z, Zo, TOL[dtype], "Z")
+    assert torch.all(y[1] == 0)
+    assert torch.equal(S[1], S0[1])
+    if in_place:
+        assert S.data_ptr() == s_kv.data_ptr()
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+def test_chunked_and_step_equal_full(dtype):
+    B, T, H, D = 2, 320, 4, 64
+    q, k, v = _inputs(B, T, H, D, dtype, 77)
+    y_full, (S_full, Z_full) = la.la_forward(q, k, v, return_state=True)
+    state = la.la_initial_state(B, H, D, D)
+    ys = []
+    for a, b in ((0, 64), (64, 100), (100, 101), (101, 256), (256, 300)):
+        y, state = la.la_forward(q[:, a:b], k[:, a:b], v[:, a:b], state=state, return_state=True)
+        ys.append(y)
+    for t in range(300, T):
+        y, state = la.la_step(q[:, t], k[:, t], v[:, t], state)
+        ys.append(y[:, None])
+    torch.cuda.synchronize()
+    y_chunked = torch.cat(ys, 1)
+    yo, So, Zo = oracle.causal(f64(q), f64(k), f64(v))
+    tol = TOL[dtype]
+    assert_close(y_full, yo, tol, "full")
+    assert_close(y_chunked, yo, tol, "chunked+steps")
+    assert_close(state[0], So, tol, "S chunked")
+    assert_close(state[1], Zo, tol, "Z chunked")
+    assert_close(S_full, So, tol, "S full")
+
+
+def test_initial_state_is_zero():
+    kv, k = la.la_initial_state(3, 4, 64, 64)
+    kv2, k2 = la.la_initial_state(3, 4, 64, 64, use_normalizer=False)
+    torch.cuda.synchronize()
+    assert kv.shape == (3, 4, 64, 64) and k.shape == (3, 4, 64) and k2 is None
+    assert torch.count_nonzero(kv) == 0 and torch.count_nonzero(k) == 0
+    assert torch.count_nonzero(kv2) == 0
+
+
+# ------------------------------------------------------------------ gated / GQA
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("gated", [True, False], ids=["gated", "linear"])
+def test_gated_small(dtype, D, G, gated):
+    B, T, Hkv = 2, 190, 2
+    Hq = Hkv * G
+    seed = 3000 + D + G + 50 * gated
+    q = synth.normal((B, T, Hq * D), 1.0, dtype, DEV, seed, "q")
+    k = synth.l2_normalized((B, T, Hkv, D), dtype, DEV, seed, "k").reshape(B, T, Hkv * D)
+    v = synth.normal((B, T, Hkv * D), 1.0, dtype, DEV, seed, "v")
+    g = synth.logsigmoid_decay((B, T, Hkv), dtype, DEV, seed, mean=1.0) if gated else None
+    past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, seed, "past")
+    out, present = la.la_gated_forward(q, k, v, Hq, Hkv, decay=g, past_state=past)
+    torch.cuda.synchronize()
+    oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "gated" if gated else "linear",
+                          past_state=f64(past), decay=None if g is None else f64(g))
+    assert_close(out, oo, TOL[dtype], "out")
+    assert_close(present, po, TOL[dtype], "present_state")
+
+
+def test_gated_present_aliases_past():
+    B, T, Hkv, G, D = 1, 300, 2, 4, 64
+    Hq = Hkv * G
+    q = synth.normal((B, T, Hq * D), 1.0, torch.bfloat16, DEV, 5, "q")
+    k = synth.l2_normalized((B, T, Hkv, D), torch.bfloat16, DEV, 5, "k").reshape(B, T, Hkv * D)
+    v = synth.normal((B, T, Hkv * D), 1.0, torch.bfloat16, DEV, 5, "v")
+    g = synth.logsigmoid_decay((B, T, Hkv), torch.bfloat16, DEV, 5)
+    past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, 5, "past")
+    out_a, pres_a = la.la_gated_forward(q, k, v, Hq, Hkv, decay=g, past_state=past.clone())
+    buf = past.clone()
+    out_b, pres_b = la.la_gated_forward(q, k, v, Hq, Hkv, decay=g, past_state=buf, present_state=buf)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b) and torch.equal(pres_a, pres_b)
+
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "onnx_examples.json")))
+
+
+@pytest.mark.parametrize("ex", [e for e in GOLDEN["examples"]
+                                if e["update_rule"] in ("linear", "gated") and e["dtype"] == "float32"
+                                and (e["update_rule"] == "linear" or
+                                     np.array(e["inputs"]["decay"]).shape[-1] == e["kv_num_heads"])],
+                         ids=lambda e: e["name"])
+def test_operator_page_examples_on_gpu(ex):
+    """The printed worked examples, zero-padded from head size 2 to 32.
+
+    Padding is exact for the linear/gated rules: padded q,k dims add 0 to every
+    dot product and padded v columns give 0 outputs.  The scale is passed
+    explicitly (the default would use the padded head size)."""
+    I = ex["inputs"]
+    Hq, Hkv = ex["q_num_heads"], ex["kv_num_heads"]
+    q, k, v = (np.array(I[n], dtype=np.float32) for n in ("query", "key", "value"))
+    B, T = q.shape[:2]
+    d = q.shape[-1] // Hq
+    P = 32
+
+    def pad(x, H):
+        x = x.reshape(B, T, H, d)
+        y = np.zeros((B, T, H, P), np.float32)
+        y[..., :d] = x
+        return torch.from_numpy(y.reshape(B, T, H * P)).to(DEV)
+
+    past = None
+    if "past_state" in I:
+        p = np.zeros((B, Hkv, P, P), np.float32)
+        p[:, :, :d, :d] = np.array(I["past_state"], np.float32)
+        past = torch.from_numpy(p).to(DEV)
+    decay = torch.tensor(I["decay"], dtype=torch.float32, device=DEV) if "decay" in I else None
+    scale = ex.get("scale", 1.0 / np.sqrt(d))
+    out, present = la.la_gated_forward(pad(q, Hq), pad(k, Hkv), pad(v, Hkv), Hq, Hkv, decay=decay,
+                                       past_state=past, scale=scale)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().reshape(B, T, Hq, P)[..., :d].reshape(B, T, Hq * d)
+    present = present.cpu().numpy()[:, :, :d, :d]
+    np.testing.assert_allclose(out, np.array(ex["output"]), rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(present, np.array(ex["present_state"]), rtol=1e-6, atol=1e-6)
