@@ -185,6 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkArgs a) {
   // LDS, phi(Q) operand registers.  Invalid tokens are selected to zero (a
   // masked token must not reach the state, whatever its values).
   u32x4_t qop[USE_Q ? NQ : 1];
+  bool qok = false;  // validity of this lane's query row in the chunk being computed
   auto stage = [&]() {
     if constexpr (USE_KV) {
 #pragma unroll
@@ -237,6 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkArgs a) {
     }
     if constexpr (USE_Q) {
       const bool ok = qvalid != 0;
+      qok = ok;
 #pragma unroll
       for (int m = 0; m < NQ; ++m) {
         float f[VEC];
@@ -281,18 +283,26 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkArgs a) {
           for (int p = 0; p < 2; ++p) {
             if (2 * p <= w) {
               const int j0 = 32 * p + 4 * lg, j1 = j0 + 16;
-              u32x4_t bv;
-              bv[0] = pack_bf16x2(at[2 * p][0], at[2 * p][1]);
-              bv[1] = pack_bf16x2(at[2 * p][2], at[2 * p][3]);
-              bv[2] = pack_bf16x2(at[2 * p + 1][0], at[2 * p + 1][1]);
-              bv[3] = pack_bf16x2(at[2 * p + 1][2], at[2 * p + 1][3]);
+              // phi >= 0 makes every A entry positive with a large common
+              // part, so one bf16 rounding of A would dominate the error;
+              // A = hi + lo, both bf16, keeps it to ~2^-16 relative.
+              u32x4_t bh, bl;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const f32x4_t& src = at[2 * p + (e >> 1)];
+                const float x0 = src[2 * (e & 1)], x1 = src[2 * (e & 1) + 1];
+                const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
+                bh[e] = h0 | (h1 << 16);
+                bl[e] = pack_bf16x2(x0 - bf16_bits_to_f32(h0), x1 - bf16_bits_to_f32(h1));
+              }
 #pragma unroll
               for (int ct = 0; ct < NVT; ++ct) {
                 const DT* vr = Vt + (16 * ct + lr) * VT_LD;
                 const u32x2_t lo = *(const u32x2_t*)(vr + j0);
                 const u32x2_t hi = *(const u32x2_t*)(vr + j1);
                 const u32x4_t av = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-                O::mma(nacc[ct], av, bv);
+                O::mma(nacc[ct], av, bh);
+                O::mma(nacc[ct], av, bl);
               }
             }
           }
@@ -323,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkArgs a) {
       // epilogue: lane holds query 16w + lr, value dims 16ct + 4lg + (0..3)
       const int tok = c * kChunk + 16 * w + lr;
       if (tok < T) {
-        const bool ok = qvalid != 0;
+        const bool ok = qok;
         float rden = 1.f;
         if constexpr (NORM) rden = 1.f / (nacc[NDT][0] + eps);
         DT* orow = ob + (int64_t)tok * HD + 4 * lg;
