@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of liblinattn on one MI355X.
+
+Default workload (the causal D=128 streaming case): B=256 H=32 Dk=Dv=128 bf16,
+elu+1, normalized; one step = reset the fp32 state, four chained 1024-token
+causal prefill calls (state updated in place), then 512 T=1 decode steps on the
+same state.  Inputs are seeded synthetic tensors already resident in HBM.
+
+Prints ONE JSON line:
+  value            prefill tokens/s (B*4096 tokens / prefill time of a step)
+  prefill          prefill kernel duration, HBM GB/s, MFMA utilisation
+  decode           decode kernel duration and state-streaming HBM GB/s
+  roofline         the dominant kernel by time in a step (the decode kernel),
+                   algorithmic bytes per launch / average launch duration
+  roofline_prefill the same for the prefill kernel
+  cpu_baseline     the fp64 oracle on a bounded sample of the same prefill
+Kernel durations come from HIP events recorded around every launch on the
+stream the library launches on (torch's current stream).
+
+--workload selects one of the other workloads for an extra measurement line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+MFMA_16x16x32_FLOPS = 2 * 16 * 16 * 32
+
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "kernelized_linear_attention_chunked_amd", "csrc")
+
+
+def _src_sha(name):
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel, src, launches_per_record=1):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None
+    when the summary is missing or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, kernel + "_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha") != _src_sha(src):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def prefill_mfma_per_chunk(D=128, norm=True):
+    """MFMA instructions one workgroup issues per 64-token chunk in the causal
+    prefill kernel (bf16, v_mfma_f32_16x16x32_bf16), from its tiling:
+    A^T tiles (w+1 per wave) x D/32 steps; intra V^T A^T: ceil((w+1)/2) tile pairs
+    x (D/16 + norm) value tiles x 2 (hi/lo split of A); inter S^T phiQ^T:
+    4 waves x (D/16 + norm) x D/32; state update: (D/16)(D/16 + norm) tiles x 2."""
+    nvt = D // 16 + (1 if norm else 0)
+    nq = D // 32
+    a_t = sum(w + 1 for w in range(4)) * nq
+    intra = sum((w + 2) // 2 for w in range(4)) * nvt * 2
+    inter = 4 * nvt * nq
+    upd = (D // 16) * nvt * 2
+    return a_t + intra + inter + upd
+
+
+def _elapsed_ms(pairs):
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+def cpu_baseline_streaming(d, target_s, log):
+    """fp64 oracle (as it stands) on a bounded sample of the prefill: the first
+    n (batch, head) units, 4096 tokens each; n sized for ~target_s seconds."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    H = d.H
+    q, k, v = d.qc, d.kc, d.vc
+
+    def units(nb):
+        # nb whole batch rows (all H heads), all 4096 tokens, as float64 on the host
+        cat = lambda parts: torch.cat([p[:nb] for p in parts], 1).to("cpu", torch.float64).numpy()
+        return cat(q), cat(k), cat(v)
+
+    qs, ks, vs = units(1)
+    t0 = time.perf_counter()
+    oracle.causal(qs, ks, vs)
+    t1 = time.perf_counter() - t0
+    nb = int(max(1, min(d.B, round(target_s / max(t1, 1e-3)))))
+    log("cpu_baseline: 1 batch row (%d units) took %.2f s; timing %d rows" % (H, t1, nb))
+    if nb > 1:
+        qs, ks, vs = units(nb)
+        t0 = time.perf_counter()
+        oracle.causal(qs, ks, vs)
+        t1 = time.perf_counter() - t0
+    tokens = nb * H * d.T
+    return {"value": tokens / t1, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "seconds": round(t1, 3),
+            "sample": "%d of %d (batch, head) units x %d prefill tokens (batch rows 0..%d), "
+                      "fp64 per-token recurrence" % (nb * H, d.B * H, d.T, nb - 1)}
+
+
+def bench_streaming(args, log):
+    import torch
+
+    from kernelized_linear_attention_chunked_amd import workloads
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    d = workloads.StreamingD128(dev)
+    B, H, D, T, Td, C = d.B, d.H, d.D, d.T, d.Td, d.chunk
+    n_chunks = T // C
+    log("streaming_d128: B=%d H=%d D=%d, %d x %d prefill + %d decode" % (B, H, D, n_chunks, C, Td))
+    for _ in range(args.warmup):
+        d.step()
+    torch.cuda.synchronize()
+
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    steps = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        s0, mid, s1 = E(), E(), E()
+        pf = [(E(), E()) for _ in range(n_chunks)]
+        dc = [(E(), E()) for _ in range(Td)]
+        s0.record()
+        d.reset_state()
+        for i in range(n_chunks):
+            pf[i][0].record()
+            d.prefill_call(i)
+            pf[i][1].record()
+        mid.record()
+        for t in range(Td):
+            dc[t][0].record()
+            d.decode_call(t)
+            dc[t][1].record()
+        s1.record()
+        steps.append((s0, mid, s1, pf, dc))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    prefill_ms = [s0.elapsed_time(mid) for s0, mid, _, _, _ in steps]
+    decode_ms = [mid.elapsed_time(s1) for _, mid, s1, _, _ in steps]
+    pf_k = [x for st in steps for x in _elapsed_ms(st[3])]
+    dc_k = [x for st in steps for x in _elapsed_ms(st[4])]
+    mean = lambda xs: sum(xs) / len(xs)
+    prefill_step_ms, pf_kernel_ms, dc_kernel_ms = mean(prefill_ms), mean(pf_k), mean(dc_k)
+
+    # algorithmic bytes / flops per launch
+    units = B * H
+    pf_bytes = units * C * D * 2 * 4 + units * (D * D + D) * 4 * 2      # q,k,v,out + state in/out
+    dc_bytes = units * (D * D + D) * 4 * 2 + units * D * 2 * 4          # state in/out + q,k,v,out
+    pf_exec_flops = units * (C // 64) * prefill_mfma_per_chunk(D) * MFMA_16x16x32_FLOPS
+    pf_alg_flops = units * C * (2 * 64 * (D + D) + 4 * D * D)           # dense 64x64 tiles + 4 Dk Dv
+    pf_gbs = pf_bytes / (pf_kernel_ms * 1e-3) / 1e9
+    dc_gbs = dc_bytes / (dc_kernel_ms * 1e-3) / 1e9
+    prefill_tps = B * T / (prefill_step_ms * 1e-3)
+
+    dc_traffic = _traffic("decode_kernel", "la_decode.hip")
+    pf_traffic = _traffic("causal_prefill_kernel", "la_chunk.hip")
+    rec = {
+        "metric": "prefill tokens/s + MFMA util (causal, D=128); decode state HBM GB/s",
+        "value": prefill_tps,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "streaming causal elu+1 normalized linear attention: "
+                               "4 x 1024-token prefill calls + 512 T=1 decode steps, fp32 state",
+                   "B": B, "H": H, "Dk": D, "Dv": D, "prefill_tokens": T, "prefill_call_tokens": C,
+                   "decode_steps": Td, "feature_map": "elu_plus_one", "eps": 1e-6},
+        "prefill": {"tokens_per_s": prefill_tps, "ms_per_step": prefill_step_ms,
+                    "kernel_ms": pf_kernel_ms, "hbm_GBps": pf_gbs, "hbm_frac": pf_gbs / HBM_PEAK_GBS,
+                    "mfma_util_executed": pf_exec_flops / (pf_kernel_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+                    "mfma_util_algorithmic": pf_alg_flops / (pf_kernel_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+                    "executed_mfma_TFLOPs": pf_exec_flops / (pf_kernel_ms * 1e-3) / 1e12},
+        "decode": {"kernel_us": dc_kernel_ms * 1e3, "ms_per_step": mean(decode_ms),
+                   "state_GBps": units * (D * D + D) * 8 / (dc_kernel_ms * 1e-3) / 1e9,
+                   "hbm_GBps": dc_gbs, "hbm_frac": dc_gbs / HBM_PEAK_GBS,
+                   "tokens_per_s": B * Td / (mean(decode_ms) * 1e-3)},
+        "roofline": {"kernel": "decode_kernel<bf16,128,elu+1,norm>", "bound": "hbm",
+                     "achieved": dc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dc_gbs / HBM_PEAK_GBS, "traffic": dc_traffic,
+                     "algorithmic_bytes_per_launch": dc_bytes},
+        "roofline_prefill": {"kernel": "chunk_kernel<bf16,128,elu+1,norm,causal>", "bound": "hbm",
+                             "achieved": pf_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": pf_gbs / HBM_PEAK_GBS, "traffic": pf_traffic,
+                             "algorithmic_bytes_per_launch": pf_bytes},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_streaming(d, args.cpu_baseline_seconds, log)
+    return rec
+
+
+def bench_other(args, log):
+    """One extra line for a non-default workload: tokens/s and algorithmic GB/s per step."""
+    import torch
+
+    from kernelized_linear_attention_chunked_amd import workloads
+
+    torch.cuda.set_device(0)
+    d = workloads.DRIVERS[args.workload]("cuda:0")
+    for _ in range(args.warmup):
+        d.step()
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        a, b = E(), E()
+        a.record()
+        d.step()
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sum(_elapsed_ms(ev)) / len(ev)
+    if args.workload == "gated_gqa_d128":
+        D, Tt = d.D, d.B * d.T
+        nbytes = Tt * (d.Hq * D * 2 * 2 + d.Hkv * D * 2 * 2 + d.Hkv * 2) + d.B * d.Hkv * D * D * 4
+    elif args.workload == "noncausal_relu_d128":
+        D, Tt = d.D, d.B * d.T
+        nbytes = Tt * d.H * D * 2 * 4 + Tt
+    else:
+        D, Tt = d.D, d.B * d.T
+        nbytes = Tt * d.H * D * 2 * 4 + d.B * d.H * (D * D + D) * 4
+    return {"metric": "tokens/s", "value": d.prefill_tokens / (ms * 1e-3), "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": wall * 1e3 / args.steps, "step_kernel_ms": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic", "config": {"workload": args.workload},
+            "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="streaming_d128",
+                    choices=["streaming_d128", "causal_bf16_d64", "noncausal_relu_d128",
+                             "gated_gqa_d128"])
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.exit("bench.py measures one GPU only (--gpus 1): this library has no multi-GPU path; "
+                 "the per-GPU kernel is the same at any GPU count")
+    log = lambda m: print("[bench] " + m, file=sys.stderr, flush=True)
+    if args.workload == "streaming_d128":
+        rec = bench_streaming(args, log)
+    else:
+        rec = bench_other(args, log)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -144,13 +144,19 @@ def la_gated_workspace_size(B, T, Hq, Hkv, Dk, Dv, dtype=torch.bfloat16) -> int:
 
 
 def la_initial_state(batch_size, num_heads, key_dim, value_dim=None, use_normalizer=True,
-                     device="cuda"):
-    """Zero state (kv (B,H,Dk,Dv), k (B,H,Dk) or None), float32, on ``device``."""
+                     device="cuda", out=None):
+    """Zero state (kv (B,H,Dk,Dv), k (B,H,Dk) or None), float32, on ``device``.
+
+    ``out``: existing (kv, k) buffers to zero instead of allocating new ones."""
     value_dim = key_dim if value_dim is None else value_dim
     lib = load_library()
-    kv = torch.empty((batch_size, num_heads, key_dim, value_dim), dtype=torch.float32, device=device)
-    k = (torch.empty((batch_size, num_heads, key_dim), dtype=torch.float32, device=device)
-         if use_normalizer else None)
+    if out is not None:
+        kv, k = out
+    else:
+        kv = torch.empty((batch_size, num_heads, key_dim, value_dim), dtype=torch.float32,
+                         device=device)
+        k = (torch.empty((batch_size, num_heads, key_dim), dtype=torch.float32, device=device)
+             if use_normalizer else None)
     _check(lib.la_initial_state(_ptr(kv), _ptr(k), batch_size, num_heads, key_dim, value_dim,
                                 _stream(kv.device)), "la_initial_state")
     return (kv, k) if use_normalizer else (kv, None)

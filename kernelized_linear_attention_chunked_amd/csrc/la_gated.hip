@@ -251,25 +251,44 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
             for (int q = 0; q < 4; ++q) at[jt][q] *= fac[jt][q];
           }
         }
+        // inter-chunk term first, with the exact query; lane's column is its own
+        // query i, so exp(b_i) is applied per lane to the accumulators.
         f32x4_t nacc[NDT];
 #pragma unroll
         for (int ct = 0; ct < NDT; ++ct) nacc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+#pragma unroll
+          for (int ct = 0; ct < NDT; ++ct) {
+            const u32x4_t av = ld16(Sb + (16 * ct + lr) * SB_LD + KB * m + VEC * lg);
+            O::mma(nacc[ct], av, qop[hh * NQ + m]);
+          }
+        }
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct) nacc[ct] *= ebi;
         if constexpr (ESZ == 2) {
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             if (2 * p <= wr) {
               const int j0 = 32 * p + 4 * lg, j1 = j0 + 16;
-              u32x4_t bv;
-              bv[0] = pack_bf16x2(at[2 * p][0], at[2 * p][1]);
-              bv[1] = pack_bf16x2(at[2 * p][2], at[2 * p][3]);
-              bv[2] = pack_bf16x2(at[2 * p + 1][0], at[2 * p + 1][1]);
-              bv[3] = pack_bf16x2(at[2 * p + 1][2], at[2 * p + 1][3]);
+              // the terms of A V cancel, so A carries its bf16 rounding residual too
+              u32x4_t bh, bl;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const f32x4_t& src = at[2 * p + (e >> 1)];
+                const float x0 = src[2 * (e & 1)], x1 = src[2 * (e & 1) + 1];
+                const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
+                bh[e] = h0 | (h1 << 16);
+                bl[e] = pack_bf16x2(x0 - bf16_bits_to_f32(h0), x1 - bf16_bits_to_f32(h1));
+              }
 #pragma unroll
               for (int ct = 0; ct < NDT; ++ct) {
                 const DT* vr = Vt + (16 * ct + lr) * VT_LD;
                 const u32x2_t lo = *(const u32x2_t*)(vr + j0);
                 const u32x2_t hi = *(const u32x2_t*)(vr + j1);
-                O::mma(nacc[ct], u32x4_t{lo[0], lo[1], hi[0], hi[1]}, bv);
+                const u32x4_t av = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+                O::mma(nacc[ct], av, bh);
+                O::mma(nacc[ct], av, bl);
               }
             }
           }
@@ -285,20 +304,6 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
                   nacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], at[jt][q], nacc[ct], 0, 0, 0);
               }
             }
-          }
-        }
-        // inter-chunk term with the query scaled by exp(b_i)
-#pragma unroll
-        for (int m = 0; m < NQ; ++m) {
-          float f[VEC];
-          O::unpack(qop[hh * NQ + m], f);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) f[e] *= ebi;
-          const u32x4_t qd = O::pack(f);
-#pragma unroll
-          for (int ct = 0; ct < NDT; ++ct) {
-            const u32x4_t av = ld16(Sb + (16 * ct + lr) * SB_LD + KB * m + VEC * lg);
-            O::mma(nacc[ct], av, qd);
           }
         }
         if (tok < T) {
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
       for (int m = 0; m < NKS; ++m)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) kw[m][e] = __expf(btot - __shfl(bcs, KB * m + VEC * lg + e));
-      u32x4_t kop[NKS];
+      u32x4_t kop[NKS], kol[NKS];
       int cur_rt = -1;
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
@@ -341,12 +346,23 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
                   f[e] = ((const float*)kc)[e * KN_LD] * kw[m][e];
               }
               kop[m] = O::pack(f);
+              if constexpr (ESZ == 2) {
+                // decayed keys = hi + lo in bf16
+                float r[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                  const uint32_t hb = (kop[m][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                  r[e] = f[e] - bf16_bits_to_f32(hb);
+                }
+                kol[m] = O::pack(r);
+              }
             }
           }
 #pragma unroll
           for (int m = 0; m < NKS; ++m) {
             const u32x4_t bv = ld16(Vt + (16 * ct + lr) * VT_LD + KB * m + VEC * lg);
             O::mma(sacc[i], kop[m], bv);
+            if constexpr (ESZ == 2) O::mma(sacc[i], kol[m], bv);
           }
         }
       }

@@ -66,8 +66,15 @@ def _load():
                                                      ctypes.c_int, ctypes.c_double, p, p]
             for f in (lib.oracle_causal, lib.oracle_noncausal, lib.oracle_la_op):
                 f.restype = ctypes.c_int
+            lib.oracle_max_threads.argtypes = []
+            lib.oracle_max_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_max_threads())
 
 
 def _f64(x):

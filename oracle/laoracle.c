@@ -18,6 +18,7 @@
  * which is byte-identical to the 4-D layout above.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -215,3 +216,6 @@ int oracle_la_op(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int6
   }
   return 0;
 }
+
+/* Number of OpenMP threads a parallel loop above will use (for reporting). */
+int oracle_max_threads(void) { return omp_get_max_threads(); }
