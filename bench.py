@@ -259,7 +259,20 @@ def main():
                              "gated_gqa_d128"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (5 times) and "
+                         "exit: the reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
+    if args.copy_calibration_mib:
+        import torch
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         sys.exit("bench.py measures one GPU only (--gpus 1): this library has no multi-GPU path; "
