@@ -22,13 +22,15 @@
 // N^T holds  sum_j A_ij + phiQ_i . Z_prev  (the denominator before eps), and
 // the extra state tile accumulates Z exactly like S.
 //
-// Work split inside a 256-thread workgroup (one (batch, head) unit and one
-// segment of chunks):
-//   wave w owns query rows [16w, 16w+16) of the chunk (A^T tiles jt <= w,
-//   N^T, outputs) and a contiguous quarter of the 16x16 tiles of S.
-// LDS holds phiK in natural [token][dk] layout, V transposed [dv][token] and a
-// copy of S transposed [dv][dk] in the operand dtype.  The next chunk's q/k/v
-// are loaded into registers while the current chunk is being computed.
+// Work split inside a workgroup (one (batch, head) unit and one segment of
+// chunks; 4 wavefronts, or 8 at head size 128):
+//   wave w owns query rows [16qr, 16qr+16) of the chunk, qr = w % 4 (A^T tiles
+//   jt <= qr), and for them the output tiles of one value half (w / 4) plus the
+//   normaliser tile; and a contiguous 1/NW of the 16x16 tiles of S.
+// LDS holds phiK and phiQ in natural [token][d] layout, V transposed
+// [dv][token] (16-byte blocks swizzled per row) and a copy of S transposed
+// [dv][dk] in the operand dtype.  The next chunk's q/k/v are loaded into
+// registers while the current chunk is being computed.
 #include "la_device.hpp"
 #include "la_launch.hpp"
 
@@ -36,37 +38,68 @@ namespace la {
 
 enum ChunkMode { kCausal = 0, kState = 1, kApply = 2 };
 
+// Wavefronts per workgroup: 8 at head size 128 (the state and the output
+// accumulators would not fit one 4-wave workgroup's registers without
+// serialising every LDS read), 4 below.
+template <int D>
+struct ChunkWaves {
+  static constexpr int NW = D >= 128 ? 8 : 4;
+};
+
+// Swizzle of the V^T tile: 16-byte block b of row r is stored at block
+// b ^ g(r).  With g(r) = (r ^ r>>3) & 7 both the transposed writes (rows 8cb+e,
+// cb = 0..15) and the 16-byte operand reads (rows 16t + lr) spread evenly over
+// the LDS banks.
+__device__ __forceinline__ int vt_swz(int r) { return (r ^ (r >> 3)) & 7; }
+
 template <typename DT, int D, int FM, bool NORM, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(64 * ChunkWaves<D>::NW, ChunkWaves<D>::NW == 8 ? 1 : 2)
+void chunk_kernel(ChunkArgs a) {
   using O = Op<DT>;
+  constexpr int NW = ChunkWaves<D>::NW;            // wavefronts
+  constexpr int NTH = 64 * NW;                     // threads
+  constexpr int NH = NW / 4;                       // value halves (waves per query block)
   constexpr int VEC = O::VEC, KB = O::KB, ESZ = O::ESZ;
   constexpr int NDT = D / 16;                      // 16-wide tiles along dk or dv
   constexpr int NVT = NDT + (NORM ? 1 : 0);        // dv tiles plus the normaliser tile
+  constexpr int NDH = NDT / NH;                    // dv tiles of one value half
+  constexpr int NVW = NDH + (NORM ? 1 : 0);        // a wave's output tiles (+ normaliser)
   constexpr int CB = D / VEC;                      // 16-byte blocks per row
-  constexpr int NTOK = kChunk * CB / kThreads;     // tokens per thread in k/v loads
+  // tokens per loading thread (bf16 V^T writes pack token pairs: at least 2)
+  constexpr int LOADERS = (kChunk * CB / NTH >= 2 || ESZ == 4) ? NTH : kChunk * CB / 2;
+  constexpr int NTOK = kChunk * CB / LOADERS;
   constexpr int NQ = D / KB;                       // operand vectors per q row per lane
   constexpr int NKS = kChunk / KB;                 // vector-steps over the chunk's tokens
-  constexpr int PADE = 16 / ESZ;                   // 16 bytes of padding per LDS row
-  constexpr int KN_LD = D + PADE;
-  constexpr int VT_LD = kChunk + PADE;
+  constexpr int PADE = 16 / ESZ;                   // 16 bytes of padding per row
+  constexpr int KN_LD = D + PADE;                  // phi(K), phi(Q) rows
+  constexpr int VT_LD = kChunk;                    // V^T rows (swizzled, unpadded)
   constexpr int SB_LD = D + PADE;
   constexpr bool USE_KV = MODE != kApply;
   constexpr bool USE_Q = MODE != kState;
   constexpr bool USE_SB = MODE != kState;
+  // phi(Q) is staged through LDS (each element evaluated once, coalesced
+  // loads), except for fp32 at head size 128 where it would not fit: there each
+  // wave loads its own query rows straight into operand registers.
+  constexpr bool QS_STAGE = !(ESZ == 4 && D >= 128);
   constexpr int KN_BYTES = USE_KV ? kChunk * KN_LD * ESZ : 0;
+  constexpr int QS_BYTES = (USE_Q && QS_STAGE) ? kChunk * KN_LD * ESZ : 0;
   constexpr int VT_BYTES = USE_KV ? NVT * 16 * VT_LD * ESZ : 0;
   constexpr int SB_BYTES = USE_SB ? NVT * 16 * SB_LD * ESZ : 0;
   constexpr int NS = NDT * NVT;                    // 16x16 tiles of the (extended) state
-  constexpr int TPW = (NS + 3) / 4;                // state tiles per wave
-  static_assert(NTOK >= 1 && NQ >= 1, "unsupported head size");
+  constexpr int TPW = (NS + NW - 1) / NW;          // state tiles per wave
+  static_assert(NTOK >= 1 && NQ >= 1 && NDH * NH == NDT, "unsupported head size");
+  static_assert(ESZ == 4 || NTOK % 2 == 0, "bf16 V^T writes pack token pairs");
 
-  __shared__ __align__(16) unsigned char smem[KN_BYTES + VT_BYTES + SB_BYTES + 16];
+  __shared__ __align__(16) unsigned char smem[KN_BYTES + QS_BYTES + VT_BYTES + SB_BYTES + 16];
   DT* Kn = (DT*)smem;
-  DT* Vt = (DT*)(smem + KN_BYTES);
-  DT* Sb = (DT*)(smem + KN_BYTES + VT_BYTES);
+  DT* Qs = (DT*)(smem + KN_BYTES);
+  DT* Vt = (DT*)(smem + KN_BYTES + QS_BYTES);
+  DT* Sb = (DT*)(smem + KN_BYTES + QS_BYTES + VT_BYTES);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qr = w & 3;   // query rows [16qr, 16qr+16) of the chunk
+  const int hv = w >> 2;  // value half: dv tiles [hv*NDH, (hv+1)*NDH) (+ normaliser tile)
   const int l = tid & 63, lr = l & 15, lg = l >> 4;
   const int bid = blockIdx.x;
   const int u = bid / a.seg_count;
@@ -84,6 +117,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkArgs a) {
   DT* ob = (DT*)a.out + unit_off;
   const uint8_t* mb = a.mask ? a.mask + (int64_t)b * T : nullptr;
   const float eps = a.eps;
+  // global dv tile of the wave's i-th output tile
+  auto vtile = [&](int i) { return (NORM && i == NDH) ? NDT : hv * NDH + i; };
+  // element offset of 16-byte block `blk` of V^T row r
+  auto vt_at = [&](int r, int blk) { return r * VT_LD + ((blk ^ vt_swz(r)) * VEC); };
 
   // ---- running state: wave w owns tiles tau = w*TPW + i of the (NDT x NVT) grid
   f32x4_t sacc[TPW];
@@ -134,91 +171,103 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkArgs a) {
   if constexpr (USE_SB) write_sb();
   if constexpr (USE_KV && NORM) {
     // rows D..D+15 of V^T are ones: they turn A V into the row sums of A
-    for (int idx = tid; idx < 16 * kChunk; idx += kThreads) {
-      const int r = D + idx / kChunk, c = idx % kChunk;
+    for (int idx = tid; idx < 16 * VT_LD; idx += NTH) {
       if constexpr (ESZ == 2)
-        ((uint16_t*)Vt)[r * VT_LD + c] = 0x3f80;  // bf16 1.0
+        ((uint16_t*)Vt)[D * VT_LD + idx] = 0x3f80;  // bf16 1.0
       else
-        ((float*)Vt)[r * VT_LD + c] = 1.f;
+        ((float*)Vt)[D * VT_LD + idx] = 1.f;
     }
   }
 
-  // ---- prefetch registers
+  // ---- prefetch registers: thread (cb, tg) loads the 16-byte block cb of
+  // NTOK consecutive tokens tg*NTOK + n, for q, k and v alike (full rows per
+  // 16 threads: coalesced).
   const int cb = tid % CB, tg = tid / CB;
-  u32x4_t pk[USE_KV ? NTOK : 1], pv[USE_KV ? NTOK : 1], pq[USE_Q ? NQ : 1];
-  uint32_t kvalid = 0, qvalid = 0;
+  const bool loader = LOADERS == NTH || tid < LOADERS;
+  u32x4_t pk[USE_KV ? NTOK : 1], pv[USE_KV ? NTOK : 1];
+  u32x4_t pq[USE_Q ? (QS_STAGE ? NTOK : NQ) : 1];
+  u32x4_t qreg[(USE_Q && !QS_STAGE) ? NQ : 1];
+  uint32_t valid = 0;   // bit n: token tg*NTOK + n exists and is not masked
+  bool qrow_ok = false; // (unstaged q) this lane's own query row exists and is not masked
   auto prefetch = [&](int c) {
     const int tb = c * kChunk;
-    if constexpr (USE_KV) {
-      kvalid = 0;
+    valid = 0;
+    if constexpr (USE_Q && !QS_STAGE) {
+      const int tok = tb + 16 * qr + lr;
+      qrow_ok = tok < T && (mb ? (mb[tok] != 0) : true);
 #pragma unroll
-      for (int n = 0; n < NTOK; ++n) {
-        const int tok = tb + tg * NTOK + n;
-        if (tok < T) {
-          const int64_t off = (int64_t)tok * HD + cb * VEC;
+      for (int m = 0; m < NQ; ++m)
+        pq[m] = tok < T ? ld16(qb + (int64_t)tok * HD + KB * m + VEC * lg) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if (!loader) return;
+#pragma unroll
+    for (int n = 0; n < NTOK; ++n) {
+      const int tok = tb + tg * NTOK + n;
+      if (tok < T) {
+        const int64_t off = (int64_t)tok * HD + cb * VEC;
+        if constexpr (USE_KV) {
           pk[n] = ld16(kb + off);
           pv[n] = ld16(vb + off);
-          const uint32_t ok = mb ? (mb[tok] != 0) : 1u;
-          kvalid |= ok << n;
-        } else {
+        }
+        if constexpr (USE_Q && QS_STAGE) pq[n] = ld16(qb + off);
+        const uint32_t ok = mb ? (mb[tok] != 0) : 1u;
+        valid |= ok << n;
+      } else {
+        if constexpr (USE_KV) {
           pk[n] = u32x4_t{0u, 0u, 0u, 0u};
           pv[n] = u32x4_t{0u, 0u, 0u, 0u};
         }
-      }
-    }
-    if constexpr (USE_Q) {
-      const int tok = tb + 16 * w + lr;
-      qvalid = 0;
-      if (tok < T) {
-        const int64_t off = (int64_t)tok * HD + VEC * lg;
-#pragma unroll
-        for (int m = 0; m < NQ; ++m) pq[m] = ld16(qb + off + KB * m);
-        qvalid = mb ? (mb[tok] != 0) : 1u;
-      } else {
-#pragma unroll
-        for (int m = 0; m < NQ; ++m) pq[m] = u32x4_t{0u, 0u, 0u, 0u};
+        if constexpr (USE_Q && QS_STAGE) pq[n] = u32x4_t{0u, 0u, 0u, 0u};
       }
     }
   };
 
-  // ---- stage: prefetched registers -> phi(K) [token][dk] and V^T [dv][token] in
-  // LDS, phi(Q) operand registers.  Invalid tokens are selected to zero (a
-  // masked token must not reach the state, whatever its values).
-  u32x4_t qop[USE_Q ? NQ : 1];
-  bool qok = false;  // validity of this lane's query row in the chunk being computed
+  // phi of one 16-byte block, then zero if the token is invalid (selected on
+  // the packed words: a masked token must not reach anything, whatever its values)
+  auto phi_vec = [&](const u32x4_t& raw, bool ok) {
+    float f[VEC];
+    O::unpack(raw, f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) f[e] = phi<FM>(f[e], eps);
+    u32x4_t r = O::pack(f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = ok ? r[e] : 0u;
+    return r;
+  };
+
+  // ---- stage: phi(K), phi(Q) -> [token][d] in LDS, V -> V^T [dv][token] (swizzled)
   auto stage = [&]() {
-    if constexpr (USE_KV) {
+    if constexpr (USE_Q && !QS_STAGE) {
 #pragma unroll
-      for (int n = 0; n < NTOK; ++n) {
-        const bool ok = (kvalid >> n) & 1u;
-        float f[VEC];
-        O::unpack(pk[n], f);
+      for (int m = 0; m < NQ; ++m) qreg[m] = phi_vec(pq[m], qrow_ok);
+    }
+    if (!loader) return;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) f[e] = ok ? phi<FM>(f[e], eps) : 0.f;
-        st16(Kn + (tg * NTOK + n) * KN_LD + cb * VEC, O::pack(f));
+    for (int n = 0; n < NTOK; ++n) {
+      const bool ok = (valid >> n) & 1u;
+      const int t = tg * NTOK + n;
+      if constexpr (USE_KV) {
+        st16(Kn + t * KN_LD + cb * VEC, phi_vec(pk[n], ok));
         if (!ok) pv[n] = u32x4_t{0u, 0u, 0u, 0u};
       }
-      // transposed V: element e of every loaded vector goes to row cb*VEC+e,
-      // the NTOK consecutive tokens of this thread side by side.
+      if constexpr (USE_Q && QS_STAGE) st16(Qs + t * KN_LD + cb * VEC, phi_vec(pq[n], ok));
+    }
+    if constexpr (USE_KV) {
+      // element e of every loaded vector goes to V^T row cb*VEC + e; the
+      // thread's NTOK consecutive tokens sit side by side in one block
+      const int t0 = tg * NTOK;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        DT* p = Vt + (cb * VEC + e) * VT_LD + tg * NTOK;
+        const int r = cb * VEC + e;
+        DT* p = Vt + vt_at(r, t0 / VEC) + (t0 % VEC);
         if constexpr (ESZ == 2) {
-          uint32_t hw[NTOK];
 #pragma unroll
-          for (int n = 0; n < NTOK; ++n) hw[n] = (pv[n][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          if constexpr (NTOK == 1) {
-            *(uint16_t*)p = (uint16_t)hw[0];
-          } else if constexpr (NTOK == 2) {
-            *(uint32_t*)p = hw[0] | (hw[1] << 16);
-          } else {
-#pragma unroll
-            for (int n = 0; n < NTOK; n += 4) {
-              u32x2_t v2;
-              v2[0] = hw[n] | (hw[n + 1] << 16);
-              v2[1] = hw[n + 2] | (hw[n + 3] << 16);
-              *(u32x2_t*)(p + n) = v2;
-            }
+          for (int n = 0; n < NTOK; n += 2) {
+            const uint32_t w0 = pv[n][e >> 1], w1 = pv[n + 1][e >> 1];
+            // low halves of both words for even e, high halves for odd e
+            const uint32_t word = (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
+                                          : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+            *(uint32_t*)(p + n) = word;
           }
         } else {
           float fv[NTOK];
@@ -236,114 +285,101 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkArgs a) {
         }
       }
     }
-    if constexpr (USE_Q) {
-      const bool ok = qvalid != 0;
-      qok = ok;
-#pragma unroll
-      for (int m = 0; m < NQ; ++m) {
-        float f[VEC];
-        O::unpack(pq[m], f);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) f[e] = ok ? phi<FM>(f[e], eps) : 0.f;
-        qop[m] = O::pack(f);
-      }
-    }
   };
 
   // ---- per-chunk compute
   auto compute = [&](int c) {
     if constexpr (USE_Q) {
-      f32x4_t nacc[NVT];
+      u32x4_t qop[NQ];
 #pragma unroll
-      for (int ct = 0; ct < NVT; ++ct) nacc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if constexpr (MODE == kCausal) {
-        // A^T tile jt: rows = keys 16jt + 4lg + q, column = own query 16w + lr.
-        // A operand: phiK rows from LDS; B operand: phiQ registers (contraction over dk).
-        f32x4_t at[4];
+      for (int m = 0; m < NQ; ++m)
+        qop[m] = QS_STAGE ? ld16(Qs + (16 * qr + lr) * KN_LD + KB * m + VEC * lg) : qreg[m];
+      f32x4_t nacc[NVW];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          at[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          if (jt <= w) {
-#pragma unroll
-            for (int m = 0; m < NQ; ++m) {
-              const u32x4_t av = ld16(Kn + (16 * jt + lr) * KN_LD + KB * m + VEC * lg);
-              O::mma(at[jt], av, qop[m]);
-            }
-            if (jt == w) {  // causal mask inside the diagonal tile: key <= query
-#pragma unroll
-              for (int q = 0; q < 4; ++q) at[jt][q] = (4 * lg + q <= lr) ? at[jt][q] : 0.f;
-            }
-          }
-        }
-        // N^T += V^T A^T: contraction over keys.  The B operand is A^T straight
-        // from the accumulators: lane group lg holds keys 16jt + 4lg + q, so the
-        // A operand (V^T rows) reads the same keys.
-        if constexpr (ESZ == 2) {
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            if (2 * p <= w) {
-              const int j0 = 32 * p + 4 * lg, j1 = j0 + 16;
-              // phi >= 0 makes every A entry positive with a large common
-              // part, so one bf16 rounding of A would dominate the error;
-              // A = hi + lo, both bf16, keeps it to ~2^-16 relative.
-              u32x4_t bh, bl;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const f32x4_t& src = at[2 * p + (e >> 1)];
-                const float x0 = src[2 * (e & 1)], x1 = src[2 * (e & 1) + 1];
-                const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
-                bh[e] = h0 | (h1 << 16);
-                bl[e] = pack_bf16x2(x0 - bf16_bits_to_f32(h0), x1 - bf16_bits_to_f32(h1));
-              }
-#pragma unroll
-              for (int ct = 0; ct < NVT; ++ct) {
-                const DT* vr = Vt + (16 * ct + lr) * VT_LD;
-                const u32x2_t lo = *(const u32x2_t*)(vr + j0);
-                const u32x2_t hi = *(const u32x2_t*)(vr + j1);
-                const u32x4_t av = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-                O::mma(nacc[ct], av, bh);
-                O::mma(nacc[ct], av, bl);
-              }
-            }
-          }
-        } else {
-#pragma unroll
-          for (int jt = 0; jt < 4; ++jt) {
-            if (jt <= w) {
-#pragma unroll
-              for (int ct = 0; ct < NVT; ++ct) {
-                const f32x4_t av = *(const f32x4_t*)(Vt + (16 * ct + lr) * VT_LD + 16 * jt + 4 * lg);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                  nacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], at[jt][q], nacc[ct], 0, 0, 0);
-              }
-            }
-          }
-        }
-      }
+      for (int i = 0; i < NVW; ++i) nacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       // N^T += S^T phiQ^T (state before this chunk): contraction over dk.
 #pragma unroll
-      for (int ct = 0; ct < NVT; ++ct) {
+      for (int m = 0; m < NQ; ++m) {
+        u32x4_t av[NVW];
 #pragma unroll
-        for (int m = 0; m < NQ; ++m) {
-          const u32x4_t av = ld16(Sb + (16 * ct + lr) * SB_LD + KB * m + VEC * lg);
-          O::mma(nacc[ct], av, qop[m]);
+        for (int i = 0; i < NVW; ++i) av[i] = ld16(Sb + (16 * vtile(i) + lr) * SB_LD + KB * m + VEC * lg);
+#pragma unroll
+        for (int i = 0; i < NVW; ++i) O::mma(nacc[i], av[i], qop[m]);
+      }
+      if constexpr (MODE == kCausal) {
+        // A^T tiles come in pairs covering keys [32p, 32p+32).  Row r of tile
+        // (p, odd) is key 32p + 8(r/4) + 4odd + r%4, so that the accumulator
+        // lane (query 16qr + lr, lane group lg) ends up holding the 8
+        // consecutive keys 32p + 8lg + (0..7) over the pair: exactly one
+        // 16-byte read of V^T per value tile in the contraction below.
+        constexpr int NP = (ESZ == 2) ? 2 : 4;  // bf16: key pairs of 32; fp32: single tiles of 16
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const bool need = (ESZ == 2) ? (32 * p <= 16 * qr + 15) : (p <= qr);
+          if (!need) continue;
+          f32x4_t at[2];
+#pragma unroll
+          for (int odd = 0; odd < (ESZ == 2 ? 2 : 1); ++odd) {
+            const int krow = (ESZ == 2) ? 32 * p + 8 * (lr >> 2) + 4 * odd + (lr & 3) : 16 * p + lr;
+            u32x4_t kv[NQ];
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) kv[m] = ld16(Kn + krow * KN_LD + KB * m + VEC * lg);
+            at[odd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) O::mma(at[odd], kv[m], qop[m]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int key = (ESZ == 2) ? 32 * p + 8 * lg + 4 * odd + q : 16 * p + 4 * lg + q;
+              at[odd][q] = (key <= 16 * qr + lr) ? at[odd][q] : 0.f;  // causal: key <= query
+            }
+          }
+          if constexpr (ESZ == 2) {
+            u32x4_t av[NVW];
+#pragma unroll
+            for (int i = 0; i < NVW; ++i) {
+              const int r = 16 * vtile(i) + lr;
+              av[i] = ld16(Vt + vt_at(r, 4 * p + lg));
+            }
+            // phi >= 0 makes every A entry positive with a large common
+            // part, so one bf16 rounding of A would dominate the error;
+            // A = hi + lo, both bf16, keeps it to ~2^-16 relative.
+            u32x4_t bh, bl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x0 = at[e >> 1][2 * (e & 1)], x1 = at[e >> 1][2 * (e & 1) + 1];
+              const uint32_t hw = pack_bf16x2(x0, x1);
+              bh[e] = hw;
+              bl[e] = pack_bf16x2(x0 - __uint_as_float(hw << 16), x1 - __uint_as_float(hw & 0xffff0000u));
+            }
+#pragma unroll
+            for (int i = 0; i < NVW; ++i) {
+              O::mma(nacc[i], av[i], bh);
+              O::mma(nacc[i], av[i], bl);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < NVW; ++i) {
+              const int r = 16 * vtile(i) + lr;
+              const f32x4_t av = *(const f32x4_t*)(Vt + vt_at(r, 4 * p + lg));
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                nacc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], at[0][q], nacc[i], 0, 0, 0);
+            }
+          }
         }
       }
-      // epilogue: lane holds query 16w + lr, value dims 16ct + 4lg + (0..3)
-      const int tok = c * kChunk + 16 * w + lr;
+      // epilogue: lane holds query 16qr + lr, value dims 16*vtile(i) + 4lg + (0..3)
+      const int tok = c * kChunk + 16 * qr + lr;
       if (tok < T) {
-        const bool ok = qok;
+        const bool ok = mb ? (mb[tok] != 0) : true;
         float rden = 1.f;
-        if constexpr (NORM) rden = 1.f / (nacc[NDT][0] + eps);
+        if constexpr (NORM) rden = ok ? 1.f / (nacc[NDH][0] + eps) : 0.f;
+        else rden = ok ? 1.f : 0.f;
         DT* orow = ob + (int64_t)tok * HD + 4 * lg;
 #pragma unroll
-        for (int ct = 0; ct < NDT; ++ct) {
-          float y0 = nacc[ct][0] * rden, y1 = nacc[ct][1] * rden;
-          float y2 = nacc[ct][2] * rden, y3 = nacc[ct][3] * rden;
-          if (!ok) y0 = y1 = y2 = y3 = 0.f;
-          store4(orow + 16 * ct, y0, y1, y2, y3);
-        }
+        for (int i = 0; i < NDH; ++i)
+          store4(orow + 16 * (hv * NDH + i), nacc[i][0] * rden, nacc[i][1] * rden,
+                 nacc[i][2] * rden, nacc[i][3] * rden);
       }
     }
     if constexpr (USE_KV) {
@@ -374,11 +410,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkArgs a) {
               }
             }
           }
+          u32x4_t bv[NKS];
 #pragma unroll
-          for (int m = 0; m < NKS; ++m) {
-            const u32x4_t bv = ld16(Vt + (16 * ct + lr) * VT_LD + KB * m + VEC * lg);
-            O::mma(sacc[i], kop[m], bv);
-          }
+          for (int m = 0; m < NKS; ++m) bv[m] = ld16(Vt + vt_at(16 * ct + lr, (KB / VEC) * m + lg));
+#pragma unroll
+          for (int m = 0; m < NKS; ++m) O::mma(sacc[i], kop[m], bv[m]);
         }
       }
     }
@@ -390,10 +426,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkArgs a) {
     __syncthreads();
     if (c + 1 < c1) prefetch(c + 1);
     compute(c);
-    if constexpr (MODE != kApply) {
-      __syncthreads();
-      if constexpr (MODE == kCausal) write_sb();
-    }
+    __syncthreads();
+    if constexpr (MODE == kCausal) write_sb();
   }
 
   // ---- state out
@@ -487,7 +521,8 @@ __global__ __launch_bounds__(kThreads) void seg_sum_kernel(float* ws_s, float* w
 
 template <typename DT, int D, int FM, bool NORM, int MODE>
 static hipError_t launch_one(const ChunkArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((chunk_kernel<DT, D, FM, NORM, MODE>), dim3(grid), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((chunk_kernel<DT, D, FM, NORM, MODE>), dim3(grid), dim3(64 * ChunkWaves<D>::NW), 0,
+                     st, a);
   return hipGetLastError();
 }
 
