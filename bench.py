@@ -14,8 +14,9 @@ Prints ONE JSON line:
                    algorithmic bytes per launch / average launch duration
   roofline_prefill the same for the prefill kernel
   cpu_baseline     the fp64 oracle on a bounded sample of the same prefill
-Kernel durations come from HIP events recorded around every launch on the
-stream the library launches on (torch's current stream).
+Kernel durations come from HIP events recorded on the stream the library
+launches on (torch's current stream) at the boundaries of each phase of every
+timed step: mean launch duration = phase time / launches in the phase.
 
 --workload selects one of the other workloads for an extra measurement line.
 """
@@ -127,34 +128,30 @@ def bench_streaming(args, log):
     torch.cuda.synchronize()
 
     E = lambda: torch.cuda.Event(enable_timing=True)
+    # events only at phase boundaries: a marker between every launch would add
+    # its own few microseconds to each short decode launch
     steps = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        s0, mid, s1 = E(), E(), E()
-        pf = [(E(), E()) for _ in range(n_chunks)]
-        dc = [(E(), E()) for _ in range(Td)]
+        s0, r1, mid, s1 = E(), E(), E(), E()
         s0.record()
         d.reset_state()
+        r1.record()
         for i in range(n_chunks):
-            pf[i][0].record()
             d.prefill_call(i)
-            pf[i][1].record()
         mid.record()
         for t in range(Td):
-            dc[t][0].record()
             d.decode_call(t)
-            dc[t][1].record()
         s1.record()
-        steps.append((s0, mid, s1, pf, dc))
+        steps.append((s0, r1, mid, s1))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    prefill_ms = [s0.elapsed_time(mid) for s0, mid, _, _, _ in steps]
-    decode_ms = [mid.elapsed_time(s1) for _, mid, s1, _, _ in steps]
-    pf_k = [x for st in steps for x in _elapsed_ms(st[3])]
-    dc_k = [x for st in steps for x in _elapsed_ms(st[4])]
     mean = lambda xs: sum(xs) / len(xs)
-    prefill_step_ms, pf_kernel_ms, dc_kernel_ms = mean(prefill_ms), mean(pf_k), mean(dc_k)
+    prefill_step_ms = mean([s0.elapsed_time(mid) for s0, _, mid, _ in steps])
+    pf_kernel_ms = mean([r1.elapsed_time(mid) for _, r1, mid, _ in steps]) / n_chunks
+    decode_ms = [mid.elapsed_time(s1) for _, _, mid, s1 in steps]
+    dc_kernel_ms = mean(decode_ms) / Td
 
     # algorithmic bytes / flops per launch
     units = B * H

@@ -403,6 +403,7 @@ LA_EXPORT la_status la_step(const void* q, const void* k, const void* v, const u
   a.z_out = state_out_k;
   a.out = out;
   a.H = (int32_t)H;
+  a.units = (int32_t)U;
   a.eps = eps;
   hipError_t e = la::launch_decode(dtype == LA_DT_BF16, (int)D, feature_map, norm, a, (int)U,
                                    (hipStream_t)stream);

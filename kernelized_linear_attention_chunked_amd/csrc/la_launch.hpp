@@ -52,6 +52,7 @@ struct DecodeArgs {
   float* z_out;
   void* out;
   int32_t H;
+  int32_t units;  // B*H
   float eps;
 };
 hipError_t launch_decode(int bf16, int D, int fm, int norm, const DecodeArgs& a, int units,
