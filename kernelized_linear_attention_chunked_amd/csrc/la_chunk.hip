@@ -121,6 +121,14 @@ void chunk_kernel(ChunkArgs a) {
   auto vtile = [&](int i) { return (NORM && i == NDH) ? NDT : hv * NDH + i; };
   // element offset of 16-byte block `blk` of V^T row r
   auto vt_at = [&](int r, int blk) { return r * VT_LD + ((blk ^ vt_swz(r)) * VEC); };
+  // element offset of element `col` of phi(K) row t: 16-byte blocks swizzled by
+  // row bits 3 and 4 so that the permuted-row operand reads (rows t and t+8 in
+  // one pass) and the column-wise reads of the state update (rows 8 apart)
+  // spread over the banks
+  auto kn_at = [&](int t, int col) {
+    const int sw = (4 * ((t >> 3) & 1) + 2 * ((t >> 4) & 1)) & (CB - 1);
+    return t * KN_LD + (((col / VEC) ^ sw) * VEC) + (col % VEC);
+  };
 
   // ---- running state: wave w owns tiles tau = w*TPW + i of the (NDT x NVT) grid
   f32x4_t sacc[TPW];
@@ -200,6 +208,20 @@ void chunk_kernel(ChunkArgs a) {
         pq[m] = tok < T ? ld16(qb + (int64_t)tok * HD + KB * m + VEC * lg) : u32x4_t{0u, 0u, 0u, 0u};
     }
     if (!loader) return;
+    if (!mb && tb + kChunk <= T) {
+      // whole chunk, no mask: every token valid, no per-token guards
+      valid = (1u << NTOK) - 1u;
+#pragma unroll
+      for (int n = 0; n < NTOK; ++n) {
+        const int64_t off = (int64_t)(tb + tg * NTOK + n) * HD + cb * VEC;
+        if constexpr (USE_KV) {
+          pk[n] = ld16(kb + off);
+          pv[n] = ld16(vb + off);
+        }
+        if constexpr (USE_Q && QS_STAGE) pq[n] = ld16(qb + off);
+      }
+      return;
+    }
 #pragma unroll
     for (int n = 0; n < NTOK; ++n) {
       const int tok = tb + tg * NTOK + n;
@@ -247,7 +269,7 @@ void chunk_kernel(ChunkArgs a) {
       const bool ok = (valid >> n) & 1u;
       const int t = tg * NTOK + n;
       if constexpr (USE_KV) {
-        st16(Kn + t * KN_LD + cb * VEC, phi_vec(pk[n], ok));
+        st16(Kn + kn_at(t, cb * VEC), phi_vec(pk[n], ok));
         if (!ok) pv[n] = u32x4_t{0u, 0u, 0u, 0u};
       }
       if constexpr (USE_Q && QS_STAGE) st16(Qs + t * KN_LD + cb * VEC, phi_vec(pq[n], ok));
@@ -323,7 +345,7 @@ void chunk_kernel(ChunkArgs a) {
             const int krow = (ESZ == 2) ? 32 * p + 8 * (lr >> 2) + 4 * odd + (lr & 3) : 16 * p + lr;
             u32x4_t kv[NQ];
 #pragma unroll
-            for (int m = 0; m < NQ; ++m) kv[m] = ld16(Kn + krow * KN_LD + KB * m + VEC * lg);
+            for (int m = 0; m < NQ; ++m) kv[m] = ld16(Kn + kn_at(krow, KB * m + VEC * lg));
             at[odd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < NQ; ++m) O::mma(at[odd], kv[m], qop[m]);
@@ -387,27 +409,36 @@ void chunk_kernel(ChunkArgs a) {
       // column-wise from the natural layout; B operand: V^T rows (dv).  Lane
       // group lg carries tokens KB*m + VEC*lg + e.
       u32x4_t kop[NKS];
+      auto load_kop = [&](int rt) {
+#pragma unroll
+        for (int m = 0; m < NKS; ++m) {
+          const int t0 = KB * m + VEC * lg, col = 16 * rt + lr;
+          if constexpr (ESZ == 2) {
+            const uint16_t* k16 = (const uint16_t*)Kn;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              kop[m][e] = (uint32_t)k16[kn_at(t0 + 2 * e, col)] |
+                          ((uint32_t)k16[kn_at(t0 + 2 * e + 1, col)] << 16);
+          } else {
+            const float* k32 = (const float*)Kn;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kop[m][e] = __float_as_uint(k32[kn_at(t0 + e, col)]);
+          }
+        }
+      };
+      // when every wave owns whole rows of state tiles the operand is loaded once
+      constexpr bool ONE_ROW = (TPW == NVT) && (NS % NW == 0);
       int cur_rt = -1;
+      if constexpr (ONE_ROW) load_kop(w);
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
         const int tau = w * TPW + i;
         if (tau < NS) {
           const int rt = tau / NVT, ct = tau % NVT;
-          if (rt != cur_rt) {
-            cur_rt = rt;
-#pragma unroll
-            for (int m = 0; m < NKS; ++m) {
-              const DT* kc = Kn + (KB * m + VEC * lg) * KN_LD + 16 * rt + lr;
-              if constexpr (ESZ == 2) {
-                const uint16_t* k16 = (const uint16_t*)kc;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  kop[m][e] = (uint32_t)k16[(2 * e) * KN_LD] | ((uint32_t)k16[(2 * e + 1) * KN_LD] << 16);
-              } else {
-                const float* k32 = (const float*)kc;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) kop[m][e] = __float_as_uint(k32[e * KN_LD]);
-              }
+          if constexpr (!ONE_ROW) {
+            if (rt != cur_rt) {
+              cur_rt = rt;
+              load_kop(rt);
             }
           }
           u32x4_t bv[NKS];
