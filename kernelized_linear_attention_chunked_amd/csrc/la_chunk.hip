@@ -130,18 +130,36 @@ void chunk_kernel(ChunkArgs a) {
     return t * KN_LD + (((col / VEC) ^ sw) * VEC) + (col % VEC);
   };
 
-  // ---- running state: wave w owns tiles tau = w*TPW + i of the (NDT x NVT) grid
-  f32x4_t sacc[TPW];
+  // ---- running state.  With FUSE, wave (qr, hv) owns state rows
+  // [R*qr, R*qr+R) across its own value tiles (the normaliser column belongs to
+  // half 0), so the V^T operands it loads for the intra-chunk product serve the
+  // state update too; otherwise wave w owns tiles w*TPW .. w*TPW+TPW-1.
+  constexpr bool FUSE = (NDT % 4 == 0) && (MODE != kApply);
+  constexpr int R = FUSE ? NDT / 4 : 1;
+  constexpr int NST = FUSE ? R * NVW : TPW;
+  auto stile = [&](int k, int& rt, int& ct) -> bool {
+    if constexpr (FUSE) {
+      const int j = k / NVW, i = k % NVW;
+      rt = R * qr + j;
+      ct = vtile(i);
+      return hv == 0 || i < NDH;
+    } else {
+      const int tau = w * TPW + k;
+      rt = tau / NVT;
+      ct = tau % NVT;
+      return tau < NS;
+    }
+  };
+  f32x4_t sacc[NST];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) sacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < NST; ++k) sacc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if constexpr (MODE != kState) {
     const float* sin = a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr;
     const float* zin = a.z_in ? a.z_in + u * a.z_in_u + s * a.z_in_s : nullptr;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int tau = w * TPW + i;
-      if (tau < NS) {
-        const int rt = tau / NVT, ct = tau % NVT;
+    for (int k = 0; k < NST; ++k) {
+      int rt, ct;
+      if (stile(k, rt, ct)) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int dk = 16 * rt + 4 * lg + q;
@@ -151,7 +169,7 @@ void chunk_kernel(ChunkArgs a) {
           } else {
             if (zin) val = zin[dk];
           }
-          sacc[i][q] = val;
+          sacc[k][q] = val;
         }
       }
     }
@@ -160,18 +178,17 @@ void chunk_kernel(ChunkArgs a) {
   // S (and Z in the extra rows) -> LDS, transposed [dv][dk], operand dtype.
   auto write_sb = [&]() {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int tau = w * TPW + i;
-      if (tau < NS) {
-        const int rt = tau / NVT, ct = tau % NVT;
+    for (int k = 0; k < NST; ++k) {
+      int rt, ct;
+      if (stile(k, rt, ct)) {
         DT* p = Sb + (16 * ct + lr) * SB_LD + 16 * rt + 4 * lg;
         if constexpr (ESZ == 2) {
           u32x2_t v2;
-          v2[0] = pack_bf16x2(sacc[i][0], sacc[i][1]);
-          v2[1] = pack_bf16x2(sacc[i][2], sacc[i][3]);
+          v2[0] = pack_bf16x2(sacc[k][0], sacc[k][1]);
+          v2[1] = pack_bf16x2(sacc[k][2], sacc[k][3]);
           *(u32x2_t*)p = v2;
         } else {
-          *(f32x4_t*)p = sacc[i];
+          *(f32x4_t*)p = sacc[k];
         }
       }
     }
@@ -310,6 +327,24 @@ void chunk_kernel(ChunkArgs a) {
   };
 
   // ---- per-chunk compute
+  // phiK^T operand of the state update for state row rt, token block m (lane
+  // group lg carries tokens KB*m + VEC*lg + e), read column-wise from phi(K)
+  auto load_kop = [&](u32x4_t& dst, int rt, int m) {
+    const int t0 = KB * m + VEC * lg, col = 16 * rt + lr;
+    if constexpr (ESZ == 2) {
+      const uint16_t* k16 = (const uint16_t*)Kn;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dst[e] = (uint32_t)k16[kn_at(t0 + 2 * e, col)] | ((uint32_t)k16[kn_at(t0 + 2 * e + 1, col)] << 16);
+    } else {
+      const float* k32 = (const float*)Kn;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = __float_as_uint(k32[kn_at(t0 + e, col)]);
+    }
+  };
+  // V^T operand (16-byte block `blk` of row 16*ct + lr)
+  auto vt_op = [&](int ct, int blk) { return ld16(Vt + vt_at(16 * ct + lr, blk)); };
+
   auto compute = [&](int c) {
     if constexpr (USE_Q) {
       u32x4_t qop[NQ];
@@ -328,17 +363,20 @@ void chunk_kernel(ChunkArgs a) {
 #pragma unroll
         for (int i = 0; i < NVW; ++i) O::mma(nacc[i], av[i], qop[m]);
       }
+      // A^T, per key block p (= token block of the update): bf16 pairs of tiles
+      // over keys [32p, 32p+32), row r of tile (p, odd) being key
+      // 32p + 8(r/4) + 4odd + r%4 so that lane group lg holds keys
+      // 32p + 8lg + (0..7), one 16-byte V^T read per value tile; fp32 single
+      // tiles over keys [16p, 16p+16).  bf16 A is kept as hi + lo: phi >= 0
+      // gives it a large common part, and one rounding would dominate the error.
+      constexpr int NP = NKS;
+      u32x4_t bh[NP], bl[NP];
+      f32x4_t at32[ESZ == 4 ? NP : 1];
+      auto need = [&](int p) { return (ESZ == 2) ? (32 * p <= 16 * qr + 15) : (p <= qr); };
       if constexpr (MODE == kCausal) {
-        // A^T tiles come in pairs covering keys [32p, 32p+32).  Row r of tile
-        // (p, odd) is key 32p + 8(r/4) + 4odd + r%4, so that the accumulator
-        // lane (query 16qr + lr, lane group lg) ends up holding the 8
-        // consecutive keys 32p + 8lg + (0..7) over the pair: exactly one
-        // 16-byte read of V^T per value tile in the contraction below.
-        constexpr int NP = (ESZ == 2) ? 2 : 4;  // bf16: key pairs of 32; fp32: single tiles of 16
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-          const bool need = (ESZ == 2) ? (32 * p <= 16 * qr + 15) : (p <= qr);
-          if (!need) continue;
+          if (!need(p)) continue;
           f32x4_t at[2];
 #pragma unroll
           for (int odd = 0; odd < (ESZ == 2 ? 2 : 1); ++odd) {
@@ -356,38 +394,54 @@ void chunk_kernel(ChunkArgs a) {
             }
           }
           if constexpr (ESZ == 2) {
-            u32x4_t av[NVW];
-#pragma unroll
-            for (int i = 0; i < NVW; ++i) {
-              const int r = 16 * vtile(i) + lr;
-              av[i] = ld16(Vt + vt_at(r, 4 * p + lg));
-            }
-            // phi >= 0 makes every A entry positive with a large common
-            // part, so one bf16 rounding of A would dominate the error;
-            // A = hi + lo, both bf16, keeps it to ~2^-16 relative.
-            u32x4_t bh, bl;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float x0 = at[e >> 1][2 * (e & 1)], x1 = at[e >> 1][2 * (e & 1) + 1];
               const uint32_t hw = pack_bf16x2(x0, x1);
-              bh[e] = hw;
-              bl[e] = pack_bf16x2(x0 - __uint_as_float(hw << 16), x1 - __uint_as_float(hw & 0xffff0000u));
-            }
-#pragma unroll
-            for (int i = 0; i < NVW; ++i) {
-              O::mma(nacc[i], av[i], bh);
-              O::mma(nacc[i], av[i], bl);
+              bh[p][e] = hw;
+              bl[p][e] = pack_bf16x2(x0 - __uint_as_float(hw << 16), x1 - __uint_as_float(hw & 0xffff0000u));
             }
           } else {
+            at32[p] = at[0];
+          }
+        }
+      }
+      // state-update operands of the wave's rows
+      u32x4_t kop[FUSE ? R : 1][NKS];
+      if constexpr (FUSE) {
 #pragma unroll
-            for (int i = 0; i < NVW; ++i) {
-              const int r = 16 * vtile(i) + lr;
-              const f32x4_t av = *(const f32x4_t*)(Vt + vt_at(r, 4 * p + lg));
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+          for (int m = 0; m < NKS; ++m) load_kop(kop[j][m], R * qr + j, m);
+      }
+      // per key/token block: V^T operands -> intra-chunk product and state update
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const bool intra = (MODE == kCausal) && need(p);
+        if (!intra && !FUSE) continue;
+        u32x4_t av[NVW];
+#pragma unroll
+        for (int i = 0; i < NVW; ++i) av[i] = vt_op(vtile(i), (KB / VEC) * p + lg);
+        if (intra) {
+#pragma unroll
+          for (int i = 0; i < NVW; ++i) {
+            if constexpr (ESZ == 2) {
+              O::mma(nacc[i], av[i], bh[p]);
+              O::mma(nacc[i], av[i], bl[p]);
+            } else {
 #pragma unroll
               for (int q = 0; q < 4; ++q)
-                nacc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], at[0][q], nacc[i], 0, 0, 0);
+                nacc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av[i][q]), at32[p][q],
+                                                               nacc[i], 0, 0, 0);
             }
           }
+        }
+        if constexpr (FUSE) {
+#pragma unroll
+          for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int i = 0; i < NVW; ++i)
+              if (hv == 0 || i < NDH) O::mma(sacc[j * NVW + i], kop[j][p], av[i]);
         }
       }
       // epilogue: lane holds query 16qr + lr, value dims 16*vtile(i) + 4lg + (0..3)
@@ -404,48 +458,24 @@ void chunk_kernel(ChunkArgs a) {
                  nacc[i][2] * rden, nacc[i][3] * rden);
       }
     }
-    if constexpr (USE_KV) {
-      // S += phiK^T V over the chunk's tokens.  A operand: phiK^T rows (dk) read
-      // column-wise from the natural layout; B operand: V^T rows (dv).  Lane
-      // group lg carries tokens KB*m + VEC*lg + e.
+    if constexpr (USE_KV && !(FUSE && USE_Q)) {
+      // S += phiK^T V on its own (state-only mode, or no fused assignment)
       u32x4_t kop[NKS];
-      auto load_kop = [&](int rt) {
-#pragma unroll
-        for (int m = 0; m < NKS; ++m) {
-          const int t0 = KB * m + VEC * lg, col = 16 * rt + lr;
-          if constexpr (ESZ == 2) {
-            const uint16_t* k16 = (const uint16_t*)Kn;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              kop[m][e] = (uint32_t)k16[kn_at(t0 + 2 * e, col)] |
-                          ((uint32_t)k16[kn_at(t0 + 2 * e + 1, col)] << 16);
-          } else {
-            const float* k32 = (const float*)Kn;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kop[m][e] = __float_as_uint(k32[kn_at(t0 + e, col)]);
-          }
-        }
-      };
-      // when every wave owns whole rows of state tiles the operand is loaded once
-      constexpr bool ONE_ROW = (TPW == NVT) && (NS % NW == 0);
       int cur_rt = -1;
-      if constexpr (ONE_ROW) load_kop(w);
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int tau = w * TPW + i;
-        if (tau < NS) {
-          const int rt = tau / NVT, ct = tau % NVT;
-          if constexpr (!ONE_ROW) {
-            if (rt != cur_rt) {
-              cur_rt = rt;
-              load_kop(rt);
-            }
+      for (int k = 0; k < NST; ++k) {
+        int rt, ct;
+        if (stile(k, rt, ct)) {
+          if (rt != cur_rt) {
+            cur_rt = rt;
+#pragma unroll
+            for (int m = 0; m < NKS; ++m) load_kop(kop[m], rt, m);
           }
           u32x4_t bv[NKS];
 #pragma unroll
-          for (int m = 0; m < NKS; ++m) bv[m] = ld16(Vt + vt_at(16 * ct + lr, (KB / VEC) * m + lg));
+          for (int m = 0; m < NKS; ++m) bv[m] = vt_op(ct, (KB / VEC) * m + lg);
 #pragma unroll
-          for (int m = 0; m < NKS; ++m) O::mma(sacc[i], kop[m], bv[m]);
+          for (int m = 0; m < NKS; ++m) O::mma(sacc[k], kop[m], bv[m]);
         }
       }
     }
@@ -475,17 +505,16 @@ void chunk_kernel(ChunkArgs a) {
   }
   if constexpr (MODE != kApply) {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int tau = w * TPW + i;
-      if (tau < NS) {
-        const int rt = tau / NVT, ct = tau % NVT;
+    for (int k = 0; k < NST; ++k) {
+      int rt, ct;
+      if (stile(k, rt, ct)) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int dk = 16 * rt + 4 * lg + q;
           if (ct < NDT) {
-            if (sout) sout[dk * D + 16 * ct + lr] = sacc[i][q];
+            if (sout) sout[dk * D + 16 * ct + lr] = sacc[k][q];
           } else {
-            if (zout && lr == 0) zout[dk] = sacc[i][q];
+            if (zout && lr == 0) zout[dk] = sacc[k][q];
           }
         }
       }
