@@ -31,6 +31,8 @@
 // [dv][token] (16-byte blocks swizzled per row) and a copy of S transposed
 // [dv][dk] in the operand dtype.  The next chunk's q/k/v are loaded into
 // registers while the current chunk is being computed.
+#include <type_traits>
+
 #include "la_device.hpp"
 #include "la_launch.hpp"
 
@@ -263,33 +265,37 @@ void chunk_kernel(ChunkArgs a) {
 
   // phi of one 16-byte block, then zero if the token is invalid (selected on
   // the packed words: a masked token must not reach anything, whatever its values)
-  auto phi_vec = [&](const u32x4_t& raw, bool ok) {
+  auto phi_vec = [&](const u32x4_t& raw, bool ok, auto full) {
     float f[VEC];
     O::unpack(raw, f);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) f[e] = phi<FM>(f[e], eps);
     u32x4_t r = O::pack(f);
+    if constexpr (!decltype(full)::value) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = ok ? r[e] : 0u;
+      for (int e = 0; e < 4; ++e) r[e] = ok ? r[e] : 0u;
+    }
     return r;
   };
 
-  // ---- stage: phi(K), phi(Q) -> [token][d] in LDS, V -> V^T [dv][token] (swizzled)
-  auto stage = [&]() {
+  // ---- stage: phi(K), phi(Q) -> [token][d] in LDS, V -> V^T [dv][token] (swizzled).
+  // `full` (a std::bool_constant) marks a whole unmasked chunk: no validity selects.
+  auto stage = [&](auto full) {
+    constexpr bool FULL = decltype(full)::value;
     if constexpr (USE_Q && !QS_STAGE) {
 #pragma unroll
-      for (int m = 0; m < NQ; ++m) qreg[m] = phi_vec(pq[m], qrow_ok);
+      for (int m = 0; m < NQ; ++m) qreg[m] = phi_vec(pq[m], qrow_ok, full);
     }
     if (!loader) return;
 #pragma unroll
     for (int n = 0; n < NTOK; ++n) {
-      const bool ok = (valid >> n) & 1u;
+      const bool ok = FULL || ((valid >> n) & 1u);
       const int t = tg * NTOK + n;
       if constexpr (USE_KV) {
-        st16(Kn + kn_at(t, cb * VEC), phi_vec(pk[n], ok));
+        st16(Kn + kn_at(t, cb * VEC), phi_vec(pk[n], ok, full));
         if (!ok) pv[n] = u32x4_t{0u, 0u, 0u, 0u};
       }
-      if constexpr (USE_Q && QS_STAGE) st16(Qs + t * KN_LD + cb * VEC, phi_vec(pq[n], ok));
+      if constexpr (USE_Q && QS_STAGE) st16(Qs + t * KN_LD + cb * VEC, phi_vec(pq[n], ok, full));
     }
     if constexpr (USE_KV) {
       // element e of every loaded vector goes to V^T row cb*VEC + e; the
@@ -483,7 +489,11 @@ void chunk_kernel(ChunkArgs a) {
 
   if (c0 < c1) prefetch(c0);
   for (int c = c0; c < c1; ++c) {
-    stage();
+    // wave-uniform: every token of the chunk exists and there is no mask
+    if (!mb && (c + 1) * kChunk <= T)
+      stage(std::true_type{});
+    else
+      stage(std::false_type{});
     __syncthreads();
     if (c + 1 < c1) prefetch(c + 1);
     compute(c);

@@ -47,10 +47,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // phi of the Keras proposal, section "Feature maps": elu(x)+1 with slope 1, or
 // relu(x)+eps.  Evaluated in fp32 (the accumulator type).
+// elu(x)+1 is taken as max(x + 1, exp(-|x|)): exp(x) >= 1 + x for every x, and
+// for x > 0 exp(-x) < 1 < 1 + x, so the maximum is exp(x) for x <= 0 and x + 1
+// otherwise, in four instructions (the -|.| is an input modifier of v_exp_f32)
+// instead of a compare and a select on top.
 template <int FM>
 __device__ __forceinline__ float phi(float x, float eps) {
   if constexpr (FM == kEluPlusOne) {
-    return x > 0.f ? x + 1.f : __expf(x);
+    return fmaxf(x + 1.f, __builtin_amdgcn_exp2f(-fabsf(x * 1.44269504088896340736f)));
   } else {
     return fmaxf(x, 0.f) + eps;
   }
