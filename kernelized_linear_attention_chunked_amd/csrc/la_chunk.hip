@@ -48,14 +48,29 @@ struct ChunkWaves {
   static constexpr int NW = D >= 128 ? 8 : 4;
 };
 
-// Swizzle of the V^T tile: 16-byte block b of row r is stored at block
-// b ^ g(r).  With g(r) = (r ^ r>>3) & 7 both the transposed writes (rows 8cb+e,
-// cb = 0..15) and the 16-byte operand reads (rows 16t + lr) spread evenly over
-// the LDS banks.
-__device__ __forceinline__ int vt_swz(int r) { return (r ^ (r >> 3)) & 7; }
+// LDS layouts.  gfx950 LDS has 64 banks of 4 bytes; a 16-byte read serves the
+// 8-lane blocks {0,3}, {1,2}, {4,7}, {5,6} of a wavefront together (16 lanes,
+// 256 bytes per cycle), while writes and narrower reads go 32 banks wide.  All
+// tiles are stored as rows of 16-byte blocks with the block index XORed by a
+// function of the row, chosen against that model so that every operand read is
+// conflict-free and the transposed writes stay at two-way:
+//   V^T  [dv][token]: g(r) = ((r >> 1) & 7) ^ ((r >> 4) & 3)
+//   phiK [token][dk]: 4*bit3(t) ^ 5*bit4(t)
+//   phiQ, S^T       : bit3(r)
+__device__ __forceinline__ int vt_swz(int r) { return ((r >> 1) & 7) ^ ((r >> 4) & 3); }
+
+// The second bound is the minimum number of waves per SIMD.  At 8 waves the
+// apply mode and the bf16 state mode ask for 4 (two workgroups per CU, at most
+// 128 registers); the causal mode and the fp32 state mode need more registers.
+template <typename DT, int D, int MODE>
+struct ChunkOccupancy {
+  static constexpr int NW = ChunkWaves<D>::NW;
+  static constexpr int value =
+      NW == 8 ? ((MODE == kApply || (MODE == kState && sizeof(DT) == 2)) ? 4 : 1) : 2;
+};
 
 template <typename DT, int D, int FM, bool NORM, int MODE>
-__global__ __launch_bounds__(64 * ChunkWaves<D>::NW, ChunkWaves<D>::NW == 8 ? 1 : 2)
+__global__ __launch_bounds__(64 * ChunkWaves<D>::NW, (ChunkOccupancy<DT, D, MODE>::value))
 void chunk_kernel(ChunkArgs a) {
   using O = Op<DT>;
   constexpr int NW = ChunkWaves<D>::NW;            // wavefronts
@@ -91,6 +106,7 @@ void chunk_kernel(ChunkArgs a) {
   constexpr int TPW = (NS + NW - 1) / NW;          // state tiles per wave
   static_assert(NTOK >= 1 && NQ >= 1 && NDH * NH == NDT, "unsupported head size");
   static_assert(ESZ == 4 || NTOK % 2 == 0, "bf16 V^T writes pack token pairs");
+  static_assert(SB_LD == KN_LD, "phi(Q) and S^T share one row layout");
 
   __shared__ __align__(16) unsigned char smem[KN_BYTES + QS_BYTES + VT_BYTES + SB_BYTES + 16];
   DT* Kn = (DT*)smem;
@@ -128,8 +144,12 @@ void chunk_kernel(ChunkArgs a) {
   // one pass) and the column-wise reads of the state update (rows 8 apart)
   // spread over the banks
   auto kn_at = [&](int t, int col) {
-    const int sw = (4 * ((t >> 3) & 1) + 2 * ((t >> 4) & 1)) & (CB - 1);
+    const int sw = ((4 * ((t >> 3) & 1)) ^ (5 * ((t >> 4) & 1))) & (CB - 1);
     return t * KN_LD + (((col / VEC) ^ sw) * VEC) + (col % VEC);
+  };
+  // element offset of element `col` of row r of phi(Q) or S^T
+  auto sq_at = [&](int r, int col) {
+    return r * SB_LD + (((col / VEC) ^ ((r >> 3) & 1)) * VEC) + (col % VEC);
   };
 
   // ---- running state.  With FUSE, wave (qr, hv) owns state rows
@@ -183,7 +203,7 @@ void chunk_kernel(ChunkArgs a) {
     for (int k = 0; k < NST; ++k) {
       int rt, ct;
       if (stile(k, rt, ct)) {
-        DT* p = Sb + (16 * ct + lr) * SB_LD + 16 * rt + 4 * lg;
+        DT* p = Sb + sq_at(16 * ct + lr, 16 * rt + 4 * lg);
         if constexpr (ESZ == 2) {
           u32x2_t v2;
           v2[0] = pack_bf16x2(sacc[k][0], sacc[k][1]);
@@ -295,7 +315,7 @@ void chunk_kernel(ChunkArgs a) {
         st16(Kn + kn_at(t, cb * VEC), phi_vec(pk[n], ok, full));
         if (!ok) pv[n] = u32x4_t{0u, 0u, 0u, 0u};
       }
-      if constexpr (USE_Q && QS_STAGE) st16(Qs + t * KN_LD + cb * VEC, phi_vec(pq[n], ok, full));
+      if constexpr (USE_Q && QS_STAGE) st16(Qs + sq_at(t, cb * VEC), phi_vec(pq[n], ok, full));
     }
     if constexpr (USE_KV) {
       // element e of every loaded vector goes to V^T row cb*VEC + e; the
@@ -356,7 +376,7 @@ void chunk_kernel(ChunkArgs a) {
       u32x4_t qop[NQ];
 #pragma unroll
       for (int m = 0; m < NQ; ++m)
-        qop[m] = QS_STAGE ? ld16(Qs + (16 * qr + lr) * KN_LD + KB * m + VEC * lg) : qreg[m];
+        qop[m] = QS_STAGE ? ld16(Qs + sq_at(16 * qr + lr, KB * m + VEC * lg)) : qreg[m];
       f32x4_t nacc[NVW];
 #pragma unroll
       for (int i = 0; i < NVW; ++i) nacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -365,7 +385,7 @@ void chunk_kernel(ChunkArgs a) {
       for (int m = 0; m < NQ; ++m) {
         u32x4_t av[NVW];
 #pragma unroll
-        for (int i = 0; i < NVW; ++i) av[i] = ld16(Sb + (16 * vtile(i) + lr) * SB_LD + KB * m + VEC * lg);
+        for (int i = 0; i < NVW; ++i) av[i] = ld16(Sb + sq_at(16 * vtile(i) + lr, KB * m + VEC * lg));
 #pragma unroll
         for (int i = 0; i < NVW; ++i) O::mma(nacc[i], av[i], qop[m]);
       }
