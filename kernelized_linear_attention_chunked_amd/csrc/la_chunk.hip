@@ -60,16 +60,16 @@ struct ChunkWaves {
 __device__ __forceinline__ int vt_swz(int r) { return ((r >> 1) & 7) ^ ((r >> 4) & 3); }
 
 // The second bound is the minimum number of waves per SIMD.  At 8 waves the
-// apply mode and the bf16 state mode ask for 4 (two workgroups per CU, at most
-// 128 registers); the causal mode and the fp32 state mode need more registers.
+// bf16 state and apply modes ask for 4 (two workgroups per CU, at most 128
+// registers); the causal mode and the fp32 kernels need more registers.
 template <typename DT, int D, int MODE>
 struct ChunkOccupancy {
   static constexpr int NW = ChunkWaves<D>::NW;
-  static constexpr int value =
-      NW == 8 ? ((MODE == kApply || (MODE == kState && sizeof(DT) == 2)) ? 4 : 1) : 2;
+  static constexpr int value = NW == 8 ? ((MODE != kCausal && sizeof(DT) == 2) ? 4 : 1) : 2;
 };
 
-template <typename DT, int D, int FM, bool NORM, int MODE>
+// MASKED: a (B,T) mask is given.  Unmasked launches carry no mask code at all.
+template <typename DT, int D, int FM, bool NORM, int MODE, bool MASKED>
 __global__ __launch_bounds__(64 * ChunkWaves<D>::NW, (ChunkOccupancy<DT, D, MODE>::value))
 void chunk_kernel(ChunkArgs a) {
   using O = Op<DT>;
@@ -133,7 +133,7 @@ void chunk_kernel(ChunkArgs a) {
   const DT* kb = (const DT*)a.k + unit_off;
   const DT* vb = (const DT*)a.v + unit_off;
   DT* ob = (DT*)a.out + unit_off;
-  const uint8_t* mb = a.mask ? a.mask + (int64_t)b * T : nullptr;
+  const uint8_t* const mb = MASKED ? a.mask + (int64_t)b * T : nullptr;
   const float eps = a.eps;
   // global dv tile of the wave's i-th output tile
   auto vtile = [&](int i) { return (NORM && i == NDH) ? NDT : hv * NDH + i; };
@@ -175,7 +175,7 @@ void chunk_kernel(ChunkArgs a) {
   f32x4_t sacc[NST];
 #pragma unroll
   for (int k = 0; k < NST; ++k) sacc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if constexpr (MODE != kState) {
+  if constexpr (MODE == kCausal) {
     const float* sin = a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr;
     const float* zin = a.z_in ? a.z_in + u * a.z_in_u + s * a.z_in_s : nullptr;
 #pragma unroll
@@ -215,7 +215,59 @@ void chunk_kernel(ChunkArgs a) {
       }
     }
   };
-  if constexpr (USE_SB) write_sb();
+  if constexpr (MODE == kCausal) write_sb();
+  if constexpr (MODE == kApply) {
+    // the fixed S and Z straight into S^T: coalesced 16-byte loads of S rows,
+    // transposed element-wise into LDS (S is not needed in registers here)
+    const float* sin = a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr;
+    const float* zin = a.z_in ? a.z_in + u * a.z_in_u + s * a.z_in_s : nullptr;
+    // a lane takes KPL consecutive dk (one 4-byte LDS word per S^T row) of four
+    // consecutive dv; consecutive lanes take consecutive dk, so the LDS writes
+    // run along S^T rows
+    constexpr int KPL = 4 / ESZ;
+    auto put = [&](int off, const float (&x)[KPL]) {
+      if constexpr (ESZ == 2)
+        *(uint32_t*)(Sb + off) = pack_bf16x2(x[0], x[1]);
+      else
+        ((float*)Sb)[off] = x[0];
+    };
+    // all loads first (one memory round trip), then the LDS writes
+    constexpr int NCOPY = (D / 4) * (D / KPL);
+    constexpr int NIT = (NCOPY + NTH - 1) / NTH;
+    f32x4_t x[NIT][KPL];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + it * NTH;
+      const int dv = 4 * (idx / (D / KPL)), dk = KPL * (idx % (D / KPL));
+#pragma unroll
+      for (int p = 0; p < KPL; ++p)
+        x[it][p] = (sin && idx < NCOPY) ? *(const f32x4_t*)(sin + (dk + p) * D + dv)
+                                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + it * NTH;
+      if (idx >= NCOPY) break;
+      const int dv = 4 * (idx / (D / KPL)), dk = KPL * (idx % (D / KPL));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float y[KPL];
+#pragma unroll
+        for (int p = 0; p < KPL; ++p) y[p] = x[it][p][j];
+        put(sq_at(dv + j, dk), y);
+      }
+    }
+    if constexpr (NORM) {
+      // the normaliser tile: 16 rows, each holding Z
+      for (int idx = tid; idx < 16 * (D / KPL); idx += NTH) {
+        const int r = idx / (D / KPL), dk = KPL * (idx % (D / KPL));
+        float y[KPL];
+#pragma unroll
+        for (int p = 0; p < KPL; ++p) y[p] = zin ? zin[dk + p] : 0.f;
+        put(sq_at(D + r, dk), y);
+      }
+    }
+  }
   if constexpr (USE_KV && NORM) {
     // rows D..D+15 of V^T are ones: they turn A V into the row sums of A
     for (int idx = tid; idx < 16 * VT_LD; idx += NTH) {
@@ -236,9 +288,29 @@ void chunk_kernel(ChunkArgs a) {
   u32x4_t qreg[(USE_Q && !QS_STAGE) ? NQ : 1];
   uint32_t valid = 0;   // bit n: token tg*NTOK + n exists and is not masked
   bool qrow_ok = false; // (unstaged q) this lane's own query row exists and is not masked
+  // the prefetched chunk holds at least one valid token (plive) / every token
+  // exists and is valid (pfull); the same in every wave (each ballots the
+  // chunk's 64 mask bytes), so the branches on them are uniform
+  bool plive = true, pfull = true;
+  static_assert(kChunk == 64, "one mask byte per lane");
+  // mask byte of token l of the chunk prefetched next, loaded one chunk ahead
+  // so that the ballot does not wait on it
+  auto load_mask = [&](int c) -> uint32_t {
+    const int t = c * kChunk + l;
+    return (c < c1 && t < T) ? (uint32_t)mb[t] : 0u;
+  };
+  uint32_t mnext = (mb && c0 < c1) ? load_mask(c0) : 0u;
   auto prefetch = [&](int c) {
     const int tb = c * kChunk;
     valid = 0;
+    pfull = tb + kChunk <= T;
+    if (mb) {
+      const uint64_t bal = __ballot(mnext != 0u);
+      plive = bal != 0;
+      pfull = pfull && bal == ~0ull;
+      mnext = load_mask(c + 1);
+      if (!plive) return;  // fully masked chunk: nothing to load
+    }
     if constexpr (USE_Q && !QS_STAGE) {
       const int tok = tb + 16 * qr + lr;
       qrow_ok = tok < T && (mb ? (mb[tok] != 0) : true);
@@ -247,8 +319,8 @@ void chunk_kernel(ChunkArgs a) {
         pq[m] = tok < T ? ld16(qb + (int64_t)tok * HD + KB * m + VEC * lg) : u32x4_t{0u, 0u, 0u, 0u};
     }
     if (!loader) return;
-    if (!mb && tb + kChunk <= T) {
-      // whole chunk, no mask: every token valid, no per-token guards
+    if (pfull) {
+      // whole chunk, every token valid: no per-token guards
       valid = (1u << NTOK) - 1u;
 #pragma unroll
       for (int n = 0; n < NTOK; ++n) {
@@ -371,7 +443,19 @@ void chunk_kernel(ChunkArgs a) {
   // V^T operand (16-byte block `blk` of row 16*ct + lr)
   auto vt_op = [&](int ct, int blk) { return ld16(Vt + vt_at(16 * ct + lr, blk)); };
 
-  auto compute = [&](int c) {
+  auto compute = [&](int c, bool live, bool full) {
+    if (!live) {
+      // fully masked chunk: state unchanged, outputs zero
+      if constexpr (USE_Q) {
+        const int tok = c * kChunk + 16 * qr + lr;
+        if (tok < T) {
+          DT* orow = ob + (int64_t)tok * HD + 4 * lg;
+#pragma unroll
+          for (int i = 0; i < NDH; ++i) store4(orow + 16 * (hv * NDH + i), 0.f, 0.f, 0.f, 0.f);
+        }
+      }
+      return;
+    }
     if constexpr (USE_Q) {
       u32x4_t qop[NQ];
 #pragma unroll
@@ -473,7 +557,7 @@ void chunk_kernel(ChunkArgs a) {
       // epilogue: lane holds query 16qr + lr, value dims 16*vtile(i) + 4lg + (0..3)
       const int tok = c * kChunk + 16 * qr + lr;
       if (tok < T) {
-        const bool ok = mb ? (mb[tok] != 0) : true;
+        const bool ok = (full || !mb) ? true : (mb[tok] != 0);
         float rden = 1.f;
         if constexpr (NORM) rden = ok ? 1.f / (nacc[NDH][0] + eps) : 0.f;
         else rden = ok ? 1.f : 0.f;
@@ -509,16 +593,23 @@ void chunk_kernel(ChunkArgs a) {
 
   if (c0 < c1) prefetch(c0);
   for (int c = c0; c < c1; ++c) {
-    // wave-uniform: every token of the chunk exists and there is no mask
-    if (!mb && (c + 1) * kChunk <= T)
-      stage(std::true_type{});
-    else
-      stage(std::false_type{});
-    __syncthreads();
+    const bool live = MASKED ? plive : true;
+    const bool full = pfull;
+    if (live) {
+      if (full)
+        stage(std::true_type{});
+      else
+        stage(std::false_type{});
+      __syncthreads();
+    }
     if (c + 1 < c1) prefetch(c + 1);
-    compute(c);
-    __syncthreads();
-    if constexpr (MODE == kCausal) write_sb();
+    // a dead chunk touches no LDS, so it needs neither barrier: the next
+    // chunk's stage cannot overwrite anything a slower wave still reads
+    compute(c, live, full);
+    if (live) {
+      __syncthreads();
+      if constexpr (MODE == kCausal) write_sb();
+    }
   }
 
   // ---- state out
@@ -611,8 +702,12 @@ __global__ __launch_bounds__(kThreads) void seg_sum_kernel(float* ws_s, float* w
 
 template <typename DT, int D, int FM, bool NORM, int MODE>
 static hipError_t launch_one(const ChunkArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((chunk_kernel<DT, D, FM, NORM, MODE>), dim3(grid), dim3(64 * ChunkWaves<D>::NW), 0,
-                     st, a);
+  if (a.mask)
+    hipLaunchKernelGGL((chunk_kernel<DT, D, FM, NORM, MODE, true>), dim3(grid),
+                       dim3(64 * ChunkWaves<D>::NW), 0, st, a);
+  else
+    hipLaunchKernelGGL((chunk_kernel<DT, D, FM, NORM, MODE, false>), dim3(grid),
+                       dim3(64 * ChunkWaves<D>::NW), 0, st, a);
   return hipGetLastError();
 }
 

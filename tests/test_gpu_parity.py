@@ -122,6 +122,41 @@ def test_masked_garbage_does_not_leak(dtype, fm):
     assert torch.all(y2[bad] == 0) and torch.all(y3[bad] == 0)
 
 
+@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+def test_fully_masked_chunks(dtype, D, causal):
+    # whole 64-token chunks without a valid token are skipped by the kernels: the
+    # state passes through them, their outputs are written as zeros (the output
+    # buffer starts as NaN) and their inputs (NaN here) are never read
+    B, T, H = 2, 330, 2
+    q, k, v = _inputs(B, T, H, D, dtype, 500 + D, qk_std=0.5 if causal else 1.0)
+    mask = torch.ones((B, T), dtype=torch.bool, device=DEV)
+    mask[0, 64:192] = False     # two dead chunks in the middle
+    mask[0, 256:] = False       # dead tail
+    mask[0, 5] = False          # and a partly masked chunk
+    mask[1, 70:] = False        # row 1: chunk 1 partly valid, the rest dead
+    qn, kn, vn = q.clone(), k.clone(), v.clone()
+    for t in (qn, kn, vn):
+        t[~mask] = float("nan")
+    out = torch.full((B, T, H, D), float("nan"), dtype=dtype, device=DEV)
+    m = mask.cpu().numpy()
+    if causal:
+        S0, Z0 = _state(B, H, D, 500 + D)
+        y, (S, Z) = la.la_forward(qn, kn, vn, mask=mask, state=(S0, Z0), causal=True,
+                                  return_state=True, out=out)
+        torch.cuda.synchronize()
+        yo, So, Zo = oracle.causal(f64(q), f64(k), f64(v), m, f64(S0), f64(Z0))
+        assert_close(S, So, TOL[dtype], "S")
+        assert_close(Z, Zo, TOL[dtype], "Z")
+    else:
+        y = la.la_forward(qn, kn, vn, mask=mask, causal=False, feature_map="relu", out=out)
+        torch.cuda.synchronize()
+        yo, _, _ = oracle.noncausal(f64(q), f64(k), f64(v), m, "relu", True, 1e-6)
+    assert torch.all(y[~mask] == 0)
+    assert_close(y, yo, TOL[dtype], "out")
+
+
 def test_all_false_and_all_true_masks():
     B, T, H, D = 2, 100, 2, 32
     q, k, v = _inputs(B, T, H, D, torch.float32, 3)
