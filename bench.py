@@ -61,14 +61,18 @@ def _traffic(kernel, src, launches_per_record=1):
 
 def prefill_mfma_per_chunk(D=128, norm=True):
     """MFMA instructions one workgroup issues per 64-token chunk in the causal
-    prefill kernel (bf16, v_mfma_f32_16x16x32_bf16), from its tiling:
-    A^T tiles (w+1 per wave) x D/32 steps; intra V^T A^T: ceil((w+1)/2) tile pairs
-    x (D/16 + norm) value tiles x 2 (hi/lo split of A); inter S^T phiQ^T:
-    4 waves x (D/16 + norm) x D/32; state update: (D/16)(D/16 + norm) tiles x 2."""
+    prefill kernel (bf16, v_mfma_f32_16x16x32_bf16), from its tiling.  Query
+    block qr (16 rows) forms A^T over key pairs of 32 up to its diagonal,
+    2 tiles per pair x D/32 steps, once per value half (two halves at D=128);
+    intra V^T A^T: pairs x (D/16 + norm) value tiles x 2 (hi/lo of A); inter
+    S^T phiQ^T: 4 blocks x (D/16 + norm) x D/32; state update: (D/16)(D/16 + norm)
+    tiles x 2 token steps."""
     nvt = D // 16 + (1 if norm else 0)
     nq = D // 32
-    a_t = sum(w + 1 for w in range(4)) * nq
-    intra = sum((w + 2) // 2 for w in range(4)) * nvt * 2
+    halves = 2 if D >= 128 else 1
+    pairs = [(16 * qr + 15) // 32 + 1 for qr in range(4)]
+    a_t = halves * sum(2 * p for p in pairs) * nq
+    intra = sum(pairs) * nvt * 2
     inter = 4 * nvt * nq
     upd = (D // 16) * nvt * 2
     return a_t + intra + inter + upd
