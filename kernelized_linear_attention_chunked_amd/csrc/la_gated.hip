@@ -129,44 +129,59 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
   const int cb = tid % CB, tg = tid / CB;
   const bool loader = tid < LOADERS;
   u32x4_t pk[NTOK], pv[NTOK], pq[OUT ? HPW * NQ : 1];
-  float pg = 0.f;
-  auto prefetch = [&](int c) {
+  // Prefetches are unconditional loads from addresses clamped to the last token
+  // (tokens past the end are zeroed when staged, or never stored), and nothing
+  // reads a prefetched register before it is consumed: a select, copy or
+  // conversion of a register still being loaded would make the load wait.
+  uint32_t pgr = 0u;  // raw bits of the decay of token l of the chunk
+  auto load_g = [&](const DT* p) -> uint32_t {
+    if constexpr (ESZ == 2)
+      return (uint32_t)*(const uint16_t*)p;
+    else
+      return *(const uint32_t*)p;
+  };
+  auto prefetch_kvg = [&](int c) {
     const int tb = c * kChunk;
     if (loader) {
 #pragma unroll
       for (int n = 0; n < NTOK; ++n) {
-        const int tok = tb + tg * NTOK + n;
-        if (tok < T) {
-          const int64_t off = (int64_t)tok * KS + cb * VEC;
-          pk[n] = ld16(kb + off);
-          pv[n] = ld16(vb + off);
-        } else {
-          pk[n] = u32x4_t{0u, 0u, 0u, 0u};
-          pv[n] = u32x4_t{0u, 0u, 0u, 0u};
-        }
+        const int tok = min(tb + tg * NTOK + n, T - 1);
+        const int64_t off = (int64_t)tok * KS + cb * VEC;
+        pk[n] = ld16(kb + off);
+        pv[n] = ld16(vb + off);
       }
     }
-    {
-      const int tok = tb + l;
-      pg = (gb && tok < T) ? ld_scalar<DT>(gb + (int64_t)tok * Hkv) : 0.f;
-    }
+    // without a decay input (the plain linear rule) some valid word is read and
+    // ignored, so that the load is unconditional
+    pgr = load_g(gb ? gb + (int64_t)min(tb + l, T - 1) * Hkv : kb);
+  };
+  // the wave's own query rows of its heads, used straight from these registers
+  auto prefetch_q = [&](int c) {
     if constexpr (OUT) {
-      const int tok = tb + 16 * wr + lr;
+      const int tok = min(c * kChunk + 16 * wr + lr, T - 1);
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
         const int hq = hp + P * hh;
 #pragma unroll
         for (int m = 0; m < NQ; ++m)
-          pq[hh * NQ + m] = tok < T ? ld16(qb + (int64_t)tok * QS + hq * D + KB * m + VEC * lg)
-                                    : u32x4_t{0u, 0u, 0u, 0u};
+          pq[hh * NQ + m] = ld16(qb + (int64_t)tok * QS + hq * D + KB * m + VEC * lg);
       }
     }
   };
 
-  u32x4_t qop[OUT ? HPW * NQ : 1];
   float bcs = 0.f;  // lane l: inclusive cumulative decay of token l of the chunk
   float seg_log = 0.f;
-  auto stage = [&]() {
+  auto stage = [&](int c) {
+    const int tb = c * kChunk;
+    if (tb + kChunk > T && loader) {
+      // ragged last chunk: tokens past the end contribute nothing
+#pragma unroll
+      for (int n = 0; n < NTOK; ++n)
+        if (tb + tg * NTOK + n >= T) {
+          pk[n] = u32x4_t{0u, 0u, 0u, 0u};
+          pv[n] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
     if (loader) {
 #pragma unroll
       for (int n = 0; n < NTOK; ++n) st16(Kn + (tg * NTOK + n) * KN_LD + cb * VEC, pk[n]);
@@ -207,17 +222,13 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
       }
     }
     // inclusive scan of the chunk's decays across the wave (each wave keeps its own copy)
-    float x = pg;
+    float x = (gb && tb + l < T) ? (ESZ == 2 ? bf16_bits_to_f32(pgr) : __uint_as_float(pgr)) : 0.f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(x, off);
       if (l >= off) x += y;
     }
     bcs = x;
-    if constexpr (OUT) {
-#pragma unroll
-      for (int i = 0; i < HPW * NQ; ++i) qop[i] = pq[i];
-    }
   };
 
   auto compute = [&](int c) {
@@ -245,7 +256,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
 #pragma unroll
             for (int m = 0; m < NQ; ++m) {
               const u32x4_t av = ld16(Kn + (16 * jt + lr) * KN_LD + KB * m + VEC * lg);
-              O::mma(at[jt], av, qop[hh * NQ + m]);
+              O::mma(at[jt], av, pq[hh * NQ + m]);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) at[jt][q] *= fac[jt][q];
@@ -261,7 +272,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
 #pragma unroll
           for (int ct = 0; ct < NDT; ++ct) {
             const u32x4_t av = ld16(Sb + (16 * ct + lr) * SB_LD + KB * m + VEC * lg);
-            O::mma(nacc[ct], av, qop[hh * NQ + m]);
+            O::mma(nacc[ct], av, pq[hh * NQ + m]);
           }
         }
 #pragma unroll
@@ -315,6 +326,9 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
         }
       }
     }
+    // the heads are done with this chunk's queries: load the next chunk's (the
+    // last chunk reloads itself: an unconditional load leaves nothing to merge)
+    prefetch_q(min(c + 1, c1 - 1));
     // state: S = exp(btot) S + sum_t exp(btot - b_t) k_t v_t^T
     {
       const float eb = __expf(btot);
@@ -370,11 +384,14 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
     }
   };
 
-  if (c0 < c1) prefetch(c0);
+  if (c0 < c1) {
+    prefetch_kvg(c0);
+    prefetch_q(c0);
+  }
   for (int c = c0; c < c1; ++c) {
-    stage();
+    stage(c);
     __syncthreads();
-    if (c + 1 < c1) prefetch(c + 1);
+    prefetch_kvg(min(c + 1, c1 - 1));
     compute(c);
     __syncthreads();
     if constexpr (OUT) write_sb();
