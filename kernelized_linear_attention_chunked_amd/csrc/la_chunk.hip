@@ -48,16 +48,7 @@ struct ChunkWaves {
   static constexpr int NW = D >= 128 ? 8 : 4;
 };
 
-// LDS layouts.  gfx950 LDS has 64 banks of 4 bytes; a 16-byte read serves the
-// 8-lane blocks {0,3}, {1,2}, {4,7}, {5,6} of a wavefront together (16 lanes,
-// 256 bytes per cycle), while writes and narrower reads go 32 banks wide.  All
-// tiles are stored as rows of 16-byte blocks with the block index XORed by a
-// function of the row, chosen against that model so that every operand read is
-// conflict-free and the transposed writes stay at two-way:
-//   V^T  [dv][token]: g(r) = ((r >> 1) & 7) ^ ((r >> 4) & 3)
-//   phiK [token][dk]: 4*bit3(t) ^ 5*bit4(t)
-//   phiQ, S^T       : bit3(r)
-__device__ __forceinline__ int vt_swz(int r) { return ((r >> 1) & 7) ^ ((r >> 4) & 3); }
+// LDS layouts: the swizzles of la_device.hpp (vt_swz, kn_swz, sq_swz).
 
 // The second bound is the minimum number of waves per SIMD.  At 8 waves the
 // bf16 state and apply modes ask for 4 (two workgroups per CU, at most 128
@@ -144,12 +135,11 @@ void chunk_kernel(ChunkArgs a) {
   // one pass) and the column-wise reads of the state update (rows 8 apart)
   // spread over the banks
   auto kn_at = [&](int t, int col) {
-    const int sw = ((4 * ((t >> 3) & 1)) ^ (5 * ((t >> 4) & 1))) & (CB - 1);
-    return t * KN_LD + (((col / VEC) ^ sw) * VEC) + (col % VEC);
+    return t * KN_LD + (((col / VEC) ^ (kn_swz(t) & (CB - 1))) * VEC) + (col % VEC);
   };
   // element offset of element `col` of row r of phi(Q) or S^T
   auto sq_at = [&](int r, int col) {
-    return r * SB_LD + (((col / VEC) ^ ((r >> 3) & 1)) * VEC) + (col % VEC);
+    return r * SB_LD + (((col / VEC) ^ sq_swz(r)) * VEC) + (col % VEC);
   };
 
   // ---- running state.  With FUSE, wave (qr, hv) owns state rows
@@ -396,20 +386,21 @@ void chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const int r = cb * VEC + e;
-        DT* p = Vt + vt_at(r, t0 / VEC) + (t0 % VEC);
+        // (a thread's tokens may span several 16-byte blocks, which the
+        // swizzle does not keep adjacent: each group is addressed by itself)
         if constexpr (ESZ == 2) {
 #pragma unroll
           for (int n = 0; n < NTOK; n += 2) {
             const uint32_t w0 = pv[n][e >> 1], w1 = pv[n + 1][e >> 1];
             // low halves of both words for even e, high halves for odd e
-            const uint32_t word = (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
-                                          : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-            *(uint32_t*)(p + n) = word;
+            *(uint32_t*)(Vt + vt_at(r, (t0 + n) / VEC) + (t0 + n) % VEC) =
+                (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u) : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
           }
         } else {
           float fv[NTOK];
 #pragma unroll
           for (int n = 0; n < NTOK; ++n) fv[n] = __uint_as_float(pv[n][e]);
+          DT* p = Vt + vt_at(r, t0 / VEC) + (t0 % VEC);
           if constexpr (NTOK == 1) {
             *(float*)p = fv[0];
           } else if constexpr (NTOK == 2) {
@@ -417,7 +408,7 @@ void chunk_kernel(ChunkArgs a) {
           } else {
 #pragma unroll
             for (int n = 0; n < NTOK; n += 4)
-              *(f32x4_t*)(p + n) = f32x4_t{fv[n], fv[n + 1], fv[n + 2], fv[n + 3]};
+              *(f32x4_t*)(Vt + vt_at(r, (t0 + n) / VEC)) = f32x4_t{fv[n], fv[n + 1], fv[n + 2], fv[n + 3]};
           }
         }
       }

@@ -61,6 +61,21 @@ __device__ __forceinline__ float phi(float x, float eps) {
 }
 
 // ---------------------------------------------------------------------------
+// LDS layouts shared by the chunk kernels.  gfx950 LDS has 64 banks of 4 bytes;
+// a 16-byte read serves the 8-lane blocks {0,3}, {1,2}, {4,7}, {5,6} of a
+// wavefront together (16 lanes, 256 bytes per cycle), while writes and
+// narrower reads go 32 banks wide (measured with SQ_LDS_BANK_CONFLICT).  Tiles
+// are rows of 16-byte blocks whose block index is XORed by a function of the
+// row, chosen against that model so that the operand reads are conflict-free
+// and the transposed writes two-way at most:
+//   V^T  [d][token], 128-byte rows : g(r) = ((r >> 1) & 7) ^ ((r >> 4) & 3)
+//   K    [token][d], rows of D + one block : 4*bit3(t) ^ 5*bit4(t)
+//   Q, S^T [row][d], rows of D + one block : bit3(r)
+__device__ __forceinline__ int vt_swz(int r) { return ((r >> 1) & 7) ^ ((r >> 4) & 3); }
+__device__ __forceinline__ int kn_swz(int t) { return (4 * ((t >> 3) & 1)) ^ (5 * ((t >> 4) & 1)); }
+__device__ __forceinline__ int sq_swz(int r) { return (r >> 3) & 1; }
+
+// ---------------------------------------------------------------------------
 // Operand traits.  A "vector" is 16 bytes of one row in memory: 8 bf16 or 4
 // fp32 values.  One vector-step contracts KB = 4 * VEC indices: lane group lg
 // carries indices [KB*m + VEC*lg, KB*m + VEC*lg + VEC).  For bf16 that is one

@@ -40,21 +40,30 @@ __device__ __forceinline__ float ld_scalar<float>(const float* p) {
   return *p;
 }
 
+// The second bound is the minimum number of waves per SIMD: the bf16 state pass
+// of an 8-wave workgroup is held to 128 registers (two workgroups per CU).
+template <typename DT, int G, int MODE>
+struct GatedOccupancy {
+  static constexpr int value = (GatedShape<G>::NW == 8 && MODE != kModeCausal && sizeof(DT) == 2) ? 4 : 1;
+};
+
 template <typename DT, int D, int G, int MODE>
-__global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) {
+__global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::value)) void gated_kernel(GatedArgs a) {
   using O = Op<DT>;
   using SH = GatedShape<G>;
   constexpr int P = SH::P, NW = SH::NW, NTH = SH::NTH, HPW = SH::HPW;
   constexpr int VEC = O::VEC, KB = O::KB, ESZ = O::ESZ;
   constexpr int NDT = D / 16;
   constexpr int CB = D / VEC;
-  constexpr int LOADERS = NTH < kChunk * CB ? NTH : kChunk * CB;
+  // loading threads; bf16 V^T writes pack token pairs, so at least 2 tokens each
+  constexpr int LOADERS = (kChunk * CB / NTH >= 2 || ESZ == 4) ? (NTH < kChunk * CB ? NTH : kChunk * CB)
+                                                                : kChunk * CB / 2;
   constexpr int NTOK = kChunk * CB / LOADERS;
   constexpr int NQ = D / KB;
   constexpr int NKS = kChunk / KB;
   constexpr int PADE = 16 / ESZ;
   constexpr int KN_LD = D + PADE;
-  constexpr int VT_LD = kChunk + PADE;
+  constexpr int VT_LD = kChunk;
   constexpr int SB_LD = D + PADE;
   constexpr bool OUT = MODE == kModeCausal;
   constexpr int KN_BYTES = kChunk * KN_LD * ESZ;
@@ -63,6 +72,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
   constexpr int NS = NDT * NDT;
   constexpr int TPW = (NS + NW - 1) / NW;
   static_assert(NTOK >= 1 && NQ >= 1, "unsupported head size");
+  static_assert(ESZ == 4 || NTOK % 2 == 0, "bf16 V^T writes pack token pairs");
 
   __shared__ __align__(16) unsigned char smem[KN_BYTES + VT_BYTES + SB_BYTES + 16];
   DT* Kn = (DT*)smem;
@@ -87,6 +97,14 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
   const DT* vb = (const DT*)a.v + (int64_t)b * T * KS + (int64_t)j * D;
   const DT* gb = a.decay ? (const DT*)a.decay + (int64_t)b * T * Hkv + j : nullptr;
   const float scale = a.scale;
+  // LDS element offsets (layouts and swizzles of la_device.hpp)
+  auto vt_at = [&](int r, int blk) { return r * VT_LD + ((blk ^ vt_swz(r)) * VEC); };
+  auto kn_at = [&](int t, int col) {
+    return t * KN_LD + (((col / VEC) ^ (kn_swz(t) & (CB - 1))) * VEC) + (col % VEC);
+  };
+  auto sq_at = [&](int r, int col) {
+    return r * SB_LD + (((col / VEC) ^ sq_swz(r)) * VEC) + (col % VEC);
+  };
 
   f32x4_t sacc[TPW];
 #pragma unroll
@@ -111,7 +129,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
       const int tau = w * TPW + i;
       if (tau < NS) {
         const int rt = tau / NDT, ct = tau % NDT;
-        DT* p = Sb + (16 * ct + lr) * SB_LD + 16 * rt + 4 * lg;
+        DT* p = Sb + sq_at(16 * ct + lr, 16 * rt + 4 * lg);
         if constexpr (ESZ == 2) {
           u32x2_t v2;
           v2[0] = pack_bf16x2(sacc[i][0], sacc[i][1]);
@@ -184,31 +202,28 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
     }
     if (loader) {
 #pragma unroll
-      for (int n = 0; n < NTOK; ++n) st16(Kn + (tg * NTOK + n) * KN_LD + cb * VEC, pk[n]);
+      for (int n = 0; n < NTOK; ++n) st16(Kn + kn_at(tg * NTOK + n, cb * VEC), pk[n]);
+      // element e of every loaded vector goes to V^T row cb*VEC + e; the
+      // thread's NTOK consecutive tokens sit side by side in one 16-byte block
+      const int t0 = tg * NTOK;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        DT* p = Vt + (cb * VEC + e) * VT_LD + tg * NTOK;
+        const int r = cb * VEC + e;
+        // (a thread's tokens may span several 16-byte blocks, which the
+        // swizzle does not keep adjacent: each group is addressed by itself)
         if constexpr (ESZ == 2) {
-          uint32_t hw[NTOK];
 #pragma unroll
-          for (int n = 0; n < NTOK; ++n) hw[n] = (pv[n][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-          if constexpr (NTOK == 1) {
-            *(uint16_t*)p = (uint16_t)hw[0];
-          } else if constexpr (NTOK == 2) {
-            *(uint32_t*)p = hw[0] | (hw[1] << 16);
-          } else {
-#pragma unroll
-            for (int n = 0; n < NTOK; n += 4) {
-              u32x2_t v2;
-              v2[0] = hw[n] | (hw[n + 1] << 16);
-              v2[1] = hw[n + 2] | (hw[n + 3] << 16);
-              *(u32x2_t*)(p + n) = v2;
-            }
+          for (int n = 0; n < NTOK; n += 2) {
+            const uint32_t w0 = pv[n][e >> 1], w1 = pv[n + 1][e >> 1];
+            // low halves of both words for even e, high halves for odd e
+            *(uint32_t*)(Vt + vt_at(r, (t0 + n) / VEC) + (t0 + n) % VEC) =
+                (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u) : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
           }
         } else {
           float fv[NTOK];
 #pragma unroll
           for (int n = 0; n < NTOK; ++n) fv[n] = __uint_as_float(pv[n][e]);
+          DT* p = Vt + vt_at(r, t0 / VEC) + (t0 % VEC);
           if constexpr (NTOK == 1) {
             *(float*)p = fv[0];
           } else if constexpr (NTOK == 2) {
@@ -216,7 +231,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
           } else {
 #pragma unroll
             for (int n = 0; n < NTOK; n += 4)
-              *(f32x4_t*)(p + n) = f32x4_t{fv[n], fv[n + 1], fv[n + 2], fv[n + 3]};
+              *(f32x4_t*)(Vt + vt_at(r, (t0 + n) / VEC)) = f32x4_t{fv[n], fv[n + 1], fv[n + 2], fv[n + 3]};
           }
         }
       }
@@ -236,30 +251,41 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
     if constexpr (OUT) {
       const float bi = __shfl(bcs, 16 * wr + lr);
       const float ebi = __expf(bi);
-      // decay factor of A^T element (key 16jt + 4lg + q, query 16wr + lr)
-      float fac[4][4];
+      // A^T tiles of the wave's query block: bf16 uses two per key pair p with
+      // permuted rows (element q of tile (p, odd) is key 32p + 8lg + 4odd + q,
+      // so that lane group lg holds keys 32p + 8lg + (0..7): one 16-byte V^T
+      // read per value tile); fp32 uses single key tiles (key 16jt + 4lg + q).
+      // fac: the decay factor exp(b_i - b_j) of each element, 0 above the diagonal.
+      constexpr int NAT = 4;
+      auto key_of = [&](int t, int q) {
+        return ESZ == 2 ? 32 * (t >> 1) + 8 * lg + 4 * (t & 1) + q : 16 * t + 4 * lg + q;
+      };
+      auto need = [&](int t) { return ESZ == 2 ? (32 * (t >> 1) <= 16 * wr + 15) : (t <= wr); };
+      float fac[NAT][4];
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
+      for (int t = 0; t < NAT; ++t)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float bj = __shfl(bcs, 16 * jt + 4 * lg + q);
-          fac[jt][q] = (jt < wr || (jt == wr && 4 * lg + q <= lr)) ? __expf(bi - bj) : 0.f;
+          const int key = key_of(t, q);
+          const float bj = __shfl(bcs, key);
+          fac[t][q] = key <= 16 * wr + lr ? __expf(bi - bj) : 0.f;
         }
       const int tok = c * kChunk + 16 * wr + lr;
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
-        f32x4_t at[4];
+        f32x4_t at[NAT];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          at[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          if (jt <= wr) {
+        for (int t = 0; t < NAT; ++t) {
+          at[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (need(t)) {
+            const int krow = ESZ == 2 ? 32 * (t >> 1) + 8 * (lr >> 2) + 4 * (t & 1) + (lr & 3) : 16 * t + lr;
 #pragma unroll
             for (int m = 0; m < NQ; ++m) {
-              const u32x4_t av = ld16(Kn + (16 * jt + lr) * KN_LD + KB * m + VEC * lg);
-              O::mma(at[jt], av, pq[hh * NQ + m]);
+              const u32x4_t kv = ld16(Kn + kn_at(krow, KB * m + VEC * lg));
+              O::mma(at[t], kv, pq[hh * NQ + m]);
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) at[jt][q] *= fac[jt][q];
+            for (int q = 0; q < 4; ++q) at[t][q] *= fac[t][q];
           }
         }
         // inter-chunk term first, with the exact query; lane's column is its own
@@ -271,7 +297,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
         for (int m = 0; m < NQ; ++m) {
 #pragma unroll
           for (int ct = 0; ct < NDT; ++ct) {
-            const u32x4_t av = ld16(Sb + (16 * ct + lr) * SB_LD + KB * m + VEC * lg);
+            const u32x4_t av = ld16(Sb + sq_at(16 * ct + lr, KB * m + VEC * lg));
             O::mma(nacc[ct], av, pq[hh * NQ + m]);
           }
         }
@@ -280,24 +306,19 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
         if constexpr (ESZ == 2) {
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
-            if (2 * p <= wr) {
-              const int j0 = 32 * p + 4 * lg, j1 = j0 + 16;
+            if (need(2 * p)) {
               // the terms of A V cancel, so A carries its bf16 rounding residual too
               u32x4_t bh, bl;
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const f32x4_t& src = at[2 * p + (e >> 1)];
-                const float x0 = src[2 * (e & 1)], x1 = src[2 * (e & 1) + 1];
-                const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
-                bh[e] = h0 | (h1 << 16);
-                bl[e] = pack_bf16x2(x0 - bf16_bits_to_f32(h0), x1 - bf16_bits_to_f32(h1));
+                const float x0 = at[2 * p + (e >> 1)][2 * (e & 1)], x1 = at[2 * p + (e >> 1)][2 * (e & 1) + 1];
+                const uint32_t hw = pack_bf16x2(x0, x1);
+                bh[e] = hw;
+                bl[e] = pack_bf16x2(x0 - __uint_as_float(hw << 16), x1 - __uint_as_float(hw & 0xffff0000u));
               }
 #pragma unroll
               for (int ct = 0; ct < NDT; ++ct) {
-                const DT* vr = Vt + (16 * ct + lr) * VT_LD;
-                const u32x2_t lo = *(const u32x2_t*)(vr + j0);
-                const u32x2_t hi = *(const u32x2_t*)(vr + j1);
-                const u32x4_t av = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+                const u32x4_t av = ld16(Vt + vt_at(16 * ct + lr, 4 * p + lg));
                 O::mma(nacc[ct], av, bh);
                 O::mma(nacc[ct], av, bl);
               }
@@ -309,10 +330,11 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
             if (jt <= wr) {
 #pragma unroll
               for (int ct = 0; ct < NDT; ++ct) {
-                const f32x4_t av = *(const f32x4_t*)(Vt + (16 * ct + lr) * VT_LD + 16 * jt + 4 * lg);
+                const u32x4_t av = ld16(Vt + vt_at(16 * ct + lr, 4 * jt + lg));
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                  nacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], at[jt][q], nacc[ct], 0, 0, 0);
+                  nacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av[q]), at[jt][q],
+                                                                  nacc[ct], 0, 0, 0);
               }
             }
           }
@@ -350,14 +372,14 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
             cur_rt = rt;
 #pragma unroll
             for (int m = 0; m < NKS; ++m) {
-              const DT* kc = Kn + (KB * m + VEC * lg) * KN_LD + 16 * rt + lr;
               float f[VEC];
 #pragma unroll
               for (int e = 0; e < VEC; ++e) {
+                const int off = kn_at(KB * m + VEC * lg + e, 16 * rt + lr);
                 if constexpr (ESZ == 2)
-                  f[e] = bf16_bits_to_f32(((const uint16_t*)kc)[e * KN_LD]) * kw[m][e];
+                  f[e] = bf16_bits_to_f32(((const uint16_t*)Kn)[off]) * kw[m][e];
                 else
-                  f[e] = ((const float*)kc)[e * KN_LD] * kw[m][e];
+                  f[e] = ((const float*)Kn)[off] * kw[m][e];
               }
               kop[m] = O::pack(f);
               if constexpr (ESZ == 2) {
@@ -374,7 +396,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH) void gated_kernel(GatedArgs a) 
           }
 #pragma unroll
           for (int m = 0; m < NKS; ++m) {
-            const u32x4_t bv = ld16(Vt + (16 * ct + lr) * VT_LD + KB * m + VEC * lg);
+            const u32x4_t bv = ld16(Vt + vt_at(16 * ct + lr, (KB / VEC) * m + lg));
             O::mma(sacc[i], kop[m], bv);
             if constexpr (ESZ == 2) O::mma(sacc[i], kol[m], bv);
           }
