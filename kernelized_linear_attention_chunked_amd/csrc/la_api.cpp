@@ -39,7 +39,6 @@ la_status device_status(hipError_t e, const char* what) {
 // that workspace sizes depend on the shape alone.
 constexpr int64_t kTargetGroups = 512;
 constexpr int64_t kChunk = 64;
-constexpr int64_t kApplyGroups = 2048;
 
 bool head_size_ok(int64_t d) { return d == 32 || d == 64 || d == 128; }
 
@@ -79,7 +78,7 @@ CausalPlan plan_causal(int64_t U, int64_t T) {
 }
 
 struct NonCausalPlan {
-  int64_t nchunks, nsplit, split_chunks, apply_chunks, napply;
+  int64_t nchunks, nsplit, split_chunks;
 };
 NonCausalPlan plan_noncausal(int64_t U, int64_t T) {
   NonCausalPlan p;
@@ -89,10 +88,6 @@ NonCausalPlan plan_noncausal(int64_t U, int64_t T) {
   if (want < 1) want = 1;
   p.split_chunks = ceil_div(p.nchunks, want);
   p.nsplit = ceil_div(p.nchunks, p.split_chunks);
-  p.apply_chunks = ceil_div(U * p.nchunks, kApplyGroups);
-  if (p.apply_chunks > p.nchunks) p.apply_chunks = p.nchunks;
-  if (p.apply_chunks < 1) p.apply_chunks = 1;
-  p.napply = ceil_div(p.nchunks, p.apply_chunks);
   return p;
 }
 
@@ -338,18 +333,19 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
   e = la::launch_chunk(la::kModeState, bf16, Di, feature_map, norm, pr, (int)(U * p.nsplit), st);
   if (e == hipSuccess) e = la::launch_seg_sum(ws_s, ws_z, (int)U, (int)p.nsplit, Di, norm, st);
   if (e == hipSuccess) {
-    la::ChunkArgs pa = a;
-    pa.s_in = ws_s;
-    pa.z_in = ws_z;
-    pa.s_in_u = p.nsplit * SE;
-    pa.s_in_s = 0;
-    pa.z_in_u = p.nsplit * ZE;
-    pa.z_in_s = 0;
-    pa.seg_count = (int32_t)p.napply;
-    pa.seg_first = 0;
-    pa.seg_chunks = (int32_t)p.apply_chunks;
-    pa.nseg_total = (int32_t)p.napply;
-    e = la::launch_chunk(la::kModeApply, bf16, Di, feature_map, norm, pa, (int)(U * p.napply), st);
+    la::ApplyArgs pa;
+    pa.q = a.q;
+    pa.mask = a.mask;
+    pa.out = a.out;
+    pa.s = ws_s;
+    pa.z = ws_z;
+    pa.s_u = p.nsplit * SE;
+    pa.z_u = p.nsplit * ZE;
+    pa.T = a.T;
+    pa.H = a.H;
+    pa.seg_count = la::apply_groups_per_unit(U, T);
+    pa.eps = a.eps;
+    e = la::launch_apply(bf16, Di, feature_map, norm, pa, (int)(U * pa.seg_count), st);
   }
   return device_status(e, "la_forward (non-causal)");
 }

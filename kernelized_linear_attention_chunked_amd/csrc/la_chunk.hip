@@ -1,6 +1,7 @@
 // Chunk-parallel kernels for causal and non-causal kernelized linear attention.
 //
-// One templated kernel, three modes:
+// One templated kernel, two modes (the non-causal readout with a fixed state is
+// the streaming kernel of la_apply.hip):
 //   kCausal : causal prefill ("[Feature] LinearAttention layer for Keras",
 //             sections "Mathematical definition / Causal", "Masking / Causal",
 //             "Streaming State").  Per chunk of 64 tokens it forms
@@ -11,8 +12,6 @@
 //   kState  : only the state increment  sum_t phiK_t^T V_t  over a segment of
 //             chunks (the partial sums of a split sequence, and the non-causal
 //             reduction of "Mathematical definition / Non-causal").
-//   kApply  : only  y = phiQ S / (phiQ Z + eps)  with a fixed S (the non-causal
-//             readout).
 // The operator page ("LinearAttention", ai.onnx v27, "Description") allows any
 // chunk-parallel evaluation with the sequential result; chunking changes only
 // the summation order.
@@ -38,7 +37,7 @@
 
 namespace la {
 
-enum ChunkMode { kCausal = 0, kState = 1, kApply = 2 };
+enum ChunkMode { kCausal = 0, kState = 1 };
 
 // Wavefronts per workgroup: 8 at head size 128 (the state and the output
 // accumulators would not fit one 4-wave workgroup's registers without
@@ -51,8 +50,8 @@ struct ChunkWaves {
 // LDS layouts: the swizzles of la_device.hpp (vt_swz, kn_swz, sq_swz).
 
 // The second bound is the minimum number of waves per SIMD.  At 8 waves the
-// bf16 state and apply modes ask for 4 (two workgroups per CU, at most 128
-// registers); the causal mode and the fp32 kernels need more registers.
+// bf16 state mode asks for 4 (two workgroups per CU, at most 128 registers);
+// the causal mode and the fp32 kernels need more registers.
 template <typename DT, int D, int MODE>
 struct ChunkOccupancy {
   static constexpr int NW = ChunkWaves<D>::NW;
@@ -82,9 +81,9 @@ void chunk_kernel(ChunkArgs a) {
   constexpr int KN_LD = D + PADE;                  // phi(K), phi(Q) rows
   constexpr int VT_LD = kChunk;                    // V^T rows (swizzled, unpadded)
   constexpr int SB_LD = D + PADE;
-  constexpr bool USE_KV = MODE != kApply;
-  constexpr bool USE_Q = MODE != kState;
-  constexpr bool USE_SB = MODE != kState;
+  constexpr bool USE_KV = true;
+  constexpr bool USE_Q = MODE == kCausal;
+  constexpr bool USE_SB = MODE == kCausal;
   // phi(Q) is staged through LDS (each element evaluated once, coalesced
   // loads), except for fp32 at head size 128 where it would not fit: there each
   // wave loads its own query rows straight into operand registers.
@@ -146,7 +145,7 @@ void chunk_kernel(ChunkArgs a) {
   // [R*qr, R*qr+R) across its own value tiles (the normaliser column belongs to
   // half 0), so the V^T operands it loads for the intra-chunk product serve the
   // state update too; otherwise wave w owns tiles w*TPW .. w*TPW+TPW-1.
-  constexpr bool FUSE = (NDT % 4 == 0) && (MODE != kApply);
+  constexpr bool FUSE = NDT % 4 == 0;
   constexpr int R = FUSE ? NDT / 4 : 1;
   constexpr int NST = FUSE ? R * NVW : TPW;
   auto stile = [&](int k, int& rt, int& ct) -> bool {
@@ -206,58 +205,6 @@ void chunk_kernel(ChunkArgs a) {
     }
   };
   if constexpr (MODE == kCausal) write_sb();
-  if constexpr (MODE == kApply) {
-    // the fixed S and Z straight into S^T: coalesced 16-byte loads of S rows,
-    // transposed element-wise into LDS (S is not needed in registers here)
-    const float* sin = a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr;
-    const float* zin = a.z_in ? a.z_in + u * a.z_in_u + s * a.z_in_s : nullptr;
-    // a lane takes KPL consecutive dk (one 4-byte LDS word per S^T row) of four
-    // consecutive dv; consecutive lanes take consecutive dk, so the LDS writes
-    // run along S^T rows
-    constexpr int KPL = 4 / ESZ;
-    auto put = [&](int off, const float (&x)[KPL]) {
-      if constexpr (ESZ == 2)
-        *(uint32_t*)(Sb + off) = pack_bf16x2(x[0], x[1]);
-      else
-        ((float*)Sb)[off] = x[0];
-    };
-    // all loads first (one memory round trip), then the LDS writes
-    constexpr int NCOPY = (D / 4) * (D / KPL);
-    constexpr int NIT = (NCOPY + NTH - 1) / NTH;
-    f32x4_t x[NIT][KPL];
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int idx = tid + it * NTH;
-      const int dv = 4 * (idx / (D / KPL)), dk = KPL * (idx % (D / KPL));
-#pragma unroll
-      for (int p = 0; p < KPL; ++p)
-        x[it][p] = (sin && idx < NCOPY) ? *(const f32x4_t*)(sin + (dk + p) * D + dv)
-                                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int idx = tid + it * NTH;
-      if (idx >= NCOPY) break;
-      const int dv = 4 * (idx / (D / KPL)), dk = KPL * (idx % (D / KPL));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float y[KPL];
-#pragma unroll
-        for (int p = 0; p < KPL; ++p) y[p] = x[it][p][j];
-        put(sq_at(dv + j, dk), y);
-      }
-    }
-    if constexpr (NORM) {
-      // the normaliser tile: 16 rows, each holding Z
-      for (int idx = tid; idx < 16 * (D / KPL); idx += NTH) {
-        const int r = idx / (D / KPL), dk = KPL * (idx % (D / KPL));
-        float y[KPL];
-#pragma unroll
-        for (int p = 0; p < KPL; ++p) y[p] = zin ? zin[dk + p] : 0.f;
-        put(sq_at(D + r, dk), y);
-      }
-    }
-  }
   if constexpr (USE_KV && NORM) {
     // rows D..D+15 of V^T are ones: they turn A V into the row sums of A
     for (int idx = tid; idx < 16 * VT_LD; idx += NTH) {
@@ -615,7 +562,7 @@ void chunk_kernel(ChunkArgs a) {
     sout = a.s_out + u * a.s_out_u + (s + a.out_slot_off) * a.s_out_s;
     zout = a.z_out ? a.z_out + u * a.z_out_u + (s + a.out_slot_off) * a.z_out_s : nullptr;
   }
-  if constexpr (MODE != kApply) {
+  {
 #pragma unroll
     for (int k = 0; k < NST; ++k) {
       int rt, ct;
@@ -704,11 +651,8 @@ static hipError_t launch_one(const ChunkArgs& a, int grid, hipStream_t st) {
 
 template <typename DT, int D, int FM, bool NORM>
 static hipError_t launch_mode(int mode, const ChunkArgs& a, int grid, hipStream_t st) {
-  switch (mode) {
-    case kCausal: return launch_one<DT, D, FM, NORM, kCausal>(a, grid, st);
-    case kState: return launch_one<DT, D, FM, NORM, kState>(a, grid, st);
-    default: return launch_one<DT, D, FM, NORM, kApply>(a, grid, st);
-  }
+  return mode == kCausal ? launch_one<DT, D, FM, NORM, kCausal>(a, grid, st)
+                         : launch_one<DT, D, FM, NORM, kState>(a, grid, st);
 }
 
 template <typename DT, int D>

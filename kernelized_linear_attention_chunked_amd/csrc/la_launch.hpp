@@ -31,7 +31,7 @@ struct ChunkArgs {
   float eps;
 };
 
-enum { kModeCausal = 0, kModeState = 1, kModeApply = 2 };
+enum { kModeCausal = 0, kModeState = 1 };
 
 hipError_t launch_chunk(int mode, int bf16, int D, int fm, int norm, const ChunkArgs& a, int grid,
                         hipStream_t st);
@@ -39,6 +39,25 @@ hipError_t launch_seg_prefix(float* ws_s, float* ws_z, const float* s_in, const 
                              int nseg, int D, int norm, hipStream_t st);
 hipError_t launch_seg_sum(float* ws_s, float* ws_z, int U, int nseg, int D, int norm,
                           hipStream_t st);
+
+// Non-causal readout with a fixed summed state (la_apply.hip).  Workgroup
+// blockIdx of unit u = blockIdx / seg_count handles the unit's 16-row query
+// blocks sg, sg + seg_count, ... (sg = blockIdx % seg_count); every wave of it
+// takes at most 16 of them, so seg_count must be apply_groups_per_unit(U, T).
+struct ApplyArgs {
+  const void* q;        // (B,T,H,D)
+  const uint8_t* mask;  // (B,T) or null
+  void* out;            // (B,T,H,D)
+  const float* s;       // summed S of unit u at s + u*s_u, [dk][dv]
+  const float* z;       // summed Z of unit u at z + u*z_u (with the normaliser)
+  int64_t s_u, z_u;
+  int32_t T, H;
+  int32_t seg_count;
+  float eps;
+};
+int apply_groups_per_unit(int64_t U, int64_t T);
+hipError_t launch_apply(int bf16, int D, int fm, int norm, const ApplyArgs& a, int grid,
+                        hipStream_t st);
 
 // T == 1 decode step (la_decode.hip).  q,k,v,out: (B,H,D); state (B,H,D,D)+(B,H,D).
 struct DecodeArgs {
