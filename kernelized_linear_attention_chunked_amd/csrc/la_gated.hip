@@ -69,15 +69,22 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
   constexpr int KN_BYTES = kChunk * KN_LD * ESZ;
   constexpr int VT_BYTES = D * VT_LD * ESZ;
   constexpr int SB_BYTES = OUT ? D * SB_LD * ESZ : 0;
+  // per-wave 16-row tiles through which q comes in and the outputs go out as
+  // whole rows (the MFMA layouts alone touch 16 rows per instruction), where
+  // LDS allows
+  constexpr int IO_BYTES_ = OUT ? NW * 16 * SB_LD * ESZ : 0;
+  constexpr bool STAGE_IO = OUT && (KN_BYTES + VT_BYTES + SB_BYTES + IO_BYTES_ + 16 <= 160 * 1024);
+  constexpr int IO_BYTES = STAGE_IO ? IO_BYTES_ : 0;
   constexpr int NS = NDT * NDT;
   constexpr int TPW = (NS + NW - 1) / NW;
   static_assert(NTOK >= 1 && NQ >= 1, "unsupported head size");
   static_assert(ESZ == 4 || NTOK % 2 == 0, "bf16 V^T writes pack token pairs");
 
-  __shared__ __align__(16) unsigned char smem[KN_BYTES + VT_BYTES + SB_BYTES + 16];
+  __shared__ __align__(16) unsigned char smem[KN_BYTES + VT_BYTES + SB_BYTES + IO_BYTES + 16];
   DT* Kn = (DT*)smem;
   DT* Vt = (DT*)(smem + KN_BYTES);
   DT* Sb = (DT*)(smem + KN_BYTES + VT_BYTES);
+  DT* Io = (DT*)(smem + KN_BYTES + VT_BYTES + SB_BYTES);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -173,19 +180,30 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
     // ignored, so that the load is unconditional
     pgr = load_g(gb ? gb + (int64_t)min(tb + l, T - 1) * Hkv : kb);
   };
-  // the wave's own query rows of its heads, used straight from these registers
+  // the wave's own query rows of its heads.  Staged: whole rows (piece g = 64n + l
+  // of a head's 16 x D block is row g / CB, 16-byte block g % CB), parked in the
+  // wave's tile when the head is computed; else straight in operand layout.
+  DT* io = Io + w * 16 * SB_LD;
   auto prefetch_q = [&](int c) {
     if constexpr (OUT) {
-      const int tok = min(c * kChunk + 16 * wr + lr, T - 1);
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
         const int hq = hp + P * hh;
 #pragma unroll
-        for (int m = 0; m < NQ; ++m)
-          pq[hh * NQ + m] = ld16(qb + (int64_t)tok * QS + hq * D + KB * m + VEC * lg);
+        for (int m = 0; m < NQ; ++m) {
+          if constexpr (STAGE_IO) {
+            const int g = 64 * m + l;
+            const int tok = min(c * kChunk + 16 * wr + g / CB, T - 1);
+            pq[hh * NQ + m] = ld16(qb + (int64_t)tok * QS + hq * D + (g % CB) * VEC);
+          } else {
+            const int tok = min(c * kChunk + 16 * wr + lr, T - 1);
+            pq[hh * NQ + m] = ld16(qb + (int64_t)tok * QS + hq * D + KB * m + VEC * lg);
+          }
+        }
       }
     }
   };
+  static_assert(!STAGE_IO || NQ * 64 == 16 * CB, "a head's 16 rows are NQ row-wise loads per lane");
 
   float bcs = 0.f;  // lane l: inclusive cumulative decay of token l of the chunk
   float seg_log = 0.f;
@@ -273,6 +291,20 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
       const int tok = c * kChunk + 16 * wr + lr;
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
+        // the head's queries in operand layout (row lr, dk KB*m + VEC*lg)
+        u32x4_t qop[NQ];
+        if constexpr (STAGE_IO) {
+#pragma unroll
+          for (int m = 0; m < NQ; ++m) {
+            const int g = 64 * m + l;
+            st16(io + sq_at(g / CB, (g % CB) * VEC), pq[hh * NQ + m]);
+          }
+#pragma unroll
+          for (int m = 0; m < NQ; ++m) qop[m] = ld16(io + sq_at(lr, KB * m + VEC * lg));
+        } else {
+#pragma unroll
+          for (int m = 0; m < NQ; ++m) qop[m] = pq[hh * NQ + m];
+        }
         f32x4_t at[NAT];
 #pragma unroll
         for (int t = 0; t < NAT; ++t) {
@@ -282,7 +314,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
 #pragma unroll
             for (int m = 0; m < NQ; ++m) {
               const u32x4_t kv = ld16(Kn + kn_at(krow, KB * m + VEC * lg));
-              O::mma(at[t], kv, pq[hh * NQ + m]);
+              O::mma(at[t], kv, qop[m]);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) at[t][q] *= fac[t][q];
@@ -298,7 +330,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
 #pragma unroll
           for (int ct = 0; ct < NDT; ++ct) {
             const u32x4_t av = ld16(Sb + sq_at(16 * ct + lr, KB * m + VEC * lg));
-            O::mma(nacc[ct], av, pq[hh * NQ + m]);
+            O::mma(nacc[ct], av, qop[m]);
           }
         }
 #pragma unroll
@@ -339,7 +371,21 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
             }
           }
         }
-        if (tok < T) {
+        if constexpr (STAGE_IO) {
+          // out through the tile (after the operand reads: one wave's LDS
+          // accesses stay in order), then whole rows to memory
+#pragma unroll
+          for (int ct = 0; ct < NDT; ++ct)
+            store4(io + sq_at(lr, 16 * ct + 4 * lg), scale * nacc[ct][0], scale * nacc[ct][1],
+                   scale * nacc[ct][2], scale * nacc[ct][3]);
+#pragma unroll
+          for (int m = 0; m < NQ; ++m) {
+            const int g = 64 * m + l;
+            const int row = c * kChunk + 16 * wr + g / CB;
+            const u32x4_t v = ld16(io + sq_at(g / CB, (g % CB) * VEC));
+            if (row < T) st16(ob + (int64_t)row * QS + (hp + P * hh) * D + (g % CB) * VEC, v);
+          }
+        } else if (tok < T) {
           DT* orow = ob + (int64_t)tok * QS + (hp + P * hh) * D + 4 * lg;
 #pragma unroll
           for (int ct = 0; ct < NDT; ++ct)
