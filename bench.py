@@ -211,7 +211,7 @@ def bench_streaming(args, log):
 
 def bench_other(args, log):
     """One extra line for a non-default workload: median step time over at least 20
-    timed steps after at least 3 warm-ups, tokens/s, algorithmic GB/s and the
+    timed steps after at least 3 warm-up steps and 0.3 s of warm-up, tokens/s, algorithmic GB/s and the
     dense-tile MFMA flops as a fraction of the bf16 peak.  The causal D=64
     workload fits the 256 MB Infinity Cache, so it is also timed cold, rotating
     over 8 input sets (about 0.54 GB)."""
@@ -225,8 +225,14 @@ def bench_other(args, log):
     E = lambda: torch.cuda.Event(enable_timing=True)
 
     def median_ms(drivers):
-        for i in range(warm):
+        # warm up for at least 0.3 s: the first few dozen steps of these short
+        # workloads run measurably slower than the steady state
+        t_w, i = time.perf_counter(), 0
+        while i < warm or time.perf_counter() - t_w < 0.3:
             drivers[i % len(drivers)].step()
+            i += 1
+            if i % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         ev = []
         for i in range(reps):
