@@ -45,7 +45,12 @@ typedef enum {
   LA_ERR_DEVICE = 8        /* the HIP runtime reported an error at launch */
 } la_status;
 
-typedef enum { LA_DT_F32 = 0, LA_DT_BF16 = 1 } la_dtype;
+/* Element type of q, k, v, decay and out.  Arithmetic is the same for both
+ * 16-bit types: they are widened to float32 for the feature map and rounded to
+ * bf16 for the matrix products, which accumulate in float32 (fp16 products
+ * would overflow on the running sums of long sequences); fp16 results are
+ * rounded to fp16 on the way out.  F32 computes in float32 throughout. */
+typedef enum { LA_DT_F32 = 0, LA_DT_BF16 = 1, LA_DT_F16 = 2 } la_dtype;
 
 /* phi: elu(x)+1 (x+1 for x>0, exp(x) otherwise), or relu(x)+eps with the same
  * eps as the denominator ("[Feature] LinearAttention layer for Keras", section

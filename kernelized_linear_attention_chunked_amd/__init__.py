@@ -39,7 +39,7 @@ EXPORTED_SYMBOLS = (
 )
 
 _FM = {"elu_plus_one": 0, "relu": 1}
-_DT = {torch.float32: 0, torch.bfloat16: 1}
+_DT = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
 _lock = threading.Lock()
 _lib = None

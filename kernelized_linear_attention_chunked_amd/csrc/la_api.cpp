@@ -105,9 +105,14 @@ size_t forward_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t D, int causal, 
   return (size_t)(U * p.nsplit * state_elems(D, norm) * 4);
 }
 
+static_assert(la::kIoF32 == LA_DT_F32 && la::kIoBF16 == LA_DT_BF16 && la::kIoF16 == LA_DT_F16,
+              "launcher I/O codes are the la_dtype values");
+bool dtype_ok(int32_t dtype) { return dtype == LA_DT_F32 || dtype == LA_DT_BF16 || dtype == LA_DT_F16; }
+int64_t dtype_size(int32_t dtype) { return dtype == LA_DT_F32 ? 4 : 2; }
+
 la_status check_common(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int32_t dtype) {
-  if (dtype != LA_DT_F32 && dtype != LA_DT_BF16)
-    return fail(LA_ERR_DTYPE, "dtype %d is not a supported floating type (0=f32, 1=bf16)", dtype);
+  if (!dtype_ok(dtype))
+    return fail(LA_ERR_DTYPE, "dtype %d is not a supported floating type (0=f32, 1=bf16, 2=f16)", dtype);
   if (B < 0 || T < 0 || H < 1 || Dk < 1 || Dv < 1)
     return fail(LA_ERR_SHAPE, "bad sizes B=%lld T=%lld H=%lld Dk=%lld Dv=%lld", (long long)B,
                 (long long)T, (long long)H, (long long)Dk, (long long)Dv);
@@ -176,7 +181,7 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
   const int norm = use_normalizer != 0;
   const int64_t D = Dk;
   const int64_t U = B * H;
-  const int64_t esz = dtype == LA_DT_BF16 ? 2 : 4;
+  const int64_t esz = dtype_size(dtype);
   const bool work = U > 0 && T > 0;
   if (work && (!q || !k || !v || !out)) return fail(LA_ERR_NULL_ARG, "q, k, v and out are required");
   if (!causal) {
@@ -225,7 +230,6 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
                 workspace ? workspace_bytes : (size_t)0);
 
   hipStream_t st = (hipStream_t)stream;
-  const int bf16 = dtype == LA_DT_BF16;
   const int Di = (int)D;
   hipError_t e = hipSuccess;
 
@@ -271,7 +275,7 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
       a.seg_first = 0;
       a.seg_chunks = (int32_t)p.nchunks;
       a.nseg_total = 1;
-      e = la::launch_chunk(la::kModeCausal, bf16, Di, feature_map, norm, a, (int)U, st);
+      e = la::launch_chunk(la::kModeCausal, dtype, Di, feature_map, norm, a, (int)U, st);
       return device_status(e, "la_forward (causal)");
     }
     // split sequence: partial states of segments 0..nseg-2 -> slots 1..nseg-1,
@@ -290,7 +294,7 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
     ps.seg_first = 0;
     ps.seg_chunks = (int32_t)p.seg_chunks;
     ps.nseg_total = (int32_t)p.nseg;
-    e = la::launch_chunk(la::kModeState, bf16, Di, feature_map, norm, ps, (int)(U * (p.nseg - 1)), st);
+    e = la::launch_chunk(la::kModeState, dtype, Di, feature_map, norm, ps, (int)(U * (p.nseg - 1)), st);
     if (e == hipSuccess)
       e = la::launch_seg_prefix(ws_s, ws_z, state_in_kv, state_in_k, (int)U, (int)p.nseg, Di, norm, st);
     if (e == hipSuccess) {
@@ -309,7 +313,7 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
       pc.seg_first = 0;
       pc.seg_chunks = (int32_t)p.seg_chunks;
       pc.nseg_total = (int32_t)p.nseg;
-      e = la::launch_chunk(la::kModeCausal, bf16, Di, feature_map, norm, pc, (int)(U * p.nseg), st);
+      e = la::launch_chunk(la::kModeCausal, dtype, Di, feature_map, norm, pc, (int)(U * p.nseg), st);
     }
     return device_status(e, "la_forward (causal, split)");
   }
@@ -330,7 +334,7 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
   pr.seg_first = 0;
   pr.seg_chunks = (int32_t)p.split_chunks;
   pr.nseg_total = (int32_t)p.nsplit;
-  e = la::launch_chunk(la::kModeState, bf16, Di, feature_map, norm, pr, (int)(U * p.nsplit), st);
+  e = la::launch_chunk(la::kModeState, dtype, Di, feature_map, norm, pr, (int)(U * p.nsplit), st);
   if (e == hipSuccess) e = la::launch_seg_sum(ws_s, ws_z, (int)U, (int)p.nsplit, Di, norm, st);
   if (e == hipSuccess) {
     la::ApplyArgs pa;
@@ -345,7 +349,7 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
     pa.H = a.H;
     pa.seg_count = la::apply_groups_per_unit(U, T);
     pa.eps = a.eps;
-    e = la::launch_apply(bf16, Di, feature_map, norm, pa, (int)(U * pa.seg_count), st);
+    e = la::launch_apply(dtype, Di, feature_map, norm, pa, (int)(U * pa.seg_count), st);
   }
   return device_status(e, "la_forward (non-causal)");
 }
@@ -362,7 +366,7 @@ LA_EXPORT la_status la_step(const void* q, const void* k, const void* v, const u
   if (!(eps >= 0.f) || isinf(eps)) return fail(LA_ERR_BAD_ARG, "eps must be finite and >= 0");
   const int norm = use_normalizer != 0;
   const int64_t D = Dk, U = B * H;
-  const int64_t esz = dtype == LA_DT_BF16 ? 2 : 4;
+  const int64_t esz = dtype_size(dtype);
   if (U == 0) return ok();
   if (!q || !k || !v || !out) return fail(LA_ERR_NULL_ARG, "q, k, v and out are required");
   if (!state_in_kv || !state_out_kv)
@@ -401,7 +405,7 @@ LA_EXPORT la_status la_step(const void* q, const void* k, const void* v, const u
   a.H = (int32_t)H;
   a.units = (int32_t)U;
   a.eps = eps;
-  hipError_t e = la::launch_decode(dtype == LA_DT_BF16, (int)D, feature_map, norm, a, (int)U,
+  hipError_t e = la::launch_decode(dtype, (int)D, feature_map, norm, a, (int)U,
                                    (hipStream_t)stream);
   return device_status(e, "la_step");
 }
@@ -436,8 +440,8 @@ size_t gated_ws_bytes(int64_t B, int64_t T, int64_t Hkv, int64_t D) {
 }
 la_status check_gated(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
                       int32_t dtype) {
-  if (dtype != LA_DT_F32 && dtype != LA_DT_BF16)
-    return fail(LA_ERR_DTYPE, "dtype %d is not a supported floating type (0=f32, 1=bf16)", dtype);
+  if (!dtype_ok(dtype))
+    return fail(LA_ERR_DTYPE, "dtype %d is not a supported floating type (0=f32, 1=bf16, 2=f16)", dtype);
   if (B < 0 || T < 0 || Hq < 1 || Hkv < 1 || Dk < 1 || Dv < 1)
     return fail(LA_ERR_SHAPE, "bad sizes");
   if (Hq % Hkv != 0)
@@ -474,7 +478,7 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
   if (s != LA_OK) return s;
   if (isnan(scale) || isinf(scale)) return fail(LA_ERR_BAD_ARG, "scale must be finite");
   const int64_t D = Dk, U = B * Hkv, G = Hq / Hkv;
-  const int64_t esz = dtype == LA_DT_BF16 ? 2 : 4;
+  const int64_t esz = dtype_size(dtype);
   if (U > 0 && !present_state) return fail(LA_ERR_NULL_ARG, "present_state is required");
   const bool work = U > 0 && T > 0;
   if (work && (!q || !k || !v || !out)) return fail(LA_ERR_NULL_ARG, "q, k, v and out are required");
@@ -500,7 +504,6 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
                 workspace ? workspace_bytes : (size_t)0);
   if (scale == 0.f) scale = 1.f / sqrtf((float)D);
   hipStream_t st = (hipStream_t)stream;
-  const int bf16 = dtype == LA_DT_BF16;
   hipError_t e = hipSuccess;
   if (!work) {
     if (U > 0)
@@ -531,7 +534,7 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
     a.seg_count = 1;
     a.seg_chunks = (int32_t)p.nchunks;
     a.nseg_total = 1;
-    e = la::launch_gated(la::kModeCausal, bf16, (int)D, (int)G, a, (int)U, st);
+    e = la::launch_gated(la::kModeCausal, dtype, (int)D, (int)G, a, (int)U, st);
     return device_status(e, "la_gated_forward");
   }
   float* ws_s = (float*)workspace;
@@ -545,7 +548,7 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
   ps.seg_count = (int32_t)(p.nseg - 1);
   ps.seg_chunks = (int32_t)p.seg_chunks;
   ps.nseg_total = (int32_t)p.nseg;
-  e = la::launch_gated(la::kModeState, bf16, (int)D, (int)G, ps, (int)(U * (p.nseg - 1)), st);
+  e = la::launch_gated(la::kModeState, dtype, (int)D, (int)G, ps, (int)(U * (p.nseg - 1)), st);
   if (e == hipSuccess)
     e = la::launch_gated_prefix(ws_s, ws_a, past_state, (int)U, (int)p.nseg, (int)D, st);
   if (e == hipSuccess) {
@@ -558,7 +561,7 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
     pc.seg_count = (int32_t)p.nseg;
     pc.seg_chunks = (int32_t)p.seg_chunks;
     pc.nseg_total = (int32_t)p.nseg;
-    e = la::launch_gated(la::kModeCausal, bf16, (int)D, (int)G, pc, (int)(U * p.nseg), st);
+    e = la::launch_gated(la::kModeCausal, dtype, (int)D, (int)G, pc, (int)(U * p.nseg), st);
   }
   return device_status(e, "la_gated_forward (split)");
 }

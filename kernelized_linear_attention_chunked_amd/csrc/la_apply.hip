@@ -27,8 +27,9 @@ constexpr int kApplyMaxBlocksPerWave = 16;  // liveness of a wave's blocks: one 
 constexpr int kApplyWaves = 8;
 constexpr int kApplyThreads = 64 * kApplyWaves;
 
-template <typename DT, int D, int FM, bool NORM, bool MASKED>
+template <typename IT, int D, int FM, bool NORM, bool MASKED>
 __global__ __launch_bounds__(kApplyThreads, 4) void apply_kernel(ApplyArgs a) {
+  using DT = typename Io<IT>::DT;  // operand type of the I/O type IT
   using O = Op<DT>;
   constexpr int VEC = O::VEC, KB = O::KB, ESZ = O::ESZ;
   constexpr int NDT = D / 16;
@@ -101,8 +102,8 @@ __global__ __launch_bounds__(kApplyThreads, 4) void apply_kernel(ApplyArgs a) {
     }
   }
 
-  const DT* qb = (const DT*)a.q + (int64_t)b * T * HD + (int64_t)h * D;
-  DT* ob = (DT*)a.out + (int64_t)b * T * HD + (int64_t)h * D;
+  const IT* qb = (const IT*)a.q + (int64_t)b * T * HD + (int64_t)h * D;
+  IT* ob = (IT*)a.out + (int64_t)b * T * HD + (int64_t)h * D;
   const uint8_t* const mb = MASKED ? a.mask + (int64_t)b * T : nullptr;
   const int nblk = (T + kApplyBlockRows - 1) / kApplyBlockRows;
   // block of the wave's i-th step (may lie past the end: then it is skipped)
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(kApplyThreads, 4) void apply_kernel(ApplyArgs a) {
     for (int n = 0; n < NLD; ++n) {
       const int g = 64 * n + l;
       float f[VEC];
-      O::unpack(q[n], f);
+      Io<IT>::unpack(q[n], f);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) f[e] = phi<FM>(f[e], a.eps);
       st16(stg + sq_at(g / CB, (g % CB) * VEC), O::pack(f));
@@ -187,8 +188,8 @@ __global__ __launch_bounds__(kApplyThreads, 4) void apply_kernel(ApplyArgs a) {
     const float rden = NORM ? 1.f / (nacc[NVT - 1][0] + a.eps) : 1.f;
 #pragma unroll
     for (int vt = 0; vt < NDT; ++vt)
-      store4(stg + sq_at(lr, 16 * vt + 4 * lg), ok ? nacc[vt][0] * rden : 0.f, ok ? nacc[vt][1] * rden : 0.f,
-             ok ? nacc[vt][2] * rden : 0.f, ok ? nacc[vt][3] * rden : 0.f);
+      store4((IT*)(stg + sq_at(lr, 16 * vt + 4 * lg)), ok ? nacc[vt][0] * rden : 0.f,
+             ok ? nacc[vt][1] * rden : 0.f, ok ? nacc[vt][2] * rden : 0.f, ok ? nacc[vt][3] * rden : 0.f);
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
       const int g = 64 * n + l;
@@ -207,31 +208,31 @@ __global__ __launch_bounds__(kApplyThreads, 4) void apply_kernel(ApplyArgs a) {
   }
 }
 
-template <typename DT, int D, int FM, bool NORM>
+template <typename IT, int D, int FM, bool NORM>
 static void launch_m(const ApplyArgs& a, int grid, hipStream_t st) {
   if (a.mask)
-    hipLaunchKernelGGL((apply_kernel<DT, D, FM, NORM, true>), dim3(grid), dim3(kApplyThreads), 0, st, a);
+    hipLaunchKernelGGL((apply_kernel<IT, D, FM, NORM, true>), dim3(grid), dim3(kApplyThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((apply_kernel<DT, D, FM, NORM, false>), dim3(grid), dim3(kApplyThreads), 0, st, a);
+    hipLaunchKernelGGL((apply_kernel<IT, D, FM, NORM, false>), dim3(grid), dim3(kApplyThreads), 0, st, a);
 }
 
-template <typename DT, int D>
+template <typename IT, int D>
 static void launch_fn(int fm, int norm, const ApplyArgs& a, int grid, hipStream_t st) {
   if (fm == kEluPlusOne) {
-    if (norm) launch_m<DT, D, kEluPlusOne, true>(a, grid, st);
-    else launch_m<DT, D, kEluPlusOne, false>(a, grid, st);
+    if (norm) launch_m<IT, D, kEluPlusOne, true>(a, grid, st);
+    else launch_m<IT, D, kEluPlusOne, false>(a, grid, st);
   } else {
-    if (norm) launch_m<DT, D, kReluEps, true>(a, grid, st);
-    else launch_m<DT, D, kReluEps, false>(a, grid, st);
+    if (norm) launch_m<IT, D, kReluEps, true>(a, grid, st);
+    else launch_m<IT, D, kReluEps, false>(a, grid, st);
   }
 }
 
-template <typename DT>
+template <typename IT>
 static void launch_d(int D, int fm, int norm, const ApplyArgs& a, int grid, hipStream_t st) {
   switch (D) {
-    case 32: launch_fn<DT, 32>(fm, norm, a, grid, st); break;
-    case 64: launch_fn<DT, 64>(fm, norm, a, grid, st); break;
-    default: launch_fn<DT, 128>(fm, norm, a, grid, st); break;
+    case 32: launch_fn<IT, 32>(fm, norm, a, grid, st); break;
+    case 64: launch_fn<IT, 64>(fm, norm, a, grid, st); break;
+    default: launch_fn<IT, 128>(fm, norm, a, grid, st); break;
   }
 }
 
@@ -248,13 +249,14 @@ int apply_groups_per_unit(int64_t U, int64_t T) {
   return (int)n;
 }
 
-hipError_t launch_apply(int bf16, int D, int fm, int norm, const ApplyArgs& a, int grid,
+hipError_t launch_apply(int io, int D, int fm, int norm, const ApplyArgs& a, int grid,
                         hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  if (bf16)
-    launch_d<uint16_t>(D, fm, norm, a, grid, st);
-  else
-    launch_d<float>(D, fm, norm, a, grid, st);
+  switch (io) {
+    case kIoBF16: launch_d<uint16_t>(D, fm, norm, a, grid, st); break;
+    case kIoF16: launch_d<f16_t>(D, fm, norm, a, grid, st); break;
+    default: launch_d<float>(D, fm, norm, a, grid, st); break;
+  }
   return hipGetLastError();
 }
 

@@ -59,9 +59,11 @@ struct ChunkOccupancy {
 };
 
 // MASKED: a (B,T) mask is given.  Unmasked launches carry no mask code at all.
-template <typename DT, int D, int FM, bool NORM, int MODE, bool MASKED>
-__global__ __launch_bounds__(64 * ChunkWaves<D>::NW, (ChunkOccupancy<DT, D, MODE>::value))
+// IT: the I/O element type (Io<IT>); DT: the operand type it is computed in.
+template <typename IT, int D, int FM, bool NORM, int MODE, bool MASKED>
+__global__ __launch_bounds__(64 * ChunkWaves<D>::NW, (ChunkOccupancy<IT, D, MODE>::value))
 void chunk_kernel(ChunkArgs a) {
+  using DT = typename Io<IT>::DT;
   using O = Op<DT>;
   constexpr int NW = ChunkWaves<D>::NW;            // wavefronts
   constexpr int NTH = 64 * NW;                     // threads
@@ -92,17 +94,23 @@ void chunk_kernel(ChunkArgs a) {
   constexpr int QS_BYTES = (USE_Q && QS_STAGE) ? kChunk * KN_LD * ESZ : 0;
   constexpr int VT_BYTES = USE_KV ? NVT * 16 * VT_LD * ESZ : 0;
   constexpr int SB_BYTES = USE_SB ? NVT * 16 * SB_LD * ESZ : 0;
+  // fp16 inputs: V is staged as hi + lo bf16 tiles (every fp16 value is the
+  // exact sum of two bf16 values), and each product with V takes one more MFMA
+  // with the lo tile, so that V reaches the products unrounded
+  constexpr bool VLO = !std::is_same_v<IT, DT>;
+  constexpr int VL_BYTES = (USE_KV && VLO) ? NDT * 16 * VT_LD * ESZ : 0;
   constexpr int NS = NDT * NVT;                    // 16x16 tiles of the (extended) state
   constexpr int TPW = (NS + NW - 1) / NW;          // state tiles per wave
   static_assert(NTOK >= 1 && NQ >= 1 && NDH * NH == NDT, "unsupported head size");
   static_assert(ESZ == 4 || NTOK % 2 == 0, "bf16 V^T writes pack token pairs");
   static_assert(SB_LD == KN_LD, "phi(Q) and S^T share one row layout");
 
-  __shared__ __align__(16) unsigned char smem[KN_BYTES + QS_BYTES + VT_BYTES + SB_BYTES + 16];
+  __shared__ __align__(16) unsigned char smem[KN_BYTES + QS_BYTES + VT_BYTES + SB_BYTES + VL_BYTES + 16];
   DT* Kn = (DT*)smem;
   DT* Qs = (DT*)(smem + KN_BYTES);
   DT* Vt = (DT*)(smem + KN_BYTES + QS_BYTES);
   DT* Sb = (DT*)(smem + KN_BYTES + QS_BYTES + VT_BYTES);
+  DT* Vl = (DT*)(smem + KN_BYTES + QS_BYTES + VT_BYTES + SB_BYTES);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -119,10 +127,10 @@ void chunk_kernel(ChunkArgs a) {
   const int c1 = min(c0 + a.seg_chunks, nchunks);
   const int HD = H * D;
   const int64_t unit_off = (int64_t)b * T * HD + (int64_t)h * D;
-  const DT* qb = (const DT*)a.q + unit_off;
-  const DT* kb = (const DT*)a.k + unit_off;
-  const DT* vb = (const DT*)a.v + unit_off;
-  DT* ob = (DT*)a.out + unit_off;
+  const IT* qb = (const IT*)a.q + unit_off;
+  const IT* kb = (const IT*)a.k + unit_off;
+  const IT* vb = (const IT*)a.v + unit_off;
+  IT* ob = (IT*)a.out + unit_off;
   const uint8_t* const mb = MASKED ? a.mask + (int64_t)b * T : nullptr;
   const float eps = a.eps;
   // global dv tile of the wave's i-th output tile
@@ -296,7 +304,7 @@ void chunk_kernel(ChunkArgs a) {
   // the packed words: a masked token must not reach anything, whatever its values)
   auto phi_vec = [&](const u32x4_t& raw, bool ok, auto full) {
     float f[VEC];
-    O::unpack(raw, f);
+    Io<IT>::unpack(raw, f);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) f[e] = phi<FM>(f[e], eps);
     u32x4_t r = O::pack(f);
@@ -305,6 +313,41 @@ void chunk_kernel(ChunkArgs a) {
       for (int e = 0; e < 4; ++e) r[e] = ok ? r[e] : 0u;
     }
     return r;
+  };
+
+  // V -> V^T [dv][token] (swizzled) at `base`: element e of every loaded vector
+  // goes to V^T row cb*VEC + e; the thread's NTOK consecutive tokens sit side by
+  // side (a thread's tokens may span several 16-byte blocks, which the swizzle
+  // does not keep adjacent: each group is addressed by itself)
+  auto write_vt = [&](DT* base, const u32x4_t (&src)[NTOK]) {
+    const int t0 = tg * NTOK;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const int r = cb * VEC + e;
+      if constexpr (ESZ == 2) {
+#pragma unroll
+        for (int n = 0; n < NTOK; n += 2) {
+          const uint32_t w0 = src[n][e >> 1], w1 = src[n + 1][e >> 1];
+          // low halves of both words for even e, high halves for odd e
+          *(uint32_t*)(base + vt_at(r, (t0 + n) / VEC) + (t0 + n) % VEC) =
+              (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u) : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+        }
+      } else {
+        float fv[NTOK];
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n) fv[n] = __uint_as_float(src[n][e]);
+        DT* p = base + vt_at(r, t0 / VEC) + (t0 % VEC);
+        if constexpr (NTOK == 1) {
+          *(float*)p = fv[0];
+        } else if constexpr (NTOK == 2) {
+          *(float2*)p = make_float2(fv[0], fv[1]);
+        } else {
+#pragma unroll
+          for (int n = 0; n < NTOK; n += 4)
+            *(f32x4_t*)(base + vt_at(r, (t0 + n) / VEC)) = f32x4_t{fv[n], fv[n + 1], fv[n + 2], fv[n + 3]};
+        }
+      }
+    }
   };
 
   // ---- stage: phi(K), phi(Q) -> [token][d] in LDS, V -> V^T [dv][token] (swizzled).
@@ -327,38 +370,23 @@ void chunk_kernel(ChunkArgs a) {
       if constexpr (USE_Q && QS_STAGE) st16(Qs + sq_at(t, cb * VEC), phi_vec(pq[n], ok, full));
     }
     if constexpr (USE_KV) {
-      // element e of every loaded vector goes to V^T row cb*VEC + e; the
-      // thread's NTOK consecutive tokens sit side by side in one block
-      const int t0 = tg * NTOK;
+      if constexpr (VLO) {
+        u32x4_t pl[NTOK];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const int r = cb * VEC + e;
-        // (a thread's tokens may span several 16-byte blocks, which the
-        // swizzle does not keep adjacent: each group is addressed by itself)
-        if constexpr (ESZ == 2) {
+        for (int n = 0; n < NTOK; ++n) {
+          float f[VEC];
+          Io<IT>::unpack(pv[n], f);
 #pragma unroll
-          for (int n = 0; n < NTOK; n += 2) {
-            const uint32_t w0 = pv[n][e >> 1], w1 = pv[n + 1][e >> 1];
-            // low halves of both words for even e, high halves for odd e
-            *(uint32_t*)(Vt + vt_at(r, (t0 + n) / VEC) + (t0 + n) % VEC) =
-                (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u) : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-          }
-        } else {
-          float fv[NTOK];
-#pragma unroll
-          for (int n = 0; n < NTOK; ++n) fv[n] = __uint_as_float(pv[n][e]);
-          DT* p = Vt + vt_at(r, t0 / VEC) + (t0 % VEC);
-          if constexpr (NTOK == 1) {
-            *(float*)p = fv[0];
-          } else if constexpr (NTOK == 2) {
-            *(float2*)p = make_float2(fv[0], fv[1]);
-          } else {
-#pragma unroll
-            for (int n = 0; n < NTOK; n += 4)
-              *(f32x4_t*)(Vt + vt_at(r, (t0 + n) / VEC)) = f32x4_t{fv[n], fv[n + 1], fv[n + 2], fv[n + 3]};
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t hw = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+            pv[n][i] = hw;
+            pl[n][i] = pack_bf16x2(f[2 * i] - __uint_as_float(hw << 16),
+                                   f[2 * i + 1] - __uint_as_float(hw & 0xffff0000u));
           }
         }
+        write_vt(Vl, pl);
       }
+      write_vt(Vt, pv);
     }
   };
 
@@ -380,6 +408,8 @@ void chunk_kernel(ChunkArgs a) {
   };
   // V^T operand (16-byte block `blk` of row 16*ct + lr)
   auto vt_op = [&](int ct, int blk) { return ld16(Vt + vt_at(16 * ct + lr, blk)); };
+  // its lo part (fp16 inputs; value tiles only, the normaliser's ones are exact)
+  auto vl_op = [&](int ct, int blk) { return ld16(Vl + vt_at(16 * ct + lr, blk)); };
 
   auto compute = [&](int c, bool live, bool full) {
     if (!live) {
@@ -387,7 +417,7 @@ void chunk_kernel(ChunkArgs a) {
       if constexpr (USE_Q) {
         const int tok = c * kChunk + 16 * qr + lr;
         if (tok < T) {
-          DT* orow = ob + (int64_t)tok * HD + 4 * lg;
+          IT* orow = ob + (int64_t)tok * HD + 4 * lg;
 #pragma unroll
           for (int i = 0; i < NDH; ++i) store4(orow + 16 * (hv * NDH + i), 0.f, 0.f, 0.f, 0.f);
         }
@@ -470,12 +500,20 @@ void chunk_kernel(ChunkArgs a) {
         u32x4_t av[NVW];
 #pragma unroll
         for (int i = 0; i < NVW; ++i) av[i] = vt_op(vtile(i), (KB / VEC) * p + lg);
+        u32x4_t avl[VLO ? NDH : 1];
+        if constexpr (VLO) {
+#pragma unroll
+          for (int i = 0; i < NDH; ++i) avl[i] = vl_op(vtile(i), (KB / VEC) * p + lg);
+        }
         if (intra) {
 #pragma unroll
           for (int i = 0; i < NVW; ++i) {
             if constexpr (ESZ == 2) {
               O::mma(nacc[i], av[i], bh[p]);
               O::mma(nacc[i], av[i], bl[p]);
+              if constexpr (VLO) {
+                if (i < NDH) O::mma(nacc[i], avl[i], bh[p]);
+              }
             } else {
 #pragma unroll
               for (int q = 0; q < 4; ++q)
@@ -490,6 +528,12 @@ void chunk_kernel(ChunkArgs a) {
 #pragma unroll
             for (int i = 0; i < NVW; ++i)
               if (hv == 0 || i < NDH) O::mma(sacc[j * NVW + i], kop[j][p], av[i]);
+          if constexpr (VLO) {
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+#pragma unroll
+              for (int i = 0; i < NDH; ++i) O::mma(sacc[j * NVW + i], kop[j][p], avl[i]);
+          }
         }
       }
       // epilogue: lane holds query 16qr + lr, value dims 16*vtile(i) + 4lg + (0..3)
@@ -499,7 +543,7 @@ void chunk_kernel(ChunkArgs a) {
         float rden = 1.f;
         if constexpr (NORM) rden = ok ? 1.f / (nacc[NDH][0] + eps) : 0.f;
         else rden = ok ? 1.f : 0.f;
-        DT* orow = ob + (int64_t)tok * HD + 4 * lg;
+        IT* orow = ob + (int64_t)tok * HD + 4 * lg;
 #pragma unroll
         for (int i = 0; i < NDH; ++i)
           store4(orow + 16 * (hv * NDH + i), nacc[i][0] * rden, nacc[i][1] * rden,
@@ -524,6 +568,12 @@ void chunk_kernel(ChunkArgs a) {
           for (int m = 0; m < NKS; ++m) bv[m] = vt_op(ct, (KB / VEC) * m + lg);
 #pragma unroll
           for (int m = 0; m < NKS; ++m) O::mma(sacc[k], kop[m], bv[m]);
+          if constexpr (VLO) {
+            if (ct < NDT) {
+#pragma unroll
+              for (int m = 0; m < NKS; ++m) O::mma(sacc[k], kop[m], vl_op(ct, (KB / VEC) * m + lg));
+            }
+          }
         }
       }
     }
@@ -638,47 +688,50 @@ __global__ __launch_bounds__(kThreads) void seg_sum_kernel(float* ws_s, float* w
 // ---------------------------------------------------------------------------
 // host-side launchers
 
-template <typename DT, int D, int FM, bool NORM, int MODE>
+template <typename IT, int D, int FM, bool NORM, int MODE>
 static hipError_t launch_one(const ChunkArgs& a, int grid, hipStream_t st) {
   if (a.mask)
-    hipLaunchKernelGGL((chunk_kernel<DT, D, FM, NORM, MODE, true>), dim3(grid),
+    hipLaunchKernelGGL((chunk_kernel<IT, D, FM, NORM, MODE, true>), dim3(grid),
                        dim3(64 * ChunkWaves<D>::NW), 0, st, a);
   else
-    hipLaunchKernelGGL((chunk_kernel<DT, D, FM, NORM, MODE, false>), dim3(grid),
+    hipLaunchKernelGGL((chunk_kernel<IT, D, FM, NORM, MODE, false>), dim3(grid),
                        dim3(64 * ChunkWaves<D>::NW), 0, st, a);
   return hipGetLastError();
 }
 
-template <typename DT, int D, int FM, bool NORM>
+template <typename IT, int D, int FM, bool NORM>
 static hipError_t launch_mode(int mode, const ChunkArgs& a, int grid, hipStream_t st) {
-  return mode == kCausal ? launch_one<DT, D, FM, NORM, kCausal>(a, grid, st)
-                         : launch_one<DT, D, FM, NORM, kState>(a, grid, st);
+  return mode == kCausal ? launch_one<IT, D, FM, NORM, kCausal>(a, grid, st)
+                         : launch_one<IT, D, FM, NORM, kState>(a, grid, st);
 }
 
-template <typename DT, int D>
+template <typename IT, int D>
 static hipError_t launch_d(int mode, int fm, int norm, const ChunkArgs& a, int grid, hipStream_t st) {
   if (fm == kEluPlusOne)
-    return norm ? launch_mode<DT, D, kEluPlusOne, true>(mode, a, grid, st)
-                : launch_mode<DT, D, kEluPlusOne, false>(mode, a, grid, st);
-  return norm ? launch_mode<DT, D, kReluEps, true>(mode, a, grid, st)
-              : launch_mode<DT, D, kReluEps, false>(mode, a, grid, st);
+    return norm ? launch_mode<IT, D, kEluPlusOne, true>(mode, a, grid, st)
+                : launch_mode<IT, D, kEluPlusOne, false>(mode, a, grid, st);
+  return norm ? launch_mode<IT, D, kReluEps, true>(mode, a, grid, st)
+              : launch_mode<IT, D, kReluEps, false>(mode, a, grid, st);
 }
 
-template <typename DT>
+template <typename IT>
 static hipError_t launch_dt(int mode, int D, int fm, int norm, const ChunkArgs& a, int grid,
                             hipStream_t st) {
   switch (D) {
-    case 32: return launch_d<DT, 32>(mode, fm, norm, a, grid, st);
-    case 64: return launch_d<DT, 64>(mode, fm, norm, a, grid, st);
-    default: return launch_d<DT, 128>(mode, fm, norm, a, grid, st);
+    case 32: return launch_d<IT, 32>(mode, fm, norm, a, grid, st);
+    case 64: return launch_d<IT, 64>(mode, fm, norm, a, grid, st);
+    default: return launch_d<IT, 128>(mode, fm, norm, a, grid, st);
   }
 }
 
-hipError_t launch_chunk(int mode, int bf16, int D, int fm, int norm, const ChunkArgs& a, int grid,
+hipError_t launch_chunk(int mode, int io, int D, int fm, int norm, const ChunkArgs& a, int grid,
                         hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  return bf16 ? launch_dt<uint16_t>(mode, D, fm, norm, a, grid, st)
-              : launch_dt<float>(mode, D, fm, norm, a, grid, st);
+  switch (io) {
+    case kIoBF16: return launch_dt<uint16_t>(mode, D, fm, norm, a, grid, st);
+    case kIoF16: return launch_dt<f16_t>(mode, D, fm, norm, a, grid, st);
+    default: return launch_dt<float>(mode, D, fm, norm, a, grid, st);
+  }
 }
 
 hipError_t launch_seg_prefix(float* ws_s, float* ws_z, const float* s_in, const float* z_in, int U,

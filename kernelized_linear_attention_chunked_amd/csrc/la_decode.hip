@@ -22,6 +22,10 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int i) {
   return bf16_bits_to_f32(p[i]);
 }
 template <>
+__device__ __forceinline__ float load_elem<f16_t>(const f16_t* p, int i) {
+  return (float)p[i];
+}
+template <>
 __device__ __forceinline__ float load_elem<float>(const float* p, int i) {
   return p[i];
 }
@@ -116,10 +120,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     if constexpr (NORM) y = y / den_s[ul];
     if (!valid) y = 0.f;
     DT* op = (DT*)a.out + (int64_t)u * D;
-    if constexpr (sizeof(DT) == 2)
-      ((uint16_t*)op)[tid] = (uint16_t)f32_to_bf16_bits(y);
+    if constexpr (std::is_same_v<DT, uint16_t>)
+      op[tid] = (uint16_t)f32_to_bf16_bits(y);
     else
-      ((float*)op)[tid] = y;
+      op[tid] = (DT)y;
   }
 }
 
@@ -167,11 +171,14 @@ static hipError_t launch_dt(int D, int fm, int norm, const DecodeArgs& a, int un
   }
 }
 
-hipError_t launch_decode(int bf16, int D, int fm, int norm, const DecodeArgs& a, int units,
+hipError_t launch_decode(int io, int D, int fm, int norm, const DecodeArgs& a, int units,
                          hipStream_t st) {
   if (units <= 0) return hipSuccess;
-  return bf16 ? launch_dt<uint16_t>(D, fm, norm, a, units, st)
-              : launch_dt<float>(D, fm, norm, a, units, st);
+  switch (io) {
+    case kIoBF16: return launch_dt<uint16_t>(D, fm, norm, a, units, st);
+    case kIoF16: return launch_dt<f16_t>(D, fm, norm, a, units, st);
+    default: return launch_dt<float>(D, fm, norm, a, units, st);
+  }
 }
 
 static int grid_for(int64_t n) {

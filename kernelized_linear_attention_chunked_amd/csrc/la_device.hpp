@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace la {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -131,6 +133,88 @@ struct Op<float> {
   }
 };
 
+// ---------------------------------------------------------------------------
+// I/O element types.  q, k, v, the decay and the outputs are bf16, fp16 or fp32
+// in memory; the MFMA operands are bf16 for both 16-bit types (an fp16 operand
+// would overflow on the running sums S and Z of long sequences) and fp32 for
+// fp32.  Io<IT> decodes 16-byte vectors of the I/O type to fp32, encodes fp32
+// results back, and converts a raw 16-byte vector to operand words.
+typedef _Float16 f16_t;
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+template <typename IT>
+struct Io;
+
+template <>
+struct Io<uint16_t> {  // bf16
+  using DT = uint16_t;
+  __device__ __forceinline__ static float to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+  __device__ __forceinline__ static uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+  __device__ __forceinline__ static void unpack(const u32x4_t& v, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static u32x4_t to_operand(const u32x4_t& v) { return v; }
+};
+
+template <>
+struct Io<f16_t> {  // fp16, fed to bf16 operands
+  using DT = uint16_t;
+  __device__ __forceinline__ static float to_f32(uint32_t bits16) {
+    return (float)__builtin_bit_cast(f16_t, (uint16_t)bits16);
+  }
+  __device__ __forceinline__ static uint32_t pack2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
+  }
+  // (the word is copied out of the vector before the bit cast: a bit cast
+  // applied to a vector element expression read element 0 whatever the index)
+  __device__ __forceinline__ static f32x2_t word_to_f32x2(uint32_t w) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
+  }
+  __device__ __forceinline__ static void unpack(const u32x4_t& v, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = v[i];
+      const f32x2_t x = word_to_f32x2(w);
+      f[2 * i] = x[0];
+      f[2 * i + 1] = x[1];
+    }
+  }
+  __device__ __forceinline__ static u32x4_t to_operand(const u32x4_t& v) {
+    u32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = v[i];
+      const f32x2_t x = word_to_f32x2(w);
+      r[i] = pack_bf16x2(x[0], x[1]);
+    }
+    return r;
+  }
+};
+
+template <>
+struct Io<float> {
+  using DT = float;
+  __device__ __forceinline__ static float to_f32(uint32_t bits) { return __uint_as_float(bits); }
+  __device__ __forceinline__ static void unpack(const u32x4_t& v, float (&f)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  }
+  __device__ __forceinline__ static u32x4_t to_operand(const u32x4_t& v) { return v; }
+};
+
+// 16x16x32 product of raw fp16 operands (8 values per lane, same lane layout
+// as the bf16 form), fp32 accumulation: the products are exact.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ void mma_f16(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                               acc, 0, 0, 0);
+}
+
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *(const u32x4_t*)p; }
 __device__ __forceinline__ void st16(void* p, const u32x4_t& v) { *(u32x4_t*)p = v; }
 
@@ -144,6 +228,12 @@ __device__ __forceinline__ void store4(uint16_t* p, float a, float b, float c, f
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
   f32x4_t v = {a, b, c, d};
   *(f32x4_t*)p = v;
+}
+__device__ __forceinline__ void store4(f16_t* p, float a, float b, float c, float d) {
+  u32x2_t v;
+  v[0] = Io<f16_t>::pack2(a, b);
+  v[1] = Io<f16_t>::pack2(c, d);
+  *(u32x2_t*)p = v;
 }
 
 }  // namespace la

@@ -29,17 +29,6 @@ struct GatedShape {
   static constexpr int HPW = G / P;         // query heads per wave
 };
 
-template <typename DT>
-__device__ __forceinline__ float ld_scalar(const DT* p);
-template <>
-__device__ __forceinline__ float ld_scalar<uint16_t>(const uint16_t* p) {
-  return bf16_bits_to_f32(*p);
-}
-template <>
-__device__ __forceinline__ float ld_scalar<float>(const float* p) {
-  return *p;
-}
-
 // The second bound is the minimum number of waves per SIMD: the bf16 state pass
 // of an 8-wave workgroup is held to 128 registers (two workgroups per CU).
 template <typename DT, int G, int MODE>
@@ -47,8 +36,10 @@ struct GatedOccupancy {
   static constexpr int value = (GatedShape<G>::NW == 8 && MODE != kModeCausal && sizeof(DT) == 2) ? 4 : 1;
 };
 
-template <typename DT, int D, int G, int MODE>
-__global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::value)) void gated_kernel(GatedArgs a) {
+// IT: the I/O element type (Io<IT>); DT: the operand type it is computed in.
+template <typename IT, int D, int G, int MODE>
+__global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::value)) void gated_kernel(GatedArgs a) {
+  using DT = typename Io<IT>::DT;
   using O = Op<DT>;
   using SH = GatedShape<G>;
   constexpr int P = SH::P, NW = SH::NW, NTH = SH::NTH, HPW = SH::HPW;
@@ -66,25 +57,33 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
   constexpr int VT_LD = kChunk;
   constexpr int SB_LD = D + PADE;
   constexpr bool OUT = MODE == kModeCausal;
+  // fp16 inputs: q and k stay fp16 for A = q k^T (an fp16 MFMA: exact products)
+  // and k is read exactly by the state update; V is staged as hi + lo bf16
+  // tiles (every fp16 value is the exact sum of two bf16 values) and each
+  // product with V takes one more MFMA with the lo tile.  Only the inter-chunk
+  // product q S rounds q to bf16, as S itself is.
+  constexpr bool VLO = !std::is_same_v<IT, DT>;
   constexpr int KN_BYTES = kChunk * KN_LD * ESZ;
   constexpr int VT_BYTES = D * VT_LD * ESZ;
+  constexpr int VL_BYTES = VLO ? D * VT_LD * ESZ : 0;
   constexpr int SB_BYTES = OUT ? D * SB_LD * ESZ : 0;
   // per-wave 16-row tiles through which q comes in and the outputs go out as
   // whole rows (the MFMA layouts alone touch 16 rows per instruction), where
   // LDS allows
   constexpr int IO_BYTES_ = OUT ? NW * 16 * SB_LD * ESZ : 0;
-  constexpr bool STAGE_IO = OUT && (KN_BYTES + VT_BYTES + SB_BYTES + IO_BYTES_ + 16 <= 160 * 1024);
+  constexpr bool STAGE_IO = OUT && (KN_BYTES + VT_BYTES + SB_BYTES + VL_BYTES + IO_BYTES_ + 16 <= 160 * 1024);
   constexpr int IO_BYTES = STAGE_IO ? IO_BYTES_ : 0;
   constexpr int NS = NDT * NDT;
   constexpr int TPW = (NS + NW - 1) / NW;
   static_assert(NTOK >= 1 && NQ >= 1, "unsupported head size");
   static_assert(ESZ == 4 || NTOK % 2 == 0, "bf16 V^T writes pack token pairs");
 
-  __shared__ __align__(16) unsigned char smem[KN_BYTES + VT_BYTES + SB_BYTES + IO_BYTES + 16];
-  DT* Kn = (DT*)smem;
+  __shared__ __align__(16) unsigned char smem[KN_BYTES + VT_BYTES + SB_BYTES + IO_BYTES + VL_BYTES + 16];
+  DT* Kn = (DT*)smem;  // k as loaded (bf16 or fp32 operands, or raw fp16)
   DT* Vt = (DT*)(smem + KN_BYTES);
   DT* Sb = (DT*)(smem + KN_BYTES + VT_BYTES);
-  DT* Io = (DT*)(smem + KN_BYTES + VT_BYTES + SB_BYTES);
+  DT* IoT = (DT*)(smem + KN_BYTES + VT_BYTES + SB_BYTES);
+  DT* Vl = (DT*)(smem + KN_BYTES + VT_BYTES + SB_BYTES + IO_BYTES);
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -98,11 +97,11 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
   const int c0 = s * a.seg_chunks;
   const int c1 = min(c0 + a.seg_chunks, nchunks);
   const int QS = Hq * D, KS = Hkv * D;  // token strides of q/out and k/v
-  const DT* qb = (const DT*)a.q + (int64_t)b * T * QS + (int64_t)(j * G) * D;
-  DT* ob = (DT*)a.out + (int64_t)b * T * QS + (int64_t)(j * G) * D;
-  const DT* kb = (const DT*)a.k + (int64_t)b * T * KS + (int64_t)j * D;
-  const DT* vb = (const DT*)a.v + (int64_t)b * T * KS + (int64_t)j * D;
-  const DT* gb = a.decay ? (const DT*)a.decay + (int64_t)b * T * Hkv + j : nullptr;
+  const IT* qb = (const IT*)a.q + (int64_t)b * T * QS + (int64_t)(j * G) * D;
+  IT* ob = (IT*)a.out + (int64_t)b * T * QS + (int64_t)(j * G) * D;
+  const IT* kb = (const IT*)a.k + (int64_t)b * T * KS + (int64_t)j * D;
+  const IT* vb = (const IT*)a.v + (int64_t)b * T * KS + (int64_t)j * D;
+  const IT* gb = a.decay ? (const IT*)a.decay + (int64_t)b * T * Hkv + j : nullptr;
   const float scale = a.scale;
   // LDS element offsets (layouts and swizzles of la_device.hpp)
   auto vt_at = [&](int r, int blk) { return r * VT_LD + ((blk ^ vt_swz(r)) * VEC); };
@@ -159,7 +158,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
   // reads a prefetched register before it is consumed: a select, copy or
   // conversion of a register still being loaded would make the load wait.
   uint32_t pgr = 0u;  // raw bits of the decay of token l of the chunk
-  auto load_g = [&](const DT* p) -> uint32_t {
+  auto load_g = [&](const IT* p) -> uint32_t {
     if constexpr (ESZ == 2)
       return (uint32_t)*(const uint16_t*)p;
     else
@@ -183,7 +182,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
   // the wave's own query rows of its heads.  Staged: whole rows (piece g = 64n + l
   // of a head's 16 x D block is row g / CB, 16-byte block g % CB), parked in the
   // wave's tile when the head is computed; else straight in operand layout.
-  DT* io = Io + w * 16 * SB_LD;
+  DT* io = IoT + w * 16 * SB_LD;
   auto prefetch_q = [&](int c) {
     if constexpr (OUT) {
 #pragma unroll
@@ -205,6 +204,41 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
   };
   static_assert(!STAGE_IO || NQ * 64 == 16 * CB, "a head's 16 rows are NQ row-wise loads per lane");
 
+  // V -> V^T [dv][token] (swizzled) at `base`: element e of every loaded vector
+  // goes to V^T row cb*VEC + e; the thread's NTOK consecutive tokens sit side by
+  // side (a thread's tokens may span several 16-byte blocks, which the swizzle
+  // does not keep adjacent: each group is addressed by itself)
+  auto write_vt = [&](DT* base, const u32x4_t (&src)[NTOK]) {
+    const int t0 = tg * NTOK;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const int r = cb * VEC + e;
+      if constexpr (ESZ == 2) {
+#pragma unroll
+        for (int n = 0; n < NTOK; n += 2) {
+          const uint32_t w0 = src[n][e >> 1], w1 = src[n + 1][e >> 1];
+          // low halves of both words for even e, high halves for odd e
+          *(uint32_t*)(base + vt_at(r, (t0 + n) / VEC) + (t0 + n) % VEC) =
+              (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u) : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+        }
+      } else {
+        float fv[NTOK];
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n) fv[n] = __uint_as_float(src[n][e]);
+        DT* p = base + vt_at(r, t0 / VEC) + (t0 % VEC);
+        if constexpr (NTOK == 1) {
+          *(float*)p = fv[0];
+        } else if constexpr (NTOK == 2) {
+          *(float2*)p = make_float2(fv[0], fv[1]);
+        } else {
+#pragma unroll
+          for (int n = 0; n < NTOK; n += 4)
+            *(f32x4_t*)(base + vt_at(r, (t0 + n) / VEC)) = f32x4_t{fv[n], fv[n + 1], fv[n + 2], fv[n + 3]};
+        }
+      }
+    }
+  };
+
   float bcs = 0.f;  // lane l: inclusive cumulative decay of token l of the chunk
   float seg_log = 0.f;
   auto stage = [&](int c) {
@@ -221,41 +255,26 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
     if (loader) {
 #pragma unroll
       for (int n = 0; n < NTOK; ++n) st16(Kn + kn_at(tg * NTOK + n, cb * VEC), pk[n]);
-      // element e of every loaded vector goes to V^T row cb*VEC + e; the
-      // thread's NTOK consecutive tokens sit side by side in one 16-byte block
-      const int t0 = tg * NTOK;
+      if constexpr (VLO) {
+        u32x4_t pl[NTOK];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const int r = cb * VEC + e;
-        // (a thread's tokens may span several 16-byte blocks, which the
-        // swizzle does not keep adjacent: each group is addressed by itself)
-        if constexpr (ESZ == 2) {
+        for (int n = 0; n < NTOK; ++n) {
+          float f[VEC];
+          Io<IT>::unpack(pv[n], f);
 #pragma unroll
-          for (int n = 0; n < NTOK; n += 2) {
-            const uint32_t w0 = pv[n][e >> 1], w1 = pv[n + 1][e >> 1];
-            // low halves of both words for even e, high halves for odd e
-            *(uint32_t*)(Vt + vt_at(r, (t0 + n) / VEC) + (t0 + n) % VEC) =
-                (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u) : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-          }
-        } else {
-          float fv[NTOK];
-#pragma unroll
-          for (int n = 0; n < NTOK; ++n) fv[n] = __uint_as_float(pv[n][e]);
-          DT* p = Vt + vt_at(r, t0 / VEC) + (t0 % VEC);
-          if constexpr (NTOK == 1) {
-            *(float*)p = fv[0];
-          } else if constexpr (NTOK == 2) {
-            *(float2*)p = make_float2(fv[0], fv[1]);
-          } else {
-#pragma unroll
-            for (int n = 0; n < NTOK; n += 4)
-              *(f32x4_t*)(Vt + vt_at(r, (t0 + n) / VEC)) = f32x4_t{fv[n], fv[n + 1], fv[n + 2], fv[n + 3]};
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t hw = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+            pv[n][i] = hw;
+            pl[n][i] = pack_bf16x2(f[2 * i] - __uint_as_float(hw << 16),
+                                   f[2 * i + 1] - __uint_as_float(hw & 0xffff0000u));
           }
         }
+        write_vt(Vl, pl);
       }
+      write_vt(Vt, pv);
     }
     // inclusive scan of the chunk's decays across the wave (each wave keeps its own copy)
-    float x = (gb && tb + l < T) ? (ESZ == 2 ? bf16_bits_to_f32(pgr) : __uint_as_float(pgr)) : 0.f;
+    float x = (gb && tb + l < T) ? Io<IT>::to_f32(pgr) : 0.f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(x, off);
@@ -273,25 +292,35 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
       // permuted rows (element q of tile (p, odd) is key 32p + 8lg + 4odd + q,
       // so that lane group lg holds keys 32p + 8lg + (0..7): one 16-byte V^T
       // read per value tile); fp32 uses single key tiles (key 16jt + 4lg + q).
-      // fac: the decay factor exp(b_i - b_j) of each element, 0 above the diagonal.
+      // Each element carries the decay factor exp(b_i - b_j), 0 above the
+      // diagonal.  With fp16 inputs (whose V lo tile adds to the live registers)
+      // a tile is formed right before its product with V, so that few are live
+      // at once; otherwise all are formed first, which schedules better.
+      constexpr bool LATE_A = VLO;
       constexpr int NAT = 4;
+      auto need = [&](int t) { return ESZ == 2 ? (32 * (t >> 1) <= 16 * wr + 15) : (t <= wr); };
       auto key_of = [&](int t, int q) {
         return ESZ == 2 ? 32 * (t >> 1) + 8 * lg + 4 * (t & 1) + q : 16 * t + 4 * lg + q;
       };
-      auto need = [&](int t) { return ESZ == 2 ? (32 * (t >> 1) <= 16 * wr + 15) : (t <= wr); };
-      float fac[NAT][4];
+      // decay factor of element q of tile t (computed once per chunk, for all
+      // heads, where the tiles are formed early)
+      auto fac_of = [&](int t, int q) {
+        const int key = key_of(t, q);
+        const float bj = __shfl(bcs, key);
+        return key <= 16 * wr + lr ? __expf(bi - bj) : 0.f;
+      };
+      float fac[LATE_A ? 1 : NAT][4];
+      if constexpr (!LATE_A) {
 #pragma unroll
-      for (int t = 0; t < NAT; ++t)
+        for (int t = 0; t < NAT; ++t)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int key = key_of(t, q);
-          const float bj = __shfl(bcs, key);
-          fac[t][q] = key <= 16 * wr + lr ? __expf(bi - bj) : 0.f;
-        }
+          for (int q = 0; q < 4; ++q) fac[t][q] = fac_of(t, q);
+      }
       const int tok = c * kChunk + 16 * wr + lr;
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
-        // the head's queries in operand layout (row lr, dk KB*m + VEC*lg)
+        // the head's queries in operand layout (row lr, dk KB*m + VEC*lg), as
+        // loaded (raw fp16 for fp16 inputs)
         u32x4_t qop[NQ];
         if constexpr (STAGE_IO) {
 #pragma unroll
@@ -305,20 +334,26 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
 #pragma unroll
           for (int m = 0; m < NQ; ++m) qop[m] = pq[hh * NQ + m];
         }
-        f32x4_t at[NAT];
+        // decayed A^T tile t (keys as above) of this head
+        auto a_tile = [&](int t) {
+          f32x4_t at = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          const int krow = ESZ == 2 ? 32 * (t >> 1) + 8 * (lr >> 2) + 4 * (t & 1) + (lr & 3) : 16 * t + lr;
 #pragma unroll
-        for (int t = 0; t < NAT; ++t) {
-          at[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          if (need(t)) {
-            const int krow = ESZ == 2 ? 32 * (t >> 1) + 8 * (lr >> 2) + 4 * (t & 1) + (lr & 3) : 16 * t + lr;
-#pragma unroll
-            for (int m = 0; m < NQ; ++m) {
-              const u32x4_t kv = ld16(Kn + kn_at(krow, KB * m + VEC * lg));
-              O::mma(at[t], kv, qop[m]);
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) at[t][q] *= fac[t][q];
+          for (int m = 0; m < NQ; ++m) {
+            const u32x4_t kv = ld16(Kn + kn_at(krow, KB * m + VEC * lg));
+            if constexpr (VLO)
+              mma_f16(at, kv, qop[m]);
+            else
+              O::mma(at, kv, qop[m]);
           }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) at[q] *= LATE_A ? fac_of(t, q) : fac[LATE_A ? 0 : t][q];
+          return at;
+        };
+        f32x4_t at_early[LATE_A ? 1 : NAT];
+        if constexpr (!LATE_A) {
+#pragma unroll
+          for (int t = 0; t < NAT; ++t) at_early[t] = need(t) ? a_tile(t) : f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
         // inter-chunk term first, with the exact query; lane's column is its own
         // query i, so exp(b_i) is applied per lane to the accumulators.
@@ -327,10 +362,12 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
         for (int ct = 0; ct < NDT; ++ct) nacc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < NQ; ++m) {
+          // (an fp16 query becomes a bf16 operand here, like S)
+          const u32x4_t qb = VLO ? Io<IT>::to_operand(qop[m]) : qop[m];
 #pragma unroll
           for (int ct = 0; ct < NDT; ++ct) {
             const u32x4_t av = ld16(Sb + sq_at(16 * ct + lr, KB * m + VEC * lg));
-            O::mma(nacc[ct], av, qop[m]);
+            O::mma(nacc[ct], av, qb);
           }
         }
 #pragma unroll
@@ -339,11 +376,14 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             if (need(2 * p)) {
+              const f32x4_t at0 = LATE_A ? a_tile(2 * p) : at_early[LATE_A ? 0 : 2 * p];
+              const f32x4_t at1 = LATE_A ? a_tile(2 * p + 1) : at_early[LATE_A ? 0 : 2 * p + 1];
               // the terms of A V cancel, so A carries its bf16 rounding residual too
               u32x4_t bh, bl;
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const float x0 = at[2 * p + (e >> 1)][2 * (e & 1)], x1 = at[2 * p + (e >> 1)][2 * (e & 1) + 1];
+                const f32x4_t& at = (e >> 1) ? at1 : at0;
+                const float x0 = at[2 * (e & 1)], x1 = at[2 * (e & 1) + 1];
                 const uint32_t hw = pack_bf16x2(x0, x1);
                 bh[e] = hw;
                 bl[e] = pack_bf16x2(x0 - __uint_as_float(hw << 16), x1 - __uint_as_float(hw & 0xffff0000u));
@@ -353,20 +393,21 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
                 const u32x4_t av = ld16(Vt + vt_at(16 * ct + lr, 4 * p + lg));
                 O::mma(nacc[ct], av, bh);
                 O::mma(nacc[ct], av, bl);
+                if constexpr (VLO) O::mma(nacc[ct], ld16(Vl + vt_at(16 * ct + lr, 4 * p + lg)), bh);
               }
             }
           }
         } else {
 #pragma unroll
           for (int jt = 0; jt < 4; ++jt) {
-            if (jt <= wr) {
+            if (need(jt)) {
+              const f32x4_t at = LATE_A ? a_tile(jt) : at_early[LATE_A ? 0 : jt];
 #pragma unroll
               for (int ct = 0; ct < NDT; ++ct) {
                 const u32x4_t av = ld16(Vt + vt_at(16 * ct + lr, 4 * jt + lg));
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                  nacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av[q]), at[jt][q],
-                                                                  nacc[ct], 0, 0, 0);
+                  nacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av[q]), at[q], nacc[ct], 0, 0, 0);
               }
             }
           }
@@ -376,7 +417,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
           // accesses stay in order), then whole rows to memory
 #pragma unroll
           for (int ct = 0; ct < NDT; ++ct)
-            store4(io + sq_at(lr, 16 * ct + 4 * lg), scale * nacc[ct][0], scale * nacc[ct][1],
+            store4((IT*)(io + sq_at(lr, 16 * ct + 4 * lg)), scale * nacc[ct][0], scale * nacc[ct][1],
                    scale * nacc[ct][2], scale * nacc[ct][3]);
 #pragma unroll
           for (int m = 0; m < NQ; ++m) {
@@ -386,7 +427,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
             if (row < T) st16(ob + (int64_t)row * QS + (hp + P * hh) * D + (g % CB) * VEC, v);
           }
         } else if (tok < T) {
-          DT* orow = ob + (int64_t)tok * QS + (hp + P * hh) * D + 4 * lg;
+          IT* orow = ob + (int64_t)tok * QS + (hp + P * hh) * D + 4 * lg;
 #pragma unroll
           for (int ct = 0; ct < NDT; ++ct)
             store4(orow + 16 * ct, scale * nacc[ct][0], scale * nacc[ct][1], scale * nacc[ct][2],
@@ -423,7 +464,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
               for (int e = 0; e < VEC; ++e) {
                 const int off = kn_at(KB * m + VEC * lg + e, 16 * rt + lr);
                 if constexpr (ESZ == 2)
-                  f[e] = bf16_bits_to_f32(((const uint16_t*)Kn)[off]) * kw[m][e];
+                  f[e] = Io<IT>::to_f32(((const uint16_t*)Kn)[off]) * kw[m][e];
                 else
                   f[e] = ((const float*)Kn)[off] * kw[m][e];
               }
@@ -445,6 +486,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<DT, G, MODE>::v
             const u32x4_t bv = ld16(Vt + vt_at(16 * ct + lr, (KB / VEC) * m + lg));
             O::mma(sacc[i], kop[m], bv);
             if constexpr (ESZ == 2) O::mma(sacc[i], kol[m], bv);
+            if constexpr (VLO) O::mma(sacc[i], kop[m], ld16(Vl + vt_at(16 * ct + lr, (KB / VEC) * m + lg)));
           }
         }
       }
@@ -505,40 +547,43 @@ __global__ __launch_bounds__(kThreads) void gated_prefix_kernel(float* ws_s, con
   }
 }
 
-template <typename DT, int D, int G>
+template <typename IT, int D, int G>
 static hipError_t launch_g(int mode, const GatedArgs& a, int grid, hipStream_t st) {
   constexpr int NTH = GatedShape<G>::NTH;
   if (mode == kModeCausal)
-    hipLaunchKernelGGL((gated_kernel<DT, D, G, kModeCausal>), dim3(grid), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((gated_kernel<IT, D, G, kModeCausal>), dim3(grid), dim3(NTH), 0, st, a);
   else
-    hipLaunchKernelGGL((gated_kernel<DT, D, G, kModeState>), dim3(grid), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((gated_kernel<IT, D, G, kModeState>), dim3(grid), dim3(NTH), 0, st, a);
   return hipGetLastError();
 }
 
-template <typename DT, int D>
+template <typename IT, int D>
 static hipError_t launch_gd(int mode, int G, const GatedArgs& a, int grid, hipStream_t st) {
   switch (G) {
-    case 1: return launch_g<DT, D, 1>(mode, a, grid, st);
-    case 2: return launch_g<DT, D, 2>(mode, a, grid, st);
-    case 4: return launch_g<DT, D, 4>(mode, a, grid, st);
-    default: return launch_g<DT, D, 8>(mode, a, grid, st);
+    case 1: return launch_g<IT, D, 1>(mode, a, grid, st);
+    case 2: return launch_g<IT, D, 2>(mode, a, grid, st);
+    case 4: return launch_g<IT, D, 4>(mode, a, grid, st);
+    default: return launch_g<IT, D, 8>(mode, a, grid, st);
   }
 }
 
-template <typename DT>
+template <typename IT>
 static hipError_t launch_gdt(int mode, int D, int G, const GatedArgs& a, int grid, hipStream_t st) {
   switch (D) {
-    case 32: return launch_gd<DT, 32>(mode, G, a, grid, st);
-    case 64: return launch_gd<DT, 64>(mode, G, a, grid, st);
-    default: return launch_gd<DT, 128>(mode, G, a, grid, st);
+    case 32: return launch_gd<IT, 32>(mode, G, a, grid, st);
+    case 64: return launch_gd<IT, 64>(mode, G, a, grid, st);
+    default: return launch_gd<IT, 128>(mode, G, a, grid, st);
   }
 }
 
-hipError_t launch_gated(int mode, int bf16, int D, int G, const GatedArgs& a, int grid,
+hipError_t launch_gated(int mode, int io, int D, int G, const GatedArgs& a, int grid,
                         hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  return bf16 ? launch_gdt<uint16_t>(mode, D, G, a, grid, st)
-              : launch_gdt<float>(mode, D, G, a, grid, st);
+  switch (io) {
+    case kIoBF16: return launch_gdt<uint16_t>(mode, D, G, a, grid, st);
+    case kIoF16: return launch_gdt<f16_t>(mode, D, G, a, grid, st);
+    default: return launch_gdt<float>(mode, D, G, a, grid, st);
+  }
 }
 
 hipError_t launch_gated_prefix(float* ws_s, const float* ws_a, const float* s_in, int U, int nseg,

@@ -32,8 +32,10 @@ struct ChunkArgs {
 };
 
 enum { kModeCausal = 0, kModeState = 1 };
+// I/O element type codes of the launchers (the values of la_dtype)
+enum { kIoF32 = 0, kIoBF16 = 1, kIoF16 = 2 };
 
-hipError_t launch_chunk(int mode, int bf16, int D, int fm, int norm, const ChunkArgs& a, int grid,
+hipError_t launch_chunk(int mode, int io, int D, int fm, int norm, const ChunkArgs& a, int grid,
                         hipStream_t st);
 hipError_t launch_seg_prefix(float* ws_s, float* ws_z, const float* s_in, const float* z_in, int U,
                              int nseg, int D, int norm, hipStream_t st);
@@ -56,7 +58,7 @@ struct ApplyArgs {
   float eps;
 };
 int apply_groups_per_unit(int64_t U, int64_t T);
-hipError_t launch_apply(int bf16, int D, int fm, int norm, const ApplyArgs& a, int grid,
+hipError_t launch_apply(int io, int D, int fm, int norm, const ApplyArgs& a, int grid,
                         hipStream_t st);
 
 // T == 1 decode step (la_decode.hip).  q,k,v,out: (B,H,D); state (B,H,D,D)+(B,H,D).
@@ -74,7 +76,7 @@ struct DecodeArgs {
   int32_t units;  // B*H
   float eps;
 };
-hipError_t launch_decode(int bf16, int D, int fm, int norm, const DecodeArgs& a, int units,
+hipError_t launch_decode(int io, int D, int fm, int norm, const DecodeArgs& a, int units,
                          hipStream_t st);
 
 // Zero fill (la_decode.hip).
@@ -98,7 +100,7 @@ struct GatedArgs {
   int32_t seg_count, seg_first, seg_chunks, nseg_total;
   float scale;
 };
-hipError_t launch_gated(int mode, int bf16, int D, int G, const GatedArgs& a, int grid,
+hipError_t launch_gated(int mode, int io, int D, int G, const GatedArgs& a, int grid,
                         hipStream_t st);
 hipError_t launch_gated_prefix(float* ws_s, const float* ws_a, const float* s_in, int U, int nseg,
                                int D, hipStream_t st);

@@ -3,8 +3,9 @@ import numpy as np
 import torch
 
 # Tolerances on the floored relative error below: 1e-4 for fp32 inputs and 2e-2
-# for bf16 inputs with fp32 state.
-TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+# for bf16 and fp16 inputs with fp32 state (both 16-bit types reach the matrix
+# products as bf16, whose rounding dominates the error).
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2, torch.float16: 2e-2}
 
 
 def f64(t):

@@ -105,6 +105,12 @@ def test_workspace_sizes(lib):
     assert lib.la_workspace_size(4, 0, 16, 128, 128, 1, 0, ctypes.byref(n)) == OK
     assert n.value == 0
     assert lib.la_workspace_size(4, 16, 16, 128, 128, 9, 0, ctypes.byref(n)) == DTYPE
+    # the workspace holds fp32 state partials: the same for every I/O dtype
+    for dt in (0, 2):
+        m = ctypes.c_size_t(0)
+        assert lib.la_workspace_size(4, 16384, 16, 128, 128, dt, 0, ctypes.byref(m)) == OK
+        assert m.value == 64 * 8 * (128 * 128 + 128) * 4
+    assert lib.la_workspace_size(4, 16, 16, 128, 128, 3, 0, ctypes.byref(n)) == DTYPE
     assert lib.la_workspace_size(4, 16, 16, 128, 128, 1, 0, None) == NULL_ARG
 
 

@@ -3,7 +3,7 @@ still span several 64-token chunks, a ragged tail, split sequences and the
 single-pass path.  Every call goes through the C ABI (via the ctypes binding).
 
 Tolerance: floored relative error (tests/_util.py) <= 1e-4 for fp32 inputs,
-<= 2e-2 for bf16 inputs with fp32 state."""
+<= 2e-2 for bf16 and fp16 inputs with fp32 state."""
 import json
 import os
 
@@ -19,7 +19,8 @@ from _util import TOL, assert_close, f64
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-DTYPES = [torch.float32, torch.bfloat16]
+DTYPES = [torch.float32, torch.bfloat16, torch.float16]
+DT_IDS = ["f32", "bf16", "f16"]
 FMS = ["elu_plus_one", "relu"]
 
 
@@ -34,7 +35,7 @@ def _state(B, H, D, seed):
     return S.to(DEV), Z.to(DEV)
 
 
-@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("fm", FMS)
 @pytest.mark.parametrize("norm", [True, False], ids=["norm", "nonorm"])
@@ -60,7 +61,7 @@ def test_causal_small(dtype, D, fm, norm):
     assert np.all(f64(y)[~m] == 0.0)
 
 
-@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("D", [64, 128])
 def test_causal_single_pass_path(dtype, D):
     # 512 (batch, head) units: one pass, state carried across all chunks in a workgroup
@@ -102,7 +103,7 @@ def test_causal_zero_length_passes_state_through():
     assert torch.count_nonzero(S) == 0 and torch.count_nonzero(Z) == 0
 
 
-@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("fm", FMS)
 def test_masked_garbage_does_not_leak(dtype, fm):
     B, T, H, D = 2, 150, 2, 64
@@ -122,7 +123,7 @@ def test_masked_garbage_does_not_leak(dtype, fm):
     assert torch.all(y2[bad] == 0) and torch.all(y3[bad] == 0)
 
 
-@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
 def test_fully_masked_chunks(dtype, D, causal):
@@ -171,7 +172,7 @@ def test_all_false_and_all_true_masks():
     assert torch.equal(ya, yb)
 
 
-@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("fm", FMS)
 @pytest.mark.parametrize("norm", [True, False], ids=["norm", "nonorm"])
@@ -187,7 +188,7 @@ def test_noncausal_small(dtype, D, fm, norm):
     assert torch.all(y[~mask] == 0)
 
 
-@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("fm", FMS)
 @pytest.mark.parametrize("norm", [True, False], ids=["norm", "nonorm"])
@@ -214,7 +215,7 @@ def test_decode_step(dtype, D, fm, norm, in_place):
         assert S.data_ptr() == s_kv.data_ptr()
 
 
-@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 def test_chunked_and_step_equal_full(dtype):
     B, T, H, D = 2, 320, 4, 64
     q, k, v = _inputs(B, T, H, D, dtype, 77)
@@ -248,7 +249,7 @@ def test_initial_state_is_zero():
 
 
 # ------------------------------------------------------------------ gated / GQA
-@pytest.mark.parametrize("dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("gated", [True, False], ids=["gated", "linear"])
