@@ -134,6 +134,22 @@ la_status la_gated_forward(const void* q, const void* k, const void* v, const vo
                            int32_t dtype, float scale, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* One token of the gated / linear recurrence with grouped-query heads: the
+ * T == 1 case of la_gated_forward, as a decode step that streams the fp32 state
+ * once (the LinearAttention operator page, "Description": the recurrence is
+ * token-by-token; its decode example is a single token with a past state):
+ *   S' = exp(g) S + k v^T   (per kv head),   o = scale q^T S'   (per query head).
+ * q (B, Hq*Dk), k (B, Hkv*Dk), v (B, Hkv*Dv), out (B, Hq*Dv) in `dtype`;
+ * decay (B, Hkv) in `dtype`, log-space (NULL = all zero);
+ * past_state (B,Hkv,Dk,Dv) float32 (NULL = zeros); present_state (same shape,
+ * float32) is always written and may alias past_state exactly (in-place step).
+ * The states must be 16-byte aligned.  scale == 0 means 1/sqrt(Dk).  Sizes,
+ * dtypes and errors as la_gated_forward; no workspace. */
+la_status la_gated_step(const void* q, const void* k, const void* v, const void* decay,
+                        const float* past_state, float* present_state, void* out, int64_t B,
+                        int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv, int32_t dtype, float scale,
+                        void* stream);
+
 /* Static string naming a status code. */
 const char* la_status_string(la_status s);
 

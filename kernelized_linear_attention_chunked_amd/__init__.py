@@ -16,6 +16,7 @@ Functions carry the C names:
 * :func:`la_step` -- one T=1 causal decode step.
 * :func:`la_gated_forward` -- gated / linear recurrence with GQA (the
   LinearAttention operator page, ai.onnx since version 27).
+* :func:`la_gated_step` -- one token of that recurrence (decode).
 """
 from __future__ import annotations
 
@@ -29,13 +30,13 @@ from .build import LIB_PATH, build as _build
 
 __all__ = [
     "LinAttnError", "la_initial_state", "la_forward", "la_step", "la_gated_forward",
-    "la_workspace_size", "la_gated_workspace_size", "library_path", "load_library",
+    "la_gated_step", "la_workspace_size", "la_gated_workspace_size", "library_path", "load_library",
     "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
     "la_initial_state", "la_workspace_size", "la_forward", "la_step", "la_gated_workspace_size",
-    "la_gated_forward", "la_status_string", "la_last_error_message",
+    "la_gated_forward", "la_gated_step", "la_status_string", "la_last_error_message",
 )
 
 _FM = {"elu_plus_one": 0, "relu": 1}
@@ -79,8 +80,9 @@ def load_library(build_if_missing: bool = True):
         lib.la_gated_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i32, ctypes.POINTER(sz)]
         lib.la_gated_forward.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32, f32,
                                          p, sz, p]
+        lib.la_gated_step.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32, f32, p]
         for name in ("la_initial_state", "la_workspace_size", "la_forward", "la_step",
-                     "la_gated_workspace_size", "la_gated_forward"):
+                     "la_gated_workspace_size", "la_gated_forward", "la_gated_step"):
             getattr(lib, name).restype = ctypes.c_int
         lib.la_status_string.argtypes = [ctypes.c_int]
         lib.la_status_string.restype = ctypes.c_char_p
@@ -275,3 +277,47 @@ def la_gated_forward(query, key, value, q_num_heads, kv_num_heads, decay=None, p
                                 0 if workspace is None else workspace.numel(), _stream(dev)),
            "la_gated_forward")
     return out, present_state
+
+
+def la_gated_step(query, key, value, q_num_heads, kv_num_heads, decay=None, past_state=None,
+                  scale=0.0, out=None, present_state=None, in_place=False):
+    """One token of the gated / linear recurrence: query (B,Hq*Dk) or (B,1,Hq*Dk),
+    key / value (B,Hkv*D) or (B,1,Hkv*D), decay (B,Hkv) / (B,1,Hkv) or None.
+
+    ``in_place`` writes the new state over ``past_state``.  Returns
+    ``(output, present_state (B,Hkv,Dk,Dv) float32)``, the output shaped like
+    the query.
+    """
+    _need_cuda(query, key, value, decay, past_state)
+    squeeze = query.dim() == 3
+    q, k, v, g = _contig(query), _contig(key), _contig(value), _contig(decay)
+    if squeeze:
+        if q.shape[1] != 1 or k.shape[1] != 1 or v.shape[1] != 1:
+            raise ValueError("la_gated_step takes one token")
+        q, k, v = q[:, 0], k[:, 0], v[:, 0]
+        g = None if g is None else g.reshape(g.shape[0], -1)
+    B, qw = q.shape
+    Hq, Hkv = int(q_num_heads), int(kv_num_heads)
+    if Hq < 1 or Hkv < 1 or qw % Hq or k.shape[-1] % Hkv or v.shape[-1] % Hkv:
+        raise ValueError("head counts do not divide the packed widths")
+    Dk = qw // Hq
+    Dv = v.shape[-1] // Hkv
+    dev = q.device
+    lib = load_library()
+    if g is not None and g.shape != (B, Hkv):
+        raise ValueError("decay must be (B,Hkv) (per-head scalar decay)")
+    if g is not None and g.dtype != q.dtype:
+        raise ValueError("decay must have the dtype of the query")
+    past = _contig(past_state)
+    if in_place:
+        if past is None:
+            raise ValueError("in_place needs past_state")
+        present_state = past
+    elif present_state is None:
+        present_state = torch.empty((B, Hkv, Dk, Dv), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((B, Hq * Dv), dtype=q.dtype, device=dev)
+    _check(lib.la_gated_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(past), _ptr(present_state),
+                             _ptr(out), B, Hq, Hkv, Dk, Dv, _dtype_code(q), float(scale), _stream(dev)),
+           "la_gated_step")
+    return (out[:, None] if squeeze else out), present_state

@@ -459,6 +459,23 @@ la_status check_gated(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,
 }
 }  // namespace
 
+hipError_t launch_step(const void* q, const void* k, const void* v, const void* decay,
+                       const float* past_state, float* present_state, void* out, int64_t U,
+                       int64_t Hkv, int64_t D, int64_t G, int32_t dtype, float scale, hipStream_t st) {
+  la::GatedStepArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.decay = decay;
+  a.s_in = past_state;
+  a.s_out = present_state;
+  a.out = out;
+  a.Hkv = (int32_t)Hkv;
+  a.units = (int32_t)U;
+  a.scale = scale;
+  return la::launch_gated_step(dtype, (int)D, (int)G, a, st);
+}
+
 LA_EXPORT la_status la_gated_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
                                             int64_t Dk, int64_t Dv, int32_t dtype, size_t* bytes) {
   if (!bytes) return fail(LA_ERR_NULL_ARG, "bytes is NULL");
@@ -513,6 +530,11 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
                      : la::launch_fill_zero(present_state, U * D * D, st);
     return device_status(e, "la_gated_forward");
   }
+  if (T == 1) {
+    // one token: the state-streaming step kernel (no chunk to tile)
+    e = launch_step(q, k, v, decay, past_state, present_state, out, U, Hkv, D, G, dtype, scale, st);
+    return device_status(e, "la_gated_forward");
+  }
   la::GatedArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -564,4 +586,33 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
     e = la::launch_gated(la::kModeCausal, dtype, (int)D, (int)G, pc, (int)(U * p.nseg), st);
   }
   return device_status(e, "la_gated_forward (split)");
+}
+
+LA_EXPORT la_status la_gated_step(const void* q, const void* k, const void* v, const void* decay,
+                                  const float* past_state, float* present_state, void* out,
+                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
+                                  int32_t dtype, float scale, void* stream) {
+  la_status s = check_gated(B, 1, Hq, Hkv, Dk, Dv, dtype);
+  if (s != LA_OK) return s;
+  if (isnan(scale) || isinf(scale)) return fail(LA_ERR_BAD_ARG, "scale must be finite");
+  const int64_t D = Dk, U = B * Hkv, G = Hq / Hkv;
+  const int64_t esz = dtype_size(dtype);
+  if (U == 0) return ok();
+  if (!q || !k || !v || !out || !present_state)
+    return fail(LA_ERR_NULL_ARG, "q, k, v, out and present_state are required");
+  if (!aligned16(past_state) || !aligned16(present_state))
+    return fail(LA_ERR_BAD_ARG, "states must be 16-byte aligned");
+  const Range rq = range(q, B * Hq * D * esz), rk = range(k, U * D * esz), rv = range(v, U * D * esz);
+  const Range ro = range(out, B * Hq * D * esz), rg = range(decay, U * esz);
+  const Range rpi = range(past_state, U * D * D * 4), rpo = range(present_state, U * D * D * 4);
+  const Range ins[4] = {rq, rk, rv, rg};
+  for (const Range& i : ins)
+    if (overlap(ro, i) || overlap(rpo, i)) return fail(LA_ERR_BAD_ARG, "an output overlaps an input");
+  if (overlap(ro, rpi) || overlap(ro, rpo)) return fail(LA_ERR_BAD_ARG, "out overlaps a state buffer");
+  if (overlap(rpo, rpi) && present_state != past_state)
+    return fail(LA_ERR_BAD_ARG, "present_state may equal past_state exactly but not partially overlap it");
+  if (scale == 0.f) scale = 1.f / sqrtf((float)D);
+  hipError_t e = launch_step(q, k, v, decay, past_state, present_state, out, U, Hkv, D, G, dtype,
+                             scale, (hipStream_t)stream);
+  return device_status(e, "la_gated_step");
 }

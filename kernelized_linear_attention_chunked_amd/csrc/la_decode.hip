@@ -127,6 +127,106 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   }
 }
 
+// T == 1 step of the gated recurrence with grouped query heads (the
+// LinearAttention operator page, "gated" / "linear" update rules, one token):
+// per (b, kv head j)
+//   S' = exp(g) S + k v^T,   o_h = scale q_h^T S'   for the G query heads of j.
+// The same streaming layout as decode_kernel: a thread owns RPT rows of four
+// consecutive state columns, issues all of its state loads first, updates in
+// registers, writes back, and keeps partial readouts of every query head; the
+// row groups are summed through LDS.  q and k are staged in LDS as fp32.
+template <typename DT, int D, int G, bool NTMP>
+__global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArgs a) {
+  constexpr int C4 = D / 4;          // float4 columns per state row
+  constexpr int RG = kThreads / C4;  // row groups
+  constexpr int RPT = D / RG;        // rows per thread
+  static_assert(RPT >= 1 && RG * RPT == D && C4 <= 32, "unsupported head size");
+  __shared__ float fk[kDecodeUnits][D], fq[kDecodeUnits][G][D];
+  __shared__ float part[kDecodeUnits][G][RG][D];
+
+  const int ul = threadIdx.x / kThreads;  // unit slot in the workgroup
+  const int tid = threadIdx.x % kThreads;
+  const int u = blockIdx.x * kDecodeUnits + ul;
+  const bool live = u < a.units;  // the last workgroup may hold one unit only
+  const int b = u / a.Hkv, j = u % a.Hkv;
+  const int c4 = tid % C4, rg = tid / C4;
+  const int64_t SE = (int64_t)D * D;
+
+  f32x4_t sv[RPT];
+  if (live && a.s_in) {
+    const float* S = a.s_in + (int64_t)u * SE;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const f32x4_t* p = (const f32x4_t*)(S + (rg + RG * r) * D + 4 * c4);
+      sv[r] = NTMP ? __builtin_nontemporal_load(p) : *p;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) sv[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int QW = a.Hkv * G * D;  // query row width
+  const DT* qp = (const DT*)a.q + (int64_t)b * QW + (int64_t)j * G * D;
+  const DT* kp = (const DT*)a.k + (int64_t)u * D;
+  const DT* vp = (const DT*)a.v + (int64_t)u * D;
+  float v4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v4[i] = live ? load_elem<DT>(vp, 4 * c4 + i) : 0.f;
+  const float e = (live && a.decay) ? __expf(load_elem<DT>((const DT*)a.decay, u)) : 1.f;
+  if (live) {
+    for (int i = tid; i < D; i += kThreads) fk[ul][i] = load_elem<DT>(kp, i);
+    for (int i = tid; i < G * D; i += kThreads) fq[ul][i / D][i % D] = load_elem<DT>(qp, i);
+  }
+  __syncthreads();
+  if (live) {
+    float acc[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[h][i] = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int dk = rg + RG * r;
+      const float f = fk[ul][dk];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[r][i] = fmaf(f, v4[i], e * sv[r][i]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float g = fq[ul][h][dk];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[h][i] = fmaf(g, sv[r][i], acc[h][i]);
+      }
+    }
+    float* So = a.s_out + (int64_t)u * SE;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      f32x4_t* p = (f32x4_t*)(So + (rg + RG * r) * D + 4 * c4);
+      if constexpr (NTMP)
+        __builtin_nontemporal_store(sv[r], p);
+      else
+        *p = sv[r];
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[ul][h][rg][4 * c4 + i] = acc[h][i];
+  }
+  __syncthreads();
+  if (live) {
+    DT* op = (DT*)a.out + (int64_t)b * QW + (int64_t)j * G * D;
+    for (int i = tid; i < G * D; i += kThreads) {
+      const int h = i / D, d = i % D;
+      float y = 0.f;
+#pragma unroll
+      for (int g = 0; g < RG; ++g) y += part[ul][h][g][d];
+      y *= a.scale;
+      if constexpr (std::is_same_v<DT, uint16_t>)
+        op[i] = (uint16_t)f32_to_bf16_bits(y);
+      else
+        op[i] = (DT)y;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * kThreads)
@@ -179,6 +279,45 @@ hipError_t launch_decode(int io, int D, int fm, int norm, const DecodeArgs& a, i
     case kIoF16: return launch_dt<f16_t>(D, fm, norm, a, units, st);
     default: return launch_dt<float>(D, fm, norm, a, units, st);
   }
+}
+
+template <typename DT, int D, int G>
+static void launch_gs(const GatedStepArgs& a, hipStream_t st) {
+  const bool ntmp = (int64_t)a.units * D * D * 4 >= ((int64_t)256 << 20);
+  const int grid = (a.units + kDecodeUnits - 1) / kDecodeUnits;
+  if (ntmp)
+    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, true>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, false>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+}
+
+template <typename DT, int D>
+static void launch_gs_g(int G, const GatedStepArgs& a, hipStream_t st) {
+  switch (G) {
+    case 1: launch_gs<DT, D, 1>(a, st); break;
+    case 2: launch_gs<DT, D, 2>(a, st); break;
+    case 4: launch_gs<DT, D, 4>(a, st); break;
+    default: launch_gs<DT, D, 8>(a, st); break;
+  }
+}
+
+template <typename DT>
+static void launch_gs_d(int D, int G, const GatedStepArgs& a, hipStream_t st) {
+  switch (D) {
+    case 32: launch_gs_g<DT, 32>(G, a, st); break;
+    case 64: launch_gs_g<DT, 64>(G, a, st); break;
+    default: launch_gs_g<DT, 128>(G, a, st); break;
+  }
+}
+
+hipError_t launch_gated_step(int io, int D, int G, const GatedStepArgs& a, hipStream_t st) {
+  if (a.units <= 0) return hipSuccess;
+  switch (io) {
+    case kIoBF16: launch_gs_d<uint16_t>(D, G, a, st); break;
+    case kIoF16: launch_gs_d<f16_t>(D, G, a, st); break;
+    default: launch_gs_d<float>(D, G, a, st); break;
+  }
+  return hipGetLastError();
 }
 
 static int grid_for(int64_t n) {

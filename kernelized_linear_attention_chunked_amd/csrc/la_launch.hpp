@@ -102,6 +102,21 @@ struct GatedArgs {
 };
 hipError_t launch_gated(int mode, int io, int D, int G, const GatedArgs& a, int grid,
                         hipStream_t st);
+
+// T == 1 step of the gated recurrence (la_decode.hip).
+struct GatedStepArgs {
+  const void* q;      // (B, Hq*D)
+  const void* k;      // (B, Hkv*D)
+  const void* v;      // (B, Hkv*D)
+  const void* decay;  // (B, Hkv) or null
+  const float* s_in;  // (B*Hkv, D, D) or null (zeros)
+  float* s_out;       // (B*Hkv, D, D), may equal s_in
+  void* out;          // (B, Hq*D)
+  int32_t Hkv;
+  int32_t units;  // B*Hkv
+  float scale;
+};
+hipError_t launch_gated_step(int io, int D, int G, const GatedStepArgs& a, hipStream_t st);
 hipError_t launch_gated_prefix(float* ws_s, const float* ws_a, const float* s_in, int U, int nseg,
                                int D, hipStream_t st);
 

@@ -190,4 +190,43 @@ class GatedGqaD128:
                                          self.ws_bytes, _stream(self.device)), "la_gated_forward")
 
 
-DRIVERS = {c.name: c for c in (StreamingD128, CausalBf16D64, NonCausalReluD128, GatedGqaD128)}
+class GatedStepD128:
+    """Gated GQA decode: B=256 sequences, Hq=32 Hkv=8 D=128, bf16, 64 one-token
+    steps per step() updating the fp32 state in place."""
+
+    name = "gated_step_d128"
+
+    def __init__(self, device="cuda:0"):
+        w = synth.WORKLOADS[self.name]
+        self.B, self.T, self.Hq, self.Hkv, self.D = w["B"], w["T"], w["Hq"], w["Hkv"], w["D"]
+        self.device = device
+        inp = synth.workload(self.name, device)
+        B, T, D = self.B, self.T, self.D
+        # step-major copies: token t of every sequence is one contiguous block
+        self.q = inp["q"].transpose(0, 1).contiguous()
+        self.k = inp["k"].transpose(0, 1).contiguous()
+        self.v = inp["v"].transpose(0, 1).contiguous()
+        self.g = inp["decay"].transpose(0, 1).contiguous()
+        self.state = inp["past"]
+        self.out = torch.empty((T, B, self.Hq * D), dtype=torch.bfloat16, device=device)
+        self.scale = 1.0 / (D ** 0.5)
+        self.lib = load_library()
+
+    @property
+    def prefill_tokens(self):
+        return self.B * self.T
+
+    def decode_call(self, t, stream=None):
+        _check(self.lib.la_gated_step(_p(self.q[t]), _p(self.k[t]), _p(self.v[t]), _p(self.g[t]),
+                                      _p(self.state), _p(self.state), _p(self.out[t]), self.B,
+                                      self.Hq, self.Hkv, self.D, self.D, 1, self.scale,
+                                      _stream(self.device) if stream is None else stream),
+               "la_gated_step")
+
+    def step(self):
+        for t in range(self.T):
+            self.decode_call(t)
+
+
+DRIVERS = {c.name: c for c in (StreamingD128, CausalBf16D64, NonCausalReluD128, GatedGqaD128,
+                               GatedStepD128)}

@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     assert sorted(la.EXPORTED_SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -159,3 +159,27 @@ def test_gated_argument_errors(lib):
     assert g(scale=float("inf")) == BAD_ARG
     assert g(T=4096) == WORKSPACE             # 2 units: the sequence is split
     assert g(out=f(1 << 30)) == BAD_ARG       # out aliases q
+
+
+def test_gated_step_argument_errors(lib):
+    f = fake
+
+    def g(**kw):
+        a = dict(q=f(1 << 30), k=f(2 << 30), v=f(3 << 30), d=None, past=f(6 << 30), pres=f(6 << 30),
+                 out=f(5 << 30), B=2, Hq=8, Hkv=2, Dk=128, Dv=128, dt=2, scale=0.0)
+        a.update(kw)
+        return lib.la_gated_step(a["q"], a["k"], a["v"], a["d"], a["past"], a["pres"], a["out"],
+                                 a["B"], a["Hq"], a["Hkv"], a["Dk"], a["Dv"], a["dt"],
+                                 ctypes.c_float(a["scale"]), None)
+
+    assert g(Hq=3) == SHAPE
+    assert g(Hq=2 * 16) == UNSUPPORTED        # 16 query heads per kv head
+    assert g(Dk=96, Dv=96) == UNSUPPORTED
+    assert g(dt=3) == DTYPE
+    assert g(pres=None) == NULL_ARG
+    assert g(q=None) == NULL_ARG
+    assert g(scale=float("nan")) == BAD_ARG
+    assert g(out=f(1 << 30)) == BAD_ARG       # out aliases q
+    assert g(pres=f((6 << 30) + 4096)) == BAD_ARG  # partial overlap of the states
+    assert g(past=f((6 << 30) + 4)) == BAD_ARG     # misaligned state
+    assert g(B=0) == OK                       # nothing to do, nothing touched

@@ -285,6 +285,55 @@ def test_gated_present_aliases_past():
     assert torch.equal(out_a, out_b) and torch.equal(pres_a, pres_b)
 
 
+# ------------------------------------------------------------ gated T=1 step
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("case", ["gated_past_in_place", "gated_no_past", "linear_past"])
+def test_gated_step(dtype, D, G, case):
+    B, Hkv = 3, 2
+    Hq = Hkv * G
+    seed = 4000 + D + G
+    q = synth.normal((B, 1, Hq * D), 1.0, dtype, DEV, seed, "q")
+    k = synth.l2_normalized((B, 1, Hkv, D), dtype, DEV, seed, "k").reshape(B, 1, Hkv * D)
+    v = synth.normal((B, 1, Hkv * D), 1.0, dtype, DEV, seed, "v")
+    g = None if case == "linear_past" else synth.logsigmoid_decay((B, 1, Hkv), dtype, DEV, seed, mean=1.0)
+    past = None if case == "gated_no_past" else synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, seed, "past")
+    past_ref = None if past is None else f64(past)
+    in_place = case == "gated_past_in_place"
+    out, present = la.la_gated_step(q, k, v, Hq, Hkv, decay=g, past_state=past, in_place=in_place)
+    torch.cuda.synchronize()
+    if in_place:
+        assert present.data_ptr() == past.data_ptr()
+    oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "linear" if g is None else "gated",
+                          past_state=past_ref, decay=None if g is None else f64(g))
+    assert out.shape == q.shape
+    assert_close(out, oo, TOL[dtype], "out")
+    assert_close(present, po, TOL[dtype], "present_state")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
+def test_gated_prefill_then_steps_equal_full(dtype):
+    """A prefill call followed by one-token steps (in place) equals one oracle
+    run over the whole sequence, outputs and final state."""
+    B, T0, N, Hkv, G, D = 2, 100, 6, 2, 4, 64
+    Hq, T = Hkv * G, T0 + N
+    q = synth.normal((B, T, Hq * D), 1.0, dtype, DEV, 77, "q")
+    k = synth.l2_normalized((B, T, Hkv, D), dtype, DEV, 77, "k").reshape(B, T, Hkv * D)
+    v = synth.normal((B, T, Hkv * D), 1.0, dtype, DEV, 77, "v")
+    g = synth.logsigmoid_decay((B, T, Hkv), dtype, DEV, 77, mean=1.0)
+    y0, state = la.la_gated_forward(q[:, :T0], k[:, :T0], v[:, :T0], Hq, Hkv, decay=g[:, :T0])
+    ys = [y0]
+    for t in range(T0, T):
+        y, state = la.la_gated_step(q[:, t], k[:, t], v[:, t], Hq, Hkv, decay=g[:, t],
+                                    past_state=state, in_place=True)
+        ys.append(y[:, None])
+    torch.cuda.synchronize()
+    oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "gated", decay=f64(g))
+    assert_close(torch.cat(ys, 1), oo, TOL[dtype], "outputs")
+    assert_close(state, po, TOL[dtype], "state")
+
+
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "onnx_examples.json")))
 
 
