@@ -253,8 +253,10 @@ def bench_other(args, log):
         U = d.B * d.Hkv
         nbytes = d.T * (U * D * D * 4 * 2 + d.B * (d.Hq * D * 2 * 2 + d.Hkv * D * 2 * 2 + d.Hkv * 2))
         flops = d.T * (U * D * D * 3 + d.B * d.Hq * D * D * 2)  # update (3/elem), readout
-    elif args.workload == "gated_gqa_d128":
-        nbytes = Tt * (d.Hq * D * 2 * 2 + d.Hkv * D * 2 * 2 + d.Hkv * 2) + d.B * d.Hkv * D * D * 4
+    elif args.workload in ("gated_gqa_d128", "gated_perdim_d128"):
+        per_dim = args.workload == "gated_perdim_d128"
+        nbytes = (Tt * (d.Hq * D * 2 * 2 + d.Hkv * D * 2 * 2 + d.Hkv * (D if per_dim else 1) * 2)
+                  + d.B * d.Hkv * D * D * 4)
         # dense 64x64 intra tiles per q head plus inter and state update (2 Dk Dv each)
         flops = Tt * d.Hq * (2 * 64 * 2 * D + 2 * D * D) + Tt * d.Hkv * 2 * D * D
     elif args.workload == "noncausal_relu_d128":
@@ -289,7 +291,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="streaming_d128",
                     choices=["streaming_d128", "causal_bf16_d64", "noncausal_relu_d128",
-                             "gated_gqa_d128", "gated_step_d128"])
+                             "gated_gqa_d128", "gated_perdim_d128", "gated_step_d128"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

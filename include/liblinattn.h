@@ -111,44 +111,53 @@ la_status la_step(const void* q, const void* k, const void* v, const uint8_t* ma
                   void* out, int64_t B, int64_t H, int64_t Dk, int64_t Dv, int32_t dtype,
                   void* stream);
 
-/* Bytes of device workspace la_gated_forward needs (0 = none); shape-only. */
+/* Bytes of device workspace la_gated_forward needs (0 = none); shape-only.
+ * per_dim_decay as in la_gated_forward (a per-dim decay needs a little more). */
 la_status la_gated_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,
-                                  int64_t Dv, int32_t dtype, size_t* bytes);
+                                  int64_t Dv, int32_t dtype, int32_t per_dim_decay, size_t* bytes);
 
 /* Gated linear recurrence with grouped-query heads (the LinearAttention
- * operator page, ai.onnx since version 27: "gated" rule with a per-head scalar
- * decay, or the "linear" rule when decay == NULL):
- *   S_t = exp(g_t) S_{t-1} + k_t v_t^T        (per kv head)
- *   o_t = scale * q_t^T S_t                   (per query head, S after the update)
- * Query head h reads kv head h / (Hq/Hkv).  No feature map, no normalizer, no
- * mask.  Packed layouts (byte-identical to the 4-D ones):
- *   q (B,T,Hq*Dk), k (B,T,Hkv*Dk), v (B,T,Hkv*Dv), out (B,T,Hq*Dv) in `dtype`;
- *   decay (B,T,Hkv) in `dtype`, log-space (NULL = all zero);
+ * operator page, ai.onnx since version 27: "gated" rule, or the "linear" rule
+ * when decay == NULL):
+ *   S_t = diag(exp(g_t)) S_{t-1} + k_t v_t^T   (per kv head)
+ *   o_t = scale * q_t^T S_t                    (per query head, S after the update)
+ * g_t is one log-space value per kv head (per_dim_decay == 0: decay (B,T,Hkv),
+ * scaling all of S) or one per key dimension (per_dim_decay != 0: decay
+ * (B,T,Hkv*Dk), scaling row dk of S; the page's "gated" rule with a decay of
+ * shape (B, T, kv_num_heads * d_k)).  Query head h reads kv head h / (Hq/Hkv).
+ * No feature map, no normalizer, no mask.  Packed layouts (byte-identical to
+ * the 4-D ones):
+ *   q (B,T,Hq*Dk), k (B,T,Hkv*Dk), v (B,T,Hkv*Dv), out (B,T,Hq*Dv) and decay
+ *   in `dtype`, the decay log-space (NULL = all zero);
  *   past_state (B,Hkv,Dk,Dv) float32 (NULL = zeros); present_state (same shape,
  *   float32) is always written and may alias past_state exactly.
  * scale == 0 means 1/sqrt(Dk).  Hq must be a positive multiple of Hkv
- * (else LA_ERR_SHAPE). */
+ * (else LA_ERR_SHAPE).  A per-dim decay is evaluated chunk-parallel with keys
+ * rescaled inside blocks of 32 tokens: decays summing below about -87 over
+ * one such block (per dimension) overflow; fp32 inputs at Dk = 128 with T > 1
+ * and a per-dim decay return LA_ERR_UNSUPPORTED. */
 la_status la_gated_forward(const void* q, const void* k, const void* v, const void* decay,
-                           const float* past_state, float* present_state, void* out,
-                           int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
-                           int32_t dtype, float scale, void* workspace, size_t workspace_bytes,
-                           void* stream);
+                           int32_t per_dim_decay, const float* past_state, float* present_state,
+                           void* out, int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,
+                           int64_t Dv, int32_t dtype, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* One token of the gated / linear recurrence with grouped-query heads: the
  * T == 1 case of la_gated_forward, as a decode step that streams the fp32 state
  * once (the LinearAttention operator page, "Description": the recurrence is
  * token-by-token; its decode example is a single token with a past state):
- *   S' = exp(g) S + k v^T   (per kv head),   o = scale q^T S'   (per query head).
+ *   S' = diag(exp(g)) S + k v^T   (per kv head),   o = scale q^T S'   (per query head).
  * q (B, Hq*Dk), k (B, Hkv*Dk), v (B, Hkv*Dv), out (B, Hq*Dv) in `dtype`;
- * decay (B, Hkv) in `dtype`, log-space (NULL = all zero);
+ * decay in `dtype`, log-space: (B, Hkv), or (B, Hkv*Dk) with per_dim_decay
+ * (NULL = all zero);
  * past_state (B,Hkv,Dk,Dv) float32 (NULL = zeros); present_state (same shape,
  * float32) is always written and may alias past_state exactly (in-place step).
  * The states must be 16-byte aligned.  scale == 0 means 1/sqrt(Dk).  Sizes,
  * dtypes and errors as la_gated_forward; no workspace. */
 la_status la_gated_step(const void* q, const void* k, const void* v, const void* decay,
-                        const float* past_state, float* present_state, void* out, int64_t B,
-                        int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv, int32_t dtype, float scale,
-                        void* stream);
+                        int32_t per_dim_decay, const float* past_state, float* present_state,
+                        void* out, int64_t B, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
+                        int32_t dtype, float scale, void* stream);
 
 /* Static string naming a status code. */
 const char* la_status_string(la_status s);

@@ -77,10 +77,11 @@ def load_library(build_if_missing: bool = True):
         lib.la_forward.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, f32, p,
                                    i64, i64, i64, i64, i64, i32, p, sz, p]
         lib.la_step.argtypes = [p, p, p, p, p, p, p, p, i32, i32, f32, p, i64, i64, i64, i64, i32, p]
-        lib.la_gated_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i32, ctypes.POINTER(sz)]
-        lib.la_gated_forward.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32, f32,
-                                         p, sz, p]
-        lib.la_gated_step.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32, f32, p]
+        lib.la_gated_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32,
+                                                ctypes.POINTER(sz)]
+        lib.la_gated_forward.argtypes = [p, p, p, p, i32, p, p, p, i64, i64, i64, i64, i64, i64, i32,
+                                         f32, p, sz, p]
+        lib.la_gated_step.argtypes = [p, p, p, p, i32, p, p, p, i64, i64, i64, i64, i64, i32, f32, p]
         for name in ("la_initial_state", "la_workspace_size", "la_forward", "la_step",
                      "la_gated_workspace_size", "la_gated_forward", "la_gated_step"):
             getattr(lib, name).restype = ctypes.c_int
@@ -138,10 +139,11 @@ def la_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16, causal=True) -> int
     return n.value
 
 
-def la_gated_workspace_size(B, T, Hq, Hkv, Dk, Dv, dtype=torch.bfloat16) -> int:
+def la_gated_workspace_size(B, T, Hq, Hkv, Dk, Dv, dtype=torch.bfloat16, per_dim_decay=False) -> int:
     n = ctypes.c_size_t(0)
     _check(load_library().la_gated_workspace_size(B, T, Hq, Hkv, Dk, Dv, _DT.get(dtype, 99),
-                                                  ctypes.byref(n)), "la_gated_workspace_size")
+                                                  int(bool(per_dim_decay)), ctypes.byref(n)),
+           "la_gated_workspace_size")
     return n.value
 
 
@@ -247,7 +249,8 @@ def la_gated_forward(query, key, value, q_num_heads, kv_num_heads, decay=None, p
                      scale=0.0, out=None, present_state=None, workspace=None):
     """Gated / linear recurrence on packed (B,T,H*D) tensors with GQA.
 
-    ``decay``: (B,T,Hkv) log-space per-head decay or None ("linear" rule).
+    ``decay``: log-space, (B,T,Hkv) per kv head or (B,T,Hkv*Dk) per key
+    dimension, or None ("linear" rule).
     Returns ``(output (B,T,Hq*Dv), present_state (B,Hkv,Dk,Dv) float32)``.
     """
     _need_cuda(query, key, value, decay, past_state)
@@ -260,18 +263,20 @@ def la_gated_forward(query, key, value, q_num_heads, kv_num_heads, decay=None, p
     Dv = value.shape[-1] // Hkv
     dev = q.device
     lib = load_library()
-    if g is not None and g.shape != (B, T, Hkv):
-        raise ValueError("decay must be (B,T,Hkv) (per-head scalar decay)")
+    per_dim = g is not None and tuple(g.shape) == (B, T, Hkv * Dk) and Dk > 1
+    if g is not None and not per_dim and tuple(g.shape) != (B, T, Hkv):
+        raise ValueError("decay must be (B,T,Hkv) (per kv head) or (B,T,Hkv*Dk) (per key dim)")
     if g is not None and g.dtype != q.dtype:
         raise ValueError("decay must have the dtype of the query")
     if out is None:
         out = torch.empty((B, T, Hq * Dv), dtype=q.dtype, device=dev)
     if present_state is None:
         present_state = torch.empty((B, Hkv, Dk, Dv), dtype=torch.float32, device=dev)
-    ws_bytes = la_gated_workspace_size(B, T, Hq, Hkv, Dk, Dv, q.dtype) if q.dtype in _DT else 0
+    ws_bytes = (la_gated_workspace_size(B, T, Hq, Hkv, Dk, Dv, q.dtype, per_dim)
+                if q.dtype in _DT else 0)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    _check(lib.la_gated_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(_contig(past_state)),
+    _check(lib.la_gated_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), int(per_dim), _ptr(_contig(past_state)),
                                 _ptr(present_state), _ptr(out), B, T, Hq, Hkv, Dk, Dv,
                                 _dtype_code(q), float(scale), _ptr(workspace),
                                 0 if workspace is None else workspace.numel(), _stream(dev)),
@@ -282,7 +287,8 @@ def la_gated_forward(query, key, value, q_num_heads, kv_num_heads, decay=None, p
 def la_gated_step(query, key, value, q_num_heads, kv_num_heads, decay=None, past_state=None,
                   scale=0.0, out=None, present_state=None, in_place=False):
     """One token of the gated / linear recurrence: query (B,Hq*Dk) or (B,1,Hq*Dk),
-    key / value (B,Hkv*D) or (B,1,Hkv*D), decay (B,Hkv) / (B,1,Hkv) or None.
+    key / value (B,Hkv*D) or (B,1,Hkv*D), decay (B,Hkv) per kv head or
+    (B,Hkv*Dk) per key dim (either with an optional token axis of 1), or None.
 
     ``in_place`` writes the new state over ``past_state``.  Returns
     ``(output, present_state (B,Hkv,Dk,Dv) float32)``, the output shaped like
@@ -304,8 +310,9 @@ def la_gated_step(query, key, value, q_num_heads, kv_num_heads, decay=None, past
     Dv = v.shape[-1] // Hkv
     dev = q.device
     lib = load_library()
-    if g is not None and g.shape != (B, Hkv):
-        raise ValueError("decay must be (B,Hkv) (per-head scalar decay)")
+    per_dim = g is not None and tuple(g.shape) == (B, Hkv * Dk) and Dk > 1
+    if g is not None and not per_dim and tuple(g.shape) != (B, Hkv):
+        raise ValueError("decay must be (B,Hkv) (per kv head) or (B,Hkv*Dk) (per key dim)")
     if g is not None and g.dtype != q.dtype:
         raise ValueError("decay must have the dtype of the query")
     past = _contig(past_state)
@@ -317,7 +324,7 @@ def la_gated_step(query, key, value, q_num_heads, kv_num_heads, decay=None, past
         present_state = torch.empty((B, Hkv, Dk, Dv), dtype=torch.float32, device=dev)
     if out is None:
         out = torch.empty((B, Hq * Dv), dtype=q.dtype, device=dev)
-    _check(lib.la_gated_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(past), _ptr(present_state),
+    _check(lib.la_gated_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), int(per_dim), _ptr(past), _ptr(present_state),
                              _ptr(out), B, Hq, Hkv, Dk, Dv, _dtype_code(q), float(scale), _stream(dev)),
            "la_gated_step")
     return (out[:, None] if squeeze else out), present_state

@@ -430,13 +430,15 @@ GatedPlan plan_gated(int64_t U, int64_t T) {
   }
   return p;
 }
-size_t gated_ws_bytes(int64_t B, int64_t T, int64_t Hkv, int64_t D) {
+size_t gated_ws_bytes(int64_t B, int64_t T, int64_t Hkv, int64_t D, bool per_dim) {
   const int64_t U = B * Hkv;
-  if (U == 0 || T == 0) return 0;
+  if (U == 0 || T <= 1) return 0;
   GatedPlan p = plan_gated(U, T);
   if (p.nseg <= 1) return 0;
-  // slots of D*D floats plus one decay factor per slot (padded to 16 bytes)
-  return (size_t)(U * p.nseg * D * D * 4 + ceil_div(U * p.nseg, 4) * 16);
+  // slots of D*D floats plus the decay factors of each slot (one, or one per
+  // key dim), padded to 16 bytes
+  const int64_t na = U * p.nseg * (per_dim ? D : 1);
+  return (size_t)(U * p.nseg * D * D * 4 + ceil_div(na, 4) * 16);
 }
 la_status check_gated(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
                       int32_t dtype) {
@@ -459,7 +461,7 @@ la_status check_gated(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,
 }
 }  // namespace
 
-hipError_t launch_step(const void* q, const void* k, const void* v, const void* decay,
+hipError_t launch_step(const void* q, const void* k, const void* v, const void* decay, bool per_dim,
                        const float* past_state, float* present_state, void* out, int64_t U,
                        int64_t Hkv, int64_t D, int64_t G, int32_t dtype, float scale, hipStream_t st) {
   la::GatedStepArgs a;
@@ -467,6 +469,7 @@ hipError_t launch_step(const void* q, const void* k, const void* v, const void* 
   a.k = k;
   a.v = v;
   a.decay = decay;
+  a.per_dim = per_dim ? 1 : 0;
   a.s_in = past_state;
   a.s_out = present_state;
   a.out = out;
@@ -477,25 +480,30 @@ hipError_t launch_step(const void* q, const void* k, const void* v, const void* 
 }
 
 LA_EXPORT la_status la_gated_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
-                                            int64_t Dk, int64_t Dv, int32_t dtype, size_t* bytes) {
+                                            int64_t Dk, int64_t Dv, int32_t dtype,
+                                            int32_t per_dim_decay, size_t* bytes) {
   if (!bytes) return fail(LA_ERR_NULL_ARG, "bytes is NULL");
   la_status s = check_gated(B, T, Hq, Hkv, Dk, Dv, dtype);
   if (s != LA_OK) return s;
-  *bytes = gated_ws_bytes(B, T, Hkv, Dk);
+  *bytes = gated_ws_bytes(B, T, Hkv, Dk, per_dim_decay != 0);
   return ok();
 }
 
 LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v,
-                                     const void* decay, const float* past_state,
-                                     float* present_state, void* out, int64_t B, int64_t T,
-                                     int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
-                                     int32_t dtype, float scale, void* workspace,
+                                     const void* decay, int32_t per_dim_decay,
+                                     const float* past_state, float* present_state, void* out,
+                                     int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,
+                                     int64_t Dv, int32_t dtype, float scale, void* workspace,
                                      size_t workspace_bytes, void* stream) {
   la_status s = check_gated(B, T, Hq, Hkv, Dk, Dv, dtype);
   if (s != LA_OK) return s;
   if (isnan(scale) || isinf(scale)) return fail(LA_ERR_BAD_ARG, "scale must be finite");
   const int64_t D = Dk, U = B * Hkv, G = Hq / Hkv;
   const int64_t esz = dtype_size(dtype);
+  const bool per_dim = per_dim_decay != 0 && decay != nullptr;
+  if (per_dim && dtype == LA_DT_F32 && D == 128 && T > 1)
+    return fail(LA_ERR_UNSUPPORTED, "per-key-dim decay with fp32 inputs at head size 128 (T > 1)");
+  if (per_dim && !aligned16(decay)) return fail(LA_ERR_BAD_ARG, "a per-dim decay must be 16-byte aligned");
   if (U > 0 && !present_state) return fail(LA_ERR_NULL_ARG, "present_state is required");
   const bool work = U > 0 && T > 0;
   if (work && (!q || !k || !v || !out)) return fail(LA_ERR_NULL_ARG, "q, k, v and out are required");
@@ -504,9 +512,9 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
     return fail(LA_ERR_BAD_ARG, "tensors and workspace must be 16-byte aligned");
   const Range rq = range(q, B * T * Hq * D * esz), rk = range(k, B * T * Hkv * D * esz);
   const Range rv = range(v, B * T * Hkv * D * esz), ro = range(out, B * T * Hq * D * esz);
-  const Range rg = range(decay, B * T * Hkv * esz);
+  const Range rg = range(decay, B * T * Hkv * (per_dim ? D : 1) * esz);
   const Range rpi = range(past_state, U * D * D * 4), rpo = range(present_state, U * D * D * 4);
-  const size_t need = gated_ws_bytes(B, T, Hkv, D);
+  const size_t need = gated_ws_bytes(B, T, Hkv, D, per_dim);
   const Range rw = range(workspace, (int64_t)need);
   const Range ins[5] = {rq, rk, rv, rg, rw};
   for (const Range& i : ins)
@@ -532,9 +540,14 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
   }
   if (T == 1) {
     // one token: the state-streaming step kernel (no chunk to tile)
-    e = launch_step(q, k, v, decay, past_state, present_state, out, U, Hkv, D, G, dtype, scale, st);
+    e = launch_step(q, k, v, decay, per_dim, past_state, present_state, out, U, Hkv, D, G, dtype,
+                    scale, st);
     return device_status(e, "la_gated_forward");
   }
+  auto launch = [&](int mode, const la::GatedArgs& ga, int grid) {
+    return per_dim ? la::launch_gated_pd(mode, dtype, (int)D, (int)G, ga, grid, st)
+                   : la::launch_gated(mode, dtype, (int)D, (int)G, ga, grid, st);
+  };
   la::GatedArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -556,7 +569,7 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
     a.seg_count = 1;
     a.seg_chunks = (int32_t)p.nchunks;
     a.nseg_total = 1;
-    e = la::launch_gated(la::kModeCausal, dtype, (int)D, (int)G, a, (int)U, st);
+    e = launch(la::kModeCausal, a, (int)U);
     return device_status(e, "la_gated_forward");
   }
   float* ws_s = (float*)workspace;
@@ -570,9 +583,9 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
   ps.seg_count = (int32_t)(p.nseg - 1);
   ps.seg_chunks = (int32_t)p.seg_chunks;
   ps.nseg_total = (int32_t)p.nseg;
-  e = la::launch_gated(la::kModeState, dtype, (int)D, (int)G, ps, (int)(U * (p.nseg - 1)), st);
+  e = launch(la::kModeState, ps, (int)(U * (p.nseg - 1)));
   if (e == hipSuccess)
-    e = la::launch_gated_prefix(ws_s, ws_a, past_state, (int)U, (int)p.nseg, (int)D, st);
+    e = la::launch_gated_prefix(ws_s, ws_a, past_state, (int)U, (int)p.nseg, (int)D, per_dim ? 1 : 0, st);
   if (e == hipSuccess) {
     la::GatedArgs pc = a;
     pc.s_in = ws_s;
@@ -583,15 +596,16 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
     pc.seg_count = (int32_t)p.nseg;
     pc.seg_chunks = (int32_t)p.seg_chunks;
     pc.nseg_total = (int32_t)p.nseg;
-    e = la::launch_gated(la::kModeCausal, dtype, (int)D, (int)G, pc, (int)(U * p.nseg), st);
+    e = launch(la::kModeCausal, pc, (int)(U * p.nseg));
   }
   return device_status(e, "la_gated_forward (split)");
 }
 
 LA_EXPORT la_status la_gated_step(const void* q, const void* k, const void* v, const void* decay,
-                                  const float* past_state, float* present_state, void* out,
-                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
-                                  int32_t dtype, float scale, void* stream) {
+                                  int32_t per_dim_decay, const float* past_state,
+                                  float* present_state, void* out, int64_t B, int64_t Hq,
+                                  int64_t Hkv, int64_t Dk, int64_t Dv, int32_t dtype, float scale,
+                                  void* stream) {
   la_status s = check_gated(B, 1, Hq, Hkv, Dk, Dv, dtype);
   if (s != LA_OK) return s;
   if (isnan(scale) || isinf(scale)) return fail(LA_ERR_BAD_ARG, "scale must be finite");
@@ -603,7 +617,8 @@ LA_EXPORT la_status la_gated_step(const void* q, const void* k, const void* v, c
   if (!aligned16(past_state) || !aligned16(present_state))
     return fail(LA_ERR_BAD_ARG, "states must be 16-byte aligned");
   const Range rq = range(q, B * Hq * D * esz), rk = range(k, U * D * esz), rv = range(v, U * D * esz);
-  const Range ro = range(out, B * Hq * D * esz), rg = range(decay, U * esz);
+  const bool per_dim = per_dim_decay != 0 && decay != nullptr;
+  const Range ro = range(out, B * Hq * D * esz), rg = range(decay, U * (per_dim ? D : 1) * esz);
   const Range rpi = range(past_state, U * D * D * 4), rpo = range(present_state, U * D * D * 4);
   const Range ins[4] = {rq, rk, rv, rg};
   for (const Range& i : ins)
@@ -612,7 +627,7 @@ LA_EXPORT la_status la_gated_step(const void* q, const void* k, const void* v, c
   if (overlap(rpo, rpi) && present_state != past_state)
     return fail(LA_ERR_BAD_ARG, "present_state may equal past_state exactly but not partially overlap it");
   if (scale == 0.f) scale = 1.f / sqrtf((float)D);
-  hipError_t e = launch_step(q, k, v, decay, past_state, present_state, out, U, Hkv, D, G, dtype,
-                             scale, (hipStream_t)stream);
+  hipError_t e = launch_step(q, k, v, decay, per_dim, past_state, present_state, out, U, Hkv, D, G,
+                             dtype, scale, (hipStream_t)stream);
   return device_status(e, "la_gated_step");
 }

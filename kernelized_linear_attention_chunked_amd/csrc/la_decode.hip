@@ -135,13 +135,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 // consecutive state columns, issues all of its state loads first, updates in
 // registers, writes back, and keeps partial readouts of every query head; the
 // row groups are summed through LDS.  q and k are staged in LDS as fp32.
-template <typename DT, int D, int G, bool NTMP>
+template <typename DT, int D, int G, bool NTMP, bool PD>
 __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArgs a) {
   constexpr int C4 = D / 4;          // float4 columns per state row
   constexpr int RG = kThreads / C4;  // row groups
   constexpr int RPT = D / RG;        // rows per thread
   static_assert(RPT >= 1 && RG * RPT == D && C4 <= 32, "unsupported head size");
-  __shared__ float fk[kDecodeUnits][D], fq[kDecodeUnits][G][D];
+  __shared__ float fk[kDecodeUnits][D], fq[kDecodeUnits][G][D], fe[kDecodeUnits][PD ? D : 1];
   __shared__ float part[kDecodeUnits][G][RG][D];
 
   const int ul = threadIdx.x / kThreads;  // unit slot in the workgroup
@@ -171,9 +171,11 @@ __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArg
   float v4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) v4[i] = live ? load_elem<DT>(vp, 4 * c4 + i) : 0.f;
-  const float e = (live && a.decay) ? __expf(load_elem<DT>((const DT*)a.decay, u)) : 1.f;
+  const float e = (live && a.decay && !PD) ? __expf(load_elem<DT>((const DT*)a.decay, u)) : 1.f;
   if (live) {
     for (int i = tid; i < D; i += kThreads) fk[ul][i] = load_elem<DT>(kp, i);
+    if constexpr (PD)  // per-key-dim decay: row dk of S scales by exp(g[dk])
+      for (int i = tid; i < D; i += kThreads) fe[ul][i] = __expf(load_elem<DT>((const DT*)a.decay + (int64_t)u * D, i));
     for (int i = tid; i < G * D; i += kThreads) fq[ul][i / D][i % D] = load_elem<DT>(qp, i);
   }
   __syncthreads();
@@ -187,8 +189,9 @@ __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArg
     for (int r = 0; r < RPT; ++r) {
       const int dk = rg + RG * r;
       const float f = fk[ul][dk];
+      const float er = PD ? fe[ul][dk] : e;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[r][i] = fmaf(f, v4[i], e * sv[r][i]);
+      for (int i = 0; i < 4; ++i) sv[r][i] = fmaf(f, v4[i], er * sv[r][i]);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float g = fq[ul][h][dk];
@@ -281,14 +284,22 @@ hipError_t launch_decode(int io, int D, int fm, int norm, const DecodeArgs& a, i
   }
 }
 
-template <typename DT, int D, int G>
-static void launch_gs(const GatedStepArgs& a, hipStream_t st) {
+template <typename DT, int D, int G, bool PD>
+static void launch_gsp(const GatedStepArgs& a, hipStream_t st) {
   const bool ntmp = (int64_t)a.units * D * D * 4 >= ((int64_t)256 << 20);
   const int grid = (a.units + kDecodeUnits - 1) / kDecodeUnits;
   if (ntmp)
-    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, true>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, true, PD>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, false>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, false, PD>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+}
+
+template <typename DT, int D, int G>
+static void launch_gs(const GatedStepArgs& a, hipStream_t st) {
+  if (a.per_dim && a.decay)
+    launch_gsp<DT, D, G, true>(a, st);
+  else
+    launch_gsp<DT, D, G, false>(a, st);
 }
 
 template <typename DT, int D>

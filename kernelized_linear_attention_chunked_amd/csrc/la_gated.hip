@@ -530,19 +530,23 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
 // In-place affine prefix over segments: slot s (s >= 1) holds the increment of
 // segment s-1 and a[s] its total decay factor on entry; on exit slot s holds
 // the state before segment s:  S(0) = past (or 0),  S(s) = a[s] S(s-1) + dS(s-1).
+// a[s] is one factor per slot, or with a per-key-dim decay one per slot and row
+// dk of S (ws_a laid out [unit][slot][dk]).
 __global__ __launch_bounds__(kThreads) void gated_prefix_kernel(float* ws_s, const float* ws_a,
                                                                 const float* s_in, int U, int nseg,
-                                                                int D) {
+                                                                int D, int per_dim) {
   const int64_t per = (int64_t)D * D;
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= (int64_t)U * per) return;
   const int u = (int)(idx / per);
   const int64_t e = idx % per;
   float* base = ws_s + (int64_t)u * nseg * per + e;
+  const float* ap = per_dim ? ws_a + (int64_t)u * nseg * D + e / D : ws_a + (int64_t)u * nseg;
+  const int astride = per_dim ? D : 1;
   float acc = s_in ? s_in[(int64_t)u * per + e] : 0.f;
   base[0] = acc;
   for (int s = 1; s < nseg; ++s) {
-    acc = fmaf(ws_a[(int64_t)u * nseg + s], acc, base[s * per]);
+    acc = fmaf(ap[s * astride], acc, base[s * per]);
     base[s * per] = acc;
   }
 }
@@ -587,11 +591,11 @@ hipError_t launch_gated(int mode, int io, int D, int G, const GatedArgs& a, int 
 }
 
 hipError_t launch_gated_prefix(float* ws_s, const float* ws_a, const float* s_in, int U, int nseg,
-                               int D, hipStream_t st) {
+                               int D, int per_dim, hipStream_t st) {
   const int64_t n = (int64_t)U * D * D;
   const int grid = (int)((n + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(gated_prefix_kernel, dim3(grid), dim3(kThreads), 0, st, ws_s, ws_a, s_in, U,
-                     nseg, D);
+                     nseg, D, per_dim);
   return hipGetLastError();
 }
 

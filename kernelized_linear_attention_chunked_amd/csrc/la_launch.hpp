@@ -88,13 +88,13 @@ struct GatedArgs {
   const void* q;      // (B,T,Hq*D)
   const void* k;      // (B,T,Hkv*D)
   const void* v;      // (B,T,Hkv*D)
-  const void* decay;  // (B,T,Hkv) or null
+  const void* decay;  // (B,T,Hkv), or (B,T,Hkv*D) for the per-dim kernel, or null
   void* out;          // (B,T,Hq*D)
   const float* s_in;  // initial state of the segment, s_in + u*s_in_u + s*s_in_s (null = zeros)
   int64_t s_in_u, s_in_s;
   float* s_out;       // final/partial state, see launch_gated
   int64_t s_out_u, s_out_s;
-  float* a_out;       // state mode: per (unit, slot) total decay factor
+  float* a_out;       // state mode: per (unit, slot) total decay factor (per (unit, slot, dk): per-dim)
   int32_t out_slot_off;
   int32_t T, Hq, Hkv;
   int32_t seg_count, seg_first, seg_chunks, nseg_total;
@@ -108,16 +108,20 @@ struct GatedStepArgs {
   const void* q;      // (B, Hq*D)
   const void* k;      // (B, Hkv*D)
   const void* v;      // (B, Hkv*D)
-  const void* decay;  // (B, Hkv) or null
+  const void* decay;  // (B, Hkv), or (B, Hkv*D) with per_dim, or null
   const float* s_in;  // (B*Hkv, D, D) or null (zeros)
   float* s_out;       // (B*Hkv, D, D), may equal s_in
   void* out;          // (B, Hq*D)
   int32_t Hkv;
   int32_t units;  // B*Hkv
+  int32_t per_dim;
   float scale;
 };
 hipError_t launch_gated_step(int io, int D, int G, const GatedStepArgs& a, hipStream_t st);
 hipError_t launch_gated_prefix(float* ws_s, const float* ws_a, const float* s_in, int U, int nseg,
-                               int D, hipStream_t st);
+                               int D, int per_dim, hipStream_t st);
+// Per-key-dim decay (la_gated_pd.hip): the same arguments and modes as
+// launch_gated; fp32 at head size 128 is not available (LDS).
+hipError_t launch_gated_pd(int mode, int io, int D, int G, const GatedArgs& a, int grid, hipStream_t st);
 
 }  // namespace la

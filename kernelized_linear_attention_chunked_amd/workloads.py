@@ -163,6 +163,7 @@ class GatedGqaD128:
     Hkv=8 D=128, bf16, scale 1/sqrt(128), zero past state."""
 
     name = "gated_gqa_d128"
+    per_dim = 0
 
     def __init__(self, device="cuda:0"):
         w = synth.WORKLOADS[self.name]
@@ -173,7 +174,7 @@ class GatedGqaD128:
         B, T, D = self.B, self.T, self.D
         self.out = torch.empty_like(self.q)
         self.present = torch.empty((B, self.Hkv, D, D), dtype=torch.float32, device=device)
-        n = la_gated_workspace_size(B, T, self.Hq, self.Hkv, D, D, torch.bfloat16)
+        n = la_gated_workspace_size(B, T, self.Hq, self.Hkv, D, D, torch.bfloat16, bool(self.per_dim))
         self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
         self.ws_bytes = n
         self.scale = 1.0 / (D ** 0.5)
@@ -184,10 +185,17 @@ class GatedGqaD128:
         return self.B * self.T
 
     def step(self):
-        _check(self.lib.la_gated_forward(_p(self.q), _p(self.k), _p(self.v), _p(self.g), None,
+        _check(self.lib.la_gated_forward(_p(self.q), _p(self.k), _p(self.v), _p(self.g), self.per_dim, None,
                                          _p(self.present), _p(self.out), self.B, self.T, self.Hq,
                                          self.Hkv, self.D, self.D, 1, self.scale, _p(self.ws),
                                          self.ws_bytes, _stream(self.device)), "la_gated_forward")
+
+
+class GatedPerdimD128(GatedGqaD128):
+    """The same recurrence with a per-key-dim decay (B,T,Hkv*D)."""
+
+    name = "gated_perdim_d128"
+    per_dim = 1
 
 
 class GatedStepD128:
@@ -217,7 +225,7 @@ class GatedStepD128:
         return self.B * self.T
 
     def decode_call(self, t, stream=None):
-        _check(self.lib.la_gated_step(_p(self.q[t]), _p(self.k[t]), _p(self.v[t]), _p(self.g[t]),
+        _check(self.lib.la_gated_step(_p(self.q[t]), _p(self.k[t]), _p(self.v[t]), _p(self.g[t]), 0,
                                       _p(self.state), _p(self.state), _p(self.out[t]), self.B,
                                       self.Hq, self.Hkv, self.D, self.D, 1, self.scale,
                                       _stream(self.device) if stream is None else stream),
@@ -229,4 +237,4 @@ class GatedStepD128:
 
 
 DRIVERS = {c.name: c for c in (StreamingD128, CausalBf16D64, NonCausalReluD128, GatedGqaD128,
-                               GatedStepD128)}
+                               GatedPerdimD128, GatedStepD128)}

@@ -138,17 +138,23 @@ def test_step_argument_errors(lib):
 def test_gated_argument_errors(lib):
     f = fake
     n = ctypes.c_size_t(0)
-    assert lib.la_gated_workspace_size(2, 64, 6, 4, 128, 128, 1, ctypes.byref(n)) == SHAPE
-    assert lib.la_gated_workspace_size(2, 64, 48, 8, 128, 128, 1, ctypes.byref(n)) == UNSUPPORTED
-    assert lib.la_gated_workspace_size(2, 32768, 32, 8, 128, 128, 1, ctypes.byref(n)) == OK
+    assert lib.la_gated_workspace_size(2, 64, 6, 4, 128, 128, 1, 0, ctypes.byref(n)) == SHAPE
+    assert lib.la_gated_workspace_size(2, 64, 48, 8, 128, 128, 1, 0, ctypes.byref(n)) == UNSUPPORTED
+    assert lib.la_gated_workspace_size(2, 32768, 32, 8, 128, 128, 1, 0, ctypes.byref(n)) == OK
     assert n.value > 0
+    # 16 units of 512 chunks split 32 ways: D*D state slots plus the decay factors
+    # of each slot (one, or one per key dim)
+    assert n.value == 16 * 32 * 128 * 128 * 4 + 16 * 32 * 4
+    m = ctypes.c_size_t(0)
+    assert lib.la_gated_workspace_size(2, 32768, 32, 8, 128, 128, 1, 1, ctypes.byref(m)) == OK
+    assert m.value == 16 * 32 * 128 * 128 * 4 + 16 * 32 * 128 * 4
 
     def g(**kw):
-        a = dict(q=f(1 << 30), k=f(2 << 30), v=f(3 << 30), d=None, past=None, pres=f(4 << 30),
+        a = dict(q=f(1 << 30), k=f(2 << 30), v=f(3 << 30), d=None, pd=0, past=None, pres=f(4 << 30),
                  out=f(5 << 30), B=1, T=64, Hq=4, Hkv=2, Dk=64, Dv=64, dt=1, scale=0.0, ws=None,
                  wsb=0)
         a.update(kw)
-        return lib.la_gated_forward(a["q"], a["k"], a["v"], a["d"], a["past"], a["pres"], a["out"],
+        return lib.la_gated_forward(a["q"], a["k"], a["v"], a["d"], a["pd"], a["past"], a["pres"], a["out"],
                                     a["B"], a["T"], a["Hq"], a["Hkv"], a["Dk"], a["Dv"], a["dt"],
                                     ctypes.c_float(a["scale"]), a["ws"], a["wsb"], None)
 
@@ -159,6 +165,11 @@ def test_gated_argument_errors(lib):
     assert g(scale=float("inf")) == BAD_ARG
     assert g(T=4096) == WORKSPACE             # 2 units: the sequence is split
     assert g(out=f(1 << 30)) == BAD_ARG       # out aliases q
+    # fp32 per-dim decay at head size 128 over more than one token does not fit LDS
+    assert g(d=f(6 << 30), pd=1, dt=0, Dk=128, Dv=128) == UNSUPPORTED
+    # a per-dim decay overlapping out (its extent is Hkv*Dk per token)
+    assert g(d=f((5 << 30) - 64 * 2 * 64 * 2 + 16), pd=1) == BAD_ARG
+    assert g(d=f((6 << 30) + 2), pd=1) == BAD_ARG  # per-dim decays are read as 16-byte vectors
 
 
 def test_gated_step_argument_errors(lib):
@@ -168,7 +179,7 @@ def test_gated_step_argument_errors(lib):
         a = dict(q=f(1 << 30), k=f(2 << 30), v=f(3 << 30), d=None, past=f(6 << 30), pres=f(6 << 30),
                  out=f(5 << 30), B=2, Hq=8, Hkv=2, Dk=128, Dv=128, dt=2, scale=0.0)
         a.update(kw)
-        return lib.la_gated_step(a["q"], a["k"], a["v"], a["d"], a["past"], a["pres"], a["out"],
+        return lib.la_gated_step(a["q"], a["k"], a["v"], a["d"], 0, a["past"], a["pres"], a["out"],
                                  a["B"], a["Hq"], a["Hkv"], a["Dk"], a["Dv"], a["dt"],
                                  ctypes.c_float(a["scale"]), None)
 

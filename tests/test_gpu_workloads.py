@@ -155,3 +155,24 @@ def test_gated_step_d128_full():
         e1 = assert_close(out, oo, 2e-2, "out %d,%d" % (b, j))
         e2 = assert_close(d.state[b:b + 1, j:j + 1], po, 2e-2, "state %d,%d" % (b, j))
         print("unit", (b, j), "out %.2e state %.2e" % (e1, e2))
+
+
+def test_gated_perdim_d128_full():
+    """The per-key-dim decay at the GQA workload's sizes (split sequences):
+    sampled (batch, kv head) units against the oracle over all 32768 tokens."""
+    d = workloads.GatedPerdimD128(DEV)
+    G, D = d.Hq // d.Hkv, d.D
+    print("workload gated_perdim_d128", tuple(d.q.shape), "decay", tuple(d.g.shape), "workspace",
+          d.ws_bytes, flush=True)
+    d.step()
+    torch.cuda.synchronize()
+    assert torch.isfinite(d.out.float()).all()
+    for b, j in _units(d.B, d.Hkv, 3, 7):
+        qs = d.q[b:b + 1, :, j * G * D:(j + 1) * G * D]
+        ks = d.k[b:b + 1, :, j * D:(j + 1) * D]
+        vs = d.v[b:b + 1, :, j * D:(j + 1) * D]
+        gs = d.g[b:b + 1, :, j * D:(j + 1) * D]
+        oo, po = oracle.la_op(f64(qs), f64(ks), f64(vs), G, 1, "gated", decay=f64(gs), scale=d.scale)
+        e1 = assert_close(d.out[b:b + 1, :, j * G * D:(j + 1) * G * D], oo, 2e-2, "out %d,%d" % (b, j))
+        e2 = assert_close(d.present[b:b + 1, j:j + 1], po, 2e-2, "present %d,%d" % (b, j))
+        print("unit", (b, j), "out %.2e present %.2e" % (e1, e2))
