@@ -253,6 +253,12 @@ def bench_other(args, log):
         U = d.B * d.Hkv
         nbytes = d.T * (U * D * D * 4 * 2 + d.B * (d.Hq * D * 2 * 2 + d.Hkv * D * 2 * 2 + d.Hkv * 2))
         flops = d.T * (U * D * D * 3 + d.B * d.Hq * D * D * 2)  # update (3/elem), readout
+    elif args.workload == "gated_delta_d128":
+        # q, k, v, out, decay and beta once; the final state written
+        nbytes = Tt * (d.Hq * D * 2 * 2 + d.Hkv * D * 2 * 2 + d.Hkv * 2 * 2) + d.B * d.Hkv * D * D * 4
+        # per token and q head: intra (64-wide A tile and A U) and inter; per kv head:
+        # R (Kbar S), the key tiles (64 wide), the update, and the solve's products
+        flops = Tt * d.Hq * (2 * 64 * 2 * D + 2 * D * D) + Tt * d.Hkv * (2 * D * D * 2 + 2 * 64 * D * 2)
     elif args.workload in ("gated_gqa_d128", "gated_perdim_d128"):
         per_dim = args.workload == "gated_perdim_d128"
         nbytes = (Tt * (d.Hq * D * 2 * 2 + d.Hkv * D * 2 * 2 + d.Hkv * (D if per_dim else 1) * 2)
@@ -291,7 +297,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="streaming_d128",
                     choices=["streaming_d128", "causal_bf16_d64", "noncausal_relu_d128",
-                             "gated_gqa_d128", "gated_perdim_d128", "gated_step_d128"])
+                             "gated_gqa_d128", "gated_perdim_d128", "gated_delta_d128",
+                             "gated_step_d128"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

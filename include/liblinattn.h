@@ -159,6 +159,26 @@ la_status la_gated_step(const void* q, const void* k, const void* v, const void*
                         void* out, int64_t B, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
                         int32_t dtype, float scale, void* stream);
 
+/* Delta-rule recurrences with grouped-query heads (the LinearAttention operator
+ * page, ai.onnx since version 27, update rules "delta" and "gated_delta"):
+ *   delta:        S_t = S_{t-1} + beta_t k_t (v_t - S_{t-1}^T k_t)^T
+ *   gated_delta:  S_t = E_t S_{t-1} + beta_t k_t (v_t - (E_t S_{t-1})^T k_t)^T,
+ *                 E_t = exp(g_t) (per kv head) or diag(exp(g_t)) (per key dim)
+ *   o_t = scale * q_t^T S_t   (per query head, S after the update)
+ * decay == NULL selects "delta"; otherwise decay is (B,T,Hkv) or, with
+ * per_dim_decay, (B,T,Hkv*Dk), log-space.  beta (required) is (B,T,Hkv) with
+ * beta_per_head, else (B,T,1) shared by all kv heads.  Other layouts, dtypes,
+ * scale, past/present state and GQA as la_gated_forward; keys are expected
+ * L2-normalised (operator page, "Inputs").  Evaluated chunk-parallel (64-token
+ * chunks, a 64 x 64 triangular solve per chunk) by one workgroup per (batch,
+ * kv head) over the whole sequence; no workspace.  The per-dim decay range of
+ * la_gated_forward applies; fp32 inputs at Dk = 128 return LA_ERR_UNSUPPORTED. */
+la_status la_delta_forward(const void* q, const void* k, const void* v, const void* decay,
+                           int32_t per_dim_decay, const void* beta, int32_t beta_per_head,
+                           const float* past_state, float* present_state, void* out, int64_t B,
+                           int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv, int32_t dtype,
+                           float scale, void* stream);
+
 /* Static string naming a status code. */
 const char* la_status_string(la_status s);
 

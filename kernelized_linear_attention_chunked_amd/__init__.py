@@ -17,6 +17,7 @@ Functions carry the C names:
 * :func:`la_gated_forward` -- gated / linear recurrence with GQA (the
   LinearAttention operator page, ai.onnx since version 27).
 * :func:`la_gated_step` -- one token of that recurrence (decode).
+* :func:`la_delta_forward` -- the delta / gated-delta rules of the same operator.
 """
 from __future__ import annotations
 
@@ -30,13 +31,14 @@ from .build import LIB_PATH, build as _build
 
 __all__ = [
     "LinAttnError", "la_initial_state", "la_forward", "la_step", "la_gated_forward",
-    "la_gated_step", "la_workspace_size", "la_gated_workspace_size", "library_path", "load_library",
+    "la_gated_step", "la_delta_forward", "la_workspace_size", "la_gated_workspace_size", "library_path", "load_library",
     "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
     "la_initial_state", "la_workspace_size", "la_forward", "la_step", "la_gated_workspace_size",
-    "la_gated_forward", "la_gated_step", "la_status_string", "la_last_error_message",
+    "la_gated_forward", "la_gated_step", "la_delta_forward", "la_status_string",
+    "la_last_error_message",
 )
 
 _FM = {"elu_plus_one": 0, "relu": 1}
@@ -82,8 +84,11 @@ def load_library(build_if_missing: bool = True):
         lib.la_gated_forward.argtypes = [p, p, p, p, i32, p, p, p, i64, i64, i64, i64, i64, i64, i32,
                                          f32, p, sz, p]
         lib.la_gated_step.argtypes = [p, p, p, p, i32, p, p, p, i64, i64, i64, i64, i64, i32, f32, p]
+        lib.la_delta_forward.argtypes = [p, p, p, p, i32, p, i32, p, p, p, i64, i64, i64, i64, i64, i64,
+                                         i32, f32, p]
         for name in ("la_initial_state", "la_workspace_size", "la_forward", "la_step",
-                     "la_gated_workspace_size", "la_gated_forward", "la_gated_step"):
+                     "la_gated_workspace_size", "la_gated_forward", "la_gated_step",
+                     "la_delta_forward"):
             getattr(lib, name).restype = ctypes.c_int
         lib.la_status_string.argtypes = [ctypes.c_int]
         lib.la_status_string.restype = ctypes.c_char_p
@@ -328,3 +333,40 @@ def la_gated_step(query, key, value, q_num_heads, kv_num_heads, decay=None, past
                              _ptr(out), B, Hq, Hkv, Dk, Dv, _dtype_code(q), float(scale), _stream(dev)),
            "la_gated_step")
     return (out[:, None] if squeeze else out), present_state
+
+
+def la_delta_forward(query, key, value, q_num_heads, kv_num_heads, beta, decay=None, past_state=None,
+                     scale=0.0, out=None, present_state=None):
+    """Delta rule (``decay`` None) or gated delta rule on packed (B,T,H*D) tensors
+    with GQA.  ``beta``: (B,T,Hkv) or (B,T,1); ``decay``: log-space, (B,T,Hkv)
+    or (B,T,Hkv*Dk).  Returns ``(output (B,T,Hq*Dv), present_state (B,Hkv,Dk,Dv)
+    float32)``.
+    """
+    _need_cuda(query, key, value, beta, decay, past_state)
+    q, k, v, g, be = _contig(query), _contig(key), _contig(value), _contig(decay), _contig(beta)
+    B, T, qw = q.shape
+    Hq, Hkv = int(q_num_heads), int(kv_num_heads)
+    if Hq < 1 or Hkv < 1 or qw % Hq or k.shape[-1] % Hkv or v.shape[-1] % Hkv:
+        raise ValueError("head counts do not divide the packed widths")
+    Dk = qw // Hq
+    Dv = v.shape[-1] // Hkv
+    dev = q.device
+    lib = load_library()
+    per_dim = g is not None and tuple(g.shape) == (B, T, Hkv * Dk) and Dk > 1
+    if g is not None and not per_dim and tuple(g.shape) != (B, T, Hkv):
+        raise ValueError("decay must be (B,T,Hkv) (per kv head) or (B,T,Hkv*Dk) (per key dim)")
+    if tuple(be.shape) not in ((B, T, Hkv), (B, T, 1)):
+        raise ValueError("beta must be (B,T,Hkv) or (B,T,1)")
+    beta_per_head = tuple(be.shape) == (B, T, Hkv) and Hkv > 1
+    for t in (g, be):
+        if t is not None and t.dtype != q.dtype:
+            raise ValueError("decay and beta must have the dtype of the query")
+    if out is None:
+        out = torch.empty((B, T, Hq * Dv), dtype=q.dtype, device=dev)
+    if present_state is None:
+        present_state = torch.empty((B, Hkv, Dk, Dv), dtype=torch.float32, device=dev)
+    _check(lib.la_delta_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), int(per_dim), _ptr(be),
+                                int(beta_per_head), _ptr(_contig(past_state)), _ptr(present_state),
+                                _ptr(out), B, T, Hq, Hkv, Dk, Dv, _dtype_code(q), float(scale),
+                                _stream(dev)), "la_delta_forward")
+    return out, present_state

@@ -631,3 +631,69 @@ LA_EXPORT la_status la_gated_step(const void* q, const void* k, const void* v, c
                              dtype, scale, (hipStream_t)stream);
   return device_status(e, "la_gated_step");
 }
+
+// ---------------------------------------------------------------------------
+// delta rules
+
+LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v, const void* decay,
+                                     int32_t per_dim_decay, const void* beta, int32_t beta_per_head,
+                                     const float* past_state, float* present_state, void* out,
+                                     int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,
+                                     int64_t Dv, int32_t dtype, float scale, void* stream) {
+  la_status s = check_gated(B, T, Hq, Hkv, Dk, Dv, dtype);
+  if (s != LA_OK) return s;
+  if (isnan(scale) || isinf(scale)) return fail(LA_ERR_BAD_ARG, "scale must be finite");
+  const int64_t D = Dk, U = B * Hkv, G = Hq / Hkv;
+  const int64_t esz = dtype_size(dtype);
+  const bool per_dim = per_dim_decay != 0 && decay != nullptr;
+  if (dtype == LA_DT_F32 && D == 128 && T > 0)
+    return fail(LA_ERR_UNSUPPORTED, "delta rules with fp32 inputs at head size 128");
+  if (U > 0 && !present_state) return fail(LA_ERR_NULL_ARG, "present_state is required");
+  const bool work = U > 0 && T > 0;
+  if (work && (!q || !k || !v || !out || !beta))
+    return fail(LA_ERR_NULL_ARG, "q, k, v, beta and out are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(past_state) ||
+      !aligned16(present_state) || (per_dim && !aligned16(decay)))
+    return fail(LA_ERR_BAD_ARG, "q, k, v, out, a per-dim decay and the states must be 16-byte aligned");
+  const int64_t bh = beta_per_head ? Hkv : 1;
+  const Range rq = range(q, B * T * Hq * D * esz), rk = range(k, B * T * Hkv * D * esz);
+  const Range rv = range(v, B * T * Hkv * D * esz), ro = range(out, B * T * Hq * D * esz);
+  const Range rg = range(decay, B * T * Hkv * (per_dim ? D : 1) * esz), rb = range(beta, B * T * bh * esz);
+  const Range rpi = range(past_state, U * D * D * 4), rpo = range(present_state, U * D * D * 4);
+  const Range ins[5] = {rq, rk, rv, rg, rb};
+  for (const Range& i : ins)
+    if (overlap(ro, i) || overlap(rpo, i)) return fail(LA_ERR_BAD_ARG, "an output overlaps an input");
+  if (overlap(ro, rpi) || overlap(ro, rpo)) return fail(LA_ERR_BAD_ARG, "out overlaps a state buffer");
+  if (overlap(rpo, rpi) && present_state != past_state)
+    return fail(LA_ERR_BAD_ARG, "present_state may equal past_state exactly but not partially overlap it");
+  if (U > (int64_t)1 << 31) return fail(LA_ERR_SHAPE, "too many (batch, kv head) units");
+  if (scale == 0.f) scale = 1.f / sqrtf((float)D);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (!work) {
+    if (U > 0)
+      e = past_state ? (present_state != past_state
+                            ? la::launch_copy(present_state, past_state, U * D * D, st)
+                            : hipSuccess)
+                     : la::launch_fill_zero(present_state, U * D * D, st);
+    return device_status(e, "la_delta_forward");
+  }
+  la::DeltaArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.decay = decay;
+  a.beta = beta;
+  a.out = out;
+  a.s_in = past_state;
+  a.s_out = present_state;
+  a.T = (int32_t)T;
+  a.Hq = (int32_t)Hq;
+  a.Hkv = (int32_t)Hkv;
+  a.units = (int32_t)U;
+  a.beta_heads = (int32_t)bh;
+  a.scale = scale;
+  const int kind = decay == nullptr ? 0 : (per_dim ? 2 : 1);
+  e = la::launch_delta(dtype, (int)D, (int)G, kind, a, st);
+  return device_status(e, "la_delta_forward");
+}

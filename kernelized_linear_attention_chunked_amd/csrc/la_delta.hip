@@ -1,0 +1,750 @@
+// Delta-rule recurrences with grouped query heads (the LinearAttention operator
+// page, ai.onnx since version 27, update rules "delta" and "gated_delta"): per
+// kv head and token,
+//   S_t = D_t S_{t-1} + beta_t k_t (v_t - (D_t S_{t-1})^T k_t)^T,   o_t = scale q_t^T S_t,
+// with D_t = I ("delta"), or diag(exp(g_t)) for a log-space decay g_t given per
+// kv head or per key dimension ("gated_delta"), and beta_t per kv head or
+// shared by all heads.
+//
+// Chunk-parallel form over chunks of 64 tokens (the delta rule's WY-style
+// chunking).  With b_t the inclusive cumulative decay inside the chunk (per key
+// dim; 0 without a decay), G_t = diag(e^{b_t}) and S_0 the state before it:
+//   S_t = G_t X_t,  X_t = X_{t-1} + (G_t^-1 k_t) u_t^T,  X_{-1} = S_0,
+//   u_t = beta_t (v_t - S_0^T (G_t k_t) - sum_{j<t} L_tj u_j),
+//   L_tj = sum_d k_td k_jd e^{b_td - b_jd}          (j < t),
+// which follows from substituting S_t = G_t X_t into the recurrence.  So the
+// pseudo-values U solve the unit lower-triangular system
+//   (I + diag(beta) L) U = diag(beta) (V - Kbar S_0),   Kbar = rows k_t e^{b_t},
+// and then, exactly as for the per-dim gated rule with U in place of V,
+//   o_t  = scale [ (q_t . e^{b_t})^T S_0 + sum_{j<=t} A_tj u_j ],
+//   A_tj = sum_d q_td k_jd e^{b_td - b_jd},
+//   S_C  = diag(e^{b_C}) S_0 + sum_j diag(e^{b_C - b_j}) k_j u_j^T.
+// L and A use the per-dim kernel's block-relative rescaling of the keys
+// (la_gated_pd.hip), with hi + lo bf16 operands for 16-bit inputs.
+//
+// The system is solved in four blocks of 16 rows, one after the other: the
+// waves of row block i subtract the earlier blocks' contributions with MFMAs
+// over U (hi + lo), then run a forward substitution over their own 16 rows in
+// registers (lane shuffles), and write their rows of U^T over the V^T tiles.
+// A sequence is processed by one workgroup from start to end (no split over T:
+// a segment's transition is a full D x D matrix, not a diagonal).
+#include "la_device.hpp"
+#include "la_launch.hpp"
+
+namespace la {
+
+template <int G>
+struct DeltaShape {
+  static constexpr int P = G >= 2 ? 2 : 1;  // head parts (and dv halves) per workgroup
+  static constexpr int NW = 4 * P;          // wavefronts
+  static constexpr int NTH = 64 * NW;       // threads
+  static constexpr int HPW = G / P;         // query heads per wave
+};
+
+// DK: 0 no decay ("delta"), 1 one decay per kv head, 2 one per key dimension.
+template <typename IT, int D, int G, int DK>
+__global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) {
+  using DT = typename Io<IT>::DT;
+  using O = Op<DT>;
+  using SH = DeltaShape<G>;
+  constexpr int P = SH::P, NW = SH::NW, NTH = SH::NTH, HPW = SH::HPW;
+  constexpr int VEC = O::VEC, KB = O::KB, ESZ = O::ESZ;
+  constexpr int NDT = D / 16;
+  constexpr int RH = NDT / P;  // dv tiles of a wave in the solve
+  constexpr int CB = D / VEC;
+  constexpr int LOADERS = (kChunk * CB / NTH >= 2 || ESZ == 4) ? (NTH < kChunk * CB ? NTH : kChunk * CB)
+                                                                : kChunk * CB / 2;
+  constexpr int NTOK = kChunk * CB / LOADERS;
+  constexpr int TW = (64 / CB) * NTOK;  // tokens of one loader wave
+  constexpr int NQ = D / KB;
+  constexpr int NKS = kChunk / KB;
+  constexpr int PADE = 16 / ESZ;
+  constexpr int KN_LD = D + PADE;
+  constexpr int VT_LD = kChunk;
+  constexpr int SB_LD = D + PADE;
+  constexpr int BC_LD = D + 4;
+  constexpr int LB_LD = 17;       // fp32 rows of a wave's 16 x 16 diagonal block of L
+  constexpr bool LO = ESZ == 2;   // 16-bit: hi + lo operands (k^, q^, U, L, A)
+  constexpr int KN_BYTES = kChunk * KN_LD * ESZ;
+  constexpr int VT_BYTES = D * VT_LD * ESZ;
+  constexpr int SB_BYTES = D * SB_LD * ESZ;
+  // the per-dim decay table only for per-dim decays; without it, the LDS holds
+  // a lo part of S (16-bit), used where S_0 meets the state (R) and the outputs
+  constexpr int BC_BYTES = DK == 2 ? kChunk * BC_LD * 4 : 0;
+  constexpr bool SLO = LO && DK != 2;
+  constexpr int SL_BYTES = SLO ? SB_BYTES : 0;
+  constexpr int WT_BYTES = NW * D * 4;
+  constexpr int BT_BYTES = 2 * kChunk * 4;  // beta and the per-head cumulative decay
+  constexpr int LB_BYTES = NW * 16 * LB_LD * 4;
+  constexpr int LDS = (LO ? 2 : 1) * (KN_BYTES + VT_BYTES) + SB_BYTES + SL_BYTES + BC_BYTES + WT_BYTES + BT_BYTES +
+                      LB_BYTES;
+  constexpr int NS = NDT * NDT;
+  constexpr int TPW = (NS + NW - 1) / NW;
+  static_assert(NTOK >= 1 && NQ >= 1 && CB <= 64 && 64 % CB == 0 && RH * P == NDT, "unsupported head size");
+  static_assert(ESZ == 4 || NTOK % 2 == 0, "bf16 V^T writes pack token pairs");
+  static_assert(32 % TW == 0 && LOADERS % 64 == 0, "whole loader waves cover tokens 0..31");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+
+  __shared__ __align__(16) unsigned char smem[LDS + 16];
+  unsigned char* sp = smem;
+  auto carve = [&](int bytes) {
+    unsigned char* p = sp;
+    sp += bytes;
+    return p;
+  };
+  DT* Kh = (DT*)carve(KN_BYTES);                  // k^ = k e^{c_sigma - b} (hi)
+  DT* Kl = (DT*)carve(LO ? KN_BYTES : 0);         // its lo part
+  DT* Vt = (DT*)carve(VT_BYTES);                  // V^T, then U^T (hi)
+  DT* Vl = (DT*)carve(LO ? VT_BYTES : 0);         // lo parts
+  DT* Sb = (DT*)carve(SB_BYTES);                  // S^T of the state before the chunk
+  DT* Sl = (DT*)carve(SL_BYTES);                  // its lo part (SLO)
+  float* Bc = (float*)carve(BC_BYTES);            // b_t per key dim (DK == 2)
+  float* Wt = (float*)carve(WT_BYTES);            // loader-wave totals of the scan
+  float* Bt = (float*)carve(BT_BYTES);            // beta_t, then (per-head decay) b_t
+  float* Lb = (float*)carve(LB_BYTES);            // per wave: L of its diagonal block
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hp = w >> 2, wr = w & 3;
+  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int u = blockIdx.x;
+  const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
+  const int b = u / Hkv, j = u % Hkv;
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const int QS = Hq * D, KS = Hkv * D;
+  const IT* qb = (const IT*)a.q + (int64_t)b * T * QS + (int64_t)(j * G) * D;
+  IT* ob = (IT*)a.out + (int64_t)b * T * QS + (int64_t)(j * G) * D;
+  const IT* kb = (const IT*)a.k + (int64_t)b * T * KS + (int64_t)j * D;
+  const IT* vb = (const IT*)a.v + (int64_t)b * T * KS + (int64_t)j * D;
+  const IT* gb = DK == 2 ? (const IT*)a.decay + (int64_t)b * T * KS + (int64_t)j * D
+                         : (DK == 1 ? (const IT*)a.decay + (int64_t)b * T * Hkv + j : nullptr);
+  const IT* betab = (const IT*)a.beta + (int64_t)b * T * a.beta_heads + (a.beta_heads > 1 ? j : 0);
+  const float scale = a.scale;
+  auto vt_at = [&](int r, int blk) { return r * VT_LD + ((blk ^ vt_swz(r)) * VEC); };
+  auto kn_at = [&](int t, int col) {
+    return t * KN_LD + (((col / VEC) ^ (kn_swz(t) & (CB - 1))) * VEC) + (col % VEC);
+  };
+  auto sq_at = [&](int r, int col) {
+    return r * SB_LD + (((col / VEC) ^ sq_swz(r)) * VEC) + (col % VEC);
+  };
+  auto to_f = [&](DT x) -> float {
+    if constexpr (ESZ == 2) return bf16_bits_to_f32(x);
+    else return x;
+  };
+  // fp32 value -> operand hi (and lo) words, for pairs packed the way O::pack does
+  auto split8 = [&](const float (&f)[VEC], u32x4_t& hi, u32x4_t& lo) {
+    hi = O::pack(f);
+    if constexpr (LO) {
+      float r[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) r[e] = f[e] - bf16_bits_to_f32((hi[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+      lo = O::pack(r);
+    }
+  };
+
+  // ---- state tiles: wave w owns tiles tau = w*TPW + i (rows rt, columns ct)
+  f32x4_t sacc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) sacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (a.s_in) {
+    const float* sin = a.s_in + (int64_t)u * D * D;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tau = w * TPW + i;
+      if (tau < NS) {
+        const int rt = tau / NDT, ct = tau % NDT;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sacc[i][q] = sin[(16 * rt + 4 * lg + q) * D + 16 * ct + lr];
+      }
+    }
+  }
+  auto write_sb = [&]() {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tau = w * TPW + i;
+      if (tau < NS) {
+        const int rt = tau / NDT, ct = tau % NDT;
+        const int off = sq_at(16 * ct + lr, 16 * rt + 4 * lg);
+        DT* p = Sb + off;
+        if constexpr (ESZ == 2) {
+          u32x2_t v2;
+          v2[0] = pack_bf16x2(sacc[i][0], sacc[i][1]);
+          v2[1] = pack_bf16x2(sacc[i][2], sacc[i][3]);
+          *(u32x2_t*)p = v2;
+          if constexpr (SLO) {
+            u32x2_t l2;
+            l2[0] = pack_bf16x2(sacc[i][0] - __uint_as_float(v2[0] << 16), sacc[i][1] - __uint_as_float(v2[0] & 0xffff0000u));
+            l2[1] = pack_bf16x2(sacc[i][2] - __uint_as_float(v2[1] << 16), sacc[i][3] - __uint_as_float(v2[1] & 0xffff0000u));
+            *(u32x2_t*)(Sl + off) = l2;
+          }
+        } else {
+          *(f32x4_t*)p = sacc[i];
+        }
+      }
+    }
+  };
+  write_sb();
+
+  const int cb = tid % CB, tg = tid / CB;
+  const bool loader = tid < LOADERS;
+  u32x4_t pk[NTOK], pv[NTOK], pg[DK == 2 ? NTOK : 1];
+
+  auto write_vt = [&](DT* base, const u32x4_t (&src)[NTOK]) {
+    const int t0 = tg * NTOK;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const int r = cb * VEC + e;
+      if constexpr (ESZ == 2) {
+#pragma unroll
+        for (int n = 0; n < NTOK; n += 2) {
+          const uint32_t w0 = src[n][e >> 1], w1 = src[n + 1][e >> 1];
+          *(uint32_t*)(base + vt_at(r, (t0 + n) / VEC) + (t0 + n) % VEC) =
+              (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u) : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+        }
+      } else {
+        float fv[NTOK];
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n) fv[n] = __uint_as_float(src[n][e]);
+        DT* p = base + vt_at(r, t0 / VEC) + (t0 % VEC);
+        if constexpr (NTOK == 1) {
+          *(float*)p = fv[0];
+        } else if constexpr (NTOK == 2) {
+          *(float2*)p = make_float2(fv[0], fv[1]);
+        } else {
+#pragma unroll
+          for (int n = 0; n < NTOK; n += 4)
+            *(f32x4_t*)(base + vt_at(r, (t0 + n) / VEC)) = f32x4_t{fv[n], fv[n + 1], fv[n + 2], fv[n + 3]};
+        }
+      }
+    }
+  };
+
+
+  // a scalar of the I/O type (beta, a per-head decay) as fp32
+  auto ld1 = [&](const IT* p) -> float {
+    if constexpr (sizeof(IT) == 2) return Io<IT>::to_f32(*(const uint16_t*)p);
+    else return *(const float*)p;
+  };
+
+  // ---- stage: beta and b_t (per-head decays: wave 0's scan), V^T (hi + lo),
+  // b_t -> Bc, k^ = k e^{c_sigma - b} (hi + lo) -> Kh, Kl.  Two barriers.
+  auto stage = [&](int c) {
+    const int tb = c * kChunk;
+    if (w == 0) {
+      const int tok = tb + l;
+      const bool ok = tok < T;
+      const int tc = min(tok, T - 1);
+      const float be = ld1(betab + (int64_t)tc * a.beta_heads);
+      Bt[l] = ok ? be : 0.f;  // tokens past the end: beta = 0, so u = 0
+      if constexpr (DK == 1) {
+        float x = ok ? ld1(gb + (int64_t)tc * Hkv) : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(x, off);
+          if (l >= off) x += y;
+        }
+        Bt[kChunk + l] = x;
+      }
+    }
+    float bx[NTOK][VEC];
+    float tot[VEC];
+    if (loader) {
+#pragma unroll
+      for (int n = 0; n < NTOK; ++n) {
+        const int tok = tb + tg * NTOK + n;
+        const int64_t off = (int64_t)min(tok, T - 1) * KS + cb * VEC;
+        pk[n] = ld16(kb + off);
+        pv[n] = ld16(vb + off);
+        if constexpr (DK == 2) pg[n] = ld16(gb + off);
+        if (tok >= T) {
+          pk[n] = u32x4_t{0u, 0u, 0u, 0u};
+          pv[n] = u32x4_t{0u, 0u, 0u, 0u};
+          if constexpr (DK == 2) pg[n] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+      if constexpr (LO) {
+        u32x4_t pl[NTOK];
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n) {
+          float f[VEC];
+          Io<IT>::unpack(pv[n], f);
+          split8(f, pv[n], pl[n]);
+        }
+        write_vt(Vl, pl);
+      }
+      write_vt(Vt, pv);
+      if constexpr (DK == 2) {
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n) Io<IT>::unpack(pg[n], bx[n]);
+#pragma unroll
+        for (int n = 1; n < NTOK; ++n)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) bx[n][e] += bx[n - 1][e];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          float x = bx[NTOK - 1][e];
+          const float own = x;
+#pragma unroll
+          for (int k = CB; k < 64; k <<= 1) {
+            const float y = __shfl_up(x, k);
+            if (l >= k) x += y;
+          }
+          tot[e] = x - own;
+          if (l >= 64 - CB) Wt[w * D + cb * VEC + e] = x;
+        }
+      }
+    }
+    __syncthreads();
+    if (loader) {
+      float c32[VEC];
+      if constexpr (DK == 2) {
+        float off[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          off[e] = tot[e];
+          c32[e] = 0.f;
+        }
+        for (int w2 = 0; w2 < w; ++w2) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) off[e] += Wt[w2 * D + cb * VEC + e];
+        }
+        constexpr int W32 = 32 / TW;
+#pragma unroll
+        for (int w2 = 0; w2 < W32; ++w2)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) c32[e] += Wt[w2 * D + cb * VEC + e];
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) bx[n][e] += off[e];
+      } else {
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n) {
+          const float bt = DK == 1 ? Bt[kChunk + tg * NTOK + n] : 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) bx[n][e] = bt;
+        }
+        const float c31 = DK == 1 ? Bt[kChunk + 31] : 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) c32[e] = c31;
+      }
+#pragma unroll
+      for (int n = 0; n < NTOK; ++n) {
+        const int t = tg * NTOK + n;
+        if constexpr (DK == 2) {
+#pragma unroll
+          for (int e = 0; e < VEC; e += 4)
+            *(f32x4_t*)(Bc + t * BC_LD + cb * VEC + e) = f32x4_t{bx[n][e], bx[n][e + 1], bx[n][e + 2], bx[n][e + 3]};
+        }
+        float kx[VEC], kh[VEC];
+        Io<IT>::unpack(pk[n], kx);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) kh[e] = kx[e] * __expf((t >= 32 ? c32[e] : 0.f) - bx[n][e]);
+        u32x4_t hi, lo;
+        split8(kh, hi, lo);
+        st16(Kh + kn_at(t, cb * VEC), hi);
+        if constexpr (LO) st16(Kl + kn_at(t, cb * VEC), lo);
+      }
+    }
+    __syncthreads();
+  };
+
+  // Row tq's vector x (operand layout, raw I/O words), times e^{b_tq - c} with
+  // c = 0 (second == false) or b_31, split into hi (+ lo) operands.  The row
+  // offsets pass through an empty asm so that each use recomputes the factors
+  // instead of the compiler keeping them live across heads.
+  const int tq = 16 * wr + lr;
+  auto scaled = [&](const u32x4_t (&x)[NQ], u32x4_t (&hi)[NQ], u32x4_t (&lo)[LO ? NQ : 1], bool second) {
+    int rt_off = tq * BC_LD, r31_off = 31 * BC_LD;
+    asm volatile("" : "+v"(rt_off), "+v"(r31_off));
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+      const int d0 = KB * m + VEC * lg;
+      float f[VEC];
+      Io<IT>::unpack(x[m], f);
+      if constexpr (DK == 2) {
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+          const f32x4_t bt = *(const f32x4_t*)(Bc + rt_off + d0 + e);
+          f32x4_t cs = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (second) cs = *(const f32x4_t*)(Bc + r31_off + d0 + e);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) f[e + i] *= __expf(bt[i] - cs[i]);
+        }
+      } else if constexpr (DK == 1) {
+        const float fac = __expf(Bt[kChunk + tq] - (second ? Bt[kChunk + 31] : 0.f));
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) f[e] *= fac;
+      }
+      u32x4_t h, lw;
+      split8(f, h, lw);
+      hi[m] = h;
+      if constexpr (LO) lo[m] = lw;
+    }
+  };
+  // key row of A^T / L^T tile t (bf16: tile pairs over 32 keys with permuted
+  // rows, element q of tile t at key key_of(t, q); fp32: 16-key tiles)
+  auto key_of = [&](int t, int q) {
+    return ESZ == 2 ? 32 * (t >> 1) + 8 * lg + 4 * (t & 1) + q : 16 * t + 4 * lg + q;
+  };
+  // unmasked tile t of (k^ rows) x (the lane's scaled row): Kh xh + Kl xh + Kh xl
+  auto k_tile = [&](int t, const u32x4_t (&xh)[NQ], const u32x4_t (&xl)[LO ? NQ : 1]) {
+    f32x4_t at = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int krow = ESZ == 2 ? 32 * (t >> 1) + 8 * (lr >> 2) + 4 * (t & 1) + (lr & 3) : 16 * t + lr;
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+      const u32x4_t kh = ld16(Kh + kn_at(krow, KB * m + VEC * lg));
+      O::mma(at, kh, xh[m]);
+      if constexpr (LO) {
+        O::mma(at, ld16(Kl + kn_at(krow, KB * m + VEC * lg)), xh[m]);
+        O::mma(at, kh, xl[m]);
+      }
+    }
+    return at;
+  };
+  // bf16 hi + lo B operands of a tile pair (keys of pair p along the contraction)
+  auto pair_operands = [&](const f32x4_t& at0, const f32x4_t& at1, u32x4_t& bh, u32x4_t& bl) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f32x4_t& at = (e >> 1) ? at1 : at0;
+      const float x0 = at[2 * (e & 1)], x1 = at[2 * (e & 1) + 1];
+      const uint32_t hw = pack_bf16x2(x0, x1);
+      bh[e] = hw;
+      bl[e] = pack_bf16x2(x0 - __uint_as_float(hw << 16), x1 - __uint_as_float(hw & 0xffff0000u));
+    }
+  };
+
+  // ---- pseudo-values: R = beta (V - Kbar S_0) for the wave's 16 rows and dv
+  // tiles hp*RH .. hp*RH + RH - 1, then the blocked solve.  Four barriers.
+  auto solve = [&](int c) {
+    const int tokc = min(c * kChunk + tq, T - 1);
+    const float bet = Bt[tq];
+    u32x4_t kr[NQ];
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) kr[m] = ld16(kb + (int64_t)tokc * KS + KB * m + VEC * lg);
+    u32x4_t k0h[NQ], k0l[LO ? NQ : 1];
+    scaled(kr, k0h, k0l, false);  // kbar, also the first key block's scaled row
+    f32x4_t val[RH];
+#pragma unroll
+    for (int i = 0; i < RH; ++i) val[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+#pragma unroll
+      for (int i = 0; i < RH; ++i) {
+        const int so = sq_at(16 * (hp * RH + i) + lr, KB * m + VEC * lg);
+        const u32x4_t av = ld16(Sb + so);
+        O::mma(val[i], av, k0h[m]);
+        if constexpr (LO) O::mma(val[i], av, k0l[m]);
+        if constexpr (SLO) O::mma(val[i], ld16(Sl + so), k0h[m]);
+      }
+    }
+    // the lane holds token tq, value dims 16 ct + 4 lg + q
+    auto vt_elem = [&](int row) { return vt_at(row, tq / VEC) + tq % VEC; };
+#pragma unroll
+    for (int i = 0; i < RH; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int off = vt_elem(16 * (hp * RH + i) + 4 * lg + q);
+        float v = to_f(Vt[off]);
+        if constexpr (LO) v += to_f(Vl[off]);
+        val[i][q] = bet * (v - val[i][q]);
+      }
+    float* lb = Lb + w * 16 * LB_LD;
+    for (int blk = 0; blk < 4; ++blk) {
+      if (wr == blk) {
+        u32x4_t k1h[NQ], k1l[LO ? NQ : 1];
+        if (blk >= 2) scaled(kr, k1h, k1l, true);
+        // earlier blocks: val -= beta_t sum_{j < 16 blk} L_tj u_j, over U^T (hi + lo)
+        if (blk > 0) {
+          f32x4_t cacc[RH];
+#pragma unroll
+          for (int i = 0; i < RH; ++i) cacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if constexpr (ESZ == 2) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              if (32 * p < 16 * blk) {
+                f32x4_t at0 = p == 0 ? k_tile(0, k0h, k0l) : k_tile(2, k1h, k1l);
+                f32x4_t at1 = p == 0 ? k_tile(1, k0h, k0l) : k_tile(3, k1h, k1l);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  at0[q] = key_of(2 * p, q) < 16 * blk ? at0[q] : 0.f;
+                  at1[q] = key_of(2 * p + 1, q) < 16 * blk ? at1[q] : 0.f;
+                }
+                u32x4_t bh, bl;
+                pair_operands(at0, at1, bh, bl);
+#pragma unroll
+                for (int i = 0; i < RH; ++i) {
+                  const int r = 16 * (hp * RH + i) + lr;
+                  const u32x4_t uh = ld16(Vt + vt_at(r, 4 * p + lg));
+                  O::mma(cacc[i], uh, bh);
+                  O::mma(cacc[i], uh, bl);
+                  O::mma(cacc[i], ld16(Vl + vt_at(r, 4 * p + lg)), bh);
+                }
+              }
+            }
+          } else {
+#pragma unroll
+            for (int jt = 0; jt < 3; ++jt) {
+              if (jt < blk) {
+                const f32x4_t at = jt < 2 ? k_tile(jt, k0h, k0l) : k_tile(jt, k1h, k1l);
+#pragma unroll
+                for (int i = 0; i < RH; ++i) {
+                  const u32x4_t uv = ld16(Vt + vt_at(16 * (hp * RH + i) + lr, 4 * jt + lg));
+#pragma unroll
+                  for (int q = 0; q < 4; ++q)
+                    cacc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(uv[q]), at[q], cacc[i], 0, 0, 0);
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < RH; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) val[i][q] -= bet * cacc[i][q];
+        }
+        // the block's own strictly lower L (fp32 accumulators) -> lb[t][j]
+        if constexpr (ESZ == 2) {
+          const int p = blk >> 1;
+          const f32x4_t at0 = p == 0 ? k_tile(0, k0h, k0l) : k_tile(2, k1h, k1l);
+          const f32x4_t at1 = p == 0 ? k_tile(1, k0h, k0l) : k_tile(3, k1h, k1l);
+#pragma unroll
+          for (int odd = 0; odd < 2; ++odd)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int jl = key_of(2 * p + odd, q) - 16 * blk;
+              if (jl >= 0 && jl < 16) lb[lr * LB_LD + jl] = jl < lr ? (odd ? at1[q] : at0[q]) : 0.f;
+            }
+        } else {
+          const f32x4_t at = blk < 2 ? k_tile(blk, k0h, k0l) : k_tile(blk, k1h, k1l);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) lb[lr * LB_LD + 4 * lg + q] = 4 * lg + q < lr ? at[q] : 0.f;
+        }
+        // forward substitution over the block's rows (one wave: its LDS
+        // accesses stay in order); lane lr = jl holds u_jl after step jl
+#pragma unroll
+        for (int jl = 0; jl < 16; ++jl) {
+          const float coef = bet * lb[lr * LB_LD + jl];
+#pragma unroll
+          for (int i = 0; i < RH; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float uj = __shfl(val[i][q], jl + 16 * lg);
+              val[i][q] -= coef * uj;
+            }
+        }
+        // rows of U^T (hi + lo) over the consumed V^T columns of this block
+#pragma unroll
+        for (int i = 0; i < RH; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int off = vt_elem(16 * (hp * RH + i) + 4 * lg + q);
+            const float x = val[i][q];
+            if constexpr (LO) {
+              const uint32_t hb = f32_to_bf16_bits(x);
+              Vt[off] = (uint16_t)hb;
+              Vl[off] = (uint16_t)f32_to_bf16_bits(x - bf16_bits_to_f32(hb));
+            } else {
+              Vt[off] = x;
+            }
+          }
+      }
+      __syncthreads();
+    }
+  };
+
+  // ---- outputs of the chunk's queries (per head), with U in V's place
+  auto outputs = [&](int c) {
+    const int tok = c * kChunk + tq;
+    const int tokc = min(tok, T - 1);
+    auto need = [&](int t) { return ESZ == 2 ? (32 * (t >> 1) <= 16 * wr + 15) : (t <= wr); };
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int hq = hp + P * hh;
+      u32x4_t qr[NQ];
+#pragma unroll
+      for (int m = 0; m < NQ; ++m) qr[m] = ld16(qb + (int64_t)tokc * QS + hq * D + KB * m + VEC * lg);
+      u32x4_t qop[NQ], qlo[LO ? NQ : 1];
+      scaled(qr, qop, qlo, false);
+      auto a_tile = [&](int t) {
+        f32x4_t at = k_tile(t, qop, qlo);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) at[q] = key_of(t, q) <= tq ? at[q] : 0.f;
+        return at;
+      };
+      f32x4_t a0[2];
+      a0[0] = a_tile(0);
+      a0[1] = need(1) ? a_tile(1) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      f32x4_t nacc[NDT];
+#pragma unroll
+      for (int ct = 0; ct < NDT; ++ct) nacc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < NQ; ++m) {
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct) {
+          const int so = sq_at(16 * ct + lr, KB * m + VEC * lg);
+          const u32x4_t av = ld16(Sb + so);
+          O::mma(nacc[ct], av, qop[m]);
+          if constexpr (LO) O::mma(nacc[ct], av, qlo[m]);
+          if constexpr (SLO) O::mma(nacc[ct], ld16(Sl + so), qop[m]);
+        }
+      }
+      if constexpr (ESZ == 2) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          if (need(2 * p)) {
+            f32x4_t at0 = a0[0], at1 = a0[1];
+            if (p == 1) {
+              scaled(qr, qop, qlo, true);
+              at0 = a_tile(2);
+              at1 = a_tile(3);
+            }
+            u32x4_t bh, bl;
+            pair_operands(at0, at1, bh, bl);
+#pragma unroll
+            for (int ct = 0; ct < NDT; ++ct) {
+              const u32x4_t uh = ld16(Vt + vt_at(16 * ct + lr, 4 * p + lg));
+              O::mma(nacc[ct], uh, bh);
+              O::mma(nacc[ct], uh, bl);
+              O::mma(nacc[ct], ld16(Vl + vt_at(16 * ct + lr, 4 * p + lg)), bh);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          if (need(jt)) {
+            if (jt == 2) scaled(qr, qop, qlo, true);
+            const f32x4_t at = jt < 2 ? a0[jt] : a_tile(jt);
+#pragma unroll
+            for (int ct = 0; ct < NDT; ++ct) {
+              const u32x4_t uv = ld16(Vt + vt_at(16 * ct + lr, 4 * jt + lg));
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                nacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(uv[q]), at[q], nacc[ct], 0, 0, 0);
+            }
+          }
+        }
+      }
+      if (tok < T) {
+        IT* orow = ob + (int64_t)tok * QS + hq * D + 4 * lg;
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct)
+          store4(orow + 16 * ct, scale * nacc[ct][0], scale * nacc[ct][1], scale * nacc[ct][2],
+                 scale * nacc[ct][3]);
+      }
+    }
+  };
+
+  // ---- state: S = diag(e^{b_C}) S + sum_j diag(e^{b_C - b_j}) k_j u_j^T, the
+  // decayed keys from k^ (hi + lo) times e^{b_C - c_sigma} in fp32, then hi + lo
+  auto update = [&]() {
+    u32x4_t kop[NKS], kol[NKS];
+    int cur_rt = -1;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tau = w * TPW + i;
+      if (tau < NS) {
+        const int rt = tau / NDT, ct = tau % NDT;
+        if constexpr (DK == 2) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sacc[i][q] *= __expf(Bc[(kChunk - 1) * BC_LD + 16 * rt + 4 * lg + q]);
+        } else if constexpr (DK == 1) {
+          sacc[i] *= __expf(Bt[kChunk + kChunk - 1]);
+        }
+        if (rt != cur_rt) {
+          cur_rt = rt;
+          const int dk = 16 * rt + lr;
+          const float bC = DK == 2 ? Bc[(kChunk - 1) * BC_LD + dk] : (DK == 1 ? Bt[kChunk + kChunk - 1] : 0.f);
+          const float c31 = DK == 2 ? Bc[31 * BC_LD + dk] : (DK == 1 ? Bt[kChunk + 31] : 0.f);
+#pragma unroll
+          for (int m = 0; m < NKS; ++m) {
+            float f[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+              const int sk = KB * m + VEC * lg + e;
+              const int off = kn_at(sk, dk);
+              float kv = to_f(Kh[off]);
+              if constexpr (LO) kv += to_f(Kl[off]);
+              f[e] = DK == 0 ? kv : kv * __expf(bC - (sk >= 32 ? c31 : 0.f));
+            }
+            split8(f, kop[m], kol[m]);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < NKS; ++m) {
+          const u32x4_t uh = ld16(Vt + vt_at(16 * ct + lr, (KB / VEC) * m + lg));
+          O::mma(sacc[i], kop[m], uh);
+          if constexpr (LO) {
+            O::mma(sacc[i], kol[m], uh);
+            O::mma(sacc[i], kop[m], ld16(Vl + vt_at(16 * ct + lr, (KB / VEC) * m + lg)));
+          }
+        }
+      }
+    }
+  };
+
+  for (int c = 0; c < nchunks; ++c) {
+    stage(c);
+    solve(c);
+    outputs(c);
+    update();
+    __syncthreads();
+    write_sb();
+  }
+  if (a.s_out) {
+    float* sout = a.s_out + (int64_t)u * D * D;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tau = w * TPW + i;
+      if (tau < NS) {
+        const int rt = tau / NDT, ct = tau % NDT;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sout[(16 * rt + 4 * lg + q) * D + 16 * ct + lr] = sacc[i][q];
+      }
+    }
+  }
+}
+
+template <typename IT, int D, int G>
+static void launch_dg(int dk, const DeltaArgs& a, hipStream_t st) {
+  constexpr int NTH = DeltaShape<G>::NTH;
+  switch (dk) {
+    case 0: hipLaunchKernelGGL((delta_kernel<IT, D, G, 0>), dim3(a.units), dim3(NTH), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((delta_kernel<IT, D, G, 1>), dim3(a.units), dim3(NTH), 0, st, a); break;
+    default: hipLaunchKernelGGL((delta_kernel<IT, D, G, 2>), dim3(a.units), dim3(NTH), 0, st, a); break;
+  }
+}
+
+template <typename IT, int D>
+static void launch_dd(int dk, int G, const DeltaArgs& a, hipStream_t st) {
+  switch (G) {
+    case 1: launch_dg<IT, D, 1>(dk, a, st); break;
+    case 2: launch_dg<IT, D, 2>(dk, a, st); break;
+    case 4: launch_dg<IT, D, 4>(dk, a, st); break;
+    default: launch_dg<IT, D, 8>(dk, a, st); break;
+  }
+}
+
+template <typename IT>
+static hipError_t launch_dt(int dk, int D, int G, const DeltaArgs& a, hipStream_t st) {
+  switch (D) {
+    case 32: launch_dd<IT, 32>(dk, G, a, st); break;
+    case 64: launch_dd<IT, 64>(dk, G, a, st); break;
+    default:
+      if constexpr (sizeof(IT) == 2) launch_dd<IT, 128>(dk, G, a, st);
+      else return hipErrorInvalidValue;  // fp32 at head size 128 does not fit LDS
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_delta(int io, int D, int G, int decay_kind, const DeltaArgs& a, hipStream_t st) {
+  if (a.units <= 0) return hipSuccess;
+  switch (io) {
+    case kIoBF16: return launch_dt<uint16_t>(decay_kind, D, G, a, st);
+    case kIoF16: return launch_dt<f16_t>(decay_kind, D, G, a, st);
+    default: return launch_dt<float>(decay_kind, D, G, a, st);
+  }
+}
+
+}  // namespace la

@@ -103,6 +103,24 @@ struct GatedArgs {
 hipError_t launch_gated(int mode, int io, int D, int G, const GatedArgs& a, int grid,
                         hipStream_t st);
 
+// Delta rules (la_delta.hip): one workgroup per (batch, kv head) unit over the
+// whole sequence.
+struct DeltaArgs {
+  const void* q;      // (B,T,Hq*D)
+  const void* k;      // (B,T,Hkv*D)
+  const void* v;      // (B,T,Hkv*D)
+  const void* decay;  // null, (B,T,Hkv) or (B,T,Hkv*D) per the decay kind
+  const void* beta;   // (B,T,beta_heads)
+  void* out;          // (B,T,Hq*D)
+  const float* s_in;  // (B*Hkv,D,D) or null (zeros)
+  float* s_out;       // (B*Hkv,D,D)
+  int32_t T, Hq, Hkv, units, beta_heads;
+  float scale;
+};
+// decay_kind: 0 none ("delta"), 1 per kv head, 2 per key dim.  fp32 at head
+// size 128 is not available (LDS).
+hipError_t launch_delta(int io, int D, int G, int decay_kind, const DeltaArgs& a, hipStream_t st);
+
 // T == 1 step of the gated recurrence (la_decode.hip).
 struct GatedStepArgs {
   const void* q;      // (B, Hq*D)

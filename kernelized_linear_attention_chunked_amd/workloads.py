@@ -198,6 +198,35 @@ class GatedPerdimD128(GatedGqaD128):
     per_dim = 1
 
 
+class GatedDeltaD128:
+    """Gated delta rule with per-head decay and beta, GQA, B=32 T=4096 Hq=32
+    Hkv=8 D=128, bf16, scale 1/sqrt(128), zero past state."""
+
+    name = "gated_delta_d128"
+
+    def __init__(self, device="cuda:0"):
+        w = synth.WORKLOADS[self.name]
+        self.B, self.T, self.Hq, self.Hkv, self.D = w["B"], w["T"], w["Hq"], w["Hkv"], w["D"]
+        self.device = device
+        inp = synth.workload(self.name, device)
+        self.q, self.k, self.v, self.g, self.beta = inp["q"], inp["k"], inp["v"], inp["decay"], inp["beta"]
+        B, T, D = self.B, self.T, self.D
+        self.out = torch.empty_like(self.q)
+        self.present = torch.empty((B, self.Hkv, D, D), dtype=torch.float32, device=device)
+        self.scale = 1.0 / (D ** 0.5)
+        self.lib = load_library()
+
+    @property
+    def prefill_tokens(self):
+        return self.B * self.T
+
+    def step(self):
+        _check(self.lib.la_delta_forward(_p(self.q), _p(self.k), _p(self.v), _p(self.g), 0, _p(self.beta),
+                                         1, None, _p(self.present), _p(self.out), self.B, self.T, self.Hq,
+                                         self.Hkv, self.D, self.D, 1, self.scale, _stream(self.device)),
+               "la_delta_forward")
+
+
 class GatedStepD128:
     """Gated GQA decode: B=256 sequences, Hq=32 Hkv=8 D=128, bf16, 64 one-token
     steps per step() updating the fp32 state in place."""
@@ -237,4 +266,4 @@ class GatedStepD128:
 
 
 DRIVERS = {c.name: c for c in (StreamingD128, CausalBf16D64, NonCausalReluD128, GatedGqaD128,
-                               GatedPerdimD128, GatedStepD128)}
+                               GatedPerdimD128, GatedDeltaD128, GatedStepD128)}

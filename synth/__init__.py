@@ -18,6 +18,9 @@ then rounded to nearest even to the storage dtype):
   g = logsigmoid(x), x ~ N(2,1), computed in fp32 then rounded.
 * ``gated_perdim_d128``   the ``gated_gqa_d128`` shapes with a per-key-dim decay
   (B,T,Hkv*D), g = logsigmoid(x), x ~ N(2,1) drawn per element.
+* ``gated_delta_d128``    the gated delta rule, B=32 T=4096 Hq=32 Hkv=8 D=128, bf16: q, v,
+  unit-norm k and the per-head decay as ``gated_gqa_d128``; beta = sigmoid(x),
+  x ~ N(0,1), per (b, t, kv head).
 * ``gated_step_d128``     the same heads and distributions as a serving batch of
   B=256 sequences decoding 64 tokens one at a time; the fp32 past state is
   drawn N(0, 0.3^2).
@@ -36,6 +39,7 @@ WORKLOADS = {
     "gated_gqa_d128": dict(B=2, T=32768, Hq=32, Hkv=8, D=128, dtype=torch.bfloat16, seed=5),
     "gated_step_d128": dict(B=256, T=64, Hq=32, Hkv=8, D=128, dtype=torch.bfloat16, seed=6),
     "gated_perdim_d128": dict(B=2, T=32768, Hq=32, Hkv=8, D=128, dtype=torch.bfloat16, seed=7),
+    "gated_delta_d128": dict(B=32, T=4096, Hq=32, Hkv=8, D=128, dtype=torch.bfloat16, seed=8),
 }
 
 
@@ -98,7 +102,7 @@ def workload(name: str, device="cpu"):
     """All inputs of a named workload as a dict of tensors on ``device``."""
     w = WORKLOADS[name]
     s, dt = w["seed"], w["dtype"]
-    if name in ("gated_gqa_d128", "gated_step_d128", "gated_perdim_d128"):
+    if name in ("gated_gqa_d128", "gated_step_d128", "gated_perdim_d128", "gated_delta_d128"):
         B, T, Hq, Hkv, D = w["B"], w["T"], w["Hq"], w["Hkv"], w["D"]
         q = normal((B, T, Hq * D), 1.0, dt, device, s, "q")
         k = l2_normalized((B, T, Hkv, D), dt, device, s, "k").reshape(B, T, Hkv * D)
@@ -107,6 +111,8 @@ def workload(name: str, device="cpu"):
         out = dict(q=q, k=k, v=v, decay=g, Hq=Hq, Hkv=Hkv, D=D)
         if name == "gated_step_d128":
             out["past"] = normal((B, Hkv, D, D), 0.3, torch.float32, device, s, "past")
+        if name == "gated_delta_d128":
+            out["beta"] = torch.sigmoid(normal((B, T, Hkv), 1.0, torch.float32, device, s, "beta")).to(dt)
         return out
     B, T, H, D = w["B"], w["T"], w["H"], w["D"]
     if name == "noncausal_relu_d128":

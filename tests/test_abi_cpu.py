@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     assert sorted(la.EXPORTED_SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -194,3 +194,28 @@ def test_gated_step_argument_errors(lib):
     assert g(pres=f((6 << 30) + 4096)) == BAD_ARG  # partial overlap of the states
     assert g(past=f((6 << 30) + 4)) == BAD_ARG     # misaligned state
     assert g(B=0) == OK                       # nothing to do, nothing touched
+
+
+def test_delta_argument_errors(lib):
+    f = fake
+
+    def g(**kw):
+        a = dict(q=f(1 << 30), k=f(2 << 30), v=f(3 << 30), d=None, pd=0, beta=f(7 << 30), bph=1,
+                 past=None, pres=f(4 << 30), out=f(5 << 30), B=1, T=64, Hq=4, Hkv=2, Dk=64, Dv=64,
+                 dt=1, scale=0.0)
+        a.update(kw)
+        return lib.la_delta_forward(a["q"], a["k"], a["v"], a["d"], a["pd"], a["beta"], a["bph"],
+                                    a["past"], a["pres"], a["out"], a["B"], a["T"], a["Hq"], a["Hkv"],
+                                    a["Dk"], a["Dv"], a["dt"], ctypes.c_float(a["scale"]), None)
+
+    assert g(Hq=3) == SHAPE
+    assert g(dt=4) == DTYPE
+    assert g(beta=None) == NULL_ARG           # the delta rules need beta
+    assert g(pres=None) == NULL_ARG
+    assert g(Dk=96, Dv=96) == UNSUPPORTED
+    assert g(dt=0, Dk=128, Dv=128) == UNSUPPORTED  # fp32 at head size 128 does not fit LDS
+    assert g(scale=float("inf")) == BAD_ARG
+    assert g(out=f(1 << 30)) == BAD_ARG       # out aliases q
+    assert g(beta=f((5 << 30) + 64)) == BAD_ARG  # beta inside out
+    assert g(d=f((6 << 30) + 2), pd=1) == BAD_ARG  # per-dim decays are read as 16-byte vectors
+    assert g(B=0) == OK

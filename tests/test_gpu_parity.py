@@ -376,6 +376,59 @@ def test_gated_perdim_prefill_then_steps(dtype):
     assert_close(state, po, TOL[dtype], "state")
 
 
+# ------------------------------------------------------- delta / gated-delta rules
+def _beta(shape, dtype, seed):
+    x = synth.normal(shape, 1.0, torch.float32, DEV, seed, "beta")
+    return torch.sigmoid(x).to(dtype)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("kind", ["delta", "gated_head", "gated_dim"])
+def test_delta_small(dtype, D, G, kind):
+    B, T, Hkv = 2, 150, 2
+    Hq = Hkv * G
+    seed = 6000 + D + G + 7 * len(kind)
+    q = synth.normal((B, T, Hq * D), 1.0, dtype, DEV, seed, "q")
+    k = synth.l2_normalized((B, T, Hkv, D), dtype, DEV, seed, "k").reshape(B, T, Hkv * D)
+    v = synth.normal((B, T, Hkv * D), 1.0, dtype, DEV, seed, "v")
+    beta = _beta((B, T, Hkv), dtype, seed)
+    g = None
+    if kind == "gated_head":
+        g = synth.logsigmoid_decay((B, T, Hkv), dtype, DEV, seed, mean=1.0)
+    elif kind == "gated_dim":
+        g = synth.logsigmoid_decay((B, T, Hkv * D), dtype, DEV, seed, mean=1.0)
+    past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, seed, "past")
+    if dtype == torch.float32 and D == 128:
+        with pytest.raises(la.LinAttnError):
+            la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=past)
+        return
+    out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=past)
+    torch.cuda.synchronize()
+    oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "delta" if g is None else "gated_delta",
+                          past_state=f64(past), decay=None if g is None else f64(g), beta=f64(beta))
+    assert_close(out, oo, TOL[dtype], "out")
+    assert_close(present, po, TOL[dtype], "present_state")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_delta_shared_beta_long(dtype):
+    """beta (B,T,1) shared by the kv heads, several chunks, no past state."""
+    B, T, Hkv, G, D = 1, 700, 3, 2, 64
+    Hq = Hkv * G
+    q = synth.normal((B, T, Hq * D), 1.0, dtype, DEV, 81, "q")
+    k = synth.l2_normalized((B, T, Hkv, D), dtype, DEV, 81, "k").reshape(B, T, Hkv * D)
+    v = synth.normal((B, T, Hkv * D), 1.0, dtype, DEV, 81, "v")
+    beta = _beta((B, T, 1), dtype, 81)
+    g = synth.logsigmoid_decay((B, T, Hkv * D), dtype, DEV, 81, mean=3.0)
+    out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g)
+    torch.cuda.synchronize()
+    oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "gated_delta", decay=f64(g), beta=f64(beta))
+    assert_close(out, oo, TOL[dtype], "out")
+    assert_close(present, po, TOL[dtype], "present_state")
+
+
 # ------------------------------------------------------------ gated T=1 step
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("D", [32, 64, 128])
@@ -428,16 +481,16 @@ def test_gated_prefill_then_steps_equal_full(dtype):
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "onnx_examples.json")))
 
 
-@pytest.mark.parametrize("ex", [e for e in GOLDEN["examples"]
-                                if e["update_rule"] in ("linear", "gated") and e["dtype"] == "float32"],
+@pytest.mark.parametrize("ex", [e for e in GOLDEN["examples"] if e["dtype"] == "float32"],
                          ids=lambda e: e["name"])
 def test_operator_page_examples_on_gpu(ex):
     """The printed worked examples, zero-padded from head size 2 to 32.
 
-    Padding is exact for the linear/gated rules: padded q,k dims add 0 to every
-    dot product and padded v columns give 0 outputs; a per-dim decay gets 0 (no
-    decay) on the padded dims, whose rows of S stay 0.  The scale is passed
-    explicitly (the default would use the padded head size)."""
+    Padding is exact for every rule: padded q,k dims add 0 to every dot product
+    (k^T S and k^T k included), padded v columns give 0 outputs and 0
+    pseudo-values, and a per-dim decay gets 0 (no decay) on the padded dims,
+    whose rows of S stay 0.  The scale is passed explicitly (the default would
+    use the padded head size)."""
     I = ex["inputs"]
     Hq, Hkv = ex["q_num_heads"], ex["kv_num_heads"]
     q, k, v = (np.array(I[n], dtype=np.float32) for n in ("query", "key", "value"))
@@ -464,8 +517,13 @@ def test_operator_page_examples_on_gpu(ex):
         else:
             decay = torch.from_numpy(g).to(DEV)
     scale = ex.get("scale", 1.0 / np.sqrt(d))
-    out, present = la.la_gated_forward(pad(q, Hq), pad(k, Hkv), pad(v, Hkv), Hq, Hkv, decay=decay,
-                                       past_state=past, scale=scale)
+    if ex["update_rule"] in ("delta", "gated_delta"):
+        beta = torch.tensor(I["beta"], dtype=torch.float32, device=DEV)
+        out, present = la.la_delta_forward(pad(q, Hq), pad(k, Hkv), pad(v, Hkv), Hq, Hkv, beta,
+                                           decay=decay, past_state=past, scale=scale)
+    else:
+        out, present = la.la_gated_forward(pad(q, Hq), pad(k, Hkv), pad(v, Hkv), Hq, Hkv, decay=decay,
+                                           past_state=past, scale=scale)
     torch.cuda.synchronize()
     out = out.cpu().numpy().reshape(B, T, Hq, P)[..., :d].reshape(B, T, Hq * d)
     present = present.cpu().numpy()[:, :, :d, :d]

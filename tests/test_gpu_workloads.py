@@ -176,3 +176,25 @@ def test_gated_perdim_d128_full():
         e1 = assert_close(d.out[b:b + 1, :, j * G * D:(j + 1) * G * D], oo, 2e-2, "out %d,%d" % (b, j))
         e2 = assert_close(d.present[b:b + 1, j:j + 1], po, 2e-2, "present %d,%d" % (b, j))
         print("unit", (b, j), "out %.2e present %.2e" % (e1, e2))
+
+
+def test_gated_delta_d128_full():
+    """The gated delta rule at B=32 T=4096 Hq=32 Hkv=8 D=128: sampled (batch, kv
+    head) units against the oracle over all 4096 tokens."""
+    d = workloads.GatedDeltaD128(DEV)
+    G, D = d.Hq // d.Hkv, d.D
+    print("workload gated_delta_d128", tuple(d.q.shape), flush=True)
+    d.step()
+    torch.cuda.synchronize()
+    assert torch.isfinite(d.out.float()).all()
+    for b, j in _units(d.B, d.Hkv, 3, 8):
+        qs = d.q[b:b + 1, :, j * G * D:(j + 1) * G * D]
+        ks = d.k[b:b + 1, :, j * D:(j + 1) * D]
+        vs = d.v[b:b + 1, :, j * D:(j + 1) * D]
+        gs = d.g[b:b + 1, :, j:j + 1]
+        bs = d.beta[b:b + 1, :, j:j + 1]
+        oo, po = oracle.la_op(f64(qs), f64(ks), f64(vs), G, 1, "gated_delta", decay=f64(gs), beta=f64(bs),
+                              scale=d.scale)
+        e1 = assert_close(d.out[b:b + 1, :, j * G * D:(j + 1) * G * D], oo, 2e-2, "out %d,%d" % (b, j))
+        e2 = assert_close(d.present[b:b + 1, j:j + 1], po, 2e-2, "present %d,%d" % (b, j))
+        print("unit", (b, j), "out %.2e present %.2e" % (e1, e2))
