@@ -11,6 +11,8 @@ Functions follow these passages:
 * :func:`causal` -- "[Feature] LinearAttention layer for Keras", sections
   "Mathematical definition / Causal", "Masking / Causal", "Streaming State";
   also the running-sum equations of "Causal Linear Attention" (Brenndoerfer).
+* :func:`causal_backward` -- gradients of :func:`causal` (same page, "Stability"
+  and "Acceptance": gradient parity, float64 numerical-gradient checks).
 * :func:`noncausal` -- same Keras page, "Mathematical definition / Non-causal"
   and "Masking / Non-causal".
 * :func:`la_op` -- the "LinearAttention" operator page (ai.onnx, since version
@@ -64,7 +66,9 @@ def _load():
                                                          ctypes.c_double, p, p, p]
             lib.oracle_la_op.argtypes = [i64] * 6 + [p, p, p, p, p, ctypes.c_int, p, ctypes.c_int,
                                                      ctypes.c_int, ctypes.c_double, p, p]
-            for f in (lib.oracle_causal, lib.oracle_noncausal, lib.oracle_la_op):
+            lib.oracle_causal_backward.argtypes = [i64] * 5 + [p, p, p, u8p, p, p, p, p, p, ctypes.c_int,
+                                                               ctypes.c_int, ctypes.c_double, p, p, p, p, p]
+            for f in (lib.oracle_causal, lib.oracle_noncausal, lib.oracle_la_op, lib.oracle_causal_backward):
                 f.restype = ctypes.c_int
             lib.oracle_max_threads.argtypes = []
             lib.oracle_max_threads.restype = ctypes.c_int
@@ -117,6 +121,35 @@ def causal(q, k, v, mask=None, S0=None, Z0=None, feature_map="elu_plus_one",
     if rc:
         raise ValueError("oracle_causal rejected its arguments (%d)" % rc)
     return y, S, Z
+
+
+def causal_backward(q, k, v, dy, mask=None, S0=None, Z0=None, dS_T=None, dZ_T=None,
+                    feature_map="elu_plus_one", use_normalizer=True, eps=1e-6):
+    """Gradients of :func:`causal` for the loss sum(dy * y) + sum(dS_T * S_T) +
+    sum(dZ_T * Z_T), by reverse-mode differentiation of the per-token recurrence
+    (Keras proposal, "Stability": float64 numerical-gradient checks; "Acceptance":
+    recurrent/parallel gradient parity).
+
+    Returns (dq, dk, dv, dS0, dZ0), float64.
+    """
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == (B, T, H, Dk) and v.shape == (B, T, H, Dv) and dy.shape == (B, T, H, Dv)
+    S0, Z0, dS_T, dZ_T = _f64(S0), _f64(Z0), _f64(dS_T), _f64(dZ_T)
+    m = _mask(mask, B, T)
+    dq = np.empty((B, T, H, Dk))
+    dk = np.empty((B, T, H, Dk))
+    dv = np.empty((B, T, H, Dv))
+    dS0 = np.empty((B, H, Dk, Dv))
+    dZ0 = np.empty((B, H, Dk))
+    rc = _load().oracle_causal_backward(B, T, H, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(S0),
+                                        _ptr(Z0), _ptr(dy), _ptr(dS_T), _ptr(dZ_T),
+                                        FEATURE_MAPS[feature_map], int(bool(use_normalizer)),
+                                        float(eps), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dS0), _ptr(dZ0))
+    if rc:
+        raise ValueError("oracle_causal_backward rejected its arguments (%d)" % rc)
+    return dq, dk, dv, dS0, dZ0
 
 
 def noncausal(q, k, v, mask=None, feature_map="elu_plus_one", use_normalizer=True, eps=1e-6):

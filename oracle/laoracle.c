@@ -218,4 +218,116 @@ int oracle_la_op(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int6
 }
 
 /* Number of OpenMP threads a parallel loop above will use (for reporting). */
+/* Derivative of phi (the Keras proposal's feature maps): elu(x)+1 has slope 1
+ * for x > 0 and exp(x) otherwise; relu(x)+eps has slope 1 for x > 0 and 0
+ * otherwise (0 taken at x = 0). */
+static double dphi(double x, int fm) {
+  if (fm == 0) return x > 0.0 ? 1.0 : exp(x);
+  return x > 0.0 ? 1.0 : 0.0;
+}
+
+/* Gradients of oracle_causal by reverse-mode differentiation of the same
+ * per-token recurrence (the Keras proposal asks for recurrent/parallel gradient
+ * parity and float64 numerical-gradient checks, "Stability" and "Acceptance").
+ * Given dy (B,T,H,Dv) and optional gradients dS_T, dZ_T of the final state:
+ * a forward sweep records S_t, Z_t after each token; a reverse sweep, with
+ * G = dL/dS_t and g = dL/dZ_t accumulated from the later tokens,
+ *   valid t:  num = S_t^T phi(q_t),  den = phi(q_t)^T Z_t + eps
+ *             dnum = dy_t / den (or dy_t),  dden = -(dy_t . num) / den^2 (or 0)
+ *             dphi(q_t) = S_t dnum + Z_t dden,   G += phi(q_t) dnum^T,  g += phi(q_t) dden
+ *             dphi(k_t) = G v_t + g,   dv_t = G^T phi(k_t)
+ *   invalid t: no gradient to q_t, k_t, v_t; G, g pass through,
+ * then dq = dphi(q) * phi'(q), dk = dphi(k) * phi'(k), dS_0 = G, dZ_0 = g. */
+int oracle_causal_backward(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                           const double* q, const double* k, const double* v,
+                           const uint8_t* mask, const double* S0, const double* Z0,
+                           const double* dy, const double* dS_T, const double* dZ_T,
+                           int fm, int use_norm, double eps,
+                           double* dq, double* dk, double* dv, double* dS0, double* dZ0) {
+  if (B < 0 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return 1;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t h = 0; h < H; ++h) {
+      const int64_t u = b * H + h;
+      double* Ss = (double*)calloc((size_t)((T + 1) * Dk * Dv), sizeof(double));  /* S after token t-1 at t */
+      double* Zs = (double*)calloc((size_t)((T + 1) * Dk), sizeof(double));
+      double* G = (double*)calloc((size_t)(Dk * Dv), sizeof(double));
+      double* g = (double*)calloc((size_t)Dk, sizeof(double));
+      double* fq = (double*)malloc((size_t)Dk * sizeof(double));
+      double* fk = (double*)malloc((size_t)Dk * sizeof(double));
+      double* dnum = (double*)malloc((size_t)Dv * sizeof(double));
+      if (S0) memcpy(Ss, S0 + u * Dk * Dv, (size_t)(Dk * Dv) * sizeof(double));
+      if (Z0) memcpy(Zs, Z0 + u * Dk, (size_t)Dk * sizeof(double));
+      /* forward sweep: Ss[t+1] = state after token t */
+      for (int64_t t = 0; t < T; ++t) {
+        const int64_t row = (b * T + t) * H + h;
+        double* S1 = Ss + (t + 1) * Dk * Dv;
+        double* Z1 = Zs + (t + 1) * Dk;
+        memcpy(S1, Ss + t * Dk * Dv, (size_t)(Dk * Dv) * sizeof(double));
+        memcpy(Z1, Zs + t * Dk, (size_t)Dk * sizeof(double));
+        if (mask && !mask[b * T + t]) continue;
+        for (int64_t d = 0; d < Dk; ++d) {
+          const double f = phi(k[row * Dk + d], fm, eps);
+          for (int64_t c = 0; c < Dv; ++c) S1[d * Dv + c] += f * v[row * Dv + c];
+          Z1[d] += f;
+        }
+      }
+      if (dS_T) memcpy(G, dS_T + u * Dk * Dv, (size_t)(Dk * Dv) * sizeof(double));
+      if (dZ_T) memcpy(g, dZ_T + u * Dk, (size_t)Dk * sizeof(double));
+      /* reverse sweep */
+      for (int64_t t = T - 1; t >= 0; --t) {
+        const int64_t row = (b * T + t) * H + h;
+        double* dqt = dq + row * Dk;
+        double* dkt = dk + row * Dk;
+        double* dvt = dv + row * Dv;
+        if (mask && !mask[b * T + t]) {
+          for (int64_t d = 0; d < Dk; ++d) dqt[d] = dkt[d] = 0.0;
+          for (int64_t c = 0; c < Dv; ++c) dvt[c] = 0.0;
+          continue;
+        }
+        const double* S = Ss + (t + 1) * Dk * Dv;
+        const double* Z = Zs + (t + 1) * Dk;
+        const double* dyt = dy + row * Dv;
+        for (int64_t d = 0; d < Dk; ++d) {
+          fq[d] = phi(q[row * Dk + d], fm, eps);
+          fk[d] = phi(k[row * Dk + d], fm, eps);
+        }
+        double den = eps, dden = 0.0;
+        for (int64_t d = 0; d < Dk; ++d) den += fq[d] * Z[d];
+        double dy_num = 0.0;
+        for (int64_t c = 0; c < Dv; ++c) {
+          double num = 0.0;
+          for (int64_t d = 0; d < Dk; ++d) num += fq[d] * S[d * Dv + c];
+          dy_num += dyt[c] * num;
+          dnum[c] = use_norm ? dyt[c] / den : dyt[c];
+        }
+        if (use_norm) dden = -dy_num / (den * den);
+        for (int64_t d = 0; d < Dk; ++d) {
+          double a = Z[d] * dden;
+          for (int64_t c = 0; c < Dv; ++c) a += S[d * Dv + c] * dnum[c];
+          dqt[d] = a * dphi(q[row * Dk + d], fm);
+        }
+        for (int64_t d = 0; d < Dk; ++d) {
+          for (int64_t c = 0; c < Dv; ++c) G[d * Dv + c] += fq[d] * dnum[c];
+          g[d] += fq[d] * dden;
+        }
+        for (int64_t d = 0; d < Dk; ++d) {
+          double a = g[d];
+          for (int64_t c = 0; c < Dv; ++c) a += G[d * Dv + c] * v[row * Dv + c];
+          dkt[d] = a * dphi(k[row * Dk + d], fm);
+        }
+        for (int64_t c = 0; c < Dv; ++c) {
+          double a = 0.0;
+          for (int64_t d = 0; d < Dk; ++d) a += G[d * Dv + c] * fk[d];
+          dvt[c] = a;
+        }
+      }
+      if (dS0) memcpy(dS0 + u * Dk * Dv, G, (size_t)(Dk * Dv) * sizeof(double));
+      if (dZ0) memcpy(dZ0 + u * Dk, g, (size_t)Dk * sizeof(double));
+      free(Ss); free(Zs); free(G); free(g); free(fq); free(fk); free(dnum);
+    }
+  }
+  return 0;
+}
+
 int oracle_max_threads(void) { return omp_get_max_threads(); }

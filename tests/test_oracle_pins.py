@@ -329,3 +329,53 @@ def test_gqa_equals_replicated_mha():
     out2, present2 = oracle.la_op(q, rep(k), rep(v), Hq, Hq, "gated", decay=np.repeat(g, G, axis=2))
     np.testing.assert_allclose(out2, out, rtol=1e-13)
     np.testing.assert_allclose(present2[:, ::G], present, rtol=1e-13)
+
+
+# ------------------------------------------------------------- gradients (backward)
+@pytest.mark.parametrize("fm", ["elu_plus_one", "relu"])
+@pytest.mark.parametrize("norm", [True, False], ids=["norm", "nonorm"])
+def test_backward_matches_finite_differences(fm, norm):
+    """The oracle backward against central differences of the fp64 forward, for
+    the loss sum(dy*y) + sum(dS*S_T) + sum(dZ*Z_T), every input element, with a
+    mask (invalid tokens get zero gradients) and an initial state (Keras
+    proposal, "Stability": float64 numerical-gradient checks)."""
+    rng = np.random.default_rng(11 + 2 * norm + (fm == "relu"))
+    B, T, H, Dk, Dv = 2, 7, 2, 3, 2
+    q = rng.normal(size=(B, T, H, Dk))
+    k = rng.normal(size=(B, T, H, Dk))
+    v = rng.normal(size=(B, T, H, Dv))
+    S0 = rng.normal(size=(B, H, Dk, Dv)) * 0.5
+    Z0 = rng.uniform(0.5, 2.0, size=(B, H, Dk))
+    mask = np.ones((B, T), bool)
+    mask[0, 2] = mask[1, 5] = mask[1, 0] = False
+    dy = rng.normal(size=(B, T, H, Dv))
+    dS = rng.normal(size=(B, H, Dk, Dv))
+    dZ = rng.normal(size=(B, H, Dk)) if norm else None
+    # keep inputs off relu's kink
+    for x in (q, k):
+        x[np.abs(x) < 1e-3] = 0.5
+
+    def loss(q_, k_, v_, S0_, Z0_):
+        y, S, Z = oracle.causal(q_, k_, v_, mask, S0_, Z0_ if norm else None, fm, norm, 1e-6)
+        out = np.sum(dy * y) + np.sum(dS * S)
+        if norm:
+            out += np.sum(dZ * Z)
+        return out
+
+    args = [q, k, v, S0, Z0]
+    dq, dk, dv, dS0, dZ0 = oracle.causal_backward(q, k, v, dy, mask, S0, Z0 if norm else None, dS, dZ,
+                                                  fm, norm, 1e-6)
+    grads = [dq, dk, dv, dS0, dZ0]
+    h = 1e-6
+    for a in range(4 if not norm else 5):
+        fd = np.zeros_like(args[a])
+        for idx in np.ndindex(args[a].shape):
+            plus = [x.copy() for x in args]
+            minus = [x.copy() for x in args]
+            plus[a][idx] += h
+            minus[a][idx] -= h
+            fd[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        np.testing.assert_allclose(grads[a], fd, rtol=1e-5, atol=1e-6, err_msg="argument %d" % a)
+    # invalid tokens: no gradient to q, k, v
+    for b, t in ((0, 2), (1, 5), (1, 0)):
+        assert not np.any(dq[b, t]) and not np.any(dk[b, t]) and not np.any(dv[b, t])
