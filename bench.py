@@ -259,6 +259,12 @@ def bench_other(args, log):
         # per token and q head: intra (64-wide A tile and A U) and inter; per kv head:
         # R (Kbar S), the key tiles (64 wide), the update, and the solve's products
         flops = Tt * d.Hq * (2 * 64 * 2 * D + 2 * D * D) + Tt * d.Hkv * (2 * D * D * 2 + 2 * 64 * D * 2)
+    elif args.workload == "backward_bf16_d64":
+        # q, k, v, dy read and dq, dk, dv written once (bf16); the state gradient
+        nbytes = Tt * d.H * D * 2 * 7 + d.B * d.H * (D * D + D) * 4
+        # three linear-rule recurrences: per token a 64-wide intra tile, A V and
+        # the inter and state products (2 D D each)
+        flops = 3 * Tt * d.H * (2 * 64 * D * 2 + 4 * D * D)
     elif args.workload in ("gated_gqa_d128", "gated_perdim_d128"):
         per_dim = args.workload == "gated_perdim_d128"
         nbytes = (Tt * (d.Hq * D * 2 * 2 + d.Hkv * D * 2 * 2 + d.Hkv * (D if per_dim else 1) * 2)
@@ -298,7 +304,7 @@ def main():
     ap.add_argument("--workload", default="streaming_d128",
                     choices=["streaming_d128", "causal_bf16_d64", "noncausal_relu_d128",
                              "gated_gqa_d128", "gated_perdim_d128", "gated_delta_d128",
-                             "gated_step_d128"])
+                             "backward_bf16_d64", "gated_step_d128"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

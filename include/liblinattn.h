@@ -179,6 +179,31 @@ la_status la_delta_forward(const void* q, const void* k, const void* v, const vo
                            int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv, int32_t dtype,
                            float scale, void* stream);
 
+/* Bytes of device workspace la_backward needs for these sizes (0 = none). */
+la_status la_backward_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                     int32_t dtype, int32_t use_normalizer, size_t* bytes);
+
+/* Gradients of causal la_forward (the Keras proposal asks for recurrent/parallel
+ * gradient parity and finite gradients, "Stability" and "Acceptance"), for the
+ * loss sum(dout * out) + sum(dstate_out_kv * S_T) + sum(dstate_out_k * Z_T):
+ *   q, k, v, mask, state_in_kv/k, feature_map, use_normalizer, eps: as passed to
+ *     the causal forward (its output is not needed);
+ *   dout (B,T,H,Dv) in `dtype`; dstate_out_kv (B,H,Dk,Dv) and, with the
+ *     normalizer, dstate_out_k (B,H,Dk), float32, or NULL (zero);
+ *   dq, dk (B,T,H,Dk), dv (B,T,H,Dv) in `dtype`: written; 0 at invalid tokens;
+ *   dstate_in_kv (B,H,Dk,Dv), dstate_in_k (B,H,Dk, normalizer only), float32:
+ *     the gradient of the initial state, always written.
+ * Outputs may not overlap the inputs or each other.  Evaluated as three
+ * chunk-parallel linear-rule recurrences (two in reversed time) plus prefix
+ * sums, in float32; needs la_backward_workspace_size bytes of workspace. */
+la_status la_backward(const void* q, const void* k, const void* v, const uint8_t* mask,
+                      const float* state_in_kv, const float* state_in_k, const void* dout,
+                      const float* dstate_out_kv, const float* dstate_out_k, int32_t feature_map,
+                      int32_t use_normalizer, float eps, void* dq, void* dk, void* dv,
+                      float* dstate_in_kv, float* dstate_in_k, int64_t B, int64_t T, int64_t H,
+                      int64_t Dk, int64_t Dv, int32_t dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
 /* Static string naming a status code. */
 const char* la_status_string(la_status s);
 

@@ -18,6 +18,7 @@ Functions carry the C names:
   LinearAttention operator page, ai.onnx since version 27).
 * :func:`la_gated_step` -- one token of that recurrence (decode).
 * :func:`la_delta_forward` -- the delta / gated-delta rules of the same operator.
+* :func:`la_backward` -- gradients of the causal :func:`la_forward`.
 """
 from __future__ import annotations
 
@@ -31,14 +32,14 @@ from .build import LIB_PATH, build as _build
 
 __all__ = [
     "LinAttnError", "la_initial_state", "la_forward", "la_step", "la_gated_forward",
-    "la_gated_step", "la_delta_forward", "la_workspace_size", "la_gated_workspace_size", "library_path", "load_library",
+    "la_gated_step", "la_delta_forward", "la_backward", "la_workspace_size", "la_gated_workspace_size", "library_path", "load_library",
     "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
     "la_initial_state", "la_workspace_size", "la_forward", "la_step", "la_gated_workspace_size",
-    "la_gated_forward", "la_gated_step", "la_delta_forward", "la_status_string",
-    "la_last_error_message",
+    "la_gated_forward", "la_gated_step", "la_delta_forward", "la_backward_workspace_size",
+    "la_backward", "la_status_string", "la_last_error_message",
 )
 
 _FM = {"elu_plus_one": 0, "relu": 1}
@@ -86,9 +87,12 @@ def load_library(build_if_missing: bool = True):
         lib.la_gated_step.argtypes = [p, p, p, p, i32, p, p, p, i64, i64, i64, i64, i64, i32, f32, p]
         lib.la_delta_forward.argtypes = [p, p, p, p, i32, p, i32, p, p, p, i64, i64, i64, i64, i64, i64,
                                          i32, f32, p]
+        lib.la_backward_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
+        lib.la_backward.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, f32, p, p, p, p, p, i64, i64, i64,
+                                    i64, i64, i32, p, sz, p]
         for name in ("la_initial_state", "la_workspace_size", "la_forward", "la_step",
                      "la_gated_workspace_size", "la_gated_forward", "la_gated_step",
-                     "la_delta_forward"):
+                     "la_delta_forward", "la_backward_workspace_size", "la_backward"):
             getattr(lib, name).restype = ctypes.c_int
         lib.la_status_string.argtypes = [ctypes.c_int]
         lib.la_status_string.restype = ctypes.c_char_p
@@ -370,3 +374,36 @@ def la_delta_forward(query, key, value, q_num_heads, kv_num_heads, beta, decay=N
                                 _ptr(out), B, T, Hq, Hkv, Dk, Dv, _dtype_code(q), float(scale),
                                 _stream(dev)), "la_delta_forward")
     return out, present_state
+
+
+def la_backward(q, k, v, dout, mask=None, state=None, dstate=None, feature_map="elu_plus_one",
+                use_normalizer=True, eps=1e-6):
+    """Gradients of the causal ``la_forward(q, k, v, mask, state, ...)`` for the
+    loss sum(dout * out) + <dstate, state_out>.
+
+    ``state``: the forward's (kv, k) initial state or None; ``dstate``: (dkv, dk)
+    gradient of its final state or None.  Returns ``(dq, dk, dv, (dS0, dZ0))``,
+    dZ0 None without the normalizer.
+    """
+    _need_cuda(q, k, v, dout)
+    q, k, v, dout = _contig(q), _contig(k), _contig(v), _contig(dout)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    lib = load_library()
+    m = _mask_u8(mask, B, T, dev)
+    s_kv, s_k = (None, None) if state is None else state
+    g_kv, g_k = (None, None) if dstate is None else dstate
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dS0 = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    dZ0 = torch.empty((B, H, Dk), dtype=torch.float32, device=dev) if use_normalizer else None
+    n = ctypes.c_size_t(0)
+    _check(lib.la_backward_workspace_size(B, T, H, Dk, Dv, _dtype_code(q), int(bool(use_normalizer)),
+                                          ctypes.byref(n)), "la_backward_workspace_size")
+    ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=dev)
+    _check(lib.la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(_contig(s_kv)), _ptr(_contig(s_k)),
+                           _ptr(dout), _ptr(_contig(g_kv)), _ptr(_contig(g_k)), _FM[feature_map],
+                           int(bool(use_normalizer)), float(eps), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dS0),
+                           _ptr(dZ0), B, T, H, Dk, Dv, _dtype_code(q), _ptr(ws), n.value, _stream(dev)),
+           "la_backward")
+    return dq, dk, dv, (dS0, dZ0)

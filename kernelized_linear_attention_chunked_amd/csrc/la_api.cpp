@@ -697,3 +697,182 @@ LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v
   e = la::launch_delta(dtype, (int)D, (int)G, kind, a, st);
   return device_status(e, "la_delta_forward");
 }
+
+// ---------------------------------------------------------------------------
+// causal backward
+
+namespace {
+struct BwdLayout {
+  size_t den, fq, fk, v32, fq_r, fk_r, v_r, zc, rs, dnum, dnum_r, dden, qa, kc_r, vd_r, s0t, dstt, scratch,
+      gws, total;
+};
+BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t D, int64_t esz, bool norm) {
+  const size_t N = (size_t)(B * T * H * D), NT = (size_t)(B * T * H), SE = (size_t)(B * H * D * D);
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  BwdLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += al(bytes);
+    return o;
+  };
+  L.den = take(norm ? NT * 4 : 0);
+  L.fq = take(N * 4);
+  L.fk = take(N * 4);
+  L.v32 = take(N * 4);
+  L.fq_r = take(N * 4);
+  L.fk_r = take(N * 4);
+  L.v_r = take(N * 4);
+  L.zc = take(norm ? N * 4 : 0);
+  L.rs = take(norm ? N * 4 : 0);
+  L.dnum = take(N * 4);
+  L.dnum_r = take(N * 4);
+  L.dden = take(NT * 4);
+  L.qa = take(N * 4);
+  L.kc_r = take(N * 4);
+  L.vd_r = take(N * 4);
+  L.s0t = take(SE * 4);
+  L.dstt = take(SE * 4);
+  L.scratch = take(SE * 4);
+  L.gws = take(gated_ws_bytes(B, T, H, D, false));
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+LA_EXPORT la_status la_backward_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                               int32_t dtype, int32_t use_normalizer, size_t* bytes) {
+  if (!bytes) return fail(LA_ERR_NULL_ARG, "bytes is NULL");
+  la_status s = check_common(B, T, H, Dk, Dv, dtype);
+  if (s != LA_OK) return s;
+  *bytes = (B * H == 0 || T == 0) ? 0 : bwd_layout(B, T, H, Dk, dtype_size(dtype), use_normalizer != 0).total;
+  return ok();
+}
+
+LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, const uint8_t* mask,
+                                const float* state_in_kv, const float* state_in_k, const void* dout,
+                                const float* dstate_out_kv, const float* dstate_out_k, int32_t feature_map,
+                                int32_t use_normalizer, float eps, void* dq, void* dk, void* dv,
+                                float* dstate_in_kv, float* dstate_in_k, int64_t B, int64_t T, int64_t H,
+                                int64_t Dk, int64_t Dv, int32_t dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  la_status s = check_common(B, T, H, Dk, Dv, dtype);
+  if (s != LA_OK) return s;
+  if (feature_map != LA_FM_ELU_PLUS_ONE && feature_map != LA_FM_RELU_EPS)
+    return fail(LA_ERR_BAD_ARG, "feature_map %d is not 0 (elu+1) or 1 (relu+eps)", feature_map);
+  if (!(eps >= 0.f) || isinf(eps)) return fail(LA_ERR_BAD_ARG, "eps must be finite and >= 0");
+  const bool norm = use_normalizer != 0;
+  const int64_t D = Dk, U = B * H, SE = U * D * D;
+  const int64_t esz = dtype_size(dtype);
+  if (U == 0) return ok();
+  if (!dstate_in_kv || (norm && !dstate_in_k))
+    return fail(LA_ERR_NULL_ARG, "dstate_in (kv, and k with the normalizer) is required");
+  if (norm) {
+    if ((state_in_kv != nullptr) != (state_in_k != nullptr))
+      return fail(LA_ERR_STATE, "normalized state_in needs both kv and k (or neither)");
+    if ((dstate_out_kv != nullptr) != (dstate_out_k != nullptr))
+      return fail(LA_ERR_STATE, "normalized dstate_out needs both kv and k (or neither)");
+  } else if (state_in_k || dstate_out_k || dstate_in_k) {
+    return fail(LA_ERR_STATE, "use_normalizer=0 carries only the kv state; k parts must be NULL");
+  }
+  const bool work = T > 0;
+  if (work && (!q || !k || !v || !dout || !dq || !dk || !dv))
+    return fail(LA_ERR_NULL_ARG, "q, k, v, dout, dq, dk and dv are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state_in_kv) || !aligned16(state_in_k) ||
+      !aligned16(dstate_out_kv) || !aligned16(dstate_out_k) || !aligned16(dstate_in_kv) ||
+      !aligned16(dstate_in_k) || !aligned16(workspace))
+    return fail(LA_ERR_BAD_ARG, "q, k, v, the states and the workspace must be 16-byte aligned");
+  const int64_t nb = B * T * H * D * esz;
+  const BwdLayout L = bwd_layout(B, T, H, D, esz, norm);
+  const size_t need = work ? L.total : 0;
+  const Range ins[9] = {range(q, nb), range(k, nb), range(v, nb), range(dout, nb), range(mask, B * T),
+                        range(state_in_kv, SE * 4), range(state_in_k, U * D * 4),
+                        range(dstate_out_kv, SE * 4), range(dstate_out_k, U * D * 4)};
+  const Range outs[6] = {range(dq, nb), range(dk, nb), range(dv, nb), range(dstate_in_kv, SE * 4),
+                         range(dstate_in_k, U * D * 4), range(workspace, (int64_t)need)};
+  for (int i = 0; i < 6; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return fail(LA_ERR_BAD_ARG, "an output or the workspace overlaps an input");
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(outs[i], outs[j])) return fail(LA_ERR_BAD_ARG, "outputs overlap each other or the workspace");
+  }
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (!work) {
+    e = dstate_out_kv ? la::launch_copy(dstate_in_kv, dstate_out_kv, SE, st) : la::launch_fill_zero(dstate_in_kv, SE, st);
+    if (e == hipSuccess && norm)
+      e = dstate_out_k ? la::launch_copy(dstate_in_k, dstate_out_k, U * D, st)
+                       : la::launch_fill_zero(dstate_in_k, U * D, st);
+    return device_status(e, "la_backward");
+  }
+  unsigned char* W = (unsigned char*)workspace;
+  auto F = [&](size_t off) { return (float*)(W + off); };
+  la::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dy = dout;
+  a.mask = mask;
+  a.den = norm ? F(L.den) : nullptr;
+  a.fq = F(L.fq);
+  a.fk = F(L.fk);
+  a.v32 = F(L.v32);
+  a.fq_r = F(L.fq_r);
+  a.fk_r = F(L.fk_r);
+  a.v_r = F(L.v_r);
+  a.dnum = F(L.dnum);
+  a.dnum_r = F(L.dnum_r);
+  a.dden = F(L.dden);
+  a.qa = F(L.qa);
+  a.kc_r = F(L.kc_r);
+  a.vd_r = F(L.vd_r);
+  a.zc = norm ? F(L.zc) : nullptr;
+  a.rs = norm ? F(L.rs) : nullptr;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = (int32_t)B;
+  a.T = (int32_t)T;
+  a.H = (int32_t)H;
+  a.D = (int32_t)D;
+  a.fm = feature_map;
+  a.eps = eps;
+  // 1. phi(q), phi(k), v in time order and reversed; 2. z_i; 3. den and dnum
+  e = la::launch_bwd_prep(dtype, a, st);
+  if (e == hipSuccess && norm)
+    e = la::launch_bwd_scan(F(L.fk), nullptr, state_in_k, F(L.zc), nullptr, (int)U, (int)T, (int)H, (int)D, 0, st);
+  if (e == hipSuccess) e = la::launch_bwd_dnum(dtype, a, st);
+  if (e == hipSuccess && state_in_kv) e = la::launch_bwd_transpose(state_in_kv, F(L.s0t), U, (int)D, st);
+  if (e == hipSuccess && dstate_out_kv) e = la::launch_bwd_transpose(dstate_out_kv, F(L.dstt), U, (int)D, st);
+  if (e != hipSuccess) return device_status(e, "la_backward");
+  // 4. qa_i = S_i dnum_i (the first linear-rule recurrence, fp32, scale 1)
+  void* gw = W + L.gws;
+  const size_t gwb = L.total - L.gws;
+  s = la_gated_forward(F(L.dnum), F(L.v32), F(L.fk), nullptr, 0, state_in_kv ? F(L.s0t) : nullptr,
+                       F(L.scratch), F(L.qa), B, T, H, H, D, D, LA_DT_F32, 1.f, gw, gwb, stream);
+  if (s != LA_OK) return s;
+  // 5. dden from qa, then dz_0 and the reverse sums dz_T + sum_{i>=j} phi_q_i dden_i
+  if (norm) {
+    e = la::launch_bwd_dden(a, st);
+    if (e == hipSuccess)
+      e = la::launch_bwd_scan(F(L.fq), F(L.dden), dstate_out_k, F(L.rs), dstate_in_k, (int)U, (int)T, (int)H,
+                              (int)D, 1, st);
+  } else {
+    e = la::launch_fill_zero(F(L.dden), B * T * H, st);
+  }
+  if (e != hipSuccess) return device_status(e, "la_backward");
+  // 6. the reversed-time recurrences
+  s = la_gated_forward(F(L.v_r), F(L.dnum_r), F(L.fq_r), nullptr, 0, dstate_out_kv ? F(L.dstt) : nullptr,
+                       F(L.scratch), F(L.kc_r), B, T, H, H, D, D, LA_DT_F32, 1.f, gw, gwb, stream);
+  if (s != LA_OK) return s;
+  s = la_gated_forward(F(L.fk_r), F(L.fq_r), F(L.dnum_r), nullptr, 0, dstate_out_kv, dstate_in_kv, F(L.vd_r), B, T,
+                       H, H, D, D, LA_DT_F32, 1.f, gw, gwb, stream);
+  if (s != LA_OK) return s;
+  // 7. dq, dk, dv
+  e = la::launch_bwd_finish(dtype, a, st);
+  return device_status(e, "la_backward");
+}

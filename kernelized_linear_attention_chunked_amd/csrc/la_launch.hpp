@@ -121,6 +121,43 @@ struct DeltaArgs {
 // size 128 is not available (LDS).
 hipError_t launch_delta(int io, int D, int G, int decay_kind, const DeltaArgs& a, hipStream_t st);
 
+// Causal backward (la_backward.hip): buffers are (B,T,H,D) fp32 unless noted;
+// *_r are in reversed time.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dy;       // (I/O type)
+  const uint8_t* mask;  // (B,T) or null
+  float* den;           // (B,T,H) denominators (formed by the dnum kernel), or null without the normalizer
+  float* fq;
+  float* fk;
+  float* v32;
+  float* fq_r;
+  float* fk_r;
+  float* v_r;
+  float* dnum;
+  float* dnum_r;
+  float* dden;          // (B,T,H)
+  const float* qa;      // S_i dnum_i
+  const float* kc_r;    // sum_{i>=j} phi_q_i (v_j . dnum_i) + dS_T v_j  (reversed)
+  const float* vd_r;    // dv (reversed)
+  const float* zc;      // z_i (normalized), or null
+  const float* rs;      // dz_T + sum_{i>=j} phi_q_i dden_i (normalized), or null
+  void* dq;
+  void* dk;
+  void* dv;
+  int32_t B, T, H, D, fm;
+  float eps;
+};
+hipError_t launch_bwd_prep(int io, const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_scan(const float* x, const float* w, const float* init, float* out, float* total, int U,
+                           int T, int H, int D, int reverse, hipStream_t st);
+hipError_t launch_bwd_dnum(int io, const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dden(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_finish(int io, const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_transpose(const float* in, float* out, int64_t U, int D, hipStream_t st);
+
 // T == 1 step of the gated recurrence (la_decode.hip).
 struct GatedStepArgs {
   const void* q;      // (B, Hq*D)

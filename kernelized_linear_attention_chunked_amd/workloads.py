@@ -227,6 +227,40 @@ class GatedDeltaD128:
                "la_delta_forward")
 
 
+class BackwardBf16D64:
+    """Gradients of the causal elu+1 normalized attention, B=8 H=16 T=2048 D=64,
+    bf16 (dq, dk, dv and the initial-state gradient)."""
+
+    name = "backward_bf16_d64"
+
+    def __init__(self, device="cuda:0", eps=1e-6):
+        w = synth.WORKLOADS[self.name]
+        self.B, self.H, self.T, self.D = w["B"], w["H"], w["T"], w["D"]
+        self.device, self.eps = device, eps
+        inp = synth.workload(self.name, device)
+        self.q, self.k, self.v, self.dy = inp["q"], inp["k"], inp["v"], inp["dy"]
+        B, H, T, D = self.B, self.H, self.T, self.D
+        self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
+        self.dS0 = torch.empty((B, H, D, D), dtype=torch.float32, device=device)
+        self.dZ0 = torch.empty((B, H, D), dtype=torch.float32, device=device)
+        self.lib = load_library()
+        n = ctypes.c_size_t(0)
+        _check(self.lib.la_backward_workspace_size(B, T, H, D, D, 1, 1, ctypes.byref(n)),
+               "la_backward_workspace_size")
+        self.ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=device)
+        self.ws_bytes = n.value
+
+    @property
+    def prefill_tokens(self):
+        return self.B * self.T
+
+    def step(self):
+        _check(self.lib.la_backward(_p(self.q), _p(self.k), _p(self.v), None, None, None, _p(self.dy), None, None,
+                                    0, 1, self.eps, _p(self.dq), _p(self.dk), _p(self.dv), _p(self.dS0),
+                                    _p(self.dZ0), self.B, self.T, self.H, self.D, self.D, 1, _p(self.ws),
+                                    self.ws_bytes, _stream(self.device)), "la_backward")
+
+
 class GatedStepD128:
     """Gated GQA decode: B=256 sequences, Hq=32 Hkv=8 D=128, bf16, 64 one-token
     steps per step() updating the fp32 state in place."""
@@ -266,4 +300,4 @@ class GatedStepD128:
 
 
 DRIVERS = {c.name: c for c in (StreamingD128, CausalBf16D64, NonCausalReluD128, GatedGqaD128,
-                               GatedPerdimD128, GatedDeltaD128, GatedStepD128)}
+                               GatedPerdimD128, GatedDeltaD128, BackwardBf16D64, GatedStepD128)}

@@ -21,6 +21,8 @@ then rounded to nearest even to the storage dtype):
 * ``gated_delta_d128``    the gated delta rule, B=32 T=4096 Hq=32 Hkv=8 D=128, bf16: q, v,
   unit-norm k and the per-head decay as ``gated_gqa_d128``; beta = sigmoid(x),
   x ~ N(0,1), per (b, t, kv head).
+* ``backward_bf16_d64``   the gradients of ``causal_bf16_d64`` (same shapes and
+  inputs), with an output gradient dy ~ N(0,1).
 * ``gated_step_d128``     the same heads and distributions as a serving batch of
   B=256 sequences decoding 64 tokens one at a time; the fp32 past state is
   drawn N(0, 0.3^2).
@@ -40,6 +42,7 @@ WORKLOADS = {
     "gated_step_d128": dict(B=256, T=64, Hq=32, Hkv=8, D=128, dtype=torch.bfloat16, seed=6),
     "gated_perdim_d128": dict(B=2, T=32768, Hq=32, Hkv=8, D=128, dtype=torch.bfloat16, seed=7),
     "gated_delta_d128": dict(B=32, T=4096, Hq=32, Hkv=8, D=128, dtype=torch.bfloat16, seed=8),
+    "backward_bf16_d64": dict(B=8, H=16, T=2048, D=64, dtype=torch.bfloat16, seed=9),
 }
 
 
@@ -121,6 +124,8 @@ def workload(name: str, device="cpu"):
         return dict(q=q, k=k, v=v, mask=mask, lengths=L)
     q, k, v = qkv(B, T, H, D, dt, device, s)
     out = dict(q=q, k=k, v=v)
+    if name == "backward_bf16_d64":
+        out["dy"] = normal((B, T, H, D), 1.0, dt, device, s, "dy")
     if name == "streaming_d128":
         Td = w["T_decode"]
         out["q_dec"], out["k_dec"], out["v_dec"] = qkv(B, Td, H, D, dt, device, s, tag="_decode")

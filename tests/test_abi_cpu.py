@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     assert sorted(la.EXPORTED_SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -218,4 +218,34 @@ def test_delta_argument_errors(lib):
     assert g(out=f(1 << 30)) == BAD_ARG       # out aliases q
     assert g(beta=f((5 << 30) + 64)) == BAD_ARG  # beta inside out
     assert g(d=f((6 << 30) + 2), pd=1) == BAD_ARG  # per-dim decays are read as 16-byte vectors
+    assert g(B=0) == OK
+
+
+def test_backward_argument_errors(lib):
+    f = fake
+    n = ctypes.c_size_t(0)
+    assert lib.la_backward_workspace_size(2, 128, 3, 64, 64, 1, 1, ctypes.byref(n)) == OK and n.value > 0
+    assert lib.la_backward_workspace_size(2, 0, 3, 64, 64, 1, 1, ctypes.byref(n)) == OK and n.value == 0
+    big = 1 << 34
+
+    def g(**kw):
+        a = dict(q=f(1 << 30), k=f(2 << 30), v=f(3 << 30), m=None, si=None, sik=None, dout=f(4 << 30),
+                 dso=None, dsok=None, fm=0, norm=1, eps=1e-6, dq=f(5 << 30), dk=f(6 << 30), dv=f(7 << 30),
+                 dsi=f(8 << 30), dsik=f(9 << 30), B=1, T=64, H=2, Dk=64, Dv=64, dt=1, ws=f(big), wsb=1 << 40)
+        a.update(kw)
+        return lib.la_backward(a["q"], a["k"], a["v"], a["m"], a["si"], a["sik"], a["dout"], a["dso"],
+                               a["dsok"], a["fm"], a["norm"], ctypes.c_float(a["eps"]), a["dq"], a["dk"], a["dv"],
+                               a["dsi"], a["dsik"], a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["dt"], a["ws"],
+                               a["wsb"], None)
+
+    assert g(dt=5) == DTYPE
+    assert g(fm=3) == BAD_ARG
+    assert g(dsi=None) == NULL_ARG
+    assert g(dsik=None) == NULL_ARG           # the normalizer's k-state gradient is required
+    assert g(norm=0) == STATE                 # k parts given without the normalizer
+    assert g(si=f(10 << 30)) == STATE         # kv state without its k part
+    assert g(dq=f(1 << 30)) == BAD_ARG        # dq aliases q
+    assert g(dk=f(5 << 30)) == BAD_ARG        # dk overlaps dq
+    assert g(ws=None, wsb=0) == WORKSPACE
+    assert g(Dk=96, Dv=96) == UNSUPPORTED
     assert g(B=0) == OK

@@ -285,6 +285,65 @@ def test_gated_present_aliases_past():
     assert torch.equal(out_a, out_b) and torch.equal(pres_a, pres_b)
 
 
+# ------------------------------------------------------------- causal backward
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("fm", FMS)
+@pytest.mark.parametrize("norm", [True, False], ids=["norm", "nonorm"])
+def test_backward_small(dtype, D, fm, norm):
+    B, T, H = 2, 150, 2
+    seed = 7000 + D + 7 * norm + 13 * (fm == "relu")
+    q, k, v = _inputs(B, T, H, D, dtype, seed)
+    dy = synth.normal((B, T, H, D), 1.0, dtype, DEV, seed, "dy")
+    dq, dk, dv, (dS0, dZ0) = la.la_backward(q, k, v, dy, feature_map=fm, use_normalizer=norm)
+    torch.cuda.synchronize()
+    oq, ok_, ov, oS, oZ = oracle.causal_backward(f64(q), f64(k), f64(v), f64(dy), feature_map=fm,
+                                                 use_normalizer=norm)
+    tol = TOL[dtype]
+    assert_close(dq, oq, tol, "dq")
+    assert_close(dk, ok_, tol, "dk")
+    assert_close(dv, ov, tol, "dv")
+    assert_close(dS0, oS, tol, "dS0")
+    if norm:
+        assert_close(dZ0, oZ, tol, "dZ0")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
+@pytest.mark.parametrize("fm", FMS)
+def test_backward_state_and_mask(dtype, fm):
+    """An initial state, a gradient of the final state, a random mask."""
+    B, T, H, D = 2, 200, 3, 64
+    q, k, v = _inputs(B, T, H, D, dtype, 91)
+    dy = synth.normal((B, T, H, D), 1.0, dtype, DEV, 91, "dy")
+    S0, Z0 = _state(B, H, D, 91)
+    gS = synth.normal((B, H, D, D), 0.2, torch.float32, DEV, 91, "gS")
+    gZ = synth.normal((B, H, D), 0.2, torch.float32, DEV, 91, "gZ")
+    mask = synth.random_mask(B, T, 0.8, DEV, 91)
+    dq, dk, dv, (dS0, dZ0) = la.la_backward(q, k, v, dy, mask=mask, state=(S0, Z0), dstate=(gS, gZ),
+                                            feature_map=fm)
+    torch.cuda.synchronize()
+    oq, ok_, ov, oS, oZ = oracle.causal_backward(f64(q), f64(k), f64(v), f64(dy), f64(mask) > 0, f64(S0),
+                                                 f64(Z0), f64(gS), f64(gZ), feature_map=fm)
+    tol = TOL[dtype]
+    for x, y, what in ((dq, oq, "dq"), (dk, ok_, "dk"), (dv, ov, "dv"), (dS0, oS, "dS0"), (dZ0, oZ, "dZ0")):
+        assert_close(x, y, tol, what)
+    invalid = ~mask.bool()
+    assert not dq[invalid].float().abs().sum() and not dk[invalid].float().abs().sum()
+    assert not dv[invalid].float().abs().sum()
+
+
+def test_backward_split_sequence():
+    """Few units and a long sequence: the recurrences run split over T."""
+    B, T, H, D = 1, 3000, 1, 64
+    q, k, v = _inputs(B, T, H, D, torch.bfloat16, 92)
+    dy = synth.normal((B, T, H, D), 1.0, torch.bfloat16, DEV, 92, "dy")
+    dq, dk, dv, (dS0, dZ0) = la.la_backward(q, k, v, dy)
+    torch.cuda.synchronize()
+    oq, ok_, ov, oS, oZ = oracle.causal_backward(f64(q), f64(k), f64(v), f64(dy))
+    for x, y, what in ((dq, oq, "dq"), (dk, ok_, "dk"), (dv, ov, "dv"), (dS0, oS, "dS0"), (dZ0, oZ, "dZ0")):
+        assert_close(x, y, 2e-2, what)
+
+
 # --------------------------------------------------- per-key-dim decay (GLA form)
 def _pd_inputs(B, T, Hq, Hkv, D, dtype, seed, mean=1.0):
     q = synth.normal((B, T, Hq * D), 1.0, dtype, DEV, seed, "q")

@@ -198,3 +198,21 @@ def test_gated_delta_d128_full():
         e1 = assert_close(d.out[b:b + 1, :, j * G * D:(j + 1) * G * D], oo, 2e-2, "out %d,%d" % (b, j))
         e2 = assert_close(d.present[b:b + 1, j:j + 1], po, 2e-2, "present %d,%d" % (b, j))
         print("unit", (b, j), "out %.2e present %.2e" % (e1, e2))
+
+
+def test_backward_bf16_d64_full():
+    """The backward workload (B=8 H=16 T=2048 D=64 bf16): sampled (batch, head)
+    units against the oracle backward over all 2048 tokens."""
+    d = workloads.BackwardBf16D64(DEV)
+    print("workload backward_bf16_d64", tuple(d.q.shape), "workspace", d.ws_bytes, flush=True)
+    d.step()
+    torch.cuda.synchronize()
+    for t in (d.dq, d.dk, d.dv):
+        assert torch.isfinite(t.float()).all()
+    for b, h in _units(d.B, d.H, 3, 9):
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        oq, ok_, ov, oS, oZ = oracle.causal_backward(f64(d.q[sl]), f64(d.k[sl]), f64(d.v[sl]), f64(d.dy[sl]))
+        errs = [assert_close(x, y, 2e-2, "%s %d,%d" % (w, b, h))
+                for x, y, w in ((d.dq[sl], oq, "dq"), (d.dk[sl], ok_, "dk"), (d.dv[sl], ov, "dv"),
+                                (d.dS0[b:b + 1, h:h + 1], oS, "dS0"), (d.dZ0[b:b + 1, h:h + 1], oZ, "dZ0"))]
+        print("unit", (b, h), " ".join("%.2e" % e for e in errs))
