@@ -106,7 +106,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hp = w >> 2, wr = w & 3;
-  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+  int l = tid & 63, lr = l & 15, lg = l >> 4;
   const int u = blockIdx.x;
   const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
   const int b = u / Hkv, j = u % Hkv;
@@ -353,7 +353,19 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   // c = 0 (second == false) or b_31, split into hi (+ lo) operands.  The row
   // offsets pass through an empty asm so that each use recomputes the factors
   // instead of the compiler keeping them live across heads.
-  const int tq = 16 * wr + lr;
+  int tq = 16 * wr + lr;
+  // The lane indices pass through an empty asm at the start of every phase, so
+  // that the swizzled LDS addresses derived from them are formed inside the
+  // phase instead of being hoisted out of the chunk loop and held (or spilled)
+  // across all of it.
+  auto refresh = [&]() {
+    int x = tid & 63;
+    asm volatile("" : "+v"(x));
+    l = x;
+    lr = x & 15;
+    lg = x >> 4;
+    tq = 16 * wr + lr;
+  };
   auto scaled = [&](const u32x4_t (&x)[NQ], u32x4_t (&hi)[NQ], u32x4_t (&lo)[LO ? NQ : 1], bool second) {
     int rt_off = tq * BC_LD, r31_off = 31 * BC_LD;
     asm volatile("" : "+v"(rt_off), "+v"(r31_off));
@@ -417,6 +429,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   // ---- pseudo-values: R = beta (V - Kbar S_0) for the wave's 16 rows and dv
   // tiles hp*RH .. hp*RH + RH - 1, then the blocked solve.  Four barriers.
   auto solve = [&](int c) {
+    refresh();
     const int tokc = min(c * kChunk + tq, T - 1);
     const float bet = Bt[tq];
     u32x4_t kr[NQ];
@@ -452,6 +465,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     float* lb = Lb + w * 16 * LB_LD;
     for (int blk = 0; blk < 4; ++blk) {
       if (wr == blk) {
+        refresh();
         u32x4_t k1h[NQ], k1l[LO ? NQ : 1];
         if (blk >= 2) scaled(kr, k1h, k1l, true);
         // earlier blocks: val -= beta_t sum_{j < 16 blk} L_tj u_j, over U^T (hi + lo)
@@ -559,6 +573,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     auto need = [&](int t) { return ESZ == 2 ? (32 * (t >> 1) <= 16 * wr + 15) : (t <= wr); };
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
+      refresh();
       const int hq = hp + P * hh;
       u32x4_t qr[NQ];
 #pragma unroll
@@ -638,6 +653,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   // ---- state: S = diag(e^{b_C}) S + sum_j diag(e^{b_C - b_j}) k_j u_j^T, the
   // decayed keys from k^ (hi + lo) times e^{b_C - c_sigma} in fp32, then hi + lo
   auto update = [&]() {
+    refresh();
     u32x4_t kop[NKS], kol[NKS];
     int cur_rt = -1;
 #pragma unroll
