@@ -63,7 +63,6 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   constexpr int VT_LD = kChunk;
   constexpr int SB_LD = D + PADE;
   constexpr int BC_LD = D + 4;
-  constexpr int LB_LD = 17;       // fp32 rows of a wave's 16 x 16 diagonal block of L
   constexpr bool LO = ESZ == 2;   // 16-bit: hi + lo operands (k^, q^, U, L, A)
   constexpr int KN_BYTES = kChunk * KN_LD * ESZ;
   constexpr int VT_BYTES = D * VT_LD * ESZ;
@@ -75,7 +74,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   constexpr int SL_BYTES = SLO ? SB_BYTES : 0;
   constexpr int WT_BYTES = NW * D * 4;
   constexpr int BT_BYTES = 2 * kChunk * 4;  // beta and the per-head cumulative decay
-  constexpr int LB_BYTES = NW * 16 * LB_LD * 4;
+  constexpr int LB_BYTES = NW * 16 * 16 * 4;  // per wave: its 16 x 16 diagonal block of L (fp32)
   constexpr int LDS = (LO ? 2 : 1) * (KN_BYTES + VT_BYTES) + SB_BYTES + SL_BYTES + BC_BYTES + WT_BYTES + BT_BYTES +
                       LB_BYTES;
   constexpr int NS = NDT * NDT;
@@ -105,7 +104,8 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hp = w >> 2, wr = w & 3;
+  // the two waves of a row block sit on different SIMDs (w % 4)
+  const int hp = P == 2 ? (w & 1) : 0, wr = P == 2 ? (w >> 1) : w;
   int l = tid & 63, lr = l & 15, lg = l >> 4;
   const int u = blockIdx.x;
   const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
@@ -140,6 +140,17 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
       for (int e = 0; e < VEC; ++e) r[e] = f[e] - bf16_bits_to_f32((hi[e >> 1] >> (16 * (e & 1))) & 0xffffu);
       lo = O::pack(r);
     }
+  };
+
+  // four fp32 values -> bf16 hi + lo operands of a 16x16x16 MFMA
+  auto split4 = [&](const float (&f)[4], s16x4_t& hi, s16x4_t& lo) {
+    u32x2_t h, r;
+    h[0] = pack_bf16x2(f[0], f[1]);
+    h[1] = pack_bf16x2(f[2], f[3]);
+    r[0] = pack_bf16x2(f[0] - __uint_as_float(h[0] << 16), f[1] - __uint_as_float(h[0] & 0xffff0000u));
+    r[1] = pack_bf16x2(f[2] - __uint_as_float(h[1] << 16), f[3] - __uint_as_float(h[1] & 0xffff0000u));
+    hi = __builtin_bit_cast(s16x4_t, h);
+    lo = __builtin_bit_cast(s16x4_t, r);
   };
 
   // ---- state tiles: wave w owns tiles tau = w*TPW + i (rows rt, columns ct)
@@ -426,17 +437,30 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     }
   };
 
-  // ---- pseudo-values: R = beta (V - Kbar S_0) for the wave's 16 rows and dv
-  // tiles hp*RH .. hp*RH + RH - 1, then the blocked solve.  Four barriers.
+  // ---- pseudo-values.  Wave (hp, wr) owns rows [16wr, 16wr+16) of the chunk
+  // and dv tiles hp*RH .. hp*RH + RH - 1, held token-major: lane (lg, lr) holds
+  // rows 16wr + 4lg + q of value dim 16ct + lr, which is also the B operand
+  // layout of a 16x16x16 MFMA over those rows.
+  //   1. R = beta (V - Kbar S_0) for its rows;
+  //   2. its rows of L: the strictly lower diagonal block -> LDS, the part left
+  //      of it -> MFMA operands (hi + lo);
+  //   3. T = (I + diag(beta) L_ii)^-1 of its diagonal block: row lr of T in
+  //      every lane group, by back substitution in registers (no lane traffic);
+  //   4. block by block, a barrier after each: X = R - beta sum_{j<i} L_ij U_j
+  //      over the U rows already written, then U_i = T X by MFMA, stored as
+  //      U^T over the consumed V^T columns.
   auto solve = [&](int c) {
     refresh();
     const int tokc = min(c * kChunk + tq, T - 1);
-    const float bet = Bt[tq];
     u32x4_t kr[NQ];
 #pragma unroll
     for (int m = 0; m < NQ; ++m) kr[m] = ld16(kb + (int64_t)tokc * KS + KB * m + VEC * lg);
     u32x4_t k0h[NQ], k0l[LO ? NQ : 1];
     scaled(kr, k0h, k0l, false);  // kbar, also the first key block's scaled row
+    const int r0 = 16 * wr + 4 * lg;  // the lane's first row
+    const f32x4_t bet4 = *(const f32x4_t*)(Bt + r0);
+    // element offset of the lane's 4 rows in row `row` of V^T / U^T
+    auto row4_at = [&](int row) { return vt_at(row, r0 / VEC) + r0 % VEC; };
     f32x4_t val[RH];
 #pragma unroll
     for (int i = 0; i < RH; ++i) val[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -446,67 +470,138 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
       for (int i = 0; i < RH; ++i) {
         const int so = sq_at(16 * (hp * RH + i) + lr, KB * m + VEC * lg);
         const u32x4_t av = ld16(Sb + so);
-        O::mma(val[i], av, k0h[m]);
-        if constexpr (LO) O::mma(val[i], av, k0l[m]);
-        if constexpr (SLO) O::mma(val[i], ld16(Sl + so), k0h[m]);
+        O::mma(val[i], k0h[m], av);
+        if constexpr (LO) O::mma(val[i], k0l[m], av);
+        if constexpr (SLO) O::mma(val[i], k0h[m], ld16(Sl + so));
       }
     }
-    // the lane holds token tq, value dims 16 ct + 4 lg + q
-    auto vt_elem = [&](int row) { return vt_at(row, tq / VEC) + tq % VEC; };
 #pragma unroll
-    for (int i = 0; i < RH; ++i)
+    for (int i = 0; i < RH; ++i) {
+      const int off = row4_at(16 * (hp * RH + i) + lr);
+      float v[4];
+      if constexpr (ESZ == 2) {
+        const u32x2_t h2 = *(const u32x2_t*)(Vt + off);
+        v[0] = __uint_as_float(h2[0] << 16);
+        v[1] = __uint_as_float(h2[0] & 0xffff0000u);
+        v[2] = __uint_as_float(h2[1] << 16);
+        v[3] = __uint_as_float(h2[1] & 0xffff0000u);
+        if constexpr (LO) {
+          const u32x2_t l2 = *(const u32x2_t*)(Vl + off);
+          v[0] += __uint_as_float(l2[0] << 16);
+          v[1] += __uint_as_float(l2[0] & 0xffff0000u);
+          v[2] += __uint_as_float(l2[1] << 16);
+          v[3] += __uint_as_float(l2[1] & 0xffff0000u);
+        }
+      } else {
+        const f32x4_t v4 = *(const f32x4_t*)(Vt + off);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int off = vt_elem(16 * (hp * RH + i) + 4 * lg + q);
-        float v = to_f(Vt[off]);
-        if constexpr (LO) v += to_f(Vl[off]);
-        val[i][q] = bet * (v - val[i][q]);
+        for (int q = 0; q < 4; ++q) v[q] = v4[q];
       }
-    float* lb = Lb + w * 16 * LB_LD;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) val[i][q] = bet4[q] * (v[q] - val[i][q]);
+    }
+
+    // L over the wave's rows.  bf16: key pairs p <= wr/2 (off-diagonal
+    // operands oh/ol, keys >= 16wr zeroed); fp32: 16-key tiles t < wr (ot).
+    float* lb = Lb + w * 256;
+    u32x4_t oh[ESZ == 2 ? 2 : 1], ol[ESZ == 2 ? 2 : 1];
+    f32x4_t ot[ESZ == 4 ? 3 : 1];
+    {
+      u32x4_t k1h[NQ], k1l[LO ? NQ : 1];
+      if (wr >= 2) scaled(kr, k1h, k1l, true);
+      if constexpr (ESZ == 2) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          if (32 * p <= 16 * wr + 15) {
+            f32x4_t at0 = p == 0 ? k_tile(0, k0h, k0l) : k_tile(2, k1h, k1l);
+            f32x4_t at1 = p == 0 ? k_tile(1, k0h, k0l) : k_tile(3, k1h, k1l);
+            if (p == (wr >> 1)) {
+#pragma unroll
+              for (int odd = 0; odd < 2; ++odd)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const int jl = key_of(2 * p + odd, q) - 16 * wr;
+                  if (jl >= 0 && jl < 16) lb[lr * 16 + jl] = jl < lr ? (odd ? at1[q] : at0[q]) : 0.f;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              at0[q] = key_of(2 * p, q) < 16 * wr ? at0[q] : 0.f;
+              at1[q] = key_of(2 * p + 1, q) < 16 * wr ? at1[q] : 0.f;
+            }
+            pair_operands(at0, at1, oh[p], ol[p]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t <= wr) {
+            const f32x4_t at = t < 2 ? k_tile(t, k0h, k0l) : k_tile(t, k1h, k1l);
+            if (t == wr) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) lb[lr * 16 + 4 * lg + q] = 4 * lg + q < lr ? at[q] : 0.f;
+            } else if (t < 3) {
+              ot[t] = at;
+            }
+          }
+        }
+      }
+    }
+    // row lr of T: y (I + diag(beta) L_ii) = e_lr, from the last column down;
+    // tr[c] gathers sum_{j>c} beta_j L_jc y_j until step c turns it into y_c
+    float tr[16];
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc) tr[cc] = 0.f;
+#pragma unroll
+    for (int jj = 15; jj >= 0; --jj) {
+      const float yj = (lr == jj ? 1.f : 0.f) - tr[jj];
+      tr[jj] = yj;
+      if (jj > 0) {
+        const float by = Bt[16 * wr + jj] * yj;
+#pragma unroll
+        for (int c4 = 0; c4 < jj; c4 += 4) {
+          const f32x4_t lrow = *(const f32x4_t*)(lb + 16 * jj + c4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c4 + e < jj) tr[c4 + e] += lrow[e] * by;
+        }
+      }
+    }
+    // the A operand of U = T X: T[lr][4lg + q]
+    float t4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t4[q] = lg == 0 ? tr[q] : (lg == 1 ? tr[4 + q] : (lg == 2 ? tr[8 + q] : tr[12 + q]));
+    s16x4_t th, tl;
+    if constexpr (ESZ == 2) split4(t4, th, tl);
+
+#pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       if (wr == blk) {
-        refresh();
-        u32x4_t k1h[NQ], k1l[LO ? NQ : 1];
-        if (blk >= 2) scaled(kr, k1h, k1l, true);
-        // earlier blocks: val -= beta_t sum_{j < 16 blk} L_tj u_j, over U^T (hi + lo)
         if (blk > 0) {
           f32x4_t cacc[RH];
 #pragma unroll
           for (int i = 0; i < RH; ++i) cacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          if constexpr (ESZ == 2) {
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-              if (32 * p < 16 * blk) {
-                f32x4_t at0 = p == 0 ? k_tile(0, k0h, k0l) : k_tile(2, k1h, k1l);
-                f32x4_t at1 = p == 0 ? k_tile(1, k0h, k0l) : k_tile(3, k1h, k1l);
+          for (int i = 0; i < RH; ++i) {
+            const int row = 16 * (hp * RH + i) + lr;
+            if constexpr (ESZ == 2) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                  at0[q] = key_of(2 * p, q) < 16 * blk ? at0[q] : 0.f;
-                  at1[q] = key_of(2 * p + 1, q) < 16 * blk ? at1[q] : 0.f;
-                }
-                u32x4_t bh, bl;
-                pair_operands(at0, at1, bh, bl);
-#pragma unroll
-                for (int i = 0; i < RH; ++i) {
-                  const int r = 16 * (hp * RH + i) + lr;
-                  const u32x4_t uh = ld16(Vt + vt_at(r, 4 * p + lg));
-                  O::mma(cacc[i], uh, bh);
-                  O::mma(cacc[i], uh, bl);
-                  O::mma(cacc[i], ld16(Vl + vt_at(r, 4 * p + lg)), bh);
+              for (int p = 0; p < 2; ++p) {
+                if (32 * p < 16 * blk) {
+                  const u32x4_t uh = ld16(Vt + vt_at(row, 4 * p + lg));
+                  O::mma(cacc[i], oh[p], uh);
+                  O::mma(cacc[i], ol[p], uh);
+                  O::mma(cacc[i], oh[p], ld16(Vl + vt_at(row, 4 * p + lg)));
                 }
               }
-            }
-          } else {
+            } else {
 #pragma unroll
-            for (int jt = 0; jt < 3; ++jt) {
-              if (jt < blk) {
-                const f32x4_t at = jt < 2 ? k_tile(jt, k0h, k0l) : k_tile(jt, k1h, k1l);
-#pragma unroll
-                for (int i = 0; i < RH; ++i) {
-                  const u32x4_t uv = ld16(Vt + vt_at(16 * (hp * RH + i) + lr, 4 * jt + lg));
+              for (int t = 0; t < 3; ++t) {
+                if (t < blk) {
+                  const u32x4_t uv = ld16(Vt + vt_at(row, 4 * t + lg));
 #pragma unroll
                   for (int q = 0; q < 4; ++q)
-                    cacc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(uv[q]), at[q], cacc[i], 0, 0, 0);
+                    cacc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(ot[t][q], __uint_as_float(uv[q]), cacc[i], 0, 0, 0);
                 }
               }
             }
@@ -514,53 +609,35 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
 #pragma unroll
           for (int i = 0; i < RH; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) val[i][q] -= bet * cacc[i][q];
+            for (int q = 0; q < 4; ++q) val[i][q] -= bet4[q] * cacc[i][q];
         }
-        // the block's own strictly lower L (fp32 accumulators) -> lb[t][j]
-        if constexpr (ESZ == 2) {
-          const int p = blk >> 1;
-          const f32x4_t at0 = p == 0 ? k_tile(0, k0h, k0l) : k_tile(2, k1h, k1l);
-          const f32x4_t at1 = p == 0 ? k_tile(1, k0h, k0l) : k_tile(3, k1h, k1l);
 #pragma unroll
-          for (int odd = 0; odd < 2; ++odd)
+        for (int i = 0; i < RH; ++i) {
+          f32x4_t uo = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if constexpr (ESZ == 2) {
+            s16x4_t xh, xl;
+            const float x4[4] = {val[i][0], val[i][1], val[i][2], val[i][3]};
+            split4(x4, xh, xl);
+            uo = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(th, xh, uo, 0, 0, 0);
+            uo = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(tl, xh, uo, 0, 0, 0);
+            uo = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(th, xl, uo, 0, 0, 0);
+          } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int jl = key_of(2 * p + odd, q) - 16 * blk;
-              if (jl >= 0 && jl < 16) lb[lr * LB_LD + jl] = jl < lr ? (odd ? at1[q] : at0[q]) : 0.f;
-            }
-        } else {
-          const f32x4_t at = blk < 2 ? k_tile(blk, k0h, k0l) : k_tile(blk, k1h, k1l);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) lb[lr * LB_LD + 4 * lg + q] = 4 * lg + q < lr ? at[q] : 0.f;
-        }
-        // forward substitution over the block's rows (one wave: its LDS
-        // accesses stay in order); lane lr = jl holds u_jl after step jl
-#pragma unroll
-        for (int jl = 0; jl < 16; ++jl) {
-          const float coef = bet * lb[lr * LB_LD + jl];
-#pragma unroll
-          for (int i = 0; i < RH; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float uj = __shfl(val[i][q], jl + 16 * lg);
-              val[i][q] -= coef * uj;
-            }
-        }
-        // rows of U^T (hi + lo) over the consumed V^T columns of this block
-#pragma unroll
-        for (int i = 0; i < RH; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int off = vt_elem(16 * (hp * RH + i) + 4 * lg + q);
-            const float x = val[i][q];
-            if constexpr (LO) {
-              const uint32_t hb = f32_to_bf16_bits(x);
-              Vt[off] = (uint16_t)hb;
-              Vl[off] = (uint16_t)f32_to_bf16_bits(x - bf16_bits_to_f32(hb));
-            } else {
-              Vt[off] = x;
-            }
+            for (int q = 0; q < 4; ++q) uo = __builtin_amdgcn_mfma_f32_16x16x4f32(t4[q], val[i][q], uo, 0, 0, 0);
           }
+          const int off = row4_at(16 * (hp * RH + i) + lr);
+          if constexpr (ESZ == 2) {
+            u32x2_t h2, l2;
+            h2[0] = pack_bf16x2(uo[0], uo[1]);
+            h2[1] = pack_bf16x2(uo[2], uo[3]);
+            l2[0] = pack_bf16x2(uo[0] - __uint_as_float(h2[0] << 16), uo[1] - __uint_as_float(h2[0] & 0xffff0000u));
+            l2[1] = pack_bf16x2(uo[2] - __uint_as_float(h2[1] << 16), uo[3] - __uint_as_float(h2[1] & 0xffff0000u));
+            *(u32x2_t*)(Vt + off) = h2;
+            *(u32x2_t*)(Vl + off) = l2;
+          } else {
+            *(f32x4_t*)(Vt + off) = uo;
+          }
+        }
       }
       __syncthreads();
     }

@@ -26,6 +26,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));  // 4 bf16 (16x16x16 MFMA operand)
 
 constexpr int kThreads = 256;  // 4 wavefronts
 constexpr int kChunk = 64;     // tokens per chunk of the chunk-parallel kernels
