@@ -237,18 +237,59 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     else return *(const float*)p;
   };
 
-  // ---- stage: beta and b_t (per-head decays: wave 0's scan), V^T (hi + lo),
-  // b_t -> Bc, k^ = k e^{c_sigma - b} (hi + lo) -> Kh, Kl.  Two barriers.
-  auto stage = [&](int c) {
+  int tq = 16 * wr + lr;
+  // The lane indices pass through an empty asm at the start of every phase, so
+  // that the swizzled LDS addresses derived from them are formed inside the
+  // phase instead of being hoisted out of the chunk loop and held (or spilled)
+  // across all of it.
+  auto refresh = [&]() {
+    int x = tid & 63;
+    asm volatile("" : "+v"(x));
+    l = x;
+    lr = x & 15;
+    lg = x >> 4;
+    tq = 16 * wr + lr;
+  };
+  // ---- prefetch: a chunk's k, v (and per-dim decays) into the loaders'
+  // registers, beta and the per-head decay of token l into wave 0's.  The
+  // addresses are clamped to the last token, so the loop's prefetch of the
+  // chunk after the last reloads the last; tokens past the end are zeroed when
+  // staged.
+  float pbe = 0.f, pgx = 0.f;
+  auto prefetch = [&](int c) {
     const int tb = c * kChunk;
     if (w == 0) {
-      const int tok = tb + l;
-      const bool ok = tok < T;
-      const int tc = min(tok, T - 1);
-      const float be = ld1(betab + (int64_t)tc * a.beta_heads);
-      Bt[l] = ok ? be : 0.f;  // tokens past the end: beta = 0, so u = 0
+      const int tc = min(tb + l, T - 1);
+      pbe = ld1(betab + (int64_t)tc * a.beta_heads);
+      if constexpr (DK == 1) pgx = ld1(gb + (int64_t)tc * Hkv);
+    }
+    if (loader) {
+#pragma unroll
+      for (int n = 0; n < NTOK; ++n) {
+        const int64_t off = (int64_t)min(tb + tg * NTOK + n, T - 1) * KS + cb * VEC;
+        pk[n] = ld16(kb + off);
+        pv[n] = ld16(vb + off);
+        if constexpr (DK == 2) pg[n] = ld16(gb + off);
+      }
+    }
+  };
+
+  // ---- stage: beta and b_t (per-head decays: wave 0's scan), V^T (hi + lo),
+  // b_t -> Bc, k^ = k e^{c_sigma - b} (hi + lo) -> Kh, Kl.  Two barriers.  The
+  // lane's own key row for the solve is loaded first, to arrive meanwhile.
+  u32x4_t kr[NQ];
+  auto stage = [&](int c) {
+    const int tb = c * kChunk;
+    {
+      const int tokc = min(tb + tq, T - 1);
+#pragma unroll
+      for (int m = 0; m < NQ; ++m) kr[m] = ld16(kb + (int64_t)tokc * KS + KB * m + VEC * lg);
+    }
+    if (w == 0) {
+      const bool ok = tb + l < T;
+      Bt[l] = ok ? pbe : 0.f;  // tokens past the end: beta = 0, so u = 0
       if constexpr (DK == 1) {
-        float x = ok ? ld1(gb + (int64_t)tc * Hkv) : 0.f;
+        float x = ok ? pgx : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
           const float y = __shfl_up(x, off);
@@ -262,12 +303,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     if (loader) {
 #pragma unroll
       for (int n = 0; n < NTOK; ++n) {
-        const int tok = tb + tg * NTOK + n;
-        const int64_t off = (int64_t)min(tok, T - 1) * KS + cb * VEC;
-        pk[n] = ld16(kb + off);
-        pv[n] = ld16(vb + off);
-        if constexpr (DK == 2) pg[n] = ld16(gb + off);
-        if (tok >= T) {
+        if (tb + tg * NTOK + n >= T) {
           pk[n] = u32x4_t{0u, 0u, 0u, 0u};
           pv[n] = u32x4_t{0u, 0u, 0u, 0u};
           if constexpr (DK == 2) pg[n] = u32x4_t{0u, 0u, 0u, 0u};
@@ -364,19 +400,6 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   // c = 0 (second == false) or b_31, split into hi (+ lo) operands.  The row
   // offsets pass through an empty asm so that each use recomputes the factors
   // instead of the compiler keeping them live across heads.
-  int tq = 16 * wr + lr;
-  // The lane indices pass through an empty asm at the start of every phase, so
-  // that the swizzled LDS addresses derived from them are formed inside the
-  // phase instead of being hoisted out of the chunk loop and held (or spilled)
-  // across all of it.
-  auto refresh = [&]() {
-    int x = tid & 63;
-    asm volatile("" : "+v"(x));
-    l = x;
-    lr = x & 15;
-    lg = x >> 4;
-    tq = 16 * wr + lr;
-  };
   auto scaled = [&](const u32x4_t (&x)[NQ], u32x4_t (&hi)[NQ], u32x4_t (&lo)[LO ? NQ : 1], bool second) {
     int rt_off = tq * BC_LD, r31_off = 31 * BC_LD;
     asm volatile("" : "+v"(rt_off), "+v"(r31_off));
@@ -437,6 +460,17 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     }
   };
 
+  // ---- query rows of head part hp, head hh, in two register sets that
+  // alternate between heads: each head's rows are requested one step ahead
+  // (the first during the solve), and no register still being loaded is copied
+  u32x4_t qbuf[2][NQ];
+  auto load_q = [&](int c, int hh) {
+    const int tokc = min(c * kChunk + tq, T - 1);
+    const int hq = hp + P * hh;
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) qbuf[hh & 1][m] = ld16(qb + (int64_t)tokc * QS + hq * D + KB * m + VEC * lg);
+  };
+
   // ---- pseudo-values.  Wave (hp, wr) owns rows [16wr, 16wr+16) of the chunk
   // and dv tiles hp*RH .. hp*RH + RH - 1, held token-major: lane (lg, lr) holds
   // rows 16wr + 4lg + q of value dim 16ct + lr, which is also the B operand
@@ -451,10 +485,6 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   //      U^T over the consumed V^T columns.
   auto solve = [&](int c) {
     refresh();
-    const int tokc = min(c * kChunk + tq, T - 1);
-    u32x4_t kr[NQ];
-#pragma unroll
-    for (int m = 0; m < NQ; ++m) kr[m] = ld16(kb + (int64_t)tokc * KS + KB * m + VEC * lg);
     u32x4_t k0h[NQ], k0l[LO ? NQ : 1];
     scaled(kr, k0h, k0l, false);  // kbar, also the first key block's scaled row
     const int r0 = 16 * wr + 4 * lg;  // the lane's first row
@@ -515,14 +545,16 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
           if (32 * p <= 16 * wr + 15) {
             f32x4_t at0 = p == 0 ? k_tile(0, k0h, k0l) : k_tile(2, k1h, k1l);
             f32x4_t at1 = p == 0 ? k_tile(1, k0h, k0l) : k_tile(3, k1h, k1l);
-            if (p == (wr >> 1)) {
+            // the diagonal block's keys 16wr + 8(lg & 1) + 4odd + q sit in
+            // lane groups 2(wr & 1) and 2(wr & 1) + 1 of pair wr / 2
+            if (p == (wr >> 1) && (lg >> 1) == (wr & 1)) {
 #pragma unroll
-              for (int odd = 0; odd < 2; ++odd)
+              for (int odd = 0; odd < 2; ++odd) {
+                f32x4_t x = odd ? at1 : at0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                  const int jl = key_of(2 * p + odd, q) - 16 * wr;
-                  if (jl >= 0 && jl < 16) lb[lr * 16 + jl] = jl < lr ? (odd ? at1[q] : at0[q]) : 0.f;
-                }
+                for (int q = 0; q < 4; ++q) x[q] = 8 * (lg & 1) + 4 * odd + q < lr ? x[q] : 0.f;
+                *(f32x4_t*)(lb + lr * 16 + 8 * (lg & 1) + 4 * odd) = x;
+              }
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -538,8 +570,10 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
           if (t <= wr) {
             const f32x4_t at = t < 2 ? k_tile(t, k0h, k0l) : k_tile(t, k1h, k1l);
             if (t == wr) {
+              f32x4_t x = at;
 #pragma unroll
-              for (int q = 0; q < 4; ++q) lb[lr * 16 + 4 * lg + q] = 4 * lg + q < lr ? at[q] : 0.f;
+              for (int q = 0; q < 4; ++q) x[q] = 4 * lg + q < lr ? x[q] : 0.f;
+              *(f32x4_t*)(lb + lr * 16 + 4 * lg) = x;
             } else if (t < 3) {
               ot[t] = at;
             }
@@ -547,33 +581,41 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
         }
       }
     }
-    // row lr of T: y (I + diag(beta) L_ii) = e_lr, from the last column down;
-    // tr[c] gathers sum_{j>c} beta_j L_jc y_j until step c turns it into y_c
-    float tr[16];
+    // row lr of T, columns 4lg .. 4lg+3 in lane group lg: y (I + diag(beta) L_ii)
+    // = e_lr, solved by 4-column blocks from the last.  Block s is finished by
+    // group s from the sums gathered so far, then sent to the lower groups,
+    // which add its terms to their sums (the other groups' sums are not used
+    // again and take the same arithmetic unmasked).
+    float t4[4] = {0.f, 0.f, 0.f, 0.f}, acc4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int cc = 0; cc < 16; ++cc) tr[cc] = 0.f;
+    for (int sb = 3; sb >= 0; --sb) {
+      f32x4_t lrow[4];
 #pragma unroll
-    for (int jj = 15; jj >= 0; --jj) {
-      const float yj = (lr == jj ? 1.f : 0.f) - tr[jj];
-      tr[jj] = yj;
-      if (jj > 0) {
-        const float by = Bt[16 * wr + jj] * yj;
+      for (int e = 0; e < 4; ++e) lrow[e] = *(const f32x4_t*)(lb + 16 * (4 * sb + e) + 4 * lg);
+      const f32x4_t bs = *(const f32x4_t*)(Bt + 16 * wr + 4 * sb);
+      float z[4];
 #pragma unroll
-        for (int c4 = 0; c4 < jj; c4 += 4) {
-          const f32x4_t lrow = *(const f32x4_t*)(lb + 16 * jj + c4);
+      for (int e = 3; e >= 0; --e) {
+        float v = (lr == 4 * sb + e ? 1.f : 0.f) - acc4[e];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (c4 + e < jj) tr[c4 + e] += lrow[e] * by;
+        for (int e2 = e + 1; e2 < 4; ++e2) v -= bs[e2] * lrow[e2][e] * z[e2];
+        z[e] = v;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t4[e] = lg == sb ? z[e] : t4[e];
+      if (sb > 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float by = bs[e] * __shfl(t4[e], 16 * sb + lr);
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) acc4[e2] += lrow[e][e2] * by;
         }
       }
     }
-    // the A operand of U = T X: T[lr][4lg + q]
-    float t4[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) t4[q] = lg == 0 ? tr[q] : (lg == 1 ? tr[4 + q] : (lg == 2 ? tr[8 + q] : tr[12 + q]));
     s16x4_t th, tl;
     if constexpr (ESZ == 2) split4(t4, th, tl);
 
+    load_q(c, 0);
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       if (wr == blk) {
@@ -646,15 +688,13 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   // ---- outputs of the chunk's queries (per head), with U in V's place
   auto outputs = [&](int c) {
     const int tok = c * kChunk + tq;
-    const int tokc = min(tok, T - 1);
     auto need = [&](int t) { return ESZ == 2 ? (32 * (t >> 1) <= 16 * wr + 15) : (t <= wr); };
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       refresh();
       const int hq = hp + P * hh;
-      u32x4_t qr[NQ];
-#pragma unroll
-      for (int m = 0; m < NQ; ++m) qr[m] = ld16(qb + (int64_t)tokc * QS + hq * D + KB * m + VEC * lg);
+      if (hh + 1 < HPW) load_q(c, hh + 1);
+      const u32x4_t (&qr)[NQ] = qbuf[hh & 1];
       u32x4_t qop[NQ], qlo[LO ? NQ : 1];
       scaled(qr, qop, qlo, false);
       auto a_tile = [&](int t) {
@@ -776,8 +816,10 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     }
   };
 
+  prefetch(0);
   for (int c = 0; c < nchunks; ++c) {
     stage(c);
+    prefetch(min(c + 1, nchunks - 1));
     solve(c);
     outputs(c);
     update();
