@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kApplyThreads, 4) void apply_kernel(ApplyArgs a) {
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+  int l = tid & 63, lr = l & 15, lg = l >> 4;
   const int nseg = a.seg_count;
   const int u = blockIdx.x / nseg, sg = blockIdx.x % nseg;
   const int T = a.T, H = a.H, HD = H * D;
@@ -148,6 +148,15 @@ __global__ __launch_bounds__(kApplyThreads, 4) void apply_kernel(ApplyArgs a) {
   };
   auto process = [&](const u32x4_t (&q)[NLD], uint32_t k, int i) {
     if (i >= nsteps) return;
+    // the lane indices pass through an empty asm, so that the LDS addresses
+    // derived from them are formed per block, not held across the loop
+    {
+      int x = tid & 63;
+      asm volatile("" : "+v"(x));
+      l = x;
+      lr = x & 15;
+      lg = x >> 4;
+    }
     const int r0 = kApplyBlockRows * blk_of(i);
     if (!((live >> i) & 1u)) {
 #pragma unroll

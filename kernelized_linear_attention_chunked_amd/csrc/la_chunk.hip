@@ -98,6 +98,10 @@ void chunk_kernel(ChunkArgs a) {
   // exact sum of two bf16 values), and each product with V takes one more MFMA
   // with the lo tile, so that V reaches the products unrounded
   constexpr bool VLO = !std::is_same_v<IT, DT>;
+  // lane indices re-derived per chunk where that removes spills (fp32 and
+  // fp16 inputs at head size 128, the bf16 state pass): elsewhere it measured
+  // slower
+  constexpr bool REFRESH = D >= 128 && (ESZ == 4 || VLO || MODE == kState);
   constexpr int VL_BYTES = (USE_KV && VLO) ? NDT * 16 * VT_LD * ESZ : 0;
   constexpr int NS = NDT * NVT;                    // 16x16 tiles of the (extended) state
   constexpr int TPW = (NS + NW - 1) / NW;          // state tiles per wave
@@ -116,7 +120,14 @@ void chunk_kernel(ChunkArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qr = w & 3;   // query rows [16qr, 16qr+16) of the chunk
   const int hv = w >> 2;  // value half: dv tiles [hv*NDH, (hv+1)*NDH) (+ normaliser tile)
-  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+  int l = tid & 63, lr = l & 15, lg = l >> 4;
+  auto refresh = [&]() {
+    if constexpr (REFRESH) {
+      l = opaque_lane(tid);
+      lr = l & 15;
+      lg = l >> 4;
+    }
+  };
   const int bid = blockIdx.x;
   const int u = bid / a.seg_count;
   const int s = a.seg_first + bid % a.seg_count;
@@ -412,6 +423,7 @@ void chunk_kernel(ChunkArgs a) {
   auto vl_op = [&](int ct, int blk) { return ld16(Vl + vt_at(16 * ct + lr, blk)); };
 
   auto compute = [&](int c, bool live, bool full) {
+    refresh();
     if (!live) {
       // fully masked chunk: state unchanged, outputs zero
       if constexpr (USE_Q) {

@@ -63,6 +63,9 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
   // product with V takes one more MFMA with the lo tile.  Only the inter-chunk
   // product q S rounds q to bf16, as S itself is.
   constexpr bool VLO = !std::is_same_v<IT, DT>;
+  // lane indices re-derived per chunk and head where that removes spills:
+  // elsewhere it measured slower
+  constexpr bool REFRESH = D >= 128 && (G == 8 || (VLO && G >= 2) || (ESZ == 4 && G >= 4));
   constexpr int KN_BYTES = kChunk * KN_LD * ESZ;
   constexpr int VT_BYTES = D * VT_LD * ESZ;
   constexpr int VL_BYTES = VLO ? D * VT_LD * ESZ : 0;
@@ -88,7 +91,14 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hp = w >> 2, wr = w & 3;
-  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+  int l = tid & 63, lr = l & 15, lg = l >> 4;
+  auto refresh = [&]() {
+    if constexpr (REFRESH) {
+      l = opaque_lane(tid);
+      lr = l & 15;
+      lg = l >> 4;
+    }
+  };
   const int u = blockIdx.x / a.seg_count;
   const int s = a.seg_first + blockIdx.x % a.seg_count;
   const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
@@ -284,6 +294,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
   };
 
   auto compute = [&](int c) {
+    refresh();
     const float btot = __shfl(bcs, 63);
     if constexpr (OUT) {
       const float bi = __shfl(bcs, 16 * wr + lr);
@@ -319,6 +330,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
       const int tok = c * kChunk + 16 * wr + lr;
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
+        refresh();
         // the head's queries in operand layout (row lr, dk KB*m + VEC*lg), as
         // loaded (raw fp16 for fp16 inputs)
         u32x4_t qop[NQ];
