@@ -669,9 +669,21 @@ __global__ __launch_bounds__(kThreads) void seg_prefix_kernel(float* ws_s, float
     acc = z_in ? z_in[(int64_t)u * D + ez] : 0.f;
   }
   base[0] = acc;
-  for (int s = 1; s < nseg; ++s) {
-    acc += base[s * stride];
-    base[s * stride] = acc;
+  // the slots are loaded a batch at a time, all before the batch's stores, so
+  // that a unit takes one memory round trip per batch rather than per segment
+  // (addresses past the last slot are clamped to it and their values unused)
+  constexpr int NB = 16;
+  for (int s0 = 1; s0 < nseg; s0 += NB) {
+    float x[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) x[j] = base[min(s0 + j, nseg - 1) * stride];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (s0 + j < nseg) {
+        acc += x[j];
+        base[(s0 + j) * stride] = acc;
+      }
+    }
   }
 }
 
@@ -692,8 +704,17 @@ __global__ __launch_bounds__(kThreads) void seg_sum_kernel(float* ws_s, float* w
     base = ws_z + (int64_t)u * nseg * D + (e - D * D);
     stride = D;
   }
+  // a batch of slots in flight at a time; summed in segment order
+  constexpr int NB = 16;
   float acc = 0.f;
-  for (int s = 0; s < nseg; ++s) acc += base[s * stride];
+  for (int s0 = 0; s0 < nseg; s0 += NB) {
+    float x[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) x[j] = base[min(s0 + j, nseg - 1) * stride];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (s0 + j < nseg) acc += x[j];
+  }
   base[0] = acc;
 }
 

@@ -557,9 +557,25 @@ __global__ __launch_bounds__(kThreads) void gated_prefix_kernel(float* ws_s, con
   const int astride = per_dim ? D : 1;
   float acc = s_in ? s_in[(int64_t)u * per + e] : 0.f;
   base[0] = acc;
-  for (int s = 1; s < nseg; ++s) {
-    acc = fmaf(ap[s * astride], acc, base[s * per]);
-    base[s * per] = acc;
+  // the slots are loaded a batch at a time, all before the batch's stores, so
+  // that a unit takes one memory round trip per batch rather than per segment
+  // (addresses past the last slot are clamped to it and their values unused)
+  constexpr int NB = 16;
+  for (int s0 = 1; s0 < nseg; s0 += NB) {
+    float x[NB], av[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int sj = min(s0 + j, nseg - 1);
+      x[j] = base[sj * per];
+      av[j] = ap[sj * astride];
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (s0 + j < nseg) {
+        acc = fmaf(av[j], acc, x[j]);
+        base[(s0 + j) * per] = acc;
+      }
+    }
   }
 }
 
