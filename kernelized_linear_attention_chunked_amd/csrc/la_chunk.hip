@@ -23,7 +23,8 @@
 //
 // Work split inside a workgroup (one (batch, head) unit and one segment of
 // chunks; 4 wavefronts, or 8 at head size 128):
-//   wave w owns query rows [16qr, 16qr+16) of the chunk, qr = w % 4 (A^T tiles
+//   wave w owns query rows [16qr, 16qr+16) of the chunk, qr = w % 4 (reversed
+//   for w >= 4, so that the two waves of a SIMD balance; A^T tiles
 //   jt <= qr), and for them the output tiles of one value half (w / 4) plus the
 //   normaliser tile; and a contiguous 1/NW of the 16x16 tiles of S.
 // LDS holds phiK and phiQ in natural [token][d] layout, V transposed
@@ -118,8 +119,11 @@ void chunk_kernel(ChunkArgs a) {
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qr = w & 3;   // query rows [16qr, 16qr+16) of the chunk
-  const int hv = w >> 2;  // value half: dv tiles [hv*NDH, (hv+1)*NDH) (+ normaliser tile)
+  // query rows [16qr, 16qr+16) of the chunk and value half hv (dv tiles
+  // [hv*NDH, (hv+1)*NDH), plus the normaliser tile).  Waves w and w + 4 share a
+  // SIMD; giving them row blocks qr and 3 - qr evens out the causal work.
+  const int qr = (w & 4) ? 3 - (w & 3) : (w & 3);
+  const int hv = w >> 2;
   int l = tid & 63, lr = l & 15, lg = l >> 4;
   auto refresh = [&]() {
     if constexpr (REFRESH) {

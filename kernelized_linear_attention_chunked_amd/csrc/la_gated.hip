@@ -13,7 +13,8 @@
 //
 // One workgroup serves one (batch, kv head) unit and a segment of chunks, with
 // all G query heads of the group: 4*P wavefronts, wave w = (head part hp =
-// w/4, row part wr = w%4); the wave owns query rows [16wr, 16wr+16) of heads
+// w/4, row part wr = w%4, reversed for w >= 4); the wave owns query rows
+// [16wr, 16wr+16) of heads
 // hp, hp+P, ...  The state tiles are spread over all waves.  The k/v/decay of
 // a chunk are loaded once and shared by the G heads.
 #include "la_device.hpp"
@@ -90,7 +91,9 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hp = w >> 2, wr = w & 3;
+  // waves w and w + 4 share a SIMD: row blocks wr and 3 - wr even out the
+  // causal work between SIMDs
+  const int hp = w >> 2, wr = (w & 4) ? 3 - (w & 3) : (w & 3);
   int l = tid & 63, lr = l & 15, lg = l >> 4;
   auto refresh = [&]() {
     if constexpr (REFRESH) {

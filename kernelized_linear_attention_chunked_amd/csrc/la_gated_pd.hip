@@ -91,7 +91,9 @@ __global__ __launch_bounds__(PdShape<G>::NTH) void gated_pd_kernel(GatedArgs a) 
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hp = w >> 2, wr = w & 3;
+  // waves w and w + 4 share a SIMD: row blocks wr and 3 - wr even out the
+  // causal work between SIMDs
+  const int hp = w >> 2, wr = (w & 4) ? 3 - (w & 3) : (w & 3);
   const int l = tid & 63, lr = l & 15, lg = l >> 4;
   const int u = blockIdx.x / a.seg_count;
   const int s = a.seg_first + blockIdx.x % a.seg_count;
