@@ -650,39 +650,46 @@ void chunk_kernel(ChunkArgs a) {
 // Exclusive prefix over segment partial states, in place.  Slot s of unit u
 // holds the increment of segment s-1 on entry (slot 0 is ignored) and the
 // state before segment s on exit; slot 0 receives the caller's initial state
-// (or zeros).  One thread per state element, sequential over segments.
+// (or zeros).  One thread per four consecutive state elements (D is a multiple
+// of 4, so a group never straddles the S and Z parts), sequential over
+// segments.  Every load of a batch of 16 slots is issued before the batch's
+// stores, so a unit takes one memory round trip per batch rather than one per
+// segment; slots past the last are clamped to it and their values unused.
+constexpr int kSegBatch = 16;
+
 __global__ __launch_bounds__(kThreads) void seg_prefix_kernel(float* ws_s, float* ws_z,
                                                               const float* s_in, const float* z_in,
                                                               int U, int nseg, int D, int norm) {
-  const int64_t per = (int64_t)D * D + (norm ? D : 0);
+  const int64_t per4 = ((int64_t)D * D + (norm ? D : 0)) / 4;
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (int64_t)U * per) return;
-  const int u = (int)(idx / per);
-  const int e = (int)(idx % per);
-  float* base;
-  int64_t stride;
-  float acc;
+  if (idx >= (int64_t)U * per4) return;
+  const int u = (int)(idx / per4);
+  const int e = 4 * (int)(idx % per4);
+  f32x4_t* base;
+  int64_t stride;  // in 4-element groups
+  const f32x4_t* init;
   if (e < D * D) {
-    base = ws_s + (int64_t)u * nseg * D * D + e;
-    stride = (int64_t)D * D;
-    acc = s_in ? s_in[(int64_t)u * D * D + e] : 0.f;
+    base = (f32x4_t*)(ws_s + (int64_t)u * nseg * D * D + e);
+    stride = (int64_t)D * D / 4;
+    init = s_in ? (const f32x4_t*)(s_in + (int64_t)u * D * D + e) : nullptr;
   } else {
     const int ez = e - D * D;
-    base = ws_z + (int64_t)u * nseg * D + ez;
-    stride = D;
-    acc = z_in ? z_in[(int64_t)u * D + ez] : 0.f;
+    base = (f32x4_t*)(ws_z + (int64_t)u * nseg * D + ez);
+    stride = D / 4;
+    init = z_in ? (const f32x4_t*)(z_in + (int64_t)u * D + ez) : nullptr;
   }
+  f32x4_t acc = init ? *init : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t x[kSegBatch];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int j = 0; j < kSegBatch; ++j) x[j] = base[min(s0 + j, nseg - 1) * stride];
+  };
+  if (nseg > 1) load_batch(1);
   base[0] = acc;
-  // the slots are loaded a batch at a time, all before the batch's stores, so
-  // that a unit takes one memory round trip per batch rather than per segment
-  // (addresses past the last slot are clamped to it and their values unused)
-  constexpr int NB = 16;
-  for (int s0 = 1; s0 < nseg; s0 += NB) {
-    float x[NB];
+  for (int s0 = 1; s0 < nseg; s0 += kSegBatch) {
+    if (s0 > 1) load_batch(s0);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) x[j] = base[min(s0 + j, nseg - 1) * stride];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
+    for (int j = 0; j < kSegBatch; ++j) {
       if (s0 + j < nseg) {
         acc += x[j];
         base[(s0 + j) * stride] = acc;
@@ -691,32 +698,31 @@ __global__ __launch_bounds__(kThreads) void seg_prefix_kernel(float* ws_s, float
   }
 }
 
-// Sum of all segment partials of a unit, in fixed segment order, into slot 0.
+// Sum of all segment partials of a unit, in fixed segment order, into slot 0
+// (four consecutive elements per thread, a batch of slots in flight at a time).
 __global__ __launch_bounds__(kThreads) void seg_sum_kernel(float* ws_s, float* ws_z, int U,
                                                            int nseg, int D, int norm) {
-  const int64_t per = (int64_t)D * D + (norm ? D : 0);
+  const int64_t per4 = ((int64_t)D * D + (norm ? D : 0)) / 4;
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (int64_t)U * per) return;
-  const int u = (int)(idx / per);
-  const int e = (int)(idx % per);
-  float* base;
+  if (idx >= (int64_t)U * per4) return;
+  const int u = (int)(idx / per4);
+  const int e = 4 * (int)(idx % per4);
+  f32x4_t* base;
   int64_t stride;
   if (e < D * D) {
-    base = ws_s + (int64_t)u * nseg * D * D + e;
-    stride = (int64_t)D * D;
+    base = (f32x4_t*)(ws_s + (int64_t)u * nseg * D * D + e);
+    stride = (int64_t)D * D / 4;
   } else {
-    base = ws_z + (int64_t)u * nseg * D + (e - D * D);
-    stride = D;
+    base = (f32x4_t*)(ws_z + (int64_t)u * nseg * D + (e - D * D));
+    stride = D / 4;
   }
-  // a batch of slots in flight at a time; summed in segment order
-  constexpr int NB = 16;
-  float acc = 0.f;
-  for (int s0 = 0; s0 < nseg; s0 += NB) {
-    float x[NB];
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nseg; s0 += kSegBatch) {
+    f32x4_t x[kSegBatch];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) x[j] = base[min(s0 + j, nseg - 1) * stride];
+    for (int j = 0; j < kSegBatch; ++j) x[j] = base[min(s0 + j, nseg - 1) * stride];
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int j = 0; j < kSegBatch; ++j)
       if (s0 + j < nseg) acc += x[j];
   }
   base[0] = acc;
@@ -773,7 +779,7 @@ hipError_t launch_chunk(int mode, int io, int D, int fm, int norm, const ChunkAr
 
 hipError_t launch_seg_prefix(float* ws_s, float* ws_z, const float* s_in, const float* z_in, int U,
                              int nseg, int D, int norm, hipStream_t st) {
-  const int64_t n = (int64_t)U * ((int64_t)D * D + (norm ? D : 0));
+  const int64_t n = (int64_t)U * ((int64_t)D * D + (norm ? D : 0)) / 4;
   const int grid = (int)((n + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(seg_prefix_kernel, dim3(grid), dim3(kThreads), 0, st, ws_s, ws_z, s_in, z_in,
                      U, nseg, D, norm);
@@ -782,7 +788,7 @@ hipError_t launch_seg_prefix(float* ws_s, float* ws_z, const float* s_in, const 
 
 hipError_t launch_seg_sum(float* ws_s, float* ws_z, int U, int nseg, int D, int norm,
                           hipStream_t st) {
-  const int64_t n = (int64_t)U * ((int64_t)D * D + (norm ? D : 0));
+  const int64_t n = (int64_t)U * ((int64_t)D * D + (norm ? D : 0)) / 4;
   const int grid = (int)((n + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(seg_sum_kernel, dim3(grid), dim3(kThreads), 0, st, ws_s, ws_z, U, nseg, D, norm);
   return hipGetLastError();

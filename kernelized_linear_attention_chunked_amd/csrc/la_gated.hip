@@ -547,36 +547,44 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
 // the state before segment s:  S(0) = past (or 0),  S(s) = a[s] S(s-1) + dS(s-1).
 // a[s] is one factor per slot, or with a per-key-dim decay one per slot and row
 // dk of S (ws_a laid out [unit][slot][dk]).
+// One thread per four consecutive elements of a row of S (one decay factor for
+// all four); every load of a batch of 16 slots is issued before the batch's
+// stores, so a unit takes one memory round trip per batch rather than one per
+// segment (slots past the last are clamped to it and their values unused).
 __global__ __launch_bounds__(kThreads) void gated_prefix_kernel(float* ws_s, const float* ws_a,
                                                                 const float* s_in, int U, int nseg,
                                                                 int D, int per_dim) {
+  constexpr int NB = 16;
   const int64_t per = (int64_t)D * D;
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (int64_t)U * per) return;
-  const int u = (int)(idx / per);
-  const int64_t e = idx % per;
-  float* base = ws_s + (int64_t)u * nseg * per + e;
+  if (idx >= (int64_t)U * per / 4) return;
+  const int u = (int)(idx / (per / 4));
+  const int64_t e = 4 * (idx % (per / 4));
+  f32x4_t* base = (f32x4_t*)(ws_s + (int64_t)u * nseg * per + e);
+  const int64_t stride = per / 4;
   const float* ap = per_dim ? ws_a + (int64_t)u * nseg * D + e / D : ws_a + (int64_t)u * nseg;
   const int astride = per_dim ? D : 1;
-  float acc = s_in ? s_in[(int64_t)u * per + e] : 0.f;
-  base[0] = acc;
-  // the slots are loaded a batch at a time, all before the batch's stores, so
-  // that a unit takes one memory round trip per batch rather than per segment
-  // (addresses past the last slot are clamped to it and their values unused)
-  constexpr int NB = 16;
-  for (int s0 = 1; s0 < nseg; s0 += NB) {
-    float x[NB], av[NB];
+  f32x4_t acc = s_in ? *(const f32x4_t*)(s_in + (int64_t)u * per + e) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t x[NB];
+  float av[NB];
+  auto load_batch = [&](int s0) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int sj = min(s0 + j, nseg - 1);
-      x[j] = base[sj * per];
+      x[j] = base[sj * stride];
       av[j] = ap[sj * astride];
     }
+  };
+  if (nseg > 1) load_batch(1);
+  base[0] = acc;
+  for (int s0 = 1; s0 < nseg; s0 += NB) {
+    if (s0 > 1) load_batch(s0);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (s0 + j < nseg) {
-        acc = fmaf(av[j], acc, x[j]);
-        base[(s0 + j) * per] = acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(av[j], acc[i], x[j][i]);
+        base[(s0 + j) * stride] = acc;
       }
     }
   }
@@ -623,7 +631,7 @@ hipError_t launch_gated(int mode, int io, int D, int G, const GatedArgs& a, int 
 
 hipError_t launch_gated_prefix(float* ws_s, const float* ws_a, const float* s_in, int U, int nseg,
                                int D, int per_dim, hipStream_t st) {
-  const int64_t n = (int64_t)U * D * D;
+  const int64_t n = (int64_t)U * D * D / 4;
   const int grid = (int)((n + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(gated_prefix_kernel, dim3(grid), dim3(kThreads), 0, st, ws_s, ws_a, s_in, U,
                      nseg, D, per_dim);
