@@ -334,6 +334,7 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
   pr.seg_first = 0;
   pr.seg_chunks = (int32_t)p.split_chunks;
   pr.nseg_total = (int32_t)p.nsplit;
+  pr.chunk_step = (int32_t)p.nsplit;  // split s sums chunks s, s + nsplit, ...: masked tails spread
   e = la::launch_chunk(la::kModeState, dtype, Di, feature_map, norm, pr, (int)(U * p.nsplit), st);
   if (e == hipSuccess) e = la::launch_seg_sum(ws_s, ws_z, (int)U, (int)p.nsplit, Di, norm, st);
   if (e == hipSuccess) {

@@ -138,8 +138,9 @@ void chunk_kernel(ChunkArgs a) {
   const int H = a.H, T = a.T;
   const int b = u / H, h = u % H;
   const int nchunks = (T + kChunk - 1) / kChunk;
-  const int c0 = s * a.seg_chunks;
-  const int c1 = min(c0 + a.seg_chunks, nchunks);
+  const int cstep = a.chunk_step > 1 ? a.chunk_step : 1;
+  const int c0 = cstep > 1 ? s : s * a.seg_chunks;
+  const int c1 = cstep > 1 ? nchunks : min(c0 + a.seg_chunks, nchunks);
   const int HD = H * D;
   const int64_t unit_off = (int64_t)b * T * HD + (int64_t)h * D;
   const IT* qb = (const IT*)a.q + unit_off;
@@ -268,7 +269,7 @@ void chunk_kernel(ChunkArgs a) {
       const uint64_t bal = __ballot(mnext != 0u);
       plive = bal != 0;
       pfull = pfull && bal == ~0ull;
-      mnext = load_mask(c + 1);
+      mnext = load_mask(c + cstep);
       if (!plive) return;  // fully masked chunk: nothing to load
     }
     if constexpr (USE_Q && !QS_STAGE) {
@@ -596,7 +597,7 @@ void chunk_kernel(ChunkArgs a) {
   };
 
   if (c0 < c1) prefetch(c0);
-  for (int c = c0; c < c1; ++c) {
+  for (int c = c0; c < c1; c += cstep) {
     const bool live = MASKED ? plive : true;
     const bool full = pfull;
     if (live) {
@@ -606,7 +607,7 @@ void chunk_kernel(ChunkArgs a) {
         stage(std::false_type{});
       __syncthreads();
     }
-    if (c + 1 < c1) prefetch(c + 1);
+    if (c + cstep < c1) prefetch(c + cstep);
     // a dead chunk touches no LDS, so it needs neither barrier: the next
     // chunk's stage cannot overwrite anything a slower wave still reads
     compute(c, live, full);

@@ -28,6 +28,11 @@ struct ChunkArgs {
   int32_t out_slot_off;
   int32_t T, H;
   int32_t seg_count, seg_first, seg_chunks, nseg_total;
+  // 0 or 1: segment s is the seg_chunks consecutive chunks from s*seg_chunks.
+  // n > 1 (the state mode of a non-causal reduction, whose sum does not depend
+  // on order): segment s takes chunks s, s+n, s+2n, ..., so masked tails are
+  // spread over all segments of a unit
+  int32_t chunk_step;
   float eps;
 };
 
