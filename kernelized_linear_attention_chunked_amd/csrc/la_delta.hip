@@ -64,6 +64,9 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   constexpr int SB_LD = D + PADE;
   constexpr int BC_LD = D + 4;
   constexpr bool LO = ESZ == 2;   // 16-bit: hi + lo operands (k^, q^, U, L, A)
+  // the scaled rows q^, kbar and the keys k^ have a lo part; without a decay
+  // they are bf16 inputs taken as they are, whose lo part is exactly zero
+  constexpr bool XLO = LO && !(DK == 0 && std::is_same_v<IT, uint16_t>);
   constexpr int KN_BYTES = kChunk * KN_LD * ESZ;
   constexpr int VT_BYTES = D * VT_LD * ESZ;
   constexpr int SB_BYTES = D * SB_LD * ESZ;
@@ -75,7 +78,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   constexpr int WT_BYTES = NW * D * 4;
   constexpr int BT_BYTES = 2 * kChunk * 4;  // beta and the per-head cumulative decay
   constexpr int LB_BYTES = NW * 16 * 16 * 4;  // per wave: its 16 x 16 diagonal block of L (fp32)
-  constexpr int LDS = (LO ? 2 : 1) * (KN_BYTES + VT_BYTES) + SB_BYTES + SL_BYTES + BC_BYTES + WT_BYTES + BT_BYTES +
+  constexpr int LDS = (XLO ? 2 : 1) * KN_BYTES + (LO ? 2 : 1) * VT_BYTES + SB_BYTES + SL_BYTES + BC_BYTES + WT_BYTES + BT_BYTES +
                       LB_BYTES;
   constexpr int NS = NDT * NDT;
   constexpr int TPW = (NS + NW - 1) / NW;
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     return p;
   };
   DT* Kh = (DT*)carve(KN_BYTES);                  // k^ = k e^{c_sigma - b} (hi)
-  DT* Kl = (DT*)carve(LO ? KN_BYTES : 0);         // its lo part
+  DT* Kl = (DT*)carve(XLO ? KN_BYTES : 0);        // its lo part
   DT* Vt = (DT*)carve(VT_BYTES);                  // V^T, then U^T (hi)
   DT* Vl = (DT*)carve(LO ? VT_BYTES : 0);         // lo parts
   DT* Sb = (DT*)carve(SB_BYTES);                  // S^T of the state before the chunk
@@ -390,7 +393,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
         u32x4_t hi, lo;
         split8(kh, hi, lo);
         st16(Kh + kn_at(t, cb * VEC), hi);
-        if constexpr (LO) st16(Kl + kn_at(t, cb * VEC), lo);
+        if constexpr (XLO) st16(Kl + kn_at(t, cb * VEC), lo);
       }
     }
     __syncthreads();
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
       u32x4_t h, lw;
       split8(f, h, lw);
       hi[m] = h;
-      if constexpr (LO) lo[m] = lw;
+      if constexpr (XLO) lo[m] = lw;
     }
   };
   // key row of A^T / L^T tile t (bf16: tile pairs over 32 keys with permuted
@@ -441,7 +444,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     for (int m = 0; m < NQ; ++m) {
       const u32x4_t kh = ld16(Kh + kn_at(krow, KB * m + VEC * lg));
       O::mma(at, kh, xh[m]);
-      if constexpr (LO) {
+      if constexpr (XLO) {
         O::mma(at, ld16(Kl + kn_at(krow, KB * m + VEC * lg)), xh[m]);
         O::mma(at, kh, xl[m]);
       }
@@ -501,7 +504,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
         const int so = sq_at(16 * (hp * RH + i) + lr, KB * m + VEC * lg);
         const u32x4_t av = ld16(Sb + so);
         O::mma(val[i], k0h[m], av);
-        if constexpr (LO) O::mma(val[i], k0l[m], av);
+        if constexpr (XLO) O::mma(val[i], k0l[m], av);
         if constexpr (SLO) O::mma(val[i], k0h[m], ld16(Sl + so));
       }
     }
@@ -716,7 +719,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
           const int so = sq_at(16 * ct + lr, KB * m + VEC * lg);
           const u32x4_t av = ld16(Sb + so);
           O::mma(nacc[ct], av, qop[m]);
-          if constexpr (LO) O::mma(nacc[ct], av, qlo[m]);
+          if constexpr (XLO) O::mma(nacc[ct], av, qlo[m]);
           if constexpr (SLO) O::mma(nacc[ct], ld16(Sl + so), qop[m]);
         }
       }
@@ -797,7 +800,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
               const int sk = KB * m + VEC * lg + e;
               const int off = kn_at(sk, dk);
               float kv = to_f(Kh[off]);
-              if constexpr (LO) kv += to_f(Kl[off]);
+              if constexpr (XLO) kv += to_f(Kl[off]);
               f[e] = DK == 0 ? kv : kv * __expf(bC - (sk >= 32 ? c31 : 0.f));
             }
             split8(f, kop[m], kol[m]);
