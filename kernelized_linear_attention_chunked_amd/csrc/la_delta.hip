@@ -64,9 +64,14 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   constexpr int SB_LD = D + PADE;
   constexpr int BC_LD = D + 4;
   constexpr bool LO = ESZ == 2;   // 16-bit: hi + lo operands (k^, q^, U, L, A)
-  // the scaled rows q^, kbar and the keys k^ have a lo part; without a decay
-  // they are bf16 inputs taken as they are, whose lo part is exactly zero
-  constexpr bool XLO = LO && !(DK == 0 && std::is_same_v<IT, uint16_t>);
+  // RAW: bf16 inputs without a per-dim decay.  q and k then enter the MFMAs as
+  // they are (exact), and a per-head decay is applied in fp32 after each
+  // product: exp(b_t - b_j) per element of A and L, exp(b_t) per row of the
+  // inter term and of Kbar S_0, as in the per-head gated kernel.  Otherwise the
+  // scaled rows q^, kbar and the keys k^ are formed first and carry a lo part.
+  constexpr bool RAW = LO && DK <= 1 && std::is_same_v<IT, uint16_t>;
+  constexpr bool XLO = LO && !RAW;
+  constexpr bool RAWDEC = RAW && DK == 1;  // RAW with factors to apply
   constexpr int KN_BYTES = kChunk * KN_LD * ESZ;
   constexpr int VT_BYTES = D * VT_LD * ESZ;
   constexpr int SB_BYTES = D * SB_LD * ESZ;
@@ -389,7 +394,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
         float kx[VEC], kh[VEC];
         Io<IT>::unpack(pk[n], kx);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) kh[e] = kx[e] * __expf((t >= 32 ? c32[e] : 0.f) - bx[n][e]);
+        for (int e = 0; e < VEC; ++e) kh[e] = RAW ? kx[e] : kx[e] * __expf((t >= 32 ? c32[e] : 0.f) - bx[n][e]);
         u32x4_t hi, lo;
         split8(kh, hi, lo);
         st16(Kh + kn_at(t, cb * VEC), hi);
@@ -404,6 +409,11 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   // offsets pass through an empty asm so that each use recomputes the factors
   // instead of the compiler keeping them live across heads.
   auto scaled = [&](const u32x4_t (&x)[NQ], u32x4_t (&hi)[NQ], u32x4_t (&lo)[LO ? NQ : 1], bool second) {
+    if constexpr (RAW) {
+#pragma unroll
+      for (int m = 0; m < NQ; ++m) hi[m] = x[m];
+      return;
+    }
     int rt_off = tq * BC_LD, r31_off = 31 * BC_LD;
     asm volatile("" : "+v"(rt_off), "+v"(r31_off));
 #pragma unroll
@@ -435,6 +445,19 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   // rows, element q of tile t at key key_of(t, q); fp32: 16-key tiles)
   auto key_of = [&](int t, int q) {
     return ESZ == 2 ? 32 * (t >> 1) + 8 * lg + 4 * (t & 1) + q : 16 * t + 4 * lg + q;
+  };
+  // RAW with a per-head decay: element q of tile t times exp(b_row - b_key),
+  // selected to 0 where key > row (or key >= row when strict), never
+  // multiplied there (the factor may overflow past the diagonal)
+  auto decay_tile = [&](f32x4_t at, int t, int row, bool strict) {
+    const float br = Bt[kChunk + row];
+    const f32x4_t bk = *(const f32x4_t*)(Bt + kChunk + key_of(t, 0));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int key = key_of(t, q);
+      at[q] = (strict ? key < row : key <= row) ? at[q] * __expf(br - bk[q]) : 0.f;
+    }
+    return at;
   };
   // unmasked tile t of (k^ rows) x (the lane's scaled row): Kh xh + Kl xh + Kh xl
   auto k_tile = [&](int t, const u32x4_t (&xh)[NQ], const u32x4_t (&xl)[LO ? NQ : 1]) {
@@ -530,6 +553,12 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = v4[q];
       }
+      if constexpr (RAWDEC) {
+        // Kbar S_0 from the raw keys: row t times exp(b_t)
+        const f32x4_t b4 = *(const f32x4_t*)(Bt + kChunk + r0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) val[i][q] *= __expf(b4[q]);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) val[i][q] = bet4[q] * (v[q] - val[i][q]);
     }
@@ -548,6 +577,10 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
           if (32 * p <= 16 * wr + 15) {
             f32x4_t at0 = p == 0 ? k_tile(0, k0h, k0l) : k_tile(2, k1h, k1l);
             f32x4_t at1 = p == 0 ? k_tile(1, k0h, k0l) : k_tile(3, k1h, k1l);
+            if constexpr (RAWDEC) {
+              at0 = decay_tile(at0, 2 * p, tq, true);
+              at1 = decay_tile(at1, 2 * p + 1, tq, true);
+            }
             // the diagonal block's keys 16wr + 8(lg & 1) + 4odd + q sit in
             // lane groups 2(wr & 1) and 2(wr & 1) + 1 of pair wr / 2
             if (p == (wr >> 1) && (lg >> 1) == (wr & 1)) {
@@ -702,6 +735,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
       scaled(qr, qop, qlo, false);
       auto a_tile = [&](int t) {
         f32x4_t at = k_tile(t, qop, qlo);
+        if constexpr (RAWDEC) return decay_tile(at, t, tq, false);
 #pragma unroll
         for (int q = 0; q < 4; ++q) at[q] = key_of(t, q) <= tq ? at[q] : 0.f;
         return at;
@@ -723,13 +757,19 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
           if constexpr (SLO) O::mma(nacc[ct], ld16(Sl + so), qop[m]);
         }
       }
+      if constexpr (RAWDEC) {
+        // q S_0 from the raw query: times exp(b_t) of the lane's token
+        const float eb = __expf(Bt[kChunk + tq]);
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct) nacc[ct] *= eb;
+      }
       if constexpr (ESZ == 2) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           if (need(2 * p)) {
             f32x4_t at0 = a0[0], at1 = a0[1];
             if (p == 1) {
-              scaled(qr, qop, qlo, true);
+              if constexpr (!RAW) scaled(qr, qop, qlo, true);
               at0 = a_tile(2);
               at1 = a_tile(3);
             }
@@ -801,7 +841,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
               const int off = kn_at(sk, dk);
               float kv = to_f(Kh[off]);
               if constexpr (XLO) kv += to_f(Kl[off]);
-              f[e] = DK == 0 ? kv : kv * __expf(bC - (sk >= 32 ? c31 : 0.f));
+              f[e] = DK == 0 ? kv : kv * __expf(bC - (RAW ? Bt[kChunk + sk] : (sk >= 32 ? c31 : 0.f)));
             }
             split8(f, kop[m], kol[m]);
           }
