@@ -64,12 +64,14 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   constexpr int SB_LD = D + PADE;
   constexpr int BC_LD = D + 4;
   constexpr bool LO = ESZ == 2;   // 16-bit: hi + lo operands (k^, q^, U, L, A)
-  // RAW: bf16 inputs without a per-dim decay.  q and k then enter the MFMAs as
-  // they are (exact), and a per-head decay is applied in fp32 after each
-  // product: exp(b_t - b_j) per element of A and L, exp(b_t) per row of the
-  // inter term and of Kbar S_0, as in the per-head gated kernel.  Otherwise the
-  // scaled rows q^, kbar and the keys k^ are formed first and carry a lo part.
-  constexpr bool RAW = LO && DK <= 1 && std::is_same_v<IT, uint16_t>;
+  // RAW: bf16 or fp32 inputs without a per-dim decay.  q and k then enter the
+  // MFMAs as they are (exact), and a per-head decay is applied in fp32 after
+  // each product: exp(b_t - b_j) per element of A and L, exp(b_t) per row of
+  // the inter term and of Kbar S_0, as in the per-head gated kernel; no factor
+  // exceeds 1 for decays <= 0.  Otherwise (fp16 inputs, per-dim decays) the
+  // scaled rows q^, kbar and the keys k^ are formed first relative to 32-token
+  // blocks, and carry a lo part.
+  constexpr bool RAW = DK <= 1 && (std::is_same_v<IT, uint16_t> || std::is_same_v<IT, float>);
   constexpr bool XLO = LO && !RAW;
   constexpr bool RAWDEC = RAW && DK == 1;  // RAW with factors to apply
   constexpr int KN_BYTES = kChunk * KN_LD * ESZ;
@@ -604,7 +606,8 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           if (t <= wr) {
-            const f32x4_t at = t < 2 ? k_tile(t, k0h, k0l) : k_tile(t, k1h, k1l);
+            f32x4_t at = t < 2 ? k_tile(t, k0h, k0l) : k_tile(t, k1h, k1l);
+            if constexpr (RAWDEC) at = decay_tile(at, t, tq, true);
             if (t == wr) {
               f32x4_t x = at;
 #pragma unroll
@@ -788,7 +791,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
           if (need(jt)) {
-            if (jt == 2) scaled(qr, qop, qlo, true);
+            if (!RAW && jt == 2) scaled(qr, qop, qlo, true);
             const f32x4_t at = jt < 2 ? a0[jt] : a_tile(jt);
 #pragma unroll
             for (int ct = 0; ct < NDT; ++ct) {

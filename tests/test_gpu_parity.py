@@ -471,6 +471,50 @@ def test_delta_small(dtype, D, G, kind):
     assert_close(present, po, TOL[dtype], "present_state")
 
 
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
+@pytest.mark.parametrize("G", [1, 4])
+def test_delta_strong_head_decay(dtype, G):
+    """Per-head decays of about -20 per token: every decay factor past the
+    diagonal would overflow, and the state forgets within a few tokens.  fp32
+    and bf16 inputs apply the factors after the products and take any
+    strength; fp16 inputs rescale the keys per 32-token block and get about
+    -1.3 per token, inside that range."""
+    B, T, Hkv, D = 1, 200, 2, 64
+    Hq = Hkv * G
+    seed = 6500 + G
+    q = synth.normal((B, T, Hq * D), 1.0, dtype, DEV, seed, "q")
+    k = synth.l2_normalized((B, T, Hkv, D), dtype, DEV, seed, "k").reshape(B, T, Hkv * D)
+    v = synth.normal((B, T, Hkv * D), 1.0, dtype, DEV, seed, "v")
+    beta = _beta((B, T, Hkv), dtype, seed)
+    g = synth.logsigmoid_decay((B, T, Hkv), dtype, DEV, seed, mean=-1.0 if dtype == torch.float16 else -20.0)
+    past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, seed, "past")
+    out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=past)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(present).all()
+    oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "gated_delta", past_state=f64(past),
+                          decay=f64(g), beta=f64(beta))
+    assert_close(out, oo, TOL[dtype], "out")
+    assert_close(present, po, TOL[dtype], "present_state")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
+def test_gated_strong_head_decay(dtype):
+    """The per-head gated recurrence with decays of about -20 per token: its
+    factors are all exp(later - earlier) <= 1, so no strength overflows."""
+    B, T, Hkv, G, D = 2, 300, 2, 2, 64
+    Hq = Hkv * G
+    q = synth.normal((B, T, Hq * D), 1.0, dtype, DEV, 6600, "q")
+    k = synth.l2_normalized((B, T, Hkv, D), dtype, DEV, 6600, "k").reshape(B, T, Hkv * D)
+    v = synth.normal((B, T, Hkv * D), 1.0, dtype, DEV, 6600, "v")
+    g = synth.logsigmoid_decay((B, T, Hkv), dtype, DEV, 6600, mean=-20.0)
+    out, present = la.la_gated_forward(q, k, v, Hq, Hkv, decay=g)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(present).all()
+    oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "gated", decay=f64(g))
+    assert_close(out, oo, TOL[dtype], "out")
+    assert_close(present, po, TOL[dtype], "present_state")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 def test_delta_shared_beta_long(dtype):
     """beta (B,T,1) shared by the kv heads, several chunks, no past state."""
