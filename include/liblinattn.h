@@ -172,7 +172,10 @@ la_status la_gated_step(const void* q, const void* k, const void* v, const void*
  * L2-normalised (operator page, "Inputs").  Evaluated chunk-parallel (64-token
  * chunks, a 64 x 64 triangular solve per chunk) by one workgroup per (batch,
  * kv head) over the whole sequence; no workspace.  The per-dim decay range of
- * la_gated_forward applies; fp32 inputs at Dk = 128 return LA_ERR_UNSUPPORTED. */
+ * la_gated_forward applies to per-dim decays, and with fp16 inputs also to
+ * per-head decays (keys rescaled per 32-token block: decays summing below
+ * about -87 over one block overflow); bf16 and fp32 inputs take per-head
+ * decays of any strength.  fp32 inputs at Dk = 128 return LA_ERR_UNSUPPORTED. */
 la_status la_delta_forward(const void* q, const void* k, const void* v, const void* decay,
                            int32_t per_dim_decay, const void* beta, int32_t beta_per_head,
                            const float* past_state, float* present_state, void* out, int64_t B,
