@@ -175,7 +175,10 @@ la_status la_gated_step(const void* q, const void* k, const void* v, const void*
  * la_gated_forward applies to per-dim decays, and with fp16 inputs also to
  * per-head decays (keys rescaled per 32-token block: decays summing below
  * about -87 over one block overflow); bf16 and fp32 inputs take per-head
- * decays of any strength.  fp32 inputs at Dk = 128 return LA_ERR_UNSUPPORTED. */
+ * decays of any strength.  fp32 inputs at Dk = 128 with T > 1 return
+ * LA_ERR_UNSUPPORTED.  T == 1 runs a streaming step instead: one read and one
+ * write of the state per (batch, kv head), in place allowed (present_state ==
+ * past_state), no decay range limit, every dtype and head size. */
 la_status la_delta_forward(const void* q, const void* k, const void* v, const void* decay,
                            int32_t per_dim_decay, const void* beta, int32_t beta_per_head,
                            const float* past_state, float* present_state, void* out, int64_t B,

@@ -466,6 +466,7 @@ hipError_t launch_step(const void* q, const void* k, const void* v, const void* 
                        const float* past_state, float* present_state, void* out, int64_t U,
                        int64_t Hkv, int64_t D, int64_t G, int32_t dtype, float scale, hipStream_t st) {
   la::GatedStepArgs a;
+  memset(&a, 0, sizeof(a));
   a.q = q;
   a.k = k;
   a.v = v;
@@ -647,8 +648,8 @@ LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v
   const int64_t D = Dk, U = B * Hkv, G = Hq / Hkv;
   const int64_t esz = dtype_size(dtype);
   const bool per_dim = per_dim_decay != 0 && decay != nullptr;
-  if (dtype == LA_DT_F32 && D == 128 && T > 0)
-    return fail(LA_ERR_UNSUPPORTED, "delta rules with fp32 inputs at head size 128");
+  if (dtype == LA_DT_F32 && D == 128 && T > 1)
+    return fail(LA_ERR_UNSUPPORTED, "delta rules with fp32 inputs at head size 128 (T > 1)");
   if (U > 0 && !present_state) return fail(LA_ERR_NULL_ARG, "present_state is required");
   const bool work = U > 0 && T > 0;
   if (work && (!q || !k || !v || !out || !beta))
@@ -678,6 +679,26 @@ LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v
                             : hipSuccess)
                      : la::launch_fill_zero(present_state, U * D * D, st);
     return device_status(e, "la_delta_forward");
+  }
+  if (T == 1) {
+    // one token: the streaming step (one read and one write of the state)
+    la::GatedStepArgs g;
+    memset(&g, 0, sizeof(g));
+    g.q = q;
+    g.k = k;
+    g.v = v;
+    g.decay = decay;
+    g.s_in = past_state;
+    g.s_out = present_state;
+    g.out = out;
+    g.Hkv = (int32_t)Hkv;
+    g.units = (int32_t)U;
+    g.per_dim = per_dim ? 1 : 0;
+    g.scale = scale;
+    g.beta = beta;
+    g.beta_heads = (int32_t)bh;
+    e = la::launch_delta_step(dtype, (int)D, (int)G, g, st);
+    return device_status(e, "la_delta_forward (T = 1)");
   }
   la::DeltaArgs a;
   a.q = q;

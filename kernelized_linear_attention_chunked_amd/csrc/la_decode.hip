@@ -230,6 +230,138 @@ __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArg
   }
 }
 
+// T == 1 step of the delta rules (the LinearAttention operator page, update
+// rules "delta" and "gated_delta", one token): per (b, kv head j)
+//   S' = E S,  u = beta (v - S'^T k),  S'' = S' + k u^T,  o_h = scale q_h^T S''
+// with E = I, exp(g) or diag(exp(g)) (DK 0, 1, 2).  The gated step's layout:
+// a thread owns RPT rows of four consecutive state columns and keeps them in
+// registers throughout.  Two sums over the rows go through LDS in turn: S'^T k
+// (then u, one value per column), and after the rank-1 update q_h^T S''.  One
+// read and one write of the state, as for the gated step.
+template <typename DT, int D, int G, bool NTMP, int DK>
+__global__ __launch_bounds__(kDecodeThreads) void delta_step_kernel(GatedStepArgs a) {
+  constexpr int C4 = D / 4;          // float4 columns per state row
+  constexpr int RG = kThreads / C4;  // row groups
+  constexpr int RPT = D / RG;        // rows per thread
+  static_assert(RPT >= 1 && RG * RPT == D && C4 <= 32, "unsupported head size");
+  __shared__ float fk[kDecodeUnits][D], fq[kDecodeUnits][G][D], fe[kDecodeUnits][DK == 2 ? D : 1];
+  __shared__ float fu[kDecodeUnits][D];
+  __shared__ float part[kDecodeUnits][G][RG][D];
+
+  const int ul = threadIdx.x / kThreads;  // unit slot in the workgroup
+  const int tid = threadIdx.x % kThreads;
+  const int u = blockIdx.x * kDecodeUnits + ul;
+  const bool live = u < a.units;  // the last workgroup may hold one unit only
+  const int b = u / a.Hkv, j = u % a.Hkv;
+  const int c4 = tid % C4, rg = tid / C4;
+  const int64_t SE = (int64_t)D * D;
+
+  f32x4_t sv[RPT];
+  if (live && a.s_in) {
+    const float* S = a.s_in + (int64_t)u * SE;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const f32x4_t* p = (const f32x4_t*)(S + (rg + RG * r) * D + 4 * c4);
+      sv[r] = NTMP ? __builtin_nontemporal_load(p) : *p;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) sv[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int QW = a.Hkv * G * D;  // query row width
+  const DT* qp = (const DT*)a.q + (int64_t)b * QW + (int64_t)j * G * D;
+  const DT* kp = (const DT*)a.k + (int64_t)u * D;
+  const DT* vp = (const DT*)a.v + (int64_t)u * D;
+  const float e = (live && DK == 1) ? __expf(load_elem<DT>((const DT*)a.decay, u)) : 1.f;
+  const float be = live ? load_elem<DT>((const DT*)a.beta, b * a.beta_heads + (a.beta_heads > 1 ? j : 0)) : 0.f;
+  const float vc = (live && tid < D) ? load_elem<DT>(vp, tid) : 0.f;  // v of column tid
+  if (live) {
+    for (int i = tid; i < D; i += kThreads) fk[ul][i] = load_elem<DT>(kp, i);
+    if constexpr (DK == 2)  // per-key-dim decay: row dk of S scales by exp(g[dk])
+      for (int i = tid; i < D; i += kThreads) fe[ul][i] = __expf(load_elem<DT>((const DT*)a.decay + (int64_t)u * D, i));
+    for (int i = tid; i < G * D; i += kThreads) fq[ul][i / D][i % D] = load_elem<DT>(qp, i);
+  }
+  __syncthreads();
+  // S' = E S, and the thread's part of S'^T k
+  if (live) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int dk = rg + RG * r;
+      const float er = DK == 2 ? fe[ul][dk] : e;
+      const float f = fk[ul][dk];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[r][i] *= er;
+        acc[i] = fmaf(f, sv[r][i], acc[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[ul][0][rg][4 * c4 + i] = acc[i];
+  }
+  __syncthreads();
+  // u = beta (v - S'^T k), one column per thread
+  if (live && tid < D) {
+    float w = 0.f;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) w += part[ul][0][g][tid];
+    fu[ul][tid] = be * (vc - w);
+  }
+  __syncthreads();
+  // S'' = S' + k u^T, written back; the threads' parts of q_h^T S''
+  if (live) {
+    float u4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u4[i] = fu[ul][4 * c4 + i];
+    float acc[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[h][i] = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int dk = rg + RG * r;
+      const float f = fk[ul][dk];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[r][i] = fmaf(f, u4[i], sv[r][i]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float g = fq[ul][h][dk];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[h][i] = fmaf(g, sv[r][i], acc[h][i]);
+      }
+    }
+    float* So = a.s_out + (int64_t)u * SE;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      f32x4_t* p = (f32x4_t*)(So + (rg + RG * r) * D + 4 * c4);
+      if constexpr (NTMP)
+        __builtin_nontemporal_store(sv[r], p);
+      else
+        *p = sv[r];
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[ul][h][rg][4 * c4 + i] = acc[h][i];
+  }
+  __syncthreads();
+  if (live) {
+    DT* op = (DT*)a.out + (int64_t)b * QW + (int64_t)j * G * D;
+    for (int i = tid; i < G * D; i += kThreads) {
+      const int h = i / D, d = i % D;
+      float y = 0.f;
+#pragma unroll
+      for (int g = 0; g < RG; ++g) y += part[ul][h][g][d];
+      y *= a.scale;
+      if constexpr (std::is_same_v<DT, uint16_t>)
+        op[i] = (uint16_t)f32_to_bf16_bits(y);
+      else
+        op[i] = (DT)y;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * kThreads)
@@ -327,6 +459,55 @@ hipError_t launch_gated_step(int io, int D, int G, const GatedStepArgs& a, hipSt
     case kIoBF16: launch_gs_d<uint16_t>(D, G, a, st); break;
     case kIoF16: launch_gs_d<f16_t>(D, G, a, st); break;
     default: launch_gs_d<float>(D, G, a, st); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename DT, int D, int G, int DK>
+static void launch_dsp(const GatedStepArgs& a, hipStream_t st) {
+  const bool ntmp = (int64_t)a.units * D * D * 4 >= ((int64_t)256 << 20);
+  const int grid = (a.units + kDecodeUnits - 1) / kDecodeUnits;
+  if (ntmp)
+    hipLaunchKernelGGL((delta_step_kernel<DT, D, G, true, DK>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((delta_step_kernel<DT, D, G, false, DK>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+}
+
+template <typename DT, int D, int G>
+static void launch_ds(const GatedStepArgs& a, hipStream_t st) {
+  if (!a.decay)
+    launch_dsp<DT, D, G, 0>(a, st);
+  else if (a.per_dim)
+    launch_dsp<DT, D, G, 2>(a, st);
+  else
+    launch_dsp<DT, D, G, 1>(a, st);
+}
+
+template <typename DT, int D>
+static void launch_ds_g(int G, const GatedStepArgs& a, hipStream_t st) {
+  switch (G) {
+    case 1: launch_ds<DT, D, 1>(a, st); break;
+    case 2: launch_ds<DT, D, 2>(a, st); break;
+    case 4: launch_ds<DT, D, 4>(a, st); break;
+    default: launch_ds<DT, D, 8>(a, st); break;
+  }
+}
+
+template <typename DT>
+static void launch_ds_d(int D, int G, const GatedStepArgs& a, hipStream_t st) {
+  switch (D) {
+    case 32: launch_ds_g<DT, 32>(G, a, st); break;
+    case 64: launch_ds_g<DT, 64>(G, a, st); break;
+    default: launch_ds_g<DT, 128>(G, a, st); break;
+  }
+}
+
+hipError_t launch_delta_step(int io, int D, int G, const GatedStepArgs& a, hipStream_t st) {
+  if (a.units <= 0) return hipSuccess;
+  switch (io) {
+    case kIoBF16: launch_ds_d<uint16_t>(D, G, a, st); break;
+    case kIoF16: launch_ds_d<f16_t>(D, G, a, st); break;
+    default: launch_ds_d<float>(D, G, a, st); break;
   }
   return hipGetLastError();
 }

@@ -176,8 +176,14 @@ struct GatedStepArgs {
   int32_t units;  // B*Hkv
   int32_t per_dim;
   float scale;
+  // delta rules only: beta (B, beta_heads), beta_heads = Hkv or 1 (shared)
+  const void* beta;
+  int32_t beta_heads;
 };
 hipError_t launch_gated_step(int io, int D, int G, const GatedStepArgs& a, hipStream_t st);
+// T == 1 step of the delta rules (la_decode.hip): decay null ("delta"), per kv
+// head, or per key dim (per_dim)
+hipError_t launch_delta_step(int io, int D, int G, const GatedStepArgs& a, hipStream_t st);
 hipError_t launch_gated_prefix(float* ws_s, const float* ws_a, const float* s_in, int U, int nseg,
                                int D, int per_dim, hipStream_t st);
 // Per-key-dim decay (la_gated_pd.hip): the same arguments and modes as

@@ -472,6 +472,74 @@ def test_delta_small(dtype, D, G, kind):
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("G", [1, 2, 8])
+@pytest.mark.parametrize("kind", ["delta", "gated_head", "gated_dim"])
+def test_delta_step(dtype, D, G, kind):
+    """T = 1 runs the streaming step kernel (fp32 at head size 128 included):
+    one token against the oracle; the per-head case runs in place and the
+    plain delta rule with beta shared by the kv heads."""
+    B, Hkv = 3, 2
+    Hq = Hkv * G
+    seed = 7000 + D + G + 7 * len(kind)
+    q = synth.normal((B, 1, Hq * D), 1.0, dtype, DEV, seed, "q")
+    k = synth.l2_normalized((B, 1, Hkv, D), dtype, DEV, seed, "k").reshape(B, 1, Hkv * D)
+    v = synth.normal((B, 1, Hkv * D), 1.0, dtype, DEV, seed, "v")
+    beta = _beta((B, 1, 1 if kind == "delta" else Hkv), dtype, seed)
+    g = None
+    if kind == "gated_head":
+        g = synth.logsigmoid_decay((B, 1, Hkv), dtype, DEV, seed, mean=1.0)
+    elif kind == "gated_dim":
+        g = synth.logsigmoid_decay((B, 1, Hkv * D), dtype, DEV, seed, mean=1.0)
+    past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, seed, "past")
+    ref_past = f64(past)
+    if kind == "gated_head":
+        state = past.clone()
+        out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=state,
+                                           present_state=state)
+        assert present.data_ptr() == state.data_ptr()
+    else:
+        out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=past)
+    torch.cuda.synchronize()
+    oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "delta" if g is None else "gated_delta",
+                          past_state=ref_past, decay=None if g is None else f64(g), beta=f64(beta))
+    assert_close(out, oo, TOL[dtype], "out")
+    assert_close(present, po, TOL[dtype], "present_state")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
+@pytest.mark.parametrize("kind", ["delta", "gated_head", "gated_dim"])
+def test_delta_prefill_then_steps(dtype, kind):
+    """A 100-token call followed by 20 T = 1 steps, each from the state the last
+    call returned, against the oracle over the whole 120 tokens."""
+    B, T0, T1, Hkv, G, D = 2, 100, 20, 2, 2, 64
+    Hq, T = Hkv * G, T0 + T1
+    seed = 7300 + len(kind)
+    q = synth.normal((B, T, Hq * D), 1.0, dtype, DEV, seed, "q")
+    k = synth.l2_normalized((B, T, Hkv, D), dtype, DEV, seed, "k").reshape(B, T, Hkv * D)
+    v = synth.normal((B, T, Hkv * D), 1.0, dtype, DEV, seed, "v")
+    beta = _beta((B, T, Hkv), dtype, seed)
+    g = None
+    if kind == "gated_head":
+        g = synth.logsigmoid_decay((B, T, Hkv), dtype, DEV, seed, mean=1.0)
+    elif kind == "gated_dim":
+        g = synth.logsigmoid_decay((B, T, Hkv * D), dtype, DEV, seed, mean=1.0)
+    sl = lambda x, a, b: None if x is None else x[:, a:b].contiguous()
+    out0, state = la.la_delta_forward(sl(q, 0, T0), sl(k, 0, T0), sl(v, 0, T0), Hq, Hkv, sl(beta, 0, T0),
+                                      decay=sl(g, 0, T0))
+    outs = [out0]
+    for t in range(T0, T):
+        o, state = la.la_delta_forward(sl(q, t, t + 1), sl(k, t, t + 1), sl(v, t, t + 1), Hq, Hkv,
+                                       sl(beta, t, t + 1), decay=sl(g, t, t + 1), past_state=state)
+        outs.append(o)
+    torch.cuda.synchronize()
+    oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "delta" if g is None else "gated_delta",
+                          decay=None if g is None else f64(g), beta=f64(beta))
+    assert_close(torch.cat(outs, dim=1), oo, TOL[dtype], "out")
+    assert_close(state, po, TOL[dtype], "present_state")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("G", [1, 4])
 def test_delta_strong_head_decay(dtype, G):
     """Per-head decays of about -20 per token: every decay factor past the
@@ -491,6 +559,28 @@ def test_delta_strong_head_decay(dtype, G):
     out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=past)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all() and torch.isfinite(present).all()
+    oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "gated_delta", past_state=f64(past),
+                          decay=f64(g), beta=f64(beta))
+    assert_close(out, oo, TOL[dtype], "out")
+    assert_close(present, po, TOL[dtype], "present_state")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
+@pytest.mark.parametrize("kind", ["gated_head", "gated_dim"])
+def test_delta_step_strong_decay(dtype, kind):
+    """The T = 1 step takes decays of any strength (about -20 here), per head
+    or per key dim, for every dtype."""
+    B, Hkv, G, D = 2, 2, 4, 64
+    Hq = Hkv * G
+    q = synth.normal((B, 1, Hq * D), 1.0, dtype, DEV, 7400, "q")
+    k = synth.l2_normalized((B, 1, Hkv, D), dtype, DEV, 7400, "k").reshape(B, 1, Hkv * D)
+    v = synth.normal((B, 1, Hkv * D), 1.0, dtype, DEV, 7400, "v")
+    beta = _beta((B, 1, Hkv), dtype, 7400)
+    gshape = (B, 1, Hkv) if kind == "gated_head" else (B, 1, Hkv * D)
+    g = synth.logsigmoid_decay(gshape, dtype, DEV, 7400, mean=-20.0)
+    past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, 7400, "past")
+    out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=past)
+    torch.cuda.synchronize()
     oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "gated_delta", past_state=f64(past),
                           decay=f64(g), beta=f64(beta))
     assert_close(out, oo, TOL[dtype], "out")
