@@ -253,6 +253,12 @@ def bench_other(args, log):
         U = d.B * d.Hkv
         nbytes = d.T * (U * D * D * 4 * 2 + d.B * (d.Hq * D * 2 * 2 + d.Hkv * D * 2 * 2 + d.Hkv * 2))
         flops = d.T * (U * D * D * 3 + d.B * d.Hq * D * D * 2)  # update (3/elem), readout
+    elif args.workload == "delta_step_d128":
+        # the gated step's bytes plus beta; per state element: decay, S'^T k, the
+        # rank-1 update (1 + 2 + 2 flops), plus the readout
+        U = d.B * d.Hkv
+        nbytes = d.T * (U * D * D * 4 * 2 + d.B * (d.Hq * D * 2 * 2 + d.Hkv * D * 2 * 2 + d.Hkv * 2 * 2))
+        flops = d.T * (U * D * D * 5 + d.B * d.Hq * D * D * 2)
     elif args.workload == "gated_delta_d128":
         # q, k, v, out, decay and beta once; the final state written
         nbytes = Tt * (d.Hq * D * 2 * 2 + d.Hkv * D * 2 * 2 + d.Hkv * 2 * 2) + d.B * d.Hkv * D * D * 4
@@ -304,7 +310,7 @@ def main():
     ap.add_argument("--workload", default="streaming_d128",
                     choices=["streaming_d128", "causal_bf16_d64", "noncausal_relu_d128",
                              "gated_gqa_d128", "gated_perdim_d128", "gated_delta_d128",
-                             "backward_bf16_d64", "gated_step_d128"])
+                             "backward_bf16_d64", "gated_step_d128", "delta_step_d128"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

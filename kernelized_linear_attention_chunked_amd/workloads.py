@@ -299,5 +299,25 @@ class GatedStepD128:
             self.decode_call(t)
 
 
+class DeltaStepD128(GatedStepD128):
+    """Gated delta decode: the shapes of gated_step_d128, beta per kv head, 64
+    one-token steps per step() updating the fp32 state in place."""
+
+    name = "delta_step_d128"
+
+    def __init__(self, device="cuda:0"):
+        super().__init__(device)
+        inp = synth.workload(self.name, device)
+        self.beta = inp["beta"].transpose(0, 1).contiguous()
+
+    def decode_call(self, t, stream=None):
+        _check(self.lib.la_delta_forward(_p(self.q[t]), _p(self.k[t]), _p(self.v[t]), _p(self.g[t]), 0,
+                                         _p(self.beta[t]), 1, _p(self.state), _p(self.state),
+                                         _p(self.out[t]), self.B, 1, self.Hq, self.Hkv, self.D, self.D,
+                                         1, self.scale, _stream(self.device) if stream is None else stream),
+               "la_delta_forward")
+
+
 DRIVERS = {c.name: c for c in (StreamingD128, CausalBf16D64, NonCausalReluD128, GatedGqaD128,
-                               GatedPerdimD128, GatedDeltaD128, BackwardBf16D64, GatedStepD128)}
+                               GatedPerdimD128, GatedDeltaD128, BackwardBf16D64, GatedStepD128,
+                               DeltaStepD128)}

@@ -157,6 +157,30 @@ def test_gated_step_d128_full():
         print("unit", (b, j), "out %.2e state %.2e" % (e1, e2))
 
 
+def test_delta_step_d128_full():
+    """The gated delta decode workload: 64 one-token steps of B=256 sequences,
+    in place, beta per kv head.  Sampled (batch, kv head) units are checked
+    against one oracle run over the 64 tokens from the same past state."""
+    d = workloads.DeltaStepD128(DEV)
+    G, D = d.Hq // d.Hkv, d.D
+    past = d.state.clone()
+    print("workload delta_step_d128", (d.B, d.T, d.Hq * D), "state", tuple(d.state.shape), flush=True)
+    d.step()
+    torch.cuda.synchronize()
+    assert torch.isfinite(d.out.float()).all() and torch.isfinite(d.state).all()
+    for b, j in _units(d.B, d.Hkv, 6, 6):
+        qs = d.q[:, b:b + 1, j * G * D:(j + 1) * G * D].transpose(0, 1)
+        ks = d.k[:, b:b + 1, j * D:(j + 1) * D].transpose(0, 1)
+        vs = d.v[:, b:b + 1, j * D:(j + 1) * D].transpose(0, 1)
+        gs = d.g[:, b:b + 1, j:j + 1].transpose(0, 1)
+        bs = d.beta[:, b:b + 1, j:j + 1].transpose(0, 1)
+        oo, po = oracle.la_op(f64(qs), f64(ks), f64(vs), G, 1, "gated_delta", decay=f64(gs), beta=f64(bs),
+                              past_state=f64(past[b:b + 1, j:j + 1]), scale=d.scale)
+        out = d.out[:, b:b + 1, j * G * D:(j + 1) * G * D].transpose(0, 1)
+        e1 = assert_close(out, oo, 2e-2, "out %d,%d" % (b, j))
+        e2 = assert_close(d.state[b:b + 1, j:j + 1], po, 2e-2, "state %d,%d" % (b, j))
+        print("unit", (b, j), "out %.2e state %.2e" % (e1, e2))
+
 def test_gated_perdim_d128_full():
     """The per-key-dim decay at the GQA workload's sizes (split sequences):
     sampled (batch, kv head) units against the oracle over all 32768 tokens."""
