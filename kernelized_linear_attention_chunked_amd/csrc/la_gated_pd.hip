@@ -36,8 +36,16 @@ struct PdShape {
   static constexpr int HPW = G / P;         // query heads per wave
 };
 
+// The state pass (no outputs) of 16-bit inputs asks for two workgroups per CU
+// (at most 128 registers); it keeps no rescaled keys, so its LDS allows it.
+template <typename IT, int G, int MODE>
+struct PdOccupancy {
+  static constexpr int value =
+      (PdShape<G>::NW == 8 && MODE != kModeCausal && sizeof(typename Io<IT>::DT) == 2) ? 4 : 1;
+};
+
 template <typename IT, int D, int G, int MODE>
-__global__ __launch_bounds__(PdShape<G>::NTH) void gated_pd_kernel(GatedArgs a) {
+__global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value)) void gated_pd_kernel(GatedArgs a) {
   using DT = typename Io<IT>::DT;
   using O = Op<DT>;
   using SH = PdShape<G>;
@@ -63,7 +71,9 @@ __global__ __launch_bounds__(PdShape<G>::NTH) void gated_pd_kernel(GatedArgs a) 
   // registers, and A = Kh qh + Kl qh + Kh ql (the rescaled operands are not
   // inputs, so a single rounding of each would double the error of A)
   constexpr bool ALO = ESZ == 2;
-  constexpr int KL_BYTES = ALO ? KN_BYTES : 0;
+  // k^ feeds A only: the state pass keeps neither tile
+  constexpr int KH_BYTES = OUT ? KN_BYTES : 0;
+  constexpr int KL_BYTES = (ALO && OUT) ? KN_BYTES : 0;
   constexpr int VT_BYTES = D * VT_LD * ESZ;
   constexpr int VL_BYTES = VLO ? D * VT_LD * ESZ : 0;
   constexpr int SB_BYTES = OUT ? D * SB_LD * ESZ : 0;
@@ -75,26 +85,27 @@ __global__ __launch_bounds__(PdShape<G>::NTH) void gated_pd_kernel(GatedArgs a) 
   static_assert(ESZ == 4 || NTOK % 2 == 0, "bf16 V^T writes pack token pairs");
   static_assert(32 % TW == 0, "whole loader waves cover tokens 0..31");
   static_assert(LOADERS % 64 == 0, "whole loader waves");
-  static_assert(2 * KN_BYTES + KL_BYTES + VT_BYTES + VL_BYTES + SB_BYTES + BC_BYTES + WT_BYTES <= 160 * 1024,
+  constexpr int K2_BYTES = KN_BYTES + KH_BYTES;
+  static_assert(K2_BYTES + KL_BYTES + VT_BYTES + VL_BYTES + SB_BYTES + BC_BYTES + WT_BYTES <= 160 * 1024,
                 "LDS budget");
 
-  __shared__ __align__(16) unsigned char smem[2 * KN_BYTES + VT_BYTES + SB_BYTES + VL_BYTES + BC_BYTES +
+  __shared__ __align__(16) unsigned char smem[K2_BYTES + VT_BYTES + SB_BYTES + VL_BYTES + BC_BYTES +
                                               WT_BYTES + KL_BYTES + 16];
   DT* Kn = (DT*)smem;                   // k as loaded (operand type, or raw fp16)
-  DT* Kh = (DT*)(smem + KN_BYTES);      // k^ = k e^{c_sigma - b} (operand type)
-  DT* Vt = (DT*)(smem + 2 * KN_BYTES);
-  DT* Sb = (DT*)(smem + 2 * KN_BYTES + VT_BYTES);
-  DT* Vl = (DT*)(smem + 2 * KN_BYTES + VT_BYTES + SB_BYTES);
-  float* Bc = (float*)(smem + 2 * KN_BYTES + VT_BYTES + SB_BYTES + VL_BYTES);
-  float* Wt = (float*)(smem + 2 * KN_BYTES + VT_BYTES + SB_BYTES + VL_BYTES + BC_BYTES);
-  DT* Kl = (DT*)(smem + 2 * KN_BYTES + VT_BYTES + SB_BYTES + VL_BYTES + BC_BYTES + WT_BYTES);  // lo of k^
+  DT* Kh = (DT*)(smem + KN_BYTES);      // k^ = k e^{c_sigma - b} (operand type; outputs only)
+  DT* Vt = (DT*)(smem + K2_BYTES);
+  DT* Sb = (DT*)(smem + K2_BYTES + VT_BYTES);
+  DT* Vl = (DT*)(smem + K2_BYTES + VT_BYTES + SB_BYTES);
+  float* Bc = (float*)(smem + K2_BYTES + VT_BYTES + SB_BYTES + VL_BYTES);
+  float* Wt = (float*)(smem + K2_BYTES + VT_BYTES + SB_BYTES + VL_BYTES + BC_BYTES);
+  DT* Kl = (DT*)(smem + K2_BYTES + VT_BYTES + SB_BYTES + VL_BYTES + BC_BYTES + WT_BYTES);  // lo of k^
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // waves w and w + 4 share a SIMD: row blocks wr and 3 - wr even out the
   // causal work between SIMDs
   const int hp = w >> 2, wr = (w & 4) ? 3 - (w & 3) : (w & 3);
-  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+  int l = tid & 63, lr = l & 15, lg = l >> 4;
   const int u = blockIdx.x / a.seg_count;
   const int s = a.seg_first + blockIdx.x % a.seg_count;
   const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
@@ -288,7 +299,7 @@ __global__ __launch_bounds__(PdShape<G>::NTH) void gated_pd_kernel(GatedArgs a) 
           *(f32x4_t*)(Bc + t * BC_LD + cb * VEC + e) = f32x4_t{bx[n][e], bx[n][e + 1], bx[n][e + 2], bx[n][e + 3]};
       }
 #pragma unroll
-      for (int n = 0; n < NTOK; ++n) {
+      for (int n = 0; n < NTOK && OUT; ++n) {
         const int t = tg * NTOK + n;
         float kx[VEC];
         Io<IT>::unpack(pk[n], kx);
@@ -314,6 +325,14 @@ __global__ __launch_bounds__(PdShape<G>::NTH) void gated_pd_kernel(GatedArgs a) 
   float seg_log = 0.f;  // state mode: thread tid < D sums b_C of dim tid
 
   auto compute = [&](int c) {
+    if constexpr (!OUT) {
+      // the state pass re-derives its lane indices per chunk (opaque_lane):
+      // the addresses built from them are not held across the loop, which
+      // keeps it within two workgroups' registers
+      l = opaque_lane(tid);
+      lr = l & 15;
+      lg = l >> 4;
+    }
     const int tq = 16 * wr + lr;  // the lane's query row in the chunk
     if constexpr (OUT) {
       const int tok = c * kChunk + tq;
