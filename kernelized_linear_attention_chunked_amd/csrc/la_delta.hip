@@ -74,6 +74,8 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   constexpr bool RAW = DK <= 1 && (std::is_same_v<IT, uint16_t> || std::is_same_v<IT, float>);
   constexpr bool XLO = LO && !RAW;
   constexpr bool RAWDEC = RAW && DK == 1;  // RAW with factors to apply
+  // RAW bf16 with an even number of query heads per wave: outputs by head pairs
+  constexpr bool PAIR = RAW && ESZ == 2 && HPW % 2 == 0;
   constexpr int KN_BYTES = kChunk * KN_LD * ESZ;
   constexpr int VT_BYTES = D * VT_LD * ESZ;
   constexpr int SB_BYTES = D * SB_LD * ESZ;
@@ -655,6 +657,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     if constexpr (ESZ == 2) split4(t4, th, tl);
 
     load_q(c, 0);
+    if constexpr (PAIR) load_q(c, 1);
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       if (wr == blk) {
@@ -813,6 +816,87 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     }
   };
 
+  // ---- the same for RAW bf16 inputs with an even number of heads per wave:
+  // the heads go in pairs, and each S^T (hi, lo) and U^T (hi, lo) operand is
+  // read from LDS once for both heads of a pair
+  auto outputs_pair = [&](int c) {
+    const int tok = c * kChunk + tq;
+    auto need = [&](int t) { return 32 * (t >> 1) <= 16 * wr + 15; };
+#pragma unroll
+    for (int hh = 0; hh < HPW; hh += 2) {
+      refresh();
+      if (hh > 0) {
+        load_q(c, hh);
+        load_q(c, hh + 1);
+      }
+      const u32x4_t (&qa)[NQ] = qbuf[0];
+      const u32x4_t (&qb2)[NQ] = qbuf[1];
+      u32x4_t unused[LO ? NQ : 1];  // lo operands: never read on the RAW path
+      f32x4_t n0[NDT], n1[NDT];
+#pragma unroll
+      for (int ct = 0; ct < NDT; ++ct) {
+        n0[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        n1[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int m = 0; m < NQ; ++m) {
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct) {
+          const int so = sq_at(16 * ct + lr, KB * m + VEC * lg);
+          const u32x4_t av = ld16(Sb + so);
+          const u32x4_t al = ld16(Sl + so);
+          O::mma(n0[ct], av, qa[m]);
+          O::mma(n1[ct], av, qb2[m]);
+          O::mma(n0[ct], al, qa[m]);
+          O::mma(n1[ct], al, qb2[m]);
+        }
+      }
+      if constexpr (RAWDEC) {
+        const float eb = __expf(Bt[kChunk + tq]);
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct) {
+          n0[ct] *= eb;
+          n1[ct] *= eb;
+        }
+      }
+      auto a_tile = [&](int t, const u32x4_t (&x)[NQ]) {
+        f32x4_t at = k_tile(t, x, unused);
+        if constexpr (RAWDEC) return decay_tile(at, t, tq, false);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) at[q] = key_of(t, q) <= tq ? at[q] : 0.f;
+        return at;
+      };
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        if (need(2 * p)) {
+          u32x4_t bh0, bl0, bh1, bl1;
+          pair_operands(a_tile(2 * p, qa), a_tile(2 * p + 1, qa), bh0, bl0);
+          pair_operands(a_tile(2 * p, qb2), a_tile(2 * p + 1, qb2), bh1, bl1);
+#pragma unroll
+          for (int ct = 0; ct < NDT; ++ct) {
+            const u32x4_t uh = ld16(Vt + vt_at(16 * ct + lr, 4 * p + lg));
+            const u32x4_t ul = ld16(Vl + vt_at(16 * ct + lr, 4 * p + lg));
+            O::mma(n0[ct], uh, bh0);
+            O::mma(n1[ct], uh, bh1);
+            O::mma(n0[ct], uh, bl0);
+            O::mma(n1[ct], uh, bl1);
+            O::mma(n0[ct], ul, bh0);
+            O::mma(n1[ct], ul, bh1);
+          }
+        }
+      }
+      if (tok < T) {
+        IT* orow0 = ob + (int64_t)tok * QS + (hp + P * hh) * D + 4 * lg;
+        IT* orow1 = ob + (int64_t)tok * QS + (hp + P * (hh + 1)) * D + 4 * lg;
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct) {
+          store4(orow0 + 16 * ct, scale * n0[ct][0], scale * n0[ct][1], scale * n0[ct][2], scale * n0[ct][3]);
+          store4(orow1 + 16 * ct, scale * n1[ct][0], scale * n1[ct][1], scale * n1[ct][2], scale * n1[ct][3]);
+        }
+      }
+    }
+  };
+
   // ---- state: S = diag(e^{b_C}) S + sum_j diag(e^{b_C - b_j}) k_j u_j^T, the
   // decayed keys from k^ (hi + lo) times e^{b_C - c_sigma} in fp32, then hi + lo
   auto update = [&]() {
@@ -867,7 +951,10 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     stage(c);
     prefetch(min(c + 1, nchunks - 1));
     solve(c);
-    outputs(c);
+    if constexpr (PAIR)
+      outputs_pair(c);
+    else
+      outputs(c);
     update();
     __syncthreads();
     write_sb();
