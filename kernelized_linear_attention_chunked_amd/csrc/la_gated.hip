@@ -66,7 +66,9 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
   constexpr bool VLO = !std::is_same_v<IT, DT>;
   // lane indices re-derived per chunk and head where that removes spills:
   // elsewhere it measured slower
-  constexpr bool REFRESH = D >= 128 && (G == 8 || (VLO && G >= 2) || (ESZ == 4 && G >= 4));
+  // bf16 outputs with two heads per wave: by head pairs
+  constexpr bool PAIR = OUT && ESZ == 2 && !VLO && GatedShape<G>::HPW == 2;
+  constexpr bool REFRESH = PAIR || (D >= 128 && (G == 8 || (VLO && G >= 2) || (ESZ == 4 && G >= 4)));
   constexpr int KN_BYTES = kChunk * KN_LD * ESZ;
   constexpr int VT_BYTES = D * VT_LD * ESZ;
   constexpr int VL_BYTES = VLO ? D * VT_LD * ESZ : 0;
@@ -331,6 +333,120 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
           for (int q = 0; q < 4; ++q) fac[t][q] = fac_of(t, q);
       }
       const int tok = c * kChunk + 16 * wr + lr;
+      if constexpr (PAIR) {
+        // head pairs: each K, S^T and V^T operand is read from LDS once for
+        // both heads of a pair
+#pragma unroll
+        for (int hh = 0; hh < HPW; hh += 2) {
+          refresh();
+          u32x4_t qo0[NQ], qo1[NQ];
+          auto q_operands = [&](int h, u32x4_t (&qo)[NQ]) {
+            if constexpr (STAGE_IO) {
+#pragma unroll
+              for (int m = 0; m < NQ; ++m) {
+                const int g = 64 * m + l;
+                st16(io + sq_at(g / CB, (g % CB) * VEC), pq[h * NQ + m]);
+              }
+#pragma unroll
+              for (int m = 0; m < NQ; ++m) qo[m] = ld16(io + sq_at(lr, KB * m + VEC * lg));
+            } else {
+#pragma unroll
+              for (int m = 0; m < NQ; ++m) qo[m] = pq[h * NQ + m];
+            }
+          };
+          q_operands(hh, qo0);
+          q_operands(hh + 1, qo1);
+          f32x4_t n0[NDT], n1[NDT];
+#pragma unroll
+          for (int ct = 0; ct < NDT; ++ct) {
+            n0[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            n1[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int m = 0; m < NQ; ++m) {
+#pragma unroll
+            for (int ct = 0; ct < NDT; ++ct) {
+              const u32x4_t av = ld16(Sb + sq_at(16 * ct + lr, KB * m + VEC * lg));
+              O::mma(n0[ct], av, qo0[m]);
+              O::mma(n1[ct], av, qo1[m]);
+            }
+          }
+#pragma unroll
+          for (int ct = 0; ct < NDT; ++ct) {
+            n0[ct] *= ebi;
+            n1[ct] *= ebi;
+          }
+          // the decayed A^T tile t of both heads
+          auto a_tiles = [&](int t, f32x4_t& at0, f32x4_t& at1) {
+            at0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            at1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const int krow = 32 * (t >> 1) + 8 * (lr >> 2) + 4 * (t & 1) + (lr & 3);
+#pragma unroll
+            for (int m = 0; m < NQ; ++m) {
+              const u32x4_t kv = ld16(Kn + kn_at(krow, KB * m + VEC * lg));
+              O::mma(at0, kv, qo0[m]);
+              O::mma(at1, kv, qo1[m]);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              at0[q] *= fac[t][q];
+              at1[q] *= fac[t][q];
+            }
+          };
+          // bf16 hi + lo B operands of a tile pair
+          auto operands = [&](const f32x4_t& at0, const f32x4_t& at1, u32x4_t& bh, u32x4_t& bl) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const f32x4_t& at = (e >> 1) ? at1 : at0;
+              const float x0 = at[2 * (e & 1)], x1 = at[2 * (e & 1) + 1];
+              const uint32_t hw = pack_bf16x2(x0, x1);
+              bh[e] = hw;
+              bl[e] = pack_bf16x2(x0 - __uint_as_float(hw << 16), x1 - __uint_as_float(hw & 0xffff0000u));
+            }
+          };
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            if (need(2 * p)) {
+              f32x4_t e0, o0, e1, o1;  // tiles 2p (even) and 2p+1 (odd) of heads 0, 1
+              a_tiles(2 * p, e0, e1);
+              a_tiles(2 * p + 1, o0, o1);
+              u32x4_t bh0, bl0, bh1, bl1;
+              operands(e0, o0, bh0, bl0);
+              operands(e1, o1, bh1, bl1);
+#pragma unroll
+              for (int ct = 0; ct < NDT; ++ct) {
+                const u32x4_t av = ld16(Vt + vt_at(16 * ct + lr, 4 * p + lg));
+                O::mma(n0[ct], av, bh0);
+                O::mma(n1[ct], av, bh1);
+                O::mma(n0[ct], av, bl0);
+                O::mma(n1[ct], av, bl1);
+              }
+            }
+          }
+          auto put = [&](int h, const f32x4_t (&n)[NDT]) {
+            if constexpr (STAGE_IO) {
+#pragma unroll
+              for (int ct = 0; ct < NDT; ++ct)
+                store4((IT*)(io + sq_at(lr, 16 * ct + 4 * lg)), scale * n[ct][0], scale * n[ct][1],
+                       scale * n[ct][2], scale * n[ct][3]);
+#pragma unroll
+              for (int m = 0; m < NQ; ++m) {
+                const int g = 64 * m + l;
+                const int row = c * kChunk + 16 * wr + g / CB;
+                const u32x4_t v = ld16(io + sq_at(g / CB, (g % CB) * VEC));
+                if (row < T) st16(ob + (int64_t)row * QS + (hp + P * h) * D + (g % CB) * VEC, v);
+              }
+            } else if (tok < T) {
+              IT* orow = ob + (int64_t)tok * QS + (hp + P * h) * D + 4 * lg;
+#pragma unroll
+              for (int ct = 0; ct < NDT; ++ct)
+                store4(orow + 16 * ct, scale * n[ct][0], scale * n[ct][1], scale * n[ct][2], scale * n[ct][3]);
+            }
+          };
+          put(hh, n0);
+          put(hh + 1, n1);
+        }
+      } else {
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
         refresh();
@@ -448,6 +564,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
             store4(orow + 16 * ct, scale * nacc[ct][0], scale * nacc[ct][1], scale * nacc[ct][2],
                    scale * nacc[ct][3]);
         }
+      }
       }
     }
     // the heads are done with this chunk's queries: load the next chunk's (the
