@@ -28,7 +28,9 @@ constexpr int kApplyWaves = 8;
 constexpr int kApplyThreads = 64 * kApplyWaves;
 
 template <typename IT, int D, int FM, bool NORM, bool MASKED>
-__global__ __launch_bounds__(kApplyThreads, 4) void apply_kernel(ApplyArgs a) {
+// 16-bit operands: two workgroups per CU (at most 128 registers); fp32 S^T
+// tiles at head size 128 fit the LDS once
+__global__ __launch_bounds__(kApplyThreads, (sizeof(typename Io<IT>::DT) == 2 || D < 128) ? 4 : 1) void apply_kernel(ApplyArgs a) {
   using DT = typename Io<IT>::DT;  // operand type of the I/O type IT
   using O = Op<DT>;
   constexpr int VEC = O::VEC, KB = O::KB, ESZ = O::ESZ;

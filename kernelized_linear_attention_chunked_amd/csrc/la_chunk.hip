@@ -91,7 +91,13 @@ void chunk_kernel(ChunkArgs a) {
   // loads), except for fp32 at head size 128 where it would not fit: there each
   // wave loads its own query rows straight into operand registers.
   constexpr bool QS_STAGE = !(ESZ == 4 && D >= 128);
-  constexpr int KN_BYTES = USE_KV ? kChunk * KN_LD * ESZ : 0;
+  // 16-bit operands keep phi(K) transposed as well, [dk][token] like V^T, so
+  // that each state-update operand is one 16-byte read; the row-major phi(K)
+  // remains for the causal A^T tiles (and for the fp32 update; the causal
+  // kernel at smaller head sizes keeps its occupancy without it)
+  constexpr bool KT = USE_KV && ESZ == 2 && (D >= 128 || MODE == kState);
+  constexpr bool KN_ROWS = USE_KV && (MODE == kCausal || !KT);
+  constexpr int KN_BYTES = KN_ROWS ? kChunk * KN_LD * ESZ : 0;
   constexpr int QS_BYTES = (USE_Q && QS_STAGE) ? kChunk * KN_LD * ESZ : 0;
   constexpr int VT_BYTES = USE_KV ? NVT * 16 * VT_LD * ESZ : 0;
   constexpr int SB_BYTES = USE_SB ? NVT * 16 * SB_LD * ESZ : 0;
@@ -104,18 +110,20 @@ void chunk_kernel(ChunkArgs a) {
   // slower
   constexpr bool REFRESH = D >= 128 && (ESZ == 4 || VLO || MODE == kState);
   constexpr int VL_BYTES = (USE_KV && VLO) ? NDT * 16 * VT_LD * ESZ : 0;
+  constexpr int KT_BYTES = KT ? D * VT_LD * ESZ : 0;
   constexpr int NS = NDT * NVT;                    // 16x16 tiles of the (extended) state
   constexpr int TPW = (NS + NW - 1) / NW;          // state tiles per wave
   static_assert(NTOK >= 1 && NQ >= 1 && NDH * NH == NDT, "unsupported head size");
   static_assert(ESZ == 4 || NTOK % 2 == 0, "bf16 V^T writes pack token pairs");
   static_assert(SB_LD == KN_LD, "phi(Q) and S^T share one row layout");
 
-  __shared__ __align__(16) unsigned char smem[KN_BYTES + QS_BYTES + VT_BYTES + SB_BYTES + VL_BYTES + 16];
+  __shared__ __align__(16) unsigned char smem[KN_BYTES + QS_BYTES + VT_BYTES + SB_BYTES + VL_BYTES + KT_BYTES + 16];
   DT* Kn = (DT*)smem;
   DT* Qs = (DT*)(smem + KN_BYTES);
   DT* Vt = (DT*)(smem + KN_BYTES + QS_BYTES);
   DT* Sb = (DT*)(smem + KN_BYTES + QS_BYTES + VT_BYTES);
   DT* Vl = (DT*)(smem + KN_BYTES + QS_BYTES + VT_BYTES + SB_BYTES);
+  DT* Kt = (DT*)(smem + KN_BYTES + QS_BYTES + VT_BYTES + SB_BYTES + VL_BYTES);  // phi(K)^T (KT)
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -375,12 +383,15 @@ void chunk_kernel(ChunkArgs a) {
       for (int m = 0; m < NQ; ++m) qreg[m] = phi_vec(pq[m], qrow_ok, full);
     }
     if (!loader) return;
+    u32x4_t pkt[KT ? NTOK : 1];
 #pragma unroll
     for (int n = 0; n < NTOK; ++n) {
       const bool ok = FULL || ((valid >> n) & 1u);
       const int t = tg * NTOK + n;
       if constexpr (USE_KV) {
-        st16(Kn + kn_at(t, cb * VEC), phi_vec(pk[n], ok, full));
+        const u32x4_t fk = phi_vec(pk[n], ok, full);
+        if constexpr (KN_ROWS) st16(Kn + kn_at(t, cb * VEC), fk);
+        if constexpr (KT) pkt[n] = fk;
         if (!ok) pv[n] = u32x4_t{0u, 0u, 0u, 0u};
       }
       if constexpr (USE_Q && QS_STAGE) st16(Qs + sq_at(t, cb * VEC), phi_vec(pq[n], ok, full));
@@ -403,6 +414,7 @@ void chunk_kernel(ChunkArgs a) {
         write_vt(Vl, pl);
       }
       write_vt(Vt, pv);
+      if constexpr (KT) write_vt(Kt, pkt);
     }
   };
 
@@ -411,7 +423,9 @@ void chunk_kernel(ChunkArgs a) {
   // group lg carries tokens KB*m + VEC*lg + e), read column-wise from phi(K)
   auto load_kop = [&](u32x4_t& dst, int rt, int m) {
     const int t0 = KB * m + VEC * lg, col = 16 * rt + lr;
-    if constexpr (ESZ == 2) {
+    if constexpr (KT) {
+      dst = ld16(Kt + vt_at(col, (KB / VEC) * m + lg));  // one row of phi(K)^T
+    } else if constexpr (ESZ == 2) {
       const uint16_t* k16 = (const uint16_t*)Kn;
 #pragma unroll
       for (int e = 0; e < 4; ++e)

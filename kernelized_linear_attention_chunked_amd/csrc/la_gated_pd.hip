@@ -36,12 +36,12 @@ struct PdShape {
   static constexpr int HPW = G / P;         // query heads per wave
 };
 
-// The state pass (no outputs) of 16-bit inputs asks for two workgroups per CU
-// (at most 128 registers); it keeps no rescaled keys, so its LDS allows it.
+// The state pass (no outputs) of bf16 inputs asks for two workgroups per CU
+// (at most 128 registers); it keeps no rescaled keys, so its LDS allows it
+// (fp16 inputs add the V lo tile, which does not fit twice).
 template <typename IT, int G, int MODE>
 struct PdOccupancy {
-  static constexpr int value =
-      (PdShape<G>::NW == 8 && MODE != kModeCausal && sizeof(typename Io<IT>::DT) == 2) ? 4 : 1;
+  static constexpr int value = (PdShape<G>::NW == 8 && MODE != kModeCausal && std::is_same_v<IT, uint16_t>) ? 4 : 1;
 };
 
 template <typename IT, int D, int G, int MODE>
