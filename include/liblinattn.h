@@ -175,8 +175,8 @@ la_status la_gated_step(const void* q, const void* k, const void* v, const void*
  * la_gated_forward applies to per-dim decays, and with fp16 inputs also to
  * per-head decays (keys rescaled per 32-token block: decays summing below
  * about -87 over one block overflow); bf16 and fp32 inputs take per-head
- * decays of any strength.  fp32 inputs at Dk = 128 with T > 1 return
- * LA_ERR_UNSUPPORTED.  T == 1 runs a streaming step instead: one read and one
+ * decays of any strength.  fp32 inputs at Dk = 128 with a per-dim decay and
+ * T > 1 return LA_ERR_UNSUPPORTED.  T == 1 runs a streaming step instead: one read and one
  * write of the state per (batch, kv head), in place allowed (present_state ==
  * past_state), no decay range limit, every dtype and head size. */
 la_status la_delta_forward(const void* q, const void* k, const void* v, const void* decay,

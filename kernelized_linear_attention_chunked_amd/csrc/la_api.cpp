@@ -648,8 +648,8 @@ LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v
   const int64_t D = Dk, U = B * Hkv, G = Hq / Hkv;
   const int64_t esz = dtype_size(dtype);
   const bool per_dim = per_dim_decay != 0 && decay != nullptr;
-  if (dtype == LA_DT_F32 && D == 128 && T > 1)
-    return fail(LA_ERR_UNSUPPORTED, "delta rules with fp32 inputs at head size 128 (T > 1)");
+  if (per_dim && dtype == LA_DT_F32 && D == 128 && T > 1)
+    return fail(LA_ERR_UNSUPPORTED, "gated delta rule, per-key-dim decay, fp32 inputs at head size 128 (T > 1)");
   if (U > 0 && !present_state) return fail(LA_ERR_NULL_ARG, "present_state is required");
   const bool work = U > 0 && T > 0;
   if (work && (!q || !k || !v || !out || !beta))

@@ -973,34 +973,42 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   }
 }
 
-template <typename IT, int D, int G>
+// FULL: every decay kind.  fp32 at head size 128 without it leaves out the
+// per-dim decay, whose fp32 table of cumulative decays does not fit the LDS
+// beside the fp32 tiles (the other two kinds take about 144 KB).
+template <typename IT, int D, int G, bool FULL>
 static void launch_dg(int dk, const DeltaArgs& a, hipStream_t st) {
   constexpr int NTH = DeltaShape<G>::NTH;
-  switch (dk) {
-    case 0: hipLaunchKernelGGL((delta_kernel<IT, D, G, 0>), dim3(a.units), dim3(NTH), 0, st, a); break;
-    case 1: hipLaunchKernelGGL((delta_kernel<IT, D, G, 1>), dim3(a.units), dim3(NTH), 0, st, a); break;
-    default: hipLaunchKernelGGL((delta_kernel<IT, D, G, 2>), dim3(a.units), dim3(NTH), 0, st, a); break;
-  }
+  if (dk == 0)
+    hipLaunchKernelGGL((delta_kernel<IT, D, G, 0>), dim3(a.units), dim3(NTH), 0, st, a);
+  else if (dk == 1 || !FULL)
+    hipLaunchKernelGGL((delta_kernel<IT, D, G, 1>), dim3(a.units), dim3(NTH), 0, st, a);
+  else if constexpr (FULL)
+    hipLaunchKernelGGL((delta_kernel<IT, D, G, 2>), dim3(a.units), dim3(NTH), 0, st, a);
 }
 
-template <typename IT, int D>
+template <typename IT, int D, bool FULL>
 static void launch_dd(int dk, int G, const DeltaArgs& a, hipStream_t st) {
   switch (G) {
-    case 1: launch_dg<IT, D, 1>(dk, a, st); break;
-    case 2: launch_dg<IT, D, 2>(dk, a, st); break;
-    case 4: launch_dg<IT, D, 4>(dk, a, st); break;
-    default: launch_dg<IT, D, 8>(dk, a, st); break;
+    case 1: launch_dg<IT, D, 1, FULL>(dk, a, st); break;
+    case 2: launch_dg<IT, D, 2, FULL>(dk, a, st); break;
+    case 4: launch_dg<IT, D, 4, FULL>(dk, a, st); break;
+    default: launch_dg<IT, D, 8, FULL>(dk, a, st); break;
   }
 }
 
 template <typename IT>
 static hipError_t launch_dt(int dk, int D, int G, const DeltaArgs& a, hipStream_t st) {
   switch (D) {
-    case 32: launch_dd<IT, 32>(dk, G, a, st); break;
-    case 64: launch_dd<IT, 64>(dk, G, a, st); break;
+    case 32: launch_dd<IT, 32, true>(dk, G, a, st); break;
+    case 64: launch_dd<IT, 64, true>(dk, G, a, st); break;
     default:
-      if constexpr (sizeof(IT) == 2) launch_dd<IT, 128>(dk, G, a, st);
-      else return hipErrorInvalidValue;  // fp32 at head size 128 does not fit LDS
+      if constexpr (sizeof(IT) == 2) {
+        launch_dd<IT, 128, true>(dk, G, a, st);
+      } else {
+        if (dk == 2) return hipErrorInvalidValue;
+        launch_dd<IT, 128, false>(dk, G, a, st);
+      }
       break;
   }
   return hipGetLastError();

@@ -213,7 +213,8 @@ def test_delta_argument_errors(lib):
     assert g(beta=None) == NULL_ARG           # the delta rules need beta
     assert g(pres=None) == NULL_ARG
     assert g(Dk=96, Dv=96) == UNSUPPORTED
-    assert g(dt=0, Dk=128, Dv=128) == UNSUPPORTED  # fp32 at head size 128 does not fit LDS
+    # fp32 at head size 128 with a per-dim decay does not fit LDS (T > 1 only)
+    assert g(dt=0, Dk=128, Dv=128, d=f(6 << 30), pd=1) == UNSUPPORTED
     assert g(scale=float("inf")) == BAD_ARG
     assert g(out=f(1 << 30)) == BAD_ARG       # out aliases q
     assert g(beta=f((5 << 30) + 64)) == BAD_ARG  # beta inside out

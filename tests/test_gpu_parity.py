@@ -459,7 +459,7 @@ def test_delta_small(dtype, D, G, kind):
     elif kind == "gated_dim":
         g = synth.logsigmoid_decay((B, T, Hkv * D), dtype, DEV, seed, mean=1.0)
     past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, seed, "past")
-    if dtype == torch.float32 and D == 128:
+    if dtype == torch.float32 and D == 128 and kind == "gated_dim":
         with pytest.raises(la.LinAttnError):
             la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=past)
         return
@@ -561,6 +561,31 @@ def test_delta_strong_head_decay(dtype, G):
     assert torch.isfinite(out.float()).all() and torch.isfinite(present).all()
     oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "gated_delta", past_state=f64(past),
                           decay=f64(g), beta=f64(beta))
+    assert_close(out, oo, TOL[dtype], "out")
+    assert_close(present, po, TOL[dtype], "present_state")
+
+
+@pytest.mark.parametrize("G", [2, 8])
+@pytest.mark.parametrize("kind", ["delta", "gated_head", "gated_head_strong"])
+def test_delta_f32_d128(G, kind):
+    """fp32 inputs at head size 128 (no decay or a per-head one) over several
+    chunks and a ragged tail, the two wider GQA groups; the strong case has
+    per-head decays of about -20 per token, which fp32 takes at any strength."""
+    dtype, D, B, T, Hkv = torch.float32, 128, 1, 213, 2
+    Hq = Hkv * G
+    seed = 6600 + G + 7 * len(kind)
+    q = synth.normal((B, T, Hq * D), 1.0, dtype, DEV, seed, "q")
+    k = synth.l2_normalized((B, T, Hkv, D), dtype, DEV, seed, "k").reshape(B, T, Hkv * D)
+    v = synth.normal((B, T, Hkv * D), 1.0, dtype, DEV, seed, "v")
+    beta = _beta((B, T, Hkv), dtype, seed)
+    g = None
+    if kind != "delta":
+        g = synth.logsigmoid_decay((B, T, Hkv), dtype, DEV, seed, mean=-20.0 if kind.endswith("strong") else 1.0)
+    past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, seed, "past")
+    out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=past)
+    torch.cuda.synchronize()
+    oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "delta" if g is None else "gated_delta",
+                          past_state=f64(past), decay=None if g is None else f64(g), beta=f64(beta))
     assert_close(out, oo, TOL[dtype], "out")
     assert_close(present, po, TOL[dtype], "present_state")
 
