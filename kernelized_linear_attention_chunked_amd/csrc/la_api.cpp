@@ -491,18 +491,22 @@ LA_EXPORT la_status la_gated_workspace_size(int64_t B, int64_t T, int64_t Hq, in
   return ok();
 }
 
-LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v,
-                                     const void* decay, int32_t per_dim_decay,
-                                     const float* past_state, float* present_state, void* out,
-                                     int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,
-                                     int64_t Dv, int32_t dtype, float scale, void* workspace,
-                                     size_t workspace_bytes, void* stream) {
+namespace {
+// la_gated_forward, optionally in reversed time (reverse = 1: token t of the
+// recurrence is row T-1-t of q, k, v and out; the backward pass's reverse sums
+// run this way on its time-ordered buffers; not with a per-dim decay).
+la_status gated_forward(const void* q, const void* k, const void* v, const void* decay,
+                        int32_t per_dim_decay, const float* past_state, float* present_state, void* out,
+                        int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
+                        int32_t dtype, float scale, void* workspace, size_t workspace_bytes, void* stream,
+                        int32_t reverse) {
   la_status s = check_gated(B, T, Hq, Hkv, Dk, Dv, dtype);
   if (s != LA_OK) return s;
   if (isnan(scale) || isinf(scale)) return fail(LA_ERR_BAD_ARG, "scale must be finite");
   const int64_t D = Dk, U = B * Hkv, G = Hq / Hkv;
   const int64_t esz = dtype_size(dtype);
   const bool per_dim = per_dim_decay != 0 && decay != nullptr;
+  if (reverse && per_dim) return fail(LA_ERR_UNSUPPORTED, "reversed time with a per-dim decay");
   if (per_dim && dtype == LA_DT_F32 && D == 128 && T > 1)
     return fail(LA_ERR_UNSUPPORTED, "per-key-dim decay with fp32 inputs at head size 128 (T > 1)");
   if (per_dim && !aligned16(decay)) return fail(LA_ERR_BAD_ARG, "a per-dim decay must be 16-byte aligned");
@@ -561,6 +565,7 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
   a.Hq = (int32_t)Hq;
   a.Hkv = (int32_t)Hkv;
   a.scale = scale;
+  a.reverse = reverse;
   const int64_t SE = D * D;
   GatedPlan p = plan_gated(U, T);
   if (p.nseg == 1) {
@@ -601,6 +606,17 @@ LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v
     e = launch(la::kModeCausal, pc, (int)(U * p.nseg));
   }
   return device_status(e, "la_gated_forward (split)");
+}
+}  // namespace
+
+LA_EXPORT la_status la_gated_forward(const void* q, const void* k, const void* v,
+                                     const void* decay, int32_t per_dim_decay,
+                                     const float* past_state, float* present_state, void* out,
+                                     int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,
+                                     int64_t Dv, int32_t dtype, float scale, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return gated_forward(q, k, v, decay, per_dim_decay, past_state, present_state, out, B, T, Hq, Hkv, Dk, Dv,
+                       dtype, scale, workspace, workspace_bytes, stream, 0);
 }
 
 LA_EXPORT la_status la_gated_step(const void* q, const void* k, const void* v, const void* decay,
@@ -725,8 +741,7 @@ LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v
 
 namespace {
 struct BwdLayout {
-  size_t den, fq, fk, v32, fq_r, fk_r, v_r, zc, rs, dnum, dnum_r, dden, qa, kc_r, vd_r, s0t, dstt, scratch,
-      gws, total;
+  size_t den, fq, fk, v32, zc, rs, dnum, dden, qa, kc, vd, s0t, dstt, scratch, gws, total;
 };
 BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t D, int64_t esz, bool norm) {
   const size_t N = (size_t)(B * T * H * D), NT = (size_t)(B * T * H), SE = (size_t)(B * H * D * D);
@@ -742,17 +757,13 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t D, int64_t esz, bo
   L.fq = take(N * 4);
   L.fk = take(N * 4);
   L.v32 = take(N * 4);
-  L.fq_r = take(N * 4);
-  L.fk_r = take(N * 4);
-  L.v_r = take(N * 4);
   L.zc = take(norm ? N * 4 : 0);
   L.rs = take(norm ? N * 4 : 0);
   L.dnum = take(N * 4);
-  L.dnum_r = take(N * 4);
   L.dden = take(NT * 4);
   L.qa = take(N * 4);
-  L.kc_r = take(N * 4);
-  L.vd_r = take(N * 4);
+  L.kc = take(N * 4);
+  L.vd = take(N * 4);
   L.s0t = take(SE * 4);
   L.dstt = take(SE * 4);
   L.scratch = take(SE * 4);
@@ -843,15 +854,11 @@ LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, con
   a.fq = F(L.fq);
   a.fk = F(L.fk);
   a.v32 = F(L.v32);
-  a.fq_r = F(L.fq_r);
-  a.fk_r = F(L.fk_r);
-  a.v_r = F(L.v_r);
   a.dnum = F(L.dnum);
-  a.dnum_r = F(L.dnum_r);
   a.dden = F(L.dden);
   a.qa = F(L.qa);
-  a.kc_r = F(L.kc_r);
-  a.vd_r = F(L.vd_r);
+  a.kc = F(L.kc);
+  a.vd = F(L.vd);
   a.zc = norm ? F(L.zc) : nullptr;
   a.rs = norm ? F(L.rs) : nullptr;
   a.dq = dq;
@@ -863,7 +870,7 @@ LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, con
   a.D = (int32_t)D;
   a.fm = feature_map;
   a.eps = eps;
-  // 1. phi(q), phi(k), v in time order and reversed; 2. z_i; 3. den and dnum
+  // 1. phi(q), phi(k), v; 2. z_i; 3. den and dnum
   e = la::launch_bwd_prep(dtype, a, st);
   if (e == hipSuccess && norm)
     e = la::launch_bwd_scan(F(L.fk), nullptr, state_in_k, F(L.zc), nullptr, (int)U, (int)T, (int)H, (int)D, 0, st);
@@ -887,12 +894,12 @@ LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, con
     e = la::launch_fill_zero(F(L.dden), B * T * H, st);
   }
   if (e != hipSuccess) return device_status(e, "la_backward");
-  // 6. the reversed-time recurrences
-  s = la_gated_forward(F(L.v_r), F(L.dnum_r), F(L.fq_r), nullptr, 0, dstate_out_kv ? F(L.dstt) : nullptr,
-                       F(L.scratch), F(L.kc_r), B, T, H, H, D, D, LA_DT_F32, 1.f, gw, gwb, stream);
+  // 6. the reversed-time recurrences, run backwards over the time-ordered buffers
+  s = gated_forward(F(L.v32), F(L.dnum), F(L.fq), nullptr, 0, dstate_out_kv ? F(L.dstt) : nullptr,
+                    F(L.scratch), F(L.kc), B, T, H, H, D, D, LA_DT_F32, 1.f, gw, gwb, stream, 1);
   if (s != LA_OK) return s;
-  s = la_gated_forward(F(L.fk_r), F(L.fq_r), F(L.dnum_r), nullptr, 0, dstate_out_kv, dstate_in_kv, F(L.vd_r), B, T,
-                       H, H, D, D, LA_DT_F32, 1.f, gw, gwb, stream);
+  s = gated_forward(F(L.fk), F(L.fq), F(L.dnum), nullptr, 0, dstate_out_kv, dstate_in_kv, F(L.vd), B, T, H, H, D,
+                    D, LA_DT_F32, 1.f, gw, gwb, stream, 1);
   if (s != LA_OK) return s;
   // 7. dq, dk, dv
   e = la::launch_bwd_finish(dtype, a, st);

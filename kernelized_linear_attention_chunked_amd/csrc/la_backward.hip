@@ -37,26 +37,17 @@ __device__ __forceinline__ float dphi(float x, int fm) {
   return x > 0.f ? 1.f : 0.f;
 }
 
-// phi(q), phi(k) (0 at invalid tokens), v (0 at invalid tokens) as fp32, in
-// time order and reversed (token t of the reversed copies is token T-1-t).
+// phi(q), phi(k) (0 at invalid tokens), v (0 at invalid tokens) as fp32.
 template <typename IT, int FM>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdArgs a) {
   const int64_t HD = (int64_t)a.H * a.D;
   const int64_t n = (int64_t)a.B * a.T * HD;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
-    const int64_t bt = i / HD, r = i % HD;
-    const int b = (int)(bt / a.T), t = (int)(bt % a.T);
+    const int64_t bt = i / HD;
     const bool m = a.mask ? a.mask[bt] != 0 : true;
-    const float fq = phi<FM>(ld_io((const IT*)a.q, i), a.eps);
-    const float fk = m ? phi<FM>(ld_io((const IT*)a.k, i), a.eps) : 0.f;
-    const float vv = m ? ld_io((const IT*)a.v, i) : 0.f;
-    const int64_t ri = ((int64_t)b * a.T + (a.T - 1 - t)) * HD + r;
-    a.fq[i] = fq;
-    a.fk[i] = fk;
-    a.v32[i] = vv;
-    a.fq_r[ri] = fq;
-    a.fk_r[ri] = fk;
-    a.v_r[ri] = vv;
+    a.fq[i] = phi<FM>(ld_io((const IT*)a.q, i), a.eps);
+    a.fk[i] = m ? phi<FM>(ld_io((const IT*)a.k, i), a.eps) : 0.f;
+    a.v32[i] = m ? ld_io((const IT*)a.v, i) : 0.f;
   }
 }
 
@@ -109,7 +100,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const float* __r
   }
 }
 
-// den (normalized: phi_q . z + eps in fp32) and dnum (time order and reversed)
+// den (normalized: phi_q . z + eps in fp32) and dnum
 // per token: one wave per (b, t, h).
 template <typename IT>
 __global__ __launch_bounds__(kThreads) void bwd_dnum_kernel(BwdArgs a) {
@@ -118,11 +109,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dnum_kernel(BwdArgs a) {
   if (tk >= ntok) return;  // whole waves
   const int l = threadIdx.x & 63;
   const int64_t bt = tk / a.H;
-  const int h = (int)(tk % a.H);
-  const int b = (int)(bt / a.T), t = (int)(bt % a.T);
   const bool m = a.mask ? a.mask[bt] != 0 : true;
   const int64_t base = tk * a.D;
-  const int64_t rbase = (((int64_t)b * a.T + (a.T - 1 - t)) * a.H + h) * a.D;
   float rden = 1.f;
   if (a.den) {
     float dot = 0.f;
@@ -134,9 +122,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dnum_kernel(BwdArgs a) {
     rden = 1.f / den;
   }
   for (int d = l; d < a.D; d += 64) {
-    const float g = m ? ld_io((const IT*)a.dy, base + d) * rden : 0.f;
-    a.dnum[base + d] = g;
-    a.dnum_r[rbase + d] = g;
+    a.dnum[base + d] = m ? ld_io((const IT*)a.dy, base + d) * rden : 0.f;
   }
 }
 
@@ -157,24 +143,22 @@ __global__ __launch_bounds__(kThreads) void bwd_dden_kernel(BwdArgs a) {
 }
 
 // dq, dk, dv from the recurrences' outputs: dq = (A + z dden) phi'(q),
-// dk = (C (reversed) + R) phi'(k), dv = Dv (reversed), 0 at invalid tokens.
+// dk = (C + R) phi'(k), dv = Dv, 0 at invalid tokens.
 template <typename IT>
 __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(BwdArgs a) {
   const int64_t HD = (int64_t)a.H * a.D;
   const int64_t n = (int64_t)a.B * a.T * HD;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) {
     const int64_t bt = i / HD, r = i % HD;
-    const int b = (int)(bt / a.T), t = (int)(bt % a.T);
     const bool m = a.mask ? a.mask[bt] != 0 : true;
-    const int64_t ri = ((int64_t)b * a.T + (a.T - 1 - t)) * HD + r;
     float gq = 0.f, gk = 0.f, gv = 0.f;
     if (m) {
-      float pq = a.qa[i], pk = a.kc_r[ri];
+      float pq = a.qa[i], pk = a.kc[i];
       if (a.zc) pq += a.zc[i] * a.dden[bt * a.H + r / a.D];
       if (a.rs) pk += a.rs[i];
       gq = pq * dphi(ld_io((const IT*)a.q, i), a.fm);
       gk = pk * dphi(ld_io((const IT*)a.k, i), a.fm);
-      gv = a.vd_r[ri];
+      gv = a.vd[i];
     }
     st_io((IT*)a.dq, i, gq);
     st_io((IT*)a.dk, i, gk);

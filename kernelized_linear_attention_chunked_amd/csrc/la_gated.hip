@@ -111,12 +111,18 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int c0 = s * a.seg_chunks;
   const int c1 = min(c0 + a.seg_chunks, nchunks);
-  const int QS = Hq * D, KS = Hkv * D;  // token strides of q/out and k/v
-  const IT* qb = (const IT*)a.q + (int64_t)b * T * QS + (int64_t)(j * G) * D;
-  IT* ob = (IT*)a.out + (int64_t)b * T * QS + (int64_t)(j * G) * D;
-  const IT* kb = (const IT*)a.k + (int64_t)b * T * KS + (int64_t)j * D;
-  const IT* vb = (const IT*)a.v + (int64_t)b * T * KS + (int64_t)j * D;
-  const IT* gb = a.decay ? (const IT*)a.decay + (int64_t)b * T * Hkv + j : nullptr;
+  // token strides of q/out, k/v and the decay.  In reversed time the bases
+  // sit at row T-1 and the strides are negated, so token t (always in
+  // [0, T) where it is addressed) is row T-1-t.
+  const int QS0 = Hq * D, KS0 = Hkv * D;
+  const bool rev = a.reverse != 0;
+  const int QS = rev ? -QS0 : QS0, KS = rev ? -KS0 : KS0, GS = rev ? -Hkv : Hkv;
+  const int64_t row0 = rev ? (int64_t)b * T + (T - 1) : (int64_t)b * T;  // row of token 0
+  const IT* qb = (const IT*)a.q + row0 * QS0 + (int64_t)(j * G) * D;
+  IT* ob = (IT*)a.out + row0 * QS0 + (int64_t)(j * G) * D;
+  const IT* kb = (const IT*)a.k + row0 * KS0 + (int64_t)j * D;
+  const IT* vb = (const IT*)a.v + row0 * KS0 + (int64_t)j * D;
+  const IT* gb = a.decay ? (const IT*)a.decay + row0 * Hkv + j : nullptr;
   const float scale = a.scale;
   // LDS element offsets (layouts and swizzles of la_device.hpp)
   auto vt_at = [&](int r, int blk) { return r * VT_LD + ((blk ^ vt_swz(r)) * VEC); };
@@ -192,7 +198,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
     }
     // without a decay input (the plain linear rule) some valid word is read and
     // ignored, so that the load is unconditional
-    pgr = load_g(gb ? gb + (int64_t)min(tb + l, T - 1) * Hkv : kb);
+    pgr = load_g(gb ? gb + (int64_t)min(tb + l, T - 1) * GS : kb);
   };
   // the wave's own query rows of its heads.  Staged: whole rows (piece g = 64n + l
   // of a head's 16 x D block is row g / CB, 16-byte block g % CB), parked in the

@@ -104,6 +104,9 @@ struct GatedArgs {
   int32_t T, Hq, Hkv;
   int32_t seg_count, seg_first, seg_chunks, nseg_total;
   float scale;
+  // 1: run in reversed time, token t of the recurrence being row T-1-t of q,
+  // k, v, the decay and out (la_gated.hip only; the per-dim kernel takes 0)
+  int32_t reverse;
 };
 hipError_t launch_gated(int mode, int io, int D, int G, const GatedArgs& a, int grid,
                         hipStream_t st);
@@ -126,8 +129,7 @@ struct DeltaArgs {
 // size 128 is not available (LDS).
 hipError_t launch_delta(int io, int D, int G, int decay_kind, const DeltaArgs& a, hipStream_t st);
 
-// Causal backward (la_backward.hip): buffers are (B,T,H,D) fp32 unless noted;
-// *_r are in reversed time.
+// Causal backward (la_backward.hip): buffers are (B,T,H,D) fp32 unless noted.
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -138,15 +140,11 @@ struct BwdArgs {
   float* fq;
   float* fk;
   float* v32;
-  float* fq_r;
-  float* fk_r;
-  float* v_r;
   float* dnum;
-  float* dnum_r;
   float* dden;          // (B,T,H)
   const float* qa;      // S_i dnum_i
-  const float* kc_r;    // sum_{i>=j} phi_q_i (v_j . dnum_i) + dS_T v_j  (reversed)
-  const float* vd_r;    // dv (reversed)
+  const float* kc;      // sum_{i>=j} phi_q_i (v_j . dnum_i) + dS_T v_j
+  const float* vd;      // dv
   const float* zc;      // z_i (normalized), or null
   const float* rs;      // dz_T + sum_{i>=j} phi_q_i dden_i (normalized), or null
   void* dq;
