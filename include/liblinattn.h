@@ -199,7 +199,8 @@ la_status la_backward_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk
  *   dq, dk (B,T,H,Dk), dv (B,T,H,Dv) in `dtype`: written; 0 at invalid tokens;
  *   dstate_in_kv (B,H,Dk,Dv), dstate_in_k (B,H,Dk, normalizer only), float32:
  *     the gradient of the initial state, always written.
- * Outputs may not overlap the inputs or each other.  Evaluated as three
+ * Outputs may not overlap the inputs or each other; every buffer is 16-byte
+ * aligned (else LA_ERR_BAD_ARG).  Evaluated as three
  * chunk-parallel linear-rule recurrences (two in reversed time) plus prefix
  * sums, in float32; needs la_backward_workspace_size bytes of workspace. */
 la_status la_backward(const void* q, const void* k, const void* v, const uint8_t* mask,

@@ -811,10 +811,10 @@ LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, con
   const bool work = T > 0;
   if (work && (!q || !k || !v || !dout || !dq || !dk || !dv))
     return fail(LA_ERR_NULL_ARG, "q, k, v, dout, dq, dk and dv are required");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state_in_kv) || !aligned16(state_in_k) ||
-      !aligned16(dstate_out_kv) || !aligned16(dstate_out_k) || !aligned16(dstate_in_kv) ||
-      !aligned16(dstate_in_k) || !aligned16(workspace))
-    return fail(LA_ERR_BAD_ARG, "q, k, v, the states and the workspace must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || !aligned16(state_in_kv) || !aligned16(state_in_k) || !aligned16(dstate_out_kv) ||
+      !aligned16(dstate_out_k) || !aligned16(dstate_in_kv) || !aligned16(dstate_in_k) || !aligned16(workspace))
+    return fail(LA_ERR_BAD_ARG, "q, k, v, dout, dq, dk, dv, the states and the workspace must be 16-byte aligned");
   const int64_t nb = B * T * H * D * esz;
   const BwdLayout L = bwd_layout(B, T, H, D, esz, norm);
   const size_t need = work ? L.total : 0;

@@ -246,6 +246,8 @@ def test_backward_argument_errors(lib):
     assert g(norm=0) == STATE                 # k parts given without the normalizer
     assert g(si=f(10 << 30)) == STATE         # kv state without its k part
     assert g(dq=f(1 << 30)) == BAD_ARG        # dq aliases q
+    assert g(dq=f((5 << 30) + 8)) == BAD_ARG  # gradients are written as 16-byte vectors
+    assert g(dout=f((4 << 30) + 4)) == BAD_ARG
     assert g(dk=f(5 << 30)) == BAD_ARG        # dk overlaps dq
     assert g(ws=None, wsb=0) == WORKSPACE
     assert g(Dk=96, Dv=96) == UNSUPPORTED
