@@ -134,8 +134,10 @@ la_status la_gated_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
  * scale == 0 means 1/sqrt(Dk).  Hq must be a positive multiple of Hkv
  * (else LA_ERR_SHAPE).  A per-dim decay is evaluated chunk-parallel with keys
  * rescaled inside blocks of 32 tokens: decays summing below about -87 over
- * one such block (per dimension) overflow; fp32 inputs at Dk = 128 with T > 1
- * and a per-dim decay return LA_ERR_UNSUPPORTED. */
+ * one such block (per dimension) overflow.  fp32 inputs at Dk = 128 with a
+ * per-dim decay and T > 1 (whose chunk tiles exceed the LDS) run the T == 1
+ * step kernel once per token instead: no range limit and no workspace, but
+ * one state read and write per token (la_gated_workspace_size reports 0). */
 la_status la_gated_forward(const void* q, const void* k, const void* v, const void* decay,
                            int32_t per_dim_decay, const float* past_state, float* present_state,
                            void* out, int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,
@@ -176,7 +178,8 @@ la_status la_gated_step(const void* q, const void* k, const void* v, const void*
  * per-head decays (keys rescaled per 32-token block: decays summing below
  * about -87 over one block overflow); bf16 and fp32 inputs take per-head
  * decays of any strength.  fp32 inputs at Dk = 128 with a per-dim decay and
- * T > 1 return LA_ERR_UNSUPPORTED.  T == 1 runs a streaming step instead: one read and one
+ * T > 1 run the step below once per token (slower: one state read and write
+ * per token).  T == 1 runs a streaming step instead: one read and one
  * write of the state per (batch, kv head), in place allowed (present_state ==
  * past_state), no decay range limit, every dtype and head size. */
 la_status la_delta_forward(const void* q, const void* k, const void* v, const void* decay,

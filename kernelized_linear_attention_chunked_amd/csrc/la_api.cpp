@@ -481,13 +481,27 @@ hipError_t launch_step(const void* q, const void* k, const void* v, const void* 
   return la::launch_gated_step(dtype, (int)D, (int)G, a, st);
 }
 
+namespace {
+// fp32 inputs at head size 128 with a per-key-dim decay: the chunk kernels'
+// fp32 tiles and decay table exceed the LDS, so T > 1 runs the one-token step
+// kernel once per token (state read and written per token; no workspace)
+bool by_token(bool per_dim, int32_t dtype, int64_t D, int64_t T) {
+  return per_dim && dtype == LA_DT_F32 && D == 128 && T > 1;
+}
+
+// token t of each (B, T, width) tensor: the step kernel reads batch b at row b*T
+const void* at_token(const void* p, int64_t t, int64_t width, int64_t esz) {
+  return p ? (const void*)((const char*)p + t * width * esz) : nullptr;
+}
+}  // namespace
+
 LA_EXPORT la_status la_gated_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
                                             int64_t Dk, int64_t Dv, int32_t dtype,
                                             int32_t per_dim_decay, size_t* bytes) {
   if (!bytes) return fail(LA_ERR_NULL_ARG, "bytes is NULL");
   la_status s = check_gated(B, T, Hq, Hkv, Dk, Dv, dtype);
   if (s != LA_OK) return s;
-  *bytes = gated_ws_bytes(B, T, Hkv, Dk, per_dim_decay != 0);
+  *bytes = by_token(per_dim_decay != 0, dtype, Dk, T) ? 0 : gated_ws_bytes(B, T, Hkv, Dk, per_dim_decay != 0);
   return ok();
 }
 
@@ -507,8 +521,6 @@ la_status gated_forward(const void* q, const void* k, const void* v, const void*
   const int64_t esz = dtype_size(dtype);
   const bool per_dim = per_dim_decay != 0 && decay != nullptr;
   if (reverse && per_dim) return fail(LA_ERR_UNSUPPORTED, "reversed time with a per-dim decay");
-  if (per_dim && dtype == LA_DT_F32 && D == 128 && T > 1)
-    return fail(LA_ERR_UNSUPPORTED, "per-key-dim decay with fp32 inputs at head size 128 (T > 1)");
   if (per_dim && !aligned16(decay)) return fail(LA_ERR_BAD_ARG, "a per-dim decay must be 16-byte aligned");
   if (U > 0 && !present_state) return fail(LA_ERR_NULL_ARG, "present_state is required");
   const bool work = U > 0 && T > 0;
@@ -520,7 +532,8 @@ la_status gated_forward(const void* q, const void* k, const void* v, const void*
   const Range rv = range(v, B * T * Hkv * D * esz), ro = range(out, B * T * Hq * D * esz);
   const Range rg = range(decay, B * T * Hkv * (per_dim ? D : 1) * esz);
   const Range rpi = range(past_state, U * D * D * 4), rpo = range(present_state, U * D * D * 4);
-  const size_t need = gated_ws_bytes(B, T, Hkv, D, per_dim);
+  const bool tokens = by_token(per_dim, dtype, D, T);
+  const size_t need = tokens ? 0 : gated_ws_bytes(B, T, Hkv, D, per_dim);
   const Range rw = range(workspace, (int64_t)need);
   const Range ins[5] = {rq, rk, rv, rg, rw};
   for (const Range& i : ins)
@@ -549,6 +562,26 @@ la_status gated_forward(const void* q, const void* k, const void* v, const void*
     e = launch_step(q, k, v, decay, per_dim, past_state, present_state, out, U, Hkv, D, G, dtype,
                     scale, st);
     return device_status(e, "la_gated_forward");
+  }
+  if (tokens) {
+    la::GatedStepArgs g;
+    memset(&g, 0, sizeof(g));
+    g.Hkv = (int32_t)Hkv;
+    g.units = (int32_t)U;
+    g.per_dim = 1;
+    g.scale = scale;
+    g.batch_rows = (int32_t)T;
+    g.s_out = present_state;
+    for (int64_t t = 0; t < T && e == hipSuccess; ++t) {
+      g.q = at_token(q, t, Hq * D, esz);
+      g.k = at_token(k, t, Hkv * D, esz);
+      g.v = at_token(v, t, Hkv * D, esz);
+      g.decay = at_token(decay, t, Hkv * D, esz);
+      g.out = (void*)at_token(out, t, Hq * D, esz);
+      g.s_in = t == 0 ? past_state : present_state;
+      e = la::launch_gated_step(dtype, (int)D, (int)G, g, st);
+    }
+    return device_status(e, "la_gated_forward (token by token)");
   }
   auto launch = [&](int mode, const la::GatedArgs& ga, int grid) {
     return per_dim ? la::launch_gated_pd(mode, dtype, (int)D, (int)G, ga, grid, st)
@@ -664,8 +697,6 @@ LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v
   const int64_t D = Dk, U = B * Hkv, G = Hq / Hkv;
   const int64_t esz = dtype_size(dtype);
   const bool per_dim = per_dim_decay != 0 && decay != nullptr;
-  if (per_dim && dtype == LA_DT_F32 && D == 128 && T > 1)
-    return fail(LA_ERR_UNSUPPORTED, "gated delta rule, per-key-dim decay, fp32 inputs at head size 128 (T > 1)");
   if (U > 0 && !present_state) return fail(LA_ERR_NULL_ARG, "present_state is required");
   const bool work = U > 0 && T > 0;
   if (work && (!q || !k || !v || !out || !beta))
@@ -715,6 +746,28 @@ LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v
     g.beta_heads = (int32_t)bh;
     e = la::launch_delta_step(dtype, (int)D, (int)G, g, st);
     return device_status(e, "la_delta_forward (T = 1)");
+  }
+  if (by_token(per_dim, dtype, D, T)) {
+    la::GatedStepArgs g;
+    memset(&g, 0, sizeof(g));
+    g.Hkv = (int32_t)Hkv;
+    g.units = (int32_t)U;
+    g.per_dim = 1;
+    g.scale = scale;
+    g.beta_heads = (int32_t)bh;
+    g.batch_rows = (int32_t)T;
+    g.s_out = present_state;
+    for (int64_t t = 0; t < T && e == hipSuccess; ++t) {
+      g.q = at_token(q, t, Hq * D, esz);
+      g.k = at_token(k, t, Hkv * D, esz);
+      g.v = at_token(v, t, Hkv * D, esz);
+      g.decay = at_token(decay, t, Hkv * D, esz);
+      g.beta = at_token(beta, t, bh, esz);
+      g.out = (void*)at_token(out, t, Hq * D, esz);
+      g.s_in = t == 0 ? past_state : present_state;
+      e = la::launch_delta_step(dtype, (int)D, (int)G, g, st);
+    }
+    return device_status(e, "la_delta_forward (token by token)");
   }
   la::DeltaArgs a;
   a.q = q;

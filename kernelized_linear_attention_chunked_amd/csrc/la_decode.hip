@@ -165,17 +165,19 @@ __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArg
     for (int r = 0; r < RPT; ++r) sv[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   const int QW = a.Hkv * G * D;  // query row width
-  const DT* qp = (const DT*)a.q + (int64_t)b * QW + (int64_t)j * G * D;
-  const DT* kp = (const DT*)a.k + (int64_t)u * D;
-  const DT* vp = (const DT*)a.v + (int64_t)u * D;
+  // row of batch b in the token tensors, and (row, kv head) index
+  const int64_t br = (int64_t)b * (a.batch_rows > 1 ? a.batch_rows : 1), uh = br * a.Hkv + j;
+  const DT* qp = (const DT*)a.q + br * QW + (int64_t)j * G * D;
+  const DT* kp = (const DT*)a.k + uh * D;
+  const DT* vp = (const DT*)a.v + uh * D;
   float v4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) v4[i] = live ? load_elem<DT>(vp, 4 * c4 + i) : 0.f;
-  const float e = (live && a.decay && !PD) ? __expf(load_elem<DT>((const DT*)a.decay, u)) : 1.f;
+  const float e = (live && a.decay && !PD) ? __expf(load_elem<DT>((const DT*)a.decay, uh)) : 1.f;
   if (live) {
     for (int i = tid; i < D; i += kThreads) fk[ul][i] = load_elem<DT>(kp, i);
     if constexpr (PD)  // per-key-dim decay: row dk of S scales by exp(g[dk])
-      for (int i = tid; i < D; i += kThreads) fe[ul][i] = __expf(load_elem<DT>((const DT*)a.decay + (int64_t)u * D, i));
+      for (int i = tid; i < D; i += kThreads) fe[ul][i] = __expf(load_elem<DT>((const DT*)a.decay + uh * D, i));
     for (int i = tid; i < G * D; i += kThreads) fq[ul][i / D][i % D] = load_elem<DT>(qp, i);
   }
   __syncthreads();
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArg
   }
   __syncthreads();
   if (live) {
-    DT* op = (DT*)a.out + (int64_t)b * QW + (int64_t)j * G * D;
+    DT* op = (DT*)a.out + br * QW + (int64_t)j * G * D;
     for (int i = tid; i < G * D; i += kThreads) {
       const int h = i / D, d = i % D;
       float y = 0.f;
@@ -269,16 +271,18 @@ __global__ __launch_bounds__(kDecodeThreads) void delta_step_kernel(GatedStepArg
     for (int r = 0; r < RPT; ++r) sv[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   const int QW = a.Hkv * G * D;  // query row width
-  const DT* qp = (const DT*)a.q + (int64_t)b * QW + (int64_t)j * G * D;
-  const DT* kp = (const DT*)a.k + (int64_t)u * D;
-  const DT* vp = (const DT*)a.v + (int64_t)u * D;
-  const float e = (live && DK == 1) ? __expf(load_elem<DT>((const DT*)a.decay, u)) : 1.f;
-  const float be = live ? load_elem<DT>((const DT*)a.beta, b * a.beta_heads + (a.beta_heads > 1 ? j : 0)) : 0.f;
+  // row of batch b in the token tensors, and (row, kv head) index
+  const int64_t br = (int64_t)b * (a.batch_rows > 1 ? a.batch_rows : 1), uh = br * a.Hkv + j;
+  const DT* qp = (const DT*)a.q + br * QW + (int64_t)j * G * D;
+  const DT* kp = (const DT*)a.k + uh * D;
+  const DT* vp = (const DT*)a.v + uh * D;
+  const float e = (live && DK == 1) ? __expf(load_elem<DT>((const DT*)a.decay, uh)) : 1.f;
+  const float be = live ? load_elem<DT>((const DT*)a.beta, br * a.beta_heads + (a.beta_heads > 1 ? j : 0)) : 0.f;
   const float vc = (live && tid < D) ? load_elem<DT>(vp, tid) : 0.f;  // v of column tid
   if (live) {
     for (int i = tid; i < D; i += kThreads) fk[ul][i] = load_elem<DT>(kp, i);
     if constexpr (DK == 2)  // per-key-dim decay: row dk of S scales by exp(g[dk])
-      for (int i = tid; i < D; i += kThreads) fe[ul][i] = __expf(load_elem<DT>((const DT*)a.decay + (int64_t)u * D, i));
+      for (int i = tid; i < D; i += kThreads) fe[ul][i] = __expf(load_elem<DT>((const DT*)a.decay + uh * D, i));
     for (int i = tid; i < G * D; i += kThreads) fq[ul][i / D][i % D] = load_elem<DT>(qp, i);
   }
   __syncthreads();
@@ -347,7 +351,7 @@ __global__ __launch_bounds__(kDecodeThreads) void delta_step_kernel(GatedStepArg
   }
   __syncthreads();
   if (live) {
-    DT* op = (DT*)a.out + (int64_t)b * QW + (int64_t)j * G * D;
+    DT* op = (DT*)a.out + br * QW + (int64_t)j * G * D;
     for (int i = tid; i < G * D; i += kThreads) {
       const int h = i / D, d = i % D;
       float y = 0.f;

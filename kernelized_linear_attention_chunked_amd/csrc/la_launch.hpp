@@ -177,6 +177,9 @@ struct GatedStepArgs {
   // delta rules only: beta (B, beta_heads), beta_heads = Hkv or 1 (shared)
   const void* beta;
   int32_t beta_heads;
+  // rows per batch of q, k, v, the decay, beta and out: 0 or 1 for (B, ...)
+  // tensors; T when the pointers sit at token t of (B, T, ...) tensors
+  int32_t batch_rows;
 };
 hipError_t launch_gated_step(int io, int D, int G, const GatedStepArgs& a, hipStream_t st);
 // T == 1 step of the delta rules (la_decode.hip): decay null ("delta"), per kv

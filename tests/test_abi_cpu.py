@@ -165,8 +165,10 @@ def test_gated_argument_errors(lib):
     assert g(scale=float("inf")) == BAD_ARG
     assert g(T=4096) == WORKSPACE             # 2 units: the sequence is split
     assert g(out=f(1 << 30)) == BAD_ARG       # out aliases q
-    # fp32 per-dim decay at head size 128 over more than one token does not fit LDS
-    assert g(d=f(6 << 30), pd=1, dt=0, Dk=128, Dv=128) == UNSUPPORTED
+    # fp32 per-dim decay at head size 128 runs token by token: no workspace
+    n = ctypes.c_size_t(1)
+    assert lib.la_gated_workspace_size(1, 4096, 4, 2, 128, 128, 0, 1, ctypes.byref(n)) == OK and n.value == 0
+    assert lib.la_gated_workspace_size(1, 4096, 4, 2, 128, 128, 1, 1, ctypes.byref(n)) == OK and n.value > 0
     # a per-dim decay overlapping out (its extent is Hkv*Dk per token)
     assert g(d=f((5 << 30) - 64 * 2 * 64 * 2 + 16), pd=1) == BAD_ARG
     assert g(d=f((6 << 30) + 2), pd=1) == BAD_ARG  # per-dim decays are read as 16-byte vectors
@@ -213,8 +215,7 @@ def test_delta_argument_errors(lib):
     assert g(beta=None) == NULL_ARG           # the delta rules need beta
     assert g(pres=None) == NULL_ARG
     assert g(Dk=96, Dv=96) == UNSUPPORTED
-    # fp32 at head size 128 with a per-dim decay does not fit LDS (T > 1 only)
-    assert g(dt=0, Dk=128, Dv=128, d=f(6 << 30), pd=1) == UNSUPPORTED
+    assert g(dt=0, Dk=128, Dv=128, d=f((6 << 30) + 2), pd=1) == BAD_ARG  # misaligned per-dim decay
     assert g(scale=float("inf")) == BAD_ARG
     assert g(out=f(1 << 30)) == BAD_ARG       # out aliases q
     assert g(beta=f((5 << 30) + 64)) == BAD_ARG  # beta inside out

@@ -361,10 +361,7 @@ def test_gated_perdim_small(dtype, D, G):
     Hq = Hkv * G
     q, k, v, g = _pd_inputs(B, T, Hq, Hkv, D, dtype, 5000 + D + G)
     past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, 5000 + D + G, "past")
-    if dtype == torch.float32 and D == 128:
-        with pytest.raises(la.LinAttnError):
-            la.la_gated_forward(q, k, v, Hq, Hkv, decay=g, past_state=past)
-        return
+    # (fp32 at head size 128 runs token by token)
     out, present = la.la_gated_forward(q, k, v, Hq, Hkv, decay=g, past_state=past)
     torch.cuda.synchronize()
     oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "gated", past_state=f64(past), decay=f64(g))
@@ -459,10 +456,7 @@ def test_delta_small(dtype, D, G, kind):
     elif kind == "gated_dim":
         g = synth.logsigmoid_decay((B, T, Hkv * D), dtype, DEV, seed, mean=1.0)
     past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, seed, "past")
-    if dtype == torch.float32 and D == 128 and kind == "gated_dim":
-        with pytest.raises(la.LinAttnError):
-            la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=past)
-        return
+    # (fp32 at head size 128 with a per-dim decay runs token by token)
     out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=past)
     torch.cuda.synchronize()
     oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "delta" if g is None else "gated_delta",
@@ -586,6 +580,36 @@ def test_delta_f32_d128(G, kind):
     torch.cuda.synchronize()
     oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, "delta" if g is None else "gated_delta",
                           past_state=f64(past), decay=None if g is None else f64(g), beta=f64(beta))
+    assert_close(out, oo, TOL[dtype], "out")
+    assert_close(present, po, TOL[dtype], "present_state")
+
+
+@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("rule", ["gated", "gated_delta"])
+def test_perdim_f32_d128_token_by_token(G, rule):
+    """fp32 inputs at head size 128 with a per-dim decay run the one-token step
+    once per token: a ragged length, strong decays (about -20 per token, beyond
+    the chunk kernels' range), the state updated in place across the tokens."""
+    dtype, D, B, T, Hkv = torch.float32, 128, 2, 97, 2
+    Hq = Hkv * G
+    seed = 6700 + G + 7 * len(rule)
+    q = synth.normal((B, T, Hq * D), 1.0, dtype, DEV, seed, "q")
+    k = synth.l2_normalized((B, T, Hkv, D), dtype, DEV, seed, "k").reshape(B, T, Hkv * D)
+    v = synth.normal((B, T, Hkv * D), 1.0, dtype, DEV, seed, "v")
+    g = synth.logsigmoid_decay((B, T, Hkv * D), dtype, DEV, seed, mean=-20.0)
+    past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, seed, "past")
+    state = past.clone()
+    if rule == "gated":
+        out, present = la.la_gated_forward(q, k, v, Hq, Hkv, decay=g, past_state=state, present_state=state)
+        beta = None
+    else:
+        beta = _beta((B, T, Hkv), dtype, seed)
+        out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=state,
+                                           present_state=state)
+    torch.cuda.synchronize()
+    assert present.data_ptr() == state.data_ptr()
+    oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, rule, past_state=f64(past), decay=f64(g),
+                          beta=None if beta is None else f64(beta))
     assert_close(out, oo, TOL[dtype], "out")
     assert_close(present, po, TOL[dtype], "present_state")
 
