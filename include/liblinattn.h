@@ -21,7 +21,7 @@
  * definition", "Streaming State", "Numerical Stability").
  *
  * Supported head sizes: Dk == Dv, one of 32, 64, 128.  Other sizes return
- * LA_ERR_UNSUPPORTED (there is no slower fallback path).
+ * LA_ERR_UNSUPPORTED (no slower path covers other sizes).
  */
 #ifndef LIBLINATTN_H
 #define LIBLINATTN_H
