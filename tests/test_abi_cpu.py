@@ -253,3 +253,34 @@ def test_backward_argument_errors(lib):
     assert g(ws=None, wsb=0) == WORKSPACE
     assert g(Dk=96, Dv=96) == UNSUPPORTED
     assert g(B=0) == OK
+
+
+def test_binding_buffer_checks_on_host_tensors():
+    """The binding's argument checks (device-independent): outputs must be
+    contiguous with the exact dtype and shape; inputs are copied when strided
+    and rejected when their dtype or shape is wrong."""
+    import torch
+    x = torch.zeros((2, 3, 4, 4))
+    assert la._output(x, "x", "cpu", torch.float32, (2, 3, 4, 4)) is x
+    with pytest.raises(ValueError):
+        la._output(x.transpose(2, 3), "x", "cpu", torch.float32, (2, 3, 4, 4))
+    with pytest.raises(ValueError):
+        la._output(x.to(torch.bfloat16), "x", "cpu", torch.float32, (2, 3, 4, 4))
+    with pytest.raises(ValueError):
+        la._output(x, "x", "cpu", torch.float32, (2, 3, 4, 5))
+    y = la._input(x.transpose(2, 3), "y", "cpu", torch.float32, (2, 3, 4, 4))
+    assert y.is_contiguous() and torch.equal(y, x.transpose(2, 3))
+    with pytest.raises(ValueError):
+        la._input(x.to(torch.bfloat16), "y", "cpu", torch.float32)
+    # state pairs: the k part follows the normaliser setting
+    z = torch.zeros((2, 3, 4))
+    assert la._state_pair((x, z), 2, 3, 4, 4, True, "cpu", "s", output=True)[0] is x
+    with pytest.raises(ValueError):
+        la._state_pair((x, z), 2, 3, 4, 4, False, "cpu", "s", output=True)
+    with pytest.raises(ValueError):
+        la._state_pair((x, None), 2, 3, 4, 4, True, "cpu", "s", output=False)
+    # a workspace smaller than needed, or strided, is refused
+    with pytest.raises(ValueError):
+        la._workspace(torch.empty(8, dtype=torch.uint8), 16, "cpu")
+    ws, n = la._workspace(torch.empty(4, dtype=torch.float32), 16, "cpu")
+    assert n == 16
