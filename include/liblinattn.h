@@ -98,6 +98,29 @@ la_status la_forward(const void* q, const void* k, const void* v, const uint8_t*
                      void* out, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
                      int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/* la_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments and results without the workspace, which is replaced by a
+ * scratch array of LA_NOALLOC_SCRATCH_BYTES that the library keeps on each GPU
+ * it runs on until the process ends.  No call allocates, frees or runs an
+ * allocating library routine.  Where la_forward would split a sequence (few
+ * (batch, head) units), the split is bounded by the scratch size: a causal
+ * call then uses fewer, longer segments (at worst one, which needs no
+ * scratch), so every causal call is accepted; a non-causal call needs at least
+ * B*H*(Dk*Dv + Dk)*4 bytes and returns LA_ERR_WORKSPACE beyond the scratch
+ * size (B*H > 1016 at Dk = Dv = 128, for example).  The stream must belong to
+ * the current device (else LA_ERR_DEVICE).  Every call on one GPU shares that
+ * GPU's scratch: calls that overlap in time on one GPU (two streams, two host
+ * threads) race and give wrong results; calls ordered on one stream are safe.
+ * The scratch needs no clearing: each call writes every byte it reads. */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+la_status la_forward_noalloc(const void* q, const void* k, const void* v, const uint8_t* mask,
+                             const float* state_in_kv, const float* state_in_k,
+                             float* state_out_kv, float* state_out_k,
+                             int32_t causal, int32_t feature_map, int32_t use_normalizer, float eps,
+                             void* out, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                             int32_t dtype, void* stream);
+
 /* One causal decode step (T == 1): q, k, v are (B, H, Dk/Dv), mask is (B) or
  * NULL, out is (B, H, Dv).  Same semantics as la_forward with T == 1
  * ("Streaming State": token-by-token execution; "Execution Modes": a single

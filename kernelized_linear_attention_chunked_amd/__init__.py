@@ -18,6 +18,8 @@ Functions carry the C names:
   State", get_initial_state).
 * :func:`la_forward` -- causal / non-causal attention with masks and streaming
   state (Keras proposal, "Mathematical definition", "Masking").
+* :func:`la_forward_noalloc` -- :func:`la_forward` without a workspace, for
+  callers that cannot allocate (the library's own per-GPU scratch array).
 * :func:`la_step` -- one T=1 causal decode step.
 * :func:`la_gated_forward` -- gated / linear recurrence with GQA (the
   LinearAttention operator page, ai.onnx since version 27).
@@ -36,13 +38,14 @@ import torch
 from .build import LIB_PATH, build as _build
 
 __all__ = [
-    "LinAttnError", "la_initial_state", "la_forward", "la_step", "la_gated_forward",
+    "LinAttnError", "la_initial_state", "la_forward", "la_forward_noalloc", "la_step", "la_gated_forward",
     "la_gated_step", "la_delta_forward", "la_backward", "la_workspace_size", "la_gated_workspace_size", "library_path", "load_library",
     "EXPORTED_SYMBOLS",
 ]
 
 EXPORTED_SYMBOLS = (
-    "la_initial_state", "la_workspace_size", "la_forward", "la_step", "la_gated_workspace_size",
+    "la_initial_state", "la_workspace_size", "la_forward", "la_forward_noalloc", "la_step",
+    "la_gated_workspace_size",
     "la_gated_forward", "la_gated_step", "la_delta_forward", "la_backward_workspace_size",
     "la_backward", "la_status_string", "la_last_error_message",
 )
@@ -84,6 +87,8 @@ def load_library(build_if_missing: bool = True):
         lib.la_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
         lib.la_forward.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, f32, p,
                                    i64, i64, i64, i64, i64, i32, p, sz, p]
+        lib.la_forward_noalloc.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, f32, p,
+                                           i64, i64, i64, i64, i64, i32, p]
         lib.la_step.argtypes = [p, p, p, p, p, p, p, p, i32, i32, f32, p, i64, i64, i64, i64, i32, p]
         lib.la_gated_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32,
                                                 ctypes.POINTER(sz)]
@@ -95,7 +100,7 @@ def load_library(build_if_missing: bool = True):
         lib.la_backward_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
         lib.la_backward.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, f32, p, p, p, p, p, i64, i64, i64,
                                     i64, i64, i32, p, sz, p]
-        for name in ("la_initial_state", "la_workspace_size", "la_forward", "la_step",
+        for name in ("la_initial_state", "la_workspace_size", "la_forward", "la_forward_noalloc", "la_step",
                      "la_gated_workspace_size", "la_gated_forward", "la_gated_step",
                      "la_delta_forward", "la_backward_workspace_size", "la_backward"):
             getattr(lib, name).restype = ctypes.c_int
@@ -268,6 +273,23 @@ def la_forward(q, k, v, mask=None, state=None, causal=True, feature_map="elu_plu
     ``state_out``: optional (kv, k) buffers for the final state (may be ``state``
     itself for in-place streaming).  Returns ``out`` or ``(out, (kv, k))``.
     """
+    return _forward(q, k, v, mask, state, causal, feature_map, use_normalizer, eps, return_state, out,
+                    state_out, workspace, False)
+
+
+def la_forward_noalloc(q, k, v, mask=None, state=None, causal=True, feature_map="elu_plus_one",
+                       use_normalizer=True, eps=1e-6, return_state=False, out=None, state_out=None):
+    """:func:`la_forward` through the C ABI's allocation-free entry point: the
+    library uses its own per-GPU scratch array instead of a workspace.  The
+    C entry point allocates nothing; this wrapper still allocates the outputs
+    it is not given and the copies it makes (a converted mask, contiguous
+    inputs)."""
+    return _forward(q, k, v, mask, state, causal, feature_map, use_normalizer, eps, return_state, out,
+                    state_out, None, True)
+
+
+def _forward(q, k, v, mask, state, causal, feature_map, use_normalizer, eps, return_state, out,
+             state_out, workspace, noalloc):
     _need_cuda(q, k, v)
     dev = q.device
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -294,12 +316,18 @@ def la_forward(q, k, v, mask=None, state=None, causal=True, feature_map="elu_plu
         else:
             s_out_kv = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
             s_out_k = torch.empty((B, H, Dk), dtype=torch.float32, device=dev) if norm else None
-    ws_bytes = la_workspace_size(B, T, H, Dk, Dv, q.dtype, causal) if q.dtype in _DT else 0
-    ws, wsb = _workspace(workspace, ws_bytes, dev)
-    _check(lib.la_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(s_in_kv), _ptr(s_in_k),
-                          _ptr(s_out_kv), _ptr(s_out_k), int(bool(causal)), _FM[feature_map],
-                          int(norm), float(eps), _ptr(out), B, T, H, Dk, Dv,
-                          _dtype_code(q), _ptr(ws), wsb, _stream(dev)), "la_forward")
+    if noalloc:
+        _check(lib.la_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(s_in_kv), _ptr(s_in_k),
+                                      _ptr(s_out_kv), _ptr(s_out_k), int(bool(causal)), _FM[feature_map],
+                                      int(norm), float(eps), _ptr(out), B, T, H, Dk, Dv,
+                                      _dtype_code(q), _stream(dev)), "la_forward_noalloc")
+    else:
+        ws_bytes = la_workspace_size(B, T, H, Dk, Dv, q.dtype, causal) if q.dtype in _DT else 0
+        ws, wsb = _workspace(workspace, ws_bytes, dev)
+        _check(lib.la_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(s_in_kv), _ptr(s_in_k),
+                              _ptr(s_out_kv), _ptr(s_out_k), int(bool(causal)), _FM[feature_map],
+                              int(norm), float(eps), _ptr(out), B, T, H, Dk, Dv,
+                              _dtype_code(q), _ptr(ws), wsb, _stream(dev)), "la_forward")
     if return_state and causal:
         return out, (s_out_kv, s_out_k)
     return out

@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "liblinattn.h"
 #include "la_launch.hpp"
 
@@ -59,11 +61,14 @@ bool overlap(Range a, Range b) {
 }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Split of a causal sequence into segments of chunks (shape-only).
+// Split of a causal sequence into segments of chunks (shape-only).  `cap`
+// bounds the workspace a split may use (bytes; SIZE_MAX = unbounded): with a
+// smaller bound the sequence is cut into fewer, longer segments, down to one
+// segment (no workspace).  `slot` is the bytes of one segment's state.
 struct CausalPlan {
   int64_t nchunks, nseg, seg_chunks;
 };
-CausalPlan plan_causal(int64_t U, int64_t T) {
+CausalPlan plan_causal(int64_t U, int64_t T, int64_t slot = 0, size_t cap = SIZE_MAX) {
   CausalPlan p;
   p.nchunks = ceil_div(T, kChunk);
   p.nseg = 1;
@@ -71,21 +76,37 @@ CausalPlan plan_causal(int64_t U, int64_t T) {
   if (U < kTargetGroups && p.nchunks > 1) {
     int64_t want = ceil_div(kTargetGroups, U);
     if (want > p.nchunks) want = p.nchunks;
-    p.seg_chunks = ceil_div(p.nchunks, want);
-    p.nseg = ceil_div(p.nchunks, p.seg_chunks);
+    if (cap != SIZE_MAX) {
+      const int64_t fit = (int64_t)(cap / (size_t)(U * slot));
+      if (want > fit) want = fit;
+    }
+    if (want >= 2) {
+      p.seg_chunks = ceil_div(p.nchunks, want);
+      p.nseg = ceil_div(p.nchunks, p.seg_chunks);
+    }
   }
   return p;
 }
 
+// Split of a non-causal reduction over T (shape-only), bounded like
+// plan_causal; nsplit = 0 when not even one slot per unit fits `cap`.
 struct NonCausalPlan {
   int64_t nchunks, nsplit, split_chunks;
 };
-NonCausalPlan plan_noncausal(int64_t U, int64_t T) {
+NonCausalPlan plan_noncausal(int64_t U, int64_t T, int64_t slot = 0, size_t cap = SIZE_MAX) {
   NonCausalPlan p;
   p.nchunks = ceil_div(T, kChunk);
   int64_t want = ceil_div(kTargetGroups, U);
   if (want > p.nchunks) want = p.nchunks;
   if (want < 1) want = 1;
+  if (cap != SIZE_MAX) {
+    const int64_t fit = (int64_t)(cap / (size_t)(U * slot));
+    if (want > fit) want = fit;
+    if (want < 1) {
+      p.nsplit = p.split_chunks = 0;
+      return p;
+    }
+  }
   p.split_chunks = ceil_div(p.nchunks, want);
   p.nsplit = ceil_div(p.nchunks, p.split_chunks);
   return p;
@@ -93,16 +114,18 @@ NonCausalPlan plan_noncausal(int64_t U, int64_t T) {
 
 int64_t state_elems(int64_t D, int norm) { return D * D + (norm ? D : 0); }
 
-size_t forward_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t D, int causal, int norm) {
+size_t forward_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t D, int causal, int norm,
+                        size_t cap = SIZE_MAX) {
   const int64_t U = B * H;
   if (U == 0 || T == 0) return 0;
+  const int64_t slot = state_elems(D, norm) * 4;
   if (causal) {
-    CausalPlan p = plan_causal(U, T);
+    CausalPlan p = plan_causal(U, T, slot, cap);
     if (p.nseg <= 1) return 0;
-    return (size_t)(U * p.nseg * state_elems(D, norm) * 4);
+    return (size_t)(U * p.nseg * slot);
   }
-  NonCausalPlan p = plan_noncausal(U, T);
-  return (size_t)(U * p.nsplit * state_elems(D, norm) * 4);
+  NonCausalPlan p = plan_noncausal(U, T, slot, cap);
+  return (size_t)(U * p.nsplit * slot);
 }
 
 static_assert(la::kIoF32 == LA_DT_F32 && la::kIoBF16 == LA_DT_BF16 && la::kIoF16 == LA_DT_F16,
@@ -166,13 +189,50 @@ LA_EXPORT la_status la_workspace_size(int64_t B, int64_t T, int64_t H, int64_t D
   return ok();
 }
 
-LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, const uint8_t* mask,
-                               const float* state_in_kv, const float* state_in_k,
-                               float* state_out_kv, float* state_out_k, int32_t causal,
-                               int32_t feature_map, int32_t use_normalizer, float eps, void* out,
-                               int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
-                               int32_t dtype, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+namespace {
+// The allocation-free variant's scratch: one array per GPU the library runs
+// on, held until the process ends.  Host code never uses the array's name as
+// an address: scratch_for_stream() looks up each device's own copy once
+// (hipGetSymbolAddress, with that device current) and keeps it.
+constexpr size_t kScratchBytes = LA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+la_status scratch_for_stream(hipStream_t st, void** ptr) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return device_status(e, "la_forward_noalloc (hipGetDevice)");
+  if (st) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(st, &sd);
+    if (e != hipSuccess) return device_status(e, "la_forward_noalloc (hipStreamGetDevice)");
+    if ((int)sd != cur)
+      return fail(LA_ERR_DEVICE, "la_forward_noalloc: the stream belongs to device %d, the current device is %d",
+                  (int)sd, cur);
+  }
+  if (cur < 0 || cur >= kMaxDevices) return fail(LA_ERR_DEVICE, "device index %d out of range", cur);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[cur]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_status(e, "la_forward_noalloc (hipGetSymbolAddress)");
+    if (!p) return fail(LA_ERR_DEVICE, "la_forward_noalloc: no address for the scratch array");
+    g_scratch_ptr[cur] = p;
+  }
+  *ptr = g_scratch_ptr[cur];
+  return LA_OK;
+}
+
+// la_forward; with noalloc the workspace is the device's scratch array and
+// the split plans are bounded by its size.
+la_status forward_impl(const void* q, const void* k, const void* v, const uint8_t* mask,
+                       const float* state_in_kv, const float* state_in_k, float* state_out_kv,
+                       float* state_out_k, int32_t causal, int32_t feature_map, int32_t use_normalizer,
+                       float eps, void* out, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                       int32_t dtype, void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
+  const size_t cap = noalloc ? kScratchBytes : SIZE_MAX;
   la_status s = check_common(B, T, H, Dk, Dv, dtype);
   if (s != LA_OK) return s;
   if (feature_map != LA_FM_ELU_PLUS_ONE && feature_map != LA_FM_RELU_EPS)
@@ -207,7 +267,14 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
   const Range rm = range(mask, B * T);
   const Range rsi = range(state_in_kv, U * D * D * 4), rzi = range(state_in_k, U * D * 4);
   const Range rso = range(state_out_kv, U * D * D * 4), rzo = range(state_out_k, U * D * 4);
-  const size_t need = forward_ws_bytes(B, T, H, D, causal != 0, norm);
+  const size_t need = forward_ws_bytes(B, T, H, D, causal != 0, norm, cap);
+  const int64_t slot = state_elems(D, norm) * 4;
+  if (noalloc && work && !causal && plan_noncausal(U, T, slot, cap).nsplit == 0)
+    return fail(LA_ERR_WORKSPACE,
+                "la_forward_noalloc: the non-causal sums of %lld (batch, head) units need %lld bytes, "
+                "more than the %zu-byte scratch",
+                (long long)U, (long long)(U * slot), kScratchBytes);
+  if (noalloc) workspace = nullptr;  // the scratch array, looked up below
   const Range rw = range(workspace, (int64_t)need);
   if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(ro, rm) || overlap(ro, rsi) ||
       overlap(ro, rzi) || overlap(ro, rso) || overlap(ro, rzo))
@@ -225,11 +292,15 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
   if (overlap(rw, rq) || overlap(rw, rk) || overlap(rw, rv) || overlap(rw, rm) || overlap(rw, rsi) ||
       overlap(rw, rzi))
     return fail(LA_ERR_BAD_ARG, "workspace overlaps an input");
-  if (need > 0 && (!workspace || workspace_bytes < need))
+  if (!noalloc && need > 0 && (!workspace || workspace_bytes < need))
     return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
 
   hipStream_t st = (hipStream_t)stream;
+  if (noalloc && need > 0) {
+    s = scratch_for_stream(st, &workspace);
+    if (s != LA_OK) return s;
+  }
   const int Di = (int)D;
   hipError_t e = hipSuccess;
 
@@ -261,7 +332,7 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
   const int64_t SE = D * D, ZE = D;
 
   if (causal) {
-    CausalPlan p = plan_causal(U, T);
+    CausalPlan p = plan_causal(U, T, slot, cap);
     if (p.nseg == 1) {
       a.s_in = state_in_kv;
       a.z_in = state_in_k;
@@ -319,7 +390,7 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
   }
 
   // non-causal: split reduction -> fixed-order sum -> readout
-  NonCausalPlan p = plan_noncausal(U, T);
+  NonCausalPlan p = plan_noncausal(U, T, slot, cap);
   float* ws_s = (float*)workspace;
   float* ws_z = norm ? ws_s + U * p.nsplit * SE : nullptr;
   la::ChunkArgs pr = a;
@@ -353,6 +424,28 @@ LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, cons
     e = la::launch_apply(dtype, Di, feature_map, norm, pa, (int)(U * pa.seg_count), st);
   }
   return device_status(e, "la_forward (non-causal)");
+}
+}  // namespace
+
+LA_EXPORT la_status la_forward(const void* q, const void* k, const void* v, const uint8_t* mask,
+                               const float* state_in_kv, const float* state_in_k,
+                               float* state_out_kv, float* state_out_k, int32_t causal,
+                               int32_t feature_map, int32_t use_normalizer, float eps, void* out,
+                               int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                               int32_t dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return forward_impl(q, k, v, mask, state_in_kv, state_in_k, state_out_kv, state_out_k, causal, feature_map,
+                      use_normalizer, eps, out, B, T, H, Dk, Dv, dtype, workspace, workspace_bytes, stream, false);
+}
+
+LA_EXPORT la_status la_forward_noalloc(const void* q, const void* k, const void* v, const uint8_t* mask,
+                                       const float* state_in_kv, const float* state_in_k,
+                                       float* state_out_kv, float* state_out_k, int32_t causal,
+                                       int32_t feature_map, int32_t use_normalizer, float eps, void* out,
+                                       int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
+                                       int32_t dtype, void* stream) {
+  return forward_impl(q, k, v, mask, state_in_kv, state_in_k, state_out_kv, state_out_k, causal, feature_map,
+                      use_normalizer, eps, out, B, T, H, Dk, Dv, dtype, nullptr, 0, stream, true);
 }
 
 LA_EXPORT la_status la_step(const void* q, const void* k, const void* v, const uint8_t* mask,

@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert sorted(la.EXPORTED_SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -284,3 +284,28 @@ def test_binding_buffer_checks_on_host_tensors():
         la._workspace(torch.empty(8, dtype=torch.uint8), 16, "cpu")
     ws, n = la._workspace(torch.empty(4, dtype=torch.float32), 16, "cpu")
     assert n == 16
+
+
+def test_forward_noalloc_host_checks(lib):
+    """The allocation-free forward validates like la_forward, and refuses a
+    non-causal call whose sums exceed its scratch array, all before any HIP
+    call (the pointers here are fake)."""
+    f = lambda a: None if a is None else fake(a)
+
+    def g(**kw):
+        a = dict(q=0x10000, k=0x20000000, v=0x40000000, mask=None, sik=None, sikk=None, sok=None, sokk=None,
+                 causal=1, fm=0, norm=1, eps=1e-6, out=0x60000000, B=2, T=100, H=4, Dk=64, Dv=64, dtype=1)
+        a.update(kw)
+        return lib.la_forward_noalloc(f(a["q"]), f(a["k"]), f(a["v"]), f(a["mask"]), f(a["sik"]), f(a["sikk"]),
+                                      f(a["sok"]), f(a["sokk"]), a["causal"], a["fm"], a["norm"], a["eps"],
+                                      f(a["out"]), a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["dtype"], None)
+
+    big = 1 << 40
+    assert g(dtype=7) == DTYPE
+    assert g(q=None) == NULL_ARG
+    assert g(causal=0, sik=big, sikk=2 * big) == STATE
+    assert g(out=0x10000 + 64) == BAD_ARG
+    # 1024 (batch, head) units at Dk = Dv = 128 need 1024 * 66048 bytes > 64 MiB
+    assert g(causal=0, B=8, H=128, T=64, Dk=128, Dv=128, q=1 << 36, k=2 << 36, v=3 << 36,
+             out=4 << 36) == WORKSPACE
+    assert b"scratch" in lib.la_last_error_message()
