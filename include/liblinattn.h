@@ -155,7 +155,8 @@ la_status la_gated_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
  *   past_state (B,Hkv,Dk,Dv) float32 (NULL = zeros); present_state (same shape,
  *   float32) is always written and may alias past_state exactly.
  * scale == 0 means 1/sqrt(Dk).  Hq must be a positive multiple of Hkv
- * (else LA_ERR_SHAPE).  A per-dim decay is evaluated chunk-parallel with keys
+ * (else LA_ERR_SHAPE); any multiple is supported, multi-query (Hkv = 1)
+ * included.  A per-dim decay is evaluated chunk-parallel with keys
  * rescaled inside blocks of 32 tokens: decays summing below about -87 over
  * one such block (per dimension) overflow.  fp32 inputs at Dk = 128 with a
  * per-dim decay and T > 1 (whose chunk tiles exceed the LDS) run the T == 1

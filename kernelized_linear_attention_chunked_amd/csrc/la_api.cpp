@@ -543,17 +543,20 @@ la_status check_gated(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,
   if (Hq % Hkv != 0)
     return fail(LA_ERR_SHAPE, "q_num_heads (%lld) must be a positive multiple of kv_num_heads (%lld)",
                 (long long)Hq, (long long)Hkv);
-  const int64_t G = Hq / Hkv;
   if (Dk != Dv || !head_size_ok(Dk))
     return fail(LA_ERR_UNSUPPORTED, "head sizes Dk=%lld Dv=%lld: only Dk == Dv in {32,64,128}",
                 (long long)Dk, (long long)Dv);
-  if (G != 1 && G != 2 && G != 4 && G != 8)
-    return fail(LA_ERR_UNSUPPORTED, "q heads per kv head = %lld: supported 1, 2, 4, 8", (long long)G);
-  if (B * Hkv > (int64_t)1 << 30 || T > ((int64_t)1 << 31) - kChunk || Hq * Dk > (int64_t)1 << 30)
+  if (B * Hq > (int64_t)1 << 30 || T > ((int64_t)1 << 31) - kChunk || Hq * Dk > (int64_t)1 << 30)
     return fail(LA_ERR_SHAPE, "sizes exceed the 32-bit index ranges of the kernels");
   return LA_OK;
 }
 }  // namespace
+
+// The chunk kernels take 1, 2, 4 or 8 query heads per workgroup: a kv head
+// with G query heads runs as G / head_tile(G) workgroups (query-head groups)
+// of head_tile(G) heads each, every one of them computing the kv head's
+// recurrence and the first writing the state.
+int64_t head_tile(int64_t G) { return G % 8 == 0 ? 8 : (G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1)); }
 
 hipError_t launch_step(const void* q, const void* k, const void* v, const void* decay, bool per_dim,
                        const float* past_state, float* present_state, void* out, int64_t U,
@@ -676,9 +679,14 @@ la_status gated_forward(const void* q, const void* k, const void* v, const void*
     }
     return device_status(e, "la_gated_forward (token by token)");
   }
+  const int64_t GW = head_tile(G), HS = G / GW;  // heads per workgroup, query-head groups
+  // the output passes run HS workgroups per (unit, segment); the state pass one
   auto launch = [&](int mode, const la::GatedArgs& ga, int grid) {
-    return per_dim ? la::launch_gated_pd(mode, dtype, (int)D, (int)G, ga, grid, st)
-                   : la::launch_gated(mode, dtype, (int)D, (int)G, ga, grid, st);
+    la::GatedArgs g2 = ga;
+    g2.hsplit = mode == la::kModeCausal ? (int32_t)HS : 1;
+    const int gr = mode == la::kModeCausal ? (int)(grid * HS) : grid;
+    return per_dim ? la::launch_gated_pd(mode, dtype, (int)D, (int)GW, g2, gr, st)
+                   : la::launch_gated(mode, dtype, (int)D, (int)GW, g2, gr, st);
   };
   la::GatedArgs a;
   memset(&a, 0, sizeof(a));
@@ -863,6 +871,7 @@ LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v
     return device_status(e, "la_delta_forward (token by token)");
   }
   la::DeltaArgs a;
+  memset(&a, 0, sizeof(a));
   a.q = q;
   a.k = k;
   a.v = v;
@@ -878,7 +887,8 @@ LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v
   a.beta_heads = (int32_t)bh;
   a.scale = scale;
   const int kind = decay == nullptr ? 0 : (per_dim ? 2 : 1);
-  e = la::launch_delta(dtype, (int)D, (int)G, kind, a, st);
+  a.hsplit = (int32_t)(G / head_tile(G));
+  e = la::launch_delta(dtype, (int)D, (int)head_tile(G), kind, a, st);
   return device_status(e, "la_delta_forward");
 }
 

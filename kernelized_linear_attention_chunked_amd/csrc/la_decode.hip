@@ -135,8 +135,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 // consecutive state columns, issues all of its state loads first, updates in
 // registers, writes back, and keeps partial readouts of every query head; the
 // row groups are summed through LDS.  q and k are staged in LDS as fp32.
-template <typename DT, int D, int G, bool NTMP, bool PD>
+template <typename DT, int D, int G, bool NTMP, bool PD, bool MP>
 __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArgs a) {
+  // G query heads per readout pass; MP: a.heads / G passes (a kv head with
+  // more heads, or a head count that is not a power of two), else one
   constexpr int C4 = D / 4;          // float4 columns per state row
   constexpr int RG = kThreads / C4;  // row groups
   constexpr int RPT = D / RG;        // rows per thread
@@ -151,6 +153,8 @@ __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArg
   const int b = u / a.Hkv, j = u % a.Hkv;
   const int c4 = tid % C4, rg = tid / C4;
   const int64_t SE = (int64_t)D * D;
+  const int NPASS = MP ? a.heads / G : 1;
+  const int GT = G * NPASS;  // query heads of the kv head
 
   f32x4_t sv[RPT];
   if (live && a.s_in) {
@@ -164,12 +168,17 @@ __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArg
 #pragma unroll
     for (int r = 0; r < RPT; ++r) sv[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const int QW = a.Hkv * G * D;  // query row width
+  const int QW = a.Hkv * GT * D;  // query row width
   // row of batch b in the token tensors, and (row, kv head) index
   const int64_t br = (int64_t)b * (a.batch_rows > 1 ? a.batch_rows : 1), uh = br * a.Hkv + j;
-  const DT* qp = (const DT*)a.q + br * QW + (int64_t)j * G * D;
+  const DT* qp = (const DT*)a.q + br * QW + (int64_t)j * GT * D;
   const DT* kp = (const DT*)a.k + uh * D;
   const DT* vp = (const DT*)a.v + uh * D;
+  // fp32 copies of the query rows of pass p
+  auto load_q = [&](int p) {
+    const DT* qpp = qp + (int64_t)p * G * D;
+    for (int i = tid; i < G * D; i += kThreads) fq[ul][i / D][i % D] = load_elem<DT>(qpp, i);
+  };
   float v4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) v4[i] = live ? load_elem<DT>(vp, 4 * c4 + i) : 0.f;
@@ -178,56 +187,67 @@ __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArg
     for (int i = tid; i < D; i += kThreads) fk[ul][i] = load_elem<DT>(kp, i);
     if constexpr (PD)  // per-key-dim decay: row dk of S scales by exp(g[dk])
       for (int i = tid; i < D; i += kThreads) fe[ul][i] = __expf(load_elem<DT>((const DT*)a.decay + uh * D, i));
-    for (int i = tid; i < G * D; i += kThreads) fq[ul][i / D][i % D] = load_elem<DT>(qp, i);
+    load_q(0);
   }
   __syncthreads();
-  if (live) {
-    float acc[G][4];
+  for (int p = 0; p < NPASS; ++p) {
+    if (p > 0) {
+      // the previous pass read fq before its last barrier
+      if (live) load_q(p);
+      __syncthreads();
+    }
+    if (live) {
+      float acc[G][4];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[h][i] = 0.f;
+        for (int i = 0; i < 4; ++i) acc[h][i] = 0.f;
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      const int dk = rg + RG * r;
-      const float f = fk[ul][dk];
-      const float er = PD ? fe[ul][dk] : e;
+      for (int r = 0; r < RPT; ++r) {
+        const int dk = rg + RG * r;
+        if (p == 0) {
+          const float f = fk[ul][dk];
+          const float er = PD ? fe[ul][dk] : e;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[r][i] = fmaf(f, v4[i], er * sv[r][i]);
+          for (int i = 0; i < 4; ++i) sv[r][i] = fmaf(f, v4[i], er * sv[r][i]);
+        }
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float g = fq[ul][h][dk];
+        for (int h = 0; h < G; ++h) {
+          const float g = fq[ul][h][dk];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[h][i] = fmaf(g, sv[r][i], acc[h][i]);
+          for (int i = 0; i < 4; ++i) acc[h][i] = fmaf(g, sv[r][i], acc[h][i]);
+        }
       }
+      if (p == 0) {
+        float* So = a.s_out + (int64_t)u * SE;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+          f32x4_t* ptr = (f32x4_t*)(So + (rg + RG * r) * D + 4 * c4);
+          if constexpr (NTMP)
+            __builtin_nontemporal_store(sv[r], ptr);
+          else
+            *ptr = sv[r];
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[ul][h][rg][4 * c4 + i] = acc[h][i];
     }
-    float* So = a.s_out + (int64_t)u * SE;
+    __syncthreads();
+    if (live) {
+      DT* op = (DT*)a.out + br * QW + (int64_t)j * GT * D + (int64_t)p * G * D;
+      for (int i = tid; i < G * D; i += kThreads) {
+        const int h = i / D, d = i % D;
+        float y = 0.f;
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      f32x4_t* p = (f32x4_t*)(So + (rg + RG * r) * D + 4 * c4);
-      if constexpr (NTMP)
-        __builtin_nontemporal_store(sv[r], p);
-      else
-        *p = sv[r];
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part[ul][h][rg][4 * c4 + i] = acc[h][i];
-  }
-  __syncthreads();
-  if (live) {
-    DT* op = (DT*)a.out + br * QW + (int64_t)j * G * D;
-    for (int i = tid; i < G * D; i += kThreads) {
-      const int h = i / D, d = i % D;
-      float y = 0.f;
-#pragma unroll
-      for (int g = 0; g < RG; ++g) y += part[ul][h][g][d];
-      y *= a.scale;
-      if constexpr (std::is_same_v<DT, uint16_t>)
-        op[i] = (uint16_t)f32_to_bf16_bits(y);
-      else
-        op[i] = (DT)y;
+        for (int g = 0; g < RG; ++g) y += part[ul][h][g][d];
+        y *= a.scale;
+        if constexpr (std::is_same_v<DT, uint16_t>)
+          op[i] = (uint16_t)f32_to_bf16_bits(y);
+        else
+          op[i] = (DT)y;
+      }
     }
   }
 }
@@ -240,8 +260,9 @@ __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArg
 // registers throughout.  Two sums over the rows go through LDS in turn: S'^T k
 // (then u, one value per column), and after the rank-1 update q_h^T S''.  One
 // read and one write of the state, as for the gated step.
-template <typename DT, int D, int G, bool NTMP, int DK>
+template <typename DT, int D, int G, bool NTMP, int DK, bool MP>
 __global__ __launch_bounds__(kDecodeThreads) void delta_step_kernel(GatedStepArgs a) {
+  // G query heads per readout pass; MP: a.heads / G passes, else one
   constexpr int C4 = D / 4;          // float4 columns per state row
   constexpr int RG = kThreads / C4;  // row groups
   constexpr int RPT = D / RG;        // rows per thread
@@ -257,6 +278,8 @@ __global__ __launch_bounds__(kDecodeThreads) void delta_step_kernel(GatedStepArg
   const int b = u / a.Hkv, j = u % a.Hkv;
   const int c4 = tid % C4, rg = tid / C4;
   const int64_t SE = (int64_t)D * D;
+  const int NPASS = MP ? a.heads / G : 1;
+  const int GT = G * NPASS;  // query heads of the kv head
 
   f32x4_t sv[RPT];
   if (live && a.s_in) {
@@ -270,12 +293,16 @@ __global__ __launch_bounds__(kDecodeThreads) void delta_step_kernel(GatedStepArg
 #pragma unroll
     for (int r = 0; r < RPT; ++r) sv[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const int QW = a.Hkv * G * D;  // query row width
+  const int QW = a.Hkv * GT * D;  // query row width
   // row of batch b in the token tensors, and (row, kv head) index
   const int64_t br = (int64_t)b * (a.batch_rows > 1 ? a.batch_rows : 1), uh = br * a.Hkv + j;
-  const DT* qp = (const DT*)a.q + br * QW + (int64_t)j * G * D;
+  const DT* qp = (const DT*)a.q + br * QW + (int64_t)j * GT * D;
   const DT* kp = (const DT*)a.k + uh * D;
   const DT* vp = (const DT*)a.v + uh * D;
+  auto load_q = [&](int p) {
+    const DT* qpp = qp + (int64_t)p * G * D;
+    for (int i = tid; i < G * D; i += kThreads) fq[ul][i / D][i % D] = load_elem<DT>(qpp, i);
+  };
   const float e = (live && DK == 1) ? __expf(load_elem<DT>((const DT*)a.decay, uh)) : 1.f;
   const float be = live ? load_elem<DT>((const DT*)a.beta, br * a.beta_heads + (a.beta_heads > 1 ? j : 0)) : 0.f;
   const float vc = (live && tid < D) ? load_elem<DT>(vp, tid) : 0.f;  // v of column tid
@@ -283,7 +310,7 @@ __global__ __launch_bounds__(kDecodeThreads) void delta_step_kernel(GatedStepArg
     for (int i = tid; i < D; i += kThreads) fk[ul][i] = load_elem<DT>(kp, i);
     if constexpr (DK == 2)  // per-key-dim decay: row dk of S scales by exp(g[dk])
       for (int i = tid; i < D; i += kThreads) fe[ul][i] = __expf(load_elem<DT>((const DT*)a.decay + uh * D, i));
-    for (int i = tid; i < G * D; i += kThreads) fq[ul][i / D][i % D] = load_elem<DT>(qp, i);
+    load_q(0);
   }
   __syncthreads();
   // S' = E S, and the thread's part of S'^T k
@@ -312,56 +339,71 @@ __global__ __launch_bounds__(kDecodeThreads) void delta_step_kernel(GatedStepArg
     fu[ul][tid] = be * (vc - w);
   }
   __syncthreads();
-  // S'' = S' + k u^T, written back; the threads' parts of q_h^T S''
-  if (live) {
-    float u4[4];
+  // S'' = S' + k u^T, written back; the threads' parts of q_h^T S'', G heads
+  // per pass
+  for (int p = 0; p < NPASS; ++p) {
+    if (p > 0) {
+      // the previous pass read fq before its last barrier
+      if (live) load_q(p);
+      __syncthreads();
+    }
+    if (live) {
+      float acc[G][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) u4[i] = fu[ul][4 * c4 + i];
-    float acc[G][4];
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+        for (int i = 0; i < 4; ++i) acc[h][i] = 0.f;
+      if (p == 0) {
+        float u4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[h][i] = 0.f;
+        for (int i = 0; i < 4; ++i) u4[i] = fu[ul][4 * c4 + i];
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      const int dk = rg + RG * r;
-      const float f = fk[ul][dk];
+        for (int r = 0; r < RPT; ++r) {
+          const float f = fk[ul][rg + RG * r];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[r][i] = fmaf(f, u4[i], sv[r][i]);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float g = fq[ul][h][dk];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[h][i] = fmaf(g, sv[r][i], acc[h][i]);
+          for (int i = 0; i < 4; ++i) sv[r][i] = fmaf(f, u4[i], sv[r][i]);
+        }
       }
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        const int dk = rg + RG * r;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float g = fq[ul][h][dk];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[h][i] = fmaf(g, sv[r][i], acc[h][i]);
+        }
+      }
+      if (p == 0) {
+        float* So = a.s_out + (int64_t)u * SE;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+          f32x4_t* ptr = (f32x4_t*)(So + (rg + RG * r) * D + 4 * c4);
+          if constexpr (NTMP)
+            __builtin_nontemporal_store(sv[r], ptr);
+          else
+            *ptr = sv[r];
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[ul][h][rg][4 * c4 + i] = acc[h][i];
     }
-    float* So = a.s_out + (int64_t)u * SE;
+    __syncthreads();
+    if (live) {
+      DT* op = (DT*)a.out + br * QW + (int64_t)j * GT * D + (int64_t)p * G * D;
+      for (int i = tid; i < G * D; i += kThreads) {
+        const int h = i / D, d = i % D;
+        float y = 0.f;
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      f32x4_t* p = (f32x4_t*)(So + (rg + RG * r) * D + 4 * c4);
-      if constexpr (NTMP)
-        __builtin_nontemporal_store(sv[r], p);
-      else
-        *p = sv[r];
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part[ul][h][rg][4 * c4 + i] = acc[h][i];
-  }
-  __syncthreads();
-  if (live) {
-    DT* op = (DT*)a.out + br * QW + (int64_t)j * G * D;
-    for (int i = tid; i < G * D; i += kThreads) {
-      const int h = i / D, d = i % D;
-      float y = 0.f;
-#pragma unroll
-      for (int g = 0; g < RG; ++g) y += part[ul][h][g][d];
-      y *= a.scale;
-      if constexpr (std::is_same_v<DT, uint16_t>)
-        op[i] = (uint16_t)f32_to_bf16_bits(y);
-      else
-        op[i] = (DT)y;
+        for (int g = 0; g < RG; ++g) y += part[ul][h][g][d];
+        y *= a.scale;
+        if constexpr (std::is_same_v<DT, uint16_t>)
+          op[i] = (uint16_t)f32_to_bf16_bits(y);
+        else
+          op[i] = (DT)y;
+      }
     }
   }
 }
@@ -420,31 +462,39 @@ hipError_t launch_decode(int io, int D, int fm, int norm, const DecodeArgs& a, i
   }
 }
 
-template <typename DT, int D, int G, bool PD>
+// Query heads per readout pass for a kv head with G of them: the largest of
+// 8, 4, 2, 1 that divides G.
+static int head_tile(int G) { return G % 8 == 0 ? 8 : (G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1)); }
+
+template <typename DT, int D, int G, bool PD, bool MP>
 static void launch_gsp(const GatedStepArgs& a, hipStream_t st) {
   const bool ntmp = (int64_t)a.units * D * D * 4 >= ((int64_t)256 << 20);
   const int grid = (a.units + kDecodeUnits - 1) / kDecodeUnits;
   if (ntmp)
-    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, true, PD>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, true, PD, MP>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, false, PD>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, false, PD, MP>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
 }
 
-template <typename DT, int D, int G>
+template <typename DT, int D, int G, bool MP>
 static void launch_gs(const GatedStepArgs& a, hipStream_t st) {
   if (a.per_dim && a.decay)
-    launch_gsp<DT, D, G, true>(a, st);
+    launch_gsp<DT, D, G, true, MP>(a, st);
   else
-    launch_gsp<DT, D, G, false>(a, st);
+    launch_gsp<DT, D, G, false, MP>(a, st);
 }
 
 template <typename DT, int D>
-static void launch_gs_g(int G, const GatedStepArgs& a, hipStream_t st) {
-  switch (G) {
-    case 1: launch_gs<DT, D, 1>(a, st); break;
-    case 2: launch_gs<DT, D, 2>(a, st); break;
-    case 4: launch_gs<DT, D, 4>(a, st); break;
-    default: launch_gs<DT, D, 8>(a, st); break;
+static void launch_gs_g(int G, const GatedStepArgs& a0, hipStream_t st) {
+  GatedStepArgs a = a0;
+  a.heads = G;
+  const int gp = head_tile(G);
+  const bool mp = gp != G;
+  switch (gp) {
+    case 1: mp ? launch_gs<DT, D, 1, true>(a, st) : launch_gs<DT, D, 1, false>(a, st); break;
+    case 2: mp ? launch_gs<DT, D, 2, true>(a, st) : launch_gs<DT, D, 2, false>(a, st); break;
+    case 4: mp ? launch_gs<DT, D, 4, true>(a, st) : launch_gs<DT, D, 4, false>(a, st); break;
+    default: mp ? launch_gs<DT, D, 8, true>(a, st) : launch_gs<DT, D, 8, false>(a, st); break;
   }
 }
 
@@ -467,33 +517,37 @@ hipError_t launch_gated_step(int io, int D, int G, const GatedStepArgs& a, hipSt
   return hipGetLastError();
 }
 
-template <typename DT, int D, int G, int DK>
+template <typename DT, int D, int G, int DK, bool MP>
 static void launch_dsp(const GatedStepArgs& a, hipStream_t st) {
   const bool ntmp = (int64_t)a.units * D * D * 4 >= ((int64_t)256 << 20);
   const int grid = (a.units + kDecodeUnits - 1) / kDecodeUnits;
   if (ntmp)
-    hipLaunchKernelGGL((delta_step_kernel<DT, D, G, true, DK>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    hipLaunchKernelGGL((delta_step_kernel<DT, D, G, true, DK, MP>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((delta_step_kernel<DT, D, G, false, DK>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    hipLaunchKernelGGL((delta_step_kernel<DT, D, G, false, DK, MP>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
 }
 
-template <typename DT, int D, int G>
+template <typename DT, int D, int G, bool MP>
 static void launch_ds(const GatedStepArgs& a, hipStream_t st) {
   if (!a.decay)
-    launch_dsp<DT, D, G, 0>(a, st);
+    launch_dsp<DT, D, G, 0, MP>(a, st);
   else if (a.per_dim)
-    launch_dsp<DT, D, G, 2>(a, st);
+    launch_dsp<DT, D, G, 2, MP>(a, st);
   else
-    launch_dsp<DT, D, G, 1>(a, st);
+    launch_dsp<DT, D, G, 1, MP>(a, st);
 }
 
 template <typename DT, int D>
-static void launch_ds_g(int G, const GatedStepArgs& a, hipStream_t st) {
-  switch (G) {
-    case 1: launch_ds<DT, D, 1>(a, st); break;
-    case 2: launch_ds<DT, D, 2>(a, st); break;
-    case 4: launch_ds<DT, D, 4>(a, st); break;
-    default: launch_ds<DT, D, 8>(a, st); break;
+static void launch_ds_g(int G, const GatedStepArgs& a0, hipStream_t st) {
+  GatedStepArgs a = a0;
+  a.heads = G;
+  const int gp = head_tile(G);
+  const bool mp = gp != G;
+  switch (gp) {
+    case 1: mp ? launch_ds<DT, D, 1, true>(a, st) : launch_ds<DT, D, 1, false>(a, st); break;
+    case 2: mp ? launch_ds<DT, D, 2, true>(a, st) : launch_ds<DT, D, 2, false>(a, st); break;
+    case 4: mp ? launch_ds<DT, D, 4, true>(a, st) : launch_ds<DT, D, 4, false>(a, st); break;
+    default: mp ? launch_ds<DT, D, 8, true>(a, st) : launch_ds<DT, D, 8, false>(a, st); break;
   }
 }
 

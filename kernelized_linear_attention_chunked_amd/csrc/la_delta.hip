@@ -119,13 +119,16 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   // the two waves of a row block sit on different SIMDs (w % 4)
   const int hp = P == 2 ? (w & 1) : 0, wr = P == 2 ? (w >> 1) : w;
   int l = tid & 63, lr = l & 15, lg = l >> 4;
-  const int u = blockIdx.x;
+  // query-head group hg of hs (the group's heads are G of the kv head's G * hs)
+  const int hs = a.hsplit > 1 ? a.hsplit : 1;
+  const int hg = blockIdx.x % hs;
+  const int u = blockIdx.x / hs;
   const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
   const int b = u / Hkv, j = u % Hkv;
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int QS = Hq * D, KS = Hkv * D;
-  const IT* qb = (const IT*)a.q + (int64_t)b * T * QS + (int64_t)(j * G) * D;
-  IT* ob = (IT*)a.out + (int64_t)b * T * QS + (int64_t)(j * G) * D;
+  const IT* qb = (const IT*)a.q + (int64_t)b * T * QS + (int64_t)(j * G * hs + hg * G) * D;
+  IT* ob = (IT*)a.out + (int64_t)b * T * QS + (int64_t)(j * G * hs + hg * G) * D;
   const IT* kb = (const IT*)a.k + (int64_t)b * T * KS + (int64_t)j * D;
   const IT* vb = (const IT*)a.v + (int64_t)b * T * KS + (int64_t)j * D;
   const IT* gb = DK == 2 ? (const IT*)a.decay + (int64_t)b * T * KS + (int64_t)j * D
@@ -959,7 +962,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     __syncthreads();
     write_sb();
   }
-  if (a.s_out) {
+  if (a.s_out && hg == 0) {
     float* sout = a.s_out + (int64_t)u * D * D;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
@@ -980,11 +983,11 @@ template <typename IT, int D, int G, bool FULL>
 static void launch_dg(int dk, const DeltaArgs& a, hipStream_t st) {
   constexpr int NTH = DeltaShape<G>::NTH;
   if (dk == 0)
-    hipLaunchKernelGGL((delta_kernel<IT, D, G, 0>), dim3(a.units), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((delta_kernel<IT, D, G, 0>), dim3(a.units * (a.hsplit > 1 ? a.hsplit : 1)), dim3(NTH), 0, st, a);
   else if (dk == 1 || !FULL)
-    hipLaunchKernelGGL((delta_kernel<IT, D, G, 1>), dim3(a.units), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((delta_kernel<IT, D, G, 1>), dim3(a.units * (a.hsplit > 1 ? a.hsplit : 1)), dim3(NTH), 0, st, a);
   else if constexpr (FULL)
-    hipLaunchKernelGGL((delta_kernel<IT, D, G, 2>), dim3(a.units), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((delta_kernel<IT, D, G, 2>), dim3(a.units * (a.hsplit > 1 ? a.hsplit : 1)), dim3(NTH), 0, st, a);
 }
 
 template <typename IT, int D, bool FULL>

@@ -104,8 +104,12 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
       lg = l >> 4;
     }
   };
-  const int u = blockIdx.x / a.seg_count;
-  const int s = a.seg_first + blockIdx.x % a.seg_count;
+  // query-head group hg of hs (the group's heads are G of the kv head's G * hs)
+  const int hs = a.hsplit > 1 ? a.hsplit : 1;
+  const int hg = blockIdx.x % hs;
+  const int bid = blockIdx.x / hs;
+  const int u = bid / a.seg_count;
+  const int s = a.seg_first + bid % a.seg_count;
   const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
   const int b = u / Hkv, j = u % Hkv;
   const int nchunks = (T + kChunk - 1) / kChunk;
@@ -118,8 +122,8 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
   const bool rev = a.reverse != 0;
   const int QS = rev ? -QS0 : QS0, KS = rev ? -KS0 : KS0, GS = rev ? -Hkv : Hkv;
   const int64_t row0 = rev ? (int64_t)b * T + (T - 1) : (int64_t)b * T;  // row of token 0
-  const IT* qb = (const IT*)a.q + row0 * QS0 + (int64_t)(j * G) * D;
-  IT* ob = (IT*)a.out + row0 * QS0 + (int64_t)(j * G) * D;
+  const IT* qb = (const IT*)a.q + row0 * QS0 + (int64_t)(j * G * hs + hg * G) * D;
+  IT* ob = (IT*)a.out + row0 * QS0 + (int64_t)(j * G * hs + hg * G) * D;
   const IT* kb = (const IT*)a.k + row0 * KS0 + (int64_t)j * D;
   const IT* vb = (const IT*)a.v + row0 * KS0 + (int64_t)j * D;
   const IT* gb = a.decay ? (const IT*)a.decay + row0 * Hkv + j : nullptr;
@@ -647,7 +651,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
 
   float* sout = nullptr;
   if constexpr (OUT) {
-    if (s == a.nseg_total - 1) sout = a.s_out + u * a.s_out_u;
+    if (s == a.nseg_total - 1 && hg == 0) sout = a.s_out + u * a.s_out_u;
   } else {
     sout = a.s_out + u * a.s_out_u + (s + a.out_slot_off) * a.s_out_s;
     if (tid == 0) a.a_out[(int64_t)u * a.nseg_total + s + a.out_slot_off] = __expf(seg_log);

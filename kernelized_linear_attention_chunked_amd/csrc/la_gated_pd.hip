@@ -106,16 +106,20 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
   // causal work between SIMDs
   const int hp = w >> 2, wr = (w & 4) ? 3 - (w & 3) : (w & 3);
   int l = tid & 63, lr = l & 15, lg = l >> 4;
-  const int u = blockIdx.x / a.seg_count;
-  const int s = a.seg_first + blockIdx.x % a.seg_count;
+  // query-head group hg of hs (the group's heads are G of the kv head's G * hs)
+  const int hs = a.hsplit > 1 ? a.hsplit : 1;
+  const int hg = blockIdx.x % hs;
+  const int bid = blockIdx.x / hs;
+  const int u = bid / a.seg_count;
+  const int s = a.seg_first + bid % a.seg_count;
   const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
   const int b = u / Hkv, j = u % Hkv;
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int c0 = s * a.seg_chunks;
   const int c1 = min(c0 + a.seg_chunks, nchunks);
   const int QS = Hq * D, KS = Hkv * D;  // token strides of q/out and of k/v/decay
-  const IT* qb = (const IT*)a.q + (int64_t)b * T * QS + (int64_t)(j * G) * D;
-  IT* ob = (IT*)a.out + (int64_t)b * T * QS + (int64_t)(j * G) * D;
+  const IT* qb = (const IT*)a.q + (int64_t)b * T * QS + (int64_t)(j * G * hs + hg * G) * D;
+  IT* ob = (IT*)a.out + (int64_t)b * T * QS + (int64_t)(j * G * hs + hg * G) * D;
   const IT* kb = (const IT*)a.k + (int64_t)b * T * KS + (int64_t)j * D;
   const IT* vb = (const IT*)a.v + (int64_t)b * T * KS + (int64_t)j * D;
   const IT* gb = (const IT*)a.decay + (int64_t)b * T * KS + (int64_t)j * D;
@@ -534,7 +538,7 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
 
   float* sout = nullptr;
   if constexpr (OUT) {
-    if (s == a.nseg_total - 1) sout = a.s_out + u * a.s_out_u;
+    if (s == a.nseg_total - 1 && hg == 0) sout = a.s_out + u * a.s_out_u;
   } else {
     sout = a.s_out + u * a.s_out_u + (s + a.out_slot_off) * a.s_out_s;
     if (tid < D) a.a_out[((int64_t)u * a.nseg_total + s + a.out_slot_off) * D + tid] = __expf(seg_log);

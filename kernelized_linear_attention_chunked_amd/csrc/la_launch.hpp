@@ -107,6 +107,11 @@ struct GatedArgs {
   // 1: run in reversed time, token t of the recurrence being row T-1-t of q,
   // k, v, the decay and out (la_gated.hip only; the per-dim kernel takes 0)
   int32_t reverse;
+  // query-head groups (0 or 1: one): a kv head's Hq/Hkv query heads are split
+  // over hsplit workgroups of G heads each (the launcher's G), which all run
+  // the unit's recurrence; group 0 writes the state.  blockIdx = (unit-segment
+  // index) * hsplit + group.  The state pass (kModeState) takes 1.
+  int32_t hsplit;
 };
 hipError_t launch_gated(int mode, int io, int D, int G, const GatedArgs& a, int grid,
                         hipStream_t st);
@@ -124,6 +129,8 @@ struct DeltaArgs {
   float* s_out;       // (B*Hkv,D,D)
   int32_t T, Hq, Hkv, units, beta_heads;
   float scale;
+  // query-head groups, as GatedArgs::hsplit (grid = units * hsplit)
+  int32_t hsplit;
 };
 // decay_kind: 0 none ("delta"), 1 per kv head, 2 per key dim.  fp32 at head
 // size 128 is not available (LDS).
@@ -177,6 +184,10 @@ struct GatedStepArgs {
   // delta rules only: beta (B, beta_heads), beta_heads = Hkv or 1 (shared)
   const void* beta;
   int32_t beta_heads;
+  // query heads per kv head (0: the launcher's G); more than 8, or a count that
+  // is not a power of two, runs the readout in passes of the largest of 8, 4,
+  // 2, 1 that divides it
+  int32_t heads;
   // rows per batch of q, k, v, the decay, beta and out: 0 or 1 for (B, ...)
   // tensors; T when the pointers sit at token t of (B, T, ...) tensors
   int32_t batch_rows;

@@ -139,7 +139,9 @@ def test_gated_argument_errors(lib):
     f = fake
     n = ctypes.c_size_t(0)
     assert lib.la_gated_workspace_size(2, 64, 6, 4, 128, 128, 1, 0, ctypes.byref(n)) == SHAPE
-    assert lib.la_gated_workspace_size(2, 64, 48, 8, 128, 128, 1, 0, ctypes.byref(n)) == UNSUPPORTED
+    # any group size is accepted (6 query heads per kv head: three groups of 2)
+    assert lib.la_gated_workspace_size(2, 64, 48, 8, 128, 128, 1, 0, ctypes.byref(n)) == OK
+    assert lib.la_gated_workspace_size(2, 64, 48, 8, 96, 96, 1, 0, ctypes.byref(n)) == UNSUPPORTED
     assert lib.la_gated_workspace_size(2, 32768, 32, 8, 128, 128, 1, 0, ctypes.byref(n)) == OK
     assert n.value > 0
     # 16 units of 512 chunks split 32 ways: D*D state slots plus the decay factors
@@ -186,7 +188,7 @@ def test_gated_step_argument_errors(lib):
                                  ctypes.c_float(a["scale"]), None)
 
     assert g(Hq=3) == SHAPE
-    assert g(Hq=2 * 16) == UNSUPPORTED        # 16 query heads per kv head
+    assert g(Hq=2 * 16, q=None) == NULL_ARG   # 16 query heads per kv head pass the shape checks
     assert g(Dk=96, Dv=96) == UNSUPPORTED
     assert g(dt=3) == DTYPE
     assert g(pres=None) == NULL_ARG
