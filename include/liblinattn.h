@@ -156,11 +156,13 @@ la_status la_gated_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
  *   float32) is always written and may alias past_state exactly.
  * scale == 0 means 1/sqrt(Dk).  Hq must be a positive multiple of Hkv
  * (else LA_ERR_SHAPE); any multiple is supported, multi-query (Hkv = 1)
- * included.  A per-dim decay is evaluated chunk-parallel with keys
- * rescaled inside blocks of 32 tokens: decays summing below about -87 over
- * one such block (per dimension) overflow.  fp32 inputs at Dk = 128 with a
- * per-dim decay and T > 1 (whose chunk tiles exceed the LDS) run the T == 1
- * step kernel once per token instead: no range limit and no workspace, but
+ * included.  Decays of any strength are supported.  A per-dim decay is
+ * evaluated chunk-parallel with keys rescaled relative to a reference token;
+ * where some dimension's cumulative decay inside a 64-token chunk exceeds 60
+ * in magnitude, the workgroup concerned re-evaluates its tokens one at a
+ * time (exact, and slower by a large factor for that workgroup).  fp32 inputs
+ * at Dk = 128 with a per-dim decay and T > 1 (whose chunk tiles exceed the
+ * LDS) run the T == 1 step kernel once per token instead: no workspace, but
  * one state read and write per token (la_gated_workspace_size reports 0). */
 la_status la_gated_forward(const void* q, const void* k, const void* v, const void* decay,
                            int32_t per_dim_decay, const float* past_state, float* present_state,
@@ -197,15 +199,16 @@ la_status la_gated_step(const void* q, const void* k, const void* v, const void*
  * scale, past/present state and GQA as la_gated_forward; keys are expected
  * L2-normalised (operator page, "Inputs").  Evaluated chunk-parallel (64-token
  * chunks, a 64 x 64 triangular solve per chunk) by one workgroup per (batch,
- * kv head) over the whole sequence; no workspace.  The per-dim decay range of
- * la_gated_forward applies to per-dim decays, and with fp16 inputs also to
- * per-head decays (keys rescaled per 32-token block: decays summing below
- * about -87 over one block overflow); bf16 and fp32 inputs take per-head
- * decays of any strength.  fp32 inputs at Dk = 128 with a per-dim decay and
- * T > 1 run the step below once per token (slower: one state read and write
- * per token).  T == 1 runs a streaming step instead: one read and one
- * write of the state per (batch, kv head), in place allowed (present_state ==
- * past_state), no decay range limit, every dtype and head size. */
+ * kv head) over the whole sequence; no workspace.  Decays of any strength are
+ * supported: per-dim decays, and per-head decays with fp16 inputs, rescale the
+ * keys relative to a reference token, and a workgroup whose cumulative decay
+ * inside a 64-token chunk exceeds 60 in magnitude re-evaluates its whole
+ * sequence one token at a time (exact, and slower by a large factor for that
+ * workgroup).  fp32 inputs at Dk = 128 with a per-dim decay and T > 1 run the
+ * step below once per token (slower: one state read and write per token).
+ * T == 1 runs a streaming step instead: one read and one write of the state
+ * per (batch, kv head), in place allowed (present_state == past_state), every
+ * dtype and head size. */
 la_status la_delta_forward(const void* q, const void* k, const void* v, const void* decay,
                            int32_t per_dim_decay, const void* beta, int32_t beta_per_head,
                            const float* past_state, float* present_state, void* out, int64_t B,

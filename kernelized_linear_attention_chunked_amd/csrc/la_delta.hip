@@ -28,10 +28,21 @@
 // registers (lane shuffles), and write their rows of U^T over the V^T tiles.
 // A sequence is processed by one workgroup from start to end (no split over T:
 // a segment's transition is a full D x D matrix, not a diagonal).
+//
+// The rescaled keys (per-dim decays, and fp16 inputs with a per-head decay)
+// leave the fp32 range when a cumulative decay inside a chunk is very strong.
+// A workgroup that meets a chunk whose |b| exceeds kDeltaExactSpan in some
+// dimension re-evaluates its whole sequence token by token (la_recur.hpp),
+// outputs and state, which holds for decays of any strength.
 #include "la_device.hpp"
 #include "la_launch.hpp"
+#include "la_recur.hpp"
 
 namespace la {
+
+// Largest |cumulative log decay| inside a chunk for which the rescaled keys
+// stay well inside the fp32 range (e^{60} ~ 1e26).
+constexpr float kDeltaExactSpan = 60.f;
 
 template <int G>
 struct DeltaShape {
@@ -96,7 +107,12 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   static_assert(32 % TW == 0 && LOADERS % 64 == 0, "whole loader waves cover tokens 0..31");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 
+  constexpr int RHP = recur_heads<D, NTH, G>(LDS);  // heads per pass of the token-by-token re-evaluation
+  // the rescaled-key forms (not RAW) with a decay can meet decays too strong for them
+  constexpr bool RERUN = !RAW && DK != 0;
+  static_assert(!RERUN || RHP >= 1, "LDS for the token-by-token re-evaluation");
   __shared__ __align__(16) unsigned char smem[LDS + 16];
+  __shared__ int rerun_flag;  // some chunk's decays exceed kDeltaExactSpan
   unsigned char* sp = smem;
   auto carve = [&](int bytes) {
     unsigned char* p = sp;
@@ -389,6 +405,14 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
         const float c31 = DK == 1 ? Bt[kChunk + 31] : 0.f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) c32[e] = c31;
+      }
+      if constexpr (RERUN) {
+        float span = 0.f;
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) span = fmaxf(span, fabsf(bx[n][e]));
+        if (!(span <= kDeltaExactSpan)) rerun_flag = 1;  // (NaN decays too)
       }
 #pragma unroll
       for (int n = 0; n < NTOK; ++n) {
@@ -902,6 +926,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
 
   // ---- state: S = diag(e^{b_C}) S + sum_j diag(e^{b_C - b_j}) k_j u_j^T, the
   // decayed keys from k^ (hi + lo) times e^{b_C - c_sigma} in fp32, then hi + lo
+  int cl = kChunk - 1;  // the chunk's last token (the sequence's last in a partial chunk)
   auto update = [&]() {
     refresh();
     u32x4_t kop[NKS], kol[NKS];
@@ -913,14 +938,14 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
         const int rt = tau / NDT, ct = tau % NDT;
         if constexpr (DK == 2) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) sacc[i][q] *= __expf(Bc[(kChunk - 1) * BC_LD + 16 * rt + 4 * lg + q]);
+          for (int q = 0; q < 4; ++q) sacc[i][q] *= __expf(Bc[cl * BC_LD + 16 * rt + 4 * lg + q]);
         } else if constexpr (DK == 1) {
-          sacc[i] *= __expf(Bt[kChunk + kChunk - 1]);
+          sacc[i] *= __expf(Bt[kChunk + cl]);
         }
         if (rt != cur_rt) {
           cur_rt = rt;
           const int dk = 16 * rt + lr;
-          const float bC = DK == 2 ? Bc[(kChunk - 1) * BC_LD + dk] : (DK == 1 ? Bt[kChunk + kChunk - 1] : 0.f);
+          const float bC = DK == 2 ? Bc[cl * BC_LD + dk] : (DK == 1 ? Bt[kChunk + cl] : 0.f);
           const float c31 = DK == 2 ? Bc[31 * BC_LD + dk] : (DK == 1 ? Bt[kChunk + 31] : 0.f);
 #pragma unroll
           for (int m = 0; m < NKS; ++m) {
@@ -950,7 +975,11 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   };
 
   prefetch(0);
+  if (tid == 0) rerun_flag = 0;  // (read only after the chunk loop's barriers)
   for (int c = 0; c < nchunks; ++c) {
+    // (its cumulative decay is then exactly the newest token's, whatever order
+    // the scan summed the padded zeros in)
+    cl = min(kChunk, T - c * kChunk) - 1;
     stage(c);
     prefetch(min(c + 1, nchunks - 1));
     solve(c);
@@ -972,6 +1001,29 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
 #pragma unroll
         for (int q = 0; q < 4; ++q) sout[(16 * rt + 4 * lg + q) * D + 16 * ct + lr] = sacc[i][q];
       }
+    }
+  }
+  if constexpr (RERUN) {
+    __syncthreads();  // the chunk loop and the state stores above are done
+    if (rerun_flag) {
+      // strong decays: the whole sequence again, token by token, outputs and state
+      RecurPtrs rp;
+      rp.q = qb;
+      rp.k = kb;
+      rp.v = vb;
+      rp.decay = gb;
+      rp.beta = betab;
+      rp.out = ob;
+      rp.s_in = a.s_in ? a.s_in + (int64_t)u * D * D : nullptr;
+      rp.s_out = (a.s_out && hg == 0) ? a.s_out + (int64_t)u * D * D : nullptr;
+      rp.qs = QS;
+      rp.ks = KS;
+      rp.gs = DK == 2 ? KS : Hkv;
+      rp.bs = a.beta_heads;
+      rp.t0 = 0;
+      rp.t1 = T;
+      rp.scale = scale;
+      token_recurrence<IT, D, NTH, G, RHP, DK, true>(smem, rp);
     }
   }
 }

@@ -310,7 +310,11 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
 
   auto compute = [&](int c) {
     refresh();
-    const float btot = __shfl(bcs, 63);
+    // b at the chunk's last token: the end of the sequence in a partial chunk,
+    // so that the newest token's factor exp(btot - b_t) is exactly 1 (the scan
+    // sums the padded zeros in another order, which strong decays, |b| in the
+    // hundreds, would turn into a relative error of 1e-4)
+    const float btot = __shfl(bcs, min(kChunk, T - c * kChunk) - 1);
     if constexpr (OUT) {
       const float bi = __shfl(bcs, 16 * wr + lr);
       const float ebi = __expf(bi);

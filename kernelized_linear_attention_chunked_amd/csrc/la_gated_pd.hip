@@ -19,14 +19,24 @@
 // least 1, bounded by the decay across the block's own 32 tokens: per-dim decays
 // stronger than about 87 (log-space, summed over 32 tokens) overflow it.  The
 // keys k^ = k e^{c - b} are formed once per chunk in LDS beside the raw keys,
-// which the state update uses with e^{b_C - b_s} applied in fp32.
+// which the state update uses with e^{b_C - b_s} applied in fp32.  When some
+// dimension's cumulative decay inside a chunk exceeds kExactSpan in magnitude
+// (the factors could leave the fp32 range), the workgroup re-evaluates its
+// segment's outputs token by token (la_recur.hpp), which holds for decays of
+// any strength; the state, whose factors never exceed 1, is kept.
 //
 // Workgroup shape, loaders, V^T staging (hi + lo tiles for fp16 inputs) and the
 // MFMA operand conventions follow the per-head-decay kernel (la_gated.hip).
 #include "la_device.hpp"
 #include "la_launch.hpp"
+#include "la_recur.hpp"
 
 namespace la {
+
+// Largest |cumulative log decay| inside a chunk (any dimension) for which the
+// factorised products stay well inside the fp32 range (e^{60} ~ 1e26); beyond
+// it the workgroup re-evaluates its outputs token by token.
+constexpr float kExactSpan = 60.f;
 
 template <int G>
 struct PdShape {
@@ -89,8 +99,11 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
   static_assert(K2_BYTES + KL_BYTES + VT_BYTES + VL_BYTES + SB_BYTES + BC_BYTES + WT_BYTES <= 160 * 1024,
                 "LDS budget");
 
-  __shared__ __align__(16) unsigned char smem[K2_BYTES + VT_BYTES + SB_BYTES + VL_BYTES + BC_BYTES +
-                                              WT_BYTES + KL_BYTES + 16];
+  constexpr int SMEM = K2_BYTES + VT_BYTES + SB_BYTES + VL_BYTES + BC_BYTES + WT_BYTES + KL_BYTES + 16;
+  constexpr int RHP = recur_heads<D, NTH, G>(SMEM);  // heads per pass of the token-by-token re-evaluation
+  static_assert(!OUT || RHP >= 1, "LDS for the token-by-token re-evaluation");
+  __shared__ __align__(16) unsigned char smem[SMEM];
+  __shared__ int rerun_flag;  // some chunk's decays exceed kExactSpan
   DT* Kn = (DT*)smem;                   // k as loaded (operand type, or raw fp16)
   DT* Kh = (DT*)(smem + KN_BYTES);      // k^ = k e^{c_sigma - b} (operand type; outputs only)
   DT* Vt = (DT*)(smem + K2_BYTES);
@@ -132,6 +145,7 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
     return r * SB_LD + (((col / VEC) ^ sq_swz(r)) * VEC) + (col % VEC);
   };
 
+  if (tid == 0) rerun_flag = 0;  // (read only after the chunk loop's barriers)
   // ---- state tiles: wave w owns tiles tau = w*TPW + i (rows rt, columns ct)
   f32x4_t sacc[TPW];
 #pragma unroll
@@ -293,15 +307,20 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
       for (int w2 = 0; w2 < W32; ++w2)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) c32[e] += Wt[w2 * D + cb * VEC + e];
+      float span = 0.f;
 #pragma unroll
       for (int n = 0; n < NTOK; ++n) {
         const int t = tg * NTOK + n;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) bx[n][e] += off[e];
+        for (int e = 0; e < VEC; ++e) {
+          bx[n][e] += off[e];
+          span = fmaxf(span, fabsf(bx[n][e]));
+        }
 #pragma unroll
         for (int e = 0; e < VEC; e += 4)
           *(f32x4_t*)(Bc + t * BC_LD + cb * VEC + e) = f32x4_t{bx[n][e], bx[n][e + 1], bx[n][e + 2], bx[n][e + 3]};
       }
+      if (OUT && !(span <= kExactSpan)) rerun_flag = 1;  // (NaN decays too)
 #pragma unroll
       for (int n = 0; n < NTOK && OUT; ++n) {
         const int t = tg * NTOK + n;
@@ -475,8 +494,12 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
     }
     // ---- state: S = diag(e^{b_C}) S + sum_s diag(e^{b_C - b_s}) k_s v_s^T, with
     // the raw keys, the factors in fp32 and the decayed keys as hi + lo
+    // the chunk's last token (the sequence's last in a partial chunk: its
+    // cumulative decay is then exactly the newest token's, whatever order the
+    // scan summed the padded zeros in)
+    const int cl = min(kChunk, T - c * kChunk) - 1;
     if constexpr (!OUT) {
-      if (tid < D) seg_log += Bc[(kChunk - 1) * BC_LD + tid];
+      if (tid < D) seg_log += Bc[cl * BC_LD + tid];
     }
     u32x4_t kop[NKS], kol[NKS];
     int cur_rt = -1;
@@ -486,11 +509,11 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
       if (tau < NS) {
         const int rt = tau / NDT, ct = tau % NDT;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sacc[i][q] *= __expf(Bc[(kChunk - 1) * BC_LD + 16 * rt + 4 * lg + q]);
+        for (int q = 0; q < 4; ++q) sacc[i][q] *= __expf(Bc[cl * BC_LD + 16 * rt + 4 * lg + q]);
         if (rt != cur_rt) {
           cur_rt = rt;
           const int dk = 16 * rt + lr;
-          const float bC = Bc[(kChunk - 1) * BC_LD + dk];
+          const float bC = Bc[cl * BC_LD + dk];
 #pragma unroll
           for (int m = 0; m < NKS; ++m) {
             float f[VEC];
@@ -552,6 +575,30 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
 #pragma unroll
         for (int q = 0; q < 4; ++q) sout[(16 * rt + 4 * lg + q) * D + 16 * ct + lr] = sacc[i][q];
       }
+    }
+  }
+  if constexpr (OUT) {
+    __syncthreads();  // the chunk loop is done with the LDS everywhere
+    if (rerun_flag) {
+      // strong decays: the segment's outputs again, token by token (the state
+      // above has factors of at most 1 and stands)
+      RecurPtrs rp;
+      rp.q = qb;
+      rp.k = kb;
+      rp.v = vb;
+      rp.decay = gb;
+      rp.beta = nullptr;
+      rp.out = ob;
+      rp.s_in = a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr;
+      rp.s_out = nullptr;
+      rp.qs = QS;
+      rp.ks = KS;
+      rp.gs = KS;
+      rp.bs = 0;
+      rp.t0 = c0 * kChunk;
+      rp.t1 = min(c1 * kChunk, T);
+      rp.scale = scale;
+      token_recurrence<IT, D, NTH, G, RHP, 2, false>(smem, rp);
     }
   }
 }
