@@ -62,20 +62,45 @@ def _traffic(kernel, src, launches_per_record=1):
 def prefill_mfma_per_chunk(D=128, norm=True):
     """MFMA instructions one workgroup issues per 64-token chunk in the causal
     prefill kernel (bf16, v_mfma_f32_16x16x32_bf16), from its tiling.  Query
-    block qr (16 rows) forms A^T over key pairs of 32 up to its diagonal,
-    2 tiles per pair x D/32 steps, once per value half (two halves at D=128);
-    intra V^T A^T: pairs x (D/16 + norm) value tiles x 2 (hi/lo of A); inter
-    S^T phiQ^T: 4 blocks x (D/16 + norm) x D/32; state update: (D/16)(D/16 + norm)
-    tiles x 2 token steps."""
-    nvt = D // 16 + (1 if norm else 0)
-    nq = D // 32
+    block qr (16 rows) forms A^T over key pairs of 32 up to its diagonal, 2
+    tiles per pair x D/32 steps, once per value half (two halves at D=128).
+    Each value half's waves hold their D/32 value tiles plus the normaliser
+    tile (both halves form the denominator they divide by): intra V^T A^T,
+    pairs x tiles x 2 (hi/lo of A); inter S^T phiQ^T, tiles x D/32 per query
+    block.  State update: (D/16)(D/16 + norm) tiles x 2 token steps.  At D=128
+    this gives 520 per chunk, which rocprofv3's SQ_INSTS_VALU_MFMA_MOPS_BF16
+    reproduces exactly (profiles/causal_prefill_kernel_mfma.md)."""
     halves = 2 if D >= 128 else 1
+    tiles = D // 16 // halves + (1 if norm else 0)   # a wave's value tiles (+ normaliser)
+    nq = D // 32
     pairs = [(16 * qr + 15) // 32 + 1 for qr in range(4)]
     a_t = halves * sum(2 * p for p in pairs) * nq
-    intra = sum(pairs) * nvt * 2
-    inter = 4 * nvt * nq
-    upd = (D // 16) * nvt * 2
+    intra = halves * sum(pairs) * tiles * 2
+    inter = halves * 4 * tiles * nq
+    upd = (D // 16) * (D // 16 + (1 if norm else 0)) * 2
     return a_t + intra + inter + upd
+
+
+def _profile_record(name, src):
+    """A committed rocprofv3 summary (profiles/<name>.json) if the kernel source
+    is unchanged since it was taken, else None."""
+    path = os.path.join(PROFILES, name + ".json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    return rec if rec.get("kernel_src_sha") == _src_sha(src) else None
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def _elapsed_ms(pairs):
@@ -111,6 +136,7 @@ def cpu_baseline_streaming(d, target_s, log):
         t1 = time.perf_counter() - t0
     tokens = nb * H * d.T
     return {"value": tokens / t1, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
             "kind": "oracle", "seconds": round(t1, 3),
             "sample": "%d of %d (batch, head) units x %d prefill tokens (batch rows 0..%d), "
                       "fp64 per-token recurrence" % (nb * H, d.B * H, d.T, nb - 1)}
@@ -169,6 +195,7 @@ def bench_streaming(args, log):
 
     dc_traffic = _traffic("decode_kernel", "la_decode.hip")
     pf_traffic = _traffic("causal_prefill_kernel", "la_chunk.hip")
+    mfma_prof = _profile_record("causal_prefill_kernel_mfma", "la_chunk.hip")
     rec = {
         "metric": "prefill tokens/s + MFMA util (causal, D=128); decode state HBM GB/s",
         "value": prefill_tps,
@@ -190,7 +217,18 @@ def bench_streaming(args, log):
                     "kernel_ms": pf_kernel_ms, "hbm_GBps": pf_gbs, "hbm_frac": pf_gbs / HBM_PEAK_GBS,
                     "mfma_util_executed": pf_exec_flops / (pf_kernel_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
                     "mfma_util_algorithmic": pf_alg_flops / (pf_kernel_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
-                    "executed_mfma_TFLOPs": pf_exec_flops / (pf_kernel_ms * 1e-3) / 1e12},
+                    "executed_mfma_TFLOPs": pf_exec_flops / (pf_kernel_ms * 1e-3) / 1e12,
+                    "executed_mfma_per_chunk": prefill_mfma_per_chunk(D),
+                    # SQ_VALU_MFMA_BUSY_CYCLES over all SIMDs, from the committed
+                    # rocprofv3 pass of this kernel source (null if it changed since)
+                    "mfma_busy_rocprof": None if mfma_prof is None else mfma_prof["mfma_busy"],
+                    # the most MFMA-busy this 64-token-chunk kernel can honestly be
+                    # while moving its bytes at the 8 TB/s HBM bound: executed bf16
+                    # MFMA time at peak / HBM time for the algorithmic bytes
+                    "mfma_busy_ceiling_at_hbm_bound": (pf_exec_flops / (BF16_PEAK_TFLOPS * 1e12))
+                                                      / (pf_bytes / (HBM_PEAK_GBS * 1e9)),
+                    "mfma_target_note": "a 50% MFMA target is above this chunk size's HBM-bound ceiling; "
+                                        "MFMA utilisation is reported as measured"},
         "decode": {"kernel_us": dc_kernel_ms * 1e3, "ms_per_step": mean(decode_ms),
                    "state_GBps": units * (D * D + D) * 8 / (dc_kernel_ms * 1e-3) / 1e9,
                    "hbm_GBps": dc_gbs, "hbm_frac": dc_gbs / HBM_PEAK_GBS,
@@ -248,6 +286,7 @@ def bench_other(args, log):
     ms = median_ms([d])
     wall = time.perf_counter() - t0
     D, Tt = d.D, d.B * d.T
+    extra = {}
     if args.workload == "gated_step_d128":
         # per token step: the fp32 state read and written once, plus q, k, v, decay, out
         U = d.B * d.Hkv
@@ -271,15 +310,22 @@ def bench_other(args, log):
         # three linear-rule recurrences: per token a 64-wide intra tile, A V and
         # the inter and state products (2 D D each)
         flops = 3 * Tt * d.H * (2 * 64 * D * 2 + 4 * D * D)
-    elif args.workload in ("gated_gqa_d128", "gated_perdim_d128"):
-        per_dim = args.workload == "gated_perdim_d128"
-        nbytes = (Tt * (d.Hq * D * 2 * 2 + d.Hkv * D * 2 * 2 + d.Hkv * (D if per_dim else 1) * 2)
+    elif args.workload in ("gated_gqa_d128", "gated_perdim_d128", "gated_perdim_f32_d128"):
+        per_dim = args.workload != "gated_gqa_d128"
+        esz = d.q.element_size()
+        nbytes = (Tt * (d.Hq * D * esz * 2 + d.Hkv * D * esz * 2 + d.Hkv * (D if per_dim else 1) * esz)
                   + d.B * d.Hkv * D * D * 4)
         # dense 64x64 intra tiles per q head plus inter and state update (2 Dk Dv each)
         flops = Tt * d.Hq * (2 * 64 * 2 * D + 2 * D * D) + Tt * d.Hkv * 2 * D * D
     elif args.workload == "noncausal_relu_d128":
-        nbytes = Tt * d.H * D * 2 * 4 + Tt
-        flops = Tt * d.H * (2 * D * (D + 1) * 2)  # reduce (phiK^T V, Z) and readout
+        # the kernels skip masked tokens' reads (whole 64-token chunks of k and v,
+        # 16-row blocks of q): q, k, v read for the valid tokens, every output
+        # row written (zeros where masked), the mask read
+        valid = int(d.lengths.sum())
+        nbytes = valid * d.H * D * 2 * 3 + Tt * d.H * D * 2 + Tt
+        flops = valid * d.H * (2 * D * (D + 1) * 2)  # reduce (phiK^T V, Z) and readout
+        extra = {"valid_tokens": valid, "valid_fraction": valid / Tt,
+                 "bytes_note": "bytes count q, k, v of valid tokens only (what the kernels read)"}
     else:
         nbytes = Tt * d.H * D * 2 * 4 + d.B * d.H * (D * D + D) * 4
         flops = Tt * d.H * (2 * 64 * (D + D) + 4 * D * D)
@@ -290,7 +336,9 @@ def bench_other(args, log):
            "data": "synthetic", "config": {"workload": args.workload},
            "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-           "mfma_util_algorithmic": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)}
+           "mfma_util_algorithmic": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), **extra}
+    if d.q.dtype.itemsize == 4:
+        rec["dtype"] = "f32"
     if args.workload == "causal_bf16_d64":
         cold = [d] + [workloads.DRIVERS[args.workload]("cuda:0") for _ in range(7)]
         ms_cold = median_ms(cold)
@@ -309,8 +357,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="streaming_d128",
                     choices=["streaming_d128", "causal_bf16_d64", "noncausal_relu_d128",
-                             "gated_gqa_d128", "gated_perdim_d128", "gated_delta_d128",
-                             "backward_bf16_d64", "gated_step_d128", "delta_step_d128"])
+                             "gated_gqa_d128", "gated_perdim_d128", "gated_perdim_f32_d128",
+                             "gated_delta_d128", "backward_bf16_d64", "gated_step_d128",
+                             "delta_step_d128"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

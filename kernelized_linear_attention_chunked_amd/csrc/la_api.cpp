@@ -579,15 +579,36 @@ hipError_t launch_step(const void* q, const void* k, const void* v, const void* 
 
 namespace {
 // fp32 inputs at head size 128 with a per-key-dim decay: the chunk kernels'
-// fp32 tiles and decay table exceed the LDS, so T > 1 runs the one-token step
-// kernel once per token (state read and written per token; no workspace)
+// fp32 tiles and decay table exceed the LDS, so T > 1 runs the whole-sequence
+// token-by-token kernel (la_recur.hip: one launch, the state in registers; no
+// workspace)
 bool by_token(bool per_dim, int32_t dtype, int64_t D, int64_t T) {
   return per_dim && dtype == LA_DT_F32 && D == 128 && T > 1;
 }
 
-// token t of each (B, T, width) tensor: the step kernel reads batch b at row b*T
-const void* at_token(const void* p, int64_t t, int64_t width, int64_t esz) {
-  return p ? (const void*)((const char*)p + t * width * esz) : nullptr;
+hipError_t launch_by_token(const void* q, const void* k, const void* v, const void* decay, const void* beta,
+                           int64_t beta_heads, int delta, const float* past_state, float* present_state,
+                           void* out, int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int32_t dtype,
+                           float scale, hipStream_t st) {
+  const int64_t G = Hq / Hkv, GW = head_tile(G);
+  la::RecurArgs r;
+  memset(&r, 0, sizeof(r));
+  r.q = q;
+  r.k = k;
+  r.v = v;
+  r.decay = decay;
+  r.beta = beta;
+  r.out = out;
+  r.s_in = past_state;
+  r.s_out = present_state;
+  r.T = (int32_t)T;
+  r.Hq = (int32_t)Hq;
+  r.Hkv = (int32_t)Hkv;
+  r.units = (int32_t)(B * Hkv);
+  r.beta_heads = (int32_t)beta_heads;
+  r.hsplit = (int32_t)(G / GW);
+  r.scale = scale;
+  return la::launch_recur(dtype, (int)D, (int)GW, 2, delta, r, st);
 }
 }  // namespace
 
@@ -660,23 +681,8 @@ la_status gated_forward(const void* q, const void* k, const void* v, const void*
     return device_status(e, "la_gated_forward");
   }
   if (tokens) {
-    la::GatedStepArgs g;
-    memset(&g, 0, sizeof(g));
-    g.Hkv = (int32_t)Hkv;
-    g.units = (int32_t)U;
-    g.per_dim = 1;
-    g.scale = scale;
-    g.batch_rows = (int32_t)T;
-    g.s_out = present_state;
-    for (int64_t t = 0; t < T && e == hipSuccess; ++t) {
-      g.q = at_token(q, t, Hq * D, esz);
-      g.k = at_token(k, t, Hkv * D, esz);
-      g.v = at_token(v, t, Hkv * D, esz);
-      g.decay = at_token(decay, t, Hkv * D, esz);
-      g.out = (void*)at_token(out, t, Hq * D, esz);
-      g.s_in = t == 0 ? past_state : present_state;
-      e = la::launch_gated_step(dtype, (int)D, (int)G, g, st);
-    }
+    e = launch_by_token(q, k, v, decay, nullptr, 0, 0, past_state, present_state, out, B, T, Hq, Hkv, D, dtype,
+                        scale, st);
     return device_status(e, "la_gated_forward (token by token)");
   }
   const int64_t GW = head_tile(G), HS = G / GW;  // heads per workgroup, query-head groups
@@ -849,25 +855,8 @@ LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v
     return device_status(e, "la_delta_forward (T = 1)");
   }
   if (by_token(per_dim, dtype, D, T)) {
-    la::GatedStepArgs g;
-    memset(&g, 0, sizeof(g));
-    g.Hkv = (int32_t)Hkv;
-    g.units = (int32_t)U;
-    g.per_dim = 1;
-    g.scale = scale;
-    g.beta_heads = (int32_t)bh;
-    g.batch_rows = (int32_t)T;
-    g.s_out = present_state;
-    for (int64_t t = 0; t < T && e == hipSuccess; ++t) {
-      g.q = at_token(q, t, Hq * D, esz);
-      g.k = at_token(k, t, Hkv * D, esz);
-      g.v = at_token(v, t, Hkv * D, esz);
-      g.decay = at_token(decay, t, Hkv * D, esz);
-      g.beta = at_token(beta, t, bh, esz);
-      g.out = (void*)at_token(out, t, Hq * D, esz);
-      g.s_in = t == 0 ? past_state : present_state;
-      e = la::launch_delta_step(dtype, (int)D, (int)G, g, st);
-    }
+    e = launch_by_token(q, k, v, decay, beta, bh, 1, past_state, present_state, out, B, T, Hq, Hkv, D, dtype,
+                        scale, st);
     return device_status(e, "la_delta_forward (token by token)");
   }
   la::DeltaArgs a;

@@ -202,4 +202,22 @@ hipError_t launch_gated_prefix(float* ws_s, const float* ws_a, const float* s_in
 // launch_gated; fp32 at head size 128 is not available (LDS).
 hipError_t launch_gated_pd(int mode, int io, int D, int G, const GatedArgs& a, int grid, hipStream_t st);
 
+// Whole-sequence token-by-token recurrence (la_recur.hip), one workgroup per
+// (batch, kv head) unit and query-head group; head size 128.
+struct RecurArgs {
+  const void* q;      // (B,T,Hq*D)
+  const void* k;      // (B,T,Hkv*D)
+  const void* v;      // (B,T,Hkv*D)
+  const void* decay;  // null, (B,T,Hkv) or (B,T,Hkv*D) per the decay kind
+  const void* beta;   // delta rule: (B,T,beta_heads)
+  void* out;          // (B,T,Hq*D)
+  const float* s_in;  // (B*Hkv,D,D) or null (zeros)
+  float* s_out;       // (B*Hkv,D,D)
+  int32_t T, Hq, Hkv, units, beta_heads, hsplit;
+  float scale;
+};
+// decay_kind: 0 none, 1 per kv head, 2 per key dim; delta: the delta rule;
+// G: query heads per workgroup (1, 2, 4, 8; hsplit groups of them per unit)
+hipError_t launch_recur(int io, int D, int G, int decay_kind, int delta, const RecurArgs& a, hipStream_t st);
+
 }  // namespace la

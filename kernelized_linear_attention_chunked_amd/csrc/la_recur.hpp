@@ -86,20 +86,48 @@ __device__ void token_recurrence(unsigned char* lds, const RecurPtrs& r) {
   auto ld = [](const IT* p, int64_t i) { return Io<IT>::to_f32(sizeof(IT) == 4 ? __float_as_uint(((const float*)p)[i])
                                                                                : (uint32_t)((const uint16_t*)p)[i]); };
 
+  static_assert(D <= NTH, "one thread per key dimension");
   f32x4_t sv[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
     sv[i] = (r.s_in && holder) ? *(const f32x4_t*)(r.s_in + (rg + RG * i) * D + 4 * c4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // the next token's inputs are loaded into registers while the current one
+  // is processed: thread i < D takes k, v (and a per-dim decay) of dimension i,
+  // every thread NQE query elements
+  constexpr int NQE = (GW * D + NTH - 1) / NTH;
+  float pk = 0.f, pv = 0.f, pg = 0.f, pb = 0.f, pq[NQE];
+  auto fetch = [&](int t) {
+    if (tid < D) {
+      pk = ld(kb + (int64_t)t * r.ks, tid);
+      pv = ld(vb + (int64_t)t * r.ks, tid);
+      if constexpr (DK == 2) pg = ld(gb + (int64_t)t * r.gs, tid);
+    }
+    if constexpr (DK == 1) pg = ld(gb + (int64_t)t * r.gs, 0);
+    if constexpr (DELTA) pb = ld(bb + (int64_t)t * r.bs, 0);
+#pragma unroll
+    for (int j = 0; j < NQE; ++j) {
+      const int i = tid + j * NTH;
+      pq[j] = i < GW * D ? ld(qb + (int64_t)t * r.qs, i) : 0.f;
+    }
+  };
+  if (r.t0 < r.t1) fetch(r.t0);
+
   for (int t = r.t0; t < r.t1; ++t) {
-    for (int i = tid; i < D; i += NTH) {
-      fk[i] = ld(kb + (int64_t)t * r.ks, i);
-      fv[i] = ld(vb + (int64_t)t * r.ks, i);
-      if constexpr (DK == 2) fe[i] = __expf(ld(gb + (int64_t)t * r.gs, i));
+    if (tid < D) {
+      fk[tid] = pk;
+      fv[tid] = pv;
+      if constexpr (DK == 2) fe[tid] = __expf(pg);
     }
     if constexpr (DK == 1)
-      if (tid == 0) fe[0] = __expf(ld(gb + (int64_t)t * r.gs, 0));
-    for (int i = tid; i < GW * D; i += NTH) fq[i] = ld(qb + (int64_t)t * r.qs, i);
+      if (tid == 0) fe[0] = __expf(pg);
+    const float be = pb;
+#pragma unroll
+    for (int j = 0; j < NQE; ++j) {
+      const int i = tid + j * NTH;
+      if (i < GW * D) fq[i] = pq[j];
+    }
+    if (t + 1 < r.t1) fetch(t + 1);
     __syncthreads();
     // S' = E S
     if (DK != 0 && holder) {
@@ -124,7 +152,6 @@ __device__ void token_recurrence(unsigned char* lds, const RecurPtrs& r) {
         for (int c = 0; c < 4; ++c) part[rg * D + 4 * c4 + c] = acc[c];
       }
       __syncthreads();
-      const float be = ld(bb + (int64_t)t * r.bs, 0);
       for (int i = tid; i < D; i += NTH) {
         float wsum = 0.f;
         for (int g = 0; g < RG; ++g) wsum += part[g * D + i];

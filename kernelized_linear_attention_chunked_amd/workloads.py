@@ -164,6 +164,7 @@ class GatedGqaD128:
 
     name = "gated_gqa_d128"
     per_dim = 0
+    io = 1  # la_dtype of the inputs
 
     def __init__(self, device="cuda:0"):
         w = synth.WORKLOADS[self.name]
@@ -174,7 +175,7 @@ class GatedGqaD128:
         B, T, D = self.B, self.T, self.D
         self.out = torch.empty_like(self.q)
         self.present = torch.empty((B, self.Hkv, D, D), dtype=torch.float32, device=device)
-        n = la_gated_workspace_size(B, T, self.Hq, self.Hkv, D, D, torch.bfloat16, bool(self.per_dim))
+        n = la_gated_workspace_size(B, T, self.Hq, self.Hkv, D, D, self.q.dtype, bool(self.per_dim))
         self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
         self.ws_bytes = n
         self.scale = 1.0 / (D ** 0.5)
@@ -187,7 +188,7 @@ class GatedGqaD128:
     def step(self):
         _check(self.lib.la_gated_forward(_p(self.q), _p(self.k), _p(self.v), _p(self.g), self.per_dim, None,
                                          _p(self.present), _p(self.out), self.B, self.T, self.Hq,
-                                         self.Hkv, self.D, self.D, 1, self.scale, _p(self.ws),
+                                         self.Hkv, self.D, self.D, self.io, self.scale, _p(self.ws),
                                          self.ws_bytes, _stream(self.device)), "la_gated_forward")
 
 
@@ -196,6 +197,15 @@ class GatedPerdimD128(GatedGqaD128):
 
     name = "gated_perdim_d128"
     per_dim = 1
+
+
+class GatedPerdimF32D128(GatedGqaD128):
+    """The per-key-dim gated rule with fp32 inputs at head size 128, B=8 T=2048
+    Hq=32 Hkv=8: the whole-sequence token-by-token path (one launch)."""
+
+    name = "gated_perdim_f32_d128"
+    per_dim = 1
+    io = 0
 
 
 class GatedDeltaD128:
@@ -319,5 +329,5 @@ class DeltaStepD128(GatedStepD128):
 
 
 DRIVERS = {c.name: c for c in (StreamingD128, CausalBf16D64, NonCausalReluD128, GatedGqaD128,
-                               GatedPerdimD128, GatedDeltaD128, BackwardBf16D64, GatedStepD128,
-                               DeltaStepD128)}
+                               GatedPerdimD128, GatedPerdimF32D128, GatedDeltaD128, BackwardBf16D64,
+                               GatedStepD128, DeltaStepD128)}

@@ -28,6 +28,8 @@ then rounded to nearest even to the storage dtype):
   drawn N(0, 0.3^2).
 * ``delta_step_d128``     ``gated_step_d128`` under the gated delta rule, with
   beta = sigmoid(N(0,1)) per kv head.
+* ``gated_perdim_f32_d128`` the per-key-dim gated rule with fp32 inputs at head
+  size 128 (B=8 T=2048 Hq=32 Hkv=8): the distributions of ``gated_perdim_d128``.
 """
 from __future__ import annotations
 
@@ -46,6 +48,7 @@ WORKLOADS = {
     "gated_delta_d128": dict(B=32, T=4096, Hq=32, Hkv=8, D=128, dtype=torch.bfloat16, seed=8),
     "backward_bf16_d64": dict(B=8, H=16, T=2048, D=64, dtype=torch.bfloat16, seed=9),
     "delta_step_d128": dict(B=256, T=64, Hq=32, Hkv=8, D=128, dtype=torch.bfloat16, seed=10),
+    "gated_perdim_f32_d128": dict(B=8, T=2048, Hq=32, Hkv=8, D=128, dtype=torch.float32, seed=11),
 }
 
 
@@ -108,12 +111,14 @@ def workload(name: str, device="cpu"):
     """All inputs of a named workload as a dict of tensors on ``device``."""
     w = WORKLOADS[name]
     s, dt = w["seed"], w["dtype"]
-    if name in ("gated_gqa_d128", "gated_step_d128", "gated_perdim_d128", "gated_delta_d128", "delta_step_d128"):
+    if name in ("gated_gqa_d128", "gated_step_d128", "gated_perdim_d128", "gated_delta_d128", "delta_step_d128",
+                "gated_perdim_f32_d128"):
         B, T, Hq, Hkv, D = w["B"], w["T"], w["Hq"], w["Hkv"], w["D"]
         q = normal((B, T, Hq * D), 1.0, dt, device, s, "q")
         k = l2_normalized((B, T, Hkv, D), dt, device, s, "k").reshape(B, T, Hkv * D)
         v = normal((B, T, Hkv * D), 1.0, dt, device, s, "v")
-        g = logsigmoid_decay((B, T, Hkv * D) if name == "gated_perdim_d128" else (B, T, Hkv), dt, device, s)
+        per_dim = name in ("gated_perdim_d128", "gated_perdim_f32_d128")
+        g = logsigmoid_decay((B, T, Hkv * D) if per_dim else (B, T, Hkv), dt, device, s)
         out = dict(q=q, k=k, v=v, decay=g, Hq=Hq, Hkv=Hkv, D=D)
         if name in ("gated_step_d128", "delta_step_d128"):
             out["past"] = normal((B, Hkv, D, D), 0.3, torch.float32, device, s, "past")
