@@ -36,19 +36,20 @@ __device__ __forceinline__ float load_elem<float>(const float* p, int i) {
 constexpr int kDecodeUnits = 2;
 constexpr int kDecodeThreads = kDecodeUnits * kThreads;
 
-template <typename DT, int D, int FM, bool NORM, bool NTMP>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
+// TPU threads per unit, UPB units per workgroup.
+template <typename DT, int D, int FM, bool NORM, bool NTMP, int TPU = kThreads, int UPB = kDecodeUnits>
+__global__ __launch_bounds__(TPU * UPB) void decode_kernel(DecodeArgs a) {
   constexpr int C4 = D / 4;          // float4 columns per state row
-  constexpr int RG = kThreads / C4;  // row groups
+  constexpr int RG = TPU / C4;       // row groups
   constexpr int RPT = D / RG;        // rows per thread
-  static_assert(RPT >= 1 && RG * RPT == D, "unsupported head size");
-  __shared__ float fk[kDecodeUnits][D], fq[kDecodeUnits][D], zs[kDecodeUnits][D];
-  __shared__ float part[kDecodeUnits][RG][D];
-  __shared__ float den_s[kDecodeUnits];
+  static_assert(RPT >= 1 && RG * RPT == D && TPU >= D && TPU >= 64, "unsupported head size");
+  __shared__ float fk[UPB][D], fq[UPB][D], zs[UPB][D];
+  __shared__ float part[UPB][RG][D];
+  __shared__ float den_s[UPB];
 
-  const int ul = threadIdx.x / kThreads;  // unit slot in the workgroup
-  const int tid = threadIdx.x % kThreads;
-  const int u = blockIdx.x * kDecodeUnits + ul;
+  const int ul = threadIdx.x / TPU;  // unit slot in the workgroup
+  const int tid = threadIdx.x % TPU;
+  const int u = blockIdx.x * UPB + ul;
   const bool live = u < a.units;  // the last workgroup may hold one unit only
   const int b = u / a.H;
   const int c4 = tid % C4, rg = tid / C4;
@@ -135,20 +136,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 // consecutive state columns, issues all of its state loads first, updates in
 // registers, writes back, and keeps partial readouts of every query head; the
 // row groups are summed through LDS.  q and k are staged in LDS as fp32.
-template <typename DT, int D, int G, bool NTMP, bool PD, bool MP>
-__global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArgs a) {
+template <typename DT, int D, int G, bool NTMP, bool PD, bool MP, int TPU = kThreads, int UPB = kDecodeUnits>
+__global__ __launch_bounds__(TPU * UPB) void gated_step_kernel(GatedStepArgs a) {
   // G query heads per readout pass; MP: a.heads / G passes (a kv head with
   // more heads, or a head count that is not a power of two), else one
   constexpr int C4 = D / 4;          // float4 columns per state row
-  constexpr int RG = kThreads / C4;  // row groups
+  constexpr int RG = TPU / C4;  // row groups
   constexpr int RPT = D / RG;        // rows per thread
   static_assert(RPT >= 1 && RG * RPT == D && C4 <= 32, "unsupported head size");
-  __shared__ float fk[kDecodeUnits][D], fq[kDecodeUnits][G][D], fe[kDecodeUnits][PD ? D : 1];
-  __shared__ float part[kDecodeUnits][G][RG][D];
+  __shared__ float fk[UPB][D], fq[UPB][G][D], fe[UPB][PD ? D : 1];
+  __shared__ float part[UPB][G][RG][D];
 
-  const int ul = threadIdx.x / kThreads;  // unit slot in the workgroup
-  const int tid = threadIdx.x % kThreads;
-  const int u = blockIdx.x * kDecodeUnits + ul;
+  const int ul = threadIdx.x / TPU;  // unit slot in the workgroup
+  const int tid = threadIdx.x % TPU;
+  const int u = blockIdx.x * UPB + ul;
   const bool live = u < a.units;  // the last workgroup may hold one unit only
   const int b = u / a.Hkv, j = u % a.Hkv;
   const int c4 = tid % C4, rg = tid / C4;
@@ -177,16 +178,16 @@ __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArg
   // fp32 copies of the query rows of pass p
   auto load_q = [&](int p) {
     const DT* qpp = qp + (int64_t)p * G * D;
-    for (int i = tid; i < G * D; i += kThreads) fq[ul][i / D][i % D] = load_elem<DT>(qpp, i);
+    for (int i = tid; i < G * D; i += TPU) fq[ul][i / D][i % D] = load_elem<DT>(qpp, i);
   };
   float v4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) v4[i] = live ? load_elem<DT>(vp, 4 * c4 + i) : 0.f;
   const float e = (live && a.decay && !PD) ? __expf(load_elem<DT>((const DT*)a.decay, uh)) : 1.f;
   if (live) {
-    for (int i = tid; i < D; i += kThreads) fk[ul][i] = load_elem<DT>(kp, i);
+    for (int i = tid; i < D; i += TPU) fk[ul][i] = load_elem<DT>(kp, i);
     if constexpr (PD)  // per-key-dim decay: row dk of S scales by exp(g[dk])
-      for (int i = tid; i < D; i += kThreads) fe[ul][i] = __expf(load_elem<DT>((const DT*)a.decay + uh * D, i));
+      for (int i = tid; i < D; i += TPU) fe[ul][i] = __expf(load_elem<DT>((const DT*)a.decay + uh * D, i));
     load_q(0);
   }
   __syncthreads();
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArg
     __syncthreads();
     if (live) {
       DT* op = (DT*)a.out + br * QW + (int64_t)j * GT * D + (int64_t)p * G * D;
-      for (int i = tid; i < G * D; i += kThreads) {
+      for (int i = tid; i < G * D; i += TPU) {
         const int h = i / D, d = i % D;
         float y = 0.f;
 #pragma unroll
@@ -260,20 +261,20 @@ __global__ __launch_bounds__(kDecodeThreads) void gated_step_kernel(GatedStepArg
 // registers throughout.  Two sums over the rows go through LDS in turn: S'^T k
 // (then u, one value per column), and after the rank-1 update q_h^T S''.  One
 // read and one write of the state, as for the gated step.
-template <typename DT, int D, int G, bool NTMP, int DK, bool MP>
-__global__ __launch_bounds__(kDecodeThreads) void delta_step_kernel(GatedStepArgs a) {
+template <typename DT, int D, int G, bool NTMP, int DK, bool MP, int TPU = kThreads, int UPB = kDecodeUnits>
+__global__ __launch_bounds__(TPU * UPB) void delta_step_kernel(GatedStepArgs a) {
   // G query heads per readout pass; MP: a.heads / G passes, else one
   constexpr int C4 = D / 4;          // float4 columns per state row
-  constexpr int RG = kThreads / C4;  // row groups
+  constexpr int RG = TPU / C4;  // row groups
   constexpr int RPT = D / RG;        // rows per thread
   static_assert(RPT >= 1 && RG * RPT == D && C4 <= 32, "unsupported head size");
-  __shared__ float fk[kDecodeUnits][D], fq[kDecodeUnits][G][D], fe[kDecodeUnits][DK == 2 ? D : 1];
-  __shared__ float fu[kDecodeUnits][D];
-  __shared__ float part[kDecodeUnits][G][RG][D];
+  __shared__ float fk[UPB][D], fq[UPB][G][D], fe[UPB][DK == 2 ? D : 1];
+  __shared__ float fu[UPB][D];
+  __shared__ float part[UPB][G][RG][D];
 
-  const int ul = threadIdx.x / kThreads;  // unit slot in the workgroup
-  const int tid = threadIdx.x % kThreads;
-  const int u = blockIdx.x * kDecodeUnits + ul;
+  const int ul = threadIdx.x / TPU;  // unit slot in the workgroup
+  const int tid = threadIdx.x % TPU;
+  const int u = blockIdx.x * UPB + ul;
   const bool live = u < a.units;  // the last workgroup may hold one unit only
   const int b = u / a.Hkv, j = u % a.Hkv;
   const int c4 = tid % C4, rg = tid / C4;
@@ -301,15 +302,15 @@ __global__ __launch_bounds__(kDecodeThreads) void delta_step_kernel(GatedStepArg
   const DT* vp = (const DT*)a.v + uh * D;
   auto load_q = [&](int p) {
     const DT* qpp = qp + (int64_t)p * G * D;
-    for (int i = tid; i < G * D; i += kThreads) fq[ul][i / D][i % D] = load_elem<DT>(qpp, i);
+    for (int i = tid; i < G * D; i += TPU) fq[ul][i / D][i % D] = load_elem<DT>(qpp, i);
   };
   const float e = (live && DK == 1) ? __expf(load_elem<DT>((const DT*)a.decay, uh)) : 1.f;
   const float be = live ? load_elem<DT>((const DT*)a.beta, br * a.beta_heads + (a.beta_heads > 1 ? j : 0)) : 0.f;
   const float vc = (live && tid < D) ? load_elem<DT>(vp, tid) : 0.f;  // v of column tid
   if (live) {
-    for (int i = tid; i < D; i += kThreads) fk[ul][i] = load_elem<DT>(kp, i);
+    for (int i = tid; i < D; i += TPU) fk[ul][i] = load_elem<DT>(kp, i);
     if constexpr (DK == 2)  // per-key-dim decay: row dk of S scales by exp(g[dk])
-      for (int i = tid; i < D; i += kThreads) fe[ul][i] = __expf(load_elem<DT>((const DT*)a.decay + uh * D, i));
+      for (int i = tid; i < D; i += TPU) fe[ul][i] = __expf(load_elem<DT>((const DT*)a.decay + uh * D, i));
     load_q(0);
   }
   __syncthreads();
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(kDecodeThreads) void delta_step_kernel(GatedStepArg
     __syncthreads();
     if (live) {
       DT* op = (DT*)a.out + br * QW + (int64_t)j * GT * D + (int64_t)p * G * D;
-      for (int i = tid; i < G * D; i += kThreads) {
+      for (int i = tid; i < G * D; i += TPU) {
         const int h = i / D, d = i % D;
         float y = 0.f;
 #pragma unroll
@@ -420,19 +421,31 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(float* dst, const float*
     dst[i] = src[i];
 }
 
+// Launch shape of the decode kernel per head size: threads per unit and units
+// per workgroup.  At head size 128 one 1024-thread workgroup per unit (4 state
+// rows per thread) measured 182 us per step of the 8192-unit streaming
+// workload, against 192 us for two 256-thread units per workgroup, 188 us for
+// 512 x 2 and 183 us for 128 x 2 (a sweep of the shapes over this kernel).
+template <int D>
+struct DecodeShape {
+  static constexpr int TPU = D == 128 ? 1024 : kThreads;
+  static constexpr int UPB = D == 128 ? 1 : kDecodeUnits;
+};
+
 template <typename DT, int D, int FM, bool NORM>
 static void launch_k(bool ntmp, const DecodeArgs& a, int grid, hipStream_t st) {
+  constexpr int TPU = DecodeShape<D>::TPU, UPB = DecodeShape<D>::UPB;
   if (ntmp)
-    hipLaunchKernelGGL((decode_kernel<DT, D, FM, NORM, true>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<DT, D, FM, NORM, true, TPU, UPB>), dim3(grid), dim3(TPU * UPB), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_kernel<DT, D, FM, NORM, false>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<DT, D, FM, NORM, false, TPU, UPB>), dim3(grid), dim3(TPU * UPB), 0, st, a);
 }
 
 template <typename DT, int D>
 static hipError_t launch_d(int fm, int norm, const DecodeArgs& a, int units, hipStream_t st) {
   // states larger than the on-chip caches stream past them (non-temporal)
   const bool ntmp = (int64_t)units * D * D * 4 >= ((int64_t)256 << 20);
-  const int grid = (units + kDecodeUnits - 1) / kDecodeUnits;
+  const int grid = (units + DecodeShape<D>::UPB - 1) / DecodeShape<D>::UPB;
   if (fm == kEluPlusOne) {
     if (norm) launch_k<DT, D, kEluPlusOne, true>(ntmp, a, grid, st);
     else launch_k<DT, D, kEluPlusOne, false>(ntmp, a, grid, st);
