@@ -217,7 +217,6 @@ int oracle_la_op(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int6
   return 0;
 }
 
-/* Number of OpenMP threads a parallel loop above will use (for reporting). */
 /* Derivative of phi (the Keras proposal's feature maps): elu(x)+1 has slope 1
  * for x > 0 and exp(x) otherwise; relu(x)+eps has slope 1 for x > 0 and 0
  * otherwise (0 taken at x = 0). */
@@ -330,4 +329,5 @@ int oracle_causal_backward(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t 
   return 0;
 }
 
+/* Number of OpenMP threads a parallel loop above will use (for reporting). */
 int oracle_max_threads(void) { return omp_get_max_threads(); }
