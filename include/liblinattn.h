@@ -20,8 +20,12 @@
  * ("[Feature] LinearAttention layer for Keras", sections "Mathematical
  * definition", "Streaming State", "Numerical Stability").
  *
- * Supported head sizes: Dk == Dv, one of 32, 64, 128.  Other sizes return
- * LA_ERR_UNSUPPORTED (no slower path covers other sizes).
+ * Supported head sizes: Dk and Dv each one of 32, 64, 128 (la_forward,
+ * la_forward_noalloc, la_step); the gated and delta calls and la_backward need
+ * Dk == Dv.  Other sizes return LA_ERR_UNSUPPORTED (no slower path covers
+ * them).  With Dk != Dv the kernels run at the larger size with the smaller
+ * side zero-padded in registers and LDS (memory is read and written at the
+ * caller's sizes).
  */
 #ifndef LIBLINATTN_H
 #define LIBLINATTN_H

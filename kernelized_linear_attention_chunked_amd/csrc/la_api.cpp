@@ -112,13 +112,13 @@ NonCausalPlan plan_noncausal(int64_t U, int64_t T, int64_t slot = 0, size_t cap 
   return p;
 }
 
-int64_t state_elems(int64_t D, int norm) { return D * D + (norm ? D : 0); }
+int64_t state_elems(int64_t Dk, int64_t Dv, int norm) { return Dk * Dv + (norm ? Dk : 0); }
 
-size_t forward_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t D, int causal, int norm,
+size_t forward_ws_bytes(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int causal, int norm,
                         size_t cap = SIZE_MAX) {
   const int64_t U = B * H;
   if (U == 0 || T == 0) return 0;
-  const int64_t slot = state_elems(D, norm) * 4;
+  const int64_t slot = state_elems(Dk, Dv, norm) * 4;
   if (causal) {
     CausalPlan p = plan_causal(U, T, slot, cap);
     if (p.nseg <= 1) return 0;
@@ -133,14 +133,19 @@ static_assert(la::kIoF32 == LA_DT_F32 && la::kIoBF16 == LA_DT_BF16 && la::kIoF16
 bool dtype_ok(int32_t dtype) { return dtype == LA_DT_F32 || dtype == LA_DT_BF16 || dtype == LA_DT_F16; }
 int64_t dtype_size(int32_t dtype) { return dtype == LA_DT_F32 ? 4 : 2; }
 
-la_status check_common(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int32_t dtype) {
+// unequal: Dk and Dv may differ (each 32, 64 or 128)
+la_status check_common(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int32_t dtype,
+                       bool unequal = true) {
   if (!dtype_ok(dtype))
     return fail(LA_ERR_DTYPE, "dtype %d is not a supported floating type (0=f32, 1=bf16, 2=f16)", dtype);
   if (B < 0 || T < 0 || H < 1 || Dk < 1 || Dv < 1)
     return fail(LA_ERR_SHAPE, "bad sizes B=%lld T=%lld H=%lld Dk=%lld Dv=%lld", (long long)B,
                 (long long)T, (long long)H, (long long)Dk, (long long)Dv);
-  if (Dk != Dv || !head_size_ok(Dk))
-    return fail(LA_ERR_UNSUPPORTED, "head sizes Dk=%lld Dv=%lld: only Dk == Dv in {32,64,128}",
+  if (!head_size_ok(Dk) || !head_size_ok(Dv))
+    return fail(LA_ERR_UNSUPPORTED, "head sizes Dk=%lld Dv=%lld: each must be 32, 64 or 128",
+                (long long)Dk, (long long)Dv);
+  if (!unequal && Dk != Dv)
+    return fail(LA_ERR_UNSUPPORTED, "head sizes Dk=%lld Dv=%lld: this call needs Dk == Dv",
                 (long long)Dk, (long long)Dv);
   if (B * H > (int64_t)1 << 30 || T > ((int64_t)1 << 31) - kChunk || H * Dk > (int64_t)1 << 30)
     return fail(LA_ERR_SHAPE, "sizes exceed the 32-bit index ranges of the kernels");
@@ -185,7 +190,7 @@ LA_EXPORT la_status la_workspace_size(int64_t B, int64_t T, int64_t H, int64_t D
   if (s != LA_OK) return s;
   // the normaliser adds Dk floats per slot; size for it so the answer does not
   // depend on use_normalizer
-  *bytes = forward_ws_bytes(B, T, H, Dk, causal != 0, 1);
+  *bytes = forward_ws_bytes(B, T, H, Dk, Dv, causal != 0, 1);
   return ok();
 }
 
@@ -239,7 +244,6 @@ la_status forward_impl(const void* q, const void* k, const void* v, const uint8_
     return fail(LA_ERR_BAD_ARG, "feature_map %d is not 0 (elu+1) or 1 (relu+eps)", feature_map);
   if (!(eps >= 0.f) || isinf(eps)) return fail(LA_ERR_BAD_ARG, "eps must be finite and >= 0");
   const int norm = use_normalizer != 0;
-  const int64_t D = Dk;
   const int64_t U = B * H;
   const int64_t esz = dtype_size(dtype);
   const bool work = U > 0 && T > 0;
@@ -262,13 +266,13 @@ la_status forward_impl(const void* q, const void* k, const void* v, const uint8_
   if (!aligned16(state_in_k) || !aligned16(state_out_k) || !aligned16(workspace))
     return fail(LA_ERR_BAD_ARG, "k states and workspace must be 16-byte aligned");
 
-  const int64_t nqk = B * T * H * D * esz;
-  const Range rq = range(q, nqk), rk = range(k, nqk), rv = range(v, nqk), ro = range(out, nqk);
+  const int64_t nqk = B * T * H * Dk * esz, nvo = B * T * H * Dv * esz;
+  const Range rq = range(q, nqk), rk = range(k, nqk), rv = range(v, nvo), ro = range(out, nvo);
   const Range rm = range(mask, B * T);
-  const Range rsi = range(state_in_kv, U * D * D * 4), rzi = range(state_in_k, U * D * 4);
-  const Range rso = range(state_out_kv, U * D * D * 4), rzo = range(state_out_k, U * D * 4);
-  const size_t need = forward_ws_bytes(B, T, H, D, causal != 0, norm, cap);
-  const int64_t slot = state_elems(D, norm) * 4;
+  const Range rsi = range(state_in_kv, U * Dk * Dv * 4), rzi = range(state_in_k, U * Dk * 4);
+  const Range rso = range(state_out_kv, U * Dk * Dv * 4), rzo = range(state_out_k, U * Dk * 4);
+  const size_t need = forward_ws_bytes(B, T, H, Dk, Dv, causal != 0, norm, cap);
+  const int64_t slot = state_elems(Dk, Dv, norm) * 4;
   if (noalloc && work && !causal && plan_noncausal(U, T, slot, cap).nsplit == 0)
     return fail(LA_ERR_WORKSPACE,
                 "la_forward_noalloc: the non-causal sums of %lld (batch, head) units need %lld bytes, "
@@ -301,20 +305,21 @@ la_status forward_impl(const void* q, const void* k, const void* v, const uint8_
     s = scratch_for_stream(st, &workspace);
     if (s != LA_OK) return s;
   }
-  const int Di = (int)D;
+  // the kernels' tile size: the larger head size (the smaller side zero-padded)
+  const int Di = (int)(Dk > Dv ? Dk : Dv);
   hipError_t e = hipSuccess;
 
   if (!work) {
     // nothing to read: a causal state passes through unchanged (zeros if none)
     if (causal && state_out_kv) {
-      const int64_t n = U * D * D;
+      const int64_t n = U * Dk * Dv;
       e = (state_in_kv) ? (state_out_kv != state_in_kv ? la::launch_copy(state_out_kv, state_in_kv, n, st)
                                                        : hipSuccess)
                         : la::launch_fill_zero(state_out_kv, n, st);
       if (e == hipSuccess && norm)
-        e = state_in_k ? (state_out_k != state_in_k ? la::launch_copy(state_out_k, state_in_k, U * D, st)
+        e = state_in_k ? (state_out_k != state_in_k ? la::launch_copy(state_out_k, state_in_k, U * Dk, st)
                                                     : hipSuccess)
-                       : la::launch_fill_zero(state_out_k, U * D, st);
+                       : la::launch_fill_zero(state_out_k, U * Dk, st);
     }
     return device_status(e, "la_forward");
   }
@@ -329,7 +334,9 @@ la_status forward_impl(const void* q, const void* k, const void* v, const uint8_
   a.T = (int32_t)T;
   a.H = (int32_t)H;
   a.eps = eps;
-  const int64_t SE = D * D, ZE = D;
+  a.dk = Dk != Dv ? (int32_t)Dk : 0;
+  a.dv = Dk != Dv ? (int32_t)Dv : 0;
+  const int64_t SE = Dk * Dv, ZE = Dk;
 
   if (causal) {
     CausalPlan p = plan_causal(U, T, slot, cap);
@@ -367,7 +374,8 @@ la_status forward_impl(const void* q, const void* k, const void* v, const uint8_
     ps.nseg_total = (int32_t)p.nseg;
     e = la::launch_chunk(la::kModeState, dtype, Di, feature_map, norm, ps, (int)(U * (p.nseg - 1)), st);
     if (e == hipSuccess)
-      e = la::launch_seg_prefix(ws_s, ws_z, state_in_kv, state_in_k, (int)U, (int)p.nseg, Di, norm, st);
+      e = la::launch_seg_prefix(ws_s, ws_z, state_in_kv, state_in_k, (int)U, (int)p.nseg, (int)Dk, (int)Dv, norm,
+                                st);
     if (e == hipSuccess) {
       la::ChunkArgs pc = a;
       pc.s_in = ws_s;
@@ -407,7 +415,7 @@ la_status forward_impl(const void* q, const void* k, const void* v, const uint8_
   pr.nseg_total = (int32_t)p.nsplit;
   pr.chunk_step = (int32_t)p.nsplit;  // split s sums chunks s, s + nsplit, ...: masked tails spread
   e = la::launch_chunk(la::kModeState, dtype, Di, feature_map, norm, pr, (int)(U * p.nsplit), st);
-  if (e == hipSuccess) e = la::launch_seg_sum(ws_s, ws_z, (int)U, (int)p.nsplit, Di, norm, st);
+  if (e == hipSuccess) e = la::launch_seg_sum(ws_s, ws_z, (int)U, (int)p.nsplit, (int)Dk, (int)Dv, norm, st);
   if (e == hipSuccess) {
     la::ApplyArgs pa;
     pa.q = a.q;
@@ -421,6 +429,8 @@ la_status forward_impl(const void* q, const void* k, const void* v, const uint8_
     pa.H = a.H;
     pa.seg_count = la::apply_groups_per_unit(U, T);
     pa.eps = a.eps;
+    pa.dk = a.dk;
+    pa.dv = a.dv;
     e = la::launch_apply(dtype, Di, feature_map, norm, pa, (int)(U * pa.seg_count), st);
   }
   return device_status(e, "la_forward (non-causal)");
@@ -459,7 +469,7 @@ LA_EXPORT la_status la_step(const void* q, const void* k, const void* v, const u
     return fail(LA_ERR_BAD_ARG, "feature_map %d is not 0 (elu+1) or 1 (relu+eps)", feature_map);
   if (!(eps >= 0.f) || isinf(eps)) return fail(LA_ERR_BAD_ARG, "eps must be finite and >= 0");
   const int norm = use_normalizer != 0;
-  const int64_t D = Dk, U = B * H;
+  const int64_t U = B * H;
   const int64_t esz = dtype_size(dtype);
   if (U == 0) return ok();
   if (!q || !k || !v || !out) return fail(LA_ERR_NULL_ARG, "q, k, v and out are required");
@@ -471,10 +481,10 @@ LA_EXPORT la_status la_step(const void* q, const void* k, const void* v, const u
     return fail(LA_ERR_STATE, "use_normalizer=0 carries only the kv state; k parts must be NULL");
   if (!aligned16(state_in_kv) || !aligned16(state_out_kv))
     return fail(LA_ERR_BAD_ARG, "kv states must be 16-byte aligned");
-  const Range rq = range(q, U * D * esz), rk = range(k, U * D * esz), rv = range(v, U * D * esz);
-  const Range ro = range(out, U * D * esz), rm = range(mask, B);
-  const Range rsi = range(state_in_kv, U * D * D * 4), rzi = range(state_in_k, U * D * 4);
-  const Range rso = range(state_out_kv, U * D * D * 4), rzo = range(state_out_k, U * D * 4);
+  const Range rq = range(q, U * Dk * esz), rk = range(k, U * Dk * esz), rv = range(v, U * Dv * esz);
+  const Range ro = range(out, U * Dv * esz), rm = range(mask, B);
+  const Range rsi = range(state_in_kv, U * Dk * Dv * 4), rzi = range(state_in_k, U * Dk * 4);
+  const Range rso = range(state_out_kv, U * Dk * Dv * 4), rzo = range(state_out_k, U * Dk * 4);
   const Range ins[4] = {rq, rk, rv, rm};
   const Range outs[3] = {ro, rso, rzo};
   for (const Range& o : outs)
@@ -499,7 +509,7 @@ LA_EXPORT la_status la_step(const void* q, const void* k, const void* v, const u
   a.H = (int32_t)H;
   a.units = (int32_t)U;
   a.eps = eps;
-  hipError_t e = la::launch_decode(dtype, (int)D, feature_map, norm, a, (int)U,
+  hipError_t e = la::launch_decode(dtype, (int)Dk, (int)Dv, feature_map, norm, a, (int)U,
                                    (hipStream_t)stream);
   return device_status(e, "la_step");
 }
@@ -921,7 +931,7 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t D, int64_t esz, bo
 LA_EXPORT la_status la_backward_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
                                                int32_t dtype, int32_t use_normalizer, size_t* bytes) {
   if (!bytes) return fail(LA_ERR_NULL_ARG, "bytes is NULL");
-  la_status s = check_common(B, T, H, Dk, Dv, dtype);
+  la_status s = check_common(B, T, H, Dk, Dv, dtype, false);
   if (s != LA_OK) return s;
   *bytes = (B * H == 0 || T == 0) ? 0 : bwd_layout(B, T, H, Dk, dtype_size(dtype), use_normalizer != 0).total;
   return ok();
@@ -934,7 +944,7 @@ LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, con
                                 float* dstate_in_kv, float* dstate_in_k, int64_t B, int64_t T, int64_t H,
                                 int64_t Dk, int64_t Dv, int32_t dtype, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  la_status s = check_common(B, T, H, Dk, Dv, dtype);
+  la_status s = check_common(B, T, H, Dk, Dv, dtype, false);
   if (s != LA_OK) return s;
   if (feature_map != LA_FM_ELU_PLUS_ONE && feature_map != LA_FM_RELU_EPS)
     return fail(LA_ERR_BAD_ARG, "feature_map %d is not 0 (elu+1) or 1 (relu+eps)", feature_map);

@@ -27,7 +27,10 @@ constexpr int kApplyMaxBlocksPerWave = 16;  // liveness of a wave's blocks: one 
 constexpr int kApplyWaves = 8;
 constexpr int kApplyThreads = 64 * kApplyWaves;
 
-template <typename IT, int D, int FM, bool NORM, bool MASKED>
+// PAD: Dk != Dv (a.dk, a.dv), as in the chunk kernel: D = max(Dk, Dv) wide
+// tiles, q blocks past Dk read as zeros with phi 0, S rows past Dk and columns
+// past Dv zero, outputs stored Dv wide.
+template <typename IT, int D, int FM, bool NORM, bool MASKED, bool PAD = false>
 // 16-bit operands: two workgroups per CU (at most 128 registers); fp32 S^T
 // tiles at head size 128 fit the LDS once
 __global__ __launch_bounds__(kApplyThreads, (sizeof(typename Io<IT>::DT) == 2 || D < 128) ? 4 : 1) void apply_kernel(ApplyArgs a) {
@@ -50,7 +53,9 @@ __global__ __launch_bounds__(kApplyThreads, (sizeof(typename Io<IT>::DT) == 2 ||
   int l = tid & 63, lr = l & 15, lg = l >> 4;
   const int nseg = a.seg_count;
   const int u = blockIdx.x / nseg, sg = blockIdx.x % nseg;
-  const int T = a.T, H = a.H, HD = H * D;
+  const int T = a.T, H = a.H;
+  const int DKr = PAD ? a.dk : D, DVr = PAD ? a.dv : D;  // head sizes in memory
+  const int HDK = H * DKr, HDV = H * DVr;
   const int b = u / H, h = u % H;
   auto sq_at = [&](int r, int col) {
     return r * SB_LD + (((col / VEC) ^ sq_swz(r)) * VEC) + (col % VEC);
@@ -78,7 +83,8 @@ __global__ __launch_bounds__(kApplyThreads, (sizeof(typename Io<IT>::DT) == 2 ||
       const int dv = 4 * (idx / (D / KPL)), dk = KPL * (idx % (D / KPL));
 #pragma unroll
       for (int p = 0; p < KPL; ++p)
-        x[it][p] = idx < NCOPY ? *(const f32x4_t*)(sin + (dk + p) * D + dv) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        x[it][p] = (idx < NCOPY && dk + p < DKr && dv < DVr) ? *(const f32x4_t*)(sin + (dk + p) * DVr + dv)
+                                                            : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
@@ -98,14 +104,14 @@ __global__ __launch_bounds__(kApplyThreads, (sizeof(typename Io<IT>::DT) == 2 ||
         const int r = idx / (D / KPL), dk = KPL * (idx % (D / KPL));
         float y[KPL];
 #pragma unroll
-        for (int p = 0; p < KPL; ++p) y[p] = zin[dk + p];
+        for (int p = 0; p < KPL; ++p) y[p] = dk + p < DKr ? zin[dk + p] : 0.f;
         put(sq_at(D + r, dk), y);
       }
     }
   }
 
-  const IT* qb = (const IT*)a.q + (int64_t)b * T * HD + (int64_t)h * D;
-  IT* ob = (IT*)a.out + (int64_t)b * T * HD + (int64_t)h * D;
+  const IT* qb = (const IT*)a.q + (int64_t)b * T * HDK + (int64_t)h * DKr;
+  IT* ob = (IT*)a.out + (int64_t)b * T * HDV + (int64_t)h * DVr;
   const uint8_t* const mb = MASKED ? a.mask + (int64_t)b * T : nullptr;
   const int nblk = (T + kApplyBlockRows - 1) / kApplyBlockRows;
   // block of the wave's i-th step (may lie past the end: then it is skipped)
@@ -143,7 +149,8 @@ __global__ __launch_bounds__(kApplyThreads, (sizeof(typename Io<IT>::DT) == 2 ||
       for (int n = 0; n < NLD; ++n) {
         const int g = 64 * n + l;
         const int row = min(r0 + g / CB, T - 1);  // rows past the end read the last
-        q[n] = ld16(qb + (int64_t)row * HD + (g % CB) * VEC);
+        q[n] = (!PAD || (g % CB) * VEC < DKr) ? ld16(qb + (int64_t)row * HDK + (g % CB) * VEC)
+                                              : u32x4_t{0u, 0u, 0u, 0u};
       }
       if constexpr (MASKED) k = mb[min(r0 + lr, T - 1)];
     }
@@ -164,7 +171,8 @@ __global__ __launch_bounds__(kApplyThreads, (sizeof(typename Io<IT>::DT) == 2 ||
 #pragma unroll
       for (int n = 0; n < NLD; ++n) {
         const int g = 64 * n + l;
-        if (r0 + g / CB < T) st16(ob + (int64_t)(r0 + g / CB) * HD + (g % CB) * VEC, u32x4_t{0u, 0u, 0u, 0u});
+        if (r0 + g / CB < T && (!PAD || (g % CB) * VEC < DVr))
+          st16(ob + (int64_t)(r0 + g / CB) * HDV + (g % CB) * VEC, u32x4_t{0u, 0u, 0u, 0u});
       }
       return;
     }
@@ -178,7 +186,8 @@ __global__ __launch_bounds__(kApplyThreads, (sizeof(typename Io<IT>::DT) == 2 ||
       Io<IT>::unpack(q[n], f);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) f[e] = phi<FM>(f[e], a.eps);
-      st16(stg + sq_at(g / CB, (g % CB) * VEC), O::pack(f));
+      const u32x4_t fq = O::pack(f);
+      st16(stg + sq_at(g / CB, (g % CB) * VEC), (!PAD || (g % CB) * VEC < DKr) ? fq : u32x4_t{0u, 0u, 0u, 0u});
     }
     u32x4_t qop[NQ];
 #pragma unroll
@@ -205,7 +214,7 @@ __global__ __launch_bounds__(kApplyThreads, (sizeof(typename Io<IT>::DT) == 2 ||
     for (int n = 0; n < NLD; ++n) {
       const int g = 64 * n + l;
       const u32x4_t v = ld16(stg + sq_at(g / CB, (g % CB) * VEC));
-      if (r0 + g / CB < T) st16(ob + (int64_t)(r0 + g / CB) * HD + (g % CB) * VEC, v);
+      if (r0 + g / CB < T && (!PAD || (g % CB) * VEC < DVr)) st16(ob + (int64_t)(r0 + g / CB) * HDV + (g % CB) * VEC, v);
     }
   };
 
@@ -221,6 +230,15 @@ __global__ __launch_bounds__(kApplyThreads, (sizeof(typename Io<IT>::DT) == 2 ||
 
 template <typename IT, int D, int FM, bool NORM>
 static void launch_m(const ApplyArgs& a, int grid, hipStream_t st) {
+  if constexpr (D > 32) {
+    if (a.dk != a.dv) {
+      if (a.mask)
+        hipLaunchKernelGGL((apply_kernel<IT, D, FM, NORM, true, true>), dim3(grid), dim3(kApplyThreads), 0, st, a);
+      else
+        hipLaunchKernelGGL((apply_kernel<IT, D, FM, NORM, false, true>), dim3(grid), dim3(kApplyThreads), 0, st, a);
+      return;
+    }
+  }
   if (a.mask)
     hipLaunchKernelGGL((apply_kernel<IT, D, FM, NORM, true>), dim3(grid), dim3(kApplyThreads), 0, st, a);
   else

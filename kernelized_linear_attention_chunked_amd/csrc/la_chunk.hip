@@ -61,7 +61,11 @@ struct ChunkOccupancy {
 
 // MASKED: a (B,T) mask is given.  Unmasked launches carry no mask code at all.
 // IT: the I/O element type (Io<IT>); DT: the operand type it is computed in.
-template <typename IT, int D, int FM, bool NORM, int MODE, bool MASKED>
+// PAD: Dk != Dv (a.dk, a.dv): the tiles are D = max(Dk, Dv) wide; q and k
+// blocks past Dk load as zeros with phi selected to 0, v blocks past Dv load as
+// zeros, and outputs and states are stored in their own (dk, dv) shapes.
+// Without PAD the head sizes are D and no guard is compiled in.
+template <typename IT, int D, int FM, bool NORM, int MODE, bool MASKED, bool PAD = false>
 __global__ __launch_bounds__(64 * ChunkWaves<D>::NW, (ChunkOccupancy<IT, D, MODE>::value))
 void chunk_kernel(ChunkArgs a) {
   using DT = typename Io<IT>::DT;
@@ -149,12 +153,12 @@ void chunk_kernel(ChunkArgs a) {
   const int cstep = a.chunk_step > 1 ? a.chunk_step : 1;
   const int c0 = cstep > 1 ? s : s * a.seg_chunks;
   const int c1 = cstep > 1 ? nchunks : min(c0 + a.seg_chunks, nchunks);
-  const int HD = H * D;
-  const int64_t unit_off = (int64_t)b * T * HD + (int64_t)h * D;
-  const IT* qb = (const IT*)a.q + unit_off;
-  const IT* kb = (const IT*)a.k + unit_off;
-  const IT* vb = (const IT*)a.v + unit_off;
-  IT* ob = (IT*)a.out + unit_off;
+  const int DKr = PAD ? a.dk : D, DVr = PAD ? a.dv : D;  // head sizes in memory
+  const int HDK = H * DKr, HDV = H * DVr;                 // token strides of q/k and v/out
+  const IT* qb = (const IT*)a.q + (int64_t)b * T * HDK + (int64_t)h * DKr;
+  const IT* kb = (const IT*)a.k + (int64_t)b * T * HDK + (int64_t)h * DKr;
+  const IT* vb = (const IT*)a.v + (int64_t)b * T * HDV + (int64_t)h * DVr;
+  IT* ob = (IT*)a.out + (int64_t)b * T * HDV + (int64_t)h * DVr;
   const uint8_t* const mb = MASKED ? a.mask + (int64_t)b * T : nullptr;
   const float eps = a.eps;
   // global dv tile of the wave's i-th output tile
@@ -208,9 +212,9 @@ void chunk_kernel(ChunkArgs a) {
           const int dk = 16 * rt + 4 * lg + q;
           float val = 0.f;
           if (ct < NDT) {
-            if (sin) val = sin[dk * D + 16 * ct + lr];
+            if (sin && dk < DKr && 16 * ct + lr < DVr) val = sin[dk * DVr + 16 * ct + lr];
           } else {
-            if (zin) val = zin[dk];
+            if (zin && dk < DKr) val = zin[dk];
           }
           sacc[k][q] = val;
         }
@@ -252,6 +256,9 @@ void chunk_kernel(ChunkArgs a) {
   // 16 threads: coalesced).
   const int cb = tid % CB, tg = tid / CB;
   const bool loader = LOADERS == NTH || tid < LOADERS;
+  // the loader's 16-byte block lies inside the q/k rows (kin) and v rows (vin)
+  const bool kin = !PAD || cb * VEC < DKr, vin = !PAD || cb * VEC < DVr;
+  const u32x4_t zero4 = u32x4_t{0u, 0u, 0u, 0u};
   u32x4_t pk[USE_KV ? NTOK : 1], pv[USE_KV ? NTOK : 1];
   u32x4_t pq[USE_Q ? (QS_STAGE ? NTOK : NQ) : 1];
   u32x4_t qreg[(USE_Q && !QS_STAGE) ? NQ : 1];
@@ -285,7 +292,8 @@ void chunk_kernel(ChunkArgs a) {
       qrow_ok = tok < T && (mb ? (mb[tok] != 0) : true);
 #pragma unroll
       for (int m = 0; m < NQ; ++m)
-        pq[m] = tok < T ? ld16(qb + (int64_t)tok * HD + KB * m + VEC * lg) : u32x4_t{0u, 0u, 0u, 0u};
+        pq[m] = (tok < T && (!PAD || KB * m + VEC * lg < DKr)) ? ld16(qb + (int64_t)tok * HDK + KB * m + VEC * lg)
+                                                            : zero4;
     }
     if (!loader) return;
     if (pfull) {
@@ -293,12 +301,13 @@ void chunk_kernel(ChunkArgs a) {
       valid = (1u << NTOK) - 1u;
 #pragma unroll
       for (int n = 0; n < NTOK; ++n) {
-        const int64_t off = (int64_t)(tb + tg * NTOK + n) * HD + cb * VEC;
+        const int64_t tok = tb + tg * NTOK + n;
+        const int64_t offk = tok * HDK + cb * VEC, offv = tok * HDV + cb * VEC;
         if constexpr (USE_KV) {
-          pk[n] = ld16(kb + off);
-          pv[n] = ld16(vb + off);
+          pk[n] = kin ? ld16(kb + offk) : zero4;
+          pv[n] = vin ? ld16(vb + offv) : zero4;
         }
-        if constexpr (USE_Q && QS_STAGE) pq[n] = ld16(qb + off);
+        if constexpr (USE_Q && QS_STAGE) pq[n] = kin ? ld16(qb + offk) : zero4;
       }
       return;
     }
@@ -306,12 +315,12 @@ void chunk_kernel(ChunkArgs a) {
     for (int n = 0; n < NTOK; ++n) {
       const int tok = tb + tg * NTOK + n;
       if (tok < T) {
-        const int64_t off = (int64_t)tok * HD + cb * VEC;
+        const int64_t offk = (int64_t)tok * HDK + cb * VEC, offv = (int64_t)tok * HDV + cb * VEC;
         if constexpr (USE_KV) {
-          pk[n] = ld16(kb + off);
-          pv[n] = ld16(vb + off);
+          pk[n] = kin ? ld16(kb + offk) : zero4;
+          pv[n] = vin ? ld16(vb + offv) : zero4;
         }
-        if constexpr (USE_Q && QS_STAGE) pq[n] = ld16(qb + off);
+        if constexpr (USE_Q && QS_STAGE) pq[n] = kin ? ld16(qb + offk) : zero4;
         const uint32_t ok = mb ? (mb[tok] != 0) : 1u;
         valid |= ok << n;
       } else {
@@ -380,7 +389,8 @@ void chunk_kernel(ChunkArgs a) {
     constexpr bool FULL = decltype(full)::value;
     if constexpr (USE_Q && !QS_STAGE) {
 #pragma unroll
-      for (int m = 0; m < NQ; ++m) qreg[m] = phi_vec(pq[m], qrow_ok, full);
+      for (int m = 0; m < NQ; ++m)
+        qreg[m] = (!PAD || KB * m + VEC * lg < DKr) ? phi_vec(pq[m], qrow_ok, full) : zero4;
     }
     if (!loader) return;
     u32x4_t pkt[KT ? NTOK : 1];
@@ -389,12 +399,12 @@ void chunk_kernel(ChunkArgs a) {
       const bool ok = FULL || ((valid >> n) & 1u);
       const int t = tg * NTOK + n;
       if constexpr (USE_KV) {
-        const u32x4_t fk = phi_vec(pk[n], ok, full);
+        const u32x4_t fk = kin ? phi_vec(pk[n], ok, full) : zero4;
         if constexpr (KN_ROWS) st16(Kn + kn_at(t, cb * VEC), fk);
         if constexpr (KT) pkt[n] = fk;
         if (!ok) pv[n] = u32x4_t{0u, 0u, 0u, 0u};
       }
-      if constexpr (USE_Q && QS_STAGE) st16(Qs + sq_at(t, cb * VEC), phi_vec(pq[n], ok, full));
+      if constexpr (USE_Q && QS_STAGE) st16(Qs + sq_at(t, cb * VEC), kin ? phi_vec(pq[n], ok, full) : zero4);
     }
     if constexpr (USE_KV) {
       if constexpr (VLO) {
@@ -448,9 +458,10 @@ void chunk_kernel(ChunkArgs a) {
       if constexpr (USE_Q) {
         const int tok = c * kChunk + 16 * qr + lr;
         if (tok < T) {
-          IT* orow = ob + (int64_t)tok * HD + 4 * lg;
+          IT* orow = ob + (int64_t)tok * HDV + 4 * lg;
 #pragma unroll
-          for (int i = 0; i < NDH; ++i) store4(orow + 16 * (hv * NDH + i), 0.f, 0.f, 0.f, 0.f);
+          for (int i = 0; i < NDH; ++i)
+            if (!PAD || 16 * (hv * NDH + i) < DVr) store4(orow + 16 * (hv * NDH + i), 0.f, 0.f, 0.f, 0.f);
         }
       }
       return;
@@ -574,11 +585,12 @@ void chunk_kernel(ChunkArgs a) {
         float rden = 1.f;
         if constexpr (NORM) rden = ok ? 1.f / (nacc[NDH][0] + eps) : 0.f;
         else rden = ok ? 1.f : 0.f;
-        IT* orow = ob + (int64_t)tok * HD + 4 * lg;
+        IT* orow = ob + (int64_t)tok * HDV + 4 * lg;
 #pragma unroll
         for (int i = 0; i < NDH; ++i)
-          store4(orow + 16 * (hv * NDH + i), nacc[i][0] * rden, nacc[i][1] * rden,
-                 nacc[i][2] * rden, nacc[i][3] * rden);
+          if (!PAD || 16 * (hv * NDH + i) < DVr)
+            store4(orow + 16 * (hv * NDH + i), nacc[i][0] * rden, nacc[i][1] * rden,
+                   nacc[i][2] * rden, nacc[i][3] * rden);
       }
     }
     if constexpr (USE_KV && !(FUSE && USE_Q)) {
@@ -652,9 +664,9 @@ void chunk_kernel(ChunkArgs a) {
         for (int q = 0; q < 4; ++q) {
           const int dk = 16 * rt + 4 * lg + q;
           if (ct < NDT) {
-            if (sout) sout[dk * D + 16 * ct + lr] = sacc[k][q];
+            if (sout && dk < DKr && 16 * ct + lr < DVr) sout[dk * DVr + 16 * ct + lr] = sacc[k][q];
           } else {
-            if (zout && lr == 0) zout[dk] = sacc[k][q];
+            if (zout && lr == 0 && dk < DKr) zout[dk] = sacc[k][q];
           }
         }
       }
@@ -674,8 +686,9 @@ constexpr int kSegBatch = 16;
 
 __global__ __launch_bounds__(kThreads) void seg_prefix_kernel(float* ws_s, float* ws_z,
                                                               const float* s_in, const float* z_in,
-                                                              int U, int nseg, int D, int norm) {
-  const int64_t per4 = ((int64_t)D * D + (norm ? D : 0)) / 4;
+                                                              int U, int nseg, int dk, int dv, int norm) {
+  const int SE = dk * dv;  // floats of S per slot (a multiple of 4, like dk)
+  const int64_t per4 = ((int64_t)SE + (norm ? dk : 0)) / 4;
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= (int64_t)U * per4) return;
   const int u = (int)(idx / per4);
@@ -683,15 +696,15 @@ __global__ __launch_bounds__(kThreads) void seg_prefix_kernel(float* ws_s, float
   f32x4_t* base;
   int64_t stride;  // in 4-element groups
   const f32x4_t* init;
-  if (e < D * D) {
-    base = (f32x4_t*)(ws_s + (int64_t)u * nseg * D * D + e);
-    stride = (int64_t)D * D / 4;
-    init = s_in ? (const f32x4_t*)(s_in + (int64_t)u * D * D + e) : nullptr;
+  if (e < SE) {
+    base = (f32x4_t*)(ws_s + (int64_t)u * nseg * SE + e);
+    stride = SE / 4;
+    init = s_in ? (const f32x4_t*)(s_in + (int64_t)u * SE + e) : nullptr;
   } else {
-    const int ez = e - D * D;
-    base = (f32x4_t*)(ws_z + (int64_t)u * nseg * D + ez);
-    stride = D / 4;
-    init = z_in ? (const f32x4_t*)(z_in + (int64_t)u * D + ez) : nullptr;
+    const int ez = e - SE;
+    base = (f32x4_t*)(ws_z + (int64_t)u * nseg * dk + ez);
+    stride = dk / 4;
+    init = z_in ? (const f32x4_t*)(z_in + (int64_t)u * dk + ez) : nullptr;
   }
   f32x4_t acc = init ? *init : f32x4_t{0.f, 0.f, 0.f, 0.f};
   f32x4_t x[kSegBatch];
@@ -716,20 +729,21 @@ __global__ __launch_bounds__(kThreads) void seg_prefix_kernel(float* ws_s, float
 // Sum of all segment partials of a unit, in fixed segment order, into slot 0
 // (four consecutive elements per thread, a batch of slots in flight at a time).
 __global__ __launch_bounds__(kThreads) void seg_sum_kernel(float* ws_s, float* ws_z, int U,
-                                                           int nseg, int D, int norm) {
-  const int64_t per4 = ((int64_t)D * D + (norm ? D : 0)) / 4;
+                                                           int nseg, int dk, int dv, int norm) {
+  const int SE = dk * dv;
+  const int64_t per4 = ((int64_t)SE + (norm ? dk : 0)) / 4;
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= (int64_t)U * per4) return;
   const int u = (int)(idx / per4);
   const int e = 4 * (int)(idx % per4);
   f32x4_t* base;
   int64_t stride;
-  if (e < D * D) {
-    base = (f32x4_t*)(ws_s + (int64_t)u * nseg * D * D + e);
-    stride = (int64_t)D * D / 4;
+  if (e < SE) {
+    base = (f32x4_t*)(ws_s + (int64_t)u * nseg * SE + e);
+    stride = SE / 4;
   } else {
-    base = (f32x4_t*)(ws_z + (int64_t)u * nseg * D + (e - D * D));
-    stride = D / 4;
+    base = (f32x4_t*)(ws_z + (int64_t)u * nseg * dk + (e - SE));
+    stride = dk / 4;
   }
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < nseg; s0 += kSegBatch) {
@@ -748,12 +762,20 @@ __global__ __launch_bounds__(kThreads) void seg_sum_kernel(float* ws_s, float* w
 
 template <typename IT, int D, int FM, bool NORM, int MODE>
 static hipError_t launch_one(const ChunkArgs& a, int grid, hipStream_t st) {
+  const dim3 blk(64 * ChunkWaves<D>::NW);
+  if constexpr (D > 32) {
+    if (a.dk != a.dv) {
+      if (a.mask)
+        hipLaunchKernelGGL((chunk_kernel<IT, D, FM, NORM, MODE, true, true>), dim3(grid), blk, 0, st, a);
+      else
+        hipLaunchKernelGGL((chunk_kernel<IT, D, FM, NORM, MODE, false, true>), dim3(grid), blk, 0, st, a);
+      return hipGetLastError();
+    }
+  }
   if (a.mask)
-    hipLaunchKernelGGL((chunk_kernel<IT, D, FM, NORM, MODE, true>), dim3(grid),
-                       dim3(64 * ChunkWaves<D>::NW), 0, st, a);
+    hipLaunchKernelGGL((chunk_kernel<IT, D, FM, NORM, MODE, true>), dim3(grid), blk, 0, st, a);
   else
-    hipLaunchKernelGGL((chunk_kernel<IT, D, FM, NORM, MODE, false>), dim3(grid),
-                       dim3(64 * ChunkWaves<D>::NW), 0, st, a);
+    hipLaunchKernelGGL((chunk_kernel<IT, D, FM, NORM, MODE, false>), dim3(grid), blk, 0, st, a);
   return hipGetLastError();
 }
 
@@ -793,19 +815,19 @@ hipError_t launch_chunk(int mode, int io, int D, int fm, int norm, const ChunkAr
 }
 
 hipError_t launch_seg_prefix(float* ws_s, float* ws_z, const float* s_in, const float* z_in, int U,
-                             int nseg, int D, int norm, hipStream_t st) {
-  const int64_t n = (int64_t)U * ((int64_t)D * D + (norm ? D : 0)) / 4;
+                             int nseg, int dk, int dv, int norm, hipStream_t st) {
+  const int64_t n = (int64_t)U * ((int64_t)dk * dv + (norm ? dk : 0)) / 4;
   const int grid = (int)((n + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(seg_prefix_kernel, dim3(grid), dim3(kThreads), 0, st, ws_s, ws_z, s_in, z_in,
-                     U, nseg, D, norm);
+                     U, nseg, dk, dv, norm);
   return hipGetLastError();
 }
 
-hipError_t launch_seg_sum(float* ws_s, float* ws_z, int U, int nseg, int D, int norm,
+hipError_t launch_seg_sum(float* ws_s, float* ws_z, int U, int nseg, int dk, int dv, int norm,
                           hipStream_t st) {
-  const int64_t n = (int64_t)U * ((int64_t)D * D + (norm ? D : 0)) / 4;
+  const int64_t n = (int64_t)U * ((int64_t)dk * dv + (norm ? dk : 0)) / 4;
   const int grid = (int)((n + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(seg_sum_kernel, dim3(grid), dim3(kThreads), 0, st, ws_s, ws_z, U, nseg, D, norm);
+  hipLaunchKernelGGL(seg_sum_kernel, dim3(grid), dim3(kThreads), 0, st, ws_s, ws_z, U, nseg, dk, dv, norm);
   return hipGetLastError();
 }
 

@@ -36,15 +36,17 @@ __device__ __forceinline__ float load_elem<float>(const float* p, int i) {
 constexpr int kDecodeUnits = 2;
 constexpr int kDecodeThreads = kDecodeUnits * kThreads;
 
-// TPU threads per unit, UPB units per workgroup.
-template <typename DT, int D, int FM, bool NORM, bool NTMP, int TPU = kThreads, int UPB = kDecodeUnits>
+// DK, DV: head sizes of q/k and v; TPU threads per unit, UPB units per
+// workgroup.  Thread (c4, rg) holds columns 4*c4 .. 4*c4+3 of state rows
+// rg + RG*r.
+template <typename DT, int DK, int DV, int FM, bool NORM, bool NTMP, int TPU = kThreads, int UPB = kDecodeUnits>
 __global__ __launch_bounds__(TPU * UPB) void decode_kernel(DecodeArgs a) {
-  constexpr int C4 = D / 4;          // float4 columns per state row
+  constexpr int C4 = DV / 4;         // float4 columns per state row
   constexpr int RG = TPU / C4;       // row groups
-  constexpr int RPT = D / RG;        // rows per thread
-  static_assert(RPT >= 1 && RG * RPT == D && TPU >= D && TPU >= 64, "unsupported head size");
-  __shared__ float fk[UPB][D], fq[UPB][D], zs[UPB][D];
-  __shared__ float part[UPB][RG][D];
+  constexpr int RPT = DK / RG;       // rows per thread
+  static_assert(RPT >= 1 && RG * RPT == DK && TPU >= DK && TPU >= DV && TPU >= 64, "unsupported head size");
+  __shared__ float fk[UPB][DK], fq[UPB][DK], zs[UPB][DK];
+  __shared__ float part[UPB][RG][DV];
   __shared__ float den_s[UPB];
 
   const int ul = threadIdx.x / TPU;  // unit slot in the workgroup
@@ -53,29 +55,29 @@ __global__ __launch_bounds__(TPU * UPB) void decode_kernel(DecodeArgs a) {
   const bool live = u < a.units;  // the last workgroup may hold one unit only
   const int b = u / a.H;
   const int c4 = tid % C4, rg = tid / C4;
-  const float* S = a.s_in + (int64_t)u * D * D;
-  float* So = a.s_out + (int64_t)u * D * D;
+  const float* S = a.s_in + (int64_t)u * DK * DV;
+  float* So = a.s_out + (int64_t)u * DK * DV;
 
   f32x4_t sv[RPT];
   if (live) {
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-      const f32x4_t* p = (const f32x4_t*)(S + (rg + RG * r) * D + 4 * c4);
+      const f32x4_t* p = (const f32x4_t*)(S + (rg + RG * r) * DV + 4 * c4);
       sv[r] = NTMP ? __builtin_nontemporal_load(p) : *p;
     }
   }
   const bool valid = live && (a.mask ? (a.mask[b] != 0) : true);
-  const DT* qp = (const DT*)a.q + (int64_t)u * D;
-  const DT* kp = (const DT*)a.k + (int64_t)u * D;
-  const DT* vp = (const DT*)a.v + (int64_t)u * D;
+  const DT* qp = (const DT*)a.q + (int64_t)u * DK;
+  const DT* kp = (const DT*)a.k + (int64_t)u * DK;
+  const DT* vp = (const DT*)a.v + (int64_t)u * DV;
   float v4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) v4[i] = valid ? load_elem<DT>(vp, 4 * c4 + i) : 0.f;
-  if (live && tid < D) {
+  if (live && tid < DK) {
     const float kf = valid ? phi<FM>(load_elem<DT>(kp, tid), a.eps) : 0.f;
     fk[ul][tid] = kf;
     fq[ul][tid] = phi<FM>(load_elem<DT>(qp, tid), a.eps);
-    if constexpr (NORM) zs[ul][tid] = a.z_in[(int64_t)u * D + tid] + kf;
+    if constexpr (NORM) zs[ul][tid] = a.z_in[(int64_t)u * DK + tid] + kf;
   }
   __syncthreads();
   if (live) {
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(TPU * UPB) void decode_kernel(DecodeArgs a) {
     if (valid || So != S) {
 #pragma unroll
       for (int r = 0; r < RPT; ++r) {
-        f32x4_t* p = (f32x4_t*)(So + (rg + RG * r) * D + 4 * c4);
+        f32x4_t* p = (f32x4_t*)(So + (rg + RG * r) * DV + 4 * c4);
         if constexpr (NTMP)
           __builtin_nontemporal_store(sv[r], p);
         else
@@ -105,22 +107,22 @@ __global__ __launch_bounds__(TPU * UPB) void decode_kernel(DecodeArgs a) {
     if constexpr (NORM) {
       if (tid < 64) {
         float d = 0.f;
-        for (int i = tid; i < D; i += 64) d = fmaf(fq[ul][i], zs[ul][i], d);
+        for (int i = tid; i < DK; i += 64) d = fmaf(fq[ul][i], zs[ul][i], d);
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
         if (tid == 0) den_s[ul] = d + a.eps;
       }
-      if (tid < D && (valid || a.z_out != a.z_in)) a.z_out[(int64_t)u * D + tid] = zs[ul][tid];
+      if (tid < DK && (valid || a.z_out != a.z_in)) a.z_out[(int64_t)u * DK + tid] = zs[ul][tid];
     }
   }
   __syncthreads();
-  if (live && tid < D) {
+  if (live && tid < DV) {
     float y = 0.f;
 #pragma unroll
     for (int g = 0; g < RG; ++g) y += part[ul][g][tid];
     if constexpr (NORM) y = y / den_s[ul];
     if (!valid) y = 0.f;
-    DT* op = (DT*)a.out + (int64_t)u * D;
+    DT* op = (DT*)a.out + (int64_t)u * DV;
     if constexpr (std::is_same_v<DT, uint16_t>)
       op[tid] = (uint16_t)f32_to_bf16_bits(y);
     else
@@ -432,46 +434,58 @@ struct DecodeShape {
   static constexpr int UPB = D == 128 ? 1 : kDecodeUnits;
 };
 
-template <typename DT, int D, int FM, bool NORM>
+// (the shape follows the larger head size)
+template <typename DT, int DK, int DV, int FM, bool NORM>
 static void launch_k(bool ntmp, const DecodeArgs& a, int grid, hipStream_t st) {
-  constexpr int TPU = DecodeShape<D>::TPU, UPB = DecodeShape<D>::UPB;
+  constexpr int DM = DK > DV ? DK : DV;
+  constexpr int TPU = DecodeShape<DM>::TPU, UPB = DecodeShape<DM>::UPB;
   if (ntmp)
-    hipLaunchKernelGGL((decode_kernel<DT, D, FM, NORM, true, TPU, UPB>), dim3(grid), dim3(TPU * UPB), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<DT, DK, DV, FM, NORM, true, TPU, UPB>), dim3(grid), dim3(TPU * UPB), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_kernel<DT, D, FM, NORM, false, TPU, UPB>), dim3(grid), dim3(TPU * UPB), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<DT, DK, DV, FM, NORM, false, TPU, UPB>), dim3(grid), dim3(TPU * UPB), 0, st, a);
 }
 
-template <typename DT, int D>
+template <typename DT, int DK, int DV>
 static hipError_t launch_d(int fm, int norm, const DecodeArgs& a, int units, hipStream_t st) {
   // states larger than the on-chip caches stream past them (non-temporal)
-  const bool ntmp = (int64_t)units * D * D * 4 >= ((int64_t)256 << 20);
-  const int grid = (units + DecodeShape<D>::UPB - 1) / DecodeShape<D>::UPB;
+  const bool ntmp = (int64_t)units * DK * DV * 4 >= ((int64_t)256 << 20);
+  constexpr int DM = DK > DV ? DK : DV;
+  const int grid = (units + DecodeShape<DM>::UPB - 1) / DecodeShape<DM>::UPB;
   if (fm == kEluPlusOne) {
-    if (norm) launch_k<DT, D, kEluPlusOne, true>(ntmp, a, grid, st);
-    else launch_k<DT, D, kEluPlusOne, false>(ntmp, a, grid, st);
+    if (norm) launch_k<DT, DK, DV, kEluPlusOne, true>(ntmp, a, grid, st);
+    else launch_k<DT, DK, DV, kEluPlusOne, false>(ntmp, a, grid, st);
   } else {
-    if (norm) launch_k<DT, D, kReluEps, true>(ntmp, a, grid, st);
-    else launch_k<DT, D, kReluEps, false>(ntmp, a, grid, st);
+    if (norm) launch_k<DT, DK, DV, kReluEps, true>(ntmp, a, grid, st);
+    else launch_k<DT, DK, DV, kReluEps, false>(ntmp, a, grid, st);
   }
   return hipGetLastError();
 }
 
-template <typename DT>
-static hipError_t launch_dt(int D, int fm, int norm, const DecodeArgs& a, int units, hipStream_t st) {
-  switch (D) {
-    case 32: return launch_d<DT, 32>(fm, norm, a, units, st);
-    case 64: return launch_d<DT, 64>(fm, norm, a, units, st);
-    default: return launch_d<DT, 128>(fm, norm, a, units, st);
+template <typename DT, int DK>
+static hipError_t launch_dv(int Dv, int fm, int norm, const DecodeArgs& a, int units, hipStream_t st) {
+  switch (Dv) {
+    case 32: return launch_d<DT, DK, 32>(fm, norm, a, units, st);
+    case 64: return launch_d<DT, DK, 64>(fm, norm, a, units, st);
+    default: return launch_d<DT, DK, 128>(fm, norm, a, units, st);
   }
 }
 
-hipError_t launch_decode(int io, int D, int fm, int norm, const DecodeArgs& a, int units,
+template <typename DT>
+static hipError_t launch_dt(int Dk, int Dv, int fm, int norm, const DecodeArgs& a, int units, hipStream_t st) {
+  switch (Dk) {
+    case 32: return launch_dv<DT, 32>(Dv, fm, norm, a, units, st);
+    case 64: return launch_dv<DT, 64>(Dv, fm, norm, a, units, st);
+    default: return launch_dv<DT, 128>(Dv, fm, norm, a, units, st);
+  }
+}
+
+hipError_t launch_decode(int io, int Dk, int Dv, int fm, int norm, const DecodeArgs& a, int units,
                          hipStream_t st) {
   if (units <= 0) return hipSuccess;
   switch (io) {
-    case kIoBF16: return launch_dt<uint16_t>(D, fm, norm, a, units, st);
-    case kIoF16: return launch_dt<f16_t>(D, fm, norm, a, units, st);
-    default: return launch_dt<float>(D, fm, norm, a, units, st);
+    case kIoBF16: return launch_dt<uint16_t>(Dk, Dv, fm, norm, a, units, st);
+    case kIoF16: return launch_dt<f16_t>(Dk, Dv, fm, norm, a, units, st);
+    default: return launch_dt<float>(Dk, Dv, fm, norm, a, units, st);
   }
 }
 

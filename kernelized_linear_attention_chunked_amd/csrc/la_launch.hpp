@@ -34,6 +34,11 @@ struct ChunkArgs {
   // spread over all segments of a unit
   int32_t chunk_step;
   float eps;
+  // head sizes when they differ (Dk != Dv): the kernel runs at the larger, D,
+  // with the smaller side zero-padded (feature map of padded q/k dims 0); q, k
+  // rows are (.., H, dk), v, out rows (.., H, dv), states dk x dv (+ dk).
+  // 0 = both D.
+  int32_t dk, dv;
 };
 
 enum { kModeCausal = 0, kModeState = 1 };
@@ -42,9 +47,10 @@ enum { kIoF32 = 0, kIoBF16 = 1, kIoF16 = 2 };
 
 hipError_t launch_chunk(int mode, int io, int D, int fm, int norm, const ChunkArgs& a, int grid,
                         hipStream_t st);
+// slots of dk x dv (+ dk with the normaliser) floats
 hipError_t launch_seg_prefix(float* ws_s, float* ws_z, const float* s_in, const float* z_in, int U,
-                             int nseg, int D, int norm, hipStream_t st);
-hipError_t launch_seg_sum(float* ws_s, float* ws_z, int U, int nseg, int D, int norm,
+                             int nseg, int dk, int dv, int norm, hipStream_t st);
+hipError_t launch_seg_sum(float* ws_s, float* ws_z, int U, int nseg, int dk, int dv, int norm,
                           hipStream_t st);
 
 // Non-causal readout with a fixed summed state (la_apply.hip).  Workgroup
@@ -61,12 +67,14 @@ struct ApplyArgs {
   int32_t T, H;
   int32_t seg_count;
   float eps;
+  int32_t dk, dv;  // as ChunkArgs (0 = both D); s is dk x dv, z dk
 };
 int apply_groups_per_unit(int64_t U, int64_t T);
 hipError_t launch_apply(int io, int D, int fm, int norm, const ApplyArgs& a, int grid,
                         hipStream_t st);
 
-// T == 1 decode step (la_decode.hip).  q,k,v,out: (B,H,D); state (B,H,D,D)+(B,H,D).
+// T == 1 decode step (la_decode.hip).  q,k: (B,H,Dk); v,out: (B,H,Dv); state
+// (B,H,Dk,Dv)+(B,H,Dk).
 struct DecodeArgs {
   const void* q;
   const void* k;
@@ -81,7 +89,7 @@ struct DecodeArgs {
   int32_t units;  // B*H
   float eps;
 };
-hipError_t launch_decode(int io, int D, int fm, int norm, const DecodeArgs& a, int units,
+hipError_t launch_decode(int io, int Dk, int Dv, int fm, int norm, const DecodeArgs& a, int units,
                          hipStream_t st);
 
 // Zero fill (la_decode.hip).

@@ -61,7 +61,13 @@ def test_forward_argument_errors(lib):
     assert fwd(lib, B=-1) == SHAPE
     assert fwd(lib, H=0) == SHAPE
     assert fwd(lib, Dk=48, Dv=48) == UNSUPPORTED
-    assert fwd(lib, Dk=64, Dv=128) == UNSUPPORTED
+    assert fwd(lib, Dk=64, Dv=96) == UNSUPPORTED
+    # Dk != Dv is accepted (each 32, 64 or 128): its checks use each side's size
+    assert fwd(lib, Dk=64, Dv=128, causal=0) == WORKSPACE
+    n = ctypes.c_size_t(0)
+    assert lib.la_workspace_size(4, 16384, 16, 64, 128, 1, 0, ctypes.byref(n)) == OK
+    assert n.value == 64 * 8 * (64 * 128 + 64) * 4
+    assert fwd(lib, Dk=128, Dv=32, out=0x10000 + 2 * 100 * 4 * 128 * 2 - 16) == BAD_ARG  # out inside q (Dk wide)
     assert fwd(lib, fm=5) == BAD_ARG
     assert fwd(lib, eps=-1.0) == BAD_ARG
     assert fwd(lib, eps=float("nan")) == BAD_ARG
@@ -131,6 +137,7 @@ def test_step_argument_errors(lib):
     assert step(norm=0) == STATE              # k parts given without the normalizer
     assert step(dt=3) == DTYPE
     assert step(Dk=96, Dv=96) == UNSUPPORTED
+    assert step(Dk=128, Dv=64, out=f(0x10000 + 2 * 3 * 128 * 2 - 16)) == BAD_ARG  # out inside q (Dk wide)
     assert step(out=f(0x10000)) == BAD_ARG    # out aliases q
     assert step(so=f((1 << 32) + 512)) == BAD_ARG
 
@@ -254,6 +261,7 @@ def test_backward_argument_errors(lib):
     assert g(dk=f(5 << 30)) == BAD_ARG        # dk overlaps dq
     assert g(ws=None, wsb=0) == WORKSPACE
     assert g(Dk=96, Dv=96) == UNSUPPORTED
+    assert g(Dk=64, Dv=128) == UNSUPPORTED   # the backward needs Dk == Dv
     assert g(B=0) == OK
 
 
