@@ -25,12 +25,13 @@ hipError_t launch_chunk(int mode, int io, int D, int fm, int norm, const ChunkAr
        "chunk");
   return hipSuccess;
 }
-hipError_t launch_seg_prefix(float* s, float*, const float*, const float*, int U, int nseg, int D, int, hipStream_t) {
-  seen(s && U > 0 && nseg > 1 && D > 0, "seg_prefix");
+hipError_t launch_seg_prefix(float* s, float*, const float*, const float*, int U, int nseg, int dk, int dv, int,
+                             hipStream_t) {
+  seen(s && U > 0 && nseg > 1 && dk > 0 && dv > 0, "seg_prefix");
   return hipSuccess;
 }
-hipError_t launch_seg_sum(float* s, float*, int U, int nseg, int D, int, hipStream_t) {
-  seen(s && U > 0 && nseg > 0 && D > 0, "seg_sum");
+hipError_t launch_seg_sum(float* s, float*, int U, int nseg, int dk, int dv, int, hipStream_t) {
+  seen(s && U > 0 && nseg > 0 && dk > 0 && dv > 0, "seg_sum");
   return hipSuccess;
 }
 int apply_groups_per_unit(int64_t U, int64_t T) { return T > 4096 ? 8 : (U > 0 ? 1 : 0); }
@@ -38,8 +39,8 @@ hipError_t launch_apply(int, int D, int, int, const ApplyArgs& a, int grid, hipS
   seen(grid > 0 && a.s && D > 0, "apply");
   return hipSuccess;
 }
-hipError_t launch_decode(int, int D, int, int, const DecodeArgs& a, int units, hipStream_t) {
-  seen(units > 0 && a.s_in && a.s_out && D > 0, "decode");
+hipError_t launch_decode(int, int Dk, int Dv, int, int, const DecodeArgs& a, int units, hipStream_t) {
+  seen(units > 0 && a.s_in && a.s_out && Dk > 0 && Dv > 0, "decode");
   return hipSuccess;
 }
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t) {
@@ -123,16 +124,17 @@ int main() {
   for (int causal = 0; causal < 2; ++causal)
     for (int dt = 0; dt < 3; ++dt)
       for (int64_t D : {32, 64, 128})
-        for (int64_t T : {0, 1, 63, 64, 200, 4096})
-          for (int64_t BH : {1, 6, 512, 4096}) {
-            expect(la_workspace_size(1, T, BH, D, D, dt, causal, &n), LA_OK, "workspace_size");
-            const uintptr_t ws = n ? 9 * G1 : 0;
-            expect(la_forward(P(G1), P(2 * G1), P(3 * G1), nullptr, causal ? F(4 * G1) : nullptr,
-                              causal ? F(5 * G1) : nullptr, causal ? F(6 * G1) : nullptr,
-                              causal ? F(7 * G1) : nullptr, causal, (int)(T % 2), 1, 1e-6f, P(8 * G1), 1, T, BH, D,
-                              D, dt, P(ws), n, nullptr),
-                   LA_OK, "forward");
-          }
+        for (int64_t Dv : {32, 64, 128})
+          for (int64_t T : {0, 1, 63, 64, 200, 4096})
+            for (int64_t BH : {1, 6, 512, 4096}) {
+              expect(la_workspace_size(1, T, BH, D, Dv, dt, causal, &n), LA_OK, "workspace_size");
+              const uintptr_t ws = n ? 9 * G1 : 0;
+              expect(la_forward(P(G1), P(2 * G1), P(3 * G1), nullptr, causal ? F(4 * G1) : nullptr,
+                                causal ? F(5 * G1) : nullptr, causal ? F(6 * G1) : nullptr,
+                                causal ? F(7 * G1) : nullptr, causal, (int)(T % 2), 1, 1e-6f, P(8 * G1), 1, T, BH,
+                                D, Dv, dt, P(ws), n, nullptr),
+                     LA_OK, "forward");
+            }
   // argument errors
   expect(la_forward(P(G1), P(2 * G1), P(3 * G1), nullptr, nullptr, nullptr, nullptr, nullptr, 1, 0, 1, 1e-6f,
                     P(G1 + 64), 2, 100, 4, 64, 64, 1, nullptr, 0, nullptr),
@@ -152,9 +154,10 @@ int main() {
   // decode steps
   for (int dt = 0; dt < 3; ++dt)
     for (int64_t D : {32, 64, 128})
-      expect(la_step(P(G1), P(2 * G1), P(3 * G1), nullptr, F(4 * G1), F(5 * G1), F(4 * G1), F(5 * G1), 0, 1, 1e-6f,
-                     P(8 * G1), 256, 32, D, D, dt, nullptr),
-             LA_OK, "step");
+      for (int64_t Dv : {32, 64, 128})
+        expect(la_step(P(G1), P(2 * G1), P(3 * G1), nullptr, F(4 * G1), F(5 * G1), F(4 * G1), F(5 * G1), 0, 1,
+                       1e-6f, P(8 * G1), 256, 32, D, Dv, dt, nullptr),
+               LA_OK, "step");
   // gated, per-dim, delta: any group size, every decay kind
   for (int dt = 0; dt < 3; ++dt)
     for (int64_t D : {32, 64, 128})
