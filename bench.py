@@ -247,6 +247,64 @@ def bench_streaming(args, log):
     return rec
 
 
+def cpu_baseline_workload(d, name, target_s, log):
+    """The fp64 oracle (as it stands) on a bounded sample of a workload's own
+    inputs: whole batch rows (all heads), as many as fit about target_s
+    seconds, scaled to tokens/s of the same kind as the GPU figure."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()
+
+    def run(nb):
+        """Oracle time for batch rows 0..nb-1, and the tokens they cover."""
+        if name in ("causal_bf16_d64", "causal_fp32_small"):
+            q, k, v = (f64(t[:nb]) for t in (d.q, d.k, d.v))
+            t0 = time.perf_counter()
+            oracle.causal(q, k, v)
+            return time.perf_counter() - t0, nb * d.T
+        if name == "noncausal_relu_d128":
+            q, k, v = (f64(t[:nb]) for t in (d.q, d.k, d.v))
+            m = d.mask[:nb].cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.noncausal(q, k, v, m, "relu", True, 1e-6)
+            return time.perf_counter() - t0, nb * d.T
+        if name == "backward_bf16_d64":
+            q, k, v, dy = (f64(t[:nb]) for t in (d.q, d.k, d.v, d.dy))
+            t0 = time.perf_counter()
+            oracle.causal_backward(q, k, v, dy)
+            return time.perf_counter() - t0, nb * d.T
+        if name in ("gated_step_d128", "delta_step_d128"):
+            # step-major inputs (T, B, ...): the oracle runs the same tokens per row
+            tb = lambda t: f64(t[:, :nb].transpose(0, 1))
+            beta = tb(d.beta) if name == "delta_step_d128" else None
+            rule = "gated_delta" if name == "delta_step_d128" else "gated"
+            past = f64(d.state[:nb])
+            args_ = (tb(d.q), tb(d.k), tb(d.v), d.Hq, d.Hkv, rule)
+            t0 = time.perf_counter()
+            oracle.la_op(*args_, decay=tb(d.g), beta=beta, past_state=past, scale=d.scale)
+            return time.perf_counter() - t0, nb * d.T
+        # gated, per-dim, gated delta: packed (B, T, ...) inputs
+        rule = "gated_delta" if name == "gated_delta_d128" else "gated"
+        beta = f64(d.beta[:nb]) if name == "gated_delta_d128" else None
+        q, k, v, g = (f64(t[:nb]) for t in (d.q, d.k, d.v, d.g))
+        t0 = time.perf_counter()
+        oracle.la_op(q, k, v, d.Hq, d.Hkv, rule, decay=g, beta=beta, scale=d.scale)
+        return time.perf_counter() - t0, nb * d.T
+
+    # the row is the unit of the sample; long rows are cut to a token prefix
+    t1, tok1 = run(1)
+    nb = int(max(1, min(d.B, round(target_s / max(t1, 1e-3)))))
+    log("cpu_baseline %s: 1 batch row took %.2f s; timing %d rows" % (name, t1, nb))
+    if nb > 1:
+        t1, tok1 = run(nb)
+    return {"value": tok1 / t1, "unit": "tokens/s", "cores": oracle.max_threads(), "cpu_model": _cpu_model(),
+            "host_cpus": os.cpu_count(), "kind": "oracle", "seconds": round(t1, 3),
+            "sample": "batch rows 0..%d of %d (all heads), every token of the workload's step" % (nb - 1, d.B)}
+
+
 def bench_other(args, log):
     """One extra line for a non-default workload: median step time over at least 20
     timed steps after at least 3 warm-up steps and 0.3 s of warm-up, tokens/s, algorithmic GB/s and the
@@ -339,6 +397,8 @@ def bench_other(args, log):
            "mfma_util_algorithmic": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), **extra}
     if d.q.dtype.itemsize == 4:
         rec["dtype"] = "f32"
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_workload(d, args.workload, args.cpu_baseline_seconds, log)
     if args.workload == "causal_bf16_d64":
         cold = [d] + [workloads.DRIVERS[args.workload]("cuda:0") for _ in range(7)]
         ms_cold = median_ms(cold)
