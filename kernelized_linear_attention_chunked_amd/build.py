@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "liblinattn.so")
 
 SOURCES = ["la_api.cpp", "la_chunk.hip", "la_decode.hip", "la_gated.hip", "la_gated_pd.hip",
-           "la_delta.hip", "la_backward.hip", "la_apply.hip", "la_recur.hip"]
+           "la_delta.hip", "la_backward.hip", "la_apply.hip", "la_recur.hip", "la_bwd_chunk.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON_FLAGS = [

@@ -926,14 +926,61 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t D, int64_t esz, bo
   L.total = off;
   return L;
 }
+
+// The chunk-parallel backward (16-bit inputs, head sizes 32 or 64): the
+// forward segment states and the reverse gradient sums in slots (split
+// sequences only), dnum and dden per token.
+struct BwdChunkLayout {
+  int64_t nseg, seg_len;
+  size_t fs, fz, rs, rz, dnum, dden, total;
+};
+BwdChunkLayout bwd_chunk_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, bool norm) {
+  const int64_t U = B * H;
+  const CausalPlan p = plan_causal(U, T);
+  BwdChunkLayout L;
+  L.nseg = p.nseg;
+  L.seg_len = p.seg_chunks * kChunk;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += al(bytes);
+    return o;
+  };
+  const size_t slots = p.nseg > 1 ? (size_t)(U * p.nseg) : 0;
+  L.fs = take(slots * Dk * Dv * 4);
+  L.fz = take(norm ? slots * Dk * 4 : 0);
+  L.rs = take(slots * Dk * Dv * 4);
+  L.rz = take(norm ? slots * Dk * 4 : 0);
+  L.dnum = take((size_t)(B * T * H * Dv) * 4);
+  L.dden = take(norm ? (size_t)(B * T * H) * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+// which backward runs: 1 chunk-parallel, 0 the recurrence-based one (head sizes
+// equal), -1 none
+int bwd_path(int32_t dtype, int64_t Dk, int64_t Dv) {
+  if ((dtype == LA_DT_BF16 || dtype == LA_DT_F16) && (Dk == 32 || Dk == 64) && (Dv == 32 || Dv == 64)) return 1;
+  return Dk == Dv ? 0 : -1;
+}
 }  // namespace
 
 LA_EXPORT la_status la_backward_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,
                                                int32_t dtype, int32_t use_normalizer, size_t* bytes) {
   if (!bytes) return fail(LA_ERR_NULL_ARG, "bytes is NULL");
-  la_status s = check_common(B, T, H, Dk, Dv, dtype, false);
+  la_status s = check_common(B, T, H, Dk, Dv, dtype);
   if (s != LA_OK) return s;
-  *bytes = (B * H == 0 || T == 0) ? 0 : bwd_layout(B, T, H, Dk, dtype_size(dtype), use_normalizer != 0).total;
+  const int path = bwd_path(dtype, Dk, Dv);
+  if (path < 0)
+    return fail(LA_ERR_UNSUPPORTED, "la_backward: Dk=%lld != Dv=%lld needs 16-bit inputs and head sizes 32 or 64",
+                (long long)Dk, (long long)Dv);
+  const bool norm = use_normalizer != 0;
+  if (B * H == 0 || T == 0)
+    *bytes = 0;
+  else
+    *bytes = path == 1 ? bwd_chunk_layout(B, T, H, Dk, Dv, norm).total
+                       : bwd_layout(B, T, H, Dk, dtype_size(dtype), norm).total;
   return ok();
 }
 
@@ -944,13 +991,17 @@ LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, con
                                 float* dstate_in_kv, float* dstate_in_k, int64_t B, int64_t T, int64_t H,
                                 int64_t Dk, int64_t Dv, int32_t dtype, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  la_status s = check_common(B, T, H, Dk, Dv, dtype, false);
+  la_status s = check_common(B, T, H, Dk, Dv, dtype);
   if (s != LA_OK) return s;
+  const int path = bwd_path(dtype, Dk, Dv);
+  if (path < 0)
+    return fail(LA_ERR_UNSUPPORTED, "la_backward: Dk=%lld != Dv=%lld needs 16-bit inputs and head sizes 32 or 64",
+                (long long)Dk, (long long)Dv);
   if (feature_map != LA_FM_ELU_PLUS_ONE && feature_map != LA_FM_RELU_EPS)
     return fail(LA_ERR_BAD_ARG, "feature_map %d is not 0 (elu+1) or 1 (relu+eps)", feature_map);
   if (!(eps >= 0.f) || isinf(eps)) return fail(LA_ERR_BAD_ARG, "eps must be finite and >= 0");
   const bool norm = use_normalizer != 0;
-  const int64_t D = Dk, U = B * H, SE = U * D * D;
+  const int64_t D = Dk, U = B * H, SE = U * Dk * Dv;
   const int64_t esz = dtype_size(dtype);
   if (U == 0) return ok();
   if (!dstate_in_kv || (norm && !dstate_in_k))
@@ -970,14 +1021,15 @@ LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, con
       !aligned16(dv) || !aligned16(state_in_kv) || !aligned16(state_in_k) || !aligned16(dstate_out_kv) ||
       !aligned16(dstate_out_k) || !aligned16(dstate_in_kv) || !aligned16(dstate_in_k) || !aligned16(workspace))
     return fail(LA_ERR_BAD_ARG, "q, k, v, dout, dq, dk, dv, the states and the workspace must be 16-byte aligned");
-  const int64_t nb = B * T * H * D * esz;
-  const BwdLayout L = bwd_layout(B, T, H, D, esz, norm);
-  const size_t need = work ? L.total : 0;
-  const Range ins[9] = {range(q, nb), range(k, nb), range(v, nb), range(dout, nb), range(mask, B * T),
-                        range(state_in_kv, SE * 4), range(state_in_k, U * D * 4),
-                        range(dstate_out_kv, SE * 4), range(dstate_out_k, U * D * 4)};
-  const Range outs[6] = {range(dq, nb), range(dk, nb), range(dv, nb), range(dstate_in_kv, SE * 4),
-                         range(dstate_in_k, U * D * 4), range(workspace, (int64_t)need)};
+  const int64_t nbk = B * T * H * Dk * esz, nbv = B * T * H * Dv * esz;
+  const size_t need = !work ? 0
+                            : (path == 1 ? bwd_chunk_layout(B, T, H, Dk, Dv, norm).total
+                                         : bwd_layout(B, T, H, D, esz, norm).total);
+  const Range ins[9] = {range(q, nbk), range(k, nbk), range(v, nbv), range(dout, nbv), range(mask, B * T),
+                        range(state_in_kv, SE * 4), range(state_in_k, U * Dk * 4),
+                        range(dstate_out_kv, SE * 4), range(dstate_out_k, U * Dk * 4)};
+  const Range outs[6] = {range(dq, nbk), range(dk, nbk), range(dv, nbv), range(dstate_in_kv, SE * 4),
+                         range(dstate_in_k, U * Dk * 4), range(workspace, (int64_t)need)};
   for (int i = 0; i < 6; ++i) {
     for (const Range& r : ins)
       if (overlap(outs[i], r)) return fail(LA_ERR_BAD_ARG, "an output or the workspace overlaps an input");
@@ -998,6 +1050,94 @@ LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, con
   }
   unsigned char* W = (unsigned char*)workspace;
   auto F = [&](size_t off) { return (float*)(W + off); };
+  if (path == 1) {
+    // chunk-parallel: forward segment states (split sequences), the forward
+    // pass over every segment, the reverse prefix of its gradient sums, the
+    // reverse pass
+    const BwdChunkLayout C = bwd_chunk_layout(B, T, H, Dk, Dv, norm);
+    const int64_t nseg = C.nseg, ZE = Dk;
+    la::BwdChunkArgs c;
+    memset(&c, 0, sizeof(c));
+    c.q = q;
+    c.k = k;
+    c.v = v;
+    c.dy = dout;
+    c.mask = mask;
+    c.dnum = F(C.dnum);
+    c.dden = norm ? F(C.dden) : nullptr;
+    c.dq = dq;
+    c.dk = dk;
+    c.dv = dv;
+    c.T = (int32_t)T;
+    c.H = (int32_t)H;
+    c.nseg = (int32_t)nseg;
+    c.seg_len = (int32_t)C.seg_len;
+    c.fm = feature_map;
+    c.eps = eps;
+    if (nseg > 1) {
+      // segments 0..nseg-2 -> slots 1..nseg-1, then the prefix (slot 0 = state_in)
+      la::BwdChunkArgs ps = c;
+      ps.nseg = (int32_t)(nseg - 1);
+      ps.s_out = F(C.fs);
+      ps.z_out = norm ? F(C.fz) : nullptr;
+      ps.s_out_u = nseg * Dk * Dv;
+      ps.s_out_s = Dk * Dv;
+      ps.z_out_u = nseg * ZE;
+      ps.z_out_s = ZE;
+      e = la::launch_bwd_chunk(2, dtype, (int)Dk, (int)Dv, norm, ps, (int)(U * (nseg - 1)), st);
+      if (e == hipSuccess)
+        e = la::launch_seg_prefix(F(C.fs), norm ? F(C.fz) : nullptr, state_in_kv, state_in_k, (int)U, (int)nseg,
+                                  (int)Dk, (int)Dv, norm, st);
+      if (e != hipSuccess) return device_status(e, "la_backward");
+    }
+    la::BwdChunkArgs c0 = c;
+    if (nseg > 1) {
+      c0.s_in = F(C.fs);
+      c0.z_in = norm ? F(C.fz) : nullptr;
+      c0.s_in_u = nseg * Dk * Dv;
+      c0.s_in_s = Dk * Dv;
+      c0.z_in_u = nseg * ZE;
+      c0.z_in_s = ZE;
+      c0.s_out = F(C.rs);
+      c0.z_out = norm ? F(C.rz) : nullptr;
+      c0.s_out_u = nseg * Dk * Dv;
+      c0.s_out_s = Dk * Dv;
+      c0.z_out_u = nseg * ZE;
+      c0.z_out_s = ZE;
+    } else {
+      c0.s_in = state_in_kv;
+      c0.z_in = state_in_k;
+      c0.s_in_u = Dk * Dv;
+      c0.z_in_u = ZE;
+    }
+    e = la::launch_bwd_chunk(0, dtype, (int)Dk, (int)Dv, norm, c0, (int)(U * nseg), st);
+    if (e == hipSuccess && nseg > 1)
+      e = la::launch_seg_prefix(F(C.rs), norm ? F(C.rz) : nullptr, dstate_out_kv, dstate_out_k, (int)U, (int)nseg,
+                                (int)Dk, (int)Dv, norm, st);
+    if (e != hipSuccess) return device_status(e, "la_backward");
+    la::BwdChunkArgs c1 = c;
+    if (nseg > 1) {
+      c1.s_in = F(C.rs);
+      c1.z_in = norm ? F(C.rz) : nullptr;
+      c1.s_in_u = nseg * Dk * Dv;
+      c1.s_in_s = Dk * Dv;
+      c1.z_in_u = nseg * ZE;
+      c1.z_in_s = ZE;
+    } else {
+      c1.s_in = dstate_out_kv;
+      c1.z_in = dstate_out_k;
+      c1.s_in_u = Dk * Dv;
+      c1.z_in_u = ZE;
+    }
+    c1.s_out = dstate_in_kv;
+    c1.z_out = dstate_in_k;
+    c1.s_out_u = Dk * Dv;
+    c1.z_out_u = ZE;
+    e = la::launch_bwd_chunk(1, dtype, (int)Dk, (int)Dv, norm, c1, (int)(U * nseg), st);
+    return device_status(e, "la_backward");
+  }
+  // the recurrence-based backward (fp32 inputs, head size 128)
+  const BwdLayout L = bwd_layout(B, T, H, D, esz, norm);
   la::BwdArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;

@@ -1,0 +1,1036 @@
+// Chunk-parallel causal backward for 16-bit inputs (bf16, fp16) at head sizes
+// Dk, Dv in {32, 64}: the gradients of the normalized causal recurrence of
+// "[Feature] LinearAttention layer for Keras" ("Mathematical definition /
+// Causal"; "Stability" and "Acceptance" ask for the gradients and their
+// float64 checks).  Per (batch, head) unit, with phi_q = phi(q), phi_k = phi(k)
+// (0 at invalid tokens), S_i, z_i the running sums through token i, and
+// num_i = S_i^T phi_q_i, den_i = phi_q_i . z_i + eps, y_i = num_i / den_i:
+//   dnum_i = m_i dy_i / den_i,  dden_i = -dnum_i . y_i     (normalized; else dnum_i = m_i dy_i, dden_i = 0)
+//   B_ij   = dnum_i . v_j + dden_i                          (j <= i)
+//   dphi_q_i = sum_{j<=i} B_ij phi_k_j + S_prev dnum_i + dden_i z_prev
+//   dphi_k_j = sum_{i>=j} B_ij phi_q_i + dS_next v_j + dz_next
+//   dv_j     = sum_{i>=j} (phi_q_i . phi_k_j) dnum_i + dS_next^T phi_k_j
+//   dS_0 = dS_T + sum_i phi_q_i dnum_i^T,  dz_0 = dz_T + sum_i phi_q_i dden_i,
+// where within a chunk S_prev, z_prev are the sums before it and dS_next,
+// dz_next the gradient sums of the tokens after it (dS_T, dz_T included).
+//
+// A sequence is cut into segments (the forward's causal split):
+//   bwd_state_kernel sums phi_k v^T (phi_k) over each segment but the last,
+//                   and a prefix over those sums gives each segment its
+//                   forward state at the start;
+//   bwd_fwd_kernel  runs each segment forward in 32-token chunks with S, z in
+//                   registers: dq, dnum and dden per token (dnum, dden to the
+//                   workspace), and the segment's sum of phi_q dnum^T, phi_q dden;
+//   (a prefix over those sums, in reverse segment order, gives each segment
+//   its dS_next, dz_next at the segment end)
+//   bwd_rev_kernel  runs each segment backwards with dS, dz in registers: dk,
+//                   dv, and dS_0, dz_0 from the first segment.
+//
+// Precision: the gradients cancel strongly (dden_i removes the dnum-weighted
+// mean of the values from every B_ij, and the state terms carry the same
+// offset), so a single bf16 rounding of any operand costs up to ~1e-1 relative
+// error.  Every operand is therefore fed as bf16 hi + lo parts (hi = x rounded,
+// lo = the remainder rounded) and every product takes hi*hi + hi*lo + lo*hi,
+// about 16 significant bits; only operands that are exact in bf16 (the values
+// of bf16 inputs, the ones of the normaliser rows) go as one part.
+//
+// Layout (8 wavefronts, one workgroup per (unit, segment)): every matrix a
+// product contracts over sits in LDS with its contraction index contiguous,
+// row-major with 16 bytes of row padding, hi part then lo part.  A product
+// C += A B^T takes A's rows from one matrix and B's from another (see
+// la_device.hpp for the MFMA lane layout).  The intra-chunk scores feed the
+// next product straight from registers: a pair of score tiles whose A rows are
+// the keys (queries) 8(r/4) + 4 odd + r%4 leaves lane group lg holding keys
+// (queries) 8lg..8lg+7 of one column, which is the operand layout of a
+// 32-wide contraction over them.
+#include <type_traits>
+
+#include "la_device.hpp"
+#include "la_launch.hpp"
+
+namespace la {
+namespace {
+
+constexpr int kBC = 32;        // tokens per chunk
+constexpr int kBW = 8;         // wavefronts per workgroup
+constexpr int kBT = 64 * kBW;  // threads
+
+__device__ __forceinline__ void mm(f32x4_t& c, const u32x4_t& a, const u32x4_t& b) { Op<uint16_t>::mma(c, a, b); }
+// (ah + al)(bh + bl) without the lo*lo term
+__device__ __forceinline__ void mm3(f32x4_t& c, const u32x4_t& ah, const u32x4_t& al, const u32x4_t& bh,
+                                    const u32x4_t& bl) {
+  mm(c, ah, bh);
+  mm(c, ah, bl);
+  mm(c, al, bh);
+}
+// bf16 hi and lo parts of x (16-bit patterns)
+__device__ __forceinline__ void split1(float x, uint32_t& h, uint32_t& lo) {
+  h = f32_to_bf16_bits(x);
+  lo = f32_to_bf16_bits(x - __uint_as_float(h << 16));
+}
+// hi and lo words of a pair (first value in bits 0..15)
+__device__ __forceinline__ u32x2_t split2(float x0, float x1) {
+  const uint32_t h = pack_bf16x2(x0, x1);
+  return u32x2_t{h, pack_bf16x2(x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xffff0000u))};
+}
+// a score tile pair (rows 8lg + 4odd + q of column lr) as operand words over
+// the 8 rows 8lg .. 8lg+7
+__device__ __forceinline__ void pair_operand(const f32x4_t (&at)[2], u32x4_t& h, u32x4_t& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { const u32x2_t t2_ = split2(at[e >> 1][2 * (e & 1)], at[e >> 1][2 * (e & 1) + 1]); h[e] = t2_[0]; lo[e] = t2_[1]; }
+}
+// four consecutive I/O values as fp32
+template <typename IT>
+__device__ __forceinline__ f32x4_t ld4f(const IT* p) {
+  const u32x2_t w = *(const u32x2_t*)p;
+  return f32x4_t{Io<IT>::to_f32(w[0] & 0xffffu), Io<IT>::to_f32(w[0] >> 16), Io<IT>::to_f32(w[1] & 0xffffu),
+                 Io<IT>::to_f32(w[1] >> 16)};
+}
+__device__ __forceinline__ float phi_rt(float x, bool elu, float eps) {
+  return elu ? phi<kEluPlusOne>(x, eps) : phi<kReluEps>(x, eps);
+}
+// derivative of phi: elu(x)+1 -> 1 (x > 0) or exp(x); relu(x)+eps -> 1 (x > 0) or 0
+__device__ __forceinline__ float dphi_rt(float x, bool elu) {
+  return x > 0.f ? 1.f : (elu ? __expf(x) : 0.f);
+}
+// the two bf16 halves of word w as fp32 (element e of a 16-bit pair)
+__device__ __forceinline__ float bf_at(uint32_t w, int e) {
+  return __uint_as_float(e ? (w & 0xffff0000u) : (w << 16));
+}
+
+// Staging item of a thread: two consecutive tokens (2p, 2p+1) of one 16-byte
+// column block (8 elements) of input matrix m.  The matrices take consecutive
+// thread ranges of sizes N0, N1, N2, N3 (each a multiple of 64, so that every
+// wave stages one matrix), with B0.. blocks per token row.
+struct Item {
+  int m, p, cb;
+  bool on;
+};
+template <int N0, int B0, int N1, int B1, int N2, int B2, int N3 = 0, int B3 = 1>
+__device__ __forceinline__ Item make_item(int tid) {
+  static_assert(N0 % 64 == 0 && N1 % 64 == 0 && N2 % 64 == 0 && N3 % 64 == 0, "wave-uniform matrices");
+  // the matrix and whether the wave stages at all are the same in every lane
+  const int wt = __builtin_amdgcn_readfirstlane(tid & ~63);
+  const int m = wt < N0 ? 0 : (wt < N0 + N1 ? 1 : (wt < N0 + N1 + N2 ? 2 : 3));
+  const bool on = wt < N0 + N1 + N2 + N3;
+  const int r = tid - (m == 0 ? 0 : (m == 1 ? N0 : (m == 2 ? N0 + N1 : N0 + N1 + N2)));
+  const int bl = m == 0 ? B0 : (m == 1 ? B1 : (m == 2 ? B2 : B3));
+  return Item{m, r / bl, r % bl, on};
+}
+
+// ---------------------------------------------------------------------------
+// Forward pass of the backward: LDS layout in 16-bit elements.
+template <int DK, int DV, bool NORM, bool VLO>
+struct FwdLds {
+  static constexpr int LDK = DK + 8, LDV = DV + 8, LDC = kBC + 8, NZ = NORM ? 16 : 0;
+  static constexpr int QRL = kBC * LDK, QTL = DK * LDC, VRL = kBC * LDV, VTL = (DV + NZ) * LDC,
+                       STL = (DV + NZ) * LDK, SRL = DK * LDV, DNL = kBC * LDV, DTL = (DV + NZ) * LDC;
+  static constexpr int QR = 0;                                // phi(Q) [token][dk]
+  static constexpr int QT = QR + 2 * QRL;                     // phi(Q)^T [dk][token]
+  static constexpr int KR = QT + 2 * QTL;                     // phi(K) [token][dk]
+  static constexpr int KT = KR + 2 * QRL;                     // phi(K)^T [dk][token]
+  static constexpr int VR = KT + 2 * QTL;                     // V [token][dv]
+  static constexpr int VT = VR + (VLO ? 2 : 1) * VRL;         // V^T [dv + 16 ones][token]; lo: dv rows
+  static constexpr int ST = VT + VTL + (VLO ? DV * LDC : 0);  // S^T [dv + 16 z][dk]
+  static constexpr int SR = ST + 2 * STL;                     // S [dk][dv]
+  static constexpr int DN = SR + 2 * SRL;                     // dnum [token][dv]
+  static constexpr int DT = DN + 2 * DNL;                     // dnum^T [dv + 16 dden parts][token]
+  static constexpr int TOTAL = DT + 2 * DTL;
+};
+
+template <typename IT, int DK, int DV, bool NORM>
+__global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
+  constexpr bool VLO = !std::is_same_v<IT, uint16_t>;  // fp16 values are not exact in bf16
+  using Ly = FwdLds<DK, DV, NORM, VLO>;
+  constexpr int LDK = Ly::LDK, LDV = Ly::LDV, LDC = Ly::LDC;
+  constexpr int NET = DV / 16, NDT = DK / 16, NZT = NORM ? 1 : 0;
+  constexpr int NST = NDT * (NET + NZT);  // 16x16 tiles of S (+ z) and of the dS sum
+  constexpr int TPW = (NST + kBW - 1) / kBW;
+  constexpr int KSK = DK / 32, KSV = DV / 32;
+  constexpr int NIQ = (kBC / 2) * (DK / 8), NIV = (kBC / 2) * (DV / 8);
+  static_assert(2 * NIQ + NIV <= kBT && NIQ % 64 == 0 && NIV % 64 == 0, "one staging item per thread");
+  __shared__ __align__(16) uint16_t sm[Ly::TOTAL];
+  __shared__ float part[NORM ? NET * kBC : 1];  // dden_i parts per value tile
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int u = blockIdx.x / a.nseg, s = blockIdx.x % a.nseg;
+  const int T = a.T, H = a.H;
+  const int b = u / H, h = u % H;
+  const int t0 = s * a.seg_len;
+  const int t1 = min(T, t0 + a.seg_len);
+  const int64_t HDK = (int64_t)H * DK, HDV = (int64_t)H * DV;
+  const IT* qb = (const IT*)a.q + (int64_t)b * T * HDK + (int64_t)h * DK;
+  const IT* kb = (const IT*)a.k + (int64_t)b * T * HDK + (int64_t)h * DK;
+  const IT* vb = (const IT*)a.v + (int64_t)b * T * HDV + (int64_t)h * DV;
+  const IT* yb = (const IT*)a.dy + (int64_t)b * T * HDV + (int64_t)h * DV;
+  IT* dqb = (IT*)a.dq + (int64_t)b * T * HDK + (int64_t)h * DK;
+  float* dnb = a.dnum + (int64_t)b * T * HDV + (int64_t)h * DV;
+  float* ddb = NORM ? a.dden + (int64_t)b * T * H + h : nullptr;
+  const uint8_t* mb = a.mask ? a.mask + (int64_t)b * T : nullptr;
+  const float eps = a.eps;
+  const bool elu = a.fm == kEluPlusOne;
+  auto valid = [&](int t) { return t < t1 && (mb == nullptr || mb[t] != 0); };
+
+  // ---- S (+ z) tiles and the dS (+ dz) sum: wave w owns tiles w + 8k; tile
+  // (dt, et) holds rows 16dt + 4lg + q (dk), column 16et + lr (dv); the z tile
+  // (et = NET) holds z in every column (the ones rows of V^T), the dz tile the
+  // parts of dden in columns 0 .. NET-1
+  f32x4_t st[TPW], ds[TPW];
+  auto tile = [&](int k, int& dt, int& et) {
+    const int tau = w + kBW * k;
+    dt = tau / (NET + NZT);
+    et = tau % (NET + NZT);
+    return tau < NST;
+  };
+  {
+    const float* sin = a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr;
+    const float* zin = (NORM && a.z_in) ? a.z_in + u * a.z_in_u + s * a.z_in_s : nullptr;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      int dt, et;
+      const bool on = tile(k, dt, et);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = 16 * dt + 4 * lg + q;
+        float x = 0.f;
+        if (on) x = et < NET ? (sin ? sin[d * DV + 16 * et + lr] : 0.f) : (zin ? zin[d] : 0.f);
+        st[k][q] = x;
+        ds[k][q] = 0.f;
+      }
+    }
+  }
+  if constexpr (NORM) {
+    // ones rows of V^T; unused dden rows of dnum^T
+    for (int i = tid; i < 16 * LDC; i += kBT) {
+      sm[Ly::VT + DV * LDC + i] = 0x3f80;  // bf16 1.0
+      if (i >= NET * LDC) {
+        sm[Ly::DT + DV * LDC + i] = 0;
+        sm[Ly::DT + Ly::DTL + DV * LDC + i] = 0;
+      }
+    }
+  }
+
+  // ---- prefetch registers
+  const Item it = make_item<NIQ, DK / 8, NIQ, DK / 8, NIV, DV / 8>(tid);
+  const IT* ibase = it.m == 0 ? qb : (it.m == 1 ? kb : vb);
+  const int64_t ild = it.m == 2 ? HDV : HDK;
+  u32x4_t raw[2];
+  uint32_t rvalid = 0;
+  const int iq = 16 * (w & 1) + lr;  // query row of the lane in a chunk (phases B, C)
+  u32x2_t dyraw = u32x2_t{0u, 0u};
+  bool qv = false;
+  auto prefetch = [&](int c0) {
+    if (it.on) {
+      rvalid = 0;
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int t = c0 + 2 * it.p + n;
+        raw[n] = t < t1 ? ld16(ibase + t * ild + 8 * it.cb) : u32x4_t{0u, 0u, 0u, 0u};
+        rvalid |= (valid(t) ? 1u : 0u) << n;
+      }
+    }
+    const int t = c0 + iq;
+    qv = valid(t);
+    if (w < 2 * NET) dyraw = t < t1 ? *(const u32x2_t*)(yb + t * HDV + 16 * (w >> 1) + 4 * lg) : u32x2_t{0u, 0u};
+  };
+
+  // ---- staging of phi(Q), phi(K), V (rows and transposed) and of S
+  auto stage = [&]() {
+    if (!it.on) return;
+    float f[2][8];
+    Io<IT>::unpack(raw[0], f[0]);
+    Io<IT>::unpack(raw[1], f[1]);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const bool ok = (rvalid >> n) & 1u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[n][e] = ok ? (it.m < 2 ? phi_rt(f[n][e], elu, eps) : f[n][e]) : 0.f;
+    }
+    const int rld = it.m == 2 ? LDV : LDK;
+    const int rbase = it.m == 0 ? Ly::QR : (it.m == 1 ? Ly::KR : Ly::VR);
+    const int rlo = it.m == 2 ? Ly::VRL : Ly::QRL;
+    const int tbase = it.m == 0 ? Ly::QT : (it.m == 1 ? Ly::KT : Ly::VT);
+    const int tlo = it.m == 2 ? Ly::VTL : Ly::QTL;
+    const bool lo_too = it.m < 2 || VLO;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      u32x4_t hw, lw;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { const u32x2_t t2_ = split2(f[n][2 * e], f[n][2 * e + 1]); hw[e] = t2_[0]; lw[e] = t2_[1]; }
+      const int off = rbase + (2 * it.p + n) * rld + 8 * it.cb;
+      st16(sm + off, hw);
+      if (lo_too) st16(sm + off + rlo, lw);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t h0, l0, h1, l1;
+      split1(f[0][e], h0, l0);
+      split1(f[1][e], h1, l1);
+      const int off = tbase + (8 * it.cb + e) * LDC + 2 * it.p;
+      *(uint32_t*)(sm + off) = h0 | (h1 << 16);
+      if (lo_too) *(uint32_t*)(sm + off + tlo) = l0 | (l1 << 16);
+    }
+  };
+  auto write_s = [&]() {
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      int dt, et;
+      if (!tile(k, dt, et)) continue;
+      u32x2_t hw, lw;
+      { const u32x2_t t2_ = split2(st[k][0], st[k][1]); hw[0] = t2_[0]; lw[0] = t2_[1]; }
+      { const u32x2_t t2_ = split2(st[k][2], st[k][3]); hw[1] = t2_[0]; lw[1] = t2_[1]; }
+      const int off = Ly::ST + (et < NET ? 16 * et + lr : DV + lr) * LDK + 16 * dt + 4 * lg;
+      *(u32x2_t*)(sm + off) = hw;
+      *(u32x2_t*)(sm + off + Ly::STL) = lw;
+      if (et < NET) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int o = Ly::SR + (16 * dt + 4 * lg + q) * LDV + 16 * et + lr;
+          sm[o] = (uint16_t)(q & 1 ? hw[q >> 1] >> 16 : hw[q >> 1] & 0xffffu);
+          sm[o + Ly::SRL] = (uint16_t)(q & 1 ? lw[q >> 1] >> 16 : lw[q >> 1] & 0xffffu);
+        }
+      }
+    }
+  };
+
+  const int nch = (t1 - t0 + kBC - 1) / kBC;
+  if (nch > 0) prefetch(t0);
+  for (int c = 0; c < nch; ++c) {
+    const int cb0 = t0 + c * kBC;
+    stage();
+    write_s();
+    const u32x2_t dyc = dyraw;
+    const bool qvc = qv;
+    if (c + 1 < nch) prefetch(cb0 + kBC);
+    __syncthreads();
+
+    // ---- phase B: num, den of the wave's query block (w & 1) and value tile
+    // (w >> 1); dnum, and the wave's part of dden
+    if (w < 2 * NET) {
+      const int et = w >> 1;
+      u32x4_t qh[KSK], ql[KSK];
+#pragma unroll
+      for (int ks = 0; ks < KSK; ++ks) {
+        qh[ks] = ld16(sm + Ly::QR + iq * LDK + 32 * ks + 8 * lg);
+        ql[ks] = ld16(sm + Ly::QR + Ly::QRL + iq * LDK + 32 * ks + 8 * lg);
+      }
+      // scores P_ij = phi_q_i . phi_k_j, j <= i: lane holds keys 8lg..8lg+7 of query iq
+      u32x4_t ph, pl;
+      {
+        f32x4_t at[2];
+#pragma unroll
+        for (int odd = 0; odd < 2; ++odd) {
+          const int krow = 8 * (lr >> 2) + 4 * odd + (lr & 3);
+          at[odd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KSK; ++ks) {
+            const int o = Ly::KR + krow * LDK + 32 * ks + 8 * lg;
+            mm3(at[odd], ld16(sm + o), ld16(sm + o + Ly::QRL), qh[ks], ql[ks]);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) at[odd][q] = (8 * lg + 4 * odd + q <= iq) ? at[odd][q] : 0.f;
+        }
+        pair_operand(at, ph, pl);
+      }
+      // num^T tile: rows 16et + 4lg + q (dv), column iq
+      f32x4_t nacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      {
+        const int o = Ly::VT + (16 * et + lr) * LDC + 8 * lg;
+        const u32x4_t vh = ld16(sm + o);
+        mm(nacc, vh, ph);
+        mm(nacc, vh, pl);
+        if constexpr (VLO) mm(nacc, ld16(sm + o + Ly::VTL), ph);
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks) {
+          const int so = Ly::ST + (16 * et + lr) * LDK + 32 * ks + 8 * lg;
+          mm3(nacc, ld16(sm + so), ld16(sm + so + Ly::STL), qh[ks], ql[ks]);
+        }
+      }
+      float rden = 1.f;
+      if constexpr (NORM) {
+        f32x4_t dacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const u32x4_t vh = ld16(sm + Ly::VT + (DV + lr) * LDC + 8 * lg);
+        mm(dacc, vh, ph);
+        mm(dacc, vh, pl);
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks) {
+          const int so = Ly::ST + (DV + lr) * LDK + 32 * ks + 8 * lg;
+          mm3(dacc, ld16(sm + so), ld16(sm + so + Ly::STL), qh[ks], ql[ks]);
+        }
+        rden = 1.f / (dacc[0] + eps);
+      }
+      const u32x2_t yw = dyc;
+      f32x4_t dn;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float y = Io<IT>::to_f32(q & 1 ? yw[q >> 1] >> 16 : yw[q >> 1] & 0xffffu);
+        dn[q] = qvc ? y * rden : 0.f;
+      }
+      // dnum rows (dv contiguous) and dnum^T (token contiguous)
+      u32x2_t hw, lw;
+      { const u32x2_t t2_ = split2(dn[0], dn[1]); hw[0] = t2_[0]; lw[0] = t2_[1]; }
+      { const u32x2_t t2_ = split2(dn[2], dn[3]); hw[1] = t2_[0]; lw[1] = t2_[1]; }
+      {
+        const int o = Ly::DN + iq * LDV + 16 * et + 4 * lg;
+        *(u32x2_t*)(sm + o) = hw;
+        *(u32x2_t*)(sm + o + Ly::DNL) = lw;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int o = Ly::DT + (16 * et + 4 * lg + q) * LDC + iq;
+        sm[o] = (uint16_t)(q & 1 ? hw[q >> 1] >> 16 : hw[q >> 1] & 0xffffu);
+        sm[o + Ly::DTL] = (uint16_t)(q & 1 ? lw[q >> 1] >> 16 : lw[q >> 1] & 0xffffu);
+      }
+      if constexpr (NORM) {
+        float p = dn[0] * nacc[0] + dn[1] * nacc[1] + dn[2] * nacc[2] + dn[3] * nacc[3];
+        p += __shfl_xor(p, 16);
+        p += __shfl_xor(p, 32);
+        const float pd = -p * rden;
+        if (lg == 0) {
+          part[et * kBC + iq] = pd;
+          uint32_t ph1, pl1;
+          split1(pd, ph1, pl1);
+          sm[Ly::DT + (DV + et) * LDC + iq] = (uint16_t)ph1;
+          sm[Ly::DT + Ly::DTL + (DV + et) * LDC + iq] = (uint16_t)pl1;
+        }
+      }
+      const int tq = cb0 + iq;
+      if (tq < t1) *(f32x4_t*)(dnb + tq * HDV + 16 * et + 4 * lg) = dn;
+    }
+    __syncthreads();
+
+    // ---- phase C: dq of the wave's query block (w & 1) and key-dim tile (w >> 1)
+    if (w < 2 * NDT) {
+      const int dt = w >> 1;
+      const int tq = cb0 + iq;
+      float dd = 0.f;
+      if constexpr (NORM) {
+#pragma unroll
+        for (int et = 0; et < NET; ++et) dd += part[et * kBC + iq];
+        if (dt == 0 && lg == 0 && tq < t1) ddb[(int64_t)tq * H] = dd;
+      }
+      u32x4_t dh[KSV], dl[KSV];
+#pragma unroll
+      for (int ks = 0; ks < KSV; ++ks) {
+        dh[ks] = ld16(sm + Ly::DN + iq * LDV + 32 * ks + 8 * lg);
+        dl[ks] = ld16(sm + Ly::DN + Ly::DNL + iq * LDV + 32 * ks + 8 * lg);
+      }
+      // B_ij = dnum_i . v_j + dden_i, j <= i: keys 8lg..8lg+7 of query iq
+      u32x4_t bh, bl;
+      {
+        f32x4_t at[2];
+#pragma unroll
+        for (int odd = 0; odd < 2; ++odd) {
+          const int krow = 8 * (lr >> 2) + 4 * odd + (lr & 3);
+          at[odd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KSV; ++ks) {
+            const int o = Ly::VR + krow * LDV + 32 * ks + 8 * lg;
+            const u32x4_t vh = ld16(sm + o);
+            mm(at[odd], vh, dh[ks]);
+            mm(at[odd], vh, dl[ks]);
+            if constexpr (VLO) mm(at[odd], ld16(sm + o + Ly::VRL), dh[ks]);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) at[odd][q] = (8 * lg + 4 * odd + q <= iq) ? at[odd][q] + dd : 0.f;
+        }
+        pair_operand(at, bh, bl);
+      }
+      // dphi_q^T tile: rows 16dt + 4lg + q (dk), column iq
+      f32x4_t g = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      {
+        const int o = Ly::KT + (16 * dt + lr) * LDC + 8 * lg;
+        mm3(g, ld16(sm + o), ld16(sm + o + Ly::QTL), bh, bl);
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks) {
+          const int so = Ly::SR + (16 * dt + lr) * LDV + 32 * ks + 8 * lg;
+          mm3(g, ld16(sm + so), ld16(sm + so + Ly::SRL), dh[ks], dl[ks]);
+        }
+      }
+      if constexpr (NORM) {
+        const int zo = Ly::ST + DV * LDK + 16 * dt + 4 * lg;
+        const u32x2_t zh = *(const u32x2_t*)(sm + zo), zl = *(const u32x2_t*)(sm + zo + Ly::STL);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) g[q] += (bf_at(zh[q >> 1], q & 1) + bf_at(zl[q >> 1], q & 1)) * dd;
+      }
+      if (tq < t1) {
+        const f32x4_t x = ld4f(qb + tq * HDK + 16 * dt + 4 * lg);
+        float o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = qvc ? g[q] * dphi_rt(x[q], elu) : 0.f;
+        store4(dqb + tq * HDK + 16 * dt + 4 * lg, o[0], o[1], o[2], o[3]);
+      }
+    }
+
+    // ---- phase D: S += phiK^T V (z += phiK^T 1), dS += phiQ^T dnum (dz parts += phiQ^T dden parts)
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      int dt, et;
+      if (!tile(k, dt, et)) continue;
+      const int ao = (16 * dt + lr) * LDC + 8 * lg;
+      const int bo = (et < NET ? 16 * et + lr : DV + lr) * LDC + 8 * lg;
+      const u32x4_t kh = ld16(sm + Ly::KT + ao), kl = ld16(sm + Ly::KT + Ly::QTL + ao);
+      const u32x4_t vh = ld16(sm + Ly::VT + bo);
+      mm(st[k], kh, vh);
+      mm(st[k], kl, vh);
+      if constexpr (VLO) {
+        if (et < NET) mm(st[k], kh, ld16(sm + Ly::VT + Ly::VTL + bo));
+      }
+      mm3(ds[k], ld16(sm + Ly::QT + ao), ld16(sm + Ly::QT + Ly::QTL + ao), ld16(sm + Ly::DT + bo),
+          ld16(sm + Ly::DT + Ly::DTL + bo));
+    }
+    __syncthreads();
+  }
+
+  // ---- the segment's dS (dz) sum -> slot nseg - s for the reverse prefix
+  if (s >= 1) {
+    const int r = a.nseg - s;
+    float* so = a.s_out + u * a.s_out_u + r * a.s_out_s;
+    float* zo = (NORM && a.z_out) ? a.z_out + u * a.z_out_u + r * a.z_out_s : nullptr;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      int dt, et;
+      if (!tile(k, dt, et)) continue;
+      if (et < NET) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) so[(16 * dt + 4 * lg + q) * DV + 16 * et + lr] = ds[k][q];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float z = 0.f;
+#pragma unroll
+          for (int c2 = 0; c2 < NET; ++c2) z += __shfl(ds[k][q], 16 * lg + c2);
+          if (lr == 0 && zo) zo[16 * dt + 4 * lg + q] = z;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Segment sums of the forward state, sum phi_k v^T (and sum phi_k), in the
+// same hi + lo precision: the state at a segment start enters the gradients
+// through the same cancelling terms.  Workgroup blockIdx sums segment
+// s = blockIdx % nseg of unit blockIdx / nseg into slot s + 1.
+template <int DK, int DV, bool NORM, bool VLO>
+struct StateLds {
+  static constexpr int LDC = kBC + 8, NZ = NORM ? 16 : 0;
+  static constexpr int KTL = DK * LDC, VTL = (DV + NZ) * LDC;
+  static constexpr int KT = 0;              // phi(K)^T [dk][token], hi then lo
+  static constexpr int VT = KT + 2 * KTL;   // V^T [dv + 16 ones][token]; lo: dv rows
+  static constexpr int TOTAL = VT + VTL + (VLO ? DV * LDC : 0);
+};
+
+template <typename IT, int DK, int DV, bool NORM>
+__global__ __launch_bounds__(kBT, 2) void bwd_state_kernel(BwdChunkArgs a) {
+  constexpr bool VLO = !std::is_same_v<IT, uint16_t>;
+  using Ly = StateLds<DK, DV, NORM, VLO>;
+  constexpr int LDC = Ly::LDC;
+  constexpr int NET = DV / 16, NDT = DK / 16, NZT = NORM ? 1 : 0;
+  constexpr int NST = NDT * (NET + NZT);
+  constexpr int TPW = (NST + kBW - 1) / kBW;
+  constexpr int NIK = (kBC / 2) * (DK / 8), NIV = (kBC / 2) * (DV / 8);
+  __shared__ __align__(16) uint16_t sm[Ly::TOTAL];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int u = blockIdx.x / a.nseg, s = blockIdx.x % a.nseg;
+  const int T = a.T, H = a.H;
+  const int b = u / H, h = u % H;
+  const int t0 = s * a.seg_len;
+  const int t1 = min(T, t0 + a.seg_len);
+  const int64_t HDK = (int64_t)H * DK, HDV = (int64_t)H * DV;
+  const IT* kb = (const IT*)a.k + (int64_t)b * T * HDK + (int64_t)h * DK;
+  const IT* vb = (const IT*)a.v + (int64_t)b * T * HDV + (int64_t)h * DV;
+  const uint8_t* mb = a.mask ? a.mask + (int64_t)b * T : nullptr;
+  const float eps = a.eps;
+  const bool elu = a.fm == kEluPlusOne;
+  auto valid = [&](int t) { return t < t1 && (mb == nullptr || mb[t] != 0); };
+
+  f32x4_t st[TPW];
+  auto tile = [&](int k, int& dt, int& et) {
+    const int tau = w + kBW * k;
+    dt = tau / (NET + NZT);
+    et = tau % (NET + NZT);
+    return tau < NST;
+  };
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) st[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (NORM) {
+    for (int i = tid; i < 16 * LDC; i += kBT) sm[Ly::VT + DV * LDC + i] = 0x3f80;  // bf16 1.0
+  }
+
+  const Item it = make_item<NIK, DK / 8, NIV, DV / 8, 0, 1>(tid);  // m: 0 k, 1 v
+  const IT* ibase = it.m == 0 ? kb : vb;
+  const int64_t ild = it.m == 0 ? HDK : HDV;
+  u32x4_t raw0, raw1;
+  uint32_t rvalid = 0;
+  auto prefetch = [&](int c0) {
+    if (!it.on) return;
+    const int ta = c0 + 2 * it.p, tb = ta + 1;
+    const u32x4_t z4 = u32x4_t{0u, 0u, 0u, 0u};
+    raw0 = ta < t1 ? ld16(ibase + ta * ild + 8 * it.cb) : z4;
+    raw1 = tb < t1 ? ld16(ibase + tb * ild + 8 * it.cb) : z4;
+    rvalid = (valid(ta) ? 1u : 0u) | (valid(tb) ? 2u : 0u);
+  };
+  auto stage = [&]() {
+    if (!it.on) return;
+    float f[2][8];
+    Io<IT>::unpack(raw0, f[0]);
+    Io<IT>::unpack(raw1, f[1]);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const bool ok = (rvalid >> n) & 1u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[n][e] = ok ? (it.m == 0 ? phi_rt(f[n][e], elu, eps) : f[n][e]) : 0.f;
+    }
+    const int tbase = it.m == 0 ? Ly::KT : Ly::VT;
+    const int tlo = it.m == 0 ? Ly::KTL : Ly::VTL;
+    const bool lo_too = it.m == 0 || VLO;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t h0, l0, h1, l1;
+      split1(f[0][e], h0, l0);
+      split1(f[1][e], h1, l1);
+      const int off = tbase + (8 * it.cb + e) * LDC + 2 * it.p;
+      *(uint32_t*)(sm + off) = h0 | (h1 << 16);
+      if (lo_too) *(uint32_t*)(sm + off + tlo) = l0 | (l1 << 16);
+    }
+  };
+
+  const int nch = (t1 - t0 + kBC - 1) / kBC;
+  if (nch > 0) prefetch(t0);
+  for (int c = 0; c < nch; ++c) {
+    stage();
+    if (c + 1 < nch) prefetch(t0 + (c + 1) * kBC);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      int dt, et;
+      if (!tile(k, dt, et)) continue;
+      const int ao = Ly::KT + (16 * dt + lr) * LDC + 8 * lg;
+      const int bo = Ly::VT + (et < NET ? 16 * et + lr : DV + lr) * LDC + 8 * lg;
+      const u32x4_t kh = ld16(sm + ao), kl = ld16(sm + ao + Ly::KTL), vh = ld16(sm + bo);
+      mm(st[k], kh, vh);
+      mm(st[k], kl, vh);
+      if constexpr (VLO) {
+        if (et < NET) mm(st[k], kh, ld16(sm + bo + Ly::VTL));
+      }
+    }
+    __syncthreads();
+  }
+
+  float* so = a.s_out + u * a.s_out_u + (s + 1) * a.s_out_s;
+  float* zo = (NORM && a.z_out) ? a.z_out + u * a.z_out_u + (s + 1) * a.z_out_s : nullptr;
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    int dt, et;
+    if (!tile(k, dt, et)) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = 16 * dt + 4 * lg + q;
+      if (et < NET)
+        so[d * DV + 16 * et + lr] = st[k][q];
+      else if (zo && lr == 0)
+        zo[d] = st[k][q];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse pass: LDS layout in 16-bit elements.
+template <int DK, int DV, bool NORM, bool VLO>
+struct RevLds {
+  static constexpr int LDK = DK + 8, LDV = DV + 8, LDC = kBC + 8, NZ = NORM ? 16 : 0;
+  static constexpr int QRL = kBC * LDK, QTL = DK * LDC, VRL = kBC * LDV, DNL = kBC * LDV, DTL = (DV + NZ) * LDC,
+                       SAL = DV * LDK, SBL = DK * LDV;
+  static constexpr int QR = 0;                         // phi(Q) [token][dk]
+  static constexpr int QT = QR + 2 * QRL;              // phi(Q)^T [dk][token]
+  static constexpr int KR = QT + 2 * QTL;              // phi(K) [token][dk]
+  static constexpr int VR = KR + 2 * QRL;              // V [token][dv]
+  static constexpr int DN = VR + (VLO ? 2 : 1) * VRL;  // dnum [token][dv]
+  static constexpr int DT = DN + 2 * DNL;              // dnum^T [dv + 16: dden, zeros][token]
+  static constexpr int SA = DT + 2 * DTL;              // dS^T [dv][dk]
+  static constexpr int SB = SA + 2 * SAL;              // dS [dk][dv]
+  static constexpr int TOTAL = SB + 2 * SBL;
+};
+
+template <typename IT, int DK, int DV, bool NORM>
+__global__ __launch_bounds__(kBT, 2) void bwd_rev_kernel(BwdChunkArgs a) {
+  constexpr bool VLO = !std::is_same_v<IT, uint16_t>;
+  using Ly = RevLds<DK, DV, NORM, VLO>;
+  constexpr int LDK = Ly::LDK, LDV = Ly::LDV, LDC = Ly::LDC;
+  constexpr int NET = DV / 16, NDT = DK / 16, NZT = NORM ? 1 : 0;
+  constexpr int NST = NDT * (NET + NZT);
+  constexpr int TPW = (NST + kBW - 1) / kBW;
+  constexpr int KSK = DK / 32, KSV = DV / 32;
+  constexpr int NIQ = (kBC / 2) * (DK / 8), NIV = (kBC / 2) * (DV / 8);
+  static_assert(2 * NIQ + 2 * NIV <= kBT && NIQ % 64 == 0 && NIV % 64 == 0, "one staging item per thread");
+  __shared__ __align__(16) uint16_t sm[Ly::TOTAL];
+  __shared__ float dzv[NORM ? DK : 1], ddv[NORM ? kBC : 1];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int u = blockIdx.x / a.nseg, s = blockIdx.x % a.nseg;
+  const int T = a.T, H = a.H;
+  const int b = u / H, h = u % H;
+  const int t0 = s * a.seg_len;
+  const int t1 = min(T, t0 + a.seg_len);
+  const int64_t HDK = (int64_t)H * DK, HDV = (int64_t)H * DV;
+  const IT* qb = (const IT*)a.q + (int64_t)b * T * HDK + (int64_t)h * DK;
+  const IT* kb = (const IT*)a.k + (int64_t)b * T * HDK + (int64_t)h * DK;
+  const IT* vb = (const IT*)a.v + (int64_t)b * T * HDV + (int64_t)h * DV;
+  const float* dnb = a.dnum + (int64_t)b * T * HDV + (int64_t)h * DV;
+  const float* ddb = NORM ? a.dden + (int64_t)b * T * H + h : nullptr;
+  IT* dkb = (IT*)a.dk + (int64_t)b * T * HDK + (int64_t)h * DK;
+  IT* dvb = (IT*)a.dv + (int64_t)b * T * HDV + (int64_t)h * DV;
+  const uint8_t* mb = a.mask ? a.mask + (int64_t)b * T : nullptr;
+  const float eps = a.eps;
+  const bool elu = a.fm == kEluPlusOne;
+  auto valid = [&](int t) { return t < t1 && (mb == nullptr || mb[t] != 0); };
+
+  // ---- dS (+ dz) tiles: the gradient sums of the tokens after the current
+  // chunk; the dz tile holds dz in column 0 (row DV of dnum^T is dden)
+  f32x4_t ds[TPW];
+  auto tile = [&](int k, int& dt, int& et) {
+    const int tau = w + kBW * k;
+    dt = tau / (NET + NZT);
+    et = tau % (NET + NZT);
+    return tau < NST;
+  };
+  {
+    const int r = a.nseg - 1 - s;
+    const float* sin = a.s_in ? a.s_in + u * a.s_in_u + r * a.s_in_s : nullptr;
+    const float* zin = (NORM && a.z_in) ? a.z_in + u * a.z_in_u + r * a.z_in_s : nullptr;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      int dt, et;
+      const bool on = tile(k, dt, et);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = 16 * dt + 4 * lg + q;
+        float x = 0.f;
+        if (on) x = et < NET ? (sin ? sin[d * DV + 16 * et + lr] : 0.f) : ((zin && lr == 0) ? zin[d] : 0.f);
+        ds[k][q] = x;
+      }
+    }
+  }
+  if constexpr (NORM) {
+    for (int i = tid; i < 15 * LDC; i += kBT) {
+      sm[Ly::DT + (DV + 1) * LDC + i] = 0;
+      sm[Ly::DT + Ly::DTL + (DV + 1) * LDC + i] = 0;
+    }
+  }
+
+  // ---- prefetch registers: q (rows and transposed), k (rows), v (rows), dnum
+  // (rows and transposed, 8 fp32 values of two tokens: 4 loads)
+  const Item it = make_item<NIQ, DK / 8, NIQ, DK / 8, NIV, DV / 8, NIV, DV / 8>(tid);
+  // the item's rows: a 16-byte block of q, k or v (token 2p: raw0, token
+  // 2p+1: raw2) or two of dnum (raw0, raw1 and raw2, raw3)
+  const bool idn = it.m == 3;
+  const unsigned char* ibase = (const unsigned char*)(it.m == 0 ? (const void*)qb
+                                                                : (it.m == 1 ? (const void*)kb
+                                                                             : (it.m == 2 ? (const void*)vb
+                                                                                          : (const void*)dnb)));
+  const int64_t ild = (it.m == 0 || it.m == 1) ? HDK * sizeof(IT) : (it.m == 2 ? HDV * sizeof(IT) : HDV * 4);
+  const int iblk = idn ? 32 * it.cb : 16 * it.cb;  // byte offset of the block in the row
+  u32x4_t raw0, raw1 = u32x4_t{0u, 0u, 0u, 0u}, raw2, raw3 = u32x4_t{0u, 0u, 0u, 0u};
+  uint32_t rvalid = 0;
+  float ddn = 0.f;                   // dden of token tid (tid < 32)
+  const int jq = 16 * (w & 1) + lr;  // key row of the lane in a chunk (phases E, F)
+  bool kv = false;
+  auto prefetch = [&](int c0) {
+    if (it.on) {
+      const u32x4_t z4 = u32x4_t{0u, 0u, 0u, 0u};
+      const int ta = c0 + 2 * it.p, tb = ta + 1;
+      const unsigned char* pa = ibase + ta * ild + iblk;
+      const unsigned char* pb = ibase + tb * ild + iblk;
+      raw0 = ta < t1 ? ld16(pa) : z4;
+      raw2 = tb < t1 ? ld16(pb) : z4;
+      if (idn) {
+        raw1 = ta < t1 ? ld16(pa + 16) : z4;
+        raw3 = tb < t1 ? ld16(pb + 16) : z4;
+      }
+      rvalid = (valid(ta) ? 1u : 0u) | (valid(tb) ? 2u : 0u);
+    }
+    if constexpr (NORM) {
+      if (tid < kBC) ddn = c0 + tid < t1 ? ddb[(int64_t)(c0 + tid) * H] : 0.f;
+    }
+    kv = valid(c0 + jq);
+  };
+
+  auto stage = [&]() {
+    if constexpr (NORM) {
+      if (tid < kBC) {
+        ddv[tid] = ddn;
+        uint32_t hh, ll;
+        split1(ddn, hh, ll);
+        sm[Ly::DT + DV * LDC + tid] = (uint16_t)hh;
+        sm[Ly::DT + Ly::DTL + DV * LDC + tid] = (uint16_t)ll;
+      }
+    }
+    if (!it.on) return;
+    float f[2][8];
+    if (!idn) {
+      Io<IT>::unpack(raw0, f[0]);
+      Io<IT>::unpack(raw2, f[1]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[0][e] = __uint_as_float(raw0[e]);
+        f[0][4 + e] = __uint_as_float(raw1[e]);
+        f[1][e] = __uint_as_float(raw2[e]);
+        f[1][4 + e] = __uint_as_float(raw3[e]);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const bool ok = (rvalid >> n) & 1u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[n][e] = ok ? (it.m < 2 ? phi_rt(f[n][e], elu, eps) : f[n][e]) : 0.f;
+    }
+    const int rld = it.m >= 2 ? LDV : LDK;
+    const int rbase = it.m == 0 ? Ly::QR : (it.m == 1 ? Ly::KR : (it.m == 2 ? Ly::VR : Ly::DN));
+    const int rlo = it.m == 3 ? Ly::DNL : (it.m == 2 ? Ly::VRL : Ly::QRL);
+    const bool lo_too = it.m != 2 || VLO;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      u32x4_t hw, lw;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { const u32x2_t t2_ = split2(f[n][2 * e], f[n][2 * e + 1]); hw[e] = t2_[0]; lw[e] = t2_[1]; }
+      const int off = rbase + (2 * it.p + n) * rld + 8 * it.cb;
+      st16(sm + off, hw);
+      if (lo_too) st16(sm + off + rlo, lw);
+    }
+    if (it.m == 0 || it.m == 3) {
+      // transposed: phi(Q)^T, dnum^T
+      const int tbase = it.m == 0 ? Ly::QT : Ly::DT;
+      const int tlo = it.m == 0 ? Ly::QTL : Ly::DTL;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t h0, l0, h1, l1;
+        split1(f[0][e], h0, l0);
+        split1(f[1][e], h1, l1);
+        const int off = tbase + (8 * it.cb + e) * LDC + 2 * it.p;
+        *(uint32_t*)(sm + off) = h0 | (h1 << 16);
+        *(uint32_t*)(sm + off + tlo) = l0 | (l1 << 16);
+      }
+    }
+  };
+  auto write_ds = [&]() {
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      int dt, et;
+      if (!tile(k, dt, et)) continue;
+      if (et < NET) {
+        u32x2_t hw, lw;
+        { const u32x2_t t2_ = split2(ds[k][0], ds[k][1]); hw[0] = t2_[0]; lw[0] = t2_[1]; }
+        { const u32x2_t t2_ = split2(ds[k][2], ds[k][3]); hw[1] = t2_[0]; lw[1] = t2_[1]; }
+        const int off = Ly::SA + (16 * et + lr) * LDK + 16 * dt + 4 * lg;
+        *(u32x2_t*)(sm + off) = hw;
+        *(u32x2_t*)(sm + off + Ly::SAL) = lw;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int o = Ly::SB + (16 * dt + 4 * lg + q) * LDV + 16 * et + lr;
+          sm[o] = (uint16_t)(q & 1 ? hw[q >> 1] >> 16 : hw[q >> 1] & 0xffffu);
+          sm[o + Ly::SBL] = (uint16_t)(q & 1 ? lw[q >> 1] >> 16 : lw[q >> 1] & 0xffffu);
+        }
+      } else if constexpr (NORM) {
+        if (lr == 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dzv[16 * dt + 4 * lg + q] = ds[k][q];
+        }
+      }
+    }
+  };
+
+  const int nch = (t1 - t0 + kBC - 1) / kBC;
+  if (nch > 0) prefetch(t0 + (nch - 1) * kBC);
+  for (int c = nch - 1; c >= 0; --c) {
+    const int cb0 = t0 + c * kBC;
+    stage();
+    write_ds();
+    const bool kvc = kv;
+    if (c > 0) prefetch(cb0 - kBC);
+    __syncthreads();
+    const int tj = cb0 + jq;
+
+    // ---- phase E: dv of the wave's key block (w & 1) and value tile (w >> 1)
+    if (w < 2 * NET) {
+      const int et = w >> 1;
+      u32x4_t kh[KSK], kl[KSK];
+#pragma unroll
+      for (int ks = 0; ks < KSK; ++ks) {
+        kh[ks] = ld16(sm + Ly::KR + jq * LDK + 32 * ks + 8 * lg);
+        kl[ks] = ld16(sm + Ly::KR + Ly::QRL + jq * LDK + 32 * ks + 8 * lg);
+      }
+      // P_ij, i >= j: lane holds queries 8lg..8lg+7 of key jq
+      u32x4_t ph, pl;
+      {
+        f32x4_t at[2];
+#pragma unroll
+        for (int odd = 0; odd < 2; ++odd) {
+          const int qrow = 8 * (lr >> 2) + 4 * odd + (lr & 3);
+          at[odd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KSK; ++ks) {
+            const int o = Ly::QR + qrow * LDK + 32 * ks + 8 * lg;
+            mm3(at[odd], ld16(sm + o), ld16(sm + o + Ly::QRL), kh[ks], kl[ks]);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) at[odd][q] = (8 * lg + 4 * odd + q >= jq) ? at[odd][q] : 0.f;
+        }
+        pair_operand(at, ph, pl);
+      }
+      // dv^T tile: rows 16et + 4lg + q (dv), column jq
+      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      {
+        const int o = Ly::DT + (16 * et + lr) * LDC + 8 * lg;
+        mm3(acc, ld16(sm + o), ld16(sm + o + Ly::DTL), ph, pl);
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks) {
+          const int so = Ly::SA + (16 * et + lr) * LDK + 32 * ks + 8 * lg;
+          mm3(acc, ld16(sm + so), ld16(sm + so + Ly::SAL), kh[ks], kl[ks]);
+        }
+      }
+      if (tj < t1)
+        store4(dvb + tj * HDV + 16 * et + 4 * lg, kvc ? acc[0] : 0.f, kvc ? acc[1] : 0.f, kvc ? acc[2] : 0.f,
+               kvc ? acc[3] : 0.f);
+    }
+
+    // ---- phase F: dk of the wave's key block (w & 1) and key-dim tile (w >> 1)
+    if (w < 2 * NDT) {
+      const int dt = w >> 1;
+      u32x4_t vh[KSV], vl[VLO ? KSV : 1];
+#pragma unroll
+      for (int ks = 0; ks < KSV; ++ks) {
+        vh[ks] = ld16(sm + Ly::VR + jq * LDV + 32 * ks + 8 * lg);
+        if constexpr (VLO) vl[ks] = ld16(sm + Ly::VR + Ly::VRL + jq * LDV + 32 * ks + 8 * lg);
+      }
+      // B_ij = dnum_i . v_j + dden_i, i >= j: queries 8lg..8lg+7 of key jq
+      u32x4_t bh, bl;
+      {
+        f32x4_t at[2];
+#pragma unroll
+        for (int odd = 0; odd < 2; ++odd) {
+          const int qrow = 8 * (lr >> 2) + 4 * odd + (lr & 3);
+          at[odd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KSV; ++ks) {
+            const int o = Ly::DN + qrow * LDV + 32 * ks + 8 * lg;
+            const u32x4_t dh = ld16(sm + o), dl = ld16(sm + o + Ly::DNL);
+            mm(at[odd], dh, vh[ks]);
+            mm(at[odd], dl, vh[ks]);
+            if constexpr (VLO) mm(at[odd], dh, vl[ks]);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i = 8 * lg + 4 * odd + q;
+            const float dd = NORM ? ddv[i] : 0.f;
+            at[odd][q] = i >= jq ? at[odd][q] + dd : 0.f;
+          }
+        }
+        pair_operand(at, bh, bl);
+      }
+      // dphi_k^T tile: rows 16dt + 4lg + q (dk), column jq
+      f32x4_t g = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      {
+        const int o = Ly::QT + (16 * dt + lr) * LDC + 8 * lg;
+        mm3(g, ld16(sm + o), ld16(sm + o + Ly::QTL), bh, bl);
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks) {
+          const int so = Ly::SB + (16 * dt + lr) * LDV + 32 * ks + 8 * lg;
+          const u32x4_t sh = ld16(sm + so), sl = ld16(sm + so + Ly::SBL);
+          mm(g, sh, vh[ks]);
+          mm(g, sl, vh[ks]);
+          if constexpr (VLO) mm(g, sh, vl[ks]);
+        }
+      }
+      if constexpr (NORM) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) g[q] += dzv[16 * dt + 4 * lg + q];
+      }
+      if (tj < t1) {
+        const f32x4_t x = ld4f(kb + tj * HDK + 16 * dt + 4 * lg);
+        float o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = kvc ? g[q] * dphi_rt(x[q], elu) : 0.f;
+        store4(dkb + tj * HDK + 16 * dt + 4 * lg, o[0], o[1], o[2], o[3]);
+      }
+    }
+
+    // ---- phase G: dS += phiQ^T dnum, dz += phiQ^T dden (column 0 of the dz tile)
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      int dt, et;
+      if (!tile(k, dt, et)) continue;
+      const int ao = (16 * dt + lr) * LDC + 8 * lg;
+      const int bo = (et < NET ? 16 * et + lr : DV + lr) * LDC + 8 * lg;
+      mm3(ds[k], ld16(sm + Ly::QT + ao), ld16(sm + Ly::QT + Ly::QTL + ao), ld16(sm + Ly::DT + bo),
+          ld16(sm + Ly::DT + Ly::DTL + bo));
+    }
+    __syncthreads();
+  }
+
+  // ---- the first segment ends with dS_0, dz_0
+  if (s == 0) {
+    float* so = a.s_out + u * a.s_out_u;
+    float* zo = (NORM && a.z_out) ? a.z_out + u * a.z_out_u : nullptr;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      int dt, et;
+      if (!tile(k, dt, et)) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = 16 * dt + 4 * lg + q;
+        if (et < NET)
+          so[d * DV + 16 * et + lr] = ds[k][q];
+        else if (zo && lr == 0)
+          zo[d] = ds[k][q];
+      }
+    }
+  }
+}
+
+template <typename IT, int DK, int DV, bool NORM>
+hipError_t launch_bwd_chunk_t(int pass, const BwdChunkArgs& a, int grid, hipStream_t st) {
+  if (pass == 0)
+    hipLaunchKernelGGL((bwd_fwd_kernel<IT, DK, DV, NORM>), dim3(grid), dim3(kBT), 0, st, a);
+  else if (pass == 1)
+    hipLaunchKernelGGL((bwd_rev_kernel<IT, DK, DV, NORM>), dim3(grid), dim3(kBT), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_state_kernel<IT, DK, DV, NORM>), dim3(grid), dim3(kBT), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename IT, int DK, int DV>
+hipError_t launch_bwd_chunk_n(int pass, int norm, const BwdChunkArgs& a, int grid, hipStream_t st) {
+  return norm ? launch_bwd_chunk_t<IT, DK, DV, true>(pass, a, grid, st)
+              : launch_bwd_chunk_t<IT, DK, DV, false>(pass, a, grid, st);
+}
+
+template <typename IT>
+hipError_t launch_bwd_chunk_d(int pass, int Dk, int Dv, int norm, const BwdChunkArgs& a, int grid,
+                              hipStream_t st) {
+  if (Dk == 32 && Dv == 32) return launch_bwd_chunk_n<IT, 32, 32>(pass, norm, a, grid, st);
+  if (Dk == 32 && Dv == 64) return launch_bwd_chunk_n<IT, 32, 64>(pass, norm, a, grid, st);
+  if (Dk == 64 && Dv == 32) return launch_bwd_chunk_n<IT, 64, 32>(pass, norm, a, grid, st);
+  if (Dk == 64 && Dv == 64) return launch_bwd_chunk_n<IT, 64, 64>(pass, norm, a, grid, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_chunk(int pass, int io, int Dk, int Dv, int norm, const BwdChunkArgs& a, int grid,
+                            hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  if (io == kIoBF16) return launch_bwd_chunk_d<uint16_t>(pass, Dk, Dv, norm, a, grid, st);
+  if (io == kIoF16) return launch_bwd_chunk_d<f16_t>(pass, Dk, Dv, norm, a, grid, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace la

@@ -176,6 +176,43 @@ hipError_t launch_bwd_dden(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_finish(int io, const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_transpose(const float* in, float* out, int64_t U, int D, hipStream_t st);
 
+// Chunk-parallel causal backward for 16-bit inputs at head sizes Dk, Dv in
+// {32, 64} (la_bwd_chunk.hip).  Workgroup blockIdx covers unit u = blockIdx /
+// nseg and tokens [s*seg_len, min((s+1)*seg_len, T)) of segment s = blockIdx %
+// nseg (seg_len a multiple of 32).
+struct BwdChunkArgs {
+  const void* q;        // (B,T,H,Dk)
+  const void* k;        // (B,T,H,Dk)
+  const void* v;        // (B,T,H,Dv)
+  const void* dy;       // (B,T,H,Dv), pass 0 only
+  const uint8_t* mask;  // (B,T) or null
+  // pass 0: forward state at the start of segment s, s_in + u*s_in_u + s*s_in_s
+  // ([dk][dv], z [dk]; null = zeros).  pass 1: the gradient sums of the tokens
+  // after segment s, at slot nseg - 1 - s (null = zeros)
+  const float* s_in;
+  const float* z_in;
+  int64_t s_in_u, s_in_s, z_in_u, z_in_s;
+  // pass 0: segment s >= 1 writes its sum of phi_q dnum^T (phi_q dden) to slot
+  // nseg - s; pass 1: segment 0 writes dS_0, dz_0 at s_out + u*s_out_u
+  float* s_out;
+  float* z_out;
+  int64_t s_out_u, s_out_s, z_out_u, z_out_s;
+  float* dnum;  // (B,T,H,Dv) fp32: written by pass 0, read by pass 1
+  float* dden;  // (B,T,H) fp32 (with the normaliser)
+  void* dq;     // pass 0
+  void* dk;     // pass 1
+  void* dv;     // pass 1
+  int32_t T, H, nseg, seg_len;
+  int32_t fm;
+  float eps;
+};
+// io: bf16 or fp16; Dk, Dv: 32 or 64 each.  pass 0: forward over each
+// segment (dq, dnum, dden, segment sums); pass 1: reverse (dk, dv, dS_0,
+// dz_0); pass 2: the forward state's sum over segment s = blockIdx % nseg of
+// each unit into slot s + 1 of s_out / z_out (strides s_out_u, s_out_s).
+hipError_t launch_bwd_chunk(int pass, int io, int Dk, int Dv, int norm, const BwdChunkArgs& a, int grid,
+                            hipStream_t st);
+
 // T == 1 step of the gated recurrence (la_decode.hip).
 struct GatedStepArgs {
   const void* q;      // (B, Hq*D)

@@ -100,6 +100,12 @@ hipError_t launch_gated_pd(int, int, int D, int G, const GatedArgs& a, int grid,
   seen(grid > 0 && D > 0 && G > 0 && a.T > 0, "gated_pd");
   return hipSuccess;
 }
+hipError_t launch_bwd_chunk(int pass, int io, int Dk, int Dv, int, const BwdChunkArgs& a, int grid, hipStream_t) {
+  seen(grid > 0 && pass >= 0 && pass <= 2 && (io == 1 || io == 2) && (Dk == 32 || Dk == 64) &&
+           (Dv == 32 || Dv == 64) && a.nseg > 0 && a.seg_len % 32 == 0 && a.T > 0 && a.dnum,
+       "bwd_chunk");
+  return hipSuccess;
+}
 hipError_t launch_recur(int, int D, int G, int, int, const RecurArgs& a, hipStream_t) {
   seen(a.units > 0 && D == 128 && G > 0, "recur");
   return hipSuccess;
@@ -177,16 +183,21 @@ int main() {
                                  Hkv, D, D, dt, 0.f, nullptr),
                    LA_OK, "gated step");
           }
-  // backward
+  // backward: equal head sizes on every path; unequal ones (16-bit, 32 or 64)
   for (int dt = 0; dt < 3; ++dt)
     for (int64_t D : {32, 64, 128})
-      for (int64_t T : {0, 1, 150, 2048}) {
-        expect(la_backward_workspace_size(2, T, 3, D, D, dt, 1, &n), LA_OK, "backward workspace");
-        expect(la_backward(P(G1), P(2 * G1), P(3 * G1), nullptr, nullptr, nullptr, P(4 * G1), nullptr, nullptr, 0, 1,
-                           1e-6f, P(5 * G1), P(6 * G1), P(7 * G1), F(8 * G1), F(9 * G1), 2, T, 3, D, D, dt,
-                           P(10 * G1), n, nullptr),
-               LA_OK, "backward");
-      }
+      for (int64_t Dv : {32, 64, 128})
+        for (int64_t T : {0, 1, 150, 2048})
+          for (int64_t BH : {3, 600})
+            for (int norm = 0; norm < 2; ++norm) {
+              const bool ok = D == Dv || (dt != 0 && D <= 64 && Dv <= 64);
+              expect(la_backward_workspace_size(2, T, BH, D, Dv, dt, norm, &n), ok ? LA_OK : LA_ERR_UNSUPPORTED,
+                     "backward workspace");
+              expect(la_backward(P(G1), P(2 * G1), P(3 * G1), nullptr, nullptr, nullptr, P(4 * G1), nullptr, nullptr,
+                                 0, norm, 1e-6f, P(5 * G1), P(6 * G1), P(7 * G1), F(8 * G1), norm ? F(9 * G1) : nullptr,
+                                 2, T, BH, D, Dv, dt, P(10 * G1), ok ? n : 0, nullptr),
+                     ok ? LA_OK : LA_ERR_UNSUPPORTED, "backward");
+            }
   printf("%s: %d failures, %d launches (%d with bad arguments)\n", fails || bad ? "FAIL" : "OK", fails, launches,
          bad);
   return (fails || bad) ? 1 : 0;

@@ -261,7 +261,11 @@ def test_backward_argument_errors(lib):
     assert g(dk=f(5 << 30)) == BAD_ARG        # dk overlaps dq
     assert g(ws=None, wsb=0) == WORKSPACE
     assert g(Dk=96, Dv=96) == UNSUPPORTED
-    assert g(Dk=64, Dv=128) == UNSUPPORTED   # the backward needs Dk == Dv
+    assert g(Dk=64, Dv=128) == UNSUPPORTED   # unequal head sizes: 32 or 64 each, 16-bit inputs
+    assert g(Dk=32, Dv=64, dt=0) == UNSUPPORTED
+    for dt in (1, 2):
+        for dk, dv in ((32, 64), (64, 32)):
+            assert lib.la_backward_workspace_size(2, 128, 3, dk, dv, dt, 1, ctypes.byref(n)) == OK and n.value > 0
     assert g(B=0) == OK
 
 
