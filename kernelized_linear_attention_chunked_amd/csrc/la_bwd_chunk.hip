@@ -79,23 +79,83 @@ __device__ __forceinline__ void pair_operand(const f32x4_t (&at)[2], u32x4_t& h,
 #pragma unroll
   for (int e = 0; e < 4; ++e) { const u32x2_t t2_ = split2(at[e >> 1][2 * (e & 1)], at[e >> 1][2 * (e & 1) + 1]); h[e] = t2_[0]; lo[e] = t2_[1]; }
 }
-// four consecutive I/O values as fp32
-template <typename IT>
-__device__ __forceinline__ f32x4_t ld4f(const IT* p) {
-  const u32x2_t w = *(const u32x2_t*)p;
-  return f32x4_t{Io<IT>::to_f32(w[0] & 0xffffu), Io<IT>::to_f32(w[0] >> 16), Io<IT>::to_f32(w[1] & 0xffffu),
-                 Io<IT>::to_f32(w[1] >> 16)};
-}
-__device__ __forceinline__ float phi_rt(float x, bool elu, float eps) {
-  return elu ? phi<kEluPlusOne>(x, eps) : phi<kReluEps>(x, eps);
-}
 // derivative of phi: elu(x)+1 -> 1 (x > 0) or exp(x); relu(x)+eps -> 1 (x > 0) or 0
 __device__ __forceinline__ float dphi_rt(float x, bool elu) {
   return x > 0.f ? 1.f : (elu ? __expf(x) : 0.f);
 }
+// Range-checked buffer access: a resource of `bytes` bytes from `base`; loads
+// past the range return 0 and stores past it are dropped, so every access of a
+// chunk's tokens is issued unconditionally (a load or store under a branch
+// would make the wait for an earlier load cover every access issued after it).
+// Offsets are in bytes.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kDrop = 0x80000000u;  // past every range: the store is dropped
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2_t bload8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload1(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, const u32x4_t& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, const u32x2_t& v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore4(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+// four fp32 results as the I/O type
+template <typename IT>
+__device__ __forceinline__ u32x2_t pack4(float a, float b, float c, float d) {
+  return u32x2_t{Io<IT>::pack2(a, b), Io<IT>::pack2(c, d)};
+}
+// the I/O value in half e of word w
+template <typename IT>
+__device__ __forceinline__ float io_at(uint32_t w, int e) {
+  return Io<IT>::to_f32(e ? w >> 16 : w & 0xffffu);
+}
+
 // the two bf16 halves of word w as fp32 (element e of a 16-bit pair)
 __device__ __forceinline__ float bf_at(uint32_t w, int e) {
   return __uint_as_float(e ? (w & 0xffff0000u) : (w << 16));
+}
+
+// Staging of two tokens' 8 values: phi applied (PHI), zeroed where the token
+// is not ok, and split into bf16 hi and lo words along the row (element 2i in
+// the low half of word i).
+template <int FM, bool PHI>
+__device__ __forceinline__ void split_rows(float (&f)[2][8], bool ok0, bool ok1, float eps, u32x4_t (&h)[2],
+                                           u32x4_t (&lo)[2]) {
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const bool ok = n ? ok1 : ok0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = PHI ? phi<FM>(f[n][e], eps) : f[n][e];
+      f[n][e] = ok ? x : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x2_t t = split2(f[n][2 * i], f[n][2 * i + 1]);
+      h[n][i] = t[0];
+      lo[n][i] = t[1];
+    }
+  }
+}
+// the transposed word of row element e from the row words of token a (low
+// half) and token b (high half)
+__device__ __forceinline__ uint32_t tword(const u32x4_t& a, const u32x4_t& b, int e) {
+  return __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
 }
 
 // Staging item of a thread: two consecutive tokens (2p, 2p+1) of one 16-byte
@@ -115,7 +175,7 @@ __device__ __forceinline__ Item make_item(int tid) {
   const bool on = wt < N0 + N1 + N2 + N3;
   const int r = tid - (m == 0 ? 0 : (m == 1 ? N0 : (m == 2 ? N0 + N1 : N0 + N1 + N2)));
   const int bl = m == 0 ? B0 : (m == 1 ? B1 : (m == 2 ? B2 : B3));
-  return Item{m, r / bl, r % bl, on};
+  return on ? Item{m, r / bl, r % bl, true} : Item{m, 0, 0, false};
 }
 
 // ---------------------------------------------------------------------------
@@ -171,7 +231,6 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
   const uint8_t* mb = a.mask ? a.mask + (int64_t)b * T : nullptr;
   const float eps = a.eps;
   const bool elu = a.fm == kEluPlusOne;
-  auto valid = [&](int t) { return t < t1 && (mb == nullptr || mb[t] != 0); };
 
   // ---- S (+ z) tiles and the dS (+ dz) sum: wave w owns tiles w + 8k; tile
   // (dt, et) holds rows 16dt + 4lg + q (dk), column 16et + lr (dv); the z tile
@@ -212,65 +271,87 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
     }
   }
 
-  // ---- prefetch registers
+  // ---- the segment's buffers (token t at byte (t - t0) * row)
+  constexpr uint32_t ESZ = sizeof(IT);
+  const uint32_t nt = (uint32_t)(t1 - t0);
+  const uint32_t RK = (uint32_t)HDK * ESZ, RV = (uint32_t)HDV * ESZ;  // row bytes
+  const rsrc_t rq = make_rsrc(qb + t0 * HDK, (nt - 1) * RK + DK * ESZ);
+  const rsrc_t rk = make_rsrc(kb + t0 * HDK, (nt - 1) * RK + DK * ESZ);
+  const rsrc_t rv = make_rsrc(vb + t0 * HDV, (nt - 1) * RV + DV * ESZ);
+  const rsrc_t ry = make_rsrc(yb + t0 * HDV, (nt - 1) * RV + DV * ESZ);
+  const rsrc_t rdq = make_rsrc(dqb + t0 * HDK, (nt - 1) * RK + DK * ESZ);
+  const rsrc_t rdn = make_rsrc(dnb + t0 * HDV, (nt - 1) * (uint32_t)HDV * 4 + DV * 4);
+  const rsrc_t rdd = make_rsrc(NORM ? ddb + (int64_t)t0 * H : (const float*)qb, NORM ? ((nt - 1) * H + 1) * 4 : 0);
+  const rsrc_t rmk = make_rsrc(mb ? mb + t0 : (const uint8_t*)qb, mb ? nt : 0);  // (no mask: read as 0, ignored)
+
+  // ---- prefetch registers: the next chunk's data, consumed before they are
+  // loaded again and tested only where they are used (a loaded value tested
+  // or copied early would make the wave wait for every load issued before it)
   const Item it = make_item<NIQ, DK / 8, NIQ, DK / 8, NIV, DV / 8>(tid);
-  const IT* ibase = it.m == 0 ? qb : (it.m == 1 ? kb : vb);
-  const int64_t ild = it.m == 2 ? HDV : HDK;
+  const int im = it.on ? it.m : 0;  // (threads without an item read block 0 of q)
+  const rsrc_t ir = im == 0 ? rq : (im == 1 ? rk : rv);
+  const uint32_t irow = im == 2 ? RV : RK;
   u32x4_t raw[2];
-  uint32_t rvalid = 0;
+  uint32_t rm0 = 1, rm1 = 1;         // mask bytes of the item's tokens
   const int iq = 16 * (w & 1) + lr;  // query row of the lane in a chunk (phases B, C)
-  u32x2_t dyraw = u32x2_t{0u, 0u};
-  bool qv = false;
-  auto prefetch = [&](int c0) {
-    if (it.on) {
-      rvalid = 0;
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const int t = c0 + 2 * it.p + n;
-        raw[n] = t < t1 ? ld16(ibase + t * ild + 8 * it.cb) : u32x4_t{0u, 0u, 0u, 0u};
-        rvalid |= (valid(t) ? 1u : 0u) << n;
-      }
-    }
-    const int t = c0 + iq;
-    qv = valid(t);
-    if (w < 2 * NET) dyraw = t < t1 ? *(const u32x2_t*)(yb + t * HDV + 16 * (w >> 1) + 4 * lg) : u32x2_t{0u, 0u};
+  u32x2_t dyraw = u32x2_t{0u, 0u};   // dy of the lane's query at value dims 16(w >> 1) + 4lg .. +3 (phase B)
+  u32x2_t qraw = u32x2_t{0u, 0u};    // q of the lane's query at key dims 16(w >> 1) + 4lg .. +3 (phase C)
+  uint32_t qm = 1;                   // mask byte of the lane's query
+  const uint32_t ycol = (16 * min(w >> 1, NET - 1) + 4 * lg) * ESZ, qcol = (16 * min(w >> 1, NDT - 1) + 4 * lg) * ESZ;
+  auto prefetch_items = [&](int c0) {
+    const uint32_t ta = (uint32_t)(c0 - t0 + 2 * it.p);
+    raw[0] = bload16(ir, ta * irow + 16 * it.cb);
+    raw[1] = bload16(ir, (ta + 1) * irow + 16 * it.cb);
+    rm0 = bload1(rmk, ta);
+    rm1 = bload1(rmk, ta + 1);
   };
+  auto prefetch_lane = [&](int c0) {
+    const uint32_t t = (uint32_t)(c0 - t0 + iq);
+    qm = bload1(rmk, t);
+    dyraw = bload8(ry, t * RV + ycol);
+    qraw = bload8(rq, t * RK + qcol);
+  };
+  // the item's token 2p + n of the chunk at c0 exists and is not masked
+  auto item_ok = [&](int c0, int n) { return c0 + 2 * it.p + n < t1 && (mb == nullptr || (n ? rm1 : rm0) != 0u); };
 
   // ---- staging of phi(Q), phi(K), V (rows and transposed) and of S
-  auto stage = [&]() {
+  auto stage = [&](int c0) {
     if (!it.on) return;
-    float f[2][8];
-    Io<IT>::unpack(raw[0], f[0]);
-    Io<IT>::unpack(raw[1], f[1]);
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const bool ok = (rvalid >> n) & 1u;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[n][e] = ok ? (it.m < 2 ? phi_rt(f[n][e], elu, eps) : f[n][e]) : 0.f;
+    const bool ok0 = item_ok(c0, 0), ok1 = item_ok(c0, 1);
+    u32x4_t h[2], lo[2];
+    if (!VLO && im == 2) {
+      // bf16 values are exact: the loaded words, no lo part
+      const u32x4_t z4 = u32x4_t{0u, 0u, 0u, 0u};
+      h[0] = ok0 ? raw[0] : z4;
+      h[1] = ok1 ? raw[1] : z4;
+    } else {
+      float f[2][8];
+      Io<IT>::unpack(raw[0], f[0]);
+      Io<IT>::unpack(raw[1], f[1]);
+      if (im == 2)
+        split_rows<kEluPlusOne, false>(f, ok0, ok1, eps, h, lo);
+      else if (elu)
+        split_rows<kEluPlusOne, true>(f, ok0, ok1, eps, h, lo);
+      else
+        split_rows<kReluEps, true>(f, ok0, ok1, eps, h, lo);
     }
-    const int rld = it.m == 2 ? LDV : LDK;
-    const int rbase = it.m == 0 ? Ly::QR : (it.m == 1 ? Ly::KR : Ly::VR);
-    const int rlo = it.m == 2 ? Ly::VRL : Ly::QRL;
-    const int tbase = it.m == 0 ? Ly::QT : (it.m == 1 ? Ly::KT : Ly::VT);
-    const int tlo = it.m == 2 ? Ly::VTL : Ly::QTL;
-    const bool lo_too = it.m < 2 || VLO;
+    const int rld = im == 2 ? LDV : LDK;
+    const int rbase = im == 0 ? Ly::QR : (im == 1 ? Ly::KR : Ly::VR);
+    const int rlo = im == 2 ? Ly::VRL : Ly::QRL;
+    const int tbase = im == 0 ? Ly::QT : (im == 1 ? Ly::KT : Ly::VT);
+    const int tlo = im == 2 ? Ly::VTL : Ly::QTL;
+    const bool lo_too = im < 2 || VLO;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      u32x4_t hw, lw;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { const u32x2_t t2_ = split2(f[n][2 * e], f[n][2 * e + 1]); hw[e] = t2_[0]; lw[e] = t2_[1]; }
       const int off = rbase + (2 * it.p + n) * rld + 8 * it.cb;
-      st16(sm + off, hw);
-      if (lo_too) st16(sm + off + rlo, lw);
+      st16(sm + off, h[n]);
+      if (lo_too) st16(sm + off + rlo, lo[n]);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      uint32_t h0, l0, h1, l1;
-      split1(f[0][e], h0, l0);
-      split1(f[1][e], h1, l1);
       const int off = tbase + (8 * it.cb + e) * LDC + 2 * it.p;
-      *(uint32_t*)(sm + off) = h0 | (h1 << 16);
-      if (lo_too) *(uint32_t*)(sm + off + tlo) = l0 | (l1 << 16);
+      *(uint32_t*)(sm + off) = tword(h[0], h[1], e);
+      if (lo_too) *(uint32_t*)(sm + off + tlo) = tword(lo[0], lo[1], e);
     }
   };
   auto write_s = [&]() {
@@ -296,14 +377,16 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
   };
 
   const int nch = (t1 - t0 + kBC - 1) / kBC;
-  if (nch > 0) prefetch(t0);
+  if (nch > 0) {
+    prefetch_items(t0);
+    prefetch_lane(t0);
+  }
   for (int c = 0; c < nch; ++c) {
     const int cb0 = t0 + c * kBC;
-    stage();
+    stage(cb0);
     write_s();
-    const u32x2_t dyc = dyraw;
-    const bool qvc = qv;
-    if (c + 1 < nch) prefetch(cb0 + kBC);
+    const bool qvc = cb0 + iq < t1 && (mb == nullptr || qm != 0u);
+    if (c + 1 < nch) prefetch_items(cb0 + kBC);
     __syncthreads();
 
     // ---- phase B: num, den of the wave's query block (w & 1) and value tile
@@ -361,13 +444,9 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
         }
         rden = 1.f / (dacc[0] + eps);
       }
-      const u32x2_t yw = dyc;
       f32x4_t dn;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float y = Io<IT>::to_f32(q & 1 ? yw[q >> 1] >> 16 : yw[q >> 1] & 0xffffu);
-        dn[q] = qvc ? y * rden : 0.f;
-      }
+      for (int q = 0; q < 4; ++q) dn[q] = qvc ? io_at<IT>(dyraw[q >> 1], q & 1) * rden : 0.f;
       // dnum rows (dv contiguous) and dnum^T (token contiguous)
       u32x2_t hw, lw;
       { const u32x2_t t2_ = split2(dn[0], dn[1]); hw[0] = t2_[0]; lw[0] = t2_[1]; }
@@ -396,20 +475,20 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
           sm[Ly::DT + Ly::DTL + (DV + et) * LDC + iq] = (uint16_t)pl1;
         }
       }
-      const int tq = cb0 + iq;
-      if (tq < t1) *(f32x4_t*)(dnb + tq * HDV + 16 * et + 4 * lg) = dn;
+      bstore16(rdn, (uint32_t)(cb0 - t0 + iq) * (uint32_t)HDV * 4 + (16 * et + 4 * lg) * 4,
+               __builtin_bit_cast(u32x4_t, dn));
     }
     __syncthreads();
 
     // ---- phase C: dq of the wave's query block (w & 1) and key-dim tile (w >> 1)
     if (w < 2 * NDT) {
       const int dt = w >> 1;
-      const int tq = cb0 + iq;
+      const uint32_t tr = (uint32_t)(cb0 - t0 + iq);  // the query's row in the segment
       float dd = 0.f;
       if constexpr (NORM) {
 #pragma unroll
         for (int et = 0; et < NET; ++et) dd += part[et * kBC + iq];
-        if (dt == 0 && lg == 0 && tq < t1) ddb[(int64_t)tq * H] = dd;
+        bstore4(rdd, (dt == 0 && lg == 0) ? tr * (uint32_t)H * 4 : kDrop, __float_as_uint(dd));
       }
       u32x4_t dh[KSV], dl[KSV];
 #pragma unroll
@@ -455,14 +534,16 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) g[q] += (bf_at(zh[q >> 1], q & 1) + bf_at(zl[q >> 1], q & 1)) * dd;
       }
-      if (tq < t1) {
-        const f32x4_t x = ld4f(qb + tq * HDK + 16 * dt + 4 * lg);
+      {
         float o[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = qvc ? g[q] * dphi_rt(x[q], elu) : 0.f;
-        store4(dqb + tq * HDK + 16 * dt + 4 * lg, o[0], o[1], o[2], o[3]);
+        for (int q = 0; q < 4; ++q) o[q] = qvc ? g[q] * dphi_rt(io_at<IT>(qraw[q >> 1], q & 1), elu) : 0.f;
+        bstore8(rdq, tr * RK + (16 * dt + 4 * lg) * ESZ, pack4<IT>(o[0], o[1], o[2], o[3]));
       }
     }
+
+    // dy, q and the mask byte of the lane's next query (this chunk's are used)
+    if (c + 1 < nch) prefetch_lane(cb0 + kBC);
 
     // ---- phase D: S += phiK^T V (z += phiK^T 1), dS += phiQ^T dnum (dz parts += phiQ^T dden parts)
 #pragma unroll
@@ -548,7 +629,6 @@ __global__ __launch_bounds__(kBT, 2) void bwd_state_kernel(BwdChunkArgs a) {
   const uint8_t* mb = a.mask ? a.mask + (int64_t)b * T : nullptr;
   const float eps = a.eps;
   const bool elu = a.fm == kEluPlusOne;
-  auto valid = [&](int t) { return t < t1 && (mb == nullptr || mb[t] != 0); };
 
   f32x4_t st[TPW];
   auto tile = [&](int k, int& dt, int& et) {
@@ -563,48 +643,61 @@ __global__ __launch_bounds__(kBT, 2) void bwd_state_kernel(BwdChunkArgs a) {
     for (int i = tid; i < 16 * LDC; i += kBT) sm[Ly::VT + DV * LDC + i] = 0x3f80;  // bf16 1.0
   }
 
+  constexpr uint32_t ESZ = sizeof(IT);
+  const uint32_t nt = (uint32_t)(t1 - t0);
+  const uint32_t RK = (uint32_t)HDK * ESZ, RV = (uint32_t)HDV * ESZ;
+  const rsrc_t rk = make_rsrc(kb + t0 * HDK, (nt - 1) * RK + DK * ESZ);
+  const rsrc_t rv = make_rsrc(vb + t0 * HDV, (nt - 1) * RV + DV * ESZ);
+  const rsrc_t rmk = make_rsrc(mb ? mb + t0 : (const uint8_t*)kb, mb ? nt : 0);
   const Item it = make_item<NIK, DK / 8, NIV, DV / 8, 0, 1>(tid);  // m: 0 k, 1 v
-  const IT* ibase = it.m == 0 ? kb : vb;
-  const int64_t ild = it.m == 0 ? HDK : HDV;
+  const int im = it.on ? it.m : 0;  // (threads without an item read block 0 of k)
+  const rsrc_t ir = im == 0 ? rk : rv;
+  const uint32_t irow = im == 0 ? RK : RV;
+  // (buffer loads, mask bytes tested at the stage: see the forward pass)
   u32x4_t raw0, raw1;
-  uint32_t rvalid = 0;
+  uint32_t rm0 = 1, rm1 = 1;
   auto prefetch = [&](int c0) {
-    if (!it.on) return;
-    const int ta = c0 + 2 * it.p, tb = ta + 1;
-    const u32x4_t z4 = u32x4_t{0u, 0u, 0u, 0u};
-    raw0 = ta < t1 ? ld16(ibase + ta * ild + 8 * it.cb) : z4;
-    raw1 = tb < t1 ? ld16(ibase + tb * ild + 8 * it.cb) : z4;
-    rvalid = (valid(ta) ? 1u : 0u) | (valid(tb) ? 2u : 0u);
+    const uint32_t ta = (uint32_t)(c0 - t0 + 2 * it.p);
+    raw0 = bload16(ir, ta * irow + 16 * it.cb);
+    raw1 = bload16(ir, (ta + 1) * irow + 16 * it.cb);
+    rm0 = bload1(rmk, ta);
+    rm1 = bload1(rmk, ta + 1);
   };
-  auto stage = [&]() {
+  auto stage = [&](int c0) {
     if (!it.on) return;
-    float f[2][8];
-    Io<IT>::unpack(raw0, f[0]);
-    Io<IT>::unpack(raw1, f[1]);
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const bool ok = (rvalid >> n) & 1u;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[n][e] = ok ? (it.m == 0 ? phi_rt(f[n][e], elu, eps) : f[n][e]) : 0.f;
+    const bool ok0 = c0 + 2 * it.p < t1 && (mb == nullptr || rm0 != 0u);
+    const bool ok1 = c0 + 2 * it.p + 1 < t1 && (mb == nullptr || rm1 != 0u);
+    u32x4_t h[2], lo[2];
+    if (!VLO && im == 1) {
+      const u32x4_t z4 = u32x4_t{0u, 0u, 0u, 0u};
+      h[0] = ok0 ? raw0 : z4;
+      h[1] = ok1 ? raw1 : z4;
+    } else {
+      float f[2][8];
+      Io<IT>::unpack(raw0, f[0]);
+      Io<IT>::unpack(raw1, f[1]);
+      if (im == 1)
+        split_rows<kEluPlusOne, false>(f, ok0, ok1, eps, h, lo);
+      else if (elu)
+        split_rows<kEluPlusOne, true>(f, ok0, ok1, eps, h, lo);
+      else
+        split_rows<kReluEps, true>(f, ok0, ok1, eps, h, lo);
     }
-    const int tbase = it.m == 0 ? Ly::KT : Ly::VT;
-    const int tlo = it.m == 0 ? Ly::KTL : Ly::VTL;
-    const bool lo_too = it.m == 0 || VLO;
+    const int tbase = im == 0 ? Ly::KT : Ly::VT;
+    const int tlo = im == 0 ? Ly::KTL : Ly::VTL;
+    const bool lo_too = im == 0 || VLO;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      uint32_t h0, l0, h1, l1;
-      split1(f[0][e], h0, l0);
-      split1(f[1][e], h1, l1);
       const int off = tbase + (8 * it.cb + e) * LDC + 2 * it.p;
-      *(uint32_t*)(sm + off) = h0 | (h1 << 16);
-      if (lo_too) *(uint32_t*)(sm + off + tlo) = l0 | (l1 << 16);
+      *(uint32_t*)(sm + off) = tword(h[0], h[1], e);
+      if (lo_too) *(uint32_t*)(sm + off + tlo) = tword(lo[0], lo[1], e);
     }
   };
 
   const int nch = (t1 - t0 + kBC - 1) / kBC;
   if (nch > 0) prefetch(t0);
   for (int c = 0; c < nch; ++c) {
-    stage();
+    stage(t0 + c * kBC);
     if (c + 1 < nch) prefetch(t0 + (c + 1) * kBC);
     __syncthreads();
 #pragma unroll
@@ -691,7 +784,6 @@ __global__ __launch_bounds__(kBT, 2) void bwd_rev_kernel(BwdChunkArgs a) {
   const uint8_t* mb = a.mask ? a.mask + (int64_t)b * T : nullptr;
   const float eps = a.eps;
   const bool elu = a.fm == kEluPlusOne;
-  auto valid = [&](int t) { return t < t1 && (mb == nullptr || mb[t] != 0); };
 
   // ---- dS (+ dz) tiles: the gradient sums of the tokens after the current
   // chunk; the dz tile holds dz in column 0 (row DV of dnum^T is dden)
@@ -729,95 +821,111 @@ __global__ __launch_bounds__(kBT, 2) void bwd_rev_kernel(BwdChunkArgs a) {
   // ---- prefetch registers: q (rows and transposed), k (rows), v (rows), dnum
   // (rows and transposed, 8 fp32 values of two tokens: 4 loads)
   const Item it = make_item<NIQ, DK / 8, NIQ, DK / 8, NIV, DV / 8, NIV, DV / 8>(tid);
-  // the item's rows: a 16-byte block of q, k or v (token 2p: raw0, token
-  // 2p+1: raw2) or two of dnum (raw0, raw1 and raw2, raw3)
-  const bool idn = it.m == 3;
-  const unsigned char* ibase = (const unsigned char*)(it.m == 0 ? (const void*)qb
-                                                                : (it.m == 1 ? (const void*)kb
-                                                                             : (it.m == 2 ? (const void*)vb
-                                                                                          : (const void*)dnb)));
-  const int64_t ild = (it.m == 0 || it.m == 1) ? HDK * sizeof(IT) : (it.m == 2 ? HDV * sizeof(IT) : HDV * 4);
-  const int iblk = idn ? 32 * it.cb : 16 * it.cb;  // byte offset of the block in the row
-  u32x4_t raw0, raw1 = u32x4_t{0u, 0u, 0u, 0u}, raw2, raw3 = u32x4_t{0u, 0u, 0u, 0u};
-  uint32_t rvalid = 0;
-  float ddn = 0.f;                   // dden of token tid (tid < 32)
+  // ---- the segment's buffers (token t at byte (t - t0) * row)
+  constexpr uint32_t ESZ = sizeof(IT);
+  const uint32_t nt = (uint32_t)(t1 - t0);
+  const uint32_t RK = (uint32_t)HDK * ESZ, RV = (uint32_t)HDV * ESZ, RD = (uint32_t)HDV * 4;
+  const rsrc_t rq = make_rsrc(qb + t0 * HDK, (nt - 1) * RK + DK * ESZ);
+  const rsrc_t rk = make_rsrc(kb + t0 * HDK, (nt - 1) * RK + DK * ESZ);
+  const rsrc_t rv = make_rsrc(vb + t0 * HDV, (nt - 1) * RV + DV * ESZ);
+  const rsrc_t rdn = make_rsrc(dnb + t0 * HDV, (nt - 1) * RD + DV * 4);
+  const rsrc_t rdd = make_rsrc(NORM ? ddb + (int64_t)t0 * H : (const float*)qb, NORM ? ((nt - 1) * H + 1) * 4 : 0);
+  const rsrc_t rdk = make_rsrc(dkb + t0 * HDK, (nt - 1) * RK + DK * ESZ);
+  const rsrc_t rdv = make_rsrc(dvb + t0 * HDV, (nt - 1) * RV + DV * ESZ);
+  const rsrc_t rmk = make_rsrc(mb ? mb + t0 : (const uint8_t*)qb, mb ? nt : 0);
+
+  // ---- prefetch registers (buffer loads, tested where used: see the forward
+  // pass).  The item's rows: a 16-byte block of q, k or v (token 2p: raw0,
+  // token 2p+1: raw2; raw1, raw3 repeat them) or two of dnum (raw0, raw1 and
+  // raw2, raw3).
+  const int im = it.on ? it.m : 0;  // (threads without an item read block 0 of q)
+  const bool idn = im == 3;
+  const rsrc_t ir = im == 0 ? rq : (im == 1 ? rk : (im == 2 ? rv : rdn));
+  const uint32_t irow = im <= 1 ? RK : (im == 2 ? RV : RD);
+  const uint32_t iblk = idn ? 32 * it.cb : 16 * it.cb;  // byte offset of the block in the row
+  const uint32_t iblk2 = idn ? iblk + 16 : iblk;
+  u32x4_t raw0, raw1, raw2, raw3;
+  uint32_t rm0 = 1, rm1 = 1;
+  float ddn = 0.f;                   // dden of token tid % 32 of the chunk
   const int jq = 16 * (w & 1) + lr;  // key row of the lane in a chunk (phases E, F)
-  bool kv = false;
-  auto prefetch = [&](int c0) {
-    if (it.on) {
-      const u32x4_t z4 = u32x4_t{0u, 0u, 0u, 0u};
-      const int ta = c0 + 2 * it.p, tb = ta + 1;
-      const unsigned char* pa = ibase + ta * ild + iblk;
-      const unsigned char* pb = ibase + tb * ild + iblk;
-      raw0 = ta < t1 ? ld16(pa) : z4;
-      raw2 = tb < t1 ? ld16(pb) : z4;
-      if (idn) {
-        raw1 = ta < t1 ? ld16(pa + 16) : z4;
-        raw3 = tb < t1 ? ld16(pb + 16) : z4;
-      }
-      rvalid = (valid(ta) ? 1u : 0u) | (valid(tb) ? 2u : 0u);
-    }
-    if constexpr (NORM) {
-      if (tid < kBC) ddn = c0 + tid < t1 ? ddb[(int64_t)(c0 + tid) * H] : 0.f;
-    }
-    kv = valid(c0 + jq);
+  u32x2_t kraw = u32x2_t{0u, 0u};    // k of the lane's key at key dims 16(w >> 1) + 4lg .. +3 (phase F)
+  uint32_t km = 1;                   // mask byte of the lane's key
+  const uint32_t kcol = (16 * min(w >> 1, NDT - 1) + 4 * lg) * ESZ;
+  auto prefetch_items = [&](int c0) {
+    const uint32_t ta = (uint32_t)(c0 - t0 + 2 * it.p);
+    raw0 = bload16(ir, ta * irow + iblk);
+    raw1 = bload16(ir, ta * irow + iblk2);
+    raw2 = bload16(ir, (ta + 1) * irow + iblk);
+    raw3 = bload16(ir, (ta + 1) * irow + iblk2);
+    rm0 = bload1(rmk, ta);
+    rm1 = bload1(rmk, ta + 1);
+    if constexpr (NORM) ddn = __uint_as_float(bload4(rdd, (uint32_t)(c0 - t0 + (tid & (kBC - 1))) * H * 4));
+  };
+  auto prefetch_lane = [&](int c0) {
+    const uint32_t t = (uint32_t)(c0 - t0 + jq);
+    km = bload1(rmk, t);
+    kraw = bload8(rk, t * RK + kcol);
   };
 
-  auto stage = [&]() {
+  auto stage = [&](int c0) {
     if constexpr (NORM) {
       if (tid < kBC) {
-        ddv[tid] = ddn;
+        const float dd = c0 + tid < t1 ? ddn : 0.f;
+        ddv[tid] = dd;
         uint32_t hh, ll;
-        split1(ddn, hh, ll);
+        split1(dd, hh, ll);
         sm[Ly::DT + DV * LDC + tid] = (uint16_t)hh;
         sm[Ly::DT + Ly::DTL + DV * LDC + tid] = (uint16_t)ll;
       }
     }
     if (!it.on) return;
-    float f[2][8];
-    if (!idn) {
-      Io<IT>::unpack(raw0, f[0]);
-      Io<IT>::unpack(raw2, f[1]);
+    const bool ok0 = c0 + 2 * it.p < t1 && (mb == nullptr || rm0 != 0u);
+    const bool ok1 = c0 + 2 * it.p + 1 < t1 && (mb == nullptr || rm1 != 0u);
+    u32x4_t h[2], lo[2];
+    if (!VLO && im == 2) {
+      const u32x4_t z4 = u32x4_t{0u, 0u, 0u, 0u};
+      h[0] = ok0 ? raw0 : z4;
+      h[1] = ok1 ? raw2 : z4;
     } else {
+      float f[2][8];
+      if (!idn) {
+        Io<IT>::unpack(raw0, f[0]);
+        Io<IT>::unpack(raw2, f[1]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[0][e] = __uint_as_float(raw0[e]);
-        f[0][4 + e] = __uint_as_float(raw1[e]);
-        f[1][e] = __uint_as_float(raw2[e]);
-        f[1][4 + e] = __uint_as_float(raw3[e]);
+        for (int e = 0; e < 4; ++e) {
+          f[0][e] = __uint_as_float(raw0[e]);
+          f[0][4 + e] = __uint_as_float(raw1[e]);
+          f[1][e] = __uint_as_float(raw2[e]);
+          f[1][4 + e] = __uint_as_float(raw3[e]);
+        }
       }
+      if (im >= 2)
+        split_rows<kEluPlusOne, false>(f, ok0, ok1, eps, h, lo);
+      else if (elu)
+        split_rows<kEluPlusOne, true>(f, ok0, ok1, eps, h, lo);
+      else
+        split_rows<kReluEps, true>(f, ok0, ok1, eps, h, lo);
     }
+    const int rld = im >= 2 ? LDV : LDK;
+    const int rbase = im == 0 ? Ly::QR : (im == 1 ? Ly::KR : (im == 2 ? Ly::VR : Ly::DN));
+    const int rlo = im == 3 ? Ly::DNL : (im == 2 ? Ly::VRL : Ly::QRL);
+    const bool lo_too = im != 2 || VLO;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      const bool ok = (rvalid >> n) & 1u;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[n][e] = ok ? (it.m < 2 ? phi_rt(f[n][e], elu, eps) : f[n][e]) : 0.f;
-    }
-    const int rld = it.m >= 2 ? LDV : LDK;
-    const int rbase = it.m == 0 ? Ly::QR : (it.m == 1 ? Ly::KR : (it.m == 2 ? Ly::VR : Ly::DN));
-    const int rlo = it.m == 3 ? Ly::DNL : (it.m == 2 ? Ly::VRL : Ly::QRL);
-    const bool lo_too = it.m != 2 || VLO;
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      u32x4_t hw, lw;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { const u32x2_t t2_ = split2(f[n][2 * e], f[n][2 * e + 1]); hw[e] = t2_[0]; lw[e] = t2_[1]; }
       const int off = rbase + (2 * it.p + n) * rld + 8 * it.cb;
-      st16(sm + off, hw);
-      if (lo_too) st16(sm + off + rlo, lw);
+      st16(sm + off, h[n]);
+      if (lo_too) st16(sm + off + rlo, lo[n]);
     }
-    if (it.m == 0 || it.m == 3) {
+    if (im == 0 || im == 3) {
       // transposed: phi(Q)^T, dnum^T
-      const int tbase = it.m == 0 ? Ly::QT : Ly::DT;
-      const int tlo = it.m == 0 ? Ly::QTL : Ly::DTL;
+      const int tbase = im == 0 ? Ly::QT : Ly::DT;
+      const int tlo = im == 0 ? Ly::QTL : Ly::DTL;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint32_t h0, l0, h1, l1;
-        split1(f[0][e], h0, l0);
-        split1(f[1][e], h1, l1);
         const int off = tbase + (8 * it.cb + e) * LDC + 2 * it.p;
-        *(uint32_t*)(sm + off) = h0 | (h1 << 16);
-        *(uint32_t*)(sm + off + tlo) = l0 | (l1 << 16);
+        *(uint32_t*)(sm + off) = tword(h[0], h[1], e);
+        *(uint32_t*)(sm + off + tlo) = tword(lo[0], lo[1], e);
       }
     }
   };
@@ -849,15 +957,18 @@ __global__ __launch_bounds__(kBT, 2) void bwd_rev_kernel(BwdChunkArgs a) {
   };
 
   const int nch = (t1 - t0 + kBC - 1) / kBC;
-  if (nch > 0) prefetch(t0 + (nch - 1) * kBC);
+  if (nch > 0) {
+    prefetch_items(t0 + (nch - 1) * kBC);
+    prefetch_lane(t0 + (nch - 1) * kBC);
+  }
   for (int c = nch - 1; c >= 0; --c) {
     const int cb0 = t0 + c * kBC;
-    stage();
+    stage(cb0);
     write_ds();
-    const bool kvc = kv;
-    if (c > 0) prefetch(cb0 - kBC);
-    __syncthreads();
     const int tj = cb0 + jq;
+    const bool kvc = tj < t1 && (mb == nullptr || km != 0u);
+    if (c > 0) prefetch_items(cb0 - kBC);
+    __syncthreads();
 
     // ---- phase E: dv of the wave's key block (w & 1) and value tile (w >> 1)
     if (w < 2 * NET) {
@@ -897,9 +1008,8 @@ __global__ __launch_bounds__(kBT, 2) void bwd_rev_kernel(BwdChunkArgs a) {
           mm3(acc, ld16(sm + so), ld16(sm + so + Ly::SAL), kh[ks], kl[ks]);
         }
       }
-      if (tj < t1)
-        store4(dvb + tj * HDV + 16 * et + 4 * lg, kvc ? acc[0] : 0.f, kvc ? acc[1] : 0.f, kvc ? acc[2] : 0.f,
-               kvc ? acc[3] : 0.f);
+      bstore8(rdv, (uint32_t)(tj - t0) * RV + (16 * et + 4 * lg) * ESZ,
+              pack4<IT>(kvc ? acc[0] : 0.f, kvc ? acc[1] : 0.f, kvc ? acc[2] : 0.f, kvc ? acc[3] : 0.f));
     }
 
     // ---- phase F: dk of the wave's key block (w & 1) and key-dim tile (w >> 1)
@@ -954,14 +1064,16 @@ __global__ __launch_bounds__(kBT, 2) void bwd_rev_kernel(BwdChunkArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) g[q] += dzv[16 * dt + 4 * lg + q];
       }
-      if (tj < t1) {
-        const f32x4_t x = ld4f(kb + tj * HDK + 16 * dt + 4 * lg);
+      {
         float o[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = kvc ? g[q] * dphi_rt(x[q], elu) : 0.f;
-        store4(dkb + tj * HDK + 16 * dt + 4 * lg, o[0], o[1], o[2], o[3]);
+        for (int q = 0; q < 4; ++q) o[q] = kvc ? g[q] * dphi_rt(io_at<IT>(kraw[q >> 1], q & 1), elu) : 0.f;
+        bstore8(rdk, (uint32_t)(tj - t0) * RK + (16 * dt + 4 * lg) * ESZ, pack4<IT>(o[0], o[1], o[2], o[3]));
       }
     }
+
+    // k and the mask byte of the lane's key in the previous chunk (this chunk's are used)
+    if (c > 0) prefetch_lane(cb0 - kBC);
 
     // ---- phase G: dS += phiQ^T dnum, dz += phiQ^T dden (column 0 of the dz tile)
 #pragma unroll
