@@ -203,7 +203,15 @@ la_status la_gated_step(const void* q, const void* k, const void* v, const void*
  * scale, past/present state and GQA as la_gated_forward; keys are expected
  * L2-normalised (operator page, "Inputs").  Evaluated chunk-parallel (64-token
  * chunks, a 64 x 64 triangular solve per chunk) by one workgroup per (batch,
- * kv head) over the whole sequence; no workspace.  Decays of any strength are
+ * kv head, query-head group) over the whole sequence.  With few of those (at
+ * most 64) and a workspace of la_delta_workspace_size bytes, the sequence is
+ * split into segments of whole chunks instead: every segment's state map
+ * S_end = M S_start + N (M = the product of its (I - beta k k^T) E_t factors)
+ * is formed by the same kernels, run from S = I with zero values (M) and from
+ * S = 0 (N), the start states follow by composing the maps in order (fp32
+ * D x D products), and every segment then runs with outputs from its start
+ * state.  workspace NULL, or fewer bytes than reported, runs without the split
+ * (same results up to rounding, one workgroup per unit).  Decays of any strength are
  * supported: per-dim decays, and per-head decays with fp16 inputs, rescale the
  * keys relative to a reference token, and a workgroup whose cumulative decay
  * inside a 64-token chunk exceeds 60 in magnitude re-evaluates its whole
@@ -217,7 +225,14 @@ la_status la_delta_forward(const void* q, const void* k, const void* v, const vo
                            int32_t per_dim_decay, const void* beta, int32_t beta_per_head,
                            const float* past_state, float* present_state, void* out, int64_t B,
                            int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv, int32_t dtype,
-                           float scale, void* stream);
+                           float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace (16-byte aligned, not overlapping any argument)
+ * with which la_delta_forward splits these sizes over T; 0 = it never splits
+ * them (enough workgroups already, T == 1, or the token-by-token path).  Sizes
+ * and errors as la_delta_forward; per_dim_decay as passed there. */
+la_status la_delta_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
+                                  int32_t dtype, int32_t per_dim_decay, size_t* bytes);
 
 /* Bytes of device workspace la_backward needs for these sizes (0 = none). */
 la_status la_backward_workspace_size(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv,

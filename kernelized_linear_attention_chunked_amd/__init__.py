@@ -46,7 +46,7 @@ __all__ = [
 EXPORTED_SYMBOLS = (
     "la_initial_state", "la_workspace_size", "la_forward", "la_forward_noalloc", "la_step",
     "la_gated_workspace_size",
-    "la_gated_forward", "la_gated_step", "la_delta_forward", "la_backward_workspace_size",
+    "la_gated_forward", "la_gated_step", "la_delta_forward", "la_delta_workspace_size", "la_backward_workspace_size",
     "la_backward", "la_status_string", "la_last_error_message",
 )
 
@@ -96,7 +96,8 @@ def load_library(build_if_missing: bool = True):
                                          f32, p, sz, p]
         lib.la_gated_step.argtypes = [p, p, p, p, i32, p, p, p, i64, i64, i64, i64, i64, i32, f32, p]
         lib.la_delta_forward.argtypes = [p, p, p, p, i32, p, i32, p, p, p, i64, i64, i64, i64, i64, i64,
-                                         i32, f32, p]
+                                         i32, f32, p, sz, p]
+        lib.la_delta_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
         lib.la_backward_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
         lib.la_backward.argtypes = [p, p, p, p, p, p, p, p, p, i32, i32, f32, p, p, p, p, p, i64, i64, i64,
                                     i64, i64, i32, p, sz, p]
@@ -508,10 +509,14 @@ def la_delta_forward(query, key, value, q_num_heads, kv_num_heads, beta, decay=N
     present_state = (torch.empty((B, Hkv, Dk, Dv), dtype=torch.float32, device=dev)
                      if present_state is None
                      else _output(present_state, "present_state", dev, torch.float32, (B, Hkv, Dk, Dv)))
+    n = ctypes.c_size_t(0)
+    _check(lib.la_delta_workspace_size(B, T, Hq, Hkv, Dk, Dv, _dtype_code(q), int(per_dim), ctypes.byref(n)),
+           "la_delta_workspace_size")
+    ws = torch.empty(n.value, dtype=torch.uint8, device=dev) if n.value else None
     _check(lib.la_delta_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), int(per_dim), _ptr(be),
                                 int(beta_per_head), _ptr(past), _ptr(present_state),
                                 _ptr(out), B, T, Hq, Hkv, Dk, Dv, _dtype_code(q), float(scale),
-                                _stream(dev)), "la_delta_forward")
+                                _ptr(ws), n.value, _stream(dev)), "la_delta_forward")
     return out, present_state
 
 

@@ -803,11 +803,51 @@ LA_EXPORT la_status la_gated_step(const void* q, const void* k, const void* v, c
 // ---------------------------------------------------------------------------
 // delta rules
 
+namespace {
+// Split of a delta-rule sequence over T (shape-only): with at most 64 (unit,
+// query-head group) workgroups, segments of whole chunks (at least 4 each)
+// bring the count towards 256; nseg = 1: no split.
+struct DeltaPlan {
+  int64_t nseg, seg_len;
+};
+DeltaPlan plan_delta(int64_t U, int64_t hs, int64_t T) {
+  DeltaPlan p{1, T};
+  const int64_t groups = U * hs, nchunks = ceil_div(T, kChunk);
+  if (groups <= 0 || groups > 64) return p;
+  int64_t want = ceil_div(256, groups);
+  if (want > nchunks / 4) want = nchunks / 4;
+  if (want < 2) return p;
+  const int64_t seg_chunks = ceil_div(nchunks, want);
+  p.nseg = ceil_div(nchunks, seg_chunks);
+  p.seg_len = seg_chunks * kChunk;
+  return p;
+}
+// workspace of a split: the maps M and N of every segment but the last, the
+// start state of every segment, and the identity
+size_t delta_ws_bytes(int64_t U, int64_t D, const DeltaPlan& p) {
+  if (p.nseg <= 1) return 0;
+  return (size_t)D * D * 4 * (size_t)(U * (p.nseg - 1) * 2 + U * p.nseg + 1);
+}
+}  // namespace
+
+LA_EXPORT la_status la_delta_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
+                                            int32_t dtype, int32_t per_dim_decay, size_t* bytes) {
+  if (!bytes) return fail(LA_ERR_NULL_ARG, "bytes is NULL");
+  la_status s = check_gated(B, T, Hq, Hkv, Dk, Dv, dtype);
+  if (s != LA_OK) return s;
+  const int64_t U = B * Hkv, G = Hq / Hkv;
+  *bytes = 0;
+  if (U > 0 && T > 1 && !by_token(per_dim_decay != 0, dtype, Dk, T))
+    *bytes = delta_ws_bytes(U, Dk, plan_delta(U, G / head_tile(G), T));
+  return ok();
+}
+
 LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v, const void* decay,
                                      int32_t per_dim_decay, const void* beta, int32_t beta_per_head,
                                      const float* past_state, float* present_state, void* out,
                                      int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,
-                                     int64_t Dv, int32_t dtype, float scale, void* stream) {
+                                     int64_t Dv, int32_t dtype, float scale, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
   la_status s = check_gated(B, T, Hq, Hkv, Dk, Dv, dtype);
   if (s != LA_OK) return s;
   if (isnan(scale) || isinf(scale)) return fail(LA_ERR_BAD_ARG, "scale must be finite");
@@ -833,6 +873,14 @@ LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v
   if (overlap(rpo, rpi) && present_state != past_state)
     return fail(LA_ERR_BAD_ARG, "present_state may equal past_state exactly but not partially overlap it");
   if (U > (int64_t)1 << 31) return fail(LA_ERR_SHAPE, "too many (batch, kv head) units");
+  if (workspace && workspace_bytes > 0) {
+    if (!aligned16(workspace)) return fail(LA_ERR_BAD_ARG, "the workspace must be 16-byte aligned");
+    const Range rw = range(workspace, (int64_t)workspace_bytes);
+    for (const Range& i : ins)
+      if (overlap(rw, i)) return fail(LA_ERR_BAD_ARG, "the workspace overlaps an input");
+    if (overlap(rw, ro) || overlap(rw, rpi) || overlap(rw, rpo))
+      return fail(LA_ERR_BAD_ARG, "the workspace overlaps out or a state buffer");
+  }
   if (scale == 0.f) scale = 1.f / sqrtf((float)D);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = hipSuccess;
@@ -887,8 +935,55 @@ LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v
   a.scale = scale;
   const int kind = decay == nullptr ? 0 : (per_dim ? 2 : 1);
   a.hsplit = (int32_t)(G / head_tile(G));
-  e = la::launch_delta(dtype, (int)D, (int)head_tile(G), kind, a, st);
-  return device_status(e, "la_delta_forward");
+  a.nseg = 1;
+  a.seg_len = (int32_t)T;
+  a.s_in_u = D * D;
+  a.s_out_u = D * D;
+  const DeltaPlan p = plan_delta(U, a.hsplit, T);
+  const size_t need = delta_ws_bytes(U, D, p);
+  if (need == 0 || !workspace || workspace_bytes < need) {
+    // one workgroup per (unit, head group) over the whole sequence
+    e = la::launch_delta(dtype, (int)D, (int)head_tile(G), kind, a, st);
+    return device_status(e, "la_delta_forward");
+  }
+  // split over T: each segment's maps M (from S = I, zero values) and N (from
+  // S = 0), the start states by composing them in order, then every segment
+  // with outputs from its start state
+  const int64_t E = D * D, nseg = p.nseg;
+  float* Mw = (float*)workspace;
+  float* Nw = Mw + U * (nseg - 1) * E;
+  float* Sw = Nw + U * (nseg - 1) * E;
+  float* I = Sw + U * nseg * E;
+  e = la::launch_eye(I, (int)D, st);
+  la::DeltaArgs m = a;
+  m.out = nullptr;
+  m.hsplit = 1;
+  m.nseg = (int32_t)(nseg - 1);
+  m.seg_len = (int32_t)p.seg_len;
+  m.s_out_u = (nseg - 1) * E;
+  m.s_out_s = E;
+  m.s_out_all = 1;
+  la::DeltaArgs n = m;
+  m.v = nullptr;
+  m.s_in = I;
+  m.s_in_u = 0;
+  m.s_in_s = 0;
+  m.s_out = Mw;
+  n.s_in = nullptr;
+  n.s_out = Nw;
+  if (e == hipSuccess) e = la::launch_delta(dtype, (int)D, 1, kind, m, st);
+  if (e == hipSuccess) e = la::launch_delta(dtype, (int)D, 1, kind, n, st);
+  if (e == hipSuccess) e = la::launch_delta_compose(Mw, Nw, past_state, Sw, (int)U, (int)nseg, (int)D, st);
+  if (e == hipSuccess) {
+    la::DeltaArgs o = a;
+    o.nseg = (int32_t)nseg;
+    o.seg_len = (int32_t)p.seg_len;
+    o.s_in = Sw;
+    o.s_in_u = nseg * E;
+    o.s_in_s = E;
+    e = la::launch_delta(dtype, (int)D, (int)head_tile(G), kind, o, st);
+  }
+  return device_status(e, "la_delta_forward (split)");
 }
 
 // ---------------------------------------------------------------------------

@@ -26,8 +26,13 @@
 // waves of row block i subtract the earlier blocks' contributions with MFMAs
 // over U (hi + lo), then run a forward substitution over their own 16 rows in
 // registers (lane shuffles), and write their rows of U^T over the V^T tiles.
-// A sequence is processed by one workgroup from start to end (no split over T:
-// a segment's transition is a full D x D matrix, not a diagonal).
+// A sequence is processed by one workgroup from start to end, or split into
+// segments when there are few (batch, kv head) units: a segment maps its
+// start state affinely, S_end = M S_start + N, with M = prod_t (I - beta_t k_t
+// k_t^T) D_t a full D x D matrix.  The same kernel runs each segment from
+// S = I with zero values (M) and from S = 0 (N), without outputs; the start
+// states follow by composing the maps in order (delta_compose_kernel), and
+// every segment then runs again from its start state with outputs.
 //
 // The rescaled keys (per-dim decays, and fp16 inputs with a per-head decay)
 // leave the fp32 range when a cumulative decay inside a chunk is very strong.
@@ -136,20 +141,30 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   const int hp = P == 2 ? (w & 1) : 0, wr = P == 2 ? (w >> 1) : w;
   int l = tid & 63, lr = l & 15, lg = l >> 4;
   // query-head group hg of hs (the group's heads are G of the kv head's G * hs)
+  // and segment s of ns: tokens [t0, t0 + T) of the unit's sequence
   const int hs = a.hsplit > 1 ? a.hsplit : 1;
+  const int ns = a.nseg > 1 ? a.nseg : 1;
   const int hg = blockIdx.x % hs;
-  const int u = blockIdx.x / hs;
-  const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
+  const int us = blockIdx.x / hs;
+  const int u = us / ns, s = us % ns;
+  const int Hq = a.Hq, Hkv = a.Hkv, TT = a.T;
+  const int sl = a.seg_len > 0 ? a.seg_len : TT;  // (a single segment may be shorter than the sequence)
+  const int t0 = s * sl;
+  const int T = min(TT, t0 + sl) - t0;
   const int b = u / Hkv, j = u % Hkv;
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int QS = Hq * D, KS = Hkv * D;
-  const IT* qb = (const IT*)a.q + (int64_t)b * T * QS + (int64_t)(j * G * hs + hg * G) * D;
-  IT* ob = (IT*)a.out + (int64_t)b * T * QS + (int64_t)(j * G * hs + hg * G) * D;
-  const IT* kb = (const IT*)a.k + (int64_t)b * T * KS + (int64_t)j * D;
-  const IT* vb = (const IT*)a.v + (int64_t)b * T * KS + (int64_t)j * D;
-  const IT* gb = DK == 2 ? (const IT*)a.decay + (int64_t)b * T * KS + (int64_t)j * D
-                         : (DK == 1 ? (const IT*)a.decay + (int64_t)b * T * Hkv + j : nullptr);
-  const IT* betab = (const IT*)a.beta + (int64_t)b * T * a.beta_heads + (a.beta_heads > 1 ? j : 0);
+  const int64_t row0 = (int64_t)b * TT + t0;  // the segment's first row
+  const IT* qb = (const IT*)a.q + row0 * QS + (int64_t)(j * G * hs + hg * G) * D;
+  IT* ob = a.out ? (IT*)a.out + row0 * QS + (int64_t)(j * G * hs + hg * G) * D : nullptr;
+  const IT* kb = (const IT*)a.k + row0 * KS + (int64_t)j * D;
+  const IT* vb = a.v ? (const IT*)a.v + row0 * KS + (int64_t)j * D : nullptr;
+  const IT* gb = DK == 2 ? (const IT*)a.decay + row0 * KS + (int64_t)j * D
+                         : (DK == 1 ? (const IT*)a.decay + row0 * Hkv + j : nullptr);
+  const IT* betab = (const IT*)a.beta + row0 * a.beta_heads + (a.beta_heads > 1 ? j : 0);
+  const float* s_in = a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr;
+  float* s_out = (a.s_out && hg == 0 && (a.s_out_all || s == ns - 1)) ? a.s_out + u * a.s_out_u + s * a.s_out_s
+                                                                      : nullptr;
   const float scale = a.scale;
   auto vt_at = [&](int r, int blk) { return r * VT_LD + ((blk ^ vt_swz(r)) * VEC); };
   auto kn_at = [&](int t, int col) {
@@ -188,8 +203,8 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   f32x4_t sacc[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) sacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (a.s_in) {
-    const float* sin = a.s_in + (int64_t)u * D * D;
+  if (s_in) {
+    const float* sin = s_in;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int tau = w * TPW + i;
@@ -299,7 +314,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
       for (int n = 0; n < NTOK; ++n) {
         const int64_t off = (int64_t)min(tb + tg * NTOK + n, T - 1) * KS + cb * VEC;
         pk[n] = ld16(kb + off);
-        pv[n] = ld16(vb + off);
+        pv[n] = vb ? ld16(vb + off) : u32x4_t{0u, 0u, 0u, 0u};
         if constexpr (DK == 2) pg[n] = ld16(gb + off);
       }
     }
@@ -683,8 +698,10 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     s16x4_t th, tl;
     if constexpr (ESZ == 2) split4(t4, th, tl);
 
-    load_q(c, 0);
-    if constexpr (PAIR) load_q(c, 1);
+    if (ob) {
+      load_q(c, 0);
+      if constexpr (PAIR) load_q(c, 1);
+    }
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       if (wr == blk) {
@@ -983,16 +1000,18 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     stage(c);
     prefetch(min(c + 1, nchunks - 1));
     solve(c);
-    if constexpr (PAIR)
-      outputs_pair(c);
-    else
-      outputs(c);
+    if (ob) {
+      if constexpr (PAIR)
+        outputs_pair(c);
+      else
+        outputs(c);
+    }
     update();
     __syncthreads();
     write_sb();
   }
-  if (a.s_out && hg == 0) {
-    float* sout = a.s_out + (int64_t)u * D * D;
+  if (s_out) {
+    float* sout = s_out;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int tau = w * TPW + i;
@@ -1014,8 +1033,8 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
       rp.decay = gb;
       rp.beta = betab;
       rp.out = ob;
-      rp.s_in = a.s_in ? a.s_in + (int64_t)u * D * D : nullptr;
-      rp.s_out = (a.s_out && hg == 0) ? a.s_out + (int64_t)u * D * D : nullptr;
+      rp.s_in = s_in;
+      rp.s_out = s_out;
       rp.qs = QS;
       rp.ks = KS;
       rp.gs = DK == 2 ? KS : Hkv;
@@ -1035,11 +1054,11 @@ template <typename IT, int D, int G, bool FULL>
 static void launch_dg(int dk, const DeltaArgs& a, hipStream_t st) {
   constexpr int NTH = DeltaShape<G>::NTH;
   if (dk == 0)
-    hipLaunchKernelGGL((delta_kernel<IT, D, G, 0>), dim3(a.units * (a.hsplit > 1 ? a.hsplit : 1)), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((delta_kernel<IT, D, G, 0>), dim3(a.units * (a.hsplit > 1 ? a.hsplit : 1) * (a.nseg > 1 ? a.nseg : 1)), dim3(NTH), 0, st, a);
   else if (dk == 1 || !FULL)
-    hipLaunchKernelGGL((delta_kernel<IT, D, G, 1>), dim3(a.units * (a.hsplit > 1 ? a.hsplit : 1)), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((delta_kernel<IT, D, G, 1>), dim3(a.units * (a.hsplit > 1 ? a.hsplit : 1) * (a.nseg > 1 ? a.nseg : 1)), dim3(NTH), 0, st, a);
   else if constexpr (FULL)
-    hipLaunchKernelGGL((delta_kernel<IT, D, G, 2>), dim3(a.units * (a.hsplit > 1 ? a.hsplit : 1)), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((delta_kernel<IT, D, G, 2>), dim3(a.units * (a.hsplit > 1 ? a.hsplit : 1) * (a.nseg > 1 ? a.nseg : 1)), dim3(NTH), 0, st, a);
 }
 
 template <typename IT, int D, bool FULL>
@@ -1066,6 +1085,83 @@ static hipError_t launch_dt(int dk, int D, int G, const DeltaArgs& a, hipStream_
       }
       break;
   }
+  return hipGetLastError();
+}
+
+// start(s + 1) = M_s start(s) + N_s, one workgroup per unit, in order over the
+// segments.  The running state and M_s sit in LDS (fp32); thread (ri, ci)
+// forms the (D/16) x (D/16) block of rows ri * D/16 .., columns ci * D/16 ..
+// of the product.
+constexpr int kComposeThreads = 256;
+template <int D>
+__global__ __launch_bounds__(kComposeThreads) void delta_compose_kernel(const float* __restrict__ M,
+                                                                     const float* __restrict__ N,
+                                                                     const float* __restrict__ past,
+                                                                     float* __restrict__ start, int nseg) {
+  constexpr int E = D * D, RB = D / 16;
+  __shared__ float Sx[E], Mx[E];
+  const int tid = threadIdx.x, u = blockIdx.x;
+  const int ri = tid / 16, ci = tid % 16;
+  const float* pu = past ? past + (int64_t)u * E : nullptr;
+  for (int i = tid; i < E; i += kComposeThreads) Sx[i] = pu ? pu[i] : 0.f;
+  __syncthreads();
+  for (int s = 0; s < nseg; ++s) {
+    float* st = start + ((int64_t)u * nseg + s) * E;
+    for (int i = tid; i < E; i += kComposeThreads) st[i] = Sx[i];
+    if (s == nseg - 1) break;
+    const float* ms = M + ((int64_t)u * (nseg - 1) + s) * E;
+    const float* nsl = N + ((int64_t)u * (nseg - 1) + s) * E;
+    for (int i = tid; i < E; i += kComposeThreads) Mx[i] = ms[i];
+    __syncthreads();
+    float acc[RB][RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int c = 0; c < RB; ++c) acc[r][c] = 0.f;
+    for (int k = 0; k < D; ++k) {
+      float mv[RB], sv[RB];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) mv[r] = Mx[(ri * RB + r) * D + k];
+#pragma unroll
+      for (int c = 0; c < RB; ++c) sv[c] = Sx[k * D + ci * RB + c];
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int c = 0; c < RB; ++c) acc[r][c] = fmaf(mv[r], sv[c], acc[r][c]);
+    }
+    __syncthreads();  // every thread is done reading Sx
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int c = 0; c < RB; ++c) {
+        const int i = (ri * RB + r) * D + ci * RB + c;
+        Sx[i] = acc[r][c] + nsl[i];
+      }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void eye_kernel(float* p, int D) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < D * D) p[i] = (i / D == i % D) ? 1.f : 0.f;
+}
+
+hipError_t launch_delta_compose(const float* M, const float* N, const float* past, float* start, int units,
+                                int nseg, int D, hipStream_t st) {
+  if (units <= 0) return hipSuccess;
+  if (D == 32)
+    hipLaunchKernelGGL(delta_compose_kernel<32>, dim3(units), dim3(kComposeThreads), 0, st, M, N, past, start, nseg);
+  else if (D == 64)
+    hipLaunchKernelGGL(delta_compose_kernel<64>, dim3(units), dim3(kComposeThreads), 0, st, M, N, past, start, nseg);
+  else if (D == 128)
+    hipLaunchKernelGGL(delta_compose_kernel<128>, dim3(units), dim3(kComposeThreads), 0, st, M, N, past, start, nseg);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_eye(float* p, int D, hipStream_t st) {
+  hipLaunchKernelGGL(eye_kernel, dim3((D * D + kThreads - 1) / kThreads), dim3(kThreads), 0, st, p, D);
   return hipGetLastError();
 }
 

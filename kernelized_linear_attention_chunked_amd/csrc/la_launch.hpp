@@ -137,12 +137,30 @@ struct DeltaArgs {
   float* s_out;       // (B*Hkv,D,D)
   int32_t T, Hq, Hkv, units, beta_heads;
   float scale;
-  // query-head groups, as GatedArgs::hsplit (grid = units * hsplit)
+  // query-head groups, as GatedArgs::hsplit (grid = units * nseg * hsplit)
   int32_t hsplit;
+  // Split over T: segment s of nseg (0 or 1: one) covers tokens
+  // [s * seg_len, min((s + 1) * seg_len, T)) (seg_len 0: T; a single segment
+  // may be shorter than the sequence); blockIdx = (u * nseg + s) * hsplit
+  // + group.  The segment starts from s_in + u * s_in_u + s * s_in_s (null:
+  // zeros) and writes its final state to s_out + u * s_out_u + s * s_out_s when
+  // s_out_all, else only the last segment does.  v null: the values are zero;
+  // out null: no outputs.
+  int32_t nseg, seg_len, s_out_all;
+  int64_t s_in_u, s_in_s, s_out_u, s_out_s;
 };
 // decay_kind: 0 none ("delta"), 1 per kv head, 2 per key dim.  fp32 at head
 // size 128 is not available (LDS).
 hipError_t launch_delta(int io, int D, int G, int decay_kind, const DeltaArgs& a, hipStream_t st);
+// Segment start states of a split delta-rule sequence (la_delta.hip): for each
+// of `units` units, start(0) = past (null: zeros) and start(s + 1) = M_s start(s)
+// + N_s, with M_s, N_s, start(s) the D x D slots s of the unit (nseg - 1 of M
+// and N, nseg of start); slot strides D * D, unit strides (nseg - 1) * D * D for
+// M, N and nseg * D * D for start.
+hipError_t launch_delta_compose(const float* M, const float* N, const float* past, float* start, int units,
+                                int nseg, int D, hipStream_t st);
+// The D x D identity.
+hipError_t launch_eye(float* p, int D, hipStream_t st);
 
 // Causal backward (la_backward.hip): buffers are (B,T,H,D) fp32 unless noted.
 struct BwdArgs {

@@ -25,10 +25,10 @@ namespace la {
 struct RecurPtrs {
   const void* q;      // query head 0 of the group at token t: q + t * qs (+ h * D)
   const void* k;      // k + t * ks
-  const void* v;      // v + t * ks
+  const void* v;      // v + t * ks, or null (values zero)
   const void* decay;  // null, or g + t * gs (one value, or D values per token)
   const void* beta;   // delta rule only: beta + t * bs
-  void* out;          // like q
+  void* out;          // like q, or null (no outputs)
   const float* s_in;  // D x D initial state or null (zeros)
   float* s_out;       // D x D final state or null (not written)
   int64_t qs, ks, gs, bs;
@@ -100,7 +100,7 @@ __device__ void token_recurrence(unsigned char* lds, const RecurPtrs& r) {
   auto fetch = [&](int t) {
     if (tid < D) {
       pk = ld(kb + (int64_t)t * r.ks, tid);
-      pv = ld(vb + (int64_t)t * r.ks, tid);
+      pv = vb ? ld(vb + (int64_t)t * r.ks, tid) : 0.f;
       if constexpr (DK == 2) pg = ld(gb + (int64_t)t * r.gs, tid);
     }
     if constexpr (DK == 1) pg = ld(gb + (int64_t)t * r.gs, 0);
@@ -169,8 +169,8 @@ __device__ void token_recurrence(unsigned char* lds, const RecurPtrs& r) {
         for (int c = 0; c < 4; ++c) sv[i][c] = fmaf(kd, uu[4 * c4 + c], sv[i][c]);
       }
     }
-    // o_h = scale q_h^T S'', HP heads per pass
-    for (int h0 = 0; h0 < GW; h0 += HP) {
+    // o_h = scale q_h^T S'', HP heads per pass (none without outputs)
+    for (int h0 = 0; ob && h0 < GW; h0 += HP) {
 #pragma unroll
       for (int h = 0; h < HP && holder; ++h) {
         float acc[4] = {0.f, 0.f, 0.f, 0.f};

@@ -233,7 +233,7 @@ class GatedDeltaD128:
     def step(self):
         _check(self.lib.la_delta_forward(_p(self.q), _p(self.k), _p(self.v), _p(self.g), 0, _p(self.beta),
                                          1, None, _p(self.present), _p(self.out), self.B, self.T, self.Hq,
-                                         self.Hkv, self.D, self.D, 1, self.scale, _stream(self.device)),
+                                         self.Hkv, self.D, self.D, 1, self.scale, None, 0, _stream(self.device)),
                "la_delta_forward")
 
 
@@ -324,7 +324,7 @@ class DeltaStepD128(GatedStepD128):
         _check(self.lib.la_delta_forward(_p(self.q[t]), _p(self.k[t]), _p(self.v[t]), _p(self.g[t]), 0,
                                          _p(self.beta[t]), 1, _p(self.state), _p(self.state),
                                          _p(self.out[t]), self.B, 1, self.Hq, self.Hkv, self.D, self.D,
-                                         1, self.scale, _stream(self.device) if stream is None else stream),
+                                         1, self.scale, None, 0, _stream(self.device) if stream is None else stream),
                "la_delta_forward")
 
 

@@ -56,7 +56,19 @@ hipError_t launch_gated(int, int, int D, int G, const GatedArgs& a, int grid, hi
   return hipSuccess;
 }
 hipError_t launch_delta(int, int D, int G, int dk, const DeltaArgs& a, hipStream_t) {
-  seen(a.units > 0 && D > 0 && (G == 1 || G == 2 || G == 4 || G == 8) && dk >= 0 && dk <= 2, "delta");
+  const int ns = a.nseg > 1 ? a.nseg : 1;
+  seen(a.units > 0 && D > 0 && (G == 1 || G == 2 || G == 4 || G == 8) && dk >= 0 && dk <= 2 && a.T > 0 && a.seg_len > 0 &&
+           (int64_t)(ns - 1) * a.seg_len < a.T && a.s_out && (a.out || a.s_out_all),
+       "delta");
+  return hipSuccess;
+}
+hipError_t launch_delta_compose(const float* M, const float* N, const float*, float* start, int units, int nseg, int D,
+                                hipStream_t) {
+  seen(M && N && start && units > 0 && nseg > 1 && (D == 32 || D == 64 || D == 128), "delta_compose");
+  return hipSuccess;
+}
+hipError_t launch_eye(float* p, int D, hipStream_t) {
+  seen(p && D > 0, "eye");
   return hipSuccess;
 }
 hipError_t launch_bwd_prep(int, const BwdArgs& a, hipStream_t) {
@@ -176,8 +188,10 @@ int main() {
             expect(la_gated_forward(P(G1), P(2 * G1), P(3 * G1), P(4 * G1), pd, nullptr, F(6 * G1), P(7 * G1), 1, T,
                                     Hq, Hkv, D, D, dt, 0.f, P(ws), n, nullptr),
                    LA_OK, "gated");
+            expect(la_delta_workspace_size(1, T, Hq, Hkv, D, D, dt, pd, &n), LA_OK, "delta workspace");
+            const uintptr_t dws = n ? 9 * G1 : 0;
             expect(la_delta_forward(P(G1), P(2 * G1), P(3 * G1), P(4 * G1), pd, P(5 * G1), 1, nullptr, F(6 * G1),
-                                    P(7 * G1), 1, T, Hq, Hkv, D, D, dt, 0.f, nullptr),
+                                    P(7 * G1), 1, T, Hq, Hkv, D, D, dt, 0.f, P(dws), n, nullptr),
                    LA_OK, "delta");
             expect(la_gated_step(P(G1), P(2 * G1), P(3 * G1), P(4 * G1), pd, F(6 * G1), F(6 * G1), P(7 * G1), 3, Hq,
                                  Hkv, D, D, dt, 0.f, nullptr),

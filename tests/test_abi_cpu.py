@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     assert sorted(la.EXPORTED_SYMBOLS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -213,11 +213,11 @@ def test_delta_argument_errors(lib):
     def g(**kw):
         a = dict(q=f(1 << 30), k=f(2 << 30), v=f(3 << 30), d=None, pd=0, beta=f(7 << 30), bph=1,
                  past=None, pres=f(4 << 30), out=f(5 << 30), B=1, T=64, Hq=4, Hkv=2, Dk=64, Dv=64,
-                 dt=1, scale=0.0)
+                 dt=1, scale=0.0, ws=None, wsb=0)
         a.update(kw)
         return lib.la_delta_forward(a["q"], a["k"], a["v"], a["d"], a["pd"], a["beta"], a["bph"],
                                     a["past"], a["pres"], a["out"], a["B"], a["T"], a["Hq"], a["Hkv"],
-                                    a["Dk"], a["Dv"], a["dt"], ctypes.c_float(a["scale"]), None)
+                                    a["Dk"], a["Dv"], a["dt"], ctypes.c_float(a["scale"]), a["ws"], a["wsb"], None)
 
     assert g(Hq=3) == SHAPE
     assert g(dt=4) == DTYPE
@@ -229,7 +229,25 @@ def test_delta_argument_errors(lib):
     assert g(out=f(1 << 30)) == BAD_ARG       # out aliases q
     assert g(beta=f((5 << 30) + 64)) == BAD_ARG  # beta inside out
     assert g(d=f((6 << 30) + 2), pd=1) == BAD_ARG  # per-dim decays are read as 16-byte vectors
+    assert g(ws=f((8 << 30) + 4), wsb=1 << 20) == BAD_ARG  # the workspace is 16-byte aligned
+    assert g(ws=f((5 << 30) + 256), wsb=1 << 20) == BAD_ARG  # and overlaps no argument
     assert g(B=0) == OK
+
+
+def test_delta_split_plan(lib):
+    """Few (batch, kv head) units and a long sequence: the delta rules split over
+    T, and the workspace holds the maps M, N of every segment but the last, the
+    start state of every segment and the identity (D x D fp32 each)."""
+    n = ctypes.c_size_t(0)
+    E = 128 * 128 * 4
+    # B=2, Hkv=8, G=4 (one query-head group per unit): 16 units, 512 chunks -> 16 segments
+    assert lib.la_delta_workspace_size(2, 32768, 32, 8, 128, 128, 1, 0, ctypes.byref(n)) == OK
+    assert n.value == E * (16 * 15 * 2 + 16 * 16 + 1)
+    # enough units already (B=32, Hkv=8), T == 1, or too few chunks per segment: no split
+    for args in ((32, 4096, 32, 8), (2, 1, 32, 8), (2, 200, 32, 8)):
+        assert lib.la_delta_workspace_size(*args, 128, 128, 1, 0, ctypes.byref(n)) == OK and n.value == 0
+    # fp32 at head size 128 with a per-dim decay runs token by token: no split
+    assert lib.la_delta_workspace_size(1, 4096, 8, 1, 128, 128, 0, 1, ctypes.byref(n)) == OK and n.value == 0
 
 
 def test_backward_argument_errors(lib):
