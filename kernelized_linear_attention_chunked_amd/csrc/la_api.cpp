@@ -1024,10 +1024,10 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t H, int64_t D, int64_t esz, bo
 
 // The chunk-parallel backward (16-bit inputs, head sizes 32 or 64): the
 // forward segment states and the reverse gradient sums in slots (split
-// sequences only), dnum and dden per token.
+// sequences only), 1/den and dden per token (with the normaliser).
 struct BwdChunkLayout {
   int64_t nseg, seg_len;
-  size_t fs, fz, rs, rz, dnum, dden, total;
+  size_t fs, fz, rs, rz, rden, dden, total;
 };
 BwdChunkLayout bwd_chunk_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, bool norm) {
   const int64_t U = B * H;
@@ -1047,7 +1047,7 @@ BwdChunkLayout bwd_chunk_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int
   L.fz = take(norm ? slots * Dk * 4 : 0);
   L.rs = take(slots * Dk * Dv * 4);
   L.rz = take(norm ? slots * Dk * 4 : 0);
-  L.dnum = take((size_t)(B * T * H * Dv) * 4);
+  L.rden = take(norm ? (size_t)(B * T * H) * 4 : 0);
   L.dden = take(norm ? (size_t)(B * T * H) * 4 : 0);
   L.total = off;
   return L;
@@ -1158,7 +1158,7 @@ LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, con
     c.v = v;
     c.dy = dout;
     c.mask = mask;
-    c.dnum = F(C.dnum);
+    c.rden = norm ? F(C.rden) : nullptr;
     c.dden = norm ? F(C.dden) : nullptr;
     c.dq = dq;
     c.dk = dk;

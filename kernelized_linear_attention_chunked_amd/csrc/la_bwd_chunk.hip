@@ -19,12 +19,15 @@
 //                   and a prefix over those sums gives each segment its
 //                   forward state at the start;
 //   bwd_fwd_kernel  runs each segment forward in 32-token chunks with S, z in
-//                   registers: dq, dnum and dden per token (dnum, dden to the
-//                   workspace), and the segment's sum of phi_q dnum^T, phi_q dden;
+//                   registers: dq, dnum and dden per token (1/den and dden to
+//                   the workspace), and the segment's sum of phi_q dnum^T,
+//                   phi_q dden;
 //   (a prefix over those sums, in reverse segment order, gives each segment
 //   its dS_next, dz_next at the segment end)
 //   bwd_rev_kernel  runs each segment backwards with dS, dz in registers: dk,
-//                   dv, and dS_0, dz_0 from the first segment.
+//                   dv, and dS_0, dz_0 from the first segment; it forms dnum
+//                   again from dy and 1/den (the same fp32 product), which
+//                   moves 4 bytes per token instead of Dv fp32 values.
 //
 // Precision: the gradients cancel strongly (dden_i removes the dnum-weighted
 // mean of the values from every B_ij, and the state terms carry the same
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
   const IT* vb = (const IT*)a.v + (int64_t)b * T * HDV + (int64_t)h * DV;
   const IT* yb = (const IT*)a.dy + (int64_t)b * T * HDV + (int64_t)h * DV;
   IT* dqb = (IT*)a.dq + (int64_t)b * T * HDK + (int64_t)h * DK;
-  float* dnb = a.dnum + (int64_t)b * T * HDV + (int64_t)h * DV;
+  float* rdb = NORM ? a.rden + (int64_t)b * T * H + h : nullptr;
   float* ddb = NORM ? a.dden + (int64_t)b * T * H + h : nullptr;
   const uint8_t* mb = a.mask ? a.mask + (int64_t)b * T : nullptr;
   const float eps = a.eps;
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
   const rsrc_t rv = make_rsrc(vb + t0 * HDV, (nt - 1) * RV + DV * ESZ);
   const rsrc_t ry = make_rsrc(yb + t0 * HDV, (nt - 1) * RV + DV * ESZ);
   const rsrc_t rdq = make_rsrc(dqb + t0 * HDK, (nt - 1) * RK + DK * ESZ);
-  const rsrc_t rdn = make_rsrc(dnb + t0 * HDV, (nt - 1) * (uint32_t)HDV * 4 + DV * 4);
+  const rsrc_t rrd = make_rsrc(NORM ? rdb + (int64_t)t0 * H : (const float*)qb, NORM ? ((nt - 1) * H + 1) * 4 : 0);
   const rsrc_t rdd = make_rsrc(NORM ? ddb + (int64_t)t0 * H : (const float*)qb, NORM ? ((nt - 1) * H + 1) * 4 : 0);
   const rsrc_t rmk = make_rsrc(mb ? mb + t0 : (const uint8_t*)qb, mb ? nt : 0);  // (no mask: read as 0, ignored)
 
@@ -475,8 +478,9 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
           sm[Ly::DT + Ly::DTL + (DV + et) * LDC + iq] = (uint16_t)pl1;
         }
       }
-      bstore16(rdn, (uint32_t)(cb0 - t0 + iq) * (uint32_t)HDV * 4 + (16 * et + 4 * lg) * 4,
-               __builtin_bit_cast(u32x4_t, dn));
+      if constexpr (NORM)
+        bstore4(rrd, (et == 0 && lg == 0) ? (uint32_t)(cb0 - t0 + iq) * (uint32_t)H * 4 : kDrop,
+                __float_as_uint(qvc ? rden : 0.f));
     }
     __syncthreads();
 
@@ -777,7 +781,8 @@ __global__ __launch_bounds__(kBT, 2) void bwd_rev_kernel(BwdChunkArgs a) {
   const IT* qb = (const IT*)a.q + (int64_t)b * T * HDK + (int64_t)h * DK;
   const IT* kb = (const IT*)a.k + (int64_t)b * T * HDK + (int64_t)h * DK;
   const IT* vb = (const IT*)a.v + (int64_t)b * T * HDV + (int64_t)h * DV;
-  const float* dnb = a.dnum + (int64_t)b * T * HDV + (int64_t)h * DV;
+  const IT* yb = (const IT*)a.dy + (int64_t)b * T * HDV + (int64_t)h * DV;
+  const float* rdb = NORM ? a.rden + (int64_t)b * T * H + h : nullptr;
   const float* ddb = NORM ? a.dden + (int64_t)b * T * H + h : nullptr;
   IT* dkb = (IT*)a.dk + (int64_t)b * T * HDK + (int64_t)h * DK;
   IT* dvb = (IT*)a.dv + (int64_t)b * T * HDV + (int64_t)h * DV;
@@ -818,33 +823,33 @@ __global__ __launch_bounds__(kBT, 2) void bwd_rev_kernel(BwdChunkArgs a) {
     }
   }
 
-  // ---- prefetch registers: q (rows and transposed), k (rows), v (rows), dnum
-  // (rows and transposed, 8 fp32 values of two tokens: 4 loads)
+  // ---- prefetch registers: q (rows and transposed), k (rows), v (rows), dy
+  // (dnum rows and transposed, with 1/den of the item's two tokens)
   const Item it = make_item<NIQ, DK / 8, NIQ, DK / 8, NIV, DV / 8, NIV, DV / 8>(tid);
   // ---- the segment's buffers (token t at byte (t - t0) * row)
   constexpr uint32_t ESZ = sizeof(IT);
   const uint32_t nt = (uint32_t)(t1 - t0);
-  const uint32_t RK = (uint32_t)HDK * ESZ, RV = (uint32_t)HDV * ESZ, RD = (uint32_t)HDV * 4;
+  const uint32_t RK = (uint32_t)HDK * ESZ, RV = (uint32_t)HDV * ESZ;
   const rsrc_t rq = make_rsrc(qb + t0 * HDK, (nt - 1) * RK + DK * ESZ);
   const rsrc_t rk = make_rsrc(kb + t0 * HDK, (nt - 1) * RK + DK * ESZ);
   const rsrc_t rv = make_rsrc(vb + t0 * HDV, (nt - 1) * RV + DV * ESZ);
-  const rsrc_t rdn = make_rsrc(dnb + t0 * HDV, (nt - 1) * RD + DV * 4);
+  const rsrc_t ry = make_rsrc(yb + t0 * HDV, (nt - 1) * RV + DV * ESZ);
+  const rsrc_t rrd = make_rsrc(NORM ? rdb + (int64_t)t0 * H : (const float*)qb, NORM ? ((nt - 1) * H + 1) * 4 : 0);
   const rsrc_t rdd = make_rsrc(NORM ? ddb + (int64_t)t0 * H : (const float*)qb, NORM ? ((nt - 1) * H + 1) * 4 : 0);
   const rsrc_t rdk = make_rsrc(dkb + t0 * HDK, (nt - 1) * RK + DK * ESZ);
   const rsrc_t rdv = make_rsrc(dvb + t0 * HDV, (nt - 1) * RV + DV * ESZ);
   const rsrc_t rmk = make_rsrc(mb ? mb + t0 : (const uint8_t*)qb, mb ? nt : 0);
 
   // ---- prefetch registers (buffer loads, tested where used: see the forward
-  // pass).  The item's rows: a 16-byte block of q, k or v (token 2p: raw0,
-  // token 2p+1: raw2; raw1, raw3 repeat them) or two of dnum (raw0, raw1 and
-  // raw2, raw3).
+  // pass).  The item's rows: a 16-byte block of q, k, v or dy (token 2p: raw0,
+  // token 2p+1: raw2), and for dy the two tokens' 1/den (rd0, rd1).
   const int im = it.on ? it.m : 0;  // (threads without an item read block 0 of q)
   const bool idn = im == 3;
-  const rsrc_t ir = im == 0 ? rq : (im == 1 ? rk : (im == 2 ? rv : rdn));
-  const uint32_t irow = im <= 1 ? RK : (im == 2 ? RV : RD);
-  const uint32_t iblk = idn ? 32 * it.cb : 16 * it.cb;  // byte offset of the block in the row
-  const uint32_t iblk2 = idn ? iblk + 16 : iblk;
-  u32x4_t raw0, raw1, raw2, raw3;
+  const rsrc_t ir = im == 0 ? rq : (im == 1 ? rk : (im == 2 ? rv : ry));
+  const uint32_t irow = im <= 1 ? RK : RV;
+  const uint32_t iblk = 16 * it.cb;  // byte offset of the block in the row
+  u32x4_t raw0, raw2;
+  uint32_t rd0 = 0, rd1 = 0;
   uint32_t rm0 = 1, rm1 = 1;
   float ddn = 0.f;                   // dden of token tid % 32 of the chunk
   const int jq = 16 * (w & 1) + lr;  // key row of the lane in a chunk (phases E, F)
@@ -854,9 +859,11 @@ __global__ __launch_bounds__(kBT, 2) void bwd_rev_kernel(BwdChunkArgs a) {
   auto prefetch_items = [&](int c0) {
     const uint32_t ta = (uint32_t)(c0 - t0 + 2 * it.p);
     raw0 = bload16(ir, ta * irow + iblk);
-    raw1 = bload16(ir, ta * irow + iblk2);
     raw2 = bload16(ir, (ta + 1) * irow + iblk);
-    raw3 = bload16(ir, (ta + 1) * irow + iblk2);
+    if constexpr (NORM) {
+      rd0 = bload4(rrd, idn ? ta * (uint32_t)H * 4 : kDrop);
+      rd1 = bload4(rrd, idn ? (ta + 1) * (uint32_t)H * 4 : kDrop);
+    }
     rm0 = bload1(rmk, ta);
     rm1 = bload1(rmk, ta + 1);
     if constexpr (NORM) ddn = __uint_as_float(bload4(rdd, (uint32_t)(c0 - t0 + (tid & (kBC - 1))) * H * 4));
@@ -888,16 +895,14 @@ __global__ __launch_bounds__(kBT, 2) void bwd_rev_kernel(BwdChunkArgs a) {
       h[1] = ok1 ? raw2 : z4;
     } else {
       float f[2][8];
-      if (!idn) {
-        Io<IT>::unpack(raw0, f[0]);
-        Io<IT>::unpack(raw2, f[1]);
-      } else {
+      Io<IT>::unpack(raw0, f[0]);
+      Io<IT>::unpack(raw2, f[1]);
+      if (NORM && idn) {
+        // dnum = dy / den, the forward pass's product
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f[0][e] = __uint_as_float(raw0[e]);
-          f[0][4 + e] = __uint_as_float(raw1[e]);
-          f[1][e] = __uint_as_float(raw2[e]);
-          f[1][4 + e] = __uint_as_float(raw3[e]);
+        for (int e = 0; e < 8; ++e) {
+          f[0][e] *= __uint_as_float(rd0);
+          f[1][e] *= __uint_as_float(rd1);
         }
       }
       if (im >= 2)

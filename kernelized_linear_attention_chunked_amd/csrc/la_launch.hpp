@@ -202,7 +202,7 @@ struct BwdChunkArgs {
   const void* q;        // (B,T,H,Dk)
   const void* k;        // (B,T,H,Dk)
   const void* v;        // (B,T,H,Dv)
-  const void* dy;       // (B,T,H,Dv), pass 0 only
+  const void* dy;       // (B,T,H,Dv), passes 0 and 1
   const uint8_t* mask;  // (B,T) or null
   // pass 0: forward state at the start of segment s, s_in + u*s_in_u + s*s_in_s
   // ([dk][dv], z [dk]; null = zeros).  pass 1: the gradient sums of the tokens
@@ -215,7 +215,10 @@ struct BwdChunkArgs {
   float* s_out;
   float* z_out;
   int64_t s_out_u, s_out_s, z_out_u, z_out_s;
-  float* dnum;  // (B,T,H,Dv) fp32: written by pass 0, read by pass 1
+  // (B,T,H) fp32 with the normaliser: 1/den_i at valid tokens, 0 elsewhere;
+  // written by pass 0, read by pass 1, which rebuilds dnum_i = dy_i / den_i
+  // (the same fp32 product pass 0 forms)
+  float* rden;
   float* dden;  // (B,T,H) fp32 (with the normaliser)
   void* dq;     // pass 0
   void* dk;     // pass 1
@@ -225,7 +228,7 @@ struct BwdChunkArgs {
   float eps;
 };
 // io: bf16 or fp16; Dk, Dv: 32 or 64 each.  pass 0: forward over each
-// segment (dq, dnum, dden, segment sums); pass 1: reverse (dk, dv, dS_0,
+// segment (dq, 1/den, dden, segment sums); pass 1: reverse (dk, dv, dS_0,
 // dz_0); pass 2: the forward state's sum over segment s = blockIdx % nseg of
 // each unit into slot s + 1 of s_out / z_out (strides s_out_u, s_out_s).
 hipError_t launch_bwd_chunk(int pass, int io, int Dk, int Dv, int norm, const BwdChunkArgs& a, int grid,

@@ -112,9 +112,11 @@ hipError_t launch_gated_pd(int, int, int D, int G, const GatedArgs& a, int grid,
   seen(grid > 0 && D > 0 && G > 0 && a.T > 0, "gated_pd");
   return hipSuccess;
 }
-hipError_t launch_bwd_chunk(int pass, int io, int Dk, int Dv, int, const BwdChunkArgs& a, int grid, hipStream_t) {
+hipError_t launch_bwd_chunk(int pass, int io, int Dk, int Dv, int norm, const BwdChunkArgs& a, int grid,
+                            hipStream_t) {
   seen(grid > 0 && pass >= 0 && pass <= 2 && (io == 1 || io == 2) && (Dk == 32 || Dk == 64) &&
-           (Dv == 32 || Dv == 64) && a.nseg > 0 && a.seg_len % 32 == 0 && a.T > 0 && a.dnum,
+           (Dv == 32 || Dv == 64) && a.nseg > 0 && a.seg_len % 32 == 0 && a.T > 0 && a.dy &&
+           (!norm || (a.rden && a.dden)),
        "bwd_chunk");
   return hipSuccess;
 }
