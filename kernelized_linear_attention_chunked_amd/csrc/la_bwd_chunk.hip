@@ -161,6 +161,15 @@ __device__ __forceinline__ uint32_t tword(const u32x4_t& a, const u32x4_t& b, in
   return __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
 }
 
+// 8 elements p[0], p[ld], ..., p[7 ld] as one MFMA operand (a column of a
+// row-major tile read as a row)
+__device__ __forceinline__ u32x4_t gather8(const uint16_t* p, int ld) {
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (uint32_t)p[2 * i * ld] | ((uint32_t)p[(2 * i + 1) * ld] << 16);
+  return r;
+}
+
 // Staging item of a thread: two consecutive tokens (2p, 2p+1) of one 16-byte
 // column block (8 elements) of input matrix m.  The matrices take consecutive
 // thread ranges of sizes N0, N1, N2, N3 (each a multiple of 64, so that every
@@ -743,7 +752,7 @@ template <int DK, int DV, bool NORM, bool VLO>
 struct RevLds {
   static constexpr int LDK = DK + 8, LDV = DV + 8, LDC = kBC + 8, NZ = NORM ? 16 : 0;
   static constexpr int QRL = kBC * LDK, QTL = DK * LDC, VRL = kBC * LDV, DNL = kBC * LDV, DTL = (DV + NZ) * LDC,
-                       SAL = DV * LDK, SBL = DK * LDV;
+                       SAL = DV * LDK;
   static constexpr int QR = 0;                         // phi(Q) [token][dk]
   static constexpr int QT = QR + 2 * QRL;              // phi(Q)^T [dk][token]
   static constexpr int KR = QT + 2 * QTL;              // phi(K) [token][dk]
@@ -751,12 +760,11 @@ struct RevLds {
   static constexpr int DN = VR + (VLO ? 2 : 1) * VRL;  // dnum [token][dv]
   static constexpr int DT = DN + 2 * DNL;              // dnum^T [dv + 16: dden, zeros][token]
   static constexpr int SA = DT + 2 * DTL;              // dS^T [dv][dk]
-  static constexpr int SB = SA + 2 * SAL;              // dS [dk][dv]
-  static constexpr int TOTAL = SB + 2 * SBL;
+  static constexpr int TOTAL = SA + 2 * SAL;
 };
 
 template <typename IT, int DK, int DV, bool NORM>
-__global__ __launch_bounds__(kBT, 2) void bwd_rev_kernel(BwdChunkArgs a) {
+__global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
   constexpr bool VLO = !std::is_same_v<IT, uint16_t>;
   using Ly = RevLds<DK, DV, NORM, VLO>;
   constexpr int LDK = Ly::LDK, LDV = Ly::LDV, LDC = Ly::LDC;
@@ -946,12 +954,6 @@ __global__ __launch_bounds__(kBT, 2) void bwd_rev_kernel(BwdChunkArgs a) {
         const int off = Ly::SA + (16 * et + lr) * LDK + 16 * dt + 4 * lg;
         *(u32x2_t*)(sm + off) = hw;
         *(u32x2_t*)(sm + off + Ly::SAL) = lw;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int o = Ly::SB + (16 * dt + 4 * lg + q) * LDV + 16 * et + lr;
-          sm[o] = (uint16_t)(q & 1 ? hw[q >> 1] >> 16 : hw[q >> 1] & 0xffffu);
-          sm[o + Ly::SBL] = (uint16_t)(q & 1 ? lw[q >> 1] >> 16 : lw[q >> 1] & 0xffffu);
-        }
       } else if constexpr (NORM) {
         if (lr == 0) {
 #pragma unroll
@@ -1058,8 +1060,9 @@ __global__ __launch_bounds__(kBT, 2) void bwd_rev_kernel(BwdChunkArgs a) {
         mm3(g, ld16(sm + o), ld16(sm + o + Ly::QTL), bh, bl);
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks) {
-          const int so = Ly::SB + (16 * dt + lr) * LDV + 32 * ks + 8 * lg;
-          const u32x4_t sh = ld16(sm + so), sl = ld16(sm + so + Ly::SBL);
+          // dS rows (dv contiguous) gathered from dS^T
+          const int so = Ly::SA + (32 * ks + 8 * lg) * LDK + 16 * dt + lr;
+          const u32x4_t sh = gather8(sm + so, LDK), sl = gather8(sm + so + Ly::SAL, LDK);
           mm(g, sh, vh[ks]);
           mm(g, sl, vh[ks]);
           if constexpr (VLO) mm(g, sh, vl[ks]);
