@@ -196,22 +196,24 @@ template <int DK, int DV, bool NORM, bool VLO>
 struct FwdLds {
   static constexpr int LDK = DK + 8, LDV = DV + 8, LDC = kBC + 8, NZ = NORM ? 16 : 0;
   static constexpr int QRL = kBC * LDK, QTL = DK * LDC, VRL = kBC * LDV, VTL = (DV + NZ) * LDC,
-                       STL = (DV + NZ) * LDK, SRL = DK * LDV, DNL = kBC * LDV, DTL = (DV + NZ) * LDC;
-  static constexpr int QR = 0;                                // phi(Q) [token][dk]
-  static constexpr int QT = QR + 2 * QRL;                     // phi(Q)^T [dk][token]
-  static constexpr int KR = QT + 2 * QTL;                     // phi(K) [token][dk]
-  static constexpr int KT = KR + 2 * QRL;                     // phi(K)^T [dk][token]
+                       STL = (DV + NZ) * LDK, DNL = kBC * LDV, DTL = (DV + NZ) * LDC;
+  static constexpr int QT = 0;                                // phi(Q)^T [dk][token]
+  static constexpr int KT = QT + 2 * QTL;                     // phi(K)^T [dk][token]
   static constexpr int VR = KT + 2 * QTL;                     // V [token][dv]
   static constexpr int VT = VR + (VLO ? 2 : 1) * VRL;         // V^T [dv + 16 ones][token]; lo: dv rows
   static constexpr int ST = VT + VTL + (VLO ? DV * LDC : 0);  // S^T [dv + 16 z][dk]
-  static constexpr int SR = ST + 2 * STL;                     // S [dk][dv]
-  static constexpr int DN = SR + 2 * SRL;                     // dnum [token][dv]
+  // the rows of phi(Q) and phi(K) are last read by the scores, and dnum takes
+  // their place after a barrier
+  static constexpr int U = ST + 2 * STL;
+  static constexpr int QR = U;                                // phi(Q) [token][dk]
+  static constexpr int KR = QR + 2 * QRL;                     // phi(K) [token][dk]
+  static constexpr int DN = U;                                // dnum [token][dv]
   static constexpr int DT = DN + 2 * DNL;                     // dnum^T [dv + 16 dden parts][token]
-  static constexpr int TOTAL = DT + 2 * DTL;
+  static constexpr int TOTAL = U + (4 * QRL > 2 * DNL + 2 * DTL ? 4 * QRL : 2 * DNL + 2 * DTL);
 };
 
 template <typename IT, int DK, int DV, bool NORM>
-__global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
+__global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
   constexpr bool VLO = !std::is_same_v<IT, uint16_t>;  // fp16 values are not exact in bf16
   using Ly = FwdLds<DK, DV, NORM, VLO>;
   constexpr int LDK = Ly::LDK, LDV = Ly::LDV, LDC = Ly::LDC;
@@ -273,14 +275,8 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
     }
   }
   if constexpr (NORM) {
-    // ones rows of V^T; unused dden rows of dnum^T
-    for (int i = tid; i < 16 * LDC; i += kBT) {
-      sm[Ly::VT + DV * LDC + i] = 0x3f80;  // bf16 1.0
-      if (i >= NET * LDC) {
-        sm[Ly::DT + DV * LDC + i] = 0;
-        sm[Ly::DT + Ly::DTL + DV * LDC + i] = 0;
-      }
-    }
+    // ones rows of V^T
+    for (int i = tid; i < 16 * LDC; i += kBT) sm[Ly::VT + DV * LDC + i] = 0x3f80;  // bf16 1.0
   }
 
   // ---- the segment's buffers (token t at byte (t - t0) * row)
@@ -377,14 +373,6 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
       const int off = Ly::ST + (et < NET ? 16 * et + lr : DV + lr) * LDK + 16 * dt + 4 * lg;
       *(u32x2_t*)(sm + off) = hw;
       *(u32x2_t*)(sm + off + Ly::STL) = lw;
-      if (et < NET) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int o = Ly::SR + (16 * dt + 4 * lg + q) * LDV + 16 * et + lr;
-          sm[o] = (uint16_t)(q & 1 ? hw[q >> 1] >> 16 : hw[q >> 1] & 0xffffu);
-          sm[o + Ly::SRL] = (uint16_t)(q & 1 ? lw[q >> 1] >> 16 : lw[q >> 1] & 0xffffu);
-        }
-      }
     }
   };
 
@@ -403,6 +391,10 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
 
     // ---- phase B: num, den of the wave's query block (w & 1) and value tile
     // (w >> 1); dnum, and the wave's part of dden
+    u32x4_t ph, pl;
+    // num^T, den^T tiles: rows 16et + 4lg + q (dv), column iq; their state
+    // terms are formed with the phi(Q) rows before those are overwritten
+    f32x4_t nacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, dacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (w < 2 * NET) {
       const int et = w >> 1;
       u32x4_t qh[KSK], ql[KSK];
@@ -412,7 +404,6 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
         ql[ks] = ld16(sm + Ly::QR + Ly::QRL + iq * LDK + 32 * ks + 8 * lg);
       }
       // scores P_ij = phi_q_i . phi_k_j, j <= i: lane holds keys 8lg..8lg+7 of query iq
-      u32x4_t ph, pl;
       {
         f32x4_t at[2];
 #pragma unroll
@@ -429,31 +420,41 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
         }
         pair_operand(at, ph, pl);
       }
-      // num^T tile: rows 16et + 4lg + q (dv), column iq
-      f32x4_t nacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSK; ++ks) {
+        const int so = Ly::ST + (16 * et + lr) * LDK + 32 * ks + 8 * lg;
+        mm3(nacc, ld16(sm + so), ld16(sm + so + Ly::STL), qh[ks], ql[ks]);
+      }
+      if constexpr (NORM) {
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks) {
+          const int so = Ly::ST + (DV + lr) * LDK + 32 * ks + 8 * lg;
+          mm3(dacc, ld16(sm + so), ld16(sm + so + Ly::STL), qh[ks], ql[ks]);
+        }
+      }
+    }
+    __syncthreads();  // the phi(Q), phi(K) rows are read: dnum goes in their place
+    if constexpr (NORM) {
+      // the unused dden rows of dnum^T (the staging of phi(K) rows wrote there)
+      for (int i = tid; i < (16 - NET) * LDC; i += kBT) {
+        sm[Ly::DT + (DV + NET) * LDC + i] = 0;
+        sm[Ly::DT + Ly::DTL + (DV + NET) * LDC + i] = 0;
+      }
+    }
+    if (w < 2 * NET) {
+      const int et = w >> 1;
       {
         const int o = Ly::VT + (16 * et + lr) * LDC + 8 * lg;
         const u32x4_t vh = ld16(sm + o);
         mm(nacc, vh, ph);
         mm(nacc, vh, pl);
         if constexpr (VLO) mm(nacc, ld16(sm + o + Ly::VTL), ph);
-#pragma unroll
-        for (int ks = 0; ks < KSK; ++ks) {
-          const int so = Ly::ST + (16 * et + lr) * LDK + 32 * ks + 8 * lg;
-          mm3(nacc, ld16(sm + so), ld16(sm + so + Ly::STL), qh[ks], ql[ks]);
-        }
       }
       float rden = 1.f;
       if constexpr (NORM) {
-        f32x4_t dacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
         const u32x4_t vh = ld16(sm + Ly::VT + (DV + lr) * LDC + 8 * lg);
         mm(dacc, vh, ph);
         mm(dacc, vh, pl);
-#pragma unroll
-        for (int ks = 0; ks < KSK; ++ks) {
-          const int so = Ly::ST + (DV + lr) * LDK + 32 * ks + 8 * lg;
-          mm3(dacc, ld16(sm + so), ld16(sm + so + Ly::STL), qh[ks], ql[ks]);
-        }
         rden = 1.f / (dacc[0] + eps);
       }
       f32x4_t dn;
@@ -537,8 +538,9 @@ __global__ __launch_bounds__(kBT, 2) void bwd_fwd_kernel(BwdChunkArgs a) {
         mm3(g, ld16(sm + o), ld16(sm + o + Ly::QTL), bh, bl);
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks) {
-          const int so = Ly::SR + (16 * dt + lr) * LDV + 32 * ks + 8 * lg;
-          mm3(g, ld16(sm + so), ld16(sm + so + Ly::SRL), dh[ks], dl[ks]);
+          // S rows (dv contiguous) gathered from S^T
+          const int so = Ly::ST + (32 * ks + 8 * lg) * LDK + 16 * dt + lr;
+          mm3(g, gather8(sm + so, LDK), gather8(sm + so + Ly::STL, LDK), dh[ks], dl[ks]);
         }
       }
       if constexpr (NORM) {
