@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+  int l = tid & 63, lr = l & 15, lg = l >> 4;  // re-derived per phase (see refresh)
   const int u = blockIdx.x / a.nseg, s = blockIdx.x % a.nseg;
   const int T = a.T, H = a.H;
   const int b = u / H, h = u % H;
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
   const uint32_t irow = im == 2 ? RV : RK;
   u32x4_t raw[2];
   uint32_t rm0 = 1, rm1 = 1;         // mask bytes of the item's tokens
-  const int iq = 16 * (w & 1) + lr;  // query row of the lane in a chunk (phases B, C)
+  int iq = 16 * (w & 1) + lr;  // query row of the lane in a chunk (phases B, C)
   u32x2_t dyraw = u32x2_t{0u, 0u};   // dy of the lane's query at value dims 16(w >> 1) + 4lg .. +3 (phase B)
   u32x2_t qraw = u32x2_t{0u, 0u};    // q of the lane's query at key dims 16(w >> 1) + 4lg .. +3 (phase C)
   uint32_t qm = 1;                   // mask byte of the lane's query
@@ -381,8 +381,17 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
     prefetch_items(t0);
     prefetch_lane(t0);
   }
+  // lane indices re-derived in every phase: the addresses formed from them are
+  // then computed where used instead of hoisted out of the loop and spilled
+  auto refresh = [&]() {
+    l = opaque_lane(tid);
+    lr = l & 15;
+    lg = l >> 4;
+    iq = 16 * (w & 1) + lr;
+  };
   for (int c = 0; c < nch; ++c) {
     const int cb0 = t0 + c * kBC;
+    refresh();
     stage(cb0);
     write_s();
     const bool qvc = cb0 + iq < t1 && (mb == nullptr || qm != 0u);
@@ -391,6 +400,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
 
     // ---- phase B: num, den of the wave's query block (w & 1) and value tile
     // (w >> 1); dnum, and the wave's part of dden
+    refresh();
     u32x4_t ph, pl;
     // num^T, den^T tiles: rows 16et + 4lg + q (dv), column iq; their state
     // terms are formed with the phi(Q) rows before those are overwritten
@@ -434,6 +444,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
       }
     }
     __syncthreads();  // the phi(Q), phi(K) rows are read: dnum goes in their place
+    refresh();
     if constexpr (NORM) {
       // the unused dden rows of dnum^T (the staging of phi(K) rows wrote there)
       for (int i = tid; i < (16 - NET) * LDC; i += kBT) {
@@ -495,6 +506,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
     __syncthreads();
 
     // ---- phase C: dq of the wave's query block (w & 1) and key-dim tile (w >> 1)
+    refresh();
     if (w < 2 * NDT) {
       const int dt = w >> 1;
       const uint32_t tr = (uint32_t)(cb0 - t0 + iq);  // the query's row in the segment
@@ -561,6 +573,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
     if (c + 1 < nch) prefetch_lane(cb0 + kBC);
 
     // ---- phase D: S += phiK^T V (z += phiK^T 1), dS += phiQ^T dnum (dz parts += phiQ^T dden parts)
+    refresh();
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
       int dt, et;
@@ -781,7 +794,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+  int l = tid & 63, lr = l & 15, lg = l >> 4;  // re-derived per phase (see refresh)
   const int u = blockIdx.x / a.nseg, s = blockIdx.x % a.nseg;
   const int T = a.T, H = a.H;
   const int b = u / H, h = u % H;
@@ -862,7 +875,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
   uint32_t rd0 = 0, rd1 = 0;
   uint32_t rm0 = 1, rm1 = 1;
   float ddn = 0.f;                   // dden of token tid % 32 of the chunk
-  const int jq = 16 * (w & 1) + lr;  // key row of the lane in a chunk (phases E, F)
+  int jq = 16 * (w & 1) + lr;  // key row of the lane in a chunk (phases E, F)
   u32x2_t kraw = u32x2_t{0u, 0u};    // k of the lane's key at key dims 16(w >> 1) + 4lg .. +3 (phase F)
   uint32_t km = 1;                   // mask byte of the lane's key
   const uint32_t kcol = (16 * min(w >> 1, NDT - 1) + 4 * lg) * ESZ;
@@ -970,7 +983,14 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
     prefetch_items(t0 + (nch - 1) * kBC);
     prefetch_lane(t0 + (nch - 1) * kBC);
   }
+  auto refresh = [&]() {
+    l = opaque_lane(tid);
+    lr = l & 15;
+    lg = l >> 4;
+    jq = 16 * (w & 1) + lr;
+  };
   for (int c = nch - 1; c >= 0; --c) {
+    refresh();
     const int cb0 = t0 + c * kBC;
     stage(cb0);
     write_ds();
@@ -980,6 +1000,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
     __syncthreads();
 
     // ---- phase E: dv of the wave's key block (w & 1) and value tile (w >> 1)
+    refresh();
     if (w < 2 * NET) {
       const int et = w >> 1;
       u32x4_t kh[KSK], kl[KSK];
@@ -1022,6 +1043,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
     }
 
     // ---- phase F: dk of the wave's key block (w & 1) and key-dim tile (w >> 1)
+    refresh();
     if (w < 2 * NDT) {
       const int dt = w >> 1;
       u32x4_t vh[KSV], vl[VLO ? KSV : 1];
@@ -1086,6 +1108,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
     if (c > 0) prefetch_lane(cb0 - kBC);
 
     // ---- phase G: dS += phiQ^T dnum, dz += phiQ^T dden (column 0 of the dz tile)
+    refresh();
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
       int dt, et;
