@@ -40,23 +40,25 @@ namespace la {
 
 enum ChunkMode { kCausal = 0, kState = 1 };
 
-// Wavefronts per workgroup: 8 at head size 128 (the state and the output
-// accumulators would not fit one 4-wave workgroup's registers without
-// serialising every LDS read), 4 below.
+// Wavefronts per workgroup: 8 at head sizes 64 and 128 (the state and the
+// output accumulators would not fit one 4-wave workgroup's registers without
+// serialising every LDS read; at 64 the halved per-wave tiles let two 8-wave
+// workgroups share a CU), 4 below.
 template <int D>
 struct ChunkWaves {
-  static constexpr int NW = D >= 128 ? 8 : 4;
+  static constexpr int NW = D >= 64 ? 8 : 4;
 };
 
 // LDS layouts: the swizzles of la_device.hpp (vt_swz, kn_swz, sq_swz).
 
 // The second bound is the minimum number of waves per SIMD.  At 8 waves the
-// bf16 state mode asks for 4 (two workgroups per CU, at most 128 registers);
-// the causal mode and the fp32 kernels need more registers.
+// bf16 state mode, and the bf16 causal mode at head size 64, ask for 4 (two
+// workgroups per CU, at most 128 registers); the causal mode at 128 and the
+// fp32 kernels need more registers.
 template <typename DT, int D, int MODE>
 struct ChunkOccupancy {
   static constexpr int NW = ChunkWaves<D>::NW;
-  static constexpr int value = NW == 8 ? ((MODE != kCausal && sizeof(DT) == 2) ? 4 : 1) : 2;
+  static constexpr int value = NW == 8 ? ((sizeof(DT) == 2 && (MODE != kCausal || D == 64)) ? 4 : 1) : 2;
 };
 
 // MASKED: a (B,T) mask is given.  Unmasked launches carry no mask code at all.
@@ -109,10 +111,10 @@ void chunk_kernel(ChunkArgs a) {
   // exact sum of two bf16 values), and each product with V takes one more MFMA
   // with the lo tile, so that V reaches the products unrounded
   constexpr bool VLO = !std::is_same_v<IT, DT>;
-  // lane indices re-derived per chunk where that removes spills (fp32 and
-  // fp16 inputs at head size 128, the bf16 state pass): elsewhere it measured
-  // slower
-  constexpr bool REFRESH = D >= 128 && (ESZ == 4 || VLO || MODE == kState);
+  // lane indices re-derived per chunk where that removes spills (head size 64;
+  // fp32 and fp16 inputs at head size 128, the bf16 state pass): elsewhere it
+  // measured slower
+  constexpr bool REFRESH = D == 64 || (D >= 128 && (ESZ == 4 || VLO || MODE == kState));
   constexpr int VL_BYTES = (USE_KV && VLO) ? NDT * 16 * VT_LD * ESZ : 0;
   constexpr int KT_BYTES = KT ? D * VT_LD * ESZ : 0;
   constexpr int NS = NDT * NVT;                    // 16x16 tiles of the (extended) state

@@ -11,6 +11,8 @@
 // Every factor is exp of a sum of g over a later stretch of tokens, so for
 // g <= 0 it never exceeds 1 (exp(-b_j) alone is never formed).
 //
+// The output scale multiplies exp(b_i) and the exp(b_i - b_j) factors.
+//
 // One workgroup serves one (batch, kv head) unit and a segment of chunks, with
 // all G query heads of the group: 4*P wavefronts, wave w = (head part hp =
 // w/4, row part wr = w%4, reversed for w >= 4); the wave owns query rows
@@ -317,7 +319,8 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
     const float btot = __shfl(bcs, min(kChunk, T - c * kChunk) - 1);
     if constexpr (OUT) {
       const float bi = __shfl(bcs, 16 * wr + lr);
-      const float ebi = __expf(bi);
+      // the output scale rides on both factors, so the outputs take no multiply
+      const float ebi = scale * __expf(bi);
       // A^T tiles of the wave's query block: bf16 uses two per key pair p with
       // permuted rows (element q of tile (p, odd) is key 32p + 8lg + 4odd + q,
       // so that lane group lg holds keys 32p + 8lg + (0..7): one 16-byte V^T
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
       auto fac_of = [&](int t, int q) {
         const int key = key_of(t, q);
         const float bj = __shfl(bcs, key);
-        return key <= 16 * wr + lr ? __expf(bi - bj) : 0.f;
+        return key <= 16 * wr + lr ? scale * __expf(bi - bj) : 0.f;
       };
       float fac[LATE_A ? 1 : NAT][4];
       if constexpr (!LATE_A) {
@@ -441,8 +444,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
             if constexpr (STAGE_IO) {
 #pragma unroll
               for (int ct = 0; ct < NDT; ++ct)
-                store4((IT*)(io + sq_at(lr, 16 * ct + 4 * lg)), scale * n[ct][0], scale * n[ct][1],
-                       scale * n[ct][2], scale * n[ct][3]);
+                store4((IT*)(io + sq_at(lr, 16 * ct + 4 * lg)), n[ct][0], n[ct][1], n[ct][2], n[ct][3]);
 #pragma unroll
               for (int m = 0; m < NQ; ++m) {
                 const int g = 64 * m + l;
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
               IT* orow = ob + (int64_t)tok * QS + (hp + P * h) * D + 4 * lg;
 #pragma unroll
               for (int ct = 0; ct < NDT; ++ct)
-                store4(orow + 16 * ct, scale * n[ct][0], scale * n[ct][1], scale * n[ct][2], scale * n[ct][3]);
+                store4(orow + 16 * ct, n[ct][0], n[ct][1], n[ct][2], n[ct][3]);
             }
           };
           put(hh, n0);
@@ -562,8 +564,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
           // accesses stay in order), then whole rows to memory
 #pragma unroll
           for (int ct = 0; ct < NDT; ++ct)
-            store4((IT*)(io + sq_at(lr, 16 * ct + 4 * lg)), scale * nacc[ct][0], scale * nacc[ct][1],
-                   scale * nacc[ct][2], scale * nacc[ct][3]);
+            store4((IT*)(io + sq_at(lr, 16 * ct + 4 * lg)), nacc[ct][0], nacc[ct][1], nacc[ct][2], nacc[ct][3]);
 #pragma unroll
           for (int m = 0; m < NQ; ++m) {
             const int g = 64 * m + l;
@@ -575,8 +576,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
           IT* orow = ob + (int64_t)tok * QS + (hp + P * hh) * D + 4 * lg;
 #pragma unroll
           for (int ct = 0; ct < NDT; ++ct)
-            store4(orow + 16 * ct, scale * nacc[ct][0], scale * nacc[ct][1], scale * nacc[ct][2],
-                   scale * nacc[ct][3]);
+            store4(orow + 16 * ct, nacc[ct][0], nacc[ct][1], nacc[ct][2], nacc[ct][3]);
         }
       }
       }
