@@ -255,14 +255,19 @@ void chunk_kernel(ChunkArgs a) {
 
   // ---- prefetch registers: thread (cb, tg) loads the 16-byte block cb of
   // NTOK consecutive tokens tg*NTOK + n, for q, k and v alike (full rows per
-  // 16 threads: coalesced).
-  const int cb = tid % CB, tg = tid / CB;
-  const bool loader = LOADERS == NTH || tid < LOADERS;
+  // 16 threads: coalesced).  Where the loaders are half the workgroup and q is
+  // staged (QSPLIT), the other half loads and stages q (into pk), so that
+  // phi(q) and phi(k) are evaluated by different waves.
+  constexpr bool QSPLIT = USE_Q && QS_STAGE && 2 * LOADERS == NTH;
+  const bool qload = QSPLIT && tid >= LOADERS;  // (wave-uniform: LOADERS is a multiple of 64)
+  const int lt = qload ? tid - LOADERS : tid;
+  const int cb = lt % CB, tg = lt / CB;
+  const bool loader = LOADERS == NTH || tid < LOADERS || QSPLIT;
   // the loader's 16-byte block lies inside the q/k rows (kin) and v rows (vin)
   const bool kin = !PAD || cb * VEC < DKr, vin = !PAD || cb * VEC < DVr;
   const u32x4_t zero4 = u32x4_t{0u, 0u, 0u, 0u};
   u32x4_t pk[USE_KV ? NTOK : 1], pv[USE_KV ? NTOK : 1];
-  u32x4_t pq[USE_Q ? (QS_STAGE ? NTOK : NQ) : 1];
+  u32x4_t pq[USE_Q ? (QS_STAGE ? (QSPLIT ? 1 : NTOK) : NQ) : 1];
   u32x4_t qreg[(USE_Q && !QS_STAGE) ? NQ : 1];
   uint32_t valid = 0;   // bit n: token tg*NTOK + n exists and is not masked
   bool qrow_ok = false; // (unstaged q) this lane's own query row exists and is not masked
@@ -298,6 +303,20 @@ void chunk_kernel(ChunkArgs a) {
                                                             : zero4;
     }
     if (!loader) return;
+    if constexpr (QSPLIT) {
+      if (qload) {
+        // the q half: the same tokens' q blocks, into pk
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n) {
+          const int tok = tb + tg * NTOK + n;
+          const bool in = pfull || tok < T;
+          pk[n] = (kin && in) ? ld16(qb + (int64_t)tok * HDK + cb * VEC) : zero4;
+          const uint32_t ok = pfull ? 1u : (in ? (mb ? (mb[tok] != 0) : 1u) : 0u);
+          valid |= ok << n;
+        }
+        return;
+      }
+    }
     if (pfull) {
       // whole chunk, every token valid: no per-token guards
       valid = (1u << NTOK) - 1u;
@@ -309,7 +328,7 @@ void chunk_kernel(ChunkArgs a) {
           pk[n] = kin ? ld16(kb + offk) : zero4;
           pv[n] = vin ? ld16(vb + offv) : zero4;
         }
-        if constexpr (USE_Q && QS_STAGE) pq[n] = kin ? ld16(qb + offk) : zero4;
+        if constexpr (USE_Q && QS_STAGE && !QSPLIT) pq[n] = kin ? ld16(qb + offk) : zero4;
       }
       return;
     }
@@ -322,7 +341,7 @@ void chunk_kernel(ChunkArgs a) {
           pk[n] = kin ? ld16(kb + offk) : zero4;
           pv[n] = vin ? ld16(vb + offv) : zero4;
         }
-        if constexpr (USE_Q && QS_STAGE) pq[n] = kin ? ld16(qb + offk) : zero4;
+        if constexpr (USE_Q && QS_STAGE && !QSPLIT) pq[n] = kin ? ld16(qb + offk) : zero4;
         const uint32_t ok = mb ? (mb[tok] != 0) : 1u;
         valid |= ok << n;
       } else {
@@ -330,7 +349,7 @@ void chunk_kernel(ChunkArgs a) {
           pk[n] = u32x4_t{0u, 0u, 0u, 0u};
           pv[n] = u32x4_t{0u, 0u, 0u, 0u};
         }
-        if constexpr (USE_Q && QS_STAGE) pq[n] = u32x4_t{0u, 0u, 0u, 0u};
+        if constexpr (USE_Q && QS_STAGE && !QSPLIT) pq[n] = u32x4_t{0u, 0u, 0u, 0u};
       }
     }
   };
@@ -395,6 +414,16 @@ void chunk_kernel(ChunkArgs a) {
         qreg[m] = (!PAD || KB * m + VEC * lg < DKr) ? phi_vec(pq[m], qrow_ok, full) : zero4;
     }
     if (!loader) return;
+    if constexpr (QSPLIT) {
+      if (qload) {
+#pragma unroll
+        for (int n = 0; n < NTOK; ++n) {
+          const bool ok = FULL || ((valid >> n) & 1u);
+          st16(Qs + sq_at(tg * NTOK + n, cb * VEC), kin ? phi_vec(pk[n], ok, full) : zero4);
+        }
+        return;
+      }
+    }
     u32x4_t pkt[KT ? NTOK : 1];
 #pragma unroll
     for (int n = 0; n < NTOK; ++n) {
@@ -406,7 +435,7 @@ void chunk_kernel(ChunkArgs a) {
         if constexpr (KT) pkt[n] = fk;
         if (!ok) pv[n] = u32x4_t{0u, 0u, 0u, 0u};
       }
-      if constexpr (USE_Q && QS_STAGE) st16(Qs + sq_at(t, cb * VEC), kin ? phi_vec(pq[n], ok, full) : zero4);
+      if constexpr (USE_Q && QS_STAGE && !QSPLIT) st16(Qs + sq_at(t, cb * VEC), kin ? phi_vec(pq[n], ok, full) : zero4);
     }
     if constexpr (USE_KV) {
       if constexpr (VLO) {
