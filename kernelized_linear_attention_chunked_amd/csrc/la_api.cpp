@@ -1151,6 +1151,7 @@ LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, con
     // reverse pass
     const BwdChunkLayout C = bwd_chunk_layout(B, T, H, Dk, Dv, norm);
     const int64_t nseg = C.nseg, ZE = Dk;
+    const bool fold = nseg <= la::kBwdFold;
     la::BwdChunkArgs c;
     memset(&c, 0, sizeof(c));
     c.q = q;
@@ -1180,12 +1181,16 @@ LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, con
       ps.z_out_u = nseg * ZE;
       ps.z_out_s = ZE;
       e = la::launch_bwd_chunk(2, dtype, (int)Dk, (int)Dv, norm, ps, (int)(U * (nseg - 1)), st);
-      if (e == hipSuccess)
+      // up to kBwdFold segments the passes add the slots themselves
+      if (e == hipSuccess && !fold)
         e = la::launch_seg_prefix(F(C.fs), norm ? F(C.fz) : nullptr, state_in_kv, state_in_k, (int)U, (int)nseg,
                                   (int)Dk, (int)Dv, norm, st);
       if (e != hipSuccess) return device_status(e, "la_backward");
     }
     la::BwdChunkArgs c0 = c;
+    c0.fold = fold ? 1 : 0;
+    c0.s_init = state_in_kv;
+    c0.z_init = norm ? state_in_k : nullptr;
     if (nseg > 1) {
       c0.s_in = F(C.fs);
       c0.z_in = norm ? F(C.fz) : nullptr;
@@ -1199,18 +1204,16 @@ LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, con
       c0.s_out_s = Dk * Dv;
       c0.z_out_u = nseg * ZE;
       c0.z_out_s = ZE;
-    } else {
-      c0.s_in = state_in_kv;
-      c0.z_in = state_in_k;
-      c0.s_in_u = Dk * Dv;
-      c0.z_in_u = ZE;
     }
     e = la::launch_bwd_chunk(0, dtype, (int)Dk, (int)Dv, norm, c0, (int)(U * nseg), st);
-    if (e == hipSuccess && nseg > 1)
+    if (e == hipSuccess && nseg > 1 && !fold)
       e = la::launch_seg_prefix(F(C.rs), norm ? F(C.rz) : nullptr, dstate_out_kv, dstate_out_k, (int)U, (int)nseg,
                                 (int)Dk, (int)Dv, norm, st);
     if (e != hipSuccess) return device_status(e, "la_backward");
     la::BwdChunkArgs c1 = c;
+    c1.fold = fold ? 1 : 0;
+    c1.s_init = dstate_out_kv;
+    c1.z_init = norm ? dstate_out_k : nullptr;
     if (nseg > 1) {
       c1.s_in = F(C.rs);
       c1.z_in = norm ? F(C.rz) : nullptr;
@@ -1218,11 +1221,6 @@ LA_EXPORT la_status la_backward(const void* q, const void* k, const void* v, con
       c1.s_in_s = Dk * Dv;
       c1.z_in_u = nseg * ZE;
       c1.z_in_s = ZE;
-    } else {
-      c1.s_in = dstate_out_kv;
-      c1.z_in = dstate_out_k;
-      c1.s_in_u = Dk * Dv;
-      c1.z_in_u = ZE;
     }
     c1.s_out = dstate_in_kv;
     c1.z_out = dstate_in_k;

@@ -190,6 +190,47 @@ __device__ __forceinline__ Item make_item(int tid) {
   return on ? Item{m, r / bl, r % bl, true} : Item{m, 0, 0, false};
 }
 
+// The state a pass starts a segment from (element [d][col] of S, or of z with
+// col < 0): slot `slot` of the prefixed slots, or with a.fold the initial
+// state plus the unprefixed slots 1 .. R in slot order (the prefix pass's sum,
+// with every slot's loads issued before the adds).
+template <int DK, int DV, bool NORM>
+struct StartState {
+  const float *s0, *z0, *sl, *zl;
+  int64_t ss, zs;
+  int R;
+  __device__ StartState(const BwdChunkArgs& a, int u, int slot, int R_) {
+    if (a.fold) {
+      s0 = a.s_init ? a.s_init + (int64_t)u * DK * DV : nullptr;
+      z0 = (NORM && a.z_init) ? a.z_init + (int64_t)u * DK : nullptr;
+      sl = a.s_in ? a.s_in + u * a.s_in_u : nullptr;
+      zl = (NORM && a.z_in) ? a.z_in + u * a.z_in_u : nullptr;
+      R = sl ? R_ : 0;
+    } else {
+      s0 = a.s_in ? a.s_in + u * a.s_in_u + slot * a.s_in_s : nullptr;
+      z0 = (NORM && a.z_in) ? a.z_in + u * a.z_in_u + slot * a.z_in_s : nullptr;
+      sl = zl = nullptr;
+      R = 0;
+    }
+    ss = a.s_in_s;
+    zs = a.z_in_s;
+  }
+  __device__ float at(int d, int col) const {
+    const float* b = col >= 0 ? s0 : z0;
+    const float* l = col >= 0 ? sl : zl;
+    const int64_t o = col >= 0 ? (int64_t)d * DV + col : d;
+    const int64_t st = col >= 0 ? ss : zs;
+    float y[kBwdFold - 1];
+#pragma unroll
+    for (int r = 1; r < kBwdFold; ++r) y[r - 1] = r <= R ? l[r * st + o] : 0.f;
+    float x = b ? b[o] : 0.f;
+#pragma unroll
+    for (int r = 1; r < kBwdFold; ++r)
+      if (r <= R) x += y[r - 1];
+    return x;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Forward pass of the backward: LDS layout in 16-bit elements.
 template <int DK, int DV, bool NORM, bool VLO>
@@ -258,8 +299,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
     return tau < NST;
   };
   {
-    const float* sin = a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr;
-    const float* zin = (NORM && a.z_in) ? a.z_in + u * a.z_in_u + s * a.z_in_s : nullptr;
+    StartState<DK, DV, NORM> ss(a, u, s, s);
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
       int dt, et;
@@ -267,9 +307,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int d = 16 * dt + 4 * lg + q;
-        float x = 0.f;
-        if (on) x = et < NET ? (sin ? sin[d * DV + 16 * et + lr] : 0.f) : (zin ? zin[d] : 0.f);
-        st[k][q] = x;
+        st[k][q] = on ? ss.at(d, et < NET ? 16 * et + lr : -1) : 0.f;
         ds[k][q] = 0.f;
       }
     }
@@ -823,9 +861,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
     return tau < NST;
   };
   {
-    const int r = a.nseg - 1 - s;
-    const float* sin = a.s_in ? a.s_in + u * a.s_in_u + r * a.s_in_s : nullptr;
-    const float* zin = (NORM && a.z_in) ? a.z_in + u * a.z_in_u + r * a.z_in_s : nullptr;
+    StartState<DK, DV, NORM> ss(a, u, a.nseg - 1 - s, a.nseg - 1 - s);
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
       int dt, et;
@@ -833,9 +869,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int d = 16 * dt + 4 * lg + q;
-        float x = 0.f;
-        if (on) x = et < NET ? (sin ? sin[d * DV + 16 * et + lr] : 0.f) : ((zin && lr == 0) ? zin[d] : 0.f);
-        ds[k][q] = x;
+        ds[k][q] = (on && (et < NET || lr == 0)) ? ss.at(d, et < NET ? 16 * et + lr : -1) : 0.f;
       }
     }
   }

@@ -206,10 +206,16 @@ struct BwdChunkArgs {
   const uint8_t* mask;  // (B,T) or null
   // pass 0: forward state at the start of segment s, s_in + u*s_in_u + s*s_in_s
   // ([dk][dv], z [dk]; null = zeros).  pass 1: the gradient sums of the tokens
-  // after segment s, at slot nseg - 1 - s (null = zeros)
+  // after segment s, at slot nseg - 1 - s (null = zeros).  With fold set the
+  // slots are not prefixed: the state is s_init + u*Dk*Dv (z_init + u*Dk; null
+  // = zeros) plus slots 1 .. R of s_in (R = s in pass 0, nseg - 1 - s in pass
+  // 1, at most kBwdFold - 1), added in slot order
   const float* s_in;
   const float* z_in;
   int64_t s_in_u, s_in_s, z_in_u, z_in_s;
+  const float* s_init;
+  const float* z_init;
+  int32_t fold;
   // pass 0: segment s >= 1 writes its sum of phi_q dnum^T (phi_q dden) to slot
   // nseg - s; pass 1: segment 0 writes dS_0, dz_0 at s_out + u*s_out_u
   float* s_out;
@@ -231,6 +237,9 @@ struct BwdChunkArgs {
 // segment (dq, 1/den, dden, segment sums); pass 1: reverse (dk, dv, dS_0,
 // dz_0); pass 2: the forward state's sum over segment s = blockIdx % nseg of
 // each unit into slot s + 1 of s_out / z_out (strides s_out_u, s_out_s).
+// segment counts up to which the chunk backward forms its segment states itself
+// (fold) instead of a prefix pass over the slots
+constexpr int kBwdFold = 8;
 hipError_t launch_bwd_chunk(int pass, int io, int Dk, int Dv, int norm, const BwdChunkArgs& a, int grid,
                             hipStream_t st);
 

@@ -116,7 +116,7 @@ hipError_t launch_bwd_chunk(int pass, int io, int Dk, int Dv, int norm, const Bw
                             hipStream_t) {
   seen(grid > 0 && pass >= 0 && pass <= 2 && (io == 1 || io == 2) && (Dk == 32 || Dk == 64) &&
            (Dv == 32 || Dv == 64) && a.nseg > 0 && a.seg_len % 32 == 0 && a.T > 0 && a.dy &&
-           (!norm || (a.rden && a.dden)),
+           (!norm || (a.rden && a.dden)) && (pass == 2 || !a.fold || a.nseg <= kBwdFold),
        "bwd_chunk");
   return hipSuccess;
 }

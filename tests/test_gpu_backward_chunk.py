@@ -129,3 +129,15 @@ def test_backward_every_head_size_pair():
             q, k, v, dy = _inputs(1, 70, 1, Dk, Dv, torch.bfloat16, 9500 + Dk + Dv)
             got = la.la_backward(q, k, v, dy)
             _check(got, q, k, v, dy)
+
+
+@pytest.mark.parametrize("T", [64, 128, 320, 512, 576, 1536], ids=lambda t: "T%d" % t)
+def test_backward_segment_counts(T):
+    """One unit: 1, 2, 5, 8, 9 and 24 segments of 64 tokens.  Up to 8 the
+    passes add the unprefixed segment sums themselves; beyond, a prefix pass
+    runs over them.  Initial state and final-state gradient included."""
+    B, H, D = 1, 1, 64
+    q, k, v, dy = _inputs(B, T, H, D, D, torch.bfloat16, 9600 + T)
+    S0, Z0, gS, gZ = _states(B, H, D, D, 9600 + T)
+    got = la.la_backward(q, k, v, dy, state=(S0, Z0), dstate=(gS, gZ))
+    _check(got, q, k, v, dy, None, (S0, Z0), (gS, gZ))
