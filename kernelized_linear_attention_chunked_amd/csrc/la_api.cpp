@@ -373,11 +373,18 @@ la_status forward_impl(const void* q, const void* k, const void* v, const uint8_
     ps.seg_chunks = (int32_t)p.seg_chunks;
     ps.nseg_total = (int32_t)p.nseg;
     e = la::launch_chunk(la::kModeState, dtype, Di, feature_map, norm, ps, (int)(U * (p.nseg - 1)), st);
-    if (e == hipSuccess)
+    // up to kChunkFold segments the causal pass adds the slots itself
+    const bool fold = p.nseg <= la::kChunkFold && Di <= 64;
+    if (e == hipSuccess && !fold)
       e = la::launch_seg_prefix(ws_s, ws_z, state_in_kv, state_in_k, (int)U, (int)p.nseg, (int)Dk, (int)Dv, norm,
                                 st);
     if (e == hipSuccess) {
       la::ChunkArgs pc = a;
+      pc.fold = fold ? 1 : 0;
+      pc.s_init = state_in_kv;
+      pc.z_init = state_in_k;
+      pc.s_init_u = SE;
+      pc.z_init_u = ZE;
       pc.s_in = ws_s;
       pc.z_in = ws_z;
       pc.s_in_u = p.nseg * SE;

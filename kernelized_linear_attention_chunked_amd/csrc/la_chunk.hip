@@ -203,8 +203,20 @@ void chunk_kernel(ChunkArgs a) {
 #pragma unroll
   for (int k = 0; k < NST; ++k) sacc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if constexpr (MODE == kCausal) {
-    const float* sin = a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr;
-    const float* zin = a.z_in ? a.z_in + u * a.z_in_u + s * a.z_in_s : nullptr;
+    // (head size 128 keeps the prefix pass: its registers have no room for the
+    // batched slot loads)
+    constexpr bool FOLD = D <= 64;
+    // the segment's start state: its prefixed slot, or (fold) the initial
+    // state plus the unprefixed slots 1 .. s in slot order, every slot's loads
+    // issued before the adds
+    const bool fold = FOLD && a.fold != 0;
+    const float* sin = fold ? (a.s_init ? a.s_init + u * a.s_init_u : nullptr)
+                            : (a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr);
+    const float* zin = fold ? (a.z_init ? a.z_init + u * a.z_init_u : nullptr)
+                            : (a.z_in ? a.z_in + u * a.z_in_u + s * a.z_in_s : nullptr);
+    const float* sl = (fold && a.s_in) ? a.s_in + u * a.s_in_u : nullptr;
+    const float* zl = (fold && a.z_in) ? a.z_in + u * a.z_in_u : nullptr;
+    const int R = sl ? s : 0;
 #pragma unroll
     for (int k = 0; k < NST; ++k) {
       int rt, ct;
@@ -212,12 +224,19 @@ void chunk_kernel(ChunkArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int dk = 16 * rt + 4 * lg + q;
-          float val = 0.f;
-          if (ct < NDT) {
-            if (sin && dk < DKr && 16 * ct + lr < DVr) val = sin[dk * DVr + 16 * ct + lr];
-          } else {
-            if (zin && dk < DKr) val = zin[dk];
-          }
+          const bool sv = ct < NDT && dk < DKr && 16 * ct + lr < DVr, zv = ct >= NDT && dk < DKr;
+          const int64_t o = ct < NDT ? (int64_t)dk * DVr + 16 * ct + lr : dk;
+          const float* b = ct < NDT ? sin : zin;
+          const float* lb = ct < NDT ? sl : zl;
+          const int64_t ls = ct < NDT ? a.s_in_s : a.z_in_s;
+          constexpr int NF = FOLD ? kChunkFold - 1 : 1;
+          float y[NF];
+#pragma unroll
+          for (int r = 1; r <= NF; ++r) y[r - 1] = (r <= R && lb && (sv || zv)) ? lb[r * ls + o] : 0.f;
+          float val = ((sv || zv) && b) ? b[o] : 0.f;
+#pragma unroll
+          for (int r = 1; r <= NF; ++r)
+            if (r <= R) val += y[r - 1];
           sacc[k][q] = val;
         }
       }

@@ -16,10 +16,17 @@ struct ChunkArgs {
   const void* v;
   const uint8_t* mask;  // (B,T) or null
   void* out;
-  // initial state of the segment (null = zeros): s_in + u*s_in_u + s*s_in_s
+  // initial state of the segment (null = zeros): s_in + u*s_in_u + s*s_in_s.
+  // With fold (causal mode) s_in holds the unprefixed segment sums in slots
+  // 1 .. nseg-1, and segment s starts from s_init + u*s_init_u (z_init + u*z_init_u;
+  // null = zeros) plus slots 1 .. s, added in slot order (s < kChunkFold)
   const float* s_in;
   const float* z_in;
   int64_t s_in_u, s_in_s, z_in_u, z_in_s;
+  const float* s_init;
+  const float* z_init;
+  int64_t s_init_u, z_init_u;
+  int32_t fold;
   // state written at the end (causal: by the last segment only; state mode:
   // slot s + out_slot_off of unit u)
   float* s_out;
@@ -45,6 +52,9 @@ enum { kModeCausal = 0, kModeState = 1 };
 // I/O element type codes of the launchers (the values of la_dtype)
 enum { kIoF32 = 0, kIoBF16 = 1, kIoF16 = 2 };
 
+// segment counts up to which the causal pass at head sizes up to 64 forms its
+// segment states itself (fold) instead of a prefix pass over the slots
+constexpr int kChunkFold = 8;
 hipError_t launch_chunk(int mode, int io, int D, int fm, int norm, const ChunkArgs& a, int grid,
                         hipStream_t st);
 // slots of dk x dv (+ dk with the normaliser) floats
