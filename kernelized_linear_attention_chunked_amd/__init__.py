@@ -148,10 +148,6 @@ def _need_cuda(*ts):
             raise ValueError("all tensors must be on one device (%s and %s)" % (dev, t.device))
 
 
-def _contig(t):
-    return None if t is None else t.contiguous()
-
-
 def _input(t, name, device, dtype=None, shape=None):
     """A read-only argument: checked, then made contiguous.  The caller keeps
     the returned tensor in a local until the library call has been made, so a
