@@ -660,10 +660,12 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
 // Segment sums of the forward state, sum phi_k v^T (and sum phi_k), in the
 // same hi + lo precision: the state at a segment start enters the gradients
 // through the same cancelling terms.  Workgroup blockIdx sums segment
-// s = blockIdx % nseg of unit blockIdx / nseg into slot s + 1.
+// s = blockIdx % nseg of unit blockIdx / nseg into slot s + 1, in 64-token
+// chunks (twice the forward passes' 32: half the chain of loads and barriers).
+constexpr int kSC = 64;
 template <int DK, int DV, bool NORM, bool VLO>
 struct StateLds {
-  static constexpr int LDC = kBC + 8, NZ = NORM ? 16 : 0;
+  static constexpr int LDC = kSC + 8, NZ = NORM ? 16 : 0;
   static constexpr int KTL = DK * LDC, VTL = (DV + NZ) * LDC;
   static constexpr int KT = 0;              // phi(K)^T [dk][token], hi then lo
   static constexpr int VT = KT + 2 * KTL;   // V^T [dv + 16 ones][token]; lo: dv rows
@@ -678,7 +680,8 @@ __global__ __launch_bounds__(kBT, 2) void bwd_state_kernel(BwdChunkArgs a) {
   constexpr int NET = DV / 16, NDT = DK / 16, NZT = NORM ? 1 : 0;
   constexpr int NST = NDT * (NET + NZT);
   constexpr int TPW = (NST + kBW - 1) / kBW;
-  constexpr int NIK = (kBC / 2) * (DK / 8), NIV = (kBC / 2) * (DV / 8);
+  constexpr int NIK = (kSC / 2) * (DK / 8), NIV = (kSC / 2) * (DV / 8);
+  static_assert(NIK + NIV <= kBT && NIK % 64 == 0 && NIV % 64 == 0, "one staging item per thread");
   __shared__ __align__(16) uint16_t sm[Ly::TOTAL];
 
   const int tid = threadIdx.x;
@@ -760,23 +763,26 @@ __global__ __launch_bounds__(kBT, 2) void bwd_state_kernel(BwdChunkArgs a) {
     }
   };
 
-  const int nch = (t1 - t0 + kBC - 1) / kBC;
+  const int nch = (t1 - t0 + kSC - 1) / kSC;
   if (nch > 0) prefetch(t0);
   for (int c = 0; c < nch; ++c) {
-    stage(t0 + c * kBC);
-    if (c + 1 < nch) prefetch(t0 + (c + 1) * kBC);
+    stage(t0 + c * kSC);
+    if (c + 1 < nch) prefetch(t0 + (c + 1) * kSC);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
       int dt, et;
       if (!tile(k, dt, et)) continue;
-      const int ao = Ly::KT + (16 * dt + lr) * LDC + 8 * lg;
-      const int bo = Ly::VT + (et < NET ? 16 * et + lr : DV + lr) * LDC + 8 * lg;
-      const u32x4_t kh = ld16(sm + ao), kl = ld16(sm + ao + Ly::KTL), vh = ld16(sm + bo);
-      mm(st[k], kh, vh);
-      mm(st[k], kl, vh);
-      if constexpr (VLO) {
-        if (et < NET) mm(st[k], kh, ld16(sm + bo + Ly::VTL));
+#pragma unroll
+      for (int ks = 0; ks < kSC / 32; ++ks) {
+        const int ao = Ly::KT + (16 * dt + lr) * LDC + 32 * ks + 8 * lg;
+        const int bo = Ly::VT + (et < NET ? 16 * et + lr : DV + lr) * LDC + 32 * ks + 8 * lg;
+        const u32x4_t kh = ld16(sm + ao), kl = ld16(sm + ao + Ly::KTL), vh = ld16(sm + bo);
+        mm(st[k], kh, vh);
+        mm(st[k], kl, vh);
+        if constexpr (VLO) {
+          if (et < NET) mm(st[k], kh, ld16(sm + bo + Ly::VTL));
+        }
       }
     }
     __syncthreads();
