@@ -39,7 +39,8 @@
 //
 // Layout (8 wavefronts, one workgroup per (unit, segment)): every matrix a
 // product contracts over sits in LDS with its contraction index contiguous,
-// row-major with 16 bytes of row padding, hi part then lo part.  A product
+// hi part then lo part, in unpadded rows whose 16-byte blocks are XOR-swizzled
+// by a function of the row (ro, to below).  A product
 // C += A B^T takes A's rows from one matrix and B's from another (see
 // la_device.hpp for the MFMA lane layout).  The intra-chunk scores feed the
 // next product straight from registers: a pair of score tiles whose A rows are
@@ -161,12 +162,47 @@ __device__ __forceinline__ uint32_t tword(const u32x4_t& a, const u32x4_t& b, in
   return __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
 }
 
-// 8 elements p[0], p[ld], ..., p[7 ld] as one MFMA operand (a column of a
-// row-major tile read as a row)
-__device__ __forceinline__ u32x4_t gather8(const uint16_t* p, int ld) {
+// LDS tiles.  Row tiles hold N = 32 or 64 elements per row (a token's q, k, v
+// or dnum, or a row of S^T or dS^T); token tiles hold the 32 tokens of a chunk
+// per row (phi(Q)^T, phi(K)^T, V^T, dnum^T).  Rows are unpadded and their
+// 16-byte blocks are XORed by a function of the row, chosen with a model of
+// the gfx950 LDS (64 banks of 4 bytes; a 16-byte read serves lanes 0-7 with
+// 24-31, 8-23, 32-39 with 56-63 and 40-55 in one cycle each, other accesses 32
+// lanes at a time) so that the operand reads, both the row reads (row = lane
+// % 16) and the permuted score rows 8(r/4) + 4 odd + r%4, are conflict-free;
+// padding rows by one block made every one of them two-way.
+template <int NB>
+__device__ __forceinline__ int rsw(int r) {
+  if constexpr (NB == 8)
+    return ((r >> 1) & 7) ^ (((r >> 4) & 1) << 1);
+  else
+    return (r >> 2) & 3;
+}
+__device__ __forceinline__ int tsw(int r) { return ((((r >> 2) ^ (r >> 4)) & 1) << 1) ^ ((r >> 5) & 1); }
+// element offset of (row r, column c) in a row tile of N elements per row
+template <int N>
+__device__ __forceinline__ int ro(int r, int c) {
+  constexpr int NB = N / 8;
+  return r * N + ((((c >> 3) ^ rsw<NB>(r)) & (NB - 1)) << 3) + (c & 7);
+}
+// element offset of (row r, token t) in a token tile
+__device__ __forceinline__ int to(int r, int t) { return r * kBC + ((((t >> 3) ^ tsw(r)) & 3) << 3) + (t & 7); }
+// column c of rows r0 .. r0+7 (r0 a multiple of 8) of a row tile as one MFMA
+// operand (the tile read transposed): within the 8 rows the swizzle changes by
+// a constant per row
+template <int N>
+__device__ __forceinline__ u32x4_t gather8(const uint16_t* tile, int r0, int c) {
+  constexpr int NB = N / 8;
+  const int s0 = rsw<NB>(r0), cb = c >> 3, ce = c & 7;
   u32x4_t r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (uint32_t)p[2 * i * ld] | ((uint32_t)p[(2 * i + 1) * ld] << 16);
+  for (int i = 0; i < 4; ++i) {
+    const int e0 = 2 * i, e1 = 2 * i + 1;
+    const int d0 = NB == 8 ? (e0 >> 1) : (e0 >> 2), d1 = NB == 8 ? (e1 >> 1) : (e1 >> 2);
+    const uint32_t x0 = tile[(r0 + e0) * N + (((cb ^ s0 ^ d0) & (NB - 1)) << 3) + ce];
+    const uint32_t x1 = tile[(r0 + e1) * N + (((cb ^ s0 ^ d1) & (NB - 1)) << 3) + ce];
+    r[i] = x0 | (x1 << 16);
+  }
   return r;
 }
 
@@ -235,7 +271,7 @@ struct StartState {
 // Forward pass of the backward: LDS layout in 16-bit elements.
 template <int DK, int DV, bool NORM, bool VLO>
 struct FwdLds {
-  static constexpr int LDK = DK + 8, LDV = DV + 8, LDC = kBC + 8, NZ = NORM ? 16 : 0;
+  static constexpr int LDK = DK, LDV = DV, LDC = kBC, NZ = NORM ? 16 : 0;
   static constexpr int QRL = kBC * LDK, QTL = DK * LDC, VRL = kBC * LDV, VTL = (DV + NZ) * LDC,
                        STL = (DV + NZ) * LDK, DNL = kBC * LDV, DTL = (DV + NZ) * LDC;
   static constexpr int QT = 0;                                // phi(Q)^T [dk][token]
@@ -381,7 +417,6 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
       else
         split_rows<kReluEps, true>(f, ok0, ok1, eps, h, lo);
     }
-    const int rld = im == 2 ? LDV : LDK;
     const int rbase = im == 0 ? Ly::QR : (im == 1 ? Ly::KR : Ly::VR);
     const int rlo = im == 2 ? Ly::VRL : Ly::QRL;
     const int tbase = im == 0 ? Ly::QT : (im == 1 ? Ly::KT : Ly::VT);
@@ -389,13 +424,13 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
     const bool lo_too = im < 2 || VLO;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      const int off = rbase + (2 * it.p + n) * rld + 8 * it.cb;
+      const int off = rbase + (im == 2 ? ro<DV>(2 * it.p + n, 8 * it.cb) : ro<DK>(2 * it.p + n, 8 * it.cb));
       st16(sm + off, h[n]);
       if (lo_too) st16(sm + off + rlo, lo[n]);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int off = tbase + (8 * it.cb + e) * LDC + 2 * it.p;
+      const int off = tbase + to(8 * it.cb + e, 2 * it.p);
       *(uint32_t*)(sm + off) = tword(h[0], h[1], e);
       if (lo_too) *(uint32_t*)(sm + off + tlo) = tword(lo[0], lo[1], e);
     }
@@ -408,7 +443,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
       u32x2_t hw, lw;
       { const u32x2_t t2_ = split2(st[k][0], st[k][1]); hw[0] = t2_[0]; lw[0] = t2_[1]; }
       { const u32x2_t t2_ = split2(st[k][2], st[k][3]); hw[1] = t2_[0]; lw[1] = t2_[1]; }
-      const int off = Ly::ST + (et < NET ? 16 * et + lr : DV + lr) * LDK + 16 * dt + 4 * lg;
+      const int off = Ly::ST + ro<DK>(et < NET ? 16 * et + lr : DV + lr, 16 * dt + 4 * lg);
       *(u32x2_t*)(sm + off) = hw;
       *(u32x2_t*)(sm + off + Ly::STL) = lw;
     }
@@ -448,8 +483,8 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
       u32x4_t qh[KSK], ql[KSK];
 #pragma unroll
       for (int ks = 0; ks < KSK; ++ks) {
-        qh[ks] = ld16(sm + Ly::QR + iq * LDK + 32 * ks + 8 * lg);
-        ql[ks] = ld16(sm + Ly::QR + Ly::QRL + iq * LDK + 32 * ks + 8 * lg);
+        qh[ks] = ld16(sm + Ly::QR + ro<DK>(iq, 32 * ks + 8 * lg));
+        ql[ks] = ld16(sm + Ly::QR + Ly::QRL + ro<DK>(iq, 32 * ks + 8 * lg));
       }
       // scores P_ij = phi_q_i . phi_k_j, j <= i: lane holds keys 8lg..8lg+7 of query iq
       {
@@ -460,7 +495,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
           at[odd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KSK; ++ks) {
-            const int o = Ly::KR + krow * LDK + 32 * ks + 8 * lg;
+            const int o = Ly::KR + ro<DK>(krow, 32 * ks + 8 * lg);
             mm3(at[odd], ld16(sm + o), ld16(sm + o + Ly::QRL), qh[ks], ql[ks]);
           }
 #pragma unroll
@@ -470,13 +505,13 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
       }
 #pragma unroll
       for (int ks = 0; ks < KSK; ++ks) {
-        const int so = Ly::ST + (16 * et + lr) * LDK + 32 * ks + 8 * lg;
+        const int so = Ly::ST + ro<DK>(16 * et + lr, 32 * ks + 8 * lg);
         mm3(nacc, ld16(sm + so), ld16(sm + so + Ly::STL), qh[ks], ql[ks]);
       }
       if constexpr (NORM) {
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks) {
-          const int so = Ly::ST + (DV + lr) * LDK + 32 * ks + 8 * lg;
+          const int so = Ly::ST + ro<DK>(DV + lr, 32 * ks + 8 * lg);
           mm3(dacc, ld16(sm + so), ld16(sm + so + Ly::STL), qh[ks], ql[ks]);
         }
       }
@@ -493,7 +528,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
     if (w < 2 * NET) {
       const int et = w >> 1;
       {
-        const int o = Ly::VT + (16 * et + lr) * LDC + 8 * lg;
+        const int o = Ly::VT + to(16 * et + lr, 8 * lg);
         const u32x4_t vh = ld16(sm + o);
         mm(nacc, vh, ph);
         mm(nacc, vh, pl);
@@ -501,7 +536,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
       }
       float rden = 1.f;
       if constexpr (NORM) {
-        const u32x4_t vh = ld16(sm + Ly::VT + (DV + lr) * LDC + 8 * lg);
+        const u32x4_t vh = ld16(sm + Ly::VT + to(DV + lr, 8 * lg));
         mm(dacc, vh, ph);
         mm(dacc, vh, pl);
         rden = 1.f / (dacc[0] + eps);
@@ -514,13 +549,13 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
       { const u32x2_t t2_ = split2(dn[0], dn[1]); hw[0] = t2_[0]; lw[0] = t2_[1]; }
       { const u32x2_t t2_ = split2(dn[2], dn[3]); hw[1] = t2_[0]; lw[1] = t2_[1]; }
       {
-        const int o = Ly::DN + iq * LDV + 16 * et + 4 * lg;
+        const int o = Ly::DN + ro<DV>(iq, 16 * et + 4 * lg);
         *(u32x2_t*)(sm + o) = hw;
         *(u32x2_t*)(sm + o + Ly::DNL) = lw;
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int o = Ly::DT + (16 * et + 4 * lg + q) * LDC + iq;
+        const int o = Ly::DT + to(16 * et + 4 * lg + q, iq);
         sm[o] = (uint16_t)(q & 1 ? hw[q >> 1] >> 16 : hw[q >> 1] & 0xffffu);
         sm[o + Ly::DTL] = (uint16_t)(q & 1 ? lw[q >> 1] >> 16 : lw[q >> 1] & 0xffffu);
       }
@@ -533,8 +568,8 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
           part[et * kBC + iq] = pd;
           uint32_t ph1, pl1;
           split1(pd, ph1, pl1);
-          sm[Ly::DT + (DV + et) * LDC + iq] = (uint16_t)ph1;
-          sm[Ly::DT + Ly::DTL + (DV + et) * LDC + iq] = (uint16_t)pl1;
+          sm[Ly::DT + to(DV + et, iq)] = (uint16_t)ph1;
+          sm[Ly::DT + Ly::DTL + to(DV + et, iq)] = (uint16_t)pl1;
         }
       }
       if constexpr (NORM)
@@ -557,8 +592,8 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
       u32x4_t dh[KSV], dl[KSV];
 #pragma unroll
       for (int ks = 0; ks < KSV; ++ks) {
-        dh[ks] = ld16(sm + Ly::DN + iq * LDV + 32 * ks + 8 * lg);
-        dl[ks] = ld16(sm + Ly::DN + Ly::DNL + iq * LDV + 32 * ks + 8 * lg);
+        dh[ks] = ld16(sm + Ly::DN + ro<DV>(iq, 32 * ks + 8 * lg));
+        dl[ks] = ld16(sm + Ly::DN + Ly::DNL + ro<DV>(iq, 32 * ks + 8 * lg));
       }
       // B_ij = dnum_i . v_j + dden_i, j <= i: keys 8lg..8lg+7 of query iq
       u32x4_t bh, bl;
@@ -570,7 +605,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
           at[odd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KSV; ++ks) {
-            const int o = Ly::VR + krow * LDV + 32 * ks + 8 * lg;
+            const int o = Ly::VR + ro<DV>(krow, 32 * ks + 8 * lg);
             const u32x4_t vh = ld16(sm + o);
             mm(at[odd], vh, dh[ks]);
             mm(at[odd], vh, dl[ks]);
@@ -584,17 +619,17 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
       // dphi_q^T tile: rows 16dt + 4lg + q (dk), column iq
       f32x4_t g = f32x4_t{0.f, 0.f, 0.f, 0.f};
       {
-        const int o = Ly::KT + (16 * dt + lr) * LDC + 8 * lg;
+        const int o = Ly::KT + to(16 * dt + lr, 8 * lg);
         mm3(g, ld16(sm + o), ld16(sm + o + Ly::QTL), bh, bl);
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks) {
           // S rows (dv contiguous) gathered from S^T
-          const int so = Ly::ST + (32 * ks + 8 * lg) * LDK + 16 * dt + lr;
-          mm3(g, gather8(sm + so, LDK), gather8(sm + so + Ly::STL, LDK), dh[ks], dl[ks]);
+          mm3(g, gather8<DK>(sm + Ly::ST, 32 * ks + 8 * lg, 16 * dt + lr),
+              gather8<DK>(sm + Ly::ST + Ly::STL, 32 * ks + 8 * lg, 16 * dt + lr), dh[ks], dl[ks]);
         }
       }
       if constexpr (NORM) {
-        const int zo = Ly::ST + DV * LDK + 16 * dt + 4 * lg;
+        const int zo = Ly::ST + ro<DK>(DV, 16 * dt + 4 * lg);
         const u32x2_t zh = *(const u32x2_t*)(sm + zo), zl = *(const u32x2_t*)(sm + zo + Ly::STL);
 #pragma unroll
         for (int q = 0; q < 4; ++q) g[q] += (bf_at(zh[q >> 1], q & 1) + bf_at(zl[q >> 1], q & 1)) * dd;
@@ -616,8 +651,8 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
     for (int k = 0; k < TPW; ++k) {
       int dt, et;
       if (!tile(k, dt, et)) continue;
-      const int ao = (16 * dt + lr) * LDC + 8 * lg;
-      const int bo = (et < NET ? 16 * et + lr : DV + lr) * LDC + 8 * lg;
+      const int ao = to(16 * dt + lr, 8 * lg);
+      const int bo = to(et < NET ? 16 * et + lr : DV + lr, 8 * lg);
       const u32x4_t kh = ld16(sm + Ly::KT + ao), kl = ld16(sm + Ly::KT + Ly::QTL + ao);
       const u32x4_t vh = ld16(sm + Ly::VT + bo);
       mm(st[k], kh, vh);
@@ -809,7 +844,7 @@ __global__ __launch_bounds__(kBT, 2) void bwd_state_kernel(BwdChunkArgs a) {
 // Reverse pass: LDS layout in 16-bit elements.
 template <int DK, int DV, bool NORM, bool VLO>
 struct RevLds {
-  static constexpr int LDK = DK + 8, LDV = DV + 8, LDC = kBC + 8, NZ = NORM ? 16 : 0;
+  static constexpr int LDK = DK, LDV = DV, LDC = kBC, NZ = NORM ? 16 : 0;
   static constexpr int QRL = kBC * LDK, QTL = DK * LDC, VRL = kBC * LDV, DNL = kBC * LDV, DTL = (DV + NZ) * LDC,
                        SAL = DV * LDK;
   static constexpr int QR = 0;                         // phi(Q) [token][dk]
@@ -944,8 +979,8 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
         ddv[tid] = dd;
         uint32_t hh, ll;
         split1(dd, hh, ll);
-        sm[Ly::DT + DV * LDC + tid] = (uint16_t)hh;
-        sm[Ly::DT + Ly::DTL + DV * LDC + tid] = (uint16_t)ll;
+        sm[Ly::DT + to(DV, tid)] = (uint16_t)hh;
+        sm[Ly::DT + Ly::DTL + to(DV, tid)] = (uint16_t)ll;
       }
     }
     if (!it.on) return;
@@ -975,13 +1010,12 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
       else
         split_rows<kReluEps, true>(f, ok0, ok1, eps, h, lo);
     }
-    const int rld = im >= 2 ? LDV : LDK;
     const int rbase = im == 0 ? Ly::QR : (im == 1 ? Ly::KR : (im == 2 ? Ly::VR : Ly::DN));
     const int rlo = im == 3 ? Ly::DNL : (im == 2 ? Ly::VRL : Ly::QRL);
     const bool lo_too = im != 2 || VLO;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      const int off = rbase + (2 * it.p + n) * rld + 8 * it.cb;
+      const int off = rbase + (im >= 2 ? ro<DV>(2 * it.p + n, 8 * it.cb) : ro<DK>(2 * it.p + n, 8 * it.cb));
       st16(sm + off, h[n]);
       if (lo_too) st16(sm + off + rlo, lo[n]);
     }
@@ -991,7 +1025,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
       const int tlo = im == 0 ? Ly::QTL : Ly::DTL;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int off = tbase + (8 * it.cb + e) * LDC + 2 * it.p;
+        const int off = tbase + to(8 * it.cb + e, 2 * it.p);
         *(uint32_t*)(sm + off) = tword(h[0], h[1], e);
         *(uint32_t*)(sm + off + tlo) = tword(lo[0], lo[1], e);
       }
@@ -1006,7 +1040,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
         u32x2_t hw, lw;
         { const u32x2_t t2_ = split2(ds[k][0], ds[k][1]); hw[0] = t2_[0]; lw[0] = t2_[1]; }
         { const u32x2_t t2_ = split2(ds[k][2], ds[k][3]); hw[1] = t2_[0]; lw[1] = t2_[1]; }
-        const int off = Ly::SA + (16 * et + lr) * LDK + 16 * dt + 4 * lg;
+        const int off = Ly::SA + ro<DK>(16 * et + lr, 16 * dt + 4 * lg);
         *(u32x2_t*)(sm + off) = hw;
         *(u32x2_t*)(sm + off + Ly::SAL) = lw;
       } else if constexpr (NORM) {
@@ -1046,8 +1080,8 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
       u32x4_t kh[KSK], kl[KSK];
 #pragma unroll
       for (int ks = 0; ks < KSK; ++ks) {
-        kh[ks] = ld16(sm + Ly::KR + jq * LDK + 32 * ks + 8 * lg);
-        kl[ks] = ld16(sm + Ly::KR + Ly::QRL + jq * LDK + 32 * ks + 8 * lg);
+        kh[ks] = ld16(sm + Ly::KR + ro<DK>(jq, 32 * ks + 8 * lg));
+        kl[ks] = ld16(sm + Ly::KR + Ly::QRL + ro<DK>(jq, 32 * ks + 8 * lg));
       }
       // P_ij, i >= j: lane holds queries 8lg..8lg+7 of key jq
       u32x4_t ph, pl;
@@ -1059,7 +1093,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
           at[odd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KSK; ++ks) {
-            const int o = Ly::QR + qrow * LDK + 32 * ks + 8 * lg;
+            const int o = Ly::QR + ro<DK>(qrow, 32 * ks + 8 * lg);
             mm3(at[odd], ld16(sm + o), ld16(sm + o + Ly::QRL), kh[ks], kl[ks]);
           }
 #pragma unroll
@@ -1070,11 +1104,11 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
       // dv^T tile: rows 16et + 4lg + q (dv), column jq
       f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
       {
-        const int o = Ly::DT + (16 * et + lr) * LDC + 8 * lg;
+        const int o = Ly::DT + to(16 * et + lr, 8 * lg);
         mm3(acc, ld16(sm + o), ld16(sm + o + Ly::DTL), ph, pl);
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks) {
-          const int so = Ly::SA + (16 * et + lr) * LDK + 32 * ks + 8 * lg;
+          const int so = Ly::SA + ro<DK>(16 * et + lr, 32 * ks + 8 * lg);
           mm3(acc, ld16(sm + so), ld16(sm + so + Ly::SAL), kh[ks], kl[ks]);
         }
       }
@@ -1089,8 +1123,8 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
       u32x4_t vh[KSV], vl[VLO ? KSV : 1];
 #pragma unroll
       for (int ks = 0; ks < KSV; ++ks) {
-        vh[ks] = ld16(sm + Ly::VR + jq * LDV + 32 * ks + 8 * lg);
-        if constexpr (VLO) vl[ks] = ld16(sm + Ly::VR + Ly::VRL + jq * LDV + 32 * ks + 8 * lg);
+        vh[ks] = ld16(sm + Ly::VR + ro<DV>(jq, 32 * ks + 8 * lg));
+        if constexpr (VLO) vl[ks] = ld16(sm + Ly::VR + Ly::VRL + ro<DV>(jq, 32 * ks + 8 * lg));
       }
       // B_ij = dnum_i . v_j + dden_i, i >= j: queries 8lg..8lg+7 of key jq
       u32x4_t bh, bl;
@@ -1102,7 +1136,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
           at[odd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KSV; ++ks) {
-            const int o = Ly::DN + qrow * LDV + 32 * ks + 8 * lg;
+            const int o = Ly::DN + ro<DV>(qrow, 32 * ks + 8 * lg);
             const u32x4_t dh = ld16(sm + o), dl = ld16(sm + o + Ly::DNL);
             mm(at[odd], dh, vh[ks]);
             mm(at[odd], dl, vh[ks]);
@@ -1120,13 +1154,13 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
       // dphi_k^T tile: rows 16dt + 4lg + q (dk), column jq
       f32x4_t g = f32x4_t{0.f, 0.f, 0.f, 0.f};
       {
-        const int o = Ly::QT + (16 * dt + lr) * LDC + 8 * lg;
+        const int o = Ly::QT + to(16 * dt + lr, 8 * lg);
         mm3(g, ld16(sm + o), ld16(sm + o + Ly::QTL), bh, bl);
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks) {
           // dS rows (dv contiguous) gathered from dS^T
-          const int so = Ly::SA + (32 * ks + 8 * lg) * LDK + 16 * dt + lr;
-          const u32x4_t sh = gather8(sm + so, LDK), sl = gather8(sm + so + Ly::SAL, LDK);
+          const u32x4_t sh = gather8<DK>(sm + Ly::SA, 32 * ks + 8 * lg, 16 * dt + lr),
+                        sl = gather8<DK>(sm + Ly::SA + Ly::SAL, 32 * ks + 8 * lg, 16 * dt + lr);
           mm(g, sh, vh[ks]);
           mm(g, sl, vh[ks]);
           if constexpr (VLO) mm(g, sh, vl[ks]);
@@ -1153,8 +1187,8 @@ __global__ __launch_bounds__(kBT, 4) void bwd_rev_kernel(BwdChunkArgs a) {
     for (int k = 0; k < TPW; ++k) {
       int dt, et;
       if (!tile(k, dt, et)) continue;
-      const int ao = (16 * dt + lr) * LDC + 8 * lg;
-      const int bo = (et < NET ? 16 * et + lr : DV + lr) * LDC + 8 * lg;
+      const int ao = to(16 * dt + lr, 8 * lg);
+      const int bo = to(et < NET ? 16 * et + lr : DV + lr, 8 * lg);
       mm3(ds[k], ld16(sm + Ly::QT + ao), ld16(sm + Ly::QT + Ly::QTL + ao), ld16(sm + Ly::DT + bo),
           ld16(sm + Ly::DT + Ly::DTL + bo));
     }
