@@ -700,7 +700,7 @@ __global__ __launch_bounds__(kBT, 4) void bwd_fwd_kernel(BwdChunkArgs a) {
 constexpr int kSC = 64;
 template <int DK, int DV, bool NORM, bool VLO>
 struct StateLds {
-  static constexpr int LDC = kSC + 8, NZ = NORM ? 16 : 0;
+  static constexpr int LDC = kSC, NZ = NORM ? 16 : 0;  // rows of kSC tokens, swizzled as row tiles
   static constexpr int KTL = DK * LDC, VTL = (DV + NZ) * LDC;
   static constexpr int KT = 0;              // phi(K)^T [dk][token], hi then lo
   static constexpr int VT = KT + 2 * KTL;   // V^T [dv + 16 ones][token]; lo: dv rows
@@ -792,7 +792,7 @@ __global__ __launch_bounds__(kBT, 2) void bwd_state_kernel(BwdChunkArgs a) {
     const bool lo_too = im == 0 || VLO;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int off = tbase + (8 * it.cb + e) * LDC + 2 * it.p;
+      const int off = tbase + ro<kSC>(8 * it.cb + e, 2 * it.p);
       *(uint32_t*)(sm + off) = tword(h[0], h[1], e);
       if (lo_too) *(uint32_t*)(sm + off + tlo) = tword(lo[0], lo[1], e);
     }
@@ -810,8 +810,8 @@ __global__ __launch_bounds__(kBT, 2) void bwd_state_kernel(BwdChunkArgs a) {
       if (!tile(k, dt, et)) continue;
 #pragma unroll
       for (int ks = 0; ks < kSC / 32; ++ks) {
-        const int ao = Ly::KT + (16 * dt + lr) * LDC + 32 * ks + 8 * lg;
-        const int bo = Ly::VT + (et < NET ? 16 * et + lr : DV + lr) * LDC + 32 * ks + 8 * lg;
+        const int ao = Ly::KT + ro<kSC>(16 * dt + lr, 32 * ks + 8 * lg);
+        const int bo = Ly::VT + ro<kSC>(et < NET ? 16 * et + lr : DV + lr, 32 * ks + 8 * lg);
         const u32x4_t kh = ld16(sm + ao), kl = ld16(sm + ao + Ly::KTL), vh = ld16(sm + bo);
         mm(st[k], kh, vh);
         mm(st[k], kl, vh);
