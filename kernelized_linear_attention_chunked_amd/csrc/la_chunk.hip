@@ -40,6 +40,26 @@ namespace la {
 
 enum ChunkMode { kCausal = 0, kState = 1 };
 
+// Block swizzles of the unpadded 16-bit phi(K) rows (ksw) and phi(Q) / S^T rows
+// (qsw), CB 16-byte blocks per row.  Chosen by a search over XOR functions of
+// the row bits against a model of the gfx950 LDS banks, for the permuted-row
+// and column reads of phi(K), the row reads and 8-byte writes of S^T and
+// phi(Q), and the staging writes; the padded rows they replace had measured
+// bank-conflict stalls on the S^T and phi(K) operand reads (about 7 and 4% of
+// the causal prefill's cycles).
+template <int CB>
+__device__ __forceinline__ int ksw(int t) {
+  if constexpr (CB == 16) return (t & 3) | (((t >> 3) & 3) << 2);
+  else if constexpr (CB == 8) return ((t >> 1) & 1) | (((t >> 3) & 3) << 1);
+  else return (t >> 3) & 3;
+}
+template <int CB>
+__device__ __forceinline__ int qsw(int r) {
+  if constexpr (CB == 16) return r & 15;
+  else if constexpr (CB == 8) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
+
 // Wavefronts per workgroup: 8 at head sizes 64 and 128 (the state and the
 // output accumulators would not fit one 4-wave workgroup's registers without
 // serialising every LDS read; at 64 the halved per-wave tiles let two 8-wave
@@ -86,7 +106,11 @@ void chunk_kernel(ChunkArgs a) {
   constexpr int NTOK = kChunk * CB / LOADERS;
   constexpr int NQ = D / KB;                       // operand vectors per q row per lane
   constexpr int NKS = kChunk / KB;                 // vector-steps over the chunk's tokens
-  constexpr int PADE = 16 / ESZ;                   // 16 bytes of padding per row
+  // 16-bit operands: unpadded phi(K), phi(Q) and S^T rows whose 16-byte
+  // blocks are XORed by a function of the row (ksw, qsw); fp32: 16 bytes of
+  // padding per row and the shared swizzles of la_device.hpp
+  constexpr bool SWZ = ESZ == 2;
+  constexpr int PADE = SWZ ? 0 : 16 / ESZ;
   constexpr int KN_LD = D + PADE;                  // phi(K), phi(Q) rows
   constexpr int VT_LD = kChunk;                    // V^T rows (swizzled, unpadded)
   constexpr int SB_LD = D + PADE;
@@ -172,11 +196,13 @@ void chunk_kernel(ChunkArgs a) {
   // one pass) and the column-wise reads of the state update (rows 8 apart)
   // spread over the banks
   auto kn_at = [&](int t, int col) {
-    return t * KN_LD + (((col / VEC) ^ (kn_swz(t) & (CB - 1))) * VEC) + (col % VEC);
+    const int sw = SWZ ? ksw<CB>(t) : (kn_swz(t) & (CB - 1));
+    return t * KN_LD + ((((col / VEC) ^ sw) & (CB - 1)) * VEC) + (col % VEC);
   };
   // element offset of element `col` of row r of phi(Q) or S^T
   auto sq_at = [&](int r, int col) {
-    return r * SB_LD + (((col / VEC) ^ sq_swz(r)) * VEC) + (col % VEC);
+    const int sw = SWZ ? qsw<CB>(r) : sq_swz(r);
+    return r * SB_LD + ((((col / VEC) ^ sw) & (CB - 1)) * VEC) + (col % VEC);
   };
 
   // ---- running state.  With FUSE, wave (qr, hv) owns state rows
