@@ -88,6 +88,26 @@ __device__ __forceinline__ int vt_swz(int r) { return ((r >> 1) & 7) ^ ((r >> 4)
 __device__ __forceinline__ int kn_swz(int t) { return (4 * ((t >> 3) & 1)) ^ (5 * ((t >> 4) & 1)); }
 __device__ __forceinline__ int sq_swz(int r) { return (r >> 3) & 1; }
 
+// Block swizzles of the unpadded 16-bit phi(K) rows (ksw) and phi(Q) / S^T rows
+// (qsw), CB 16-byte blocks per row.  Chosen by a search over XOR functions of
+// the row bits against a model of the gfx950 LDS banks, for the permuted-row
+// and column reads of phi(K), the row reads and 8-byte writes of S^T and
+// phi(Q), and the staging writes; the padded rows they replace had measured
+// bank-conflict stalls on the S^T and phi(K) operand reads (about 7 and 4% of
+// the causal prefill's cycles).
+template <int CB>
+__device__ __forceinline__ int ksw(int t) {
+  if constexpr (CB == 16) return (t & 3) | (((t >> 3) & 3) << 2);
+  else if constexpr (CB == 8) return ((t >> 1) & 1) | (((t >> 3) & 3) << 1);
+  else return (t >> 3) & 3;
+}
+template <int CB>
+__device__ __forceinline__ int qsw(int r) {
+  if constexpr (CB == 16) return r & 15;
+  else if constexpr (CB == 8) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
+
 // ---------------------------------------------------------------------------
 // Operand traits.  A "vector" is 16 bytes of one row in memory: 8 bf16 or 4
 // fp32 values.  One vector-step contracts KB = 4 * VEC indices: lane group lg
