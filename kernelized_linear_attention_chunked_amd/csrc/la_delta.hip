@@ -74,7 +74,9 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   constexpr int TW = (64 / CB) * NTOK;  // tokens of one loader wave
   constexpr int NQ = D / KB;
   constexpr int NKS = kChunk / KB;
-  constexpr int PADE = 16 / ESZ;
+  // 16-bit operands: unpadded rows with the swizzles ksw / qsw (la_device.hpp)
+  constexpr bool SWZ = ESZ == 2;
+  constexpr int PADE = SWZ ? 0 : 16 / ESZ;
   constexpr int KN_LD = D + PADE;
   constexpr int VT_LD = kChunk;
   constexpr int SB_LD = D + PADE;
@@ -168,10 +170,12 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   const float scale = a.scale;
   auto vt_at = [&](int r, int blk) { return r * VT_LD + ((blk ^ vt_swz(r)) * VEC); };
   auto kn_at = [&](int t, int col) {
-    return t * KN_LD + (((col / VEC) ^ (kn_swz(t) & (CB - 1))) * VEC) + (col % VEC);
+    const int sw = SWZ ? ksw<CB>(t) : (kn_swz(t) & (CB - 1));
+    return t * KN_LD + ((((col / VEC) ^ sw) & (CB - 1)) * VEC) + (col % VEC);
   };
   auto sq_at = [&](int r, int col) {
-    return r * SB_LD + (((col / VEC) ^ sq_swz(r)) * VEC) + (col % VEC);
+    const int sw = SWZ ? qsw<CB>(r) : sq_swz(r);
+    return r * SB_LD + ((((col / VEC) ^ sw) & (CB - 1)) * VEC) + (col % VEC);
   };
   auto to_f = [&](DT x) -> float {
     if constexpr (ESZ == 2) return bf16_bits_to_f32(x);
