@@ -288,7 +288,8 @@ hipError_t launch_gated_prefix(float* ws_s, const float* ws_a, const float* s_in
 hipError_t launch_gated_pd(int mode, int io, int D, int G, const GatedArgs& a, int grid, hipStream_t st);
 
 // Whole-sequence token-by-token recurrence (la_recur.hip), one workgroup per
-// (batch, kv head) unit and query-head group; head size 128.
+// (batch, kv head) unit, query-head group and group of 32 state columns; head
+// size 128.
 struct RecurArgs {
   const void* q;      // (B,T,Hq*D)
   const void* k;      // (B,T,Hkv*D)
@@ -300,6 +301,7 @@ struct RecurArgs {
   float* s_out;       // (B*Hkv,D,D)
   int32_t T, Hq, Hkv, units, beta_heads, hsplit;
   float scale;
+  int32_t hg_first, hg_count;  // query-head groups of one launch (set by launch_recur)
 };
 // decay_kind: 0 none, 1 per kv head, 2 per key dim; delta: the delta rule;
 // G: query heads per workgroup (1, 2, 4, 8; hsplit groups of them per unit)

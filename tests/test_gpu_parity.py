@@ -584,30 +584,38 @@ def test_delta_f32_d128(G, kind):
     assert_close(present, po, TOL[dtype], "present_state")
 
 
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G,in_place", [(1, True), (4, True), (8, False), (16, True), (16, False)])
 @pytest.mark.parametrize("rule", ["gated", "gated_delta"])
-def test_perdim_f32_d128_token_by_token(G, rule):
-    """fp32 inputs at head size 128 with a per-dim decay run the one-token step
-    once per token: a ragged length, strong decays (about -20 per token, beyond
-    the chunk kernels' range), the state updated in place across the tokens."""
+@pytest.mark.parametrize("mean", [1.0, -20.0], ids=["mild", "strong"])
+def test_perdim_f32_d128_token_by_token(G, in_place, rule, mean):
+    """fp32 inputs at head size 128 with a per-dim decay run the whole-sequence
+    token-by-token kernel (the state's columns split over four workgroups): a
+    ragged length over several 16-token input blocks, mild and strong decays
+    (about -20 per token, beyond the chunk kernels' range), the state updated in
+    place or written to a new tensor, and groups of up to 16 query heads (two
+    head groups per kv head: in place, the reading group runs before the one
+    that writes the state)."""
     dtype, D, B, T, Hkv = torch.float32, 128, 2, 97, 2
     Hq = Hkv * G
-    seed = 6700 + G + 7 * len(rule)
+    seed = 6700 + G + 7 * len(rule) + (0 if mean < 0 else 50)
     q = synth.normal((B, T, Hq * D), 1.0, dtype, DEV, seed, "q")
     k = synth.l2_normalized((B, T, Hkv, D), dtype, DEV, seed, "k").reshape(B, T, Hkv * D)
     v = synth.normal((B, T, Hkv * D), 1.0, dtype, DEV, seed, "v")
-    g = synth.logsigmoid_decay((B, T, Hkv * D), dtype, DEV, seed, mean=-20.0)
+    g = synth.logsigmoid_decay((B, T, Hkv * D), dtype, DEV, seed, mean=mean)
     past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, seed, "past")
     state = past.clone()
+    dst = state if in_place else torch.empty_like(state)
     if rule == "gated":
-        out, present = la.la_gated_forward(q, k, v, Hq, Hkv, decay=g, past_state=state, present_state=state)
+        out, present = la.la_gated_forward(q, k, v, Hq, Hkv, decay=g, past_state=state, present_state=dst)
         beta = None
     else:
         beta = _beta((B, T, Hkv), dtype, seed)
         out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=state,
-                                           present_state=state)
+                                           present_state=dst)
     torch.cuda.synchronize()
-    assert present.data_ptr() == state.data_ptr()
+    assert present.data_ptr() == dst.data_ptr()
+    if not in_place:
+        assert torch.equal(state, past)
     oo, po = oracle.la_op(f64(q), f64(k), f64(v), Hq, Hkv, rule, past_state=f64(past), decay=f64(g),
                           beta=None if beta is None else f64(beta))
     assert_close(out, oo, TOL[dtype], "out")
