@@ -70,7 +70,7 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
   // elsewhere it measured slower
   // bf16 outputs with two heads per wave: by head pairs
   constexpr bool PAIR = OUT && ESZ == 2 && !VLO && GatedShape<G>::HPW == 2;
-  constexpr bool REFRESH = PAIR || (D >= 128 && (G == 8 || (VLO && G >= 2) || (ESZ == 4 && G >= 4)));
+  constexpr bool REFRESH = PAIR || (D >= 128 && (G == 8 || (VLO && G >= 2) || (ESZ == 4 && G >= 4) || !OUT));
   constexpr int KN_BYTES = kChunk * KN_LD * ESZ;
   constexpr int VT_BYTES = D * VT_LD * ESZ;
   constexpr int VL_BYTES = VLO ? D * VT_LD * ESZ : 0;
@@ -589,11 +589,8 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
       const float eb = __expf(btot);
 #pragma unroll
       for (int i = 0; i < TPW; ++i) sacc[i] *= eb;
-      float kw[NKS][VEC];
-#pragma unroll
-      for (int m = 0; m < NKS; ++m)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) kw[m][e] = __expf(btot - __shfl(bcs, KB * m + VEC * lg + e));
+      // weight of token l in the update, one exp per lane, gathered where used
+      const float wl = __expf(btot - bcs);
       u32x4_t kop[NKS], kol[NKS];
       int cur_rt = -1;
 #pragma unroll
@@ -609,10 +606,11 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
 #pragma unroll
               for (int e = 0; e < VEC; ++e) {
                 const int off = kn_at(KB * m + VEC * lg + e, 16 * rt + lr);
+                const float kw = __shfl(wl, KB * m + VEC * lg + e);
                 if constexpr (ESZ == 2)
-                  f[e] = Io<IT>::to_f32(((const uint16_t*)Kn)[off]) * kw[m][e];
+                  f[e] = Io<IT>::to_f32(((const uint16_t*)Kn)[off]) * kw;
                 else
-                  f[e] = ((const float*)Kn)[off] * kw[m][e];
+                  f[e] = ((const float*)Kn)[off] * kw;
               }
               kop[m] = O::pack(f);
               if constexpr (ESZ == 2) {
