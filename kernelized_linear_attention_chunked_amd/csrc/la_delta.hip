@@ -951,20 +951,20 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   auto update = [&]() {
     refresh();
     u32x4_t kop[NKS], kol[NKS];
+    float er[4];  // per-dim decay of state rows 16 rt + 4 lg + q over the chunk (shared by a row tile's column tiles)
     int cur_rt = -1;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int tau = w * TPW + i;
       if (tau < NS) {
         const int rt = tau / NDT, ct = tau % NDT;
-        if constexpr (DK == 2) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) sacc[i][q] *= __expf(Bc[cl * BC_LD + 16 * rt + 4 * lg + q]);
-        } else if constexpr (DK == 1) {
-          sacc[i] *= __expf(Bt[kChunk + cl]);
-        }
+        if constexpr (DK == 1) sacc[i] *= __expf(Bt[kChunk + cl]);
         if (rt != cur_rt) {
           cur_rt = rt;
+          if constexpr (DK == 2) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) er[q] = __expf(Bc[cl * BC_LD + 16 * rt + 4 * lg + q]);
+          }
           const int dk = 16 * rt + lr;
           const float bC = DK == 2 ? Bc[cl * BC_LD + dk] : (DK == 1 ? Bt[kChunk + cl] : 0.f);
           const float c31 = DK == 2 ? Bc[31 * BC_LD + dk] : (DK == 1 ? Bt[kChunk + 31] : 0.f);
@@ -981,6 +981,10 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
             }
             split8(f, kop[m], kol[m]);
           }
+        }
+        if constexpr (DK == 2) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sacc[i][q] *= er[q];
         }
 #pragma unroll
         for (int m = 0; m < NKS; ++m) {

@@ -502,16 +502,17 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
       if (tid < D) seg_log += Bc[cl * BC_LD + tid];
     }
     u32x4_t kop[NKS], kol[NKS];
+    float er[4];  // the chunk's decay of state rows 16 rt + 4 lg + q (the same for a row tile's column tiles)
     int cur_rt = -1;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int tau = w * TPW + i;
       if (tau < NS) {
         const int rt = tau / NDT, ct = tau % NDT;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sacc[i][q] *= __expf(Bc[cl * BC_LD + 16 * rt + 4 * lg + q]);
         if (rt != cur_rt) {
           cur_rt = rt;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) er[q] = __expf(Bc[cl * BC_LD + 16 * rt + 4 * lg + q]);
           const int dk = 16 * rt + lr;
           const float bC = Bc[cl * BC_LD + dk];
 #pragma unroll
@@ -539,6 +540,8 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
             }
           }
         }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sacc[i][q] *= er[q];
 #pragma unroll
         for (int m = 0; m < NKS; ++m) {
           const u32x4_t bv = ld16(Vt + vt_at(16 * ct + lr, (KB / VEC) * m + lg));
