@@ -563,10 +563,14 @@ void chunk_kernel(ChunkArgs a) {
             at[odd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < NQ; ++m) O::mma(at[odd], kv[m], qop[m]);
+            // causal: key <= query, only where the key block reaches past the
+            // block's first query (below it every key is earlier)
+            if ((ESZ == 2 ? 32 * p + 31 : 16 * p + 15) > 16 * qr) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int key = (ESZ == 2) ? 32 * p + 8 * lg + 4 * odd + q : 16 * p + 4 * lg + q;
-              at[odd][q] = (key <= 16 * qr + lr) ? at[odd][q] : 0.f;  // causal: key <= query
+              for (int q = 0; q < 4; ++q) {
+                const int key = (ESZ == 2) ? 32 * p + 8 * lg + 4 * odd + q : 16 * p + 4 * lg + q;
+                at[odd][q] = (key <= 16 * qr + lr) ? at[odd][q] : 0.f;
+              }
             }
           }
           if constexpr (ESZ == 2) {
@@ -639,7 +643,7 @@ void chunk_kernel(ChunkArgs a) {
       if (tok < T) {
         const bool ok = (full || !mb) ? true : (mb[tok] != 0);
         float rden = 1.f;
-        if constexpr (NORM) rden = ok ? 1.f / (nacc[NDH][0] + eps) : 0.f;
+        if constexpr (NORM) rden = ok ? __builtin_amdgcn_rcpf(nacc[NDH][0] + eps) : 0.f;  // (v_rcp_f32: 1 ulp)
         else rden = ok ? 1.f : 0.f;
         IT* orow = ob + (int64_t)tok * HDV + 4 * lg;
 #pragma unroll
