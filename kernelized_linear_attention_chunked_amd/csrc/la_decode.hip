@@ -489,18 +489,30 @@ hipError_t launch_decode(int io, int Dk, int Dv, int fm, int norm, const DecodeA
   }
 }
 
+// Launch shape of the gated and delta steps: at head size 128 with up to 4
+// query heads per pass one 1024-thread workgroup per unit (4 state rows per
+// thread; the readout partials of 32 row groups take 16 KB of LDS per head),
+// else two 256-thread units per workgroup.
+template <int D, int G>
+struct StepShape {
+  static constexpr bool WIDE = D == 128 && G <= 4;
+  static constexpr int TPU = WIDE ? 1024 : kThreads;
+  static constexpr int UPB = WIDE ? 1 : kDecodeUnits;
+};
+
 // Query heads per readout pass for a kv head with G of them: the largest of
 // 8, 4, 2, 1 that divides G.
 static int head_tile(int G) { return G % 8 == 0 ? 8 : (G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1)); }
 
 template <typename DT, int D, int G, bool PD, bool MP>
 static void launch_gsp(const GatedStepArgs& a, hipStream_t st) {
+  constexpr int TPU = StepShape<D, G>::TPU, UPB = StepShape<D, G>::UPB;
   const bool ntmp = (int64_t)a.units * D * D * 4 >= ((int64_t)256 << 20);
-  const int grid = (a.units + kDecodeUnits - 1) / kDecodeUnits;
+  const int grid = (a.units + UPB - 1) / UPB;
   if (ntmp)
-    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, true, PD, MP>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, true, PD, MP, TPU, UPB>), dim3(grid), dim3(TPU * UPB), 0, st, a);
   else
-    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, false, PD, MP>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    hipLaunchKernelGGL((gated_step_kernel<DT, D, G, false, PD, MP, TPU, UPB>), dim3(grid), dim3(TPU * UPB), 0, st, a);
 }
 
 template <typename DT, int D, int G, bool MP>
@@ -546,12 +558,13 @@ hipError_t launch_gated_step(int io, int D, int G, const GatedStepArgs& a, hipSt
 
 template <typename DT, int D, int G, int DK, bool MP>
 static void launch_dsp(const GatedStepArgs& a, hipStream_t st) {
+  constexpr int TPU = StepShape<D, G>::TPU, UPB = StepShape<D, G>::UPB;
   const bool ntmp = (int64_t)a.units * D * D * 4 >= ((int64_t)256 << 20);
-  const int grid = (a.units + kDecodeUnits - 1) / kDecodeUnits;
+  const int grid = (a.units + UPB - 1) / UPB;
   if (ntmp)
-    hipLaunchKernelGGL((delta_step_kernel<DT, D, G, true, DK, MP>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    hipLaunchKernelGGL((delta_step_kernel<DT, D, G, true, DK, MP, TPU, UPB>), dim3(grid), dim3(TPU * UPB), 0, st, a);
   else
-    hipLaunchKernelGGL((delta_step_kernel<DT, D, G, false, DK, MP>), dim3(grid), dim3(kDecodeThreads), 0, st, a);
+    hipLaunchKernelGGL((delta_step_kernel<DT, D, G, false, DK, MP, TPU, UPB>), dim3(grid), dim3(TPU * UPB), 0, st, a);
 }
 
 template <typename DT, int D, int G, bool MP>
