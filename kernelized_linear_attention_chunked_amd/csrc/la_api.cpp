@@ -703,14 +703,18 @@ la_status gated_forward(const void* q, const void* k, const void* v, const void*
     return device_status(e, "la_gated_forward (token by token)");
   }
   const int64_t GW = head_tile(G), HS = G / GW;  // heads per workgroup, query-head groups
-  // the output passes run HS workgroups per (unit, segment); the state pass one
-  auto launch = [&](int mode, const la::GatedArgs& ga, int grid) {
+  // the output passes run HS workgroups per (unit, segment), query-head groups
+  // first .. first + count - 1 per launch; the state pass one
+  auto launch_groups = [&](int mode, const la::GatedArgs& ga, int grid, int64_t first, int64_t count) {
     la::GatedArgs g2 = ga;
     g2.hsplit = mode == la::kModeCausal ? (int32_t)HS : 1;
-    const int gr = mode == la::kModeCausal ? (int)(grid * HS) : grid;
+    g2.hg_first = mode == la::kModeCausal ? (int32_t)first : 0;
+    g2.hg_count = mode == la::kModeCausal ? (int32_t)count : 1;
+    const int gr = (int)(grid * g2.hg_count);
     return per_dim ? la::launch_gated_pd(mode, dtype, (int)D, (int)GW, g2, gr, st)
                    : la::launch_gated(mode, dtype, (int)D, (int)GW, g2, gr, st);
   };
+  auto launch = [&](int mode, const la::GatedArgs& ga, int grid) { return launch_groups(mode, ga, grid, 0, HS); };
   la::GatedArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -733,7 +737,15 @@ la_status gated_forward(const void* q, const void* k, const void* v, const void*
     a.seg_count = 1;
     a.seg_chunks = (int32_t)p.nchunks;
     a.nseg_total = 1;
-    e = launch(la::kModeCausal, a, (int)U);
+    if (HS > 1 && past_state && past_state == present_state) {
+      // the state updated in place by several query-head groups that each
+      // read it at their start: the groups that only read it run first, then
+      // group 0, which also writes it
+      e = launch_groups(la::kModeCausal, a, (int)U, 1, HS - 1);
+      if (e == hipSuccess) e = launch_groups(la::kModeCausal, a, (int)U, 0, 1);
+    } else {
+      e = launch(la::kModeCausal, a, (int)U);
+    }
     return device_status(e, "la_gated_forward");
   }
   float* ws_s = (float*)workspace;
@@ -949,8 +961,20 @@ LA_EXPORT la_status la_delta_forward(const void* q, const void* k, const void* v
   const DeltaPlan p = plan_delta(U, a.hsplit, T);
   const size_t need = delta_ws_bytes(U, D, p);
   if (need == 0 || !workspace || workspace_bytes < need) {
-    // one workgroup per (unit, head group) over the whole sequence
-    e = la::launch_delta(dtype, (int)D, (int)head_tile(G), kind, a, st);
+    // one workgroup per (unit, head group) over the whole sequence; with the
+    // state updated in place by several head groups, the groups that only read
+    // it run first, then group 0, which also writes it
+    if (a.hsplit > 1 && past_state && past_state == present_state) {
+      la::DeltaArgs r = a;
+      r.hg_first = 1;
+      r.hg_count = a.hsplit - 1;
+      e = la::launch_delta(dtype, (int)D, (int)head_tile(G), kind, r, st);
+      r.hg_first = 0;
+      r.hg_count = 1;
+      if (e == hipSuccess) e = la::launch_delta(dtype, (int)D, (int)head_tile(G), kind, r, st);
+    } else {
+      e = la::launch_delta(dtype, (int)D, (int)head_tile(G), kind, a, st);
+    }
     return device_status(e, "la_delta_forward");
   }
   // split over T: each segment's maps M (from S = I, zero values) and N (from

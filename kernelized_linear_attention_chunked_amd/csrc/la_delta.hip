@@ -146,8 +146,9 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
   // and segment s of ns: tokens [t0, t0 + T) of the unit's sequence
   const int hs = a.hsplit > 1 ? a.hsplit : 1;
   const int ns = a.nseg > 1 ? a.nseg : 1;
-  const int hg = blockIdx.x % hs;
-  const int us = blockIdx.x / hs;
+  const int hc = a.hg_count > 0 ? a.hg_count : hs;  // groups of this launch, from hg_first
+  const int hg = a.hg_first + blockIdx.x % hc;
+  const int us = blockIdx.x / hc;
   const int u = us / ns, s = us % ns;
   const int Hq = a.Hq, Hkv = a.Hkv, TT = a.T;
   const int sl = a.seg_len > 0 ? a.seg_len : TT;  // (a single segment may be shorter than the sequence)
@@ -1018,7 +1019,10 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     __syncthreads();
     write_sb();
   }
-  if (s_out) {
+  // (with a re-evaluation below the state is stored by it: stored here, it
+  // would overwrite a start state the re-evaluation reads when the state is
+  // updated in place)
+  if (s_out && !(RERUN && rerun_flag)) {
     float* sout = s_out;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
@@ -1031,7 +1035,7 @@ __global__ __launch_bounds__(DeltaShape<G>::NTH) void delta_kernel(DeltaArgs a) 
     }
   }
   if constexpr (RERUN) {
-    __syncthreads();  // the chunk loop and the state stores above are done
+    __syncthreads();  // the chunk loop and any state stores above are done
     if (rerun_flag) {
       // strong decays: the whole sequence again, token by token, outputs and state
       RecurPtrs rp;
@@ -1062,11 +1066,11 @@ template <typename IT, int D, int G, bool FULL>
 static void launch_dg(int dk, const DeltaArgs& a, hipStream_t st) {
   constexpr int NTH = DeltaShape<G>::NTH;
   if (dk == 0)
-    hipLaunchKernelGGL((delta_kernel<IT, D, G, 0>), dim3(a.units * (a.hsplit > 1 ? a.hsplit : 1) * (a.nseg > 1 ? a.nseg : 1)), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((delta_kernel<IT, D, G, 0>), dim3(a.units * (a.hg_count > 0 ? a.hg_count : (a.hsplit > 1 ? a.hsplit : 1)) * (a.nseg > 1 ? a.nseg : 1)), dim3(NTH), 0, st, a);
   else if (dk == 1 || !FULL)
-    hipLaunchKernelGGL((delta_kernel<IT, D, G, 1>), dim3(a.units * (a.hsplit > 1 ? a.hsplit : 1) * (a.nseg > 1 ? a.nseg : 1)), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((delta_kernel<IT, D, G, 1>), dim3(a.units * (a.hg_count > 0 ? a.hg_count : (a.hsplit > 1 ? a.hsplit : 1)) * (a.nseg > 1 ? a.nseg : 1)), dim3(NTH), 0, st, a);
   else if constexpr (FULL)
-    hipLaunchKernelGGL((delta_kernel<IT, D, G, 2>), dim3(a.units * (a.hsplit > 1 ? a.hsplit : 1) * (a.nseg > 1 ? a.nseg : 1)), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((delta_kernel<IT, D, G, 2>), dim3(a.units * (a.hg_count > 0 ? a.hg_count : (a.hsplit > 1 ? a.hsplit : 1)) * (a.nseg > 1 ? a.nseg : 1)), dim3(NTH), 0, st, a);
 }
 
 template <typename IT, int D, bool FULL>

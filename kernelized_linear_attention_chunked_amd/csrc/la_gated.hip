@@ -108,8 +108,9 @@ __global__ __launch_bounds__(GatedShape<G>::NTH, (GatedOccupancy<IT, G, MODE>::v
   };
   // query-head group hg of hs (the group's heads are G of the kv head's G * hs)
   const int hs = a.hsplit > 1 ? a.hsplit : 1;
-  const int hg = blockIdx.x % hs;
-  const int bid = blockIdx.x / hs;
+  const int hc = a.hg_count > 0 ? a.hg_count : hs;  // groups of this launch, from hg_first
+  const int hg = a.hg_first + blockIdx.x % hc;
+  const int bid = blockIdx.x / hc;
   const int u = bid / a.seg_count;
   const int s = a.seg_first + bid % a.seg_count;
   const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;

@@ -121,8 +121,9 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
   int l = tid & 63, lr = l & 15, lg = l >> 4;
   // query-head group hg of hs (the group's heads are G of the kv head's G * hs)
   const int hs = a.hsplit > 1 ? a.hsplit : 1;
-  const int hg = blockIdx.x % hs;
-  const int bid = blockIdx.x / hs;
+  const int hc = a.hg_count > 0 ? a.hg_count : hs;  // groups of this launch, from hg_first
+  const int hg = a.hg_first + blockIdx.x % hc;
+  const int bid = blockIdx.x / hc;
   const int u = bid / a.seg_count;
   const int s = a.seg_first + bid % a.seg_count;
   const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
@@ -569,7 +570,10 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
     sout = a.s_out + u * a.s_out_u + (s + a.out_slot_off) * a.s_out_s;
     if (tid < D) a.a_out[((int64_t)u * a.nseg_total + s + a.out_slot_off) * D + tid] = __expf(seg_log);
   }
-  if (sout) {
+  // (with a re-evaluation below the state is stored by it: stored here, it
+  // would overwrite a start state the re-evaluation reads when the state is
+  // updated in place)
+  if (sout && !(OUT && rerun_flag)) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int tau = w * TPW + i;
@@ -583,8 +587,8 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
   if constexpr (OUT) {
     __syncthreads();  // the chunk loop is done with the LDS everywhere
     if (rerun_flag) {
-      // strong decays: the segment's outputs again, token by token (the state
-      // above has factors of at most 1 and stands)
+      // strong decays: the segment's outputs and its final state again, token
+      // by token
       RecurPtrs rp;
       rp.q = qb;
       rp.k = kb;
@@ -593,7 +597,7 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
       rp.beta = nullptr;
       rp.out = ob;
       rp.s_in = a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr;
-      rp.s_out = nullptr;
+      rp.s_out = sout;
       rp.qs = QS;
       rp.ks = KS;
       rp.gs = KS;

@@ -127,9 +127,11 @@ struct GatedArgs {
   int32_t reverse;
   // query-head groups (0 or 1: one): a kv head's Hq/Hkv query heads are split
   // over hsplit workgroups of G heads each (the launcher's G), which all run
-  // the unit's recurrence; group 0 writes the state.  blockIdx = (unit-segment
-  // index) * hsplit + group.  The state pass (kModeState) takes 1.
-  int32_t hsplit;
+  // the unit's recurrence; group 0 writes the state.  A launch runs groups
+  // hg_first .. hg_first + hg_count - 1 (hg_count 0: all), blockIdx = (unit-
+  // segment index) * hg_count + group - hg_first.  The state pass (kModeState)
+  // takes 1.
+  int32_t hsplit, hg_first, hg_count;
 };
 hipError_t launch_gated(int mode, int io, int D, int G, const GatedArgs& a, int grid,
                         hipStream_t st);
@@ -147,11 +149,12 @@ struct DeltaArgs {
   float* s_out;       // (B*Hkv,D,D)
   int32_t T, Hq, Hkv, units, beta_heads;
   float scale;
-  // query-head groups, as GatedArgs::hsplit (grid = units * nseg * hsplit)
-  int32_t hsplit;
+  // query-head groups, as GatedArgs::hsplit, hg_first and hg_count
+  // (grid = units * nseg * hg_count, hg_count 0: hsplit)
+  int32_t hsplit, hg_first, hg_count;
   // Split over T: segment s of nseg (0 or 1: one) covers tokens
   // [s * seg_len, min((s + 1) * seg_len, T)) (seg_len 0: T; a single segment
-  // may be shorter than the sequence); blockIdx = (u * nseg + s) * hsplit
+  // may be shorter than the sequence); blockIdx = (u * nseg + s) * hg_count
   // + group.  The segment starts from s_in + u * s_in_u + s * s_in_s (null:
   // zeros) and writes its final state to s_out + u * s_out_u + s * s_out_s when
   // s_out_all, else only the last segment does.  v null: the values are zero;

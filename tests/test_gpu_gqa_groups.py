@@ -96,3 +96,28 @@ def test_multi_query_32_to_1(dtype, rule):
     oo, po = _oracle(q, k, v, g, beta, past, Hq, Hkv, rule)
     assert_close(out, oo, TOL[dtype], "out")
     assert_close(present, po, TOL[dtype], "present_state")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("G", [16, 32])
+@pytest.mark.parametrize("rule", RULES)
+def test_group_sizes_single_pass_in_place(dtype, G, rule):
+    """One pass per sequence (a single ragged chunk: no split) with the state
+    updated in place by several query-head groups, each of which reads the
+    past state at its start: the groups that only read it run before group 0,
+    which writes it.  288 units, so the workgroups do not all fit the GPU at
+    once."""
+    B, T, Hkv, D = 144, 60, 2, 64
+    Hq = Hkv * G
+    seed = 8400 + G + 11 * RULES.index(rule)
+    q, k, v, g, beta, past = _inputs(B, T, Hq, Hkv, D, dtype, seed, rule)
+    ref_past = past.clone()
+    if rule.endswith("delta"):
+        out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=past, present_state=past)
+    else:
+        out, present = la.la_gated_forward(q, k, v, Hq, Hkv, decay=g, past_state=past, present_state=past)
+    torch.cuda.synchronize()
+    assert present.data_ptr() == past.data_ptr()
+    oo, po = _oracle(q, k, v, g, beta, ref_past, Hq, Hkv, rule)
+    assert_close(out, oo, TOL[dtype], "out")
+    assert_close(present, po, TOL[dtype], "present_state")

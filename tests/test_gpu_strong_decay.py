@@ -103,3 +103,23 @@ def test_gated_delta_very_strong_d128(dtype):
     q, k, v, g, beta = _inputs(B, T, Hq, Hkv, D, dtype, 9500, -4.0)
     out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g)
     _check(out, present, q, k, v, g, beta, Hq, Hkv, "gated_delta", dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("rule", ["gated", "gated_delta"])
+def test_strong_perdim_single_pass_in_place(dtype, rule):
+    """One pass per sequence (no split, no workspace), a past state updated in
+    place, decays of about -4 per token: the token-by-token re-evaluation
+    starts from the past state, not from a state the pass has already written."""
+    B, T, Hkv, G, D = 64, 200, 8, 2, 64
+    Hq = Hkv * G
+    q, k, v, g, beta = _inputs(B, T, Hq, Hkv, D, dtype, 9600, -4.0)
+    past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, 9600, "past")
+    state = past.clone()
+    if rule == "gated":
+        out, present = la.la_gated_forward(q, k, v, Hq, Hkv, decay=g, past_state=state, present_state=state)
+        beta = None
+    else:
+        out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=state, present_state=state)
+    assert present.data_ptr() == state.data_ptr()
+    _check(out, present, q, k, v, g, beta, Hq, Hkv, rule, dtype, past)
