@@ -373,8 +373,12 @@ la_status forward_impl(const void* q, const void* k, const void* v, const uint8_
     ps.seg_chunks = (int32_t)p.seg_chunks;
     ps.nseg_total = (int32_t)p.nseg;
     e = la::launch_chunk(la::kModeState, dtype, Di, feature_map, norm, ps, (int)(U * (p.nseg - 1)), st);
-    // up to kChunkFold segments the causal pass adds the slots itself
-    const bool fold = p.nseg <= la::kChunkFold && Di <= 64;
+    // up to kChunkFold segments the causal pass adds the slots itself, reading
+    // the initial state in every segment; a state updated in place goes
+    // through the prefix pass instead (its slot 0 holds the initial state), so
+    // that no segment reads it after the last one has written it
+    const bool in_place = (state_in_kv && state_in_kv == state_out_kv) || (state_in_k && state_in_k == state_out_k);
+    const bool fold = p.nseg <= la::kChunkFold && Di <= 64 && !in_place;
     if (e == hipSuccess && !fold)
       e = la::launch_seg_prefix(ws_s, ws_z, state_in_kv, state_in_k, (int)U, (int)p.nseg, (int)Dk, (int)Dv, norm,
                                 st);

@@ -61,6 +61,24 @@ def test_causal_small(dtype, D, fm, norm):
     assert np.all(f64(y)[~m] == 0.0)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_causal_split_state_in_place(dtype, D):
+    """A split sequence (6 units of 16 chunks) whose state is updated in place:
+    every segment starts from the initial state before the last one writes the
+    final state over it."""
+    B, T, H = 2, 1000, 3
+    q, k, v = _inputs(B, T, H, D, dtype, 4400 + D)
+    S0, Z0 = _state(B, H, D, 4400 + D)
+    S, Z = S0.clone(), Z0.clone()
+    y = la.la_forward(q, k, v, state=(S, Z), causal=True, state_out=(S, Z))
+    torch.cuda.synchronize()
+    yo, So, Zo = oracle.causal(f64(q), f64(k), f64(v), None, f64(S0), f64(Z0))
+    assert_close(y, yo, TOL[dtype], "out")
+    assert_close(S, So, TOL[dtype], "S")
+    assert_close(Z, Zo, TOL[dtype], "Z")
+
+
 @pytest.mark.parametrize("dtype", DTYPES, ids=DT_IDS)
 @pytest.mark.parametrize("D", [64, 128])
 def test_causal_single_pass_path(dtype, D):
