@@ -139,7 +139,10 @@ la_status la_step(const void* q, const void* k, const void* v, const uint8_t* ma
                   void* stream);
 
 /* Bytes of device workspace la_gated_forward needs (0 = none); shape-only.
- * per_dim_decay as in la_gated_forward (a per-dim decay needs a little more). */
+ * per_dim_decay as in la_gated_forward.  With few (batch, kv head) units and a
+ * long sequence the sequence is split, and the workspace holds one fp32 state
+ * per segment; a per-dim decay adds one int flag per (unit, segment), so it
+ * needs a workspace whenever T > 1 (except fp32 at Dk = 128, see below). */
 la_status la_gated_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,
                                   int64_t Dv, int32_t dtype, int32_t per_dim_decay, size_t* bytes);
 
@@ -163,11 +166,15 @@ la_status la_gated_workspace_size(int64_t B, int64_t T, int64_t Hq, int64_t Hkv,
  * included.  Decays of any strength are supported.  A per-dim decay is
  * evaluated chunk-parallel with keys rescaled relative to a reference token;
  * where some dimension's cumulative decay inside a 64-token chunk exceeds 60
- * in magnitude, the workgroup concerned re-evaluates its tokens one at a
- * time (exact, and slower by a large factor for that workgroup).  fp32 inputs
- * at Dk = 128 with a per-dim decay and T > 1 (whose chunk tiles exceed the
- * LDS) run the T == 1 step kernel once per token instead: no workspace, but
- * one state read and write per token (la_gated_workspace_size reports 0). */
+ * in magnitude, the segment concerned is flagged in the workspace and a
+ * second launch re-evaluates its tokens one at a time (exact, and slower by a
+ * large factor for that segment).  fp32 inputs at Dk = 128 with a per-dim
+ * decay and T > 1 (whose chunk tiles exceed the LDS) run a token-by-token
+ * recurrence over the whole sequence instead, the state held on chip: no
+ * workspace (la_gated_workspace_size reports 0).
+ * workspace: la_gated_workspace_size bytes, 16-byte aligned, overlapping no
+ * other argument (NULL when that is 0); a smaller one is LA_ERR_WORKSPACE.
+ * Its contents need no initialisation and are scratch after the call. */
 la_status la_gated_forward(const void* q, const void* k, const void* v, const void* decay,
                            int32_t per_dim_decay, const float* past_state, float* present_state,
                            void* out, int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk,

@@ -545,15 +545,20 @@ GatedPlan plan_gated(int64_t U, int64_t T) {
   }
   return p;
 }
-size_t gated_ws_bytes(int64_t B, int64_t T, int64_t Hkv, int64_t D, bool per_dim) {
-  const int64_t U = B * Hkv;
-  if (U == 0 || T <= 1) return 0;
-  GatedPlan p = plan_gated(U, T);
+// bytes of the split's state slots and decay factors (0 without a split)
+size_t gated_split_bytes(int64_t U, const GatedPlan& p, int64_t D, bool per_dim) {
   if (p.nseg <= 1) return 0;
   // slots of D*D floats plus the decay factors of each slot (one, or one per
   // key dim), padded to 16 bytes
   const int64_t na = U * p.nseg * (per_dim ? D : 1);
   return (size_t)(U * p.nseg * D * D * 4 + ceil_div(na, 4) * 16);
+}
+size_t gated_ws_bytes(int64_t B, int64_t T, int64_t Hkv, int64_t D, bool per_dim) {
+  const int64_t U = B * Hkv;
+  if (U == 0 || T <= 1) return 0;
+  GatedPlan p = plan_gated(U, T);
+  // a per-dim decay adds one strong-decay flag per (unit, segment)
+  return gated_split_bytes(U, p, D, per_dim) + (per_dim ? (size_t)ceil_div(U * p.nseg, 4) * 16 : 0);
 }
 la_status check_gated(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t Dk, int64_t Dv,
                       int32_t dtype) {
@@ -711,14 +716,31 @@ la_status gated_forward(const void* q, const void* k, const void* v, const void*
   // first .. first + count - 1 per launch; the state pass one
   auto launch_groups = [&](int mode, const la::GatedArgs& ga, int grid, int64_t first, int64_t count) {
     la::GatedArgs g2 = ga;
-    g2.hsplit = mode == la::kModeCausal ? (int32_t)HS : 1;
-    g2.hg_first = mode == la::kModeCausal ? (int32_t)first : 0;
-    g2.hg_count = mode == la::kModeCausal ? (int32_t)count : 1;
+    const bool grouped = mode != la::kModeState;
+    g2.hsplit = grouped ? (int32_t)HS : 1;
+    g2.hg_first = grouped ? (int32_t)first : 0;
+    g2.hg_count = grouped ? (int32_t)count : 1;
     const int gr = (int)(grid * g2.hg_count);
     return per_dim ? la::launch_gated_pd(mode, dtype, (int)D, (int)GW, g2, gr, st)
                    : la::launch_gated(mode, dtype, (int)D, (int)GW, g2, gr, st);
   };
-  auto launch = [&](int mode, const la::GatedArgs& ga, int grid) { return launch_groups(mode, ga, grid, 0, HS); };
+  // the output pass over grid (unit, segment) workgroups per query-head group;
+  // with a per-dim decay, then the re-evaluation of its flagged segments.  A
+  // state updated in place by several groups that each read it at their start:
+  // the groups that only read it run first, then group 0, which also writes it.
+  auto launch_out = [&](const la::GatedArgs& ga, int grid, bool in_place) {
+    hipError_t r = hipSuccess;
+    for (int pass = 0; pass < (per_dim ? 2 : 1) && r == hipSuccess; ++pass) {
+      const int mode = pass == 0 ? la::kModeCausal : la::kModeRerun;
+      if (in_place && HS > 1) {
+        r = launch_groups(mode, ga, grid, 1, HS - 1);
+        if (r == hipSuccess) r = launch_groups(mode, ga, grid, 0, 1);
+      } else {
+        r = launch_groups(mode, ga, grid, 0, HS);
+      }
+    }
+    return r;
+  };
   la::GatedArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -733,6 +755,7 @@ la_status gated_forward(const void* q, const void* k, const void* v, const void*
   a.reverse = reverse;
   const int64_t SE = D * D;
   GatedPlan p = plan_gated(U, T);
+  if (per_dim) a.flags = (int32_t*)((char*)workspace + gated_split_bytes(U, p, D, true));
   if (p.nseg == 1) {
     a.s_in = past_state;
     a.s_in_u = SE;
@@ -741,15 +764,7 @@ la_status gated_forward(const void* q, const void* k, const void* v, const void*
     a.seg_count = 1;
     a.seg_chunks = (int32_t)p.nchunks;
     a.nseg_total = 1;
-    if (HS > 1 && past_state && past_state == present_state) {
-      // the state updated in place by several query-head groups that each
-      // read it at their start: the groups that only read it run first, then
-      // group 0, which also writes it
-      e = launch_groups(la::kModeCausal, a, (int)U, 1, HS - 1);
-      if (e == hipSuccess) e = launch_groups(la::kModeCausal, a, (int)U, 0, 1);
-    } else {
-      e = launch(la::kModeCausal, a, (int)U);
-    }
+    e = launch_out(a, (int)U, past_state && past_state == present_state);
     return device_status(e, "la_gated_forward");
   }
   float* ws_s = (float*)workspace;
@@ -763,7 +778,7 @@ la_status gated_forward(const void* q, const void* k, const void* v, const void*
   ps.seg_count = (int32_t)(p.nseg - 1);
   ps.seg_chunks = (int32_t)p.seg_chunks;
   ps.nseg_total = (int32_t)p.nseg;
-  e = launch(la::kModeState, ps, (int)(U * (p.nseg - 1)));
+  e = launch_groups(la::kModeState, ps, (int)(U * (p.nseg - 1)), 0, 1);
   if (e == hipSuccess)
     e = la::launch_gated_prefix(ws_s, ws_a, past_state, (int)U, (int)p.nseg, (int)D, per_dim ? 1 : 0, st);
   if (e == hipSuccess) {
@@ -776,7 +791,7 @@ la_status gated_forward(const void* q, const void* k, const void* v, const void*
     pc.seg_count = (int32_t)p.nseg;
     pc.seg_chunks = (int32_t)p.seg_chunks;
     pc.nseg_total = (int32_t)p.nseg;
-    e = launch(la::kModeCausal, pc, (int)(U * p.nseg));
+    e = launch_out(pc, (int)(U * p.nseg), false);
   }
   return device_status(e, "la_gated_forward (split)");
 }

@@ -21,9 +21,9 @@
 // keys k^ = k e^{c - b} are formed once per chunk in LDS beside the raw keys,
 // which the state update uses with e^{b_C - b_s} applied in fp32.  When some
 // dimension's cumulative decay inside a chunk exceeds kExactSpan in magnitude
-// (the factors could leave the fp32 range), the workgroup re-evaluates its
-// segment's outputs token by token (la_recur.hpp), which holds for decays of
-// any strength; the state, whose factors never exceed 1, is kept.
+// (the factors could leave the fp32 range), the workgroup flags its segment,
+// and a second launch re-evaluates the segment's outputs and state token by
+// token (la_recur.hpp), which holds for decays of any strength.
 //
 // Workgroup shape, loaders, V^T staging (hi + lo tiles for fp16 inputs) and the
 // MFMA operand conventions follow the per-head-decay kernel (la_gated.hip).
@@ -100,8 +100,6 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
                 "LDS budget");
 
   constexpr int SMEM = K2_BYTES + VT_BYTES + SB_BYTES + VL_BYTES + BC_BYTES + WT_BYTES + KL_BYTES + 16;
-  constexpr int RHP = recur_heads<D, NTH, G>(SMEM);  // heads per pass of the token-by-token re-evaluation
-  static_assert(!OUT || RHP >= 1, "LDS for the token-by-token re-evaluation");
   __shared__ __align__(16) unsigned char smem[SMEM];
   __shared__ int rerun_flag;  // some chunk's decays exceed kExactSpan
   DT* Kn = (DT*)smem;                   // k as loaded (operand type, or raw fp16)
@@ -570,8 +568,8 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
     sout = a.s_out + u * a.s_out_u + (s + a.out_slot_off) * a.s_out_s;
     if (tid < D) a.a_out[((int64_t)u * a.nseg_total + s + a.out_slot_off) * D + tid] = __expf(seg_log);
   }
-  // (with a re-evaluation below the state is stored by it: stored here, it
-  // would overwrite a start state the re-evaluation reads when the state is
+  // (a flagged segment's state is stored by the re-evaluation: stored here,
+  // it would overwrite a start state the re-evaluation reads when the state is
   // updated in place)
   if (sout && !(OUT && rerun_flag)) {
 #pragma unroll
@@ -585,29 +583,55 @@ __global__ __launch_bounds__(PdShape<G>::NTH, (PdOccupancy<IT, G, MODE>::value))
     }
   }
   if constexpr (OUT) {
-    __syncthreads();  // the chunk loop is done with the LDS everywhere
-    if (rerun_flag) {
-      // strong decays: the segment's outputs and its final state again, token
-      // by token
-      RecurPtrs rp;
-      rp.q = qb;
-      rp.k = kb;
-      rp.v = vb;
-      rp.decay = gb;
-      rp.beta = nullptr;
-      rp.out = ob;
-      rp.s_in = a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr;
-      rp.s_out = sout;
-      rp.qs = QS;
-      rp.ks = KS;
-      rp.gs = KS;
-      rp.bs = 0;
-      rp.t0 = c0 * kChunk;
-      rp.t1 = min(c1 * kChunk, T);
-      rp.scale = scale;
-      token_recurrence<IT, D, NTH, G, RHP, 2, false>(smem, rp);
-    }
+    // (all query-head groups see the same decays: group 0 stores the flag)
+    if (tid == 0 && hg == 0) a.flags[u * a.nseg_total + s] = rerun_flag;
   }
+}
+
+// Strong decays: the segments whose output pass set their flag, outputs and
+// final state again token by token (la_recur.hpp), which holds for decays of
+// any strength.  Same grid, query-head groups and pointers as the output pass;
+// the others return at once.  The re-evaluation lives in a launch of its own:
+// inside the output kernel its code cost that kernel about 7% on the per-dim
+// workload, though it rarely runs.
+template <typename IT, int D, int G>
+__global__ __launch_bounds__(PdShape<G>::NTH) void gated_pd_rerun_kernel(GatedArgs a) {
+  constexpr int NTH = PdShape<G>::NTH;
+  constexpr int RHP = recur_heads<D, NTH, G>(128 * 1024);  // heads per pass
+  static_assert(RHP >= 1, "LDS for the token-by-token re-evaluation");
+  __shared__ __align__(16) unsigned char smem[recur_lds_bytes<D, NTH, G, RHP>()];
+  const int hs = a.hsplit > 1 ? a.hsplit : 1;
+  const int hc = a.hg_count > 0 ? a.hg_count : hs;
+  const int hg = a.hg_first + blockIdx.x % hc;
+  const int bid = blockIdx.x / hc;
+  const int u = bid / a.seg_count;
+  const int s = a.seg_first + bid % a.seg_count;
+  if (!a.flags[u * a.nseg_total + s]) return;
+  const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
+  const int b = u / Hkv, j = u % Hkv;
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const int c0 = s * a.seg_chunks;
+  const int c1 = min(c0 + a.seg_chunks, nchunks);
+  const int QS = Hq * D, KS = Hkv * D;
+  const int64_t qo = (int64_t)b * T * QS + (int64_t)(j * G * hs + hg * G) * D;
+  const int64_t ko = (int64_t)b * T * KS + (int64_t)j * D;
+  RecurPtrs rp;
+  rp.q = (const IT*)a.q + qo;
+  rp.k = (const IT*)a.k + ko;
+  rp.v = (const IT*)a.v + ko;
+  rp.decay = (const IT*)a.decay + ko;
+  rp.beta = nullptr;
+  rp.out = (IT*)a.out + qo;
+  rp.s_in = a.s_in ? a.s_in + u * a.s_in_u + s * a.s_in_s : nullptr;
+  rp.s_out = (s == a.nseg_total - 1 && hg == 0) ? a.s_out + u * a.s_out_u : nullptr;
+  rp.qs = QS;
+  rp.ks = KS;
+  rp.gs = KS;
+  rp.bs = 0;
+  rp.t0 = c0 * kChunk;
+  rp.t1 = min(c1 * kChunk, T);
+  rp.scale = a.scale;
+  token_recurrence<IT, D, NTH, G, RHP, 2, false>(smem, rp);
 }
 
 template <typename IT, int D, int G>
@@ -615,6 +639,8 @@ static hipError_t launch_pg(int mode, const GatedArgs& a, int grid, hipStream_t 
   constexpr int NTH = PdShape<G>::NTH;
   if (mode == kModeCausal)
     hipLaunchKernelGGL((gated_pd_kernel<IT, D, G, kModeCausal>), dim3(grid), dim3(NTH), 0, st, a);
+  else if (mode == kModeRerun)
+    hipLaunchKernelGGL((gated_pd_rerun_kernel<IT, D, G>), dim3(grid), dim3(NTH), 0, st, a);
   else
     hipLaunchKernelGGL((gated_pd_kernel<IT, D, G, kModeState>), dim3(grid), dim3(NTH), 0, st, a);
   return hipGetLastError();

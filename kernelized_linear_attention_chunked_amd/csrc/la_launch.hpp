@@ -48,7 +48,7 @@ struct ChunkArgs {
   int32_t dk, dv;
 };
 
-enum { kModeCausal = 0, kModeState = 1 };
+enum { kModeCausal = 0, kModeState = 1, kModeRerun = 2 };
 // I/O element type codes of the launchers (the values of la_dtype)
 enum { kIoF32 = 0, kIoBF16 = 1, kIoF16 = 2 };
 
@@ -132,6 +132,12 @@ struct GatedArgs {
   // segment index) * hg_count + group - hg_first.  The state pass (kModeState)
   // takes 1.
   int32_t hsplit, hg_first, hg_count;
+  // per-dim kernel: one int per (unit, segment), u * nseg_total + s.  The
+  // output pass (kModeCausal) stores 1 where the segment's decays are too
+  // strong for its chunk form (and then leaves its state unwritten), else 0;
+  // the re-evaluation launch (kModeRerun, same grid and groups) redoes those
+  // segments token by token, outputs and state.
+  int32_t* flags;
 };
 hipError_t launch_gated(int mode, int io, int D, int G, const GatedArgs& a, int grid,
                         hipStream_t st);
@@ -287,7 +293,8 @@ hipError_t launch_delta_step(int io, int D, int G, const GatedStepArgs& a, hipSt
 hipError_t launch_gated_prefix(float* ws_s, const float* ws_a, const float* s_in, int U, int nseg,
                                int D, int per_dim, hipStream_t st);
 // Per-key-dim decay (la_gated_pd.hip): the same arguments and modes as
-// launch_gated; fp32 at head size 128 is not available (LDS).
+// launch_gated, plus kModeRerun after each output pass (flags required in both);
+// fp32 at head size 128 is not available (LDS).
 hipError_t launch_gated_pd(int mode, int io, int D, int G, const GatedArgs& a, int grid, hipStream_t st);
 
 // Whole-sequence token-by-token recurrence (la_recur.hip), one workgroup per

@@ -156,7 +156,11 @@ def test_gated_argument_errors(lib):
     assert n.value == 16 * 32 * 128 * 128 * 4 + 16 * 32 * 4
     m = ctypes.c_size_t(0)
     assert lib.la_gated_workspace_size(2, 32768, 32, 8, 128, 128, 1, 1, ctypes.byref(m)) == OK
-    assert m.value == 16 * 32 * 128 * 128 * 4 + 16 * 32 * 128 * 4
+    # ... plus one strong-decay flag (int) per (unit, segment) with a per-dim decay
+    assert m.value == 16 * 32 * 128 * 128 * 4 + 16 * 32 * 128 * 4 + 16 * 32 * 4
+    # without a split a per-dim decay still needs its flags: 2 units, padded to 16 bytes
+    assert lib.la_gated_workspace_size(1, 64, 4, 2, 64, 64, 1, 0, ctypes.byref(m)) == OK and m.value == 0
+    assert lib.la_gated_workspace_size(1, 64, 4, 2, 64, 64, 1, 1, ctypes.byref(m)) == OK and m.value == 16
 
     def g(**kw):
         a = dict(q=f(1 << 30), k=f(2 << 30), v=f(3 << 30), d=None, pd=0, past=None, pres=f(4 << 30),
@@ -173,6 +177,8 @@ def test_gated_argument_errors(lib):
     assert g(dt=5) == DTYPE
     assert g(scale=float("inf")) == BAD_ARG
     assert g(T=4096) == WORKSPACE             # 2 units: the sequence is split
+    assert g(d=f(6 << 30), pd=1) == WORKSPACE  # a per-dim decay's strong-decay flags
+    assert g(d=f(6 << 30), pd=1, ws=f(7 << 30), wsb=8) == WORKSPACE
     assert g(out=f(1 << 30)) == BAD_ARG       # out aliases q
     # fp32 per-dim decay at head size 128 runs token by token: no workspace
     n = ctypes.c_size_t(1)
