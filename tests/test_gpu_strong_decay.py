@@ -123,3 +123,36 @@ def test_strong_perdim_single_pass_in_place(dtype, rule):
         out, present = la.la_delta_forward(q, k, v, Hq, Hkv, beta, decay=g, past_state=state, present_state=state)
     assert present.data_ptr() == state.data_ptr()
     _check(out, present, q, k, v, g, beta, Hq, Hkv, rule, dtype, past)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("G", [2, 16])
+@pytest.mark.parametrize("layout", ["single_pass_in_place", "split"])
+def test_strong_perdim_some_segments_groups(dtype, G, layout):
+    """Strong per-dim decays in some (unit, segment) pairs only, with one or
+    several query-head groups per kv head: the flagged pairs are re-evaluated
+    token by token for every group (outputs, and the final state from group
+    0), the others keep the chunk pass's results.  The single pass updates the
+    state in place (288 units of one chunk); the split call has 2 units of 6
+    segments."""
+    Hkv, D = 2, 64
+    B, T = (144, 60) if layout == "single_pass_in_place" else (1, 330)
+    Hq = Hkv * G
+    q, k, v, g, _ = _inputs(B, T, Hq, Hkv, D, dtype, 9700 + G, 2.0)
+    g = g.float()
+    # about -180 and -80 accumulated inside a chunk: past the factorised range
+    if layout == "single_pass_in_place":
+        g[0::3, 10:40, 3] = -6.0
+        g[1::3, 20:30, D + 7] = -8.0
+    else:
+        g[0, 70:100, 3] = -6.0
+        g[0, 260:270, D + 7] = -8.0
+    g = g.to(dtype)
+    past = synth.normal((B, Hkv, D, D), 0.3, torch.float32, DEV, 9700 + G, "past")
+    if layout == "single_pass_in_place":
+        state = past.clone()
+        out, present = la.la_gated_forward(q, k, v, Hq, Hkv, decay=g, past_state=state, present_state=state)
+        assert present.data_ptr() == state.data_ptr()
+    else:
+        out, present = la.la_gated_forward(q, k, v, Hq, Hkv, decay=g, past_state=past)
+    _check(out, present, q, k, v, g, None, Hq, Hkv, "gated", dtype, past)
